@@ -1,0 +1,266 @@
+/*
+ * Plain fp64 CPU oracle for Lizard attention (forward and one decode step).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
+ * load this file: only the tests, the smoke check and the benchmark's CPU
+ * baseline leg use it.  It shares no code, header, table or helper with the
+ * HIP library.
+ *
+ * What it computes, and where the pages define it:
+ *
+ *   Feature map        phi(x) = softmax over features of (x . W_phi)
+ *                      (the softmax-over-features map of the synthetic
+ *                      workloads; the Lizard paper's own map is the
+ *                      exp(xW) (+) exp(-xW) "Hedgehog" map, arXiv page,
+ *                      Method section, hardware-efficient reparameterization
+ *                      paragraph).
+ *   Global branch      h_i = gamma_i (.) h_{i-1} + phi(k_i) v_i^T,
+ *                      y_i = phi(q_i)^T h_i, with a per-key-dimension gate
+ *                      gamma_i = exp(log_gamma_i) that scales every row of h
+ *                      (papernotes.org summary of the Lizard paper, section
+ *                      "key designs", Gated Linear Attention item).
+ *   Local branch       softmax over [q_i.T_k ; q_i.k_j for the W most recent
+ *                      keys j, i included] applied to [T_v ; v_j]
+ *                      (same summary, "key designs", Anchor Window Attention
+ *                      item; the meta-memory tokens T are always visible).
+ *   Merge              y = mix * y_gla + (1 - mix) * y_win
+ *                      (same summary, "overall framework": the two branch
+ *                      outputs are combined with weights).
+ *
+ * It is deliberately the literal token-by-token recurrence and a brute-force
+ * window softmax, in double precision, with no blocking, chunking or
+ * reordering.  OpenMP runs independent (batch, query head) pairs in parallel.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* phi = softmax_f( sum_i x[i] * w[i*df + f] ), max subtracted first. */
+static void feature_map(const double *x, const double *w, int d, int df,
+                        double *z, double *phi) {
+  double zmax = -INFINITY;
+  for (int f = 0; f < df; ++f) {
+    double acc = 0.0;
+    for (int i = 0; i < d; ++i) acc += x[i] * w[(int64_t)i * df + f];
+    z[f] = acc;
+    if (acc > zmax) zmax = acc;
+  }
+  double sum = 0.0;
+  for (int f = 0; f < df; ++f) {
+    phi[f] = exp(z[f] - zmax);
+    sum += phi[f];
+  }
+  for (int f = 0; f < df; ++f) phi[f] /= sum;
+}
+
+static double dot(const double *a, const double *b, int n) {
+  double acc = 0.0;
+  for (int i = 0; i < n; ++i) acc += a[i] * b[i];
+  return acc;
+}
+
+/*
+ * Forward over whole sequences.
+ *   q [B,Hq,L,d]; k, v [B,Hkv,L,d]; lg (log gamma) [B,Hkv,L,df]
+ *   wq, wk: W_phi for query / key side, [.,d,df]; head h uses w + h*w_stride
+ *           (w_stride = 0: one matrix shared by all heads)
+ *   tk, tv  [Hkv,M,d] meta-memory keys / values
+ *   y, y_gla, y_win [B,Hq,L,d] (y_gla / y_win may be NULL)
+ *   state_out [B,Hkv,df,d] final h (may be NULL)
+ * Query head hq reads key/value head hq / (Hq/Hkv).
+ * Returns 0, or -1 on a shape it cannot take.
+ */
+int oracle_lizard_fwd(const double *q, const double *k, const double *v,
+                      const double *lg, const double *wq, const double *wk,
+                      int64_t w_stride, const double *tk, const double *tv,
+                      int B, int Hq, int Hkv, int L, int d, int df, int W,
+                      int M, double mix, double scale, double *y,
+                      double *y_gla, double *y_win, double *state_out) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || L < 0 || d < 1 || df < 1 || W < 1 ||
+      M < 0 || Hq % Hkv != 0)
+    return -1;
+  const int G = Hq / Hkv;
+  const int nb = B * Hq;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int bh = 0; bh < nb; ++bh) {
+    const int b = bh / Hq, hq = bh % Hq, hk = hq / G;
+    const double *qh = q + ((int64_t)b * Hq + hq) * L * d;
+    const double *kh = k + ((int64_t)b * Hkv + hk) * L * d;
+    const double *vh = v + ((int64_t)b * Hkv + hk) * L * d;
+    const double *gh = lg + ((int64_t)b * Hkv + hk) * L * df;
+    const double *wqh = wq + (int64_t)hq * w_stride;
+    const double *wkh = wk + (int64_t)hk * w_stride;
+    const double *tkh = tk + (int64_t)hk * M * d;
+    const double *tvh = tv + (int64_t)hk * M * d;
+    double *S = calloc((size_t)df * d, sizeof(double));
+    double *phq = malloc(sizeof(double) * df);
+    double *phk = malloc(sizeof(double) * df);
+    double *z = malloc(sizeof(double) * df);
+    double *logit = malloc(sizeof(double) * (M + (W < L ? W : L) + 1));
+    double *yg = malloc(sizeof(double) * d);
+    double *yw = malloc(sizeof(double) * d);
+    for (int i = 0; i < L; ++i) {
+      const double *qi = qh + (int64_t)i * d;
+      const double *ki = kh + (int64_t)i * d;
+      const double *vi = vh + (int64_t)i * d;
+      const double *gi = gh + (int64_t)i * df;
+      /* global branch: decay every key-dimension row, then add phi(k) v^T */
+      feature_map(ki, wkh, d, df, z, phk);
+      feature_map(qi, wqh, d, df, z, phq);
+      for (int f = 0; f < df; ++f) {
+        const double gam = exp(gi[f]);
+        double *row = S + (int64_t)f * d;
+        for (int e = 0; e < d; ++e) row[e] = gam * row[e] + phk[f] * vi[e];
+      }
+      for (int e = 0; e < d; ++e) yg[e] = 0.0;
+      for (int f = 0; f < df; ++f) {
+        const double *row = S + (int64_t)f * d;
+        for (int e = 0; e < d; ++e) yg[e] += phq[f] * row[e];
+      }
+      /* local branch: M meta keys plus keys j in [i-W+1, i] */
+      const int lo = i - W + 1 > 0 ? i - W + 1 : 0;
+      int n = 0;
+      double mx = -INFINITY;
+      for (int m = 0; m < M; ++m) {
+        logit[n] = scale * dot(qi, tkh + (int64_t)m * d, d);
+        if (logit[n] > mx) mx = logit[n];
+        ++n;
+      }
+      for (int j = lo; j <= i; ++j) {
+        logit[n] = scale * dot(qi, kh + (int64_t)j * d, d);
+        if (logit[n] > mx) mx = logit[n];
+        ++n;
+      }
+      double zsum = 0.0;
+      for (int a = 0; a < n; ++a) {
+        logit[a] = exp(logit[a] - mx);
+        zsum += logit[a];
+      }
+      for (int e = 0; e < d; ++e) yw[e] = 0.0;
+      n = 0;
+      for (int m = 0; m < M; ++m, ++n)
+        for (int e = 0; e < d; ++e) yw[e] += logit[n] * tvh[(int64_t)m * d + e];
+      for (int j = lo; j <= i; ++j, ++n)
+        for (int e = 0; e < d; ++e) yw[e] += logit[n] * vh[(int64_t)j * d + e];
+      for (int e = 0; e < d; ++e) yw[e] /= zsum;
+      const int64_t o = (((int64_t)b * Hq + hq) * L + i) * d;
+      for (int e = 0; e < d; ++e) {
+        y[o + e] = mix * yg[e] + (1.0 - mix) * yw[e];
+        if (y_gla) y_gla[o + e] = yg[e];
+        if (y_win) y_win[o + e] = yw[e];
+      }
+    }
+    if (state_out && hq % G == 0)
+      memcpy(state_out + ((int64_t)b * Hkv + hk) * df * d, S,
+             sizeof(double) * df * d);
+    free(S); free(phq); free(phk); free(z); free(logit); free(yg); free(yw);
+  }
+  return 0;
+}
+
+/*
+ * One decode step: every sequence n takes one new token.
+ *   state [N,Hkv,df,d]           h, updated in place
+ *   ring_k, ring_v [N,Hkv,W,d]   the last W keys / values; token t sits in
+ *                                slot t % W; updated in place
+ *   pos [N]                      tokens already seen (index of the new token);
+ *                                incremented
+ *   q [N,Hq,d]; k, v [N,Hkv,d]; lg [N,Hkv,df]; out, y_gla, y_win [N,Hq,d]
+ * The per-token arithmetic is the forward's: decay then add, read out, and a
+ * softmax over the M meta keys and the min(pos+1, W) newest keys.
+ */
+int oracle_lizard_decode(double *state, double *ring_k, double *ring_v,
+                         int32_t *pos, const double *q, const double *k,
+                         const double *v, const double *lg, const double *wq,
+                         const double *wk, int64_t w_stride, const double *tk,
+                         const double *tv, int N, int Hq, int Hkv, int d,
+                         int df, int W, int M, double mix, double scale,
+                         double *out, double *y_gla, double *y_win) {
+  if (N < 1 || Hq < 1 || Hkv < 1 || d < 1 || df < 1 || W < 1 || M < 0 ||
+      Hq % Hkv != 0)
+    return -1;
+  for (int n = 0; n < N; ++n)
+    if (pos[n] < 0) return -1;
+  const int G = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int n = 0; n < N; ++n) {
+    const int p = pos[n];
+    const int slot = p % W;
+    const int nvalid = p + 1 < W ? p + 1 : W;
+    double *phi = malloc(sizeof(double) * df);
+    double *z = malloc(sizeof(double) * df);
+    double *logit = malloc(sizeof(double) * (M + W));
+    double *yg = malloc(sizeof(double) * d);
+    double *yw = malloc(sizeof(double) * d);
+    for (int hk = 0; hk < Hkv; ++hk) {
+      const int64_t nh = (int64_t)n * Hkv + hk;
+      const double *kt = k + nh * d, *vt = v + nh * d, *gt = lg + nh * df;
+      double *S = state + nh * df * d;
+      feature_map(kt, wk + (int64_t)hk * w_stride, d, df, z, phi);
+      for (int f = 0; f < df; ++f) {
+        const double gam = exp(gt[f]);
+        for (int e = 0; e < d; ++e)
+          S[(int64_t)f * d + e] = gam * S[(int64_t)f * d + e] + phi[f] * vt[e];
+      }
+      memcpy(ring_k + (nh * W + slot) * d, kt, sizeof(double) * d);
+      memcpy(ring_v + (nh * W + slot) * d, vt, sizeof(double) * d);
+    }
+    for (int hq = 0; hq < Hq; ++hq) {
+      const int hk = hq / G;
+      const int64_t nh = (int64_t)n * Hkv + hk;
+      const double *qt = q + ((int64_t)n * Hq + hq) * d;
+      const double *S = state + nh * df * d;
+      feature_map(qt, wq + (int64_t)hq * w_stride, d, df, z, phi);
+      for (int e = 0; e < d; ++e) yg[e] = 0.0;
+      for (int f = 0; f < df; ++f)
+        for (int e = 0; e < d; ++e) yg[e] += phi[f] * S[(int64_t)f * d + e];
+      int cnt = 0;
+      double mx = -INFINITY;
+      for (int m = 0; m < M; ++m, ++cnt) {
+        logit[cnt] = scale * dot(qt, tk + ((int64_t)hk * M + m) * d, d);
+        if (logit[cnt] > mx) mx = logit[cnt];
+      }
+      for (int a = 0; a < nvalid; ++a, ++cnt) {
+        const int s = (p - a) % W;
+        logit[cnt] = scale * dot(qt, ring_k + (nh * W + s) * d, d);
+        if (logit[cnt] > mx) mx = logit[cnt];
+      }
+      double zsum = 0.0;
+      for (int a = 0; a < cnt; ++a) {
+        logit[a] = exp(logit[a] - mx);
+        zsum += logit[a];
+      }
+      for (int e = 0; e < d; ++e) yw[e] = 0.0;
+      cnt = 0;
+      for (int m = 0; m < M; ++m, ++cnt)
+        for (int e = 0; e < d; ++e)
+          yw[e] += logit[cnt] * tv[((int64_t)hk * M + m) * d + e];
+      for (int a = 0; a < nvalid; ++a, ++cnt) {
+        const int s = (p - a) % W;
+        for (int e = 0; e < d; ++e)
+          yw[e] += logit[cnt] * ring_v[(nh * W + s) * d + e];
+      }
+      const int64_t o = ((int64_t)n * Hq + hq) * d;
+      for (int e = 0; e < d; ++e) {
+        yw[e] /= zsum;
+        out[o + e] = mix * yg[e] + (1.0 - mix) * yw[e];
+        if (y_gla) y_gla[o + e] = yg[e];
+        if (y_win) y_win[o + e] = yw[e];
+      }
+    }
+    pos[n] = p + 1;
+    free(phi); free(z); free(logit); free(yg); free(yw);
+  }
+  return 0;
+}
+
+/* Threads the OpenMP runtime will use (reported by the CPU baseline). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  extern int omp_get_max_threads(void);
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

@@ -1,0 +1,94 @@
+"""The pins must catch plausible mistakes: build mutated copies of the oracle's
+C source (on the CPU, in a temp dir), point the oracle binding at each, and
+check that at least one pin fails for every mutant."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import tests.test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "lizard_oracle.c")
+
+# (name, original text, mutated text)
+MUTANTS = [
+    ("gate after add",
+     "row[e] = gam * row[e] + phk[f] * vi[e];",
+     "row[e] = gam * (row[e] + phk[f] * vi[e]);"),
+    ("gate of previous token",
+     "const double gam = exp(gi[f]);",
+     "const double gam = exp(i > 0 ? gi[f - df] : gi[f]);"),
+    ("readout with phi_k",
+     "for (int e = 0; e < d; ++e) yg[e] += phq[f] * row[e];",
+     "for (int e = 0; e < d; ++e) yg[e] += phk[f] * row[e];"),
+    ("window one key too many",
+     "const int lo = i - W + 1 > 0 ? i - W + 1 : 0;",
+     "const int lo = i - W > 0 ? i - W : 0;"),
+    ("window excludes current token",
+     "for (int j = lo; j <= i; ++j) {\n        logit[n]",
+     "for (int j = lo; j < i; ++j) {\n        logit[n]"),
+    ("no softmax scale",
+     "logit[n] = scale * dot(qi, kh + (int64_t)j * d, d);",
+     "logit[n] = dot(qi, kh + (int64_t)j * d, d);"),
+    ("meta tokens dropped from normaliser",
+     "zsum += logit[a];\n      }\n      for (int e = 0; e < d; ++e) yw[e] = 0.0;\n      n = 0;",
+     "if (a >= M) zsum += logit[a];\n      }\n      for (int e = 0; e < d; ++e) yw[e] = 0.0;\n      n = 0;"),
+    ("merge weights swapped",
+     "y[o + e] = mix * yg[e] + (1.0 - mix) * yw[e];",
+     "y[o + e] = (1.0 - mix) * yg[e] + mix * yw[e];"),
+    ("feature map normalised wrongly",
+     "for (int f = 0; f < df; ++f) phi[f] /= sum;",
+     "for (int f = 0; f < df; ++f) phi[f] /= (sum + 1.0);"),
+    ("gqa maps heads round-robin",
+     "const int b = bh / Hq, hq = bh % Hq, hk = hq / G;",
+     "const int b = bh / Hq, hq = bh % Hq, hk = hq % Hkv;"),
+    ("decode writes the slot after pos",
+     "const int slot = p % W;",
+     "const int slot = (p + 1) % W;"),
+    ("decode decays after adding",
+     "S[(int64_t)f * d + e] = gam * S[(int64_t)f * d + e] + phi[f] * vt[e];",
+     "S[(int64_t)f * d + e] = gam * (S[(int64_t)f * d + e] + phi[f] * vt[e]);"),
+    ("decode window one slot short",
+     "const int nvalid = p + 1 < W ? p + 1 : W;",
+     "const int nvalid = p + 1 < W ? p + 1 : W - 1;"),
+]
+
+PIN_FUNCS = [
+    pins.test_hand_worked_example,
+    pins.test_gamma_one_is_causal_linear_attention,
+    pins.test_gamma_zero_keeps_only_current_token,
+    pins.test_per_dim_gate_brute_force_products,
+    pins.test_window_covering_sequence_is_causal_softmax_attention,
+    lambda: pins.test_window_with_meta_tokens_matches_masked_sdpa(3, 4),
+    pins.test_mix_isolates_branches,
+    pins.test_gqa_equals_repeated_heads,
+    pins.test_decode_from_empty_equals_forward,
+    pins.test_decode_window_reads_ring_by_position,
+]
+
+
+@pytest.mark.parametrize("name,orig,mut", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(name, orig, mut, tmp_path, monkeypatch):
+    src = open(SRC).read()
+    assert src.count(orig) >= 1, f"mutation anchor for {name!r} not found"
+    msrc = src.replace(orig, mut, 1)
+    cpath = tmp_path / "mut.c"
+    cpath.write_text(msrc)
+    so = tmp_path / "libmut.so"
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-std=c99", str(cpath),
+                    "-o", str(so), "-lm"], check=True)
+    real = oracle._load()
+    lib = ctypes.CDLL(str(so))
+    for fn in ("oracle_lizard_fwd", "oracle_lizard_decode", "oracle_num_threads"):
+        getattr(lib, fn).argtypes = getattr(real, fn).argtypes
+        getattr(lib, fn).restype = getattr(real, fn).restype
+    monkeypatch.setattr(oracle, "_lib", lib)
+    failures = 0
+    for fn in PIN_FUNCS:
+        try:
+            fn()
+        except AssertionError:
+            failures += 1
+    assert failures > 0, f"no pin caught mutant {name!r}"
