@@ -1,0 +1,141 @@
+/*
+ * lizard_attn.h -- C ABI of liblizard_attn.so: Lizard attention on AMD
+ * MI355X (gfx950), forward over whole sequences and a one-token decode step.
+ *
+ * What is computed (for every batch entry b and query head h, with key/value
+ * head hk = h / (Hq/Hkv)):
+ *
+ *   phi_q(x) = softmax over features of (x . W_phi_q[h])   (likewise phi_k
+ *   with W_phi_k[hk]); softmax over the d features, max subtracted.
+ *
+ *   Global branch -- gated linear attention.  With the per-key-dimension gate
+ *   gamma_i = exp(log_gamma_i) (d values per token, one per row of the d x d
+ *   state):
+ *       S_i = diag(gamma_i) S_{i-1} + phi_k(k_i) v_i^T,    S_{-1} = 0
+ *       y_gla_i = phi_q(q_i)^T S_i
+ *   ("Lizard: An Efficient Linearization Framework for Large Language
+ *   Models", papernotes.org summary, section "key designs", Gated Linear
+ *   Attention item; the arXiv page's Method section explains why the gate is
+ *   handled in log space.)
+ *
+ *   Local branch -- anchor window attention.  One softmax over the M
+ *   meta-memory keys and the W most recent keys (token i included):
+ *       y_win_i = softmax([scale q_i.T_k[hk,m] ; scale q_i.k_j]) . [T_v ; v_j],
+ *       m < M, max(0, i-W+1) <= j <= i
+ *   (same summary, "key designs", Anchor Window Attention item.)
+ *
+ *   Output: y_i = mix * y_gla_i + (1 - mix) * y_win_i (same summary, "overall
+ *   framework": the two branch outputs are combined with weights).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor arguments are DEVICE pointers to contiguous row-major
+ *     arrays, 16-byte aligned, in the element type given by `dtype`
+ *     (except where a type is spelled out).  The caller owns every buffer.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work on it and return; nothing synchronises the host unless the
+ *     environment variable LIZARD_DEBUG_SYNC=1 is set.
+ *   - The library allocates no device memory.  Scratch space comes from the
+ *     caller's `workspace` argument.
+ *   - Errors are reported only through the return value.  On any status other
+ *     than LIZARD_OK nothing has been launched and no output was written
+ *     (LIZARD_ERR_HIP: a launch or HIP call failed; work enqueued before the
+ *     failure may have run).  lizard_last_error() returns a thread-local text
+ *     with the detail.  Device-side faults surface at the caller's next
+ *     synchronisation as HIP errors.
+ *   - Preconditions not checked on the device: inputs are finite;
+ *     log_gamma <= 0 (gamma in (0,1]; use a large finite negative value such
+ *     as -1e4 for gamma = 0, never -inf); outputs do not alias inputs.
+ *   - Supported head dimensions: d = 64 or 128 for bf16, d = 64 for fp32.
+ *     The feature dimension equals d.  Meta tokens: 0 <= M <= 16.
+ */
+#ifndef LIZARD_ATTN_H
+#define LIZARD_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LIZARD_OK = 0,
+  LIZARD_ERR_INVALID_ARG = 1, /* null pointer, bad size, misaligned pointer */
+  LIZARD_ERR_UNSUPPORTED = 2, /* valid request this build has no kernel for  */
+  LIZARD_ERR_WORKSPACE = 3,   /* workspace missing or too small              */
+  LIZARD_ERR_HIP = 4          /* a HIP runtime call or a launch failed       */
+} lizard_status;
+
+typedef enum { LIZARD_F32 = 0, LIZARD_BF16 = 1 } lizard_dtype;
+
+/*
+ * Forward over whole sequences.
+ *   q          [B, Hq, L, d]     queries
+ *   k, v       [B, Hkv, L, d]    keys, values
+ *   log_gamma  [B, Hkv, L, d]    log of the gate, one value per key dimension
+ *   w_phi_q    query-side feature-map weights [d, d] for head h at
+ *              w_phi_q + h * w_phi_head_stride elements (stride 0: one matrix
+ *              for every head); w_phi_k likewise, indexed by key/value head
+ *   t_k, t_v   [Hkv, M, d]       meta-memory keys / values (may be NULL if M = 0)
+ *   out        [B, Hq, L, d]     written
+ *   Hq must be a multiple of Hkv.  B = 0 or L = 0 is an empty problem: OK,
+ *   nothing launched.  `scale` multiplies the window logits (1/sqrt(d) gives
+ *   standard scaled dot-product attention).
+ *   workspace  device scratch of at least lizard_attn_fwd_workspace_bytes()
+ *              bytes for the same shapes (may be NULL when that is 0); its
+ *              contents on entry do not matter and are clobbered.
+ */
+lizard_status lizard_attn_fwd(const void *q, const void *k, const void *v,
+                              const void *log_gamma, const void *w_phi_q,
+                              const void *w_phi_k, int64_t w_phi_head_stride,
+                              const void *t_k, const void *t_v, void *out,
+                              int B, int Hq, int Hkv, int L, int d, int W,
+                              int M, float mix, float scale,
+                              lizard_dtype dtype, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* Workspace bytes lizard_attn_fwd needs for these shapes (0 if none). */
+size_t lizard_attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int L, int d,
+                                       int W, lizard_dtype dtype);
+
+/*
+ * One decode step: every sequence n takes one new token, in place.
+ *   state       [N, Hkv, d, d] float32 (always fp32), the S matrix of the
+ *               global branch; row f is key dimension f.  Updated.
+ *   win_k, win_v [N, Hkv, W, d] ring buffers of the last W keys / values; the
+ *               token with index t sits in slot t % W.  The new token is
+ *               written into slot pos[n] % W.  Updated.
+ *   pos         [N] int32: tokens already seen by sequence n (the index of the
+ *               new token); slots beyond pos[n] are ignored while
+ *               pos[n] + 1 < W.  Incremented by one.
+ *   q [N, Hq, d]; k, v, log_gamma [N, Hkv, d]; out [N, Hq, d] (written)
+ *   w_phi_q, w_phi_k, w_phi_head_stride, t_k, t_v, M, mix, scale: as in the
+ *   forward.  The per-token arithmetic is the forward's: decay, add, read out;
+ *   then a softmax over the M meta keys and the min(pos+1, W) newest keys.
+ *   Running L steps from a zero state, pos = 0, reproduces the forward on
+ *   those L tokens.
+ */
+lizard_status lizard_attn_decode(float *state, void *win_k, void *win_v,
+                                 int32_t *pos, const void *q, const void *k,
+                                 const void *v, const void *log_gamma,
+                                 const void *w_phi_q, const void *w_phi_k,
+                                 int64_t w_phi_head_stride, const void *t_k,
+                                 const void *t_v, void *out, int N, int Hq,
+                                 int Hkv, int d, int W, int M, float mix,
+                                 float scale, lizard_dtype dtype,
+                                 void *stream);
+
+/* Static text for a status code. */
+const char *lizard_status_string(lizard_status s);
+
+/* Thread-local detail of the last non-OK status returned on this thread. */
+const char *lizard_last_error(void);
+
+/* Library version string, e.g. "lizard_attn 0.1.0 gfx950". */
+const char *lizard_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIZARD_ATTN_H */

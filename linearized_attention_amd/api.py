@@ -1,0 +1,187 @@
+"""ctypes binding for liblizard_attn.so (see include/lizard_attn.h).
+
+Argument marshalling only: torch tensors are checked for device, dtype, shape
+and contiguity, their device pointers and the current HIP stream are passed to
+the C ABI, and non-OK statuses become exceptions.  Every step of the attention
+runs in the library's HIP kernels; there is no CPU path here.  torch provides
+device memory (outputs, workspace) and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+from . import build as _build
+
+LIB_PATH = _build.LIB
+
+LIZARD_OK = 0
+_STATUS = {0: "LIZARD_OK", 1: "LIZARD_ERR_INVALID_ARG", 2: "LIZARD_ERR_UNSUPPORTED",
+           3: "LIZARD_ERR_WORKSPACE", 4: "LIZARD_ERR_HIP"}
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+
+EXPORTED = ("lizard_attn_fwd", "lizard_attn_fwd_workspace_bytes", "lizard_attn_decode",
+            "lizard_status_string", "lizard_last_error", "lizard_version")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class LizardError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+def _declare(lib):
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.lizard_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp, vp, vp,
+                                    i32, i32, i32, i32, i32, i32, i32, f32, f32, i32, vp, sz, vp]
+    lib.lizard_attn_fwd.restype = i32
+    lib.lizard_attn_fwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.lizard_attn_fwd_workspace_bytes.restype = sz
+    lib.lizard_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp,
+                                       i32, i32, i32, i32, i32, i32, f32, f32, i32, vp]
+    lib.lizard_attn_decode.restype = i32
+    lib.lizard_status_string.argtypes = [i32]
+    lib.lizard_status_string.restype = ctypes.c_char_p
+    lib.lizard_last_error.argtypes = []
+    lib.lizard_last_error.restype = ctypes.c_char_p
+    lib.lizard_version.argtypes = []
+    lib.lizard_version.restype = ctypes.c_char_p
+    return lib
+
+
+def load(path: str | None = None):
+    """Load the HIP library (building it first only if no build exists)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            p = path or LIB_PATH
+            if not os.path.exists(p):
+                _build.build()
+            _lib = _declare(ctypes.CDLL(p))
+    return _lib
+
+
+def _check(status: int):
+    if status != LIZARD_OK:
+        lib = load()
+        raise LizardError(status, lib.lizard_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, name, dtype=None):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def lizard_attn_fwd_workspace_bytes(B: int, Hq: int, Hkv: int, L: int, d: int, W: int,
+                                    dtype: torch.dtype) -> int:
+    return int(load().lizard_attn_fwd_workspace_bytes(B, Hq, Hkv, L, d, W, _DTYPES[dtype]))
+
+
+def _w_stride(w_q, w_k, d):
+    if w_q.dim() == 2 and w_k.dim() == 2:
+        return 0
+    if w_q.dim() == 3 and w_k.dim() == 3:
+        return d * d
+    raise ValueError("w_phi_q and w_phi_k must both be [d,d] (shared) or both per head")
+
+
+def lizard_attn_fwd(q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v, *, W: int, M: int,
+                    mix: float = 0.5, scale: float | None = None, out=None, workspace=None,
+                    stream=None):
+    """Lizard attention forward on the GPU.  Shapes: q [B,Hq,L,d]; k, v, log_gamma
+    [B,Hkv,L,d]; w_phi_q/w_phi_k [d,d] or [Hq|Hkv,d,d]; t_k, t_v [Hkv,M,d].
+    Returns out [B,Hq,L,d] in the input dtype."""
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (log_gamma, "log_gamma"), (w_phi_q, "w_phi_q"),
+                 (w_phi_k, "w_phi_k")):
+        _dev(t, n, dt)
+    if M > 0:
+        _dev(t_k, "t_k", dt)
+        _dev(t_v, "t_v", dt)
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, L, d) or v.shape != k.shape or log_gamma.shape != k.shape:
+        raise ValueError("k, v, log_gamma must be [B,Hkv,L,d] matching q")
+    if M > 0 and (t_k.shape != (Hkv, M, d) or t_v.shape != (Hkv, M, d)):
+        raise ValueError("t_k, t_v must be [Hkv,M,d]")
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, "out", dt)
+    need = lizard_attn_fwd_workspace_bytes(B, Hq, Hkv, L, d, W, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().lizard_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), _ptr(w_phi_q), _ptr(w_phi_k),
+        _w_stride(w_phi_q, w_phi_k, d), _ptr(t_k) if M > 0 else None, _ptr(t_v) if M > 0 else None,
+        _ptr(out), B, Hq, Hkv, L, d, W, M, float(mix), float(scale), _DTYPES[dt],
+        _ptr(workspace), wbytes, _stream(stream)))
+    return out
+
+
+def lizard_attn_decode(state, win_k, win_v, pos, q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v,
+                       *, M: int, mix: float = 0.5, scale: float | None = None, out=None,
+                       stream=None):
+    """One decode step, in place on state [N,Hkv,d,d] fp32, win_k/win_v [N,Hkv,W,d],
+    pos [N] int32.  q [N,Hq,d]; k, v, log_gamma [N,Hkv,d].  Returns out [N,Hq,d]."""
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    _dev(state, "state", torch.float32)
+    _dev(pos, "pos", torch.int32)
+    for t, n in ((win_k, "win_k"), (win_v, "win_v"), (q, "q"), (k, "k"), (v, "v"),
+                 (log_gamma, "log_gamma"), (w_phi_q, "w_phi_q"), (w_phi_k, "w_phi_k")):
+        _dev(t, n, dt)
+    if M > 0:
+        _dev(t_k, "t_k", dt)
+        _dev(t_v, "t_v", dt)
+    N, Hq, d = q.shape
+    Hkv = k.shape[1]
+    W = win_k.shape[2]
+    if state.shape != (N, Hkv, d, d) or win_k.shape != (N, Hkv, W, d) or win_v.shape != win_k.shape:
+        raise ValueError("state [N,Hkv,d,d] and win_k/win_v [N,Hkv,W,d] expected")
+    if k.shape != (N, Hkv, d) or v.shape != k.shape or log_gamma.shape != k.shape or pos.shape != (N,):
+        raise ValueError("k, v, log_gamma must be [N,Hkv,d] and pos [N]")
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, "out", dt)
+    _check(load().lizard_attn_decode(
+        _ptr(state), _ptr(win_k), _ptr(win_v), _ptr(pos), _ptr(q), _ptr(k), _ptr(v),
+        _ptr(log_gamma), _ptr(w_phi_q), _ptr(w_phi_k), _w_stride(w_phi_q, w_phi_k, d),
+        _ptr(t_k) if M > 0 else None, _ptr(t_v) if M > 0 else None, _ptr(out),
+        N, Hq, Hkv, d, W, M, float(mix), float(scale), _DTYPES[dt], _stream(stream)))
+    return out
+
+
+def version() -> str:
+    return load().lizard_version().decode()

@@ -1,0 +1,194 @@
+// C-ABI entry points of liblizard_attn.so: argument validation, launch plan,
+// dispatch to the gfx950 kernels.  Declared and documented in
+// include/lizard_attn.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/lizard_attn.h"
+#include "internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+lizard_status fail(lizard_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool debug_sync() {
+  static const int v = [] {
+    const char *e = getenv("LIZARD_DEBUG_SYNC");
+    return (e && e[0] == '1') ? 1 : 0;
+  }();
+  return v != 0;
+}
+
+lizard_status finish(hipError_t e, hipStream_t stream) {
+  if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(LIZARD_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+  return LIZARD_OK;
+}
+
+bool supported_d(int d, lizard_dtype dt) { return dt == LIZARD_BF16 ? (d == 64 || d == 128) : d == 64; }
+
+constexpr int kChunk = 64;
+constexpr int kDV = 64;       // value columns per workgroup
+constexpr int kMaxMeta = 16;
+constexpr int kTargetBlocks = 256;
+
+struct FwdPlan {
+  int nchunks, nseg, cps, ndvb, nring;
+  size_t ws_state_bytes, ws_decay_bytes;
+};
+
+// Sequence segments are added until there are about 256 workgroups; an
+// environment override (LIZARD_FWD_SEGMENTS) exists for tests and tuning.
+FwdPlan make_plan(int B, int Hkv, int L, int d, int W) {
+  FwdPlan p{};
+  p.nchunks = (L + kChunk - 1) / kChunk;
+  p.ndvb = d / kDV;
+  const long base = (long)B * Hkv * p.ndvb;
+  long nseg = (kTargetBlocks + base - 1) / base;
+  if (const char *e = getenv("LIZARD_FWD_SEGMENTS")) {
+    const long v = atol(e);
+    if (v >= 1) nseg = v;
+  }
+  if (nseg > p.nchunks) nseg = p.nchunks;
+  if (nseg < 1) nseg = 1;
+  p.cps = (int)((p.nchunks + nseg - 1) / nseg);
+  p.nseg = (p.nchunks + p.cps - 1) / p.cps;
+  p.nring = (W - 1 <= kChunk) ? 2 : 3;
+  if (p.nseg > 1) {
+    p.ws_state_bytes = (size_t)B * Hkv * p.ndvb * (p.nseg - 1) * (size_t)d * kDV * sizeof(float);
+    p.ws_decay_bytes = (size_t)B * Hkv * (p.nseg - 1) * (size_t)d * sizeof(float);
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *lizard_status_string(lizard_status s) {
+  switch (s) {
+    case LIZARD_OK: return "ok";
+    case LIZARD_ERR_INVALID_ARG: return "invalid argument";
+    case LIZARD_ERR_UNSUPPORTED: return "unsupported configuration";
+    case LIZARD_ERR_WORKSPACE: return "workspace missing or too small";
+    case LIZARD_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char *lizard_last_error(void) { return g_err; }
+
+const char *lizard_version(void) { return "lizard_attn 0.1.0 gfx950"; }
+
+size_t lizard_attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int W, lizard_dtype dtype) {
+  (void)Hq;
+  (void)dtype;
+  if (B <= 0 || L <= 0 || Hkv <= 0 || d <= 0 || d % kDV != 0) return 0;
+  const FwdPlan p = make_plan(B, Hkv, L, d, W < 1 ? 1 : W);
+  return p.ws_state_bytes + p.ws_decay_bytes;
+}
+
+lizard_status lizard_attn_fwd(const void *q, const void *k, const void *v, const void *log_gamma,
+                              const void *w_phi_q, const void *w_phi_k, int64_t w_phi_head_stride,
+                              const void *t_k, const void *t_v, void *out, int B, int Hq, int Hkv, int L,
+                              int d, int W, int M, float mix, float scale, lizard_dtype dtype,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+  if (dtype != LIZARD_F32 && dtype != LIZARD_BF16) return fail(LIZARD_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (B < 0 || L < 0) return fail(LIZARD_ERR_INVALID_ARG, "B=%d and L=%d must be >= 0", B, L);
+  if (Hq < 1 || Hkv < 1 || d < 1 || W < 1 || M < 0)
+    return fail(LIZARD_ERR_INVALID_ARG, "need Hq, Hkv, d, W >= 1 and M >= 0 (got Hq=%d Hkv=%d d=%d W=%d M=%d)", Hq,
+                Hkv, d, W, M);
+  if (Hq % Hkv != 0) return fail(LIZARD_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (w_phi_head_stride < 0) return fail(LIZARD_ERR_INVALID_ARG, "negative w_phi_head_stride");
+  if (!supported_d(d, dtype))
+    return fail(LIZARD_ERR_UNSUPPORTED, "head dim d=%d not built for %s", d, dtype == LIZARD_BF16 ? "bf16" : "fp32");
+  if (M > kMaxMeta) return fail(LIZARD_ERR_UNSUPPORTED, "M=%d meta tokens (at most %d)", M, kMaxMeta);
+  if (w_phi_head_stride != 0 && w_phi_head_stride < (int64_t)d * d)
+    return fail(LIZARD_ERR_INVALID_ARG, "w_phi_head_stride=%lld overlaps matrices of d*d elements",
+                (long long)w_phi_head_stride);
+  if (B == 0 || L == 0) return LIZARD_OK;  // empty problem
+  if (!q || !k || !v || !log_gamma || !w_phi_q || !w_phi_k || !out)
+    return fail(LIZARD_ERR_INVALID_ARG, "null tensor pointer");
+  if (M > 0 && (!t_k || !t_v)) return fail(LIZARD_ERR_INVALID_ARG, "t_k/t_v null with M=%d", M);
+  const void *ptrs[] = {q, k, v, log_gamma, w_phi_q, w_phi_k, out, t_k, t_v};
+  for (const void *ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return fail(LIZARD_ERR_INVALID_ARG, "tensor pointer %p not 16-byte aligned", ptr);
+  if ((int64_t)B * Hq * L > (int64_t)1 << 40) return fail(LIZARD_ERR_INVALID_ARG, "problem too large");
+
+  const FwdPlan plan = make_plan(B, Hkv, L, d, W);
+  const size_t need = plan.ws_state_bytes + plan.ws_decay_bytes;
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(LIZARD_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(LIZARD_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+  }
+
+  lz::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.lg = log_gamma; p.wq = w_phi_q; p.wk = w_phi_k;
+  p.tk = t_k; p.tv = t_v; p.out = out;
+  p.ws_state = need ? static_cast<float *>(workspace) : nullptr;
+  p.ws_decay = need ? reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.ws_state_bytes) : nullptr;
+  p.w_stride = w_phi_head_stride;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.L = L; p.W = W; p.M = M; p.G = Hq / Hkv;
+  p.nchunks = plan.nchunks; p.nseg = plan.nseg; p.cps = plan.cps; p.ndvb = plan.ndvb; p.nring = plan.nring;
+  p.per_head_q = w_phi_head_stride != 0;
+  p.mix = mix; p.scale = scale;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return finish(lz::launch_fwd(p, dtype == LIZARD_BF16, d, st), st);
+}
+
+lizard_status lizard_attn_decode(float *state, void *win_k, void *win_v, int32_t *pos, const void *q, const void *k,
+                                 const void *v, const void *log_gamma, const void *w_phi_q, const void *w_phi_k,
+                                 int64_t w_phi_head_stride, const void *t_k, const void *t_v, void *out, int N, int Hq,
+                                 int Hkv, int d, int W, int M, float mix, float scale, lizard_dtype dtype,
+                                 void *stream) {
+  if (dtype != LIZARD_F32 && dtype != LIZARD_BF16) return fail(LIZARD_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (N < 0) return fail(LIZARD_ERR_INVALID_ARG, "N=%d must be >= 0", N);
+  if (Hq < 1 || Hkv < 1 || d < 1 || W < 1 || M < 0)
+    return fail(LIZARD_ERR_INVALID_ARG, "need Hq, Hkv, d, W >= 1 and M >= 0 (got Hq=%d Hkv=%d d=%d W=%d M=%d)", Hq,
+                Hkv, d, W, M);
+  if (Hq % Hkv != 0) return fail(LIZARD_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (w_phi_head_stride < 0) return fail(LIZARD_ERR_INVALID_ARG, "negative w_phi_head_stride");
+  if (!supported_d(d, dtype))
+    return fail(LIZARD_ERR_UNSUPPORTED, "head dim d=%d not built for %s", d, dtype == LIZARD_BF16 ? "bf16" : "fp32");
+  if (M > kMaxMeta) return fail(LIZARD_ERR_UNSUPPORTED, "M=%d meta tokens (at most %d)", M, kMaxMeta);
+  if (W > lz::decode_max_window())
+    return fail(LIZARD_ERR_UNSUPPORTED, "decode window W=%d (at most %d)", W, lz::decode_max_window());
+  if (w_phi_head_stride != 0 && w_phi_head_stride < (int64_t)d * d)
+    return fail(LIZARD_ERR_INVALID_ARG, "w_phi_head_stride=%lld overlaps matrices of d*d elements",
+                (long long)w_phi_head_stride);
+  if (N == 0) return LIZARD_OK;
+  if (!state || !win_k || !win_v || !pos || !q || !k || !v || !log_gamma || !w_phi_q || !w_phi_k || !out)
+    return fail(LIZARD_ERR_INVALID_ARG, "null tensor pointer");
+  if (M > 0 && (!t_k || !t_v)) return fail(LIZARD_ERR_INVALID_ARG, "t_k/t_v null with M=%d", M);
+  const void *ptrs[] = {state, win_k, win_v, q, k, v, log_gamma, w_phi_q, w_phi_k, out, t_k, t_v};
+  for (const void *ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return fail(LIZARD_ERR_INVALID_ARG, "tensor pointer %p not 16-byte aligned", ptr);
+  if (!aligned16(pos) && (reinterpret_cast<uintptr_t>(pos) & 3u))
+    return fail(LIZARD_ERR_INVALID_ARG, "pos not 4-byte aligned");
+
+  lz::DecParams p{};
+  p.state = state; p.win_k = win_k; p.win_v = win_v; p.pos = pos;
+  p.q = q; p.k = k; p.v = v; p.lg = log_gamma; p.wq = w_phi_q; p.wk = w_phi_k; p.tk = t_k; p.tv = t_v;
+  p.out = out; p.w_stride = w_phi_head_stride;
+  p.N = N; p.Hq = Hq; p.Hkv = Hkv; p.W = W; p.M = M; p.G = Hq / Hkv; p.mix = mix; p.scale = scale;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return finish(lz::launch_decode(p, dtype == LIZARD_BF16, d, st), st);
+}
+
+}  // extern "C"

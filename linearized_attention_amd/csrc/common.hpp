@@ -1,0 +1,147 @@
+// Device helpers shared by the Lizard attention kernels (gfx950 / CDNA4).
+//
+// MFMA conventions used throughout (16x16 output tiles, wave of 64 lanes,
+// lane = 16 * kq + r with r = lane % 16 and kq = lane / 16):
+//   * operand fragment for one K = 32 step: lane (r, kq) holds the 8 values
+//     k = 8*kq .. 8*kq+7 of row r (A operand: row m = r; B operand: column
+//     n = r).  bf16 uses one v_mfma_f32_16x16x32_bf16; fp32 issues eight
+//     v_mfma_f32_16x16x4_f32, call j pairing k-slot kq with k = 8*kq + j.
+//   * accumulator: lane (r, kq) holds D[4*kq + i][r], i = 0..3.
+// Both were checked on the hardware with an in-bounds probe.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lz {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { float v[8]; };
+
+__device__ __forceinline__ f32x4 mma(const Frag<bf16> &a, const Frag<bf16> &b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(const Frag<float> &a, const Frag<float> &b, f32x4 c) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], c, 0, 0, 0);
+  return c;
+}
+
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f(float x) { return x; }
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }  // RNE
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+
+template <typename T> __device__ __forceinline__ Frag<T> frag_zero() {
+  Frag<T> f;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f.v[j] = (bf16)0.0f;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f.v[j] = 0.0f;
+  }
+  return f;
+}
+
+// Fragment from 8 floats (rounded to T).
+template <typename T> __device__ __forceinline__ Frag<T> frag_from(const float (&x)[8]) {
+  Frag<T> f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f.v[j] = from_f<T>(x[j]);
+  return f;
+}
+
+// 8 contiguous elements (16-byte aligned for bf16, 32-byte for fp32).
+template <typename T> __device__ __forceinline__ Frag<T> load8(const T *p) {
+  Frag<T> f;
+  if constexpr (sizeof(T) == 2) {
+    f.v = *reinterpret_cast<const bf16x8 *>(p);
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { f.v[j] = a[j]; f.v[4 + j] = b[j]; }
+  }
+  return f;
+}
+
+// 4 contiguous elements at p0 (slots 0..3) and 4 at p1 (slots 4..7).
+template <typename T> __device__ __forceinline__ Frag<T> load4x2(const T *p0, const T *p1) {
+  Frag<T> f;
+  if constexpr (sizeof(T) == 2) {
+    const bf16x4 a = *reinterpret_cast<const bf16x4 *>(p0);
+    const bf16x4 b = *reinterpret_cast<const bf16x4 *>(p1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { f.v[j] = a[j]; f.v[4 + j] = b[j]; }
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(p0);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(p1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { f.v[j] = a[j]; f.v[4 + j] = b[j]; }
+  }
+  return f;
+}
+
+// 8 / 4 contiguous elements converted to float.
+template <typename T> __device__ __forceinline__ void load8f(const T *p, float (&x)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(p);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = (float)a[j];
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { x[j] = a[j]; x[4 + j] = b[j]; }
+  }
+}
+template <typename T> __device__ __forceinline__ void load4f(const T *p, float (&x)[4]) {
+  if constexpr (sizeof(T) == 2) {
+    const bf16x4 a = *reinterpret_cast<const bf16x4 *>(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = (float)a[j];
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = a[j];
+  }
+}
+
+// Store 4 floats as 4 contiguous T.
+template <typename T> __device__ __forceinline__ void store4(T *p, float a, float b, float c, float d) {
+  if constexpr (sizeof(T) == 2) {
+    bf16x4 v;
+    v[0] = (bf16)a; v[1] = (bf16)b; v[2] = (bf16)c; v[3] = (bf16)d;
+    *reinterpret_cast<bf16x4 *>(p) = v;
+  } else {
+    f32x4 v = {a, b, c, d};
+    *reinterpret_cast<f32x4 *>(p) = v;
+  }
+}
+
+__device__ __forceinline__ float wave_max_cols(float x) {
+  // max over the four lanes that share lane % 16
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float wave_sum_cols(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+__device__ __forceinline__ float wave_max_all(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+
+}  // namespace lz

@@ -1,0 +1,39 @@
+// Internal launch interface between the C-ABI host code and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lz {
+
+struct FwdParams {
+  const void *q, *k, *v, *lg, *wq, *wk, *tk, *tv;
+  void *out;
+  float *ws_state;  // per-segment end states, fp32, fragment order
+  float *ws_decay;  // per-segment sums of log gamma, [B][Hkv][nseg-1][d]
+  int64_t w_stride;
+  int B, Hq, Hkv, L, W, M, G;
+  int nchunks, nseg, cps, ndvb, nring, ngroups;
+  int per_head_q;
+  float mix, scale;
+};
+
+hipError_t launch_fwd(const FwdParams &p, int dtype_bf16, int d, hipStream_t stream);
+
+struct DecParams {
+  float *state;
+  void *win_k, *win_v;
+  int32_t *pos;
+  const void *q, *k, *v, *lg, *wq, *wk, *tk, *tv;
+  void *out;
+  int64_t w_stride;
+  int N, Hq, Hkv, W, M, G;
+  float mix, scale;
+};
+
+hipError_t launch_decode(const DecParams &p, int dtype_bf16, int d, hipStream_t stream);
+
+}  // namespace lz
+
+namespace lz {
+int decode_max_window();
+}

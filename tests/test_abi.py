@@ -1,0 +1,116 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and host-side validation returns the documented status codes
+without launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linearized_attention_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lizard_attn.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lizard_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared()
+    for n in api.EXPORTED:
+        assert n in names
+    assert set(names) == set(api.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(api.LIB_PATH) if os.path.exists(api.LIB_PATH) else api.load()
+    for n in _declared():
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_status_strings_and_version():
+    lib = api.load()
+    for code in range(5):
+        assert lib.lizard_status_string(code)
+    assert b"gfx950" in lib.lizard_version()
+
+
+def _fwd(lib, **kw):
+    a = dict(q=16, k=16, v=16, lg=16, wq=16, wk=16, stride=0, tk=16, tv=16, out=16, B=1, Hq=2, Hkv=2,
+             L=64, d=128, W=64, M=4, mix=0.5, scale=0.1, dtype=1, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.lizard_attn_fwd(P(a["q"]), P(a["k"]), P(a["v"]), P(a["lg"]), P(a["wq"]), P(a["wk"]),
+                               a["stride"], P(a["tk"]), P(a["tv"]), P(a["out"]), a["B"], a["Hq"],
+                               a["Hkv"], a["L"], a["d"], a["W"], a["M"], a["mix"], a["scale"],
+                               a["dtype"], P(a["ws"]), a["wsb"], P(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(out=None), 1), (dict(Hq=3, Hkv=2), 1), (dict(Hkv=0), 1),
+    (dict(W=0), 1), (dict(M=-1), 1), (dict(L=-5), 1), (dict(dtype=7), 1),
+    (dict(q=24), 1),                       # misaligned
+    (dict(stride=-1), 1), (dict(stride=100), 1),
+    (dict(d=96), 2), (dict(d=128, dtype=0), 2), (dict(M=17), 2),
+    (dict(tk=None), 1),
+])
+def test_fwd_validation_codes(kw, code):
+    lib = api.load()
+    assert _fwd(lib, **kw) == code
+    assert lib.lizard_last_error()
+
+
+def test_fwd_empty_problem_is_ok_without_launch():
+    lib = api.load()
+    assert _fwd(lib, B=0) == 0
+    assert _fwd(lib, L=0) == 0
+    assert _fwd(lib, B=0, q=None, k=None) == 0
+
+
+def test_fwd_workspace_required_when_segmented():
+    lib = api.load()
+    need = lib.lizard_attn_fwd_workspace_bytes(1, 32, 32, 32768, 128, 128, 1)
+    assert need > 0
+    assert _fwd(lib, B=1, Hq=32, Hkv=32, L=32768, ws=None) == 3
+    assert _fwd(lib, B=1, Hq=32, Hkv=32, L=32768, ws=4096, wsb=need - 1) == 3
+    # one chunk: nothing to split, no workspace
+    assert lib.lizard_attn_fwd_workspace_bytes(1, 2, 2, 64, 128, 64, 1) == 0
+
+
+def test_workspace_bytes_matches_plan_formula():
+    lib = api.load()
+    # B*Hkv*ndvb = 64 groups -> 4 segments of 512/4 = 128 chunks each
+    B, Hkv, L, d = 1, 32, 32768, 128
+    got = lib.lizard_attn_fwd_workspace_bytes(B, Hkv, Hkv, L, d, 128, 1)
+    nseg = 4
+    want = B * Hkv * 2 * (nseg - 1) * d * 64 * 4 + B * Hkv * (nseg - 1) * d * 4
+    assert got == want
+
+
+def _dec(lib, **kw):
+    a = dict(state=16, wk=16, wv=16, pos=16, q=16, k=16, v=16, lg=16, wq=16, wkm=16, stride=0, tk=16,
+             tv=16, out=16, N=4, Hq=2, Hkv=2, d=128, W=64, M=4, mix=0.5, scale=0.1, dtype=1, stream=None)
+    a.update(kw)
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.lizard_attn_decode(P(a["state"]), P(a["wk"]), P(a["wv"]), P(a["pos"]), P(a["q"]),
+                                  P(a["k"]), P(a["v"]), P(a["lg"]), P(a["wq"]), P(a["wkm"]),
+                                  a["stride"], P(a["tk"]), P(a["tv"]), P(a["out"]), a["N"], a["Hq"],
+                                  a["Hkv"], a["d"], a["W"], a["M"], a["mix"], a["scale"], a["dtype"],
+                                  P(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(state=None), 1), (dict(pos=None), 1), (dict(Hq=3), 1), (dict(W=0), 1), (dict(N=-1), 1),
+    (dict(d=32), 2), (dict(W=257), 2), (dict(M=20), 2), (dict(q=8), 1),
+])
+def test_decode_validation_codes(kw, code):
+    lib = api.load()
+    assert _dec(lib, **kw) == code
+
+
+def test_decode_empty_is_ok():
+    assert _dec(api.load(), N=0) == 0

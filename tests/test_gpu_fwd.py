@@ -1,0 +1,145 @@
+"""Parity of the HIP forward kernel with the fp64 oracle.
+
+Relative L2 error per (batch, head) over L x d, for the merged output and for
+each branch on its own (mix = 1 isolates the gated-linear-attention branch,
+mix = 0 the window branch): <= 1e-4 for fp32 inputs, <= 2e-2 for bf16.
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linearized_attention_amd import api
+from linearized_attention_amd.synthetic import make_fwd_inputs, workload_fwd_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def rel_l2_per_head(got, want):
+    num = np.sqrt(((got - want) ** 2).sum(axis=(-2, -1)))
+    den = np.sqrt((want ** 2).sum(axis=(-2, -1)))
+    return num / np.maximum(den, 1e-300)
+
+
+def gpu_fwd(inp, mix, dev=None):
+    g = dev if dev is not None else inp.to("cuda")
+    out = api.lizard_attn_fwd(g.q, g.k, g.v, g.log_gamma, g.w_phi_q, g.w_phi_k, g.t_k, g.t_v,
+                              W=inp.W, M=inp.M, mix=mix, scale=inp.scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def check_case(label, inp, dtype):
+    _say(f"[fwd] {label}: B={inp.q.shape[0]} Hq={inp.q.shape[1]} Hkv={inp.k.shape[1]} "
+         f"L={inp.q.shape[2]} d={inp.q.shape[3]} W={inp.W} M={inp.M} {dtype}")
+    y, yg, yw = oracle.lizard_fwd(*inp.tensors(), W=inp.W, M=inp.M, mix=inp.mix, scale=inp.scale,
+                                  return_branches=True)
+    dev = inp.to("cuda")
+    worst = {}
+    for mix, want, name in ((inp.mix, y, "merged"), (1.0, yg, "gla"), (0.0, yw, "window")):
+        got = gpu_fwd(inp, mix, dev).double().cpu().numpy()
+        assert np.isfinite(got).all(), f"{label}/{name}: non-finite output"
+        err = rel_l2_per_head(got, want)
+        worst[name] = float(err.max())
+    _say(f"      rel-L2 max per head: {worst}")
+    for name, e in worst.items():
+        assert e <= TOL[dtype], f"{label}/{name}: rel L2 {e:.3e} > {TOL[dtype]}"
+    return worst
+
+
+SMALL = [
+    ("workload0 fp32 d64 L256", None, "f32"),
+    ("bf16 d128 ragged L200", dict(B=2, Hq=2, Hkv=2, L=200, d=128, W=64, M=4), "bf16"),
+    ("bf16 d64 L130", dict(B=1, Hq=3, Hkv=3, L=130, d=64, W=64, M=4), "bf16"),
+    ("fp32 d64 ragged L150 W20 M3", dict(B=2, Hq=1, Hkv=1, L=150, d=64, W=20, M=3), "f32"),
+    ("bf16 uniform gate W128 M8", dict(B=1, Hq=2, Hkv=2, L=256, d=128, W=128, M=8, gate="uniform"), "bf16"),
+    ("fp32 uniform gate -8 (mixed safe/exact diag)", dict(B=1, Hq=2, Hkv=2, L=192, d=64, W=64, M=4,
+                                                          gate="uniform:-8"), "f32"),
+    ("bf16 gamma=0 (exact diag)", dict(B=1, Hq=2, Hkv=2, L=130, d=128, W=64, M=4, gate="zero"), "bf16"),
+    ("fp32 gamma=0 (exact diag)", dict(B=1, Hq=2, Hkv=2, L=100, d=64, W=64, M=4, gate="zero"), "f32"),
+    ("bf16 gamma=1", dict(B=1, Hq=2, Hkv=2, L=256, d=128, W=64, M=4, gate="one"), "bf16"),
+    ("fp32 gamma=1", dict(B=1, Hq=1, Hkv=1, L=256, d=64, W=64, M=4, gate="one"), "f32"),
+    ("bf16 W>=L M0 (full causal softmax)", dict(B=1, Hq=2, Hkv=2, L=300, d=128, W=300, M=0), "bf16"),
+    ("fp32 W>=L M0", dict(B=1, Hq=1, Hkv=1, L=257, d=64, W=1000, M=0), "f32"),
+    ("fp32 W1 M0", dict(B=1, Hq=2, Hkv=2, L=70, d=64, W=1, M=0), "f32"),
+    ("fp32 W65 M16", dict(B=1, Hq=1, Hkv=1, L=200, d=64, W=65, M=16), "f32"),
+    ("fp32 W66 (3-chunk ring)", dict(B=1, Hq=1, Hkv=1, L=200, d=64, W=66, M=1), "f32"),
+    ("fp32 L1", dict(B=2, Hq=2, Hkv=2, L=1, d=64, W=64, M=4), "f32"),
+    ("fp32 L17", dict(B=1, Hq=2, Hkv=2, L=17, d=64, W=8, M=2), "f32"),
+    ("fp32 L64", dict(B=1, Hq=2, Hkv=2, L=64, d=64, W=64, M=4), "f32"),
+    ("fp32 L65", dict(B=1, Hq=2, Hkv=2, L=65, d=64, W=64, M=4), "f32"),
+    ("bf16 gqa 4:2 shared W", dict(B=2, Hq=4, Hkv=2, L=150, d=128, W=64, M=4), "bf16"),
+    ("fp32 gqa 6:2 per-head W", dict(B=1, Hq=6, Hkv=2, L=140, d=64, W=32, M=4, per_head_w=True,
+                                     separate_wk=True), "f32"),
+    ("bf16 per-head W G1", dict(B=1, Hq=2, Hkv=2, L=100, d=128, W=64, M=4, per_head_w=True,
+                                separate_wk=True), "bf16"),
+]
+
+
+@pytest.mark.parametrize("label,kw,dtype", SMALL, ids=[s[0] for s in SMALL])
+def test_fwd_matches_oracle(gpu_lib, label, kw, dtype):
+    if kw is None:
+        inp = workload_fwd_inputs(0)
+    else:
+        inp = make_fwd_inputs(dtype=dtype, seed=zlib.crc32(label.encode()) % 10000, **kw)
+    check_case(label, inp, dtype)
+
+
+@pytest.mark.parametrize("nseg", [2, 3, 5])
+def test_fwd_sequence_segments(gpu_lib, monkeypatch, nseg):
+    """Segments joined through the workspace states give the same answer."""
+    monkeypatch.setenv("LIZARD_FWD_SEGMENTS", str(nseg))
+    inp = make_fwd_inputs(B=1, Hq=2, Hkv=2, L=330, d=64, W=70, M=4, dtype="f32", seed=31,
+                          gate="uniform:-1")
+    check_case(f"fp32 {nseg} segments", inp, "f32")
+    inp = make_fwd_inputs(B=1, Hq=4, Hkv=2, L=300, d=128, W=64, M=4, dtype="bf16", seed=32)
+    check_case(f"bf16 gqa {nseg} segments", inp, "bf16")
+
+
+def _sampled_check(index, heads, label):
+    inp = workload_fwd_inputs(index)
+    dtype = "bf16"
+    _say(f"[fwd] {label}: full size, shapes q{tuple(inp.q.shape)} k{tuple(inp.k.shape)}")
+    dev = inp.to("cuda")
+    outs = {}
+    for mix in (inp.mix, 1.0, 0.0):
+        outs[mix] = gpu_fwd(inp, mix, dev).cpu()
+    G = inp.q.shape[1] // inp.k.shape[1]
+    for (b, h) in heads:
+        hk = h // G
+        sl = lambda t, hh: t[b:b + 1, hh:hh + 1]
+        y, yg, yw = oracle.lizard_fwd(sl(inp.q, h), sl(inp.k, hk), sl(inp.v, hk), sl(inp.log_gamma, hk),
+                                      inp.w_phi_q, inp.w_phi_k, inp.t_k[hk:hk + 1], inp.t_v[hk:hk + 1],
+                                      W=inp.W, M=inp.M, mix=inp.mix, scale=inp.scale, return_branches=True)
+        for mix, want, name in ((inp.mix, y, "merged"), (1.0, yg, "gla"), (0.0, yw, "window")):
+            got = outs[mix][b:b + 1, h:h + 1].double().numpy()
+            e = float(rel_l2_per_head(got, want).max())
+            _say(f"      (b={b}, h={h}) {name}: rel-L2 {e:.3e}")
+            assert e <= TOL[dtype], f"{label} (b={b},h={h}) {name}: {e:.3e}"
+    return outs
+
+
+def test_fwd_workload1_full_size_sampled_heads(gpu_lib):
+    outs = _sampled_check(1, [(0, 0), (3, 31), (2, 17)], "llama3-8b layer")
+    # run-to-run determinism at full size (no atomics in the forward)
+    inp = workload_fwd_inputs(1)
+    again = gpu_fwd(inp, inp.mix).cpu()
+    assert torch.equal(again, outs[inp.mix]), "forward is not bitwise reproducible"
+
+
+def test_fwd_workload2_full_size_sampled_heads(gpu_lib):
+    _sampled_check(2, [(0, 5), (0, 30)], "32K stress")
+
+
+def test_fwd_workload4_full_size_sampled_heads(gpu_lib):
+    _sampled_check(4, [(0, 0), (1, 13), (1, 31)], "gqa 32/8")
