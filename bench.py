@@ -1,0 +1,256 @@
+"""Benchmark: Lizard attention forward on one MI355X (plus the decode step).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one forward pass (feature maps, chunk-local gate sums, intra- and
+inter-chunk products, state scan, anchor window, merge) over the
+Llama-3-8B-shaped layer: B=4, H=32, L=4096, d=128, W=64, M=4, bf16 inputs with
+fp32 accumulation, seeded synthetic data.  Inputs are resident in HBM before
+the timed region.  The JSON line also carries the decode step (N=256
+sequences, H=32, d=128, fp32 state, W=64, M=4; 128 consecutive steps) with its
+own HBM roofline, and the fp64 oracle timed on the host cores on a bounded
+sample of the forward workload.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from linearized_attention_amd import api  # noqa: E402
+from linearized_attention_amd.synthetic import (WORKLOADS, WORKLOAD_NAMES,  # noqa: E402
+                                                workload_decode_inputs, workload_fwd_inputs)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_kernel_workload1.json")
+KERNEL_SOURCES = ["linearized_attention_amd/csrc/fwd.hip", "linearized_attention_amd/csrc/common.hpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def fwd_algorithmic(c) -> tuple[float, float]:
+    """Algorithmic bytes and flops of one forward over workload c.
+
+    Bytes: q, k, v, log gamma read once and out written once (per-KV tensors
+    counted once); weights and meta tokens are negligible.  Flops per query
+    token-head: feature maps 4 d d_f (key side counted per query head here,
+    as in the layer without grouping), intra-chunk (C+1)(d_f+d_v), inter-chunk
+    read-out 2 d_f d_v, state update 2 d_f d_v, window 2 (M + W) (d + d_v)."""
+    B, Hq, Hkv, L, d, W, M = c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], c["W"], c["M"]
+    e = 2 if c["dtype"] == "bf16" else 4
+    nbytes = e * d * (2 * B * Hq * L + 3 * B * Hkv * L)
+    C = 64
+    per = 4 * d * d + (C + 1) * (2 * d) + 2 * d * d + 2 * d * d + 2 * (M + W) * (2 * d)
+    return float(nbytes), float(per) * B * Hq * L
+
+
+def decode_bytes_per_step(c) -> float:
+    """HBM bytes of one decode step: fp32 state read+written, ring K/V read,
+    the new k/v written into the ring, q/k/v/log gamma read and out written."""
+    N, Hq, Hkv, d, W = c["N"], c["Hq"], c["Hkv"], c["d"], c["W"]
+    e = 2
+    per_kv = 2 * d * d * 4 + 2 * W * d * e + 2 * d * e + 3 * d * e
+    per_q = 2 * d * e
+    return float(N * (Hkv * per_kv + Hq * per_q))
+
+
+def time_launches(fn, steps: int):
+    """Time `steps` calls of fn on the current stream with HIP events: per-launch
+    durations and the bracketed total."""
+    st = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(st)
+    for a, b in evs:
+        a.record(st)
+        fn()
+        b.record(st)
+    t_end.record(st)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in evs]
+    return t_start.elapsed_time(t_end), per
+
+
+def bench_forward(steps: int, warmup: int):
+    c = WORKLOADS[1]
+    log("[bench] generating forward workload:", WORKLOAD_NAMES[1])
+    inp = workload_fwd_inputs(1)
+    g = inp.to("cuda")
+    out = torch.empty_like(g.q)
+    need = api.lizard_attn_fwd_workspace_bytes(c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], c["W"], g.q.dtype)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+
+    def step():
+        api.lizard_attn_fwd(g.q, g.k, g.v, g.log_gamma, g.w_phi_q, g.w_phi_k, g.t_k, g.t_v, W=inp.W,
+                            M=inp.M, mix=inp.mix, scale=inp.scale, out=out, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] forward: {warmup} warmup done, timing {steps} steps")
+    total_ms, per = time_launches(step, steps)
+    return c, inp, total_ms, per
+
+
+def bench_decode(steps: int, warmup: int):
+    c = WORKLOADS[3]
+    log("[bench] generating decode workload:", WORKLOAD_NAMES[3])
+    dec = workload_decode_inputs(3, steps=steps)
+    st = dec.state.cuda()
+    rk, rv, pos = dec.ring_k.cuda(), dec.ring_v.cuda(), dec.pos.cuda()
+    w = [t.cuda() for t in (dec.w_phi_q, dec.w_phi_k, dec.t_k, dec.t_v)]
+    xs = [tuple(t.cuda() for t in s) for s in dec.steps]
+    out = torch.empty_like(xs[0][0])
+    it = [0]
+
+    def step():
+        q, k, v, lg = xs[it[0] % len(xs)]
+        it[0] += 1
+        api.lizard_attn_decode(st, rk, rv, pos, q, k, v, lg, *w, M=dec.M, mix=dec.mix, scale=dec.scale,
+                               out=out)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    it[0] = 0
+    log(f"[bench] decode: timing {steps} consecutive steps")
+    total_ms, per = time_launches(step, steps)
+    return c, total_ms, per
+
+
+def cpu_baseline():
+    """The fp64 oracle on the host cores over the whole forward workload (128
+    heads x 4096 tokens; about 20 thread-seconds of fp64 work)."""
+    import oracle
+    c = WORKLOADS[1]
+    inp = workload_fwd_inputs(1)
+    threads = oracle.num_threads()
+    heads = c["B"] * c["Hq"]
+    log(f"[bench] cpu baseline: oracle on the full forward workload ({heads} heads x {c['L']} tokens), "
+        f"{threads} threads")
+    t0 = time.perf_counter()
+    oracle.lizard_fwd(*inp.tensors(), W=inp.W, M=inp.M, mix=inp.mix, scale=inp.scale)
+    dt = time.perf_counter() - t0
+    tokens = c["B"] * c["L"]
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": min(threads, heads), "kind": "oracle",
+            "sample": f"the whole forward workload ({c['B']} x {c['Hq']} heads x {c['L']} tokens), fp64, "
+                      f"{dt:.2f} s wall"}
+
+
+def load_traffic(launch_bytes: float):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="one forward plus a plain copy of known size, for rocprofv3 counter passes")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the forward shards by batch/head with no exchange; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    api.load()
+
+    if args.pmc_run:
+        c, inp, _, _ = bench_forward(1, 1)
+        nbytes = 1 << 30
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] pmc run: one forward, then a copy of {nbytes} bytes read + {nbytes} bytes written")
+        return
+
+    c, inp, total_ms, per = bench_forward(args.steps, args.warmup)
+    ms_per_step = total_ms / args.steps
+    tokens = c["B"] * c["L"]
+    value = tokens / (ms_per_step * 1e-3)
+    nbytes, flops = fwd_algorithmic(c)
+    kern_ms = sum(per) / len(per)
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    mfma_tflops = flops / (kern_ms * 1e-3) / 1e12
+    traffic = load_traffic(nbytes)
+    result = {
+        "metric": "Lizard-attn fwd tokens/sec at L=4096,H=32,d=128; % MFMA peak; decode % HBM BW",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[1], "B": c["B"], "H": c["Hq"], "L": c["L"], "d": c["d"],
+                   "W": c["W"], "M": c["M"], "chunk": 64, "accumulation": "fp32"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "fwd_kernel<bf16,128,64,2,false>", "kernel_ms": kern_ms,
+                     "algorithmic_bytes_per_launch": nbytes},
+        "mfma": {"algorithmic_flops_per_launch": flops, "achieved_tflops": mfma_tflops,
+                 "peak_tflops": BF16_PEAK_TFLOPS, "frac": mfma_tflops / BF16_PEAK_TFLOPS},
+    }
+    del inp
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        dc, dtot, dper = bench_decode(args.decode_steps, 4)
+        dbytes = decode_bytes_per_step(dc)
+        dms = sum(dper) / len(dper)
+        dach = dbytes / (dms * 1e-3) / 1e9
+        result["decode"] = {
+            "workload": WORKLOAD_NAMES[3], "steps": args.decode_steps,
+            "ms_per_step": dtot / args.decode_steps,
+            "tokens_per_s": dc["N"] / (dtot / args.decode_steps * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": dach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": dach / HBM_PEAK_GBS, "bytes_per_step": dbytes, "step_ms": dms},
+        }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
