@@ -13,19 +13,24 @@
 // The arXiv page's Method section observes that the cumulative gate product
 // underflows in low precision and moves it into log space so the work becomes
 // dense matrix products; this kernel keeps that idea but not the page's
-// formulation.  Per 64-token chunk the log gate is summed inside the chunk only
-// (chunk-local, fp32), and every exponential that multiplies an MFMA operand is
-// taken relative to a reference point inside the chunk so that it is <= 1:
+// formulation.  The log gate is summed inside each 16-token sub-chunk only, in
+// fp32, and every exponential that multiplies an MFMA operand is taken relative
+// to a reference point inside the chunk so that it stays in range:
 //
-//   b_t   = sum of log gamma over chunk tokens 0..t (16-token sub-chunk I,
-//           local sum bl_t, sub-chunk totals tot_J)
-//   intra (s <= t, s in sub-chunk J < I):  phi_q(t) e^{bl_t} . e^{sum_{J<J'<I} tot_J'}
-//           . phi_k(s) e^{tot_J - bl_s}                       (all factors <= 1)
-//   intra (s <= t in the same sub-chunk):  reference at the sub-chunk's 8th
-//           token; exact per-element fallback when the sub-chunk's decay span
-//           is too large for that (e.g. gamma = 0).
-//   inter:  phi_q(t) e^{b_t} . S_chunk_start
-//   state:  S <- diag(e^{b_63}) S + sum_s phi_k(s) e^{b_63 - b_s} v_s^T
+//   per sub-chunk I (rows t = 0..15):  p_t = sum_{s<=t} lg_s (prefix),
+//       r_t = sum_{s>t} lg_s (suffix), tot = p_15, p7 = p_7
+//   keys    ko_s  = phi_k(s) e^{r_s}           (decay to the sub-chunk end, <= 1)
+//   queries qo_t  = phi_q(t) e^{p_t}           (decay from the sub-chunk start, <= 1)
+//   intra, key sub-chunk J < I:   qo_t . ko_s . prod_{J<J'<I} e^{tot_J'}
+//   intra, same sub-chunk (s<=t): (qo_t e^{-p7}) . (ko_s e^{p7-tot}), both
+//         within e^{+-span}; exact per-element fallback if the span of the
+//         sub-chunk's log decay exceeds SPAN_MAX (e.g. gamma = 0)
+//   inter:  qo_t prod_{J<I} e^{tot_J} . S_chunk_start
+//   state:  S <- diag(prod_J e^{tot_J}) S + sum_s ko_s prod_{J'>J(s)} e^{tot_J'} v_s^T
+// The per-element exponentials are the four above (phi_k, phi_q, e^{r}, e^{p});
+// all per-feature factors come from small tables built once per chunk.  The
+// prefix and suffix sums are MFMA products with constant triangular 0/1
+// matrices (exact: bf16 inputs, fp32 accumulation).
 //
 // Work split: one workgroup (4 waves) per (batch, key/value head, 64-column
 // block of the value dimension, sequence segment).  Wave I owns query/key rows
@@ -33,41 +38,67 @@
 // inter-chunk products and the window; for the state update the four waves
 // split S by rows of the key dimension.  The state is fp32 in registers; a
 // copy in the operand dtype sits in LDS for the inter-chunk product.
+//
+// Memory pipeline: the next chunk's k, v and log gamma are loaded into
+// registers at the top of the current chunk (q after the query loop) and
+// written to LDS at the top of the next one.  Keys and values of the last
+// few chunks stay in LDS rings, so the window reads no global memory.
 // Segments after the first start from a state assembled from the per-segment
-// end states that fwd_state_kernel (the same code with everything but the
-// state update switched off) leaves in the workspace.
+// end states that the state-only variant of this kernel leaves in the
+// workspace.
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace lz {
 
-constexpr int CH = 64;          // chunk length
+constexpr int CH = 64;            // chunk length
 constexpr float SPAN_MAX = 80.f;  // max |log-decay| across one 16-token sub-chunk for the
                                   // mid-reference MFMA path (e^80 ~ 5.5e34 < fp32/bf16 max)
 constexpr float NEG_BIG = -1.0e30f;
+constexpr int LDS_LIMIT = 160 * 1024;
+constexpr int WIN_BATCH = 8;      // key tiles per online-softmax batch in the window
 
-template <typename T, int D, int DV, int NR, bool STATE_ONLY> struct FwdLayout {
+template <typename T, int D, int DV> struct FwdGeom {
   static constexpr int PADE = 16 / (int)sizeof(T);
   static constexpr int LDW = D + PADE;   // rows of D elements
   static constexpr int LDC = CH + PADE;  // rows of 64 tokens
   static constexpr int LDM = 16 + PADE;  // rows of 16 meta tokens
-  static constexpr size_t SZ_W = (size_t)D * LDW * sizeof(T);
-  static constexpr size_t SZ_VT = (size_t)DV * LDC * sizeof(T);
-  static constexpr size_t SZ_KOWN = (size_t)CH * LDW * sizeof(T);
-  static constexpr size_t SZ_KST = (size_t)D * LDC * sizeof(T);
-  static constexpr size_t SZ_SBF = (size_t)DV * LDW * sizeof(T);
-  static constexpr size_t SZ_TOT = (size_t)4 * D * sizeof(float);
-  static constexpr size_t SZ_TVT = (size_t)DV * LDM * sizeof(T);
-  static constexpr size_t OFF_WK = 0;
-  static constexpr size_t OFF_WQ = OFF_WK + SZ_W;
-  static constexpr size_t OFF_VT = OFF_WQ + (STATE_ONLY ? 0 : SZ_W);
-  static constexpr size_t OFF_KST = OFF_VT + NR * SZ_VT;
-  static constexpr size_t OFF_TOT = OFF_KST + SZ_KST;
-  static constexpr size_t OFF_KOWN = OFF_TOT + SZ_TOT;
-  static constexpr size_t OFF_SBF = OFF_KOWN + (STATE_ONLY ? 0 : SZ_KOWN);
-  static constexpr size_t OFF_TVT = OFF_SBF + (STATE_ONLY ? 0 : SZ_SBF);
-  static constexpr size_t TOTAL = OFF_TVT + (STATE_ONLY ? 0 : SZ_TVT);
+  static constexpr int SZ_W = D * LDW * (int)sizeof(T);
+  static constexpr int SZ_VT = DV * LDC * (int)sizeof(T);
+  static constexpr int SZ_KR = CH * LDW * (int)sizeof(T);
+  // keys decayed to their sub-chunk end [s][f], overlaid on log gamma^T [f][s]
+  static constexpr int SZ_KOWN = (CH * LDW > D * LDC ? CH * LDW : D * LDC) * (int)sizeof(T);
+  static constexpr int SZ_SUB = 4 * D * (int)sizeof(float);  // one [4][D] fp32 table
+  static constexpr int SZ_SBF = DV * LDW * (int)sizeof(T);
+  static constexpr int SZ_TVT = DV * LDM * (int)sizeof(T);
+  static constexpr int SZ_TK = 16 * LDW * (int)sizeof(T);
 };
+
+// Byte offsets of the LDS regions for one launch (computed on the host).
+template <typename T, int D, int DV>
+static FwdLds make_lds(bool state_only, bool shared_w, int nr, int kr) {
+  using Gm = FwdGeom<T, D, DV>;
+  FwdLds l{};
+  int o = 0;
+  l.wk = o; o += Gm::SZ_W;
+  l.wq = (state_only || shared_w) ? l.wk : o;
+  if (!(state_only || shared_w)) o += Gm::SZ_W;
+  l.vt = o; o += nr * Gm::SZ_VT;
+  l.kr = o; o += kr * Gm::SZ_KR;
+  l.kown = o; o += Gm::SZ_KOWN;
+  l.tot = o; o += Gm::SZ_SUB;   // tot_J[f]
+  l.p7 = o; o += Gm::SZ_SUB;    // p7_J[f]
+  l.etot = o; o += Gm::SZ_SUB;  // e^{tot_J}
+  if (!state_only) {
+    l.enp7 = o; o += Gm::SZ_SUB;  // e^{-p7_J}
+    l.enr8 = o; o += Gm::SZ_SUB;  // e^{p7_J - tot_J}
+    l.sbf = o; o += Gm::SZ_SBF;
+    l.tvt = o; o += Gm::SZ_TVT;
+    l.tk = o; o += Gm::SZ_TK;
+  }
+  l.total = o;
+  return l;
+}
 
 // W_phi [d][f] row-major in global -> W^T [f][d] in LDS (row stride LDW).
 template <typename T, int D, int LDW>
@@ -81,50 +112,183 @@ __device__ __forceinline__ void load_wT(T *dst, const T *src) {
   }
 }
 
-// V rows c0..c0+63 (columns dv0..dv0+DV-1) -> V^T [dv][token] in LDS; rows past L are zero.
-template <typename T, int D, int DV, int LDC>
-__device__ __forceinline__ void load_vT(T *dst, const T *vh, int c0, int L, int dv0) {
-  for (int idx = threadIdx.x; idx < (CH / 2) * (DV / 8); idx += 256) {
-    const int tp = idx / (DV / 8), dq = idx % (DV / 8);
-    const int t0 = 2 * tp;
-    float a[8], b[8];
-    if (c0 + t0 < L) load8f(vh + (size_t)(c0 + t0) * D + dv0 + 8 * dq, a);
-    else {
+// Per-thread share of one chunk: keys (row-major), values and log gamma
+// (both stored transposed, token pairs 2*tp, 2*tp+1 x 8 columns).
+template <typename T, int D, int DV> struct ChunkRegs {
+  static constexpr int KFR = CH * D / 8 / 256;      // 8-element pieces of k per thread
+  static constexpr int LFR = (CH / 2) * (D / 8) / 256;  // token-pair pieces of log gamma
+  Frag<T> k[KFR];
+  Frag<T> v[2];
+  Frag<T> lg[LFR][2];
+};
+
+template <typename T, int D, int DV>
+__device__ __forceinline__ void load_chunk(ChunkRegs<T, D, DV> &r, const T *Kh, const T *Vh, const T *LGh,
+                                           int c0, int L, int dv0, bool with_v) {
+  static_assert(DV == 64, "value block of 64 columns");
+  const int tid = threadIdx.x;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) a[j] = 0.f;
+  for (int j = 0; j < ChunkRegs<T, D, DV>::KFR; ++j) {
+    const int idx = tid + 256 * j;
+    const int row = idx / (D / 8), c8 = idx % (D / 8);
+    r.k[j] = (c0 + row < L) ? load8(Kh + (size_t)(c0 + row) * D + 8 * c8) : frag_zero<T>();
+  }
+  if (with_v) {
+    const int tp = tid / (DV / 8), dq = tid % (DV / 8);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = c0 + 2 * tp + h;
+      r.v[h] = (t < L) ? load8(Vh + (size_t)t * D + dv0 + 8 * dq) : frag_zero<T>();
     }
-    if (c0 + t0 + 1 < L) load8f(vh + (size_t)(c0 + t0 + 1) * D + dv0 + 8 * dq, b);
-    else {
+  }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) b[j] = 0.f;
-    }
+  for (int j = 0; j < ChunkRegs<T, D, DV>::LFR; ++j) {
+    const int idx = tid + 256 * j;
+    const int tp = idx / (D / 8), fq = idx % (D / 8);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      dst[(8 * dq + j) * LDC + t0] = from_f<T>(a[j]);
-      dst[(8 * dq + j) * LDC + t0 + 1] = from_f<T>(b[j]);
+    for (int h = 0; h < 2; ++h) {
+      const int t = c0 + 2 * tp + h;
+      r.lg[j][h] = (t < L) ? load8(LGh + (size_t)t * D + 8 * fq) : frag_zero<T>();
     }
   }
 }
 
-template <typename T, int D, int DV, int NR, bool STATE_ONLY>
+template <typename T, int D, int DV, int LDW>
+__device__ __forceinline__ void store_keys(const ChunkRegs<T, D, DV> &r, T *sK) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < ChunkRegs<T, D, DV>::KFR; ++j) {
+    const int idx = tid + 256 * j;
+    const int row = idx / (D / 8), c8 = idx % (D / 8);
+    T *dst = sK + row * LDW + 8 * c8;
+    if constexpr (sizeof(T) == 2) {
+      *reinterpret_cast<bf16x8 *>(dst) = r.k[j].v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[e] = r.k[j].v[e];
+    }
+  }
+}
+
+// Two tokens x 8 columns -> transposed [col][token] (token pair adjacent).
+template <typename T, int LDC>
+__device__ __forceinline__ void store_pairT(const Frag<T> &a, const Frag<T> &b, T *dst) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    T *d = dst + e * LDC;
+    if constexpr (sizeof(T) == 2) {
+      bf16 pair[2] = {a.v[e], b.v[e]};
+      *reinterpret_cast<uint32_t *>(d) = *reinterpret_cast<const uint32_t *>(pair);
+    } else {
+      d[0] = a.v[e];
+      d[1] = b.v[e];
+    }
+  }
+}
+
+template <typename T, int D, int DV, int LDC>
+__device__ __forceinline__ void store_values(const ChunkRegs<T, D, DV> &r, T *sVt) {
+  const int tid = threadIdx.x;
+  const int tp = tid / (DV / 8), dq = tid % (DV / 8);
+  store_pairT<T, LDC>(r.v[0], r.v[1], sVt + (8 * dq) * LDC + 2 * tp);
+}
+
+template <typename T, int D, int DV, int LDC>
+__device__ __forceinline__ void store_lgT(const ChunkRegs<T, D, DV> &r, T *sLgT) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < ChunkRegs<T, D, DV>::LFR; ++j) {
+    const int idx = tid + 256 * j;
+    const int tp = idx / (D / 8), fq = idx % (D / 8);
+    store_pairT<T, LDC>(r.lg[j][0], r.lg[j][1], sLgT + (8 * fq) * LDC + 2 * tp);
+  }
+}
+
+// Constant B operand of the prefix / exclusive-suffix sums over the 16 rows of
+// a sub-chunk: lane (t = r16, kq) holds B[s = 8kq + j][t].
+template <typename T>
+__device__ __forceinline__ Frag<T> tri_frag(int r16, int g4, bool prefix) {
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int s = 8 * g4 + j;
+    x[j] = (s < 16 && (prefix ? (s <= r16) : (s > r16))) ? 1.f : 0.f;
+  }
+  return frag_from<T>(x);
+}
+
+// 8 fp32 table values for the operand slots of K-step js (features
+// 32js + 4g4 + 0..3 and 32js + 16 + 4g4 + 0..3).
+__device__ __forceinline__ void tab8(const float *row, int js, int g4, float (&x)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(row + 32 * js + 4 * g4);
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(row + 32 * js + 16 + 4 * g4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
+}
+
+template <int NFT>
+__device__ __forceinline__ void softmax_rows(const f32x4 (&z)[NFT], float (&phi)[NFT][4]) {
+  float zm = NEG_BIG;
+#pragma unroll
+  for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) zm = fmaxf(zm, z[ft][i]);
+  zm = wave_max_cols(zm);
+  float zs = 0.f;
+#pragma unroll
+  for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      phi[ft][i] = __expf(z[ft][i] - zm);
+      zs += phi[ft][i];
+    }
+  zs = wave_sum_cols(zs);
+  const float inv = 1.f / zs;
+#pragma unroll
+  for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) phi[ft][i] *= inv;
+}
+
+// z^T[f][t] = sum_d W[d][f] x[t][d] for the wave's 16 rows (W^T in LDS).
+template <typename T, int D, int LDW>
+__device__ __forceinline__ void feature_logits(const T *sW, const Frag<T> (&xf)[D / 32], int r16, int g4,
+                                               f32x4 (&z)[D / 16]) {
+#pragma unroll
+  for (int ft = 0; ft < D / 16; ++ft) {
+    z[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) z[ft] = mma(load8(sW + (16 * ft + r16) * LDW + 32 * j + 8 * g4), xf[j], z[ft]);
+  }
+}
+
+template <typename T, int D, int DV, bool STATE_ONLY>
 __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
-  using Lay = FwdLayout<T, D, DV, NR, STATE_ONLY>;
+  using Gm = FwdGeom<T, D, DV>;
   constexpr int NFT = D / 16;   // 16-row tiles of the feature dimension
   constexpr int KS = D / 32;    // K = 32 steps over d (or over features)
   constexpr int NDT = DV / 16;  // 16-column tiles of this block's value columns
   constexpr int FTW = NFT / 4;  // feature tiles of S owned by each wave
-  constexpr int LDW = Lay::LDW, LDC = Lay::LDC, LDM = Lay::LDM;
+  constexpr int LDW = Gm::LDW, LDC = Gm::LDC, LDM = Gm::LDM;
   static_assert(NFT % 4 == 0, "d must be a multiple of 64");
 
-  __shared__ __attribute__((aligned(16))) char smem[Lay::TOTAL];
-  T *sWk = reinterpret_cast<T *>(smem + Lay::OFF_WK);
-  T *sWq = reinterpret_cast<T *>(smem + Lay::OFF_WQ);
-  T *sVt = reinterpret_cast<T *>(smem + Lay::OFF_VT);
-  T *sKSt = reinterpret_cast<T *>(smem + Lay::OFF_KST);
-  float *sTot = reinterpret_cast<float *>(smem + Lay::OFF_TOT);
-  T *sKown = reinterpret_cast<T *>(smem + Lay::OFF_KOWN);
-  T *sSbf = reinterpret_cast<T *>(smem + Lay::OFF_SBF);
-  T *sTvT = reinterpret_cast<T *>(smem + Lay::OFF_TVT);
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const FwdLds &ly = p.lds;
+  T *sWk = reinterpret_cast<T *>(smem + ly.wk);
+  T *sWq = reinterpret_cast<T *>(smem + ly.wq);
+  T *sVt = reinterpret_cast<T *>(smem + ly.vt);
+  T *sKr = reinterpret_cast<T *>(smem + ly.kr);
+  T *sKown = reinterpret_cast<T *>(smem + ly.kown);
+  T *sLgT = sKown;  // log gamma^T [f][s], dead before the keys are written
+  float *sTot = reinterpret_cast<float *>(smem + ly.tot);
+  float *sP7 = reinterpret_cast<float *>(smem + ly.p7);
+  float *sETot = reinterpret_cast<float *>(smem + ly.etot);
+  float *sENP7 = reinterpret_cast<float *>(smem + ly.enp7);
+  float *sENR8 = reinterpret_cast<float *>(smem + ly.enr8);
+  T *sSbf = reinterpret_cast<T *>(smem + ly.sbf);
+  T *sTvT = reinterpret_cast<T *>(smem + ly.tvt);
+  T *sTk = reinterpret_cast<T *>(smem + ly.tk);
+  const int NR = p.nring, KR = p.kring;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
@@ -149,19 +313,38 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   const T *Vh = reinterpret_cast<const T *>(p.v) + kv_off;
   const T *LGh = reinterpret_cast<const T *>(p.lg) + kv_off;
   const T *Wk = reinterpret_cast<const T *>(p.wk) + (size_t)kvh * p.w_stride;
+  const T *Qbase = reinterpret_cast<const T *>(p.q);
 
   // ---- prologue
   load_wT<T, D, LDW>(sWk, Wk);
   if constexpr (!STATE_ONLY) {
-    load_wT<T, D, LDW>(sWq, reinterpret_cast<const T *>(p.wq) + (size_t)(kvh * G) * p.w_stride);
+    if (ly.wq != ly.wk)
+      load_wT<T, D, LDW>(sWq, reinterpret_cast<const T *>(p.wq) + (size_t)(kvh * G) * p.w_stride);
     const T *Tv = reinterpret_cast<const T *>(p.tv);
+    const T *Tk = reinterpret_cast<const T *>(p.tk);
     for (int idx = tid; idx < DV * 16; idx += 256) {
       const int dv = idx / 16, m = idx % 16;
       sTvT[dv * LDM + m] = (m < p.M) ? Tv[((size_t)kvh * p.M + m) * D + dv0 + dv] : from_f<T>(0.f);
     }
-    // previous chunks needed by the window of this segment's first chunk
-    for (int cc = max(0, c_begin - (NR - 1)); cc < c_begin; ++cc)
-      load_vT<T, D, DV, LDC>(sVt + (cc % NR) * (DV * LDC), Vh, cc * CH, L, dv0);
+    for (int idx = tid; idx < 16 * D; idx += 256) {
+      const int m = idx / D, e = idx % D;
+      sTk[m * LDW + e] = (m < p.M) ? Tk[((size_t)kvh * p.M + m) * D + e] : from_f<T>(0.f);
+    }
+    // rings start as zeros: a masked window slot (probability 0) must not meet a NaN pattern
+    {
+      uint4 *vz = reinterpret_cast<uint4 *>(smem + ly.vt);
+      const int nz = (ly.kown - ly.vt) / 16;  // value ring and key ring are contiguous
+      for (int idx = tid; idx < nz; idx += 256) vz[idx] = uint4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+    // earlier chunks reached by the window of this segment's first chunk
+    const int R = max(NR, KR);
+    for (int cc = max(0, c_begin - (R - 1)); cc < c_begin; ++cc) {
+      ChunkRegs<T, D, DV> pre;
+      load_chunk<T, D, DV>(pre, Kh, Vh, LGh, cc * CH, L, dv0, true);
+      if (cc > c_begin - KR) store_keys<T, D, DV, LDW>(pre, sKr + (cc % KR) * (CH * LDW));
+      if (cc > c_begin - NR) store_values<T, D, DV, LDC>(pre, sVt + (cc % NR) * (DV * LDC));
+    }
   }
 
   // S owned by this wave: feature tiles wv*FTW .. +FTW-1, all value tiles.
@@ -191,6 +374,27 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
         }
       }
     }
+  }
+  float dsum = 0.f;  // state-only: running sum of log gamma for feature tid
+
+  const int I = wv;  // sub-chunk owned by this wave
+  const float mix = p.mix, scale = p.scale;
+  const bool win_fast = (p.W <= CH + 1) && KR >= 2 && NR >= 2;
+  const Frag<T> tri_pre = tri_frag<T>(r16, g4, true);
+  const Frag<T> tri_suf = tri_frag<T>(r16, g4, false);
+
+  // first chunk's data into registers
+  ChunkRegs<T, D, DV> pf;
+  Frag<T> pfq[KS];
+  load_chunk<T, D, DV>(pf, Kh, Vh, LGh, c_begin * CH, L, dv0, true);
+  if constexpr (!STATE_ONLY) {
+    const int pos0 = c_begin * CH + 16 * I + r16;
+    const T *Q0 = Qbase + ((size_t)b * p.Hq + kvh * G) * (size_t)L * D;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) pfq[j] = (pos0 < L) ? load8(Q0 + (size_t)pos0 * D + 32 * j + 8 * g4) : frag_zero<T>();
+  }
+  __syncthreads();  // prologue LDS writes complete
+  if constexpr (!STATE_ONLY) {
     // operand copy S^T [dv][f]
 #pragma unroll
     for (int ft = 0; ft < FTW; ++ft)
@@ -199,156 +403,108 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
         store4<T>(sSbf + (16 * dt + r16) * LDW + 16 * (wv * FTW + ft) + 4 * g4, S[ft][dt][0], S[ft][dt][1],
                   S[ft][dt][2], S[ft][dt][3]);
   }
-  float dsum = 0.f;  // state-only: running sum of log gamma for feature tid
-  __syncthreads();
-
-  const int I = wv;  // sub-chunk owned by this wave
-  const float mix = p.mix, scale = p.scale;
 
   for (int c = c_begin; c < c_end; ++c) {
     const int c0 = c * CH;
+    const int kcur = (c % KR) * (CH * LDW);
     const int cur = (c % NR) * (DV * LDC);
-    // ---- V of this chunk -> ring slot
-    load_vT<T, D, DV, LDC>(sVt + cur, Vh, c0, L, dv0);
+    const int kprev = ((c + KR - 1) % KR) * (CH * LDW);  // used only when KR >= 2
+    const int vprev = ((c + NR - 1) % NR) * (DV * LDC);
+    // ---- this chunk's keys, values, log gamma (loaded one chunk ahead) -> LDS
+    store_keys<T, D, DV, LDW>(pf, sKr + kcur);
+    store_values<T, D, DV, LDC>(pf, sVt + cur);
+    store_lgT<T, D, DV, LDC>(pf, sLgT);
+    Frag<T> qf[KS];
+    if constexpr (!STATE_ONLY) {
+#pragma unroll
+      for (int j = 0; j < KS; ++j) qf[j] = pfq[j];
+    }
+    // ---- next chunk in flight during this one
+    if (c + 1 < c_end) load_chunk<T, D, DV>(pf, Kh, Vh, LGh, c0 + CH, L, dv0, true);
+    __syncthreads();  // B0: this chunk in LDS
 
-    // ---- own rows: keys (B-operand fragments over d) and log gamma
     const int pos = c0 + 16 * I + r16;
     const bool valid = pos < L;
-    Frag<T> kf[KS];
-#pragma unroll
-    for (int j = 0; j < KS; ++j)
-      kf[j] = valid ? load8(Kh + (size_t)pos * D + 32 * j + 8 * g4) : frag_zero<T>();
-    float bl[NFT][4];  // log gamma -> local inclusive cumsum within the sub-chunk
+    // ---- prefix / exclusive suffix sums of log gamma within the sub-chunk (MFMA with 0/1 matrices)
+    float pfx[NFT][4], sfx[NFT][4];
 #pragma unroll
     for (int ft = 0; ft < NFT; ++ft) {
-      if (valid) load4f(LGh + (size_t)pos * D + 16 * ft + 4 * g4, bl[ft]);
-      else {
+      const Frag<T> a = (g4 < 2) ? load8(sLgT + (16 * ft + r16) * LDC + 16 * I + 8 * g4) : frag_zero<T>();
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 pp = mma(a, tri_pre, zero);
+      const f32x4 ss = mma(a, tri_suf, zero);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bl[ft][i] = 0.f;
-      }
+      for (int i = 0; i < 4; ++i) { pfx[ft][i] = pp[i]; sfx[ft][i] = ss[i]; }
     }
-#pragma unroll
-    for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x = bl[ft][i];
-#pragma unroll
-        for (int dd = 1; dd < 16; dd <<= 1) {
-          const float y = __shfl_up(x, dd, 16);
-          if (r16 >= dd) x += y;
-        }
-        bl[ft][i] = x;
-      }
-    float tot[NFT][4];  // this sub-chunk's total, broadcast from its last row
-#pragma unroll
-    for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) tot[ft][i] = __shfl(bl[ft][i], 16 * g4 + 15);
-    if (r16 == 15) {
+    if (r16 == 15 || r16 == 7) {
+      float *dst = (r16 == 15 ? sTot : sP7) + I * D + 4 * g4;
 #pragma unroll
       for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sTot[I * D + 16 * ft + 4 * g4 + i] = bl[ft][i];
+        *reinterpret_cast<f32x4 *>(dst + 16 * ft) = f32x4{pfx[ft][0], pfx[ft][1], pfx[ft][2], pfx[ft][3]};
     }
 
-    // ---- phi_k for own rows: z^T[f][t] = sum_d W[d][f] k[t][d]
-    float phik[NFT][4];
+    // ---- phi_k for own rows; keys decayed to the sub-chunk end
+    float ko[NFT][4];
     {
+      Frag<T> kf[KS];
+#pragma unroll
+      for (int j = 0; j < KS; ++j) kf[j] = load8(sKr + kcur + (16 * I + r16) * LDW + 32 * j + 8 * g4);
       f32x4 z[NFT];
-#pragma unroll
-      for (int ft = 0; ft < NFT; ++ft) {
-        z[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < KS; ++j) z[ft] = mma(load8(sWk + (16 * ft + r16) * LDW + 32 * j + 8 * g4), kf[j], z[ft]);
-      }
-      float zm = NEG_BIG;
+      feature_logits<T, D, LDW>(sWk, kf, r16, g4, z);
+      softmax_rows<NFT>(z, ko);
 #pragma unroll
       for (int ft = 0; ft < NFT; ++ft)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) zm = fmaxf(zm, z[ft][i]);
-      zm = wave_max_cols(zm);
-      float zs = 0.f;
-#pragma unroll
-      for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          phik[ft][i] = __expf(z[ft][i] - zm);
-          zs += phik[ft][i];
-        }
-      zs = wave_sum_cols(zs);
-      const float inv = 1.f / zs;
-#pragma unroll
-      for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) phik[ft][i] *= inv;
+        for (int i = 0; i < 4; ++i) ko[ft][i] *= __expf(sfx[ft][i]);
     }
-
-    // ---- keys relative to the end of their own sub-chunk (<= 1) -> LDS [s][f]
-    Frag<T> kmid[KS];
     bool safe = true;
     if constexpr (!STATE_ONLY) {
-#pragma unroll
-      for (int ft = 0; ft < NFT; ++ft) {
-        float o[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = phik[ft][i] * __expf(tot[ft][i] - bl[ft][i]);
-        store4<T>(sKown + (16 * I + r16) * LDW + 16 * ft + 4 * g4, o[0], o[1], o[2], o[3]);
-      }
-      // diagonal block operands, reference at row 7 of the sub-chunk
-      float span = 0.f;
+      float span = 0.f;  // -tot = -(prefix + suffix) at any row
 #pragma unroll
       for (int ft = 0; ft < NFT; ++ft)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) span = fmaxf(span, -tot[ft][i]);
-      span = wave_max_all(span);
-      safe = span <= SPAN_MAX;
-#pragma unroll
-      for (int js = 0; js < KS; ++js) {
-        float x[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int ft = 2 * js + (jj >> 2), i = jj & 3;
-          const float b7 = __shfl(bl[ft][i], 16 * g4 + 7);
-          x[jj] = safe ? phik[ft][i] * __expf(b7 - bl[ft][i]) : 0.f;
-        }
-        kmid[js] = frag_from<T>(x);
-      }
+        for (int i = 0; i < 4; ++i) span = fmaxf(span, -(pfx[ft][i] + sfx[ft][i]));
+      safe = wave_max_all(span) <= SPAN_MAX;
     }
-    __syncthreads();  // B1: sub-chunk totals (and own-sub-chunk keys) visible
+    __syncthreads();  // B1: sub-chunk totals visible, log gamma^T consumed
 
-    // ---- chunk prefix sums for own features: pre = sum_{J<I} tot_J, btot = sum_J tot_J
-    float pre[NFT][4], btot[NFT][4];
+    // ---- per-feature tables for this chunk; decayed keys -> LDS [s][f]
+    {
+      constexpr int PER = 4 / (256 / D);  // sub-chunks handled per thread
+      const int f = tid % D, j0 = (tid / D) * PER;
 #pragma unroll
-    for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int f = 16 * ft + 4 * g4 + i;
-        float a = 0.f, s = 0.f;
-#pragma unroll
-        for (int J = 0; J < 4; ++J) {
-          const float x = sTot[J * D + f];
-          if (J < I) a += x;
-          s += x;
+      for (int jj = 0; jj < PER; ++jj) {
+        const int J = j0 + jj;
+        const float tt = sTot[J * D + f];
+        sETot[J * D + f] = __expf(tt);
+        if constexpr (STATE_ONLY) {
+          dsum += tt;
+        } else {
+          const float p7 = sP7[J * D + f];
+          sENP7[J * D + f] = __expf(-p7);
+          sENR8[J * D + f] = __expf(p7 - tt);
         }
-        pre[ft][i] = a;
-        btot[ft][i] = s;
-      }
-    if constexpr (STATE_ONLY) {
-      if (tid < D) {
-#pragma unroll
-        for (int J = 0; J < 4; ++J) dsum += sTot[J * D + tid];
       }
     }
-    // keys decayed to the chunk end (<= 1) -> LDS [f][s]
 #pragma unroll
     for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sKSt[(16 * ft + 4 * g4 + i) * LDC + 16 * I + r16] =
-            from_f<T>(phik[ft][i] * __expf(btot[ft][i] - pre[ft][i] - bl[ft][i]));
-    __syncthreads();  // B2: keys for the intra products and the state update visible
+      store4<T>(sKown + (16 * I + r16) * LDW + 16 * ft + 4 * g4, ko[ft][0], ko[ft][1], ko[ft][2], ko[ft][3]);
+    __syncthreads();  // B2: tables and keys visible
 
     if constexpr (!STATE_ONLY) {
+      // diagonal-block key operand: ko e^{p7 - tot} (reference at row 7)
+      Frag<T> kmid[KS];
+      if (safe) {
+#pragma unroll
+        for (int js = 0; js < KS; ++js) {
+          float t8[8], x[8];
+          tab8(sENR8 + I * D, js, g4, t8);
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) x[jj] = ko[2 * js + (jj >> 2)][jj & 3] * t8[jj];
+          kmid[js] = frag_from<T>(x);
+        }
+      }
+
       for (int g = 0; g < G; ++g) {
         const int hq = kvh * G + g;
         if (p.per_head_q && G > 1) {  // a different W_phi_q for every query head
@@ -356,45 +512,23 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
           load_wT<T, D, LDW>(sWq, reinterpret_cast<const T *>(p.wq) + (size_t)hq * p.w_stride);
           __syncthreads();
         }
-        const T *Qh = reinterpret_cast<const T *>(p.q) + ((size_t)b * p.Hq + hq) * (size_t)L * D;
-        Frag<T> qf[KS];
+        const T *Qh = Qbase + ((size_t)b * p.Hq + hq) * (size_t)L * D;
+        if (g > 0) {
 #pragma unroll
-        for (int j = 0; j < KS; ++j)
-          qf[j] = valid ? load8(Qh + (size_t)pos * D + 32 * j + 8 * g4) : frag_zero<T>();
+          for (int j = 0; j < KS; ++j)
+            qf[j] = valid ? load8(Qh + (size_t)pos * D + 32 * j + 8 * g4) : frag_zero<T>();
+        }
 
-        // phi_q for own rows, then q~ = phi_q e^{bl} (<= 1)
-        float qo[NFT][4], phiq[NFT][4];
+        // phi_q for own rows, then qo = phi_q e^{prefix} (<= 1)
+        float qo[NFT][4];
         {
           f32x4 z[NFT];
-#pragma unroll
-          for (int ft = 0; ft < NFT; ++ft) {
-            z[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < KS; ++j) z[ft] = mma(load8(sWq + (16 * ft + r16) * LDW + 32 * j + 8 * g4), qf[j], z[ft]);
-          }
-          float zm = NEG_BIG;
+          feature_logits<T, D, LDW>(sWq, qf, r16, g4, z);
+          softmax_rows<NFT>(z, qo);
 #pragma unroll
           for (int ft = 0; ft < NFT; ++ft)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) zm = fmaxf(zm, z[ft][i]);
-          zm = wave_max_cols(zm);
-          float zs = 0.f;
-#pragma unroll
-          for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              phiq[ft][i] = __expf(z[ft][i] - zm);
-              zs += phiq[ft][i];
-            }
-          zs = wave_sum_cols(zs);
-          const float inv = 1.f / zs;
-#pragma unroll
-          for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              phiq[ft][i] *= inv;
-              qo[ft][i] = phiq[ft][i] * __expf(bl[ft][i]);
-            }
+            for (int i = 0; i < 4; ++i) qo[ft][i] *= __expf(pfx[ft][i]);
         }
 
         // ---- intra-chunk scores A^T[s][t] for key sub-chunks J <= I
@@ -404,20 +538,21 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int J = 0; J < 3; ++J) {
           if (J < I) {
-            // factor e^{sum_{J<J'<I} tot_J'} joins the two references
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int js = 0; js < KS; ++js) {
               float x[8];
 #pragma unroll
-              for (int jj = 0; jj < 8; ++jj) {
-                const int ft = 2 * js + (jj >> 2), i = jj & 3;
-                const int f = 16 * ft + 4 * g4 + i;
-                float gap = 0.f;
+              for (int jj = 0; jj < 8; ++jj) x[jj] = qo[2 * js + (jj >> 2)][jj & 3];
+              // prod_{J<J'<I} e^{tot_J'} joins the two references
 #pragma unroll
-                for (int J2 = 0; J2 < 3; ++J2)
-                  if (J2 > J && J2 < I) gap += sTot[J2 * D + f];
-                x[jj] = qo[ft][i] * __expf(gap);
+              for (int J2 = 1; J2 < 3; ++J2) {
+                if (J2 > J && J2 < I) {
+                  float t8[8];
+                  tab8(sETot + J2 * D, js, g4, t8);
+#pragma unroll
+                  for (int jj = 0; jj < 8; ++jj) x[jj] *= t8[jj];
+                }
               }
               const T *kr = sKown + (16 * J + r16) * LDW + 32 * js + 4 * g4;
               acc = mma(load4x2(kr, kr + 16), frag_from<T>(x), acc);
@@ -430,17 +565,26 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
           if (safe) {
 #pragma unroll
             for (int js = 0; js < KS; ++js) {
-              float x[8];
+              float t8[8], x[8];
+              tab8(sENP7 + I * D, js, g4, t8);
 #pragma unroll
-              for (int jj = 0; jj < 8; ++jj) {
-                const int ft = 2 * js + (jj >> 2), i = jj & 3;
-                const float b7 = __shfl(bl[ft][i], 16 * g4 + 7);
-                x[jj] = phiq[ft][i] * __expf(bl[ft][i] - b7);
-              }
+              for (int jj = 0; jj < 8; ++jj) x[jj] = qo[2 * js + (jj >> 2)][jj & 3] * t8[jj];
               acc = mma(kmid[js], frag_from<T>(x), acc);
             }
           } else {
-            // exact: A[t][s] = sum_f phi_q[t][f] phi_k[s][f] e^{bl_t[f] - bl_s[f]}
+            // exact: A[t][s] = sum_f phi_q[t][f] phi_k[s][f] e^{p_t[f] - p_s[f]}, with phi
+            // recomputed in fp32 (rare path: a sub-chunk whose log decay spans > SPAN_MAX)
+            float phk[NFT][4], phq[NFT][4];
+            {
+              Frag<T> kf[KS];
+#pragma unroll
+              for (int j = 0; j < KS; ++j) kf[j] = load8(sKr + kcur + (16 * I + r16) * LDW + 32 * j + 8 * g4);
+              f32x4 z[NFT];
+              feature_logits<T, D, LDW>(sWk, kf, r16, g4, z);
+              softmax_rows<NFT>(z, phk);
+              feature_logits<T, D, LDW>(sWq, qf, r16, g4, z);
+              softmax_rows<NFT>(z, phq);
+            }
 #pragma unroll 1
             for (int s2 = 0; s2 < 16; ++s2) {
               float part = 0.f;
@@ -448,9 +592,9 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
               for (int ft = 0; ft < NFT; ++ft)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                  const float pk = __shfl(phik[ft][i], 16 * g4 + s2);
-                  const float bs = __shfl(bl[ft][i], 16 * g4 + s2);
-                  const float term = phiq[ft][i] * pk * __expf(bl[ft][i] - bs);
+                  const float pk = __shfl(phk[ft][i], 16 * g4 + s2);
+                  const float bs = __shfl(pfx[ft][i], 16 * g4 + s2);
+                  const float term = phq[ft][i] * pk * __expf(pfx[ft][i] - bs);
                   part += (s2 <= r16) ? term : 0.f;
                 }
               part = wave_sum_cols(part);
@@ -489,137 +633,206 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
             }
           }
         }
-        {
 #pragma unroll
-          for (int js = 0; js < KS; ++js) {
-            float x[8];
+        for (int js = 0; js < KS; ++js) {
+          float x[8];
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-              const int ft = 2 * js + (jj >> 2), i = jj & 3;
-              x[jj] = qo[ft][i] * __expf(pre[ft][i]);
+          for (int jj = 0; jj < 8; ++jj) x[jj] = qo[2 * js + (jj >> 2)][jj & 3];
+          // prod_{J<I} e^{tot_J}: decay from the chunk start to the sub-chunk start
+#pragma unroll
+          for (int J2 = 0; J2 < 3; ++J2) {
+            if (J2 < I) {
+              float t8[8];
+              tab8(sETot + J2 * D, js, g4, t8);
+#pragma unroll
+              for (int jj = 0; jj < 8; ++jj) x[jj] *= t8[jj];
             }
-            const Frag<T> bf = frag_from<T>(x);
+          }
+          const Frag<T> bf = frag_from<T>(x);
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-              const T *sr = sSbf + (16 * dt + r16) * LDW + 32 * js + 4 * g4;
-              yacc[dt] = mma(load4x2(sr, sr + 16), bf, yacc[dt]);
-            }
+          for (int dt = 0; dt < NDT; ++dt) {
+            const T *sr = sSbf + (16 * dt + r16) * LDW + 32 * js + 4 * g4;
+            yacc[dt] = mma(load4x2(sr, sr + 16), bf, yacc[dt]);
           }
         }
 
-        // ---- anchor window: meta keys + keys j with pos-W < j <= pos, online softmax
+        // ---- anchor window: meta keys + keys j with pos-W < j <= pos
         f32x4 ywin[NDT];
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) ywin[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float m_run = NEG_BIG, l_run = 0.f;
-        const int kt_hi = (c0 >> 4) + I;
-        const int lo_key = c0 + 16 * I - p.W + 1;
-        const int kt_lo = lo_key <= 0 ? 0 : (lo_key >> 4);
-        // tile list: u = -1 is the meta tile (if M > 0), then kt_lo..kt_hi
-        const int u_first = (p.M > 0) ? -1 : 0;
-        const int n_tiles = (kt_hi - kt_lo + 1) - u_first;
-        const T *Tk = reinterpret_cast<const T *>(p.tk);
-        for (int u0 = 0; u0 < n_tiles; u0 += 4) {
-          f32x4 lt[4];
-          int kts[4];
+        float l_run = 0.f;
+        if (win_fast) {
+          // W <= 65 and two chunks of keys/values in the rings: exactly the meta tile and the
+          // five 16-key tiles ending at this sub-chunk, one softmax pass.  Band tile u (1..5)
+          // starts at chunk-relative row 16 (I - 5 + u); kj - pos = 16u - 80 + 4 g4 + i - r16.
+          f32x4 lt[6];
+          {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int uu = 0; uu < 4; ++uu) {
-            const int u = u0 + uu;
-            lt[uu] = f32x4{NEG_BIG, NEG_BIG, NEG_BIG, NEG_BIG};
-            kts[uu] = -2;  // none
-            if (u < n_tiles) {
-              const int kt = (u + u_first < 0) ? -1 : kt_lo + u + u_first;
-              kts[uu] = kt;
-              f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-              if (kt < 0) {
-                const bool mv = r16 < p.M;
+            for (int j = 0; j < KS; ++j) acc = mma(load8(sTk + r16 * LDW + 32 * j + 8 * g4), qf[j], acc);
 #pragma unroll
-                for (int j = 0; j < KS; ++j) {
-                  const Frag<T> a = mv ? load8(Tk + ((size_t)kvh * p.M + r16) * D + 32 * j + 8 * g4) : frag_zero<T>();
-                  acc = mma(a, qf[j], acc);
-                }
+            for (int i = 0; i < 4; ++i) lt[0][i] = (4 * g4 + i < p.M) ? acc[i] * scale : NEG_BIG;
+          }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) lt[uu][i] = (4 * g4 + i < p.M) ? acc[i] * scale : NEG_BIG;
-              } else {
-                const int key = 16 * kt + r16;
-                const bool kv = key < L;
+          for (int u = 1; u < 6; ++u) {
+            const int rt = I - 5 + u;  // chunk-relative tile, < 0: previous chunk
+            const T *kr = sKr + (rt < 0 ? kprev + (rt + 4) * 16 * LDW : kcur + rt * 16 * LDW) + r16 * LDW + 8 * g4;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j < KS; ++j) {
-                  const Frag<T> a = kv ? load8(Kh + (size_t)key * D + 32 * j + 8 * g4) : frag_zero<T>();
-                  acc = mma(a, qf[j], acc);
-                }
+            for (int j = 0; j < KS; ++j) acc = mma(load8(kr + 32 * j), qf[j], acc);
+            const bool before_start = (c == 0) && rt < 0;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  const int kj = 16 * kt + 4 * g4 + i;
-                  lt[uu][i] = (kj <= pos && kj > pos - p.W) ? acc[i] * scale : NEG_BIG;
-                }
-              }
+            for (int i = 0; i < 4; ++i) {
+              const int dk = 16 * u - 80 + 4 * g4 + i - r16;
+              lt[u][i] = (!before_start && dk <= 0 && dk > -p.W) ? acc[i] * scale : NEG_BIG;
             }
           }
           float bm = NEG_BIG;
 #pragma unroll
-          for (int uu = 0; uu < 4; ++uu)
+          for (int u = 0; u < 6; ++u)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) bm = fmaxf(bm, lt[uu][i]);
+            for (int i = 0; i < 4; ++i) bm = fmaxf(bm, lt[u][i]);
           bm = wave_max_cols(bm);
-          const float m_new = fmaxf(m_run, bm);
-          const float alpha = __expf(m_run - m_new);
-          l_run *= alpha;
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ywin[dt][i] *= alpha;
-          m_run = m_new;
-          float pv[4][4];
-#pragma unroll
-          for (int uu = 0; uu < 4; ++uu)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              pv[uu][i] = (lt[uu][i] > 0.5f * NEG_BIG) ? __expf(lt[uu][i] - m_new) : 0.f;
-              l_run += pv[uu][i];
-            }
-          // P V: pairs of tiles form one K = 32 step
-#pragma unroll
-          for (int pr = 0; pr < 2; ++pr) {
-            const int ua = 2 * pr, ub = 2 * pr + 1;
-            if (kts[ua] == -2) continue;
+          for (int pr = 0; pr < 3; ++pr) {
             float x[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              x[i] = pv[ua][i];
-              x[4 + i] = (kts[ub] == -2) ? 0.f : pv[ub][i];
-            }
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float pv = __expf(lt[2 * pr + h][i] - bm);  // masked: exp(-1e30) = 0
+                x[4 * h + i] = pv;
+                l_run += pv;
+              }
             const Frag<T> bf = frag_from<T>(x);
+            const int ua = 2 * pr, ub = 2 * pr + 1;
+            const int rta = I - 5 + ua, rtb = I - 5 + ub;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
               const int dvl = 16 * dt + r16;
-              float av[8];
+              const T *pa = (ua == 0) ? sTvT + dvl * LDM + 4 * g4
+                                      : sVt + (rta < 0 ? vprev + 16 * (rta + 4) : cur + 16 * rta) + dvl * LDC + 4 * g4;
+              const T *pb = sVt + (rtb < 0 ? vprev + 16 * (rtb + 4) : cur + 16 * rtb) + dvl * LDC + 4 * g4;
+              ywin[dt] = mma(load4x2(pa, pb), bf, ywin[dt]);
+            }
+          }
+        } else {
+          // general window: batches of key tiles with an online softmax
+          float m_run = NEG_BIG;
+          const int kt_hi = (c0 >> 4) + I;
+          const int lo_key = c0 + 16 * I - p.W + 1;
+          const int kt_lo = lo_key <= 0 ? 0 : (lo_key >> 4);
+          // tile list: u = -1 is the meta tile (if M > 0), then kt_lo..kt_hi
+          const int u_first = (p.M > 0) ? -1 : 0;
+          const int n_tiles = (kt_hi - kt_lo + 1) - u_first;
+          for (int u0 = 0; u0 < n_tiles; u0 += WIN_BATCH) {
+            f32x4 lt[WIN_BATCH];
 #pragma unroll
-              for (int half = 0; half < 2; ++half) {
-                const int kt = kts[half ? ub : ua];
-                if (kt == -2) {
+            for (int uu = 0; uu < WIN_BATCH; ++uu) {
+              const int u = u0 + uu;
+              lt[uu] = f32x4{NEG_BIG, NEG_BIG, NEG_BIG, NEG_BIG};
+              if (u < n_tiles) {
+                const int kt = (u + u_first < 0) ? -1 : kt_lo + u + u_first;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                if (kt < 0) {
 #pragma unroll
-                  for (int i = 0; i < 4; ++i) av[4 * half + i] = 0.f;
-                } else if (kt == -1) {
-                  float t4[4];
-                  load4f(sTvT + dvl * LDM + 4 * g4, t4);
+                  for (int j = 0; j < KS; ++j) acc = mma(load8(sTk + r16 * LDW + 32 * j + 8 * g4), qf[j], acc);
 #pragma unroll
-                  for (int i = 0; i < 4; ++i) av[4 * half + i] = t4[i];
-                } else if ((kt >> 2) > c - NR) {
-                  float t4[4];
-                  load4f(sVt + ((kt >> 2) % NR) * (DV * LDC) + dvl * LDC + 16 * (kt & 3) + 4 * g4, t4);
-#pragma unroll
-                  for (int i = 0; i < 4; ++i) av[4 * half + i] = t4[i];
+                  for (int i = 0; i < 4; ++i) lt[uu][i] = (4 * g4 + i < p.M) ? acc[i] * scale : NEG_BIG;
                 } else {
-                  // key tile older than the LDS ring: gather from global memory
+                  const int kc = kt >> 2;
+                  if (kc > c - KR) {
+                    const T *kr = sKr + (kc % KR) * (CH * LDW) + (16 * (kt & 3) + r16) * LDW + 8 * g4;
+#pragma unroll
+                    for (int j = 0; j < KS; ++j) acc = mma(load8(kr + 32 * j), qf[j], acc);
+                  } else {
+                    // key tile older than the LDS ring: global memory
+                    const int key = 16 * kt + r16;
+                    const bool kv = key < L;
+#pragma unroll
+                    for (int j = 0; j < KS; ++j) {
+                      const Frag<T> a = kv ? load8(Kh + (size_t)key * D + 32 * j + 8 * g4) : frag_zero<T>();
+                      acc = mma(a, qf[j], acc);
+                    }
+                  }
 #pragma unroll
                   for (int i = 0; i < 4; ++i) {
-                    const int key = 16 * kt + 4 * g4 + i;
-                    av[4 * half + i] = (key < L) ? to_f(Vh[(size_t)key * D + dv0 + dvl]) : 0.f;
+                    const int kj = 16 * kt + 4 * g4 + i;
+                    lt[uu][i] = (kj <= pos && kj > pos - p.W) ? acc[i] * scale : NEG_BIG;
                   }
                 }
               }
-              ywin[dt] = mma(frag_from<T>(av), bf, ywin[dt]);
+            }
+            float bm = NEG_BIG;
+#pragma unroll
+            for (int uu = 0; uu < WIN_BATCH; ++uu)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) bm = fmaxf(bm, lt[uu][i]);
+            bm = wave_max_cols(bm);
+            const float m_new = fmaxf(m_run, bm);
+            const float alpha = __expf(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) ywin[dt][i] *= alpha;
+            m_run = m_new;
+            // P V: pairs of tiles form one K = 32 step
+#pragma unroll
+            for (int pr = 0; pr < WIN_BATCH / 2; ++pr) {
+              const int ua = u0 + 2 * pr, ub = ua + 1;
+              if (ua >= n_tiles) continue;
+              float x[8];
+#pragma unroll
+              for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const float l = lt[2 * pr + h][i];
+                  const float pv = (l > 0.5f * NEG_BIG) ? __expf(l - m_new) : 0.f;
+                  x[4 * h + i] = pv;
+                  l_run += pv;
+                }
+              const Frag<T> bf = frag_from<T>(x);
+              const int kta = (ua + u_first < 0) ? -1 : kt_lo + ua + u_first;
+              const int ktb = (ub >= n_tiles) ? -2 : kt_lo + ub + u_first;
+              const bool ring_a = kta >= 0 && (kta >> 2) > c - NR;
+              const bool ring_b = ktb >= 0 && (ktb >> 2) > c - NR;
+#pragma unroll
+              for (int dt = 0; dt < NDT; ++dt) {
+                const int dvl = 16 * dt + r16;
+                const T *pa = (kta < 0) ? sTvT + dvl * LDM + 4 * g4
+                                        : sVt + ((kta >> 2) % NR) * (DV * LDC) + dvl * LDC + 16 * (kta & 3) + 4 * g4;
+                const T *pb = (ktb < 0) ? pa : sVt + ((ktb >> 2) % NR) * (DV * LDC) + dvl * LDC + 16 * (ktb & 3) + 4 * g4;
+                Frag<T> af;
+                if ((kta < 0 || ring_a) && (ktb < 0 || ring_b)) {
+                  af = load4x2(pa, pb);  // slots of a missing second tile meet P = 0
+                } else {
+                  // a value tile older than the LDS ring: gather from global memory
+                  float av[8];
+#pragma unroll
+                  for (int h = 0; h < 2; ++h) {
+                    const int kt = h ? ktb : kta;
+                    const bool inring = h ? ring_b : ring_a;
+                    if (kt == -2) {
+#pragma unroll
+                      for (int i = 0; i < 4; ++i) av[4 * h + i] = 0.f;
+                    } else if (kt == -1 || inring) {
+                      float t4[4];
+                      load4f(h ? pb : pa, t4);
+#pragma unroll
+                      for (int i = 0; i < 4; ++i) av[4 * h + i] = t4[i];
+                    } else {
+#pragma unroll
+                      for (int i = 0; i < 4; ++i) {
+                        const int key = 16 * kt + 4 * g4 + i;
+                        av[4 * h + i] = (key < L) ? to_f(Vh[(size_t)key * D + dv0 + dvl]) : 0.f;
+                      }
+                    }
+                  }
+                  af = frag_from<T>(av);
+                }
+                ywin[dt] = mma(af, bf, ywin[dt]);
+              }
             }
           }
         }
@@ -638,21 +851,43 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
           }
         }
       }  // g
+      // next chunk's first query head in flight during the state update
+      if (c + 1 < c_end) {
+        const int pn = pos + CH;
+        const T *Q0 = Qbase + ((size_t)b * p.Hq + kvh * G) * (size_t)L * D;
+#pragma unroll
+        for (int j = 0; j < KS; ++j) pfq[j] = (pn < L) ? load8(Q0 + (size_t)pn * D + 32 * j + 8 * g4) : frag_zero<T>();
+      }
     }
-    __syncthreads();  // B3: all reads of the state copy and this chunk's keys done
+    __syncthreads();  // B3: all reads of the state copy done
 
-    // ---- state update on owned rows: S = diag(e^{btot}) S + KSt^T V
+    // ---- state update on owned rows: S = diag(prod_J e^{tot_J}) S + sum_s KSt[s] v_s^T with
+    //      KSt[s][f] = ko[s][f] prod_{J' > J(s)} e^{tot_J'}[f] gathered from LDS
 #pragma unroll
     for (int ft = 0; ft < FTW; ++ft) {
       const int fr = 16 * (wv * FTW + ft);
-      float e[4];
+      float e[4] = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int f = fr + 4 * g4 + i;
-        float s = 0.f;
+      for (int J = 0; J < 4; ++J) {
+        const f32x4 t = *reinterpret_cast<const f32x4 *>(sETot + J * D + fr + 4 * g4);
 #pragma unroll
-        for (int J = 0; J < 4; ++J) s += sTot[J * D + f];
-        e[i] = __expf(s);
+        for (int i = 0; i < 4; ++i) e[i] *= t[i];
+      }
+      float et[4];
+#pragma unroll
+      for (int J = 0; J < 4; ++J) et[J] = sETot[J * D + fr + r16];
+      Frag<T> ka[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int J = 2 * ks + (g4 >> 1);  // rows 32ks + 8g4 .. +7 lie in sub-chunk J
+        float fac = 1.f;
+#pragma unroll
+        for (int J2 = 1; J2 < 4; ++J2)
+          if (J2 > J) fac *= et[J2];
+        float x[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) x[jj] = to_f(sKown[(32 * ks + 8 * g4 + jj) * LDW + fr + r16]) * fac;
+        ka[ks] = frag_from<T>(x);
       }
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
@@ -660,8 +895,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
         for (int i = 0; i < 4; ++i) S[ft][dt][i] *= e[i];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-          S[ft][dt] = mma(load8(sKSt + (fr + r16) * LDC + 32 * ks + 8 * g4),
-                          load8(sVt + cur + (16 * dt + r16) * LDC + 32 * ks + 8 * g4), S[ft][dt]);
+          S[ft][dt] = mma(ka[ks], load8(sVt + cur + (16 * dt + r16) * LDC + 32 * ks + 8 * g4), S[ft][dt]);
         if constexpr (!STATE_ONLY)
           store4<T>(sSbf + (16 * dt + r16) * LDW + fr + 4 * g4, S[ft][dt][0], S[ft][dt][1], S[ft][dt][2],
                     S[ft][dt][3]);
@@ -677,39 +911,65 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
         *reinterpret_cast<f32x4 *>(E + (((size_t)(wv * FTW + ft) * NDT + dt) * 64 + lane) * 4) = S[ft][dt];
-    if (dvb == 0 && tid < D) p.ws_decay[(((size_t)b * p.Hkv + kvh) * (p.nseg - 1) + seg) * D + tid] = dsum;
+    // thread tid accumulated features tid % D for sub-chunks of its quarter/half; combine
+    __shared__ float sDs[256];
+    sDs[tid] = dsum;
+    __syncthreads();
+    if (dvb == 0 && tid < D) {
+      float s = 0.f;
+      for (int h = 0; h < 256 / D; ++h) s += sDs[tid + h * D];
+      p.ws_decay[(((size_t)b * p.Hkv + kvh) * (p.nseg - 1) + seg) * D + tid] = s;
+    }
   }
 }
 
 // ---------------------------------------------------------------- host side
-template <typename T, int D, int DV, int NR>
-static hipError_t launch_fwd_t(const FwdParams &prm, int nseg, hipStream_t stream) {
-  FwdParams p = prm;
-  if (nseg > 1) {
-    p.ngroups = p.B * p.Hkv * (nseg - 1);
-    const int grid = ((p.ngroups + 7) / 8) * 8 * p.ndvb;
-    hipLaunchKernelGGL((fwd_kernel<T, D, DV, 1, true>), dim3(grid), dim3(256), 0, stream, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  p.ngroups = p.B * p.Hkv * nseg;
+template <typename T, int D, int DV, bool STATE_ONLY>
+static hipError_t launch_one(const FwdParams &p, hipStream_t stream) {
   const int grid = ((p.ngroups + 7) / 8) * 8 * p.ndvb;
-  hipLaunchKernelGGL((fwd_kernel<T, D, DV, NR, false>), dim3(grid), dim3(256), 0, stream, p);
+  auto kern = fwd_kernel<T, D, DV, STATE_ONLY>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, p.lds.total);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), p.lds.total, stream, p);
   return hipGetLastError();
 }
 
 template <typename T, int D, int DV>
-static hipError_t launch_fwd_nr(const FwdParams &p, int nseg, hipStream_t stream) {
-  if (p.nring <= 2) return launch_fwd_t<T, D, DV, 2>(p, nseg, stream);
-  return launch_fwd_t<T, D, DV, 3>(p, nseg, stream);
+static hipError_t launch_fwd_t(const FwdParams &prm, hipStream_t stream) {
+  FwdParams p = prm;
+  const bool shared_w = (p.wq == p.wk) && p.w_stride == 0;
+  if (p.nseg > 1) {
+    FwdParams s = p;
+    s.ngroups = p.B * p.Hkv * (p.nseg - 1);
+    s.nring = 1;
+    s.kring = 1;
+    s.lds = make_lds<T, D, DV>(true, shared_w, 1, 1);
+    hipError_t e = launch_one<T, D, DV, true>(s, stream);
+    if (e != hipSuccess) return e;
+  }
+  p.ngroups = p.B * p.Hkv * p.nseg;
+  // deepest value / key rings that fit; tiles older than a ring are read from global memory
+  bool fit = false;
+  for (int nr = p.nring; nr >= 2 && !fit; --nr)
+    for (int kr = nr; kr >= 1 && !fit; --kr) {
+      p.lds = make_lds<T, D, DV>(false, shared_w, nr, kr);
+      if (p.lds.total <= LDS_LIMIT) {
+        p.nring = nr;
+        p.kring = kr;
+        fit = true;
+      }
+    }
+  if (!fit) return hipErrorInvalidConfiguration;
+  return launch_one<T, D, DV, false>(p, stream);
 }
 
 hipError_t launch_fwd(const FwdParams &p, int dtype_bf16, int d, hipStream_t stream) {
   if (dtype_bf16) {
-    if (d == 64) return launch_fwd_nr<bf16, 64, 64>(p, p.nseg, stream);
-    if (d == 128) return launch_fwd_nr<bf16, 128, 64>(p, p.nseg, stream);
+    if (d == 64) return launch_fwd_t<bf16, 64, 64>(p, stream);
+    if (d == 128) return launch_fwd_t<bf16, 128, 64>(p, stream);
   } else {
-    if (d == 64) return launch_fwd_nr<float, 64, 64>(p, p.nseg, stream);
+    if (d == 64) return launch_fwd_t<float, 64, 64>(p, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -5,6 +5,11 @@
 
 namespace lz {
 
+// Byte offsets of the forward kernel's LDS regions (dynamic shared memory).
+struct FwdLds {
+  int wk, wq, vt, kr, kown, tot, p7, etot, enp7, enr8, sbf, tvt, tk, total;
+};
+
 struct FwdParams {
   const void *q, *k, *v, *lg, *wq, *wk, *tk, *tv;
   void *out;
@@ -12,7 +17,8 @@ struct FwdParams {
   float *ws_decay;  // per-segment sums of log gamma, [B][Hkv][nseg-1][d]
   int64_t w_stride;
   int B, Hq, Hkv, L, W, M, G;
-  int nchunks, nseg, cps, ndvb, nring, ngroups;
+  int nchunks, nseg, cps, ndvb, nring, kring, ngroups;
+  FwdLds lds;
   int per_head_q;
   float mix, scale;
 };

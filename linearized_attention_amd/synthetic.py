@@ -91,8 +91,11 @@ class FwdInputs:
                 self.t_k, self.t_v)
 
     def to(self, device) -> "FwdInputs":
-        return FwdInputs(*[t.to(device) for t in self.tensors()], W=self.W, M=self.M,
-                         mix=self.mix, scale=self.scale, extra=self.extra)
+        """Copy to `device`; a W_phi shared by both sides stays one tensor."""
+        moved = [t.to(device) for t in self.tensors()]
+        if self.w_phi_k is self.w_phi_q:
+            moved[5] = moved[4]
+        return FwdInputs(*moved, W=self.W, M=self.M, mix=self.mix, scale=self.scale, extra=self.extra)
 
 
 def make_fwd_inputs(*, B: int, Hq: int, Hkv: int, L: int, d: int, W: int, M: int,

@@ -81,6 +81,9 @@ SMALL = [
     ("bf16 gqa 4:2 shared W", dict(B=2, Hq=4, Hkv=2, L=150, d=128, W=64, M=4), "bf16"),
     ("fp32 gqa 6:2 per-head W", dict(B=1, Hq=6, Hkv=2, L=140, d=64, W=32, M=4, per_head_w=True,
                                      separate_wk=True), "f32"),
+    ("bf16 separate W, W128 (value/key tiles past the LDS rings)", dict(B=1, Hq=2, Hkv=2, L=300, d=128,
+                                                                      W=128, M=8, gate="uniform",
+                                                                      separate_wk=True), "bf16"),
     ("bf16 per-head W G1", dict(B=1, Hq=2, Hkv=2, L=100, d=128, W=64, M=4, per_head_w=True,
                                 separate_wk=True), "bf16"),
 ]
