@@ -262,6 +262,23 @@ __device__ __forceinline__ void feature_logits(const T *sW, const Frag<T> (&xf)[
   }
 }
 
+// Same for two inputs against one W (each W fragment read once, two MFMA chains).
+template <typename T, int D, int LDW>
+__device__ __forceinline__ void feature_logits2(const T *sW, const Frag<T> (&xa)[D / 32], const Frag<T> (&xb)[D / 32],
+                                                int r16, int g4, f32x4 (&za)[D / 16], f32x4 (&zb)[D / 16]) {
+#pragma unroll
+  for (int ft = 0; ft < D / 16; ++ft) {
+    za[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+    zb[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) {
+      const Frag<T> w = load8(sW + (16 * ft + r16) * LDW + 32 * j + 8 * g4);
+      za[ft] = mma(w, xa[j], za[ft]);
+      zb[ft] = mma(w, xb[j], zb[ft]);
+    }
+  }
+}
+
 template <typename T, int D, int DV, bool STATE_ONLY>
 __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   using Gm = FwdGeom<T, D, DV>;
@@ -380,6 +397,17 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   const int I = wv;  // sub-chunk owned by this wave
   const float mix = p.mix, scale = p.scale;
   const bool win_fast = (p.W <= CH + 1) && KR >= 2 && NR >= 2;
+  // fast window: bit 4u+i set when slot (tile u, row 4 g4 + i) is inside the window of this
+  // lane's query (u = 0 meta; band tile u: kj - pos = 16u - 80 + 4 g4 + i - r16)
+  uint32_t wmask = 0;
+#pragma unroll
+  for (int u = 0; u < 6; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int dk = 16 * u - 80 + 4 * g4 + i - r16;
+      const bool in = (u == 0) ? (4 * g4 + i < p.M) : (dk <= 0 && dk > -p.W);
+      wmask |= (in ? 1u : 0u) << (4 * u + i);
+    }
   const Frag<T> tri_pre = tri_frag<T>(r16, g4, true);
   const Frag<T> tri_suf = tri_frag<T>(r16, g4, false);
 
@@ -419,8 +447,11 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int j = 0; j < KS; ++j) qf[j] = pfq[j];
     }
-    // ---- next chunk in flight during this one
-    if (c + 1 < c_end) load_chunk<T, D, DV>(pf, Kh, Vh, LGh, c0 + CH, L, dv0, true);
+    // ---- state-only variant: next chunk in flight during this one (the full kernel issues
+    //      it after the query loop, where fewer registers are live)
+    if constexpr (STATE_ONLY) {
+      if (c + 1 < c_end) load_chunk<T, D, DV>(pf, Kh, Vh, LGh, c0 + CH, L, dv0, true);
+    }
     __syncthreads();  // B0: this chunk in LDS
 
     const int pos = c0 + 16 * I + r16;
@@ -443,14 +474,31 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
         *reinterpret_cast<f32x4 *>(dst + 16 * ft) = f32x4{pfx[ft][0], pfx[ft][1], pfx[ft][2], pfx[ft][3]};
     }
 
-    // ---- phi_k for own rows; keys decayed to the sub-chunk end
+    // ---- phi_k for own rows (keys decayed to the sub-chunk end); phi_q of the first query
+    //      head (queries decayed from the sub-chunk start), sharing W reads when W_phi is shared
     float ko[NFT][4];
+    float qo[NFT][4];
     {
       Frag<T> kf[KS];
 #pragma unroll
       for (int j = 0; j < KS; ++j) kf[j] = load8(sKr + kcur + (16 * I + r16) * LDW + 32 * j + 8 * g4);
       f32x4 z[NFT];
-      feature_logits<T, D, LDW>(sWk, kf, r16, g4, z);
+      if constexpr (STATE_ONLY) {
+        feature_logits<T, D, LDW>(sWk, kf, r16, g4, z);
+      } else {
+        f32x4 zq[NFT];
+        if (ly.wq == ly.wk) {
+          feature_logits2<T, D, LDW>(sWk, kf, qf, r16, g4, z, zq);
+        } else {
+          feature_logits<T, D, LDW>(sWk, kf, r16, g4, z);
+          feature_logits<T, D, LDW>(sWq, qf, r16, g4, zq);
+        }
+        softmax_rows<NFT>(zq, qo);
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) qo[ft][i] *= __expf(pfx[ft][i]);
+      }
       softmax_rows<NFT>(z, ko);
 #pragma unroll
       for (int ft = 0; ft < NFT; ++ft)
@@ -514,14 +562,10 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
         }
         const T *Qh = Qbase + ((size_t)b * p.Hq + hq) * (size_t)L * D;
         if (g > 0) {
+          // later query heads: phi_q here, qo = phi_q e^{prefix} (<= 1)
 #pragma unroll
           for (int j = 0; j < KS; ++j)
             qf[j] = valid ? load8(Qh + (size_t)pos * D + 32 * j + 8 * g4) : frag_zero<T>();
-        }
-
-        // phi_q for own rows, then qo = phi_q e^{prefix} (<= 1)
-        float qo[NFT][4];
-        {
           f32x4 z[NFT];
           feature_logits<T, D, LDW>(sWq, qf, r16, g4, z);
           softmax_rows<NFT>(z, qo);
@@ -671,7 +715,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
 #pragma unroll
             for (int j = 0; j < KS; ++j) acc = mma(load8(sTk + r16 * LDW + 32 * j + 8 * g4), qf[j], acc);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) lt[0][i] = (4 * g4 + i < p.M) ? acc[i] * scale : NEG_BIG;
+            for (int i = 0; i < 4; ++i) lt[0][i] = ((wmask >> i) & 1u) ? acc[i] * scale : NEG_BIG;
           }
 #pragma unroll
           for (int u = 1; u < 6; ++u) {
@@ -680,12 +724,9 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < KS; ++j) acc = mma(load8(kr + 32 * j), qf[j], acc);
-            const bool before_start = (c == 0) && rt < 0;
+            const uint32_t mu = ((c == 0) && rt < 0) ? 0u : (wmask >> (4 * u));  // no keys before 0
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int dk = 16 * u - 80 + 4 * g4 + i - r16;
-              lt[u][i] = (!before_start && dk <= 0 && dk > -p.W) ? acc[i] * scale : NEG_BIG;
-            }
+            for (int i = 0; i < 4; ++i) lt[u][i] = ((mu >> i) & 1u) ? acc[i] * scale : NEG_BIG;
           }
           float bm = NEG_BIG;
 #pragma unroll
@@ -851,8 +892,9 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
           }
         }
       }  // g
-      // next chunk's first query head in flight during the state update
+      // next chunk's keys, values, log gamma and first query head in flight during the state update
       if (c + 1 < c_end) {
+        load_chunk<T, D, DV>(pf, Kh, Vh, LGh, c0 + CH, L, dv0, true);
         const int pn = pos + CH;
         const T *Q0 = Qbase + ((size_t)b * p.Hq + kvh * G) * (size_t)L * D;
 #pragma unroll
