@@ -11,46 +11,45 @@
 //   y_win = softmax over M meta keys + min(pos+1, W) ring keys
 //   out = mix y_gla + (1-mix) y_win
 // The step is bound by HBM traffic on the state (2*d*d*4 bytes per (sequence,
-// head), read and written once).  Each thread streams its rows of float4
-// columns with all loads issued before any use.  Workgroup: 256 threads for
-// DEC_NS sequences of one key/value head, so the feature-map weights are read
-// once per DEC_NS sequences.  The position counter is advanced by a separate
-// kernel once every head has read it.
+// head), read and written once) and the ring (2*W*d elements read).  One
+// workgroup per (sequence, key/value head).  Every independent load is issued
+// at the top -- the thread's rows of the state, its 16-byte pieces of the ring
+// keys and values -- so the whole step costs about one memory round trip; the
+// feature maps (W_phi from L2, one pass for phi_k and all phi_q) run while
+// those loads are in flight.  Partial sums are reduced inside each wave with
+// shuffles before meeting in LDS.  The position counter is advanced by a
+// separate kernel once every head has read it.
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace lz {
 
-constexpr int DEC_NS = 4;     // sequences per workgroup
-constexpr int DEC_MAXG = 4;   // query heads per key/value head per pass
-constexpr int DEC_MAXW = 256; // ring length limit (logit buffer)
+constexpr int DEC_MAXG = 4;   // query heads per key/value head per pass (grouped heads)
+constexpr int DEC_MAXW = 256; // ring length limit
 constexpr int DEC_MAXM = 16;
+constexpr int DEC_RKEYS = 64; // ring keys per logits pass (4 lanes per key)
 constexpr float DEC_NEG = -1.0e30f;
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void decode_kernel(DecParams p) {
+template <typename T, int D, int GM>  // GM: query heads per pass (1 or DEC_MAXG)
+__global__ __launch_bounds__(256, 2) void decode_kernel(DecParams p) {
   constexpr int C4 = D / 4;     // float4 columns per state row
-  constexpr int RG = 256 / C4;  // row groups
-  constexpr int RPT = D / RG;   // rows per thread
-  constexpr int NPART = 256 / D;
+  constexpr int RG = 256 / C4;  // row groups of the state
+  constexpr int RPT = D / RG;   // state rows per thread
+  constexpr int F8 = D / 8;     // 8-column pieces of a row
+  constexpr int JG = 256 / F8;  // key / row groups for 8-column work
+  constexpr int QD = D / 4;     // quarter row (window logits: 4 lanes per key)
+  constexpr int NV = GM + 1;
+  constexpr int VPT = DEC_RKEYS / JG;  // value pieces per thread loaded up front
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int G = p.G, Hq = p.Hq, Hkv = p.Hkv, W = p.W, M = p.M;
-  const int nblk = (p.N + DEC_NS - 1) / DEC_NS;
-  const int hk = blockIdx.x / nblk;
-  const int n0 = (blockIdx.x % nblk) * DEC_NS;
-  const int ns = min(DEC_NS, p.N - n0);
+  const int n = blockIdx.x / Hkv, hk = blockIdx.x % Hkv;
+  const size_t nh = (size_t)n * Hkv + hk;
 
-  __shared__ float sq[DEC_NS][DEC_MAXG][D];    // raw queries
-  __shared__ float sphq[DEC_NS][DEC_MAXG][D];  // phi_q
-  __shared__ float skr[DEC_NS][D];             // raw key
-  __shared__ float sphk[DEC_NS][D];            // phi_k
-  __shared__ float sgam[DEC_NS][D];
-  __shared__ float sv[DEC_NS][D];
-  __shared__ float sy[RG][DEC_MAXG][D];        // partial y_gla per row group
-  __shared__ float sygla[DEC_MAXG][D];
-  __shared__ float slog[DEC_MAXG][DEC_MAXM + DEC_MAXW];
-  __shared__ float sred[NPART][DEC_MAXG][D];
-  __shared__ int spos[DEC_NS];
+  __shared__ float sx[NV][D];        // queries (0..3) and the raw key (4); later y_win per head
+  __shared__ float sphi[NV][D];      // phi_q per head, phi_k
+  __shared__ float sgam[D], sv[D];
+  __shared__ float sred[4][NV][D];   // per-wave partial sums (feature maps, y_win, y_gla)
+  __shared__ float slog[GM][DEC_MAXM + DEC_MAXW];
 
   const T *Q = reinterpret_cast<const T *>(p.q);
   const T *K = reinterpret_cast<const T *>(p.k);
@@ -63,229 +62,303 @@ __global__ __launch_bounds__(256) void decode_kernel(DecParams p) {
   T *RK = reinterpret_cast<T *>(p.win_k);
   T *RV = reinterpret_cast<T *>(p.win_v);
   T *OUT = reinterpret_cast<T *>(p.out);
+  const bool shared_w = (p.wq == p.wk) && p.w_stride == 0;
 
-  if (tid < DEC_NS) spos[tid] = (tid < ns) ? p.pos[n0 + tid] : 0;
-  for (int idx = tid; idx < DEC_NS * D; idx += 256) {
-    const int s = idx / D, e = idx % D;
-    float kk = 0.f, gm = 1.f, vv = 0.f;
-    if (s < ns) {
-      const size_t o = ((size_t)(n0 + s) * Hkv + hk) * D + e;
-      kk = to_f(K[o]);
-      gm = __expf(to_f(LG[o]));
-      vv = to_f(V[o]);
-    }
-    skr[s][e] = kk;
-    sgam[s][e] = gm;
-    sv[s][e] = vv;
+  const int pn = p.pos[n];
+  const int slot = pn % W;
+  const int nvalid = min(pn + 1, W);
+  const size_t rbase = nh * (size_t)W * D;
+  float *St = p.state + nh * D * D;
+  const int c4 = tid % C4, rg = tid / C4;
+
+  // ---- loads in flight from here on: state rows, ring key quarter, ring value pieces
+  f32x4 x[RPT];
+#pragma unroll
+  for (int rr = 0; rr < RPT; ++rr)
+    x[rr] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(St + (size_t)(rg + RG * rr) * D + 4 * c4));
+  const int kq = tid / 4, kpart = tid % 4;  // ring slot kq (+ multiples of 64), dims kpart*QD ..
+  Frag<T> kfr[QD / 8];
+#pragma unroll
+  for (int e8 = 0; e8 < QD / 8; ++e8)
+    kfr[e8] = (kq < W) ? load8(RK + rbase + (size_t)kq * D + kpart * QD + 8 * e8) : frag_zero<T>();
+  const int f8 = tid % F8, jg = tid / F8;   // value columns 8*f8 .., ring slots jg, jg+JG, ...
+  Frag<T> vfr[VPT];
+#pragma unroll
+  for (int m = 0; m < VPT; ++m) {
+    const int j = jg + JG * m;
+    vfr[m] = (j < W) ? load8(RV + rbase + (size_t)j * D + 8 * f8) : frag_zero<T>();
   }
 
-  for (int g0 = 0; g0 < G; g0 += DEC_MAXG) {
-    const int gp = min(DEC_MAXG, G - g0);
+  for (int e = tid; e < D; e += 256) {
+    const size_t o = nh * D + e;
+    sx[GM][e] = to_f(K[o]);
+    sgam[e] = __expf(to_f(LG[o]));
+    sv[e] = to_f(V[o]);
+  }
+
+  for (int g0 = 0; g0 < G; g0 += GM) {
+    const int gp = min(GM, G - g0);
     const bool first = (g0 == 0);
-    for (int idx = tid; idx < DEC_NS * DEC_MAXG * D; idx += 256) {
-      const int s = idx / (DEC_MAXG * D), u = (idx / D) % DEC_MAXG, e = idx % D;
-      float x = 0.f;
-      if (s < ns && u < gp) x = to_f(Q[((size_t)(n0 + s) * Hq + hk * G + g0 + u) * D + e]);
-      sq[s][u][e] = x;
+    for (int idx = tid; idx < GM * D; idx += 256) {
+      const int u = idx / D, e = idx % D;
+      sx[u][e] = (u < gp) ? to_f(Q[((size_t)n * Hq + hk * G + g0 + u) * D + e]) : 0.f;
     }
     __syncthreads();
-    // ---- feature maps z = x W; job 0 = key side (first pass), job 1 + u = query head u
+
+    // ---- feature maps: z[v][f] = sum_i x_v[i] W[i][f]; thread (f8, jg) sums rows jg, jg+JG, ...
     {
-      const int f = tid % D, part = tid / D;
-      for (int job = part; job < 1 + gp; job += NPART) {
-        if (job == 0 && !first) continue;
-        float z[DEC_NS];
+      float z[NV][8];
 #pragma unroll
-        for (int s = 0; s < DEC_NS; ++s) z[s] = 0.f;
-        if (job == 0) {
-          for (int i = 0; i < D; ++i) {
-            const float w = to_f(Wk[(size_t)i * D + f]);
+      for (int v = 0; v < NV; ++v)
 #pragma unroll
-            for (int s = 0; s < DEC_NS; ++s) z[s] += skr[s][i] * w;
+        for (int j = 0; j < 8; ++j) z[v][j] = 0.f;
+#pragma unroll 2
+      for (int i = jg; i < D; i += JG) {
+        float wk8[8];
+        if (first) {
+          load8f(Wk + (size_t)i * D + 8 * f8, wk8);
+          const float xi = sx[GM][i];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) z[GM][j] += xi * wk8[j];
+        }
+#pragma unroll
+        for (int u = 0; u < GM; ++u) {
+          if (u < gp) {
+            float w8[8];
+            if (shared_w && first) {
+#pragma unroll
+              for (int j = 0; j < 8; ++j) w8[j] = wk8[j];
+            } else {
+              load8f(Wq + (size_t)(hk * G + g0 + u) * p.w_stride + (size_t)i * D + 8 * f8, w8);
+            }
+            const float xi = sx[u][i];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) z[u][j] += xi * w8[j];
           }
-#pragma unroll
-          for (int s = 0; s < DEC_NS; ++s) sphk[s][f] = z[s];
-        } else {
-          const int u = job - 1;
-          const T *Wm = Wq + (size_t)(hk * G + g0 + u) * p.w_stride;
-          for (int i = 0; i < D; ++i) {
-            const float w = to_f(Wm[(size_t)i * D + f]);
-#pragma unroll
-            for (int s = 0; s < DEC_NS; ++s) z[s] += sq[s][u][i] * w;
-          }
-#pragma unroll
-          for (int s = 0; s < DEC_NS; ++s) sphq[s][u][f] = z[s];
         }
       }
+      // the 64/F8 row groups of a wave, then the 4 waves in LDS
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int o = F8; o < 64; o <<= 1) z[v][j] += __shfl_xor(z[v][j], o);
+      if (lane < F8) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sred[wv][v][8 * f8 + j] = z[v][j];
+      }
+      __syncthreads();
+      // softmax over features: wave w handles vectors w, w+4
+      for (int v = wv; v < NV; v += 4) {
+        if (v == GM ? !first : v >= gp) continue;
+        float zz[D / 64];
+        float m = DEC_NEG;
+#pragma unroll
+        for (int q = 0; q < D / 64; ++q) {
+          const int f = lane + 64 * q;
+          zz[q] = sred[0][v][f] + sred[1][v][f] + sred[2][v][f] + sred[3][v][f];
+          m = fmaxf(m, zz[q]);
+        }
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+        float s = 0.f;
+#pragma unroll
+        for (int q = 0; q < D / 64; ++q) {
+          zz[q] = __expf(zz[q] - m);
+          s += zz[q];
+        }
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o);
+        const float inv = 1.f / s;
+#pragma unroll
+        for (int q = 0; q < D / 64; ++q) sphi[v][lane + 64 * q] = zz[q] * inv;
+      }
+    }
+
+    // ---- window logits over ring slots: slot jb + kq, quarter kpart (first pass from registers)
+    for (int jb = 0; jb < W; jb += DEC_RKEYS) {
+      const int jj = jb + kq;
+      const bool in = jj < W;
+      const int age = in ? ((slot - jj) % W + W) % W : W;  // pn - (token in slot jj)
+      const bool ok = in && age < nvalid;
+      float acc[GM];
+#pragma unroll
+      for (int u = 0; u < GM; ++u) acc[u] = 0.f;
+      if (ok) {
+#pragma unroll
+        for (int e8 = 0; e8 < QD / 8; ++e8) {
+          const int e0 = kpart * QD + 8 * e8;
+          float kv8[8];
+          if (jj == slot) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) kv8[t] = sx[GM][e0 + t];
+          } else if (jb == 0) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) kv8[t] = to_f(kfr[e8].v[t]);
+          } else {
+            load8f(RK + rbase + (size_t)jj * D + e0, kv8);
+          }
+#pragma unroll
+          for (int u = 0; u < GM; ++u)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) acc[u] += sx[u][e0 + t] * kv8[t];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < GM; ++u) {
+        acc[u] += __shfl_xor(acc[u], 1);
+        acc[u] += __shfl_xor(acc[u], 2);
+      }
+      if (in && kpart == 0)
+        for (int u = 0; u < gp; ++u) slog[u][M + jj] = ok ? acc[u] * p.scale : DEC_NEG;
+    }
+    // meta keys: thread (u, m), full dot product (T_k from L2)
+    for (int idx = tid; idx < gp * M; idx += 256) {
+      const int u = idx / M, m = idx % M;
+      const T *kr = Tk + ((size_t)hk * M + m) * D;
+      float a = 0.f;
+      for (int e8 = 0; e8 < D; e8 += 8) {
+        float kv8[8];
+        load8f(kr + e8, kv8);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) a += sx[u][e8 + t] * kv8[t];
+      }
+      slog[u][m] = a * p.scale;
     }
     __syncthreads();
-    // softmax over features, one wave per vector
-    for (int vec = wv; vec < DEC_NS * (1 + DEC_MAXG); vec += 4) {
-      const int s = vec / (1 + DEC_MAXG), u = vec % (1 + DEC_MAXG);
-      if (u == 0 ? !first : (u - 1) >= gp) continue;
-      float *row = (u == 0) ? sphk[s] : sphq[s][u - 1];
+    // softmax per head (one wave per head)
+    for (int u = wv; u < gp; u += 4) {
       float m = DEC_NEG;
-      for (int e = lane; e < D; e += 64) m = fmaxf(m, row[e]);
+      for (int j = lane; j < M + W; j += 64) m = fmaxf(m, slog[u][j]);
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
       float sum = 0.f;
-      for (int e = lane; e < D; e += 64) sum += __expf(row[e] - m);
+      for (int j = lane; j < M + W; j += 64) {
+        const float ex = __expf(slog[u][j] - m);  // masked entries: exp(-1e30) = 0
+        slog[u][j] = ex;
+        sum += ex;
+      }
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) sum += __shfl_xor(sum, o);
       const float inv = 1.f / sum;
-      for (int e = lane; e < D; e += 64) row[e] = __expf(row[e] - m) * inv;
+      for (int j = lane; j < M + W; j += 64) slog[u][j] *= inv;
     }
     __syncthreads();
 
-    for (int s = 0; s < ns; ++s) {
-      const int n = n0 + s;
-      const int pn = spos[s];
-      const int slot = pn % W;
-      const size_t nh = (size_t)n * Hkv + hk;
-      const size_t rbase = nh * (size_t)W * D;
-      // ---- state stream: S = diag(gamma) S + phi_k v^T (first pass), partial y = phi_q^T S
-      {
-        float *St = p.state + nh * D * D;
-        const int c4 = tid % C4, rg = tid / C4;
-        f32x4 x[RPT];
+    // ---- y_win over ring slots: thread (f8, jg) sums slots jg, jg+JG, ... for columns 8*f8 ..
+    {
+      float acc[GM][8];
 #pragma unroll
-        for (int rr = 0; rr < RPT; ++rr)
-          x[rr] = *reinterpret_cast<const f32x4 *>(St + (size_t)(rg + RG * rr) * D + 4 * c4);
-        if (first) {
-          const float v0 = sv[s][4 * c4], v1 = sv[s][4 * c4 + 1], v2 = sv[s][4 * c4 + 2], v3 = sv[s][4 * c4 + 3];
+      for (int u = 0; u < GM; ++u)
 #pragma unroll
-          for (int rr = 0; rr < RPT; ++rr) {
-            const int f = rg + RG * rr;
-            const float gm = sgam[s][f], pk = sphk[s][f];
-            x[rr][0] = gm * x[rr][0] + pk * v0;
-            x[rr][1] = gm * x[rr][1] + pk * v1;
-            x[rr][2] = gm * x[rr][2] + pk * v2;
-            x[rr][3] = gm * x[rr][3] + pk * v3;
-            *reinterpret_cast<f32x4 *>(St + (size_t)f * D + 4 * c4) = x[rr];
+        for (int t = 0; t < 8; ++t) acc[u][t] = 0.f;
+#pragma unroll
+      for (int m = 0; m < VPT; ++m) {  // slots whose values are already in registers
+        const int j = jg + JG * m;
+        if (j < W) {
+          float vv[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) vv[t] = (j == slot) ? sv[8 * f8 + t] : to_f(vfr[m].v[t]);
+#pragma unroll
+          for (int u = 0; u < GM; ++u) {
+            const float pj = slog[u][M + j];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) acc[u][t] += pj * vv[t];
           }
         }
-        for (int u = 0; u < gp; ++u) {
-          float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
-#pragma unroll
-          for (int rr = 0; rr < RPT; ++rr) {
-            const float pq = sphq[s][u][rg + RG * rr];
-            y0 += pq * x[rr][0];
-            y1 += pq * x[rr][1];
-            y2 += pq * x[rr][2];
-            y3 += pq * x[rr][3];
-          }
-          sy[rg][u][4 * c4] = y0;
-          sy[rg][u][4 * c4 + 1] = y1;
-          sy[rg][u][4 * c4 + 2] = y2;
-          sy[rg][u][4 * c4 + 3] = y3;
-        }
       }
-      // ---- window logits: 4 lanes per key, each a quarter of d; keys 0..M-1 meta, then ring slots
-      for (int jb = 0; jb < M + W; jb += 64) {
-        const int j = jb + tid / 4, part = tid % 4;
-        const bool in = j < M + W;
-        bool ok = false;
-        const T *kr = nullptr;
-        const float *kl = nullptr;
-        if (in) {
-          if (j < M) {
-            ok = true;
-            kr = Tk + ((size_t)hk * M + j) * D;
-          } else {
-            const int jj = j - M;
-            const int age = ((slot - jj) % W + W) % W;  // pn - (token in slot jj)
-            ok = age <= pn;
-            if (jj == slot) kl = skr[s];
-            else kr = RK + rbase + (size_t)jj * D;
-          }
-        }
-        float acc[DEC_MAXG];
+      for (int j = jg + JG * VPT; j < W; j += JG) {  // longer rings
+        float vv[8];
+        if (j == slot) {
 #pragma unroll
-        for (int u = 0; u < DEC_MAXG; ++u) acc[u] = 0.f;
-        if (ok) {
-          constexpr int QD = D / 4;
-#pragma unroll
-          for (int e8 = 0; e8 < QD; e8 += 8) {
-            float kv8[8];
-            const int e0 = part * QD + e8;
-            if (kl) {
-#pragma unroll
-              for (int t = 0; t < 8; ++t) kv8[t] = kl[e0 + t];
-            } else {
-              load8f(kr + e0, kv8);
-            }
-#pragma unroll
-            for (int u = 0; u < DEC_MAXG; ++u)
-#pragma unroll
-              for (int t = 0; t < 8; ++t) acc[u] += sq[s][u][e0 + t] * kv8[t];
-          }
+          for (int t = 0; t < 8; ++t) vv[t] = sv[8 * f8 + t];
+        } else {
+          load8f(RV + rbase + (size_t)j * D + 8 * f8, vv);
         }
 #pragma unroll
-        for (int u = 0; u < DEC_MAXG; ++u) {
-          acc[u] += __shfl_xor(acc[u], 1);
-          acc[u] += __shfl_xor(acc[u], 2);
+        for (int u = 0; u < GM; ++u) {
+          const float pj = slog[u][M + j];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) acc[u][t] += pj * vv[t];
         }
-        if (in && part == 0)
-          for (int u = 0; u < gp; ++u) slog[u][j] = ok ? acc[u] * p.scale : DEC_NEG;
       }
-      __syncthreads();
-      // reduce partial y_gla; softmax per head (one wave per head)
-      for (int idx = tid; idx < gp * D; idx += 256) {
-        const int u = idx / D, e = idx % D;
-        float a = 0.f;
 #pragma unroll
-        for (int r = 0; r < RG; ++r) a += sy[r][u][e];
-        sygla[u][e] = a;
+      for (int u = 0; u < GM; ++u)
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+          for (int o = F8; o < 64; o <<= 1) acc[u][t] += __shfl_xor(acc[u][t], o);
+      if (lane < F8) {
+#pragma unroll
+        for (int u = 0; u < GM; ++u)
+#pragma unroll
+          for (int t = 0; t < 8; ++t) sred[wv][u][8 * f8 + t] = acc[u][t];
       }
-      for (int u = wv; u < gp; u += 4) {
-        float m = DEC_NEG;
-        for (int j = lane; j < M + W; j += 64) m = fmaxf(m, slog[u][j]);
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-        float sum = 0.f;
-        for (int j = lane; j < M + W; j += 64) {
-          const float l = slog[u][j];
-          const float ex = (l > 0.5f * DEC_NEG) ? __expf(l - m) : 0.f;
-          slog[u][j] = ex;
-          sum += ex;
-        }
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) sum += __shfl_xor(sum, o);
-        const float inv = 1.f / sum;
-        for (int j = lane; j < M + W; j += 64) slog[u][j] *= inv;
-      }
-      __syncthreads();
-      // ---- y_win = P [T_v ; ring V]: thread (e, part) sums keys j = part (mod NPART)
-      {
-        const int e = tid % D, part = tid / D;
-        float acc[DEC_MAXG];
-#pragma unroll
-        for (int u = 0; u < DEC_MAXG; ++u) acc[u] = 0.f;
-        for (int j = part; j < M + W; j += NPART) {
-          float vv;
-          if (j < M) vv = to_f(Tv[((size_t)hk * M + j) * D + e]);
-          else if (j - M == slot) vv = sv[s][e];
-          else vv = to_f(RV[rbase + (size_t)(j - M) * D + e]);
-#pragma unroll
-          for (int u = 0; u < DEC_MAXG; ++u) acc[u] += slog[u][j] * vv;
-        }
-        for (int u = 0; u < gp; ++u) sred[part][u][e] = acc[u];
-      }
-      __syncthreads();
-      for (int idx = tid; idx < gp * D; idx += 256) {
-        const int u = idx / D, e = idx % D;
-        float a = 0.f;
-#pragma unroll
-        for (int pp = 0; pp < NPART; ++pp) a += sred[pp][u][e];
-        const float y = p.mix * sygla[u][e] + (1.f - p.mix) * a;
-        OUT[((size_t)n * Hq + hk * G + g0 + u) * D + e] = from_f<T>(y);
-      }
-      if (first && tid < D) {
-        RK[rbase + (size_t)slot * D + tid] = from_f<T>(skr[s][tid]);
-        RV[rbase + (size_t)slot * D + tid] = from_f<T>(sv[s][tid]);
-      }
-      __syncthreads();
     }
+
+    // ---- state: S = diag(gamma) S + phi_k v^T (first pass), partial y = phi_q^T S
+    if (first) {
+      const float v0 = sv[4 * c4], v1 = sv[4 * c4 + 1], v2 = sv[4 * c4 + 2], v3 = sv[4 * c4 + 3];
+#pragma unroll
+      for (int rr = 0; rr < RPT; ++rr) {
+        const int f = rg + RG * rr;
+        const float gm = sgam[f], pk = sphi[GM][f];
+        x[rr][0] = gm * x[rr][0] + pk * v0;
+        x[rr][1] = gm * x[rr][1] + pk * v1;
+        x[rr][2] = gm * x[rr][2] + pk * v2;
+        x[rr][3] = gm * x[rr][3] + pk * v3;
+        __builtin_nontemporal_store(x[rr], reinterpret_cast<f32x4 *>(St + (size_t)f * D + 4 * c4));
+      }
+    }
+    float yp[GM][4];
+#pragma unroll
+    for (int u = 0; u < GM; ++u) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) yp[u][i] = 0.f;
+      if (u < gp) {
+#pragma unroll
+        for (int rr = 0; rr < RPT; ++rr) {
+          const float pq = sphi[u][rg + RG * rr];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) yp[u][i] += pq * x[rr][i];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < GM; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int o = C4; o < 64; o <<= 1) yp[u][i] += __shfl_xor(yp[u][i], o);
+    __syncthreads();  // y_win partials complete
+    // y_win per head (ring part + meta values) -> sx (the raw queries are no longer needed)
+    for (int idx = tid; idx < gp * D; idx += 256) {
+      const int u = idx / D, e = idx % D;
+      float w = sred[0][u][e] + sred[1][u][e] + sred[2][u][e] + sred[3][u][e];
+      for (int m = 0; m < M; ++m) w += slog[u][m] * to_f(Tv[((size_t)hk * M + m) * D + e]);
+      sx[u][e] = w;
+    }
+    __syncthreads();
+    if (lane < C4) {
+#pragma unroll
+      for (int u = 0; u < GM; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sred[wv][u][4 * c4 + i] = yp[u][i];
+    }
+    __syncthreads();
+    for (int idx = tid; idx < gp * D; idx += 256) {
+      const int u = idx / D, e = idx % D;
+      const float a = sred[0][u][e] + sred[1][u][e] + sred[2][u][e] + sred[3][u][e];
+      OUT[((size_t)n * Hq + hk * G + g0 + u) * D + e] = from_f<T>(p.mix * a + (1.f - p.mix) * sx[u][e]);
+    }
+    __syncthreads();
+  }
+  if (tid < D) {
+    RK[rbase + (size_t)slot * D + tid] = K[nh * D + tid];
+    RV[rbase + (size_t)slot * D + tid] = V[nh * D + tid];
   }
 }
 
@@ -296,8 +369,10 @@ __global__ void decode_advance_pos(int32_t *pos, int N) {
 
 template <typename T, int D>
 static hipError_t launch_dec_t(const DecParams &p, hipStream_t stream) {
-  const int nblk = (p.N + DEC_NS - 1) / DEC_NS;
-  hipLaunchKernelGGL((decode_kernel<T, D>), dim3(nblk * p.Hkv), dim3(256), 0, stream, p);
+  if (p.G == 1)
+    hipLaunchKernelGGL((decode_kernel<T, D, 1>), dim3(p.N * p.Hkv), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_kernel<T, D, DEC_MAXG>), dim3(p.N * p.Hkv), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_advance_pos, dim3((p.N + 255) / 256), dim3(256), 0, stream, p.pos, p.N);
