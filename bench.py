@@ -124,13 +124,15 @@ def bench_decode(steps: int, warmup: int):
     w = [t.cuda() for t in (dec.w_phi_q, dec.w_phi_k, dec.t_k, dec.t_v)]
     xs = [tuple(t.cuda() for t in s) for s in dec.steps]
     out = torch.empty_like(xs[0][0])
+    wsb = api.lizard_attn_decode_workspace_bytes(c["N"], c["Hq"], c["Hkv"], c["d"], out.dtype)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     it = [0]
 
     def step():
         q, k, v, lg = xs[it[0] % len(xs)]
         it[0] += 1
         api.lizard_attn_decode(st, rk, rv, pos, q, k, v, lg, *w, M=dec.M, mix=dec.mix, scale=dec.scale,
-                               out=out)
+                               out=out, workspace=ws)
 
     for _ in range(warmup):
         step()

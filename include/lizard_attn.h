@@ -114,6 +114,12 @@ size_t lizard_attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int L, int d,
  *   then a softmax over the M meta keys and the min(pos+1, W) newest keys.
  *   Running L steps from a zero state, pos = 0, reproduces the forward on
  *   those L tokens.
+ *   workspace   device scratch of at least lizard_attn_decode_workspace_bytes()
+ *               bytes (16-byte aligned), clobbered: the step's feature maps
+ *               pass through it between its two kernels, with one counter per
+ *               sequence.
+ *   Calls on one stream run in order; calls on different streams that share
+ *   state, rings, pos or workspace race.
  */
 lizard_status lizard_attn_decode(float *state, void *win_k, void *win_v,
                                  int32_t *pos, const void *q, const void *k,
@@ -123,7 +129,13 @@ lizard_status lizard_attn_decode(float *state, void *win_k, void *win_v,
                                  const void *t_v, void *out, int N, int Hq,
                                  int Hkv, int d, int W, int M, float mix,
                                  float scale, lizard_dtype dtype,
+                                 void *workspace, size_t workspace_bytes,
                                  void *stream);
+
+/* Workspace bytes lizard_attn_decode needs: 4 * (N*Hkv*(1 + Hq/Hkv)*d + N);
+ * 0 for an empty or invalid shape. */
+size_t lizard_attn_decode_workspace_bytes(int N, int Hq, int Hkv, int d,
+                                          lizard_dtype dtype);
 
 /* Static text for a status code. */
 const char *lizard_status_string(lizard_status s);

@@ -24,7 +24,7 @@ _STATUS = {0: "LIZARD_OK", 1: "LIZARD_ERR_INVALID_ARG", 2: "LIZARD_ERR_UNSUPPORT
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
 EXPORTED = ("lizard_attn_fwd", "lizard_attn_fwd_workspace_bytes", "lizard_attn_decode",
-            "lizard_status_string", "lizard_last_error", "lizard_version")
+            "lizard_attn_decode_workspace_bytes", "lizard_status_string", "lizard_last_error", "lizard_version")
 
 _lock = threading.Lock()
 _lib = None
@@ -45,8 +45,10 @@ def _declare(lib):
     lib.lizard_attn_fwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.lizard_attn_fwd_workspace_bytes.restype = sz
     lib.lizard_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp,
-                                       i32, i32, i32, i32, i32, i32, f32, f32, i32, vp]
+                                       i32, i32, i32, i32, i32, i32, f32, f32, i32, vp, sz, vp]
     lib.lizard_attn_decode.restype = i32
+    lib.lizard_attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.lizard_attn_decode_workspace_bytes.restype = sz
     lib.lizard_status_string.argtypes = [i32]
     lib.lizard_status_string.restype = ctypes.c_char_p
     lib.lizard_last_error.argtypes = []
@@ -146,9 +148,13 @@ def lizard_attn_fwd(q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v, *, W: int, M
     return out
 
 
+def lizard_attn_decode_workspace_bytes(N: int, Hq: int, Hkv: int, d: int, dtype: torch.dtype) -> int:
+    return int(load().lizard_attn_decode_workspace_bytes(N, Hq, Hkv, d, _DTYPES[dtype]))
+
+
 def lizard_attn_decode(state, win_k, win_v, pos, q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v,
                        *, M: int, mix: float = 0.5, scale: float | None = None, out=None,
-                       stream=None):
+                       workspace=None, stream=None):
     """One decode step, in place on state [N,Hkv,d,d] fp32, win_k/win_v [N,Hkv,W,d],
     pos [N] int32.  q [N,Hq,d]; k, v, log_gamma [N,Hkv,d].  Returns out [N,Hq,d]."""
     dt = q.dtype
@@ -175,11 +181,16 @@ def lizard_attn_decode(state, win_k, win_v, pos, q, k, v, log_gamma, w_phi_q, w_
         out = torch.empty_like(q)
     else:
         _dev(out, "out", dt)
+    if workspace is None:
+        need = lizard_attn_decode_workspace_bytes(N, Hq, Hkv, d, dt)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
     _check(load().lizard_attn_decode(
         _ptr(state), _ptr(win_k), _ptr(win_v), _ptr(pos), _ptr(q), _ptr(k), _ptr(v),
         _ptr(log_gamma), _ptr(w_phi_q), _ptr(w_phi_k), _w_stride(w_phi_q, w_phi_k, d),
         _ptr(t_k) if M > 0 else None, _ptr(t_v) if M > 0 else None, _ptr(out),
-        N, Hq, Hkv, d, W, M, float(mix), float(scale), _DTYPES[dt], _stream(stream)))
+        N, Hq, Hkv, d, W, M, float(mix), float(scale), _DTYPES[dt], _ptr(workspace), wbytes,
+        _stream(stream)))
     return out
 
 

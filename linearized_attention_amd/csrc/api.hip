@@ -152,11 +152,17 @@ lizard_status lizard_attn_fwd(const void *q, const void *k, const void *v, const
   return finish(lz::launch_fwd(p, dtype == LIZARD_BF16, d, st), st);
 }
 
+size_t lizard_attn_decode_workspace_bytes(int N, int Hq, int Hkv, int d, lizard_dtype dtype) {
+  (void)dtype;
+  if (N <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv != 0) return 0;
+  return lz::decode_workspace_bytes(N, Hq, Hkv, d);
+}
+
 lizard_status lizard_attn_decode(float *state, void *win_k, void *win_v, int32_t *pos, const void *q, const void *k,
                                  const void *v, const void *log_gamma, const void *w_phi_q, const void *w_phi_k,
                                  int64_t w_phi_head_stride, const void *t_k, const void *t_v, void *out, int N, int Hq,
                                  int Hkv, int d, int W, int M, float mix, float scale, lizard_dtype dtype,
-                                 void *stream) {
+                                 void *workspace, size_t workspace_bytes, void *stream) {
   if (dtype != LIZARD_F32 && dtype != LIZARD_BF16) return fail(LIZARD_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
   if (N < 0) return fail(LIZARD_ERR_INVALID_ARG, "N=%d must be >= 0", N);
   if (Hq < 1 || Hkv < 1 || d < 1 || W < 1 || M < 0)
@@ -179,13 +185,19 @@ lizard_status lizard_attn_decode(float *state, void *win_k, void *win_v, int32_t
   const void *ptrs[] = {state, win_k, win_v, q, k, v, log_gamma, w_phi_q, w_phi_k, out, t_k, t_v};
   for (const void *ptr : ptrs)
     if (ptr && !aligned16(ptr)) return fail(LIZARD_ERR_INVALID_ARG, "tensor pointer %p not 16-byte aligned", ptr);
-  if (!aligned16(pos) && (reinterpret_cast<uintptr_t>(pos) & 3u))
-    return fail(LIZARD_ERR_INVALID_ARG, "pos not 4-byte aligned");
+  if (reinterpret_cast<uintptr_t>(pos) & 3u) return fail(LIZARD_ERR_INVALID_ARG, "pos not 4-byte aligned");
+  const size_t need = lz::decode_workspace_bytes(N, Hq, Hkv, d);
+  if (!workspace || workspace_bytes < need)
+    return fail(LIZARD_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(LIZARD_ERR_INVALID_ARG, "workspace not 16-byte aligned");
 
   lz::DecParams p{};
   p.state = state; p.win_k = win_k; p.win_v = win_v; p.pos = pos;
   p.q = q; p.k = k; p.v = v; p.lg = log_gamma; p.wq = w_phi_q; p.wk = w_phi_k; p.tk = t_k; p.tv = t_v;
   p.out = out; p.w_stride = w_phi_head_stride;
+  p.ws_phi = static_cast<float *>(workspace);
+  p.ws_count = reinterpret_cast<int *>(p.ws_phi + (size_t)N * Hq * d + (size_t)N * Hkv * d);  // after phi
   p.N = N; p.Hq = Hq; p.Hkv = Hkv; p.W = W; p.M = M; p.G = Hq / Hkv; p.mix = mix; p.scale = scale;
   hipStream_t st = static_cast<hipStream_t>(stream);
   return finish(lz::launch_decode(p, dtype == LIZARD_BF16, d, st), st);

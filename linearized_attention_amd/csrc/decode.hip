@@ -10,15 +10,24 @@
 //   ring[pos % W] <- (k_t, v_t)
 //   y_win = softmax over M meta keys + min(pos+1, W) ring keys
 //   out = mix y_gla + (1-mix) y_win
-// The step is bound by HBM traffic on the state (2*d*d*4 bytes per (sequence,
-// head), read and written once) and the ring (2*W*d elements read).  One
-// workgroup per (sequence, key/value head).  Every independent load is issued
-// at the top -- the thread's rows of the state, its 16-byte pieces of the ring
-// keys and values -- so the whole step costs about one memory round trip; the
-// feature maps (W_phi from L2, one pass for phi_k and all phi_q) run while
-// those loads are in flight.  Partial sums are reduced inside each wave with
-// shuffles before meeting in LDS.  The position counter is advanced by a
-// separate kernel once every head has read it.
+//
+// Two kernels:
+//   decode_phi   every feature map of the step as one small GEMM on the matrix
+//                cores: rows are the new keys (per key/value head) and queries
+//                (per query head) of 64 sequences, times W_phi staged
+//                transposed in LDS, then the softmax over features.  fp32
+//                results go to the workspace.
+//   decode_step  one workgroup per (sequence, key/value head), bound by HBM
+//                traffic.  It issues its loads in the order it consumes them
+//                -- the per-token vectors and meta tokens, the ring
+//                keys/values, then its fp32 state rows -- because the memory
+//                counter retires loads in order: the window branch then runs
+//                while the state is still in flight.  Then it decays and
+//                updates the state, writes it back, reads out phi_q^T S and
+//                merges.  The last workgroup of a
+//                sequence to finish (a counter in the workspace, cleared by
+//                decode_phi) advances pos: by then every workgroup of that
+//                sequence has read it.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -28,155 +37,197 @@ constexpr int DEC_MAXG = 4;   // query heads per key/value head per pass (groupe
 constexpr int DEC_MAXW = 256; // ring length limit
 constexpr int DEC_MAXM = 16;
 constexpr int DEC_RKEYS = 64; // ring keys per logits pass (4 lanes per key)
+constexpr int DEC_ROWS = 64;  // sequences per decode_phi workgroup
 constexpr float DEC_NEG = -1.0e30f;
 
+// Keeps the compiler from converting a fragment to fp32 ahead of its use
+// (which would double the registers it occupies across the head loop).
+template <typename T> __device__ __forceinline__ void opaque(Frag<T> &f) {
+  if constexpr (sizeof(T) == 2) {
+    asm volatile("" : "+v"(f.v));
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(f.v[j]));
+  }
+}
+
+// grid (ceil(N / 64), Hkv + Hq): y < Hkv is the key side of key/value head y,
+// otherwise query head y - Hkv.  Wave w owns rows 16w .. 16w+15 of the tile.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_phi_kernel(DecParams p) {
+  constexpr int LDW = D + 16 / (int)sizeof(T);  // padded row of W^T (elements)
+  constexpr int NC = D / 16;                    // 16-column output tiles
+  constexpr int KS = D / 32;                    // K = 32 steps
+  __shared__ __align__(16) T wt[D * LDW];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int r = lane & 15, kq = lane >> 4;
+  const int Hkv = p.Hkv, Hq = p.Hq, G = p.G, N = p.N;
+  const int hs = blockIdx.y;
+  const bool key = hs < Hkv;
+  const int h = key ? hs : hs - Hkv;
+  const int n0 = blockIdx.x * DEC_ROWS;
+
+  if (hs == 0 && tid < DEC_ROWS && n0 + tid < N) p.ws_count[n0 + tid] = 0;
+
+  const T *Wsrc = reinterpret_cast<const T *>(key ? p.wk : p.wq) + (size_t)h * p.w_stride;
+  for (int idx = tid; idx < D * (D / 8); idx += 256) {  // W[i][f] -> wt[f][i]
+    const int i = idx / (D / 8), f0 = (idx % (D / 8)) * 8;
+    const Frag<T> w = load8(Wsrc + (size_t)i * D + f0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wt[(f0 + j) * LDW + i] = w.v[j];
+  }
+
+  // A fragments straight from global: row n = n0 + 16*wv + r
+  const int n = min(n0 + 16 * wv + r, N - 1);
+  const T *X = reinterpret_cast<const T *>(key ? p.k : p.q) + ((size_t)n * (key ? Hkv : Hq) + h) * D;
+  Frag<T> a[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) a[s] = load8(X + 32 * s + 8 * kq);  // rows past N: clamped, not stored
+  __syncthreads();
+
+  f32x4 acc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) acc[c] = mma(a[s], load8(wt + (16 * c + r) * LDW + 32 * s + 8 * kq), acc[c]);
+  }
+
+  // lane (r, kq) holds z[row 16wv + 4kq + i][feature 16c + r]; softmax over features
+  const int hk = key ? h : h / G;
+  const int sub = key ? 0 : 1 + h % G;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float m = DEC_NEG;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) m = fmaxf(m, acc[c][i]);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      acc[c][i] = __expf(acc[c][i] - m);
+      s += acc[c][i];
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
+    const float inv = 1.f / s;
+    const int nr = n0 + 16 * wv + 4 * kq + i;
+    if (nr < N) {
+      float *dst = p.ws_phi + (((size_t)nr * Hkv + hk) * (1 + G) + sub) * D;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) dst[16 * c + r] = acc[c][i] * inv;
+    }
+  }
+}
+
 template <typename T, int D, int GM>  // GM: query heads per pass (1 or DEC_MAXG)
-__global__ __launch_bounds__(256, 2) void decode_kernel(DecParams p) {
+__global__ __launch_bounds__(256, 2) void decode_step_kernel(DecParams p) {
   constexpr int C4 = D / 4;     // float4 columns per state row
   constexpr int RG = 256 / C4;  // row groups of the state
   constexpr int RPT = D / RG;   // state rows per thread
   constexpr int F8 = D / 8;     // 8-column pieces of a row
-  constexpr int JG = 256 / F8;  // key / row groups for 8-column work
+  constexpr int JG = 256 / F8;  // ring slot groups for 8-column work
   constexpr int QD = D / 4;     // quarter row (window logits: 4 lanes per key)
-  constexpr int NV = GM + 1;
   constexpr int VPT = DEC_RKEYS / JG;  // value pieces per thread loaded up front
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int G = p.G, Hq = p.Hq, Hkv = p.Hkv, W = p.W, M = p.M;
   const int n = blockIdx.x / Hkv, hk = blockIdx.x % Hkv;
   const size_t nh = (size_t)n * Hkv + hk;
 
-  __shared__ float sx[NV][D];        // queries (0..3) and the raw key (4); later y_win per head
-  __shared__ float sphi[NV][D];      // phi_q per head, phi_k
-  __shared__ float sgam[D], sv[D];
-  __shared__ float sred[4][NV][D];   // per-wave partial sums (feature maps, y_win, y_gla)
+  __shared__ float sx[GM][D];        // raw queries of the pass
+  __shared__ float sk[D], sv[D], sgam[D], sphik[D];
+  __shared__ float sphq[GM][D];
+  __shared__ float sy[GM][D];        // y_win of the pass
+  __shared__ float sred[4][GM][D];   // per-wave partial sums
   __shared__ float slog[GM][DEC_MAXM + DEC_MAXW];
+  __shared__ __align__(16) T stk[DEC_MAXM * D], stv[DEC_MAXM * D];  // meta keys / values
 
   const T *Q = reinterpret_cast<const T *>(p.q);
   const T *K = reinterpret_cast<const T *>(p.k);
   const T *V = reinterpret_cast<const T *>(p.v);
   const T *LG = reinterpret_cast<const T *>(p.lg);
-  const T *Wq = reinterpret_cast<const T *>(p.wq);
-  const T *Wk = reinterpret_cast<const T *>(p.wk) + (size_t)hk * p.w_stride;
   const T *Tk = reinterpret_cast<const T *>(p.tk);
   const T *Tv = reinterpret_cast<const T *>(p.tv);
   T *RK = reinterpret_cast<T *>(p.win_k);
   T *RV = reinterpret_cast<T *>(p.win_v);
   T *OUT = reinterpret_cast<T *>(p.out);
-  const bool shared_w = (p.wq == p.wk) && p.w_stride == 0;
+  const float *phi = p.ws_phi + nh * (size_t)(1 + G) * D;
 
   const int pn = p.pos[n];
   const int slot = pn % W;
   const int nvalid = min(pn + 1, W);
   const size_t rbase = nh * (size_t)W * D;
   float *St = p.state + nh * D * D;
-  const int c4 = tid % C4, rg = tid / C4;
+  const int c4 = tid % C4, rg = tid / C4;  // state columns 4*c4 .., rows rg, rg+RG, ...
 
-  // ---- loads in flight from here on: state rows, ring key quarter, ring value pieces
-  f32x4 x[RPT];
+  // Every load below is unconditional, from an index clamped into bounds (a
+  // conditional load becomes a branch that waits for all loads before it);
+  // lanes whose index was clamped ignore what they read.
+  // ---- 1. per-token vectors (thread tid < D owns element tid) and meta tokens
+  const int gp0 = min(GM, G);
+  const int te = tid % D;
+  const float xk = to_f(K[nh * D + te]);
+  const float xv = to_f(V[nh * D + te]);
+  const float xg = to_f(LG[nh * D + te]);
+  const float xpk = phi[te];
+  float xq[GM], xpq[GM];
 #pragma unroll
-  for (int rr = 0; rr < RPT; ++rr)
-    x[rr] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(St + (size_t)(rg + RG * rr) * D + 4 * c4));
+  for (int u = 0; u < GM; ++u) {
+    const int uu = min(u, gp0 - 1);
+    xq[u] = to_f(Q[((size_t)n * Hq + hk * G + uu) * D + te]);
+    xpq[u] = phi[(size_t)(1 + uu) * D + te];
+  }
+  // meta tokens: thread tid < M * F8 takes row tid / F8, columns 8 * (tid % F8) ..
+  const size_t toff = (size_t)hk * M * D + 8 * (size_t)min(tid, max(M * F8 - 1, 0));
+  const Frag<T> tkf = load8(M > 0 ? Tk + toff : K);
+  const Frag<T> tvf = load8(M > 0 ? Tv + toff : K);
+  // ---- 2. ring key quarter and value pieces
   const int kq = tid / 4, kpart = tid % 4;  // ring slot kq (+ multiples of 64), dims kpart*QD ..
   Frag<T> kfr[QD / 8];
 #pragma unroll
   for (int e8 = 0; e8 < QD / 8; ++e8)
-    kfr[e8] = (kq < W) ? load8(RK + rbase + (size_t)kq * D + kpart * QD + 8 * e8) : frag_zero<T>();
+    kfr[e8] = load8(RK + rbase + (size_t)min(kq, W - 1) * D + kpart * QD + 8 * e8);
   const int f8 = tid % F8, jg = tid / F8;   // value columns 8*f8 .., ring slots jg, jg+JG, ...
   Frag<T> vfr[VPT];
 #pragma unroll
-  for (int m = 0; m < VPT; ++m) {
-    const int j = jg + JG * m;
-    vfr[m] = (j < W) ? load8(RV + rbase + (size_t)j * D + 8 * f8) : frag_zero<T>();
+  for (int m = 0; m < VPT; ++m) vfr[m] = load8(RV + rbase + (size_t)min(jg + JG * m, W - 1) * D + 8 * f8);
+  // ---- 3. the state rows
+  f32x4 x[RPT];
+#pragma unroll
+  for (int rr = 0; rr < RPT; ++rr)
+    x[rr] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(St + (size_t)(rg + RG * rr) * D + 4 * c4));
+
+  // LDS copies, written by every thread (duplicates carry equal values), so no
+  // branch pulls the loads above down past the state loads
+  sk[te] = xk;
+  sv[te] = xv;
+  sgam[te] = __expf(xg);
+  sphik[te] = xpk;
+  {
+    const int tp = min(tid, max(M * F8 - 1, 0));
+    *reinterpret_cast<Frag<T> *>(stk + 8 * tp) = tkf;
+    *reinterpret_cast<Frag<T> *>(stv + 8 * tp) = tvf;
   }
 
-  for (int e = tid; e < D; e += 256) {
-    const size_t o = nh * D + e;
-    sx[GM][e] = to_f(K[o]);
-    sgam[e] = __expf(to_f(LG[o]));
-    sv[e] = to_f(V[o]);
-  }
-
-  for (int g0 = 0; g0 < G; g0 += GM) {
+  for (int g0 = 0; g0 < (GM == 1 ? 1 : G); g0 += GM) {  // GM = 1 runs only for G = 1
     const int gp = min(GM, G - g0);
     const bool first = (g0 == 0);
-    for (int idx = tid; idx < GM * D; idx += 256) {
-      const int u = idx / D, e = idx % D;
-      sx[u][e] = (u < gp) ? to_f(Q[((size_t)n * Hq + hk * G + g0 + u) * D + e]) : 0.f;
+    if (first) {
+#pragma unroll
+      for (int u = 0; u < GM; ++u) {
+        sx[u][te] = (u < gp0) ? xq[u] : 0.f;
+        sphq[u][te] = (u < gp0) ? xpq[u] : 0.f;
+      }
+    } else {
+      for (int idx = tid; idx < GM * D; idx += 256) {
+        const int u = idx / D, e = idx % D;
+        const bool on = u < gp;
+        sx[u][e] = on ? to_f(Q[((size_t)n * Hq + hk * G + g0 + u) * D + e]) : 0.f;
+        sphq[u][e] = on ? phi[(size_t)(1 + g0 + u) * D + e] : 0.f;
+      }
     }
     __syncthreads();
-
-    // ---- feature maps: z[v][f] = sum_i x_v[i] W[i][f]; thread (f8, jg) sums rows jg, jg+JG, ...
-    {
-      float z[NV][8];
-#pragma unroll
-      for (int v = 0; v < NV; ++v)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) z[v][j] = 0.f;
-#pragma unroll 2
-      for (int i = jg; i < D; i += JG) {
-        float wk8[8];
-        if (first) {
-          load8f(Wk + (size_t)i * D + 8 * f8, wk8);
-          const float xi = sx[GM][i];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) z[GM][j] += xi * wk8[j];
-        }
-#pragma unroll
-        for (int u = 0; u < GM; ++u) {
-          if (u < gp) {
-            float w8[8];
-            if (shared_w && first) {
-#pragma unroll
-              for (int j = 0; j < 8; ++j) w8[j] = wk8[j];
-            } else {
-              load8f(Wq + (size_t)(hk * G + g0 + u) * p.w_stride + (size_t)i * D + 8 * f8, w8);
-            }
-            const float xi = sx[u][i];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) z[u][j] += xi * w8[j];
-          }
-        }
-      }
-      // the 64/F8 row groups of a wave, then the 4 waves in LDS
-#pragma unroll
-      for (int v = 0; v < NV; ++v)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-          for (int o = F8; o < 64; o <<= 1) z[v][j] += __shfl_xor(z[v][j], o);
-      if (lane < F8) {
-#pragma unroll
-        for (int v = 0; v < NV; ++v)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) sred[wv][v][8 * f8 + j] = z[v][j];
-      }
-      __syncthreads();
-      // softmax over features: wave w handles vectors w, w+4
-      for (int v = wv; v < NV; v += 4) {
-        if (v == GM ? !first : v >= gp) continue;
-        float zz[D / 64];
-        float m = DEC_NEG;
-#pragma unroll
-        for (int q = 0; q < D / 64; ++q) {
-          const int f = lane + 64 * q;
-          zz[q] = sred[0][v][f] + sred[1][v][f] + sred[2][v][f] + sred[3][v][f];
-          m = fmaxf(m, zz[q]);
-        }
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-        float s = 0.f;
-#pragma unroll
-        for (int q = 0; q < D / 64; ++q) {
-          zz[q] = __expf(zz[q] - m);
-          s += zz[q];
-        }
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o);
-        const float inv = 1.f / s;
-#pragma unroll
-        for (int q = 0; q < D / 64; ++q) sphi[v][lane + 64 * q] = zz[q] * inv;
-      }
-    }
 
     // ---- window logits over ring slots: slot jb + kq, quarter kpart (first pass from registers)
     for (int jb = 0; jb < W; jb += DEC_RKEYS) {
@@ -194,10 +245,12 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecParams p) {
           float kv8[8];
           if (jj == slot) {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) kv8[t] = sx[GM][e0 + t];
+            for (int t = 0; t < 8; ++t) kv8[t] = sk[e0 + t];
           } else if (jb == 0) {
+            Frag<T> kk = kfr[e8];
+            opaque(kk);
 #pragma unroll
-            for (int t = 0; t < 8; ++t) kv8[t] = to_f(kfr[e8].v[t]);
+            for (int t = 0; t < 8; ++t) kv8[t] = to_f(kk.v[t]);
           } else {
             load8f(RK + rbase + (size_t)jj * D + e0, kv8);
           }
@@ -215,22 +268,14 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecParams p) {
       if (in && kpart == 0)
         for (int u = 0; u < gp; ++u) slog[u][M + jj] = ok ? acc[u] * p.scale : DEC_NEG;
     }
-    // meta keys: thread (u, m), full dot product (T_k from L2)
-    for (int idx = tid; idx < gp * M; idx += 256) {
+    for (int idx = tid; idx < gp * M; idx += 256) {  // meta keys
       const int u = idx / M, m = idx % M;
-      const T *kr = Tk + ((size_t)hk * M + m) * D;
       float a = 0.f;
-      for (int e8 = 0; e8 < D; e8 += 8) {
-        float kv8[8];
-        load8f(kr + e8, kv8);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) a += sx[u][e8 + t] * kv8[t];
-      }
+      for (int e = 0; e < D; ++e) a += sx[u][e] * to_f(stk[m * D + e]);
       slog[u][m] = a * p.scale;
     }
     __syncthreads();
-    // softmax per head (one wave per head)
-    for (int u = wv; u < gp; u += 4) {
+    for (int u = wv; u < gp; u += 4) {  // softmax per head (one wave per head)
       float m = DEC_NEG;
       for (int j = lane; j < M + W; j += 64) m = fmaxf(m, slog[u][j]);
 #pragma unroll
@@ -260,8 +305,10 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecParams p) {
         const int j = jg + JG * m;
         if (j < W) {
           float vv[8];
+          Frag<T> vk = vfr[m];
+          opaque(vk);
 #pragma unroll
-          for (int t = 0; t < 8; ++t) vv[t] = (j == slot) ? sv[8 * f8 + t] : to_f(vfr[m].v[t]);
+          for (int t = 0; t < 8; ++t) vv[t] = (j == slot) ? sv[8 * f8 + t] : to_f(vk.v[t]);
 #pragma unroll
           for (int u = 0; u < GM; ++u) {
             const float pj = slog[u][M + j];
@@ -305,7 +352,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecParams p) {
 #pragma unroll
       for (int rr = 0; rr < RPT; ++rr) {
         const int f = rg + RG * rr;
-        const float gm = sgam[f], pk = sphi[GM][f];
+        const float gm = sgam[f], pk = sphik[f];
         x[rr][0] = gm * x[rr][0] + pk * v0;
         x[rr][1] = gm * x[rr][1] + pk * v1;
         x[rr][2] = gm * x[rr][2] + pk * v2;
@@ -318,13 +365,11 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecParams p) {
     for (int u = 0; u < GM; ++u) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) yp[u][i] = 0.f;
-      if (u < gp) {
 #pragma unroll
-        for (int rr = 0; rr < RPT; ++rr) {
-          const float pq = sphi[u][rg + RG * rr];
+      for (int rr = 0; rr < RPT; ++rr) {
+        const float pq = sphq[u][rg + RG * rr];  // zero for u >= gp
 #pragma unroll
-          for (int i = 0; i < 4; ++i) yp[u][i] += pq * x[rr][i];
-        }
+        for (int i = 0; i < 4; ++i) yp[u][i] += pq * x[rr][i];
       }
     }
 #pragma unroll
@@ -334,12 +379,11 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecParams p) {
 #pragma unroll
         for (int o = C4; o < 64; o <<= 1) yp[u][i] += __shfl_xor(yp[u][i], o);
     __syncthreads();  // y_win partials complete
-    // y_win per head (ring part + meta values) -> sx (the raw queries are no longer needed)
-    for (int idx = tid; idx < gp * D; idx += 256) {
+    for (int idx = tid; idx < gp * D; idx += 256) {  // y_win = ring part + meta values
       const int u = idx / D, e = idx % D;
       float w = sred[0][u][e] + sred[1][u][e] + sred[2][u][e] + sred[3][u][e];
-      for (int m = 0; m < M; ++m) w += slog[u][m] * to_f(Tv[((size_t)hk * M + m) * D + e]);
-      sx[u][e] = w;
+      for (int m = 0; m < M; ++m) w += slog[u][m] * to_f(stv[m * D + e]);
+      sy[u][e] = w;
     }
     __syncthreads();
     if (lane < C4) {
@@ -352,7 +396,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecParams p) {
     for (int idx = tid; idx < gp * D; idx += 256) {
       const int u = idx / D, e = idx % D;
       const float a = sred[0][u][e] + sred[1][u][e] + sred[2][u][e] + sred[3][u][e];
-      OUT[((size_t)n * Hq + hk * G + g0 + u) * D + e] = from_f<T>(p.mix * a + (1.f - p.mix) * sx[u][e]);
+      OUT[((size_t)n * Hq + hk * G + g0 + u) * D + e] = from_f<T>(p.mix * a + (1.f - p.mix) * sy[u][e]);
     }
     __syncthreads();
   }
@@ -360,22 +404,25 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecParams p) {
     RK[rbase + (size_t)slot * D + tid] = K[nh * D + tid];
     RV[rbase + (size_t)slot * D + tid] = V[nh * D + tid];
   }
-}
-
-__global__ void decode_advance_pos(int32_t *pos, int N) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < N) pos[i] += 1;
+  if (tid == 0) {
+    // Every wave consumed its read of pos[n] before the last barrier, so a
+    // relaxed count is enough (a device-scope fence here would write back and
+    // invalidate this XCD's L2 once per workgroup).
+    if (__hip_atomic_fetch_add(p.ws_count + n, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == Hkv - 1)
+      p.pos[n] = pn + 1;
+  }
 }
 
 template <typename T, int D>
 static hipError_t launch_dec_t(const DecParams &p, hipStream_t stream) {
-  if (p.G == 1)
-    hipLaunchKernelGGL((decode_kernel<T, D, 1>), dim3(p.N * p.Hkv), dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL((decode_kernel<T, D, DEC_MAXG>), dim3(p.N * p.Hkv), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((decode_phi_kernel<T, D>), dim3((p.N + DEC_ROWS - 1) / DEC_ROWS, p.Hkv + p.Hq), dim3(256),
+                     0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_advance_pos, dim3((p.N + 255) / 256), dim3(256), 0, stream, p.pos, p.N);
+  if (p.G == 1)
+    hipLaunchKernelGGL((decode_step_kernel<T, D, 1>), dim3(p.N * p.Hkv), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_step_kernel<T, D, DEC_MAXG>), dim3(p.N * p.Hkv), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -390,5 +437,9 @@ hipError_t launch_decode(const DecParams &p, int dtype_bf16, int d, hipStream_t 
 }
 
 int decode_max_window() { return DEC_MAXW; }
+
+size_t decode_workspace_bytes(int N, int Hq, int Hkv, int d) {
+  return ((size_t)N * Hkv * (1 + Hq / Hkv) * d + (size_t)N) * sizeof(float);
+}
 
 }  // namespace lz

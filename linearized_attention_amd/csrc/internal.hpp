@@ -31,6 +31,8 @@ struct DecParams {
   int32_t *pos;
   const void *q, *k, *v, *lg, *wq, *wk, *tk, *tv;
   void *out;
+  float *ws_phi;   // [N][Hkv][1+G][d]: phi_k, then phi_q of each grouped query head
+  int *ws_count;   // [N]: workgroups of the step that have read pos[n]
   int64_t w_stride;
   int N, Hq, Hkv, W, M, G;
   float mix, scale;
@@ -42,4 +44,5 @@ hipError_t launch_decode(const DecParams &p, int dtype_bf16, int d, hipStream_t 
 
 namespace lz {
 int decode_max_window();
+size_t decode_workspace_bytes(int N, int Hq, int Hkv, int d);
 }

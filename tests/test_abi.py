@@ -93,19 +93,21 @@ def test_workspace_bytes_matches_plan_formula():
 
 def _dec(lib, **kw):
     a = dict(state=16, wk=16, wv=16, pos=16, q=16, k=16, v=16, lg=16, wq=16, wkm=16, stride=0, tk=16,
-             tv=16, out=16, N=4, Hq=2, Hkv=2, d=128, W=64, M=4, mix=0.5, scale=0.1, dtype=1, stream=None)
+             tv=16, out=16, N=4, Hq=2, Hkv=2, d=128, W=64, M=4, mix=0.5, scale=0.1, dtype=1, ws=16,
+             wsb=1 << 30, stream=None)
     a.update(kw)
     P = lambda x: None if x is None else ctypes.c_void_p(x)
     return lib.lizard_attn_decode(P(a["state"]), P(a["wk"]), P(a["wv"]), P(a["pos"]), P(a["q"]),
                                   P(a["k"]), P(a["v"]), P(a["lg"]), P(a["wq"]), P(a["wkm"]),
                                   a["stride"], P(a["tk"]), P(a["tv"]), P(a["out"]), a["N"], a["Hq"],
                                   a["Hkv"], a["d"], a["W"], a["M"], a["mix"], a["scale"], a["dtype"],
-                                  P(a["stream"]))
+                                  P(a["ws"]), a["wsb"], P(a["stream"]))
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(state=None), 1), (dict(pos=None), 1), (dict(Hq=3), 1), (dict(W=0), 1), (dict(N=-1), 1),
-    (dict(d=32), 2), (dict(W=257), 2), (dict(M=20), 2), (dict(q=8), 1),
+    (dict(d=32), 2), (dict(W=257), 2), (dict(M=20), 2), (dict(q=8), 1), (dict(pos=18), 1),
+    (dict(ws=None), 3), (dict(wsb=100), 3), (dict(ws=24), 1),
 ])
 def test_decode_validation_codes(kw, code):
     lib = api.load()
@@ -114,3 +116,14 @@ def test_decode_validation_codes(kw, code):
 
 def test_decode_empty_is_ok():
     assert _dec(api.load(), N=0) == 0
+
+
+def test_decode_workspace_bytes_formula():
+    lib = api.load()
+    N, Hq, Hkv, d = 256, 32, 8, 128
+    G = Hq // Hkv
+    assert lib.lizard_attn_decode_workspace_bytes(N, Hq, Hkv, d, 1) == 4 * (N * Hkv * (1 + G) * d + N)
+    assert lib.lizard_attn_decode_workspace_bytes(0, Hq, Hkv, d, 1) == 0
+    assert lib.lizard_attn_decode_workspace_bytes(N, 3, 2, d, 1) == 0
+    need = lib.lizard_attn_decode_workspace_bytes(4, 2, 2, 128, 1)
+    assert _dec(lib, wsb=need - 1) == 3

@@ -26,14 +26,19 @@ def rel_l2(got, want, axes):
     return num / np.maximum(den, 1e-300)
 
 
-def run_gpu_steps(dec, nsteps=None):
+def run_gpu_steps(dec, nsteps=None, shared_workspace=False):
+    ws = None
+    if shared_workspace:
+        N, Hq, d = dec.steps[0][0].shape
+        nb = api.lizard_attn_decode_workspace_bytes(N, Hq, dec.steps[0][1].shape[1], d, dec.steps[0][0].dtype)
+        ws = torch.full((nb,), 255, dtype=torch.uint8, device="cuda")  # stale contents must not matter
     st = dec.state.clone().cuda()
     rk, rv, pos = dec.ring_k.clone().cuda(), dec.ring_v.clone().cuda(), dec.pos.clone().cuda()
     args = [t.cuda() for t in (dec.w_phi_q, dec.w_phi_k, dec.t_k, dec.t_v)]
     outs = []
     for (q, k, v, lg) in dec.steps[:nsteps]:
         o = api.lizard_attn_decode(st, rk, rv, pos, q.cuda(), k.cuda(), v.cuda(), lg.cuda(), *args,
-                                   M=dec.M, mix=dec.mix, scale=dec.scale)
+                                   M=dec.M, mix=dec.mix, scale=dec.scale, workspace=ws)
         outs.append(o.double().cpu().numpy())
     torch.cuda.synchronize()
     return np.stack(outs, axis=2), st.double().cpu().numpy(), rk.cpu(), rv.cpu(), pos.cpu()
@@ -59,6 +64,8 @@ CASES = [
     ("bf16 d64 gqa 8:2 W100", dict(N=9, Hq=8, Hkv=2, d=64, W=100, M=16, steps=4, pos0=250, dtype="bf16"), "bf16"),
     ("bf16 d128 gqa 6:1 (two head passes)", dict(N=4, Hq=6, Hkv=1, d=128, W=64, M=4, steps=3, pos0=64,
                                                   dtype="bf16"), "bf16"),
+    ("bf16 d128 W256 M16 (four logits passes)", dict(N=3, Hq=2, Hkv=2, d=128, W=256, M=16, steps=3, pos0=300,
+                                                      dtype="bf16"), "bf16"),
 ]
 
 
@@ -77,6 +84,16 @@ def test_decode_matches_oracle(gpu_lib, label, kw, dtype):
     # the rings hold exactly the input keys/values (bit-exact copies)
     assert np.array_equal(rkg.double().numpy(), rko)
     assert np.array_equal(rvg.double().numpy(), rvo)
+
+
+def test_decode_shared_workspace_is_deterministic(gpu_lib):
+    """One workspace reused (with stale contents) across steps gives the same
+    bits as a fresh workspace per call."""
+    _say("[decode] shared workspace vs per-call workspace")
+    dec = make_decode_inputs(seed=5, N=7, Hq=8, Hkv=2, d=128, W=64, M=4, steps=4, pos0=30, dtype="bf16")
+    a = run_gpu_steps(dec)
+    b = run_gpu_steps(dec, shared_workspace=True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
