@@ -46,238 +46,12 @@
 // Segments after the first start from a state assembled from the per-segment
 // end states that the state-only variant of this kernel leaves in the
 // workspace.
-#include "common.hpp"
-#include "internal.hpp"
+#include <cstdlib>
+#include <cstring>
+
+#include "fwd_common.hpp"
 
 namespace lz {
-
-constexpr int CH = 64;            // chunk length
-constexpr float SPAN_MAX = 80.f;  // max |log-decay| across one 16-token sub-chunk for the
-                                  // mid-reference MFMA path (e^80 ~ 5.5e34 < fp32/bf16 max)
-constexpr float NEG_BIG = -1.0e30f;
-constexpr int LDS_LIMIT = 160 * 1024;
-constexpr int WIN_BATCH = 8;      // key tiles per online-softmax batch in the window
-
-template <typename T, int D, int DV> struct FwdGeom {
-  static constexpr int PADE = 16 / (int)sizeof(T);
-  static constexpr int LDW = D + PADE;   // rows of D elements
-  static constexpr int LDC = CH + PADE;  // rows of 64 tokens
-  static constexpr int LDM = 16 + PADE;  // rows of 16 meta tokens
-  static constexpr int SZ_W = D * LDW * (int)sizeof(T);
-  static constexpr int SZ_VT = DV * LDC * (int)sizeof(T);
-  static constexpr int SZ_KR = CH * LDW * (int)sizeof(T);
-  // keys decayed to their sub-chunk end [s][f], overlaid on log gamma^T [f][s]
-  static constexpr int SZ_KOWN = (CH * LDW > D * LDC ? CH * LDW : D * LDC) * (int)sizeof(T);
-  static constexpr int SZ_SUB = 4 * D * (int)sizeof(float);  // one [4][D] fp32 table
-  static constexpr int SZ_SBF = DV * LDW * (int)sizeof(T);
-  static constexpr int SZ_TVT = DV * LDM * (int)sizeof(T);
-  static constexpr int SZ_TK = 16 * LDW * (int)sizeof(T);
-};
-
-// Byte offsets of the LDS regions for one launch (computed on the host).
-template <typename T, int D, int DV>
-static FwdLds make_lds(bool state_only, bool shared_w, int nr, int kr) {
-  using Gm = FwdGeom<T, D, DV>;
-  FwdLds l{};
-  int o = 0;
-  l.wk = o; o += Gm::SZ_W;
-  l.wq = (state_only || shared_w) ? l.wk : o;
-  if (!(state_only || shared_w)) o += Gm::SZ_W;
-  l.vt = o; o += nr * Gm::SZ_VT;
-  l.kr = o; o += kr * Gm::SZ_KR;
-  l.kown = o; o += Gm::SZ_KOWN;
-  l.tot = o; o += Gm::SZ_SUB;   // tot_J[f]
-  l.p7 = o; o += Gm::SZ_SUB;    // p7_J[f]
-  l.etot = o; o += Gm::SZ_SUB;  // e^{tot_J}
-  if (!state_only) {
-    l.enp7 = o; o += Gm::SZ_SUB;  // e^{-p7_J}
-    l.enr8 = o; o += Gm::SZ_SUB;  // e^{p7_J - tot_J}
-    l.sbf = o; o += Gm::SZ_SBF;
-    l.tvt = o; o += Gm::SZ_TVT;
-    l.tk = o; o += Gm::SZ_TK;
-  }
-  l.total = o;
-  return l;
-}
-
-// W_phi [d][f] row-major in global -> W^T [f][d] in LDS (row stride LDW).
-template <typename T, int D, int LDW>
-__device__ __forceinline__ void load_wT(T *dst, const T *src) {
-  for (int idx = threadIdx.x; idx < D * (D / 8); idx += 256) {
-    const int dd = idx / (D / 8), f0 = (idx % (D / 8)) * 8;
-    float x[8];
-    load8f(src + (size_t)dd * D + f0, x);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) dst[(f0 + j) * LDW + dd] = from_f<T>(x[j]);
-  }
-}
-
-// Per-thread share of one chunk: keys (row-major), values and log gamma
-// (both stored transposed, token pairs 2*tp, 2*tp+1 x 8 columns).
-template <typename T, int D, int DV> struct ChunkRegs {
-  static constexpr int KFR = CH * D / 8 / 256;      // 8-element pieces of k per thread
-  static constexpr int LFR = (CH / 2) * (D / 8) / 256;  // token-pair pieces of log gamma
-  Frag<T> k[KFR];
-  Frag<T> v[2];
-  Frag<T> lg[LFR][2];
-};
-
-template <typename T, int D, int DV>
-__device__ __forceinline__ void load_chunk(ChunkRegs<T, D, DV> &r, const T *Kh, const T *Vh, const T *LGh,
-                                           int c0, int L, int dv0, bool with_v) {
-  static_assert(DV == 64, "value block of 64 columns");
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int j = 0; j < ChunkRegs<T, D, DV>::KFR; ++j) {
-    const int idx = tid + 256 * j;
-    const int row = idx / (D / 8), c8 = idx % (D / 8);
-    r.k[j] = (c0 + row < L) ? load8(Kh + (size_t)(c0 + row) * D + 8 * c8) : frag_zero<T>();
-  }
-  if (with_v) {
-    const int tp = tid / (DV / 8), dq = tid % (DV / 8);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int t = c0 + 2 * tp + h;
-      r.v[h] = (t < L) ? load8(Vh + (size_t)t * D + dv0 + 8 * dq) : frag_zero<T>();
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < ChunkRegs<T, D, DV>::LFR; ++j) {
-    const int idx = tid + 256 * j;
-    const int tp = idx / (D / 8), fq = idx % (D / 8);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int t = c0 + 2 * tp + h;
-      r.lg[j][h] = (t < L) ? load8(LGh + (size_t)t * D + 8 * fq) : frag_zero<T>();
-    }
-  }
-}
-
-template <typename T, int D, int DV, int LDW>
-__device__ __forceinline__ void store_keys(const ChunkRegs<T, D, DV> &r, T *sK) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int j = 0; j < ChunkRegs<T, D, DV>::KFR; ++j) {
-    const int idx = tid + 256 * j;
-    const int row = idx / (D / 8), c8 = idx % (D / 8);
-    T *dst = sK + row * LDW + 8 * c8;
-    if constexpr (sizeof(T) == 2) {
-      *reinterpret_cast<bf16x8 *>(dst) = r.k[j].v;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dst[e] = r.k[j].v[e];
-    }
-  }
-}
-
-// Two tokens x 8 columns -> transposed [col][token] (token pair adjacent).
-template <typename T, int LDC>
-__device__ __forceinline__ void store_pairT(const Frag<T> &a, const Frag<T> &b, T *dst) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    T *d = dst + e * LDC;
-    if constexpr (sizeof(T) == 2) {
-      bf16 pair[2] = {a.v[e], b.v[e]};
-      *reinterpret_cast<uint32_t *>(d) = *reinterpret_cast<const uint32_t *>(pair);
-    } else {
-      d[0] = a.v[e];
-      d[1] = b.v[e];
-    }
-  }
-}
-
-template <typename T, int D, int DV, int LDC>
-__device__ __forceinline__ void store_values(const ChunkRegs<T, D, DV> &r, T *sVt) {
-  const int tid = threadIdx.x;
-  const int tp = tid / (DV / 8), dq = tid % (DV / 8);
-  store_pairT<T, LDC>(r.v[0], r.v[1], sVt + (8 * dq) * LDC + 2 * tp);
-}
-
-template <typename T, int D, int DV, int LDC>
-__device__ __forceinline__ void store_lgT(const ChunkRegs<T, D, DV> &r, T *sLgT) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int j = 0; j < ChunkRegs<T, D, DV>::LFR; ++j) {
-    const int idx = tid + 256 * j;
-    const int tp = idx / (D / 8), fq = idx % (D / 8);
-    store_pairT<T, LDC>(r.lg[j][0], r.lg[j][1], sLgT + (8 * fq) * LDC + 2 * tp);
-  }
-}
-
-// Constant B operand of the prefix / exclusive-suffix sums over the 16 rows of
-// a sub-chunk: lane (t = r16, kq) holds B[s = 8kq + j][t].
-template <typename T>
-__device__ __forceinline__ Frag<T> tri_frag(int r16, int g4, bool prefix) {
-  float x[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int s = 8 * g4 + j;
-    x[j] = (s < 16 && (prefix ? (s <= r16) : (s > r16))) ? 1.f : 0.f;
-  }
-  return frag_from<T>(x);
-}
-
-// 8 fp32 table values for the operand slots of K-step js (features
-// 32js + 4g4 + 0..3 and 32js + 16 + 4g4 + 0..3).
-__device__ __forceinline__ void tab8(const float *row, int js, int g4, float (&x)[8]) {
-  const f32x4 a = *reinterpret_cast<const f32x4 *>(row + 32 * js + 4 * g4);
-  const f32x4 b = *reinterpret_cast<const f32x4 *>(row + 32 * js + 16 + 4 * g4);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
-}
-
-template <int NFT>
-__device__ __forceinline__ void softmax_rows(const f32x4 (&z)[NFT], float (&phi)[NFT][4]) {
-  float zm = NEG_BIG;
-#pragma unroll
-  for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) zm = fmaxf(zm, z[ft][i]);
-  zm = wave_max_cols(zm);
-  float zs = 0.f;
-#pragma unroll
-  for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      phi[ft][i] = __expf(z[ft][i] - zm);
-      zs += phi[ft][i];
-    }
-  zs = wave_sum_cols(zs);
-  const float inv = 1.f / zs;
-#pragma unroll
-  for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) phi[ft][i] *= inv;
-}
-
-// z^T[f][t] = sum_d W[d][f] x[t][d] for the wave's 16 rows (W^T in LDS).
-template <typename T, int D, int LDW>
-__device__ __forceinline__ void feature_logits(const T *sW, const Frag<T> (&xf)[D / 32], int r16, int g4,
-                                               f32x4 (&z)[D / 16]) {
-#pragma unroll
-  for (int ft = 0; ft < D / 16; ++ft) {
-    z[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < D / 32; ++j) z[ft] = mma(load8(sW + (16 * ft + r16) * LDW + 32 * j + 8 * g4), xf[j], z[ft]);
-  }
-}
-
-// Same for two inputs against one W (each W fragment read once, two MFMA chains).
-template <typename T, int D, int LDW>
-__device__ __forceinline__ void feature_logits2(const T *sW, const Frag<T> (&xa)[D / 32], const Frag<T> (&xb)[D / 32],
-                                                int r16, int g4, f32x4 (&za)[D / 16], f32x4 (&zb)[D / 16]) {
-#pragma unroll
-  for (int ft = 0; ft < D / 16; ++ft) {
-    za[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
-    zb[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < D / 32; ++j) {
-      const Frag<T> w = load8(sW + (16 * ft + r16) * LDW + 32 * j + 8 * g4);
-      za[ft] = mma(w, xa[j], za[ft]);
-      zb[ft] = mma(w, xb[j], zb[ft]);
-    }
-  }
-}
 
 template <typename T, int D, int DV, bool STATE_ONLY>
 __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
@@ -333,10 +107,10 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   const T *Qbase = reinterpret_cast<const T *>(p.q);
 
   // ---- prologue
-  load_wT<T, D, LDW>(sWk, Wk);
+  load_wT<T, D, LDW>(sWk, Wk, tid);
   if constexpr (!STATE_ONLY) {
     if (ly.wq != ly.wk)
-      load_wT<T, D, LDW>(sWq, reinterpret_cast<const T *>(p.wq) + (size_t)(kvh * G) * p.w_stride);
+      load_wT<T, D, LDW>(sWq, reinterpret_cast<const T *>(p.wq) + (size_t)(kvh * G) * p.w_stride, tid);
     const T *Tv = reinterpret_cast<const T *>(p.tv);
     const T *Tk = reinterpret_cast<const T *>(p.tk);
     for (int idx = tid; idx < DV * 16; idx += 256) {
@@ -358,9 +132,9 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
     const int R = max(NR, KR);
     for (int cc = max(0, c_begin - (R - 1)); cc < c_begin; ++cc) {
       ChunkRegs<T, D, DV> pre;
-      load_chunk<T, D, DV>(pre, Kh, Vh, LGh, cc * CH, L, dv0, true);
-      if (cc > c_begin - KR) store_keys<T, D, DV, LDW>(pre, sKr + (cc % KR) * (CH * LDW));
-      if (cc > c_begin - NR) store_values<T, D, DV, LDC>(pre, sVt + (cc % NR) * (DV * LDC));
+      load_chunk<T, D, DV>(pre, Kh, Vh, LGh, cc * CH, L, dv0, true, tid);
+      if (cc > c_begin - KR) store_keys<T, D, DV, LDW>(pre, sKr + (cc % KR) * (CH * LDW), tid);
+      if (cc > c_begin - NR) store_values<T, D, DV, LDC>(pre, sVt + (cc % NR) * (DV * LDC), tid);
     }
   }
 
@@ -414,7 +188,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   // first chunk's data into registers
   ChunkRegs<T, D, DV> pf;
   Frag<T> pfq[KS];
-  load_chunk<T, D, DV>(pf, Kh, Vh, LGh, c_begin * CH, L, dv0, true);
+  load_chunk<T, D, DV>(pf, Kh, Vh, LGh, c_begin * CH, L, dv0, true, tid);
   if constexpr (!STATE_ONLY) {
     const int pos0 = c_begin * CH + 16 * I + r16;
     const T *Q0 = Qbase + ((size_t)b * p.Hq + kvh * G) * (size_t)L * D;
@@ -439,9 +213,9 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
     const int kprev = ((c + KR - 1) % KR) * (CH * LDW);  // used only when KR >= 2
     const int vprev = ((c + NR - 1) % NR) * (DV * LDC);
     // ---- this chunk's keys, values, log gamma (loaded one chunk ahead) -> LDS
-    store_keys<T, D, DV, LDW>(pf, sKr + kcur);
-    store_values<T, D, DV, LDC>(pf, sVt + cur);
-    store_lgT<T, D, DV, LDC>(pf, sLgT);
+    store_keys<T, D, DV, LDW>(pf, sKr + kcur, tid);
+    store_values<T, D, DV, LDC>(pf, sVt + cur, tid);
+    store_lgT<T, D, DV, LDC>(pf, sLgT, tid);
     Frag<T> qf[KS];
     if constexpr (!STATE_ONLY) {
 #pragma unroll
@@ -450,7 +224,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
     // ---- state-only variant: next chunk in flight during this one (the full kernel issues
     //      it after the query loop, where fewer registers are live)
     if constexpr (STATE_ONLY) {
-      if (c + 1 < c_end) load_chunk<T, D, DV>(pf, Kh, Vh, LGh, c0 + CH, L, dv0, true);
+      if (c + 1 < c_end) load_chunk<T, D, DV>(pf, Kh, Vh, LGh, c0 + CH, L, dv0, true, tid);
     }
     __syncthreads();  // B0: this chunk in LDS
 
@@ -557,7 +331,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
         const int hq = kvh * G + g;
         if (p.per_head_q && G > 1) {  // a different W_phi_q for every query head
           __syncthreads();
-          load_wT<T, D, LDW>(sWq, reinterpret_cast<const T *>(p.wq) + (size_t)hq * p.w_stride);
+          load_wT<T, D, LDW>(sWq, reinterpret_cast<const T *>(p.wq) + (size_t)hq * p.w_stride, tid);
           __syncthreads();
         }
         const T *Qh = Qbase + ((size_t)b * p.Hq + hq) * (size_t)L * D;
@@ -894,7 +668,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
       }  // g
       // next chunk's keys, values, log gamma and first query head in flight during the state update
       if (c + 1 < c_end) {
-        load_chunk<T, D, DV>(pf, Kh, Vh, LGh, c0 + CH, L, dv0, true);
+        load_chunk<T, D, DV>(pf, Kh, Vh, LGh, c0 + CH, L, dv0, true, tid);
         const int pn = pos + CH;
         const T *Q0 = Qbase + ((size_t)b * p.Hq + kvh * G) * (size_t)L * D;
 #pragma unroll
@@ -1003,6 +777,13 @@ static hipError_t launch_fwd_t(const FwdParams &prm, hipStream_t stream) {
       }
     }
   if (!fit) return hipErrorInvalidConfiguration;
+  // The role-split kernel keeps one W_phi_q per workgroup; a different one per grouped
+  // query head (reloaded inside the head loop) runs on the 4-wave kernel.
+  static const bool force_4wave = [] {
+    const char *e = getenv("LIZARD_FWD_KERNEL");
+    return e && strcmp(e, "4wave") == 0;
+  }();
+  if (!force_4wave && !(p.per_head_q && p.G > 1)) return launch_fwd_split<T, D, DV>(p, stream);
   return launch_one<T, D, DV, false>(p, stream);
 }
 

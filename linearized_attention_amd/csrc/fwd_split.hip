@@ -1,0 +1,735 @@
+// Lizard attention forward, role-split variant: 8 waves per workgroup.
+//
+// Same arithmetic and LDS layout as the 4-wave kernel in fwd.hip (the method,
+// the sub-chunk decay references and the work split over (batch, key/value
+// head, value block, segment) are described there).  Here the chunk's work is
+// divided by role instead of being repeated per wave:
+//   key waves (4..7), sub-chunk I = wave - 4: gate sums inside the sub-chunk,
+//       phi_k and the decayed keys, the per-chunk factor tables, and the
+//       state update (S lives in their registers);
+//   query waves (0..3), sub-chunk I = wave: phi_q, the anchor window, the
+//       intra- and inter-chunk products, the merge and the stores.
+// Each role runs its own loop over the chunks; both loops pass the same four
+// workgroup barriers per chunk, so the roles stay in step:
+//   B0  chunk c's keys, values and log gamma are in LDS
+//   B1  sub-chunk totals written (key waves), log gamma consumed (both)
+//   B2  factor tables and decayed keys in LDS
+//   B3  every read of the state copy, the decayed keys and the ring slot about
+//       to be reused is done; the key waves then publish the new state copy.
+// Two waves per SIMD (512 threads, one workgroup per CU) let one role's
+// memory and matrix-core latency hide behind the other's work.
+#include "fwd_common.hpp"
+
+namespace lz {
+
+// FASTWIN: W <= 65 with two chunks in each ring (the window is exactly six 16-key
+// tiles); MULTI_G: more than one query head per key/value head.  Both are known
+// on the host; fixing them at compile time keeps each variant within 256 VGPRs.
+template <typename T, int D, int DV, bool FASTWIN, bool MULTI_G>
+__global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
+  using Gm = FwdGeom<T, D, DV>;
+  constexpr int NFT = D / 16;   // 16-row tiles of the feature dimension
+  constexpr int KS = D / 32;    // K = 32 steps over d (or over features)
+  constexpr int NDT = DV / 16;  // 16-column tiles of this block's value columns
+  constexpr int FTW = NFT / 4;  // feature tiles of S owned by each key wave
+  constexpr int LDW = Gm::LDW, LDC = Gm::LDC, LDM = Gm::LDM;
+  static_assert(NFT % 4 == 0, "d must be a multiple of 64");
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const FwdLds &ly = p.lds;
+  T *sWk = reinterpret_cast<T *>(smem + ly.wk);
+  T *sWq = reinterpret_cast<T *>(smem + ly.wq);
+  T *sVt = reinterpret_cast<T *>(smem + ly.vt);
+  T *sKr = reinterpret_cast<T *>(smem + ly.kr);
+  T *sKown = reinterpret_cast<T *>(smem + ly.kown);
+  T *sLgT = sKown;  // log gamma^T [f][s], dead before the keys are written
+  float *sTot = reinterpret_cast<float *>(smem + ly.tot);
+  float *sP7 = reinterpret_cast<float *>(smem + ly.p7);
+  float *sETot = reinterpret_cast<float *>(smem + ly.etot);
+  float *sENP7 = reinterpret_cast<float *>(smem + ly.enp7);
+  float *sENR8 = reinterpret_cast<float *>(smem + ly.enr8);
+  T *sSbf = reinterpret_cast<T *>(smem + ly.sbf);
+  T *sTvT = reinterpret_cast<T *>(smem + ly.tvt);
+  T *sTk = reinterpret_cast<T *>(smem + ly.tk);
+  const int NR = p.nring, KR = p.kring;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const bool key_wave = wv >= 4;
+  const int I = wv & 3;  // sub-chunk of this wave
+
+  // ---- block -> (group, value block), keeping a group's value blocks on one XCD
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, slot = bid >> 3;
+  const int grp = (slot / p.ndvb) * 8 + xcd;
+  const int dvb = slot % p.ndvb;
+  if (grp >= p.ngroups) return;
+  const int seg = grp % p.nseg;
+  const int bh = grp / p.nseg;
+  const int b = bh / p.Hkv, kvh = bh % p.Hkv;
+  const int L = p.L, G = MULTI_G ? p.G : 1;
+  const int dv0 = dvb * DV;
+  const int c_begin = seg * p.cps;
+  const int c_end = min(p.nchunks, c_begin + p.cps);
+
+  const size_t kv_off = ((size_t)b * p.Hkv + kvh) * (size_t)L * D;
+  const T *Kh = reinterpret_cast<const T *>(p.k) + kv_off;
+  const T *Vh = reinterpret_cast<const T *>(p.v) + kv_off;
+  const T *LGh = reinterpret_cast<const T *>(p.lg) + kv_off;
+  const T *Wk = reinterpret_cast<const T *>(p.wk) + (size_t)kvh * p.w_stride;
+  const T *Qbase = reinterpret_cast<const T *>(p.q);
+  const Frag<T> tri_pre = tri_frag<T>(r16, g4, true);
+
+  // ---- prologue, all waves: weights, meta tokens, zeroed rings
+  load_wT<T, D, LDW, 512>(sWk, Wk, tid);
+  if (ly.wq != ly.wk)
+    load_wT<T, D, LDW, 512>(sWq, reinterpret_cast<const T *>(p.wq) + (size_t)(kvh * G) * p.w_stride, tid);
+  {
+    const T *Tv = reinterpret_cast<const T *>(p.tv);
+    const T *Tk = reinterpret_cast<const T *>(p.tk);
+    for (int idx = tid; idx < DV * 16; idx += 512) {
+      const int dv = idx / 16, m = idx % 16;
+      sTvT[dv * LDM + m] = (m < p.M) ? Tv[((size_t)kvh * p.M + m) * D + dv0 + dv] : from_f<T>(0.f);
+    }
+    for (int idx = tid; idx < 16 * D; idx += 512) {
+      const int m = idx / D, e = idx % D;
+      sTk[m * LDW + e] = (m < p.M) ? Tk[((size_t)kvh * p.M + m) * D + e] : from_f<T>(0.f);
+    }
+    // rings start as zeros: a masked window slot (probability 0) must not meet a NaN pattern
+    uint4 *vz = reinterpret_cast<uint4 *>(smem + ly.vt);
+    const int nz = (ly.kown - ly.vt) / 16;  // value ring and key ring are contiguous
+    for (int idx = tid; idx < nz; idx += 512) vz[idx] = uint4{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();  // P1
+
+  if (key_wave) {
+    // ======================================================= key waves
+    const int kt = tid - 256;
+    // earlier chunks reached by the window of this segment's first chunk
+    const int R = max(NR, KR);
+    for (int cc = max(0, c_begin - (R - 1)); cc < c_begin; ++cc) {
+      ChunkRegs<T, D, DV> pre;
+      load_chunk<T, D, DV>(pre, Kh, Vh, LGh, cc * CH, L, dv0, true, kt);
+      if (cc > c_begin - KR) store_keys<T, D, DV, LDW>(pre, sKr + (cc % KR) * (CH * LDW), kt);
+      if (cc > c_begin - NR) store_values<T, D, DV, LDC>(pre, sVt + (cc % NR) * (DV * LDC), kt);
+    }
+    // S owned by this wave: feature tiles I*FTW .. +FTW-1, all value tiles.
+    // S[ft][dt][i] = S[16*(I*FTW+ft) + 4*g4 + i][dv0 + 16*dt + r16]
+    f32x4 S[FTW][NDT];
+#pragma unroll
+    for (int ft = 0; ft < FTW; ++ft)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) S[ft][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+      // start state of this segment: S = sum_j diag(prod of later decays) E_j
+      const size_t st_per_grp = (size_t)D * DV;
+      for (int j = 0; j < seg; ++j) {
+        const float *E = p.ws_state + ((((size_t)b * p.Hkv + kvh) * p.ndvb + dvb) * (p.nseg - 1) + j) * st_per_grp;
+        const float *Dj = p.ws_decay + (((size_t)b * p.Hkv + kvh) * (p.nseg - 1) + j) * D;
+#pragma unroll
+        for (int ft = 0; ft < FTW; ++ft) {
+          float e[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) e[i] = __expf(Dj[16 * (I * FTW + ft) + 4 * g4 + i]);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            const f32x4 x = *reinterpret_cast<const f32x4 *>(E + (((size_t)(I * FTW + ft) * NDT + dt) * 64 + lane) * 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[ft][dt][i] = e[i] * S[ft][dt][i] + x[i];
+          }
+        }
+      }
+    }
+    const Frag<T> tri_suf = tri_frag<T>(r16, g4, false);
+    ChunkRegs<T, D, DV> pf;
+    load_chunk<T, D, DV>(pf, Kh, Vh, LGh, c_begin * CH, L, dv0, true, kt);
+    __syncthreads();  // P2: prologue LDS writes complete
+#pragma unroll
+    for (int ft = 0; ft < FTW; ++ft)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        store4<T>(sSbf + (16 * dt + r16) * LDW + 16 * (I * FTW + ft) + 4 * g4, S[ft][dt][0], S[ft][dt][1],
+                  S[ft][dt][2], S[ft][dt][3]);
+
+    for (int c = c_begin; c < c_end; ++c) {
+      const int c0 = c * CH;
+      const int kcur = (c % KR) * (CH * LDW);
+      const int cur = (c % NR) * (DV * LDC);
+      store_keys<T, D, DV, LDW>(pf, sKr + kcur, kt);
+      store_values<T, D, DV, LDC>(pf, sVt + cur, kt);
+      store_lgT<T, D, DV, LDC>(pf, sLgT, kt);
+      __syncthreads();  // B0
+
+      // ---- A: gate sums inside the sub-chunk, phi_k, keys decayed to the sub-chunk end
+      float pfx[NFT][4], sfx[NFT][4];
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft) {
+        const Frag<T> a = (g4 < 2) ? load8(sLgT + (16 * ft + r16) * LDC + 16 * I + 8 * g4) : frag_zero<T>();
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 pp = mma(a, tri_pre, zero);
+        const f32x4 ss = mma(a, tri_suf, zero);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { pfx[ft][i] = pp[i]; sfx[ft][i] = ss[i]; }
+      }
+      if (r16 == 15 || r16 == 7) {
+        float *dst = (r16 == 15 ? sTot : sP7) + I * D + 4 * g4;
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft)
+          *reinterpret_cast<f32x4 *>(dst + 16 * ft) = f32x4{pfx[ft][0], pfx[ft][1], pfx[ft][2], pfx[ft][3]};
+      }
+      float ko[NFT][4];
+      {
+        Frag<T> kf[KS];
+#pragma unroll
+        for (int j = 0; j < KS; ++j) kf[j] = load8(sKr + kcur + (16 * I + r16) * LDW + 32 * j + 8 * g4);
+        f32x4 z[NFT];
+        feature_logits<T, D, LDW>(sWk, kf, r16, g4, z);
+        softmax_rows<NFT>(z, ko);
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ko[ft][i] *= __expf(sfx[ft][i]);
+      }
+      // next chunk's keys, values and log gamma in flight during the rest of this one
+      if (c + 1 < c_end) load_chunk<T, D, DV>(pf, Kh, Vh, LGh, c0 + CH, L, dv0, true, kt);
+      __syncthreads();  // B1
+
+      // ---- B: per-feature tables for this chunk; decayed keys -> LDS [s][f]
+      {
+        constexpr int PER = 4 / (256 / D);  // sub-chunks handled per thread
+        const int f = kt % D, j0 = (kt / D) * PER;
+#pragma unroll
+        for (int jj = 0; jj < PER; ++jj) {
+          const int J = j0 + jj;
+          const float tt = sTot[J * D + f];
+          const float p7 = sP7[J * D + f];
+          sETot[J * D + f] = __expf(tt);
+          sENP7[J * D + f] = __expf(-p7);
+          sENR8[J * D + f] = __expf(p7 - tt);
+        }
+      }
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft)
+        store4<T>(sKown + (16 * I + r16) * LDW + 16 * ft + 4 * g4, ko[ft][0], ko[ft][1], ko[ft][2], ko[ft][3]);
+      __syncthreads();  // B2
+
+      // ---- C: state update in registers: S = diag(prod_J e^{tot_J}) S + sum_s KSt[s] v_s^T with
+      //      KSt[s][f] = ko[s][f] prod_{J' > J(s)} e^{tot_J'}[f] gathered from LDS
+#pragma unroll
+      for (int ft = 0; ft < FTW; ++ft) {
+        const int fr = 16 * (I * FTW + ft);
+        float e[4] = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+          const f32x4 t = *reinterpret_cast<const f32x4 *>(sETot + J * D + fr + 4 * g4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) e[i] *= t[i];
+        }
+        float et[4];
+#pragma unroll
+        for (int J = 0; J < 4; ++J) et[J] = sETot[J * D + fr + r16];
+        Frag<T> ka[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int J = 2 * ks + (g4 >> 1);  // rows 32ks + 8g4 .. +7 lie in sub-chunk J
+          float fac = 1.f;
+#pragma unroll
+          for (int J2 = 1; J2 < 4; ++J2)
+            if (J2 > J) fac *= et[J2];
+          float x[8];
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) x[jj] = to_f(sKown[(32 * ks + 8 * g4 + jj) * LDW + fr + r16]) * fac;
+          ka[ks] = frag_from<T>(x);
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S[ft][dt][i] *= e[i];
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+            S[ft][dt] = mma(ka[ks], load8(sVt + cur + (16 * dt + r16) * LDC + 32 * ks + 8 * g4), S[ft][dt]);
+        }
+      }
+      __syncthreads();  // B3
+
+      // ---- D: publish the new state copy (read by the query waves after the next B2)
+#pragma unroll
+      for (int ft = 0; ft < FTW; ++ft)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          store4<T>(sSbf + (16 * dt + r16) * LDW + 16 * (I * FTW + ft) + 4 * g4, S[ft][dt][0], S[ft][dt][1],
+                    S[ft][dt][2], S[ft][dt][3]);
+    }
+  } else {
+    // ======================================================= query waves
+    const float mix = p.mix, scale = p.scale;
+    constexpr bool win_fast = FASTWIN;
+    // fast window: bit 4u+i set when slot (tile u, row 4 g4 + i) is inside the window of this
+    // lane's query (u = 0 meta; band tile u: kj - pos = 16u - 80 + 4 g4 + i - r16)
+    uint32_t wmask = 0;
+#pragma unroll
+    for (int u = 0; u < 6; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int dk = 16 * u - 80 + 4 * g4 + i - r16;
+        const bool in = (u == 0) ? (4 * g4 + i < p.M) : (dk <= 0 && dk > -p.W);
+        wmask |= (in ? 1u : 0u) << (4 * u + i);
+      }
+    const T *Q0 = Qbase + ((size_t)b * p.Hq + kvh * G) * (size_t)L * D;
+    Frag<T> pfq[KS];
+    {
+      const int pos0 = c_begin * CH + 16 * I + r16;
+#pragma unroll
+      for (int j = 0; j < KS; ++j) pfq[j] = (pos0 < L) ? load8(Q0 + (size_t)pos0 * D + 32 * j + 8 * g4) : frag_zero<T>();
+    }
+    __syncthreads();  // P2
+
+    for (int c = c_begin; c < c_end; ++c) {
+      const int c0 = c * CH;
+      const int kcur = (c % KR) * (CH * LDW);
+      const int cur = (c % NR) * (DV * LDC);
+      const int kprev = ((c + KR - 1) % KR) * (CH * LDW);  // used only when KR >= 2
+      const int vprev = ((c + NR - 1) % NR) * (DV * LDC);
+      const int pos = c0 + 16 * I + r16;
+      const bool valid = pos < L;
+      Frag<T> qf[KS];
+#pragma unroll
+      for (int j = 0; j < KS; ++j) qf[j] = pfq[j];
+
+      // phi_q for the rows of this wave, decayed from the sub-chunk start (qo <= phi_q)
+      auto query_features = [&](const float (&pfx)[NFT][4], float (&qo)[NFT][4]) {
+        f32x4 z[NFT];
+        feature_logits<T, D, LDW>(sWq, qf, r16, g4, z);
+        softmax_rows<NFT>(z, qo);
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) qo[ft][i] *= __expf(pfx[ft][i]);
+      };
+
+      // fast window, logits: the meta tile and the five 16-key tiles ending at this
+      // sub-chunk; band tile u (1..5) starts at chunk-relative row 16 (I - 5 + u).
+      // Leaves the unnormalised probabilities as three K = 32 operand fragments.
+      auto window_fast_logits = [&](Frag<T> (&pw)[3], float &l_run) {
+        f32x4 lt[6];
+        {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < KS; ++j) acc = mma(load8(sTk + r16 * LDW + 32 * j + 8 * g4), qf[j], acc);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lt[0][i] = ((wmask >> i) & 1u) ? acc[i] * scale : NEG_BIG;
+        }
+#pragma unroll
+        for (int u = 1; u < 6; ++u) {
+          const int rt = I - 5 + u;  // chunk-relative tile, < 0: previous chunk
+          const T *kr = sKr + (rt < 0 ? kprev + (rt + 4) * 16 * LDW : kcur + rt * 16 * LDW) + r16 * LDW + 8 * g4;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < KS; ++j) acc = mma(load8(kr + 32 * j), qf[j], acc);
+          const uint32_t mu = ((c == 0) && rt < 0) ? 0u : (wmask >> (4 * u));  // no keys before 0
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lt[u][i] = ((mu >> i) & 1u) ? acc[i] * scale : NEG_BIG;
+        }
+        float bm = NEG_BIG;
+#pragma unroll
+        for (int u = 0; u < 6; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) bm = fmaxf(bm, lt[u][i]);
+        bm = wave_max_cols(bm);
+        l_run = 0.f;
+#pragma unroll
+        for (int pr = 0; pr < 3; ++pr) {
+          float x[8];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float pv = __expf(lt[2 * pr + h][i] - bm);  // masked: exp(-1e30) = 0
+              x[4 * h + i] = pv;
+              l_run += pv;
+            }
+          pw[pr] = frag_from<T>(x);
+        }
+      };
+      auto window_fast_pv = [&](const Frag<T> (&pw)[3], f32x4 (&ywin)[NDT]) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) ywin[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int pr = 0; pr < 3; ++pr) {
+          const int ua = 2 * pr, ub = 2 * pr + 1;
+          const int rta = I - 5 + ua, rtb = I - 5 + ub;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            const int dvl = 16 * dt + r16;
+            const T *pa = (ua == 0) ? sTvT + dvl * LDM + 4 * g4
+                                    : sVt + (rta < 0 ? vprev + 16 * (rta + 4) : cur + 16 * rta) + dvl * LDC + 4 * g4;
+            const T *pb = sVt + (rtb < 0 ? vprev + 16 * (rtb + 4) : cur + 16 * rtb) + dvl * LDC + 4 * g4;
+            ywin[dt] = mma(load4x2(pa, pb), pw[pr], ywin[dt]);
+          }
+        }
+      };
+      // general window: batches of key tiles with an online softmax (keys older than
+      // the LDS rings come from global memory)
+      auto window_general = [&](f32x4 (&ywin)[NDT], float &l_run) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) ywin[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        l_run = 0.f;
+        float m_run = NEG_BIG;
+        const int kt_hi = (c0 >> 4) + I;
+        const int lo_key = c0 + 16 * I - p.W + 1;
+        const int kt_lo = lo_key <= 0 ? 0 : (lo_key >> 4);
+        // tile list: u = -1 is the meta tile (if M > 0), then kt_lo..kt_hi
+        const int u_first = (p.M > 0) ? -1 : 0;
+        const int n_tiles = (kt_hi - kt_lo + 1) - u_first;
+        for (int u0 = 0; u0 < n_tiles; u0 += WIN_BATCH) {
+          f32x4 lt[WIN_BATCH];
+#pragma unroll
+          for (int uu = 0; uu < WIN_BATCH; ++uu) {
+            const int u = u0 + uu;
+            lt[uu] = f32x4{NEG_BIG, NEG_BIG, NEG_BIG, NEG_BIG};
+            if (u < n_tiles) {
+              const int kt = (u + u_first < 0) ? -1 : kt_lo + u + u_first;
+              f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+              if (kt < 0) {
+#pragma unroll
+                for (int j = 0; j < KS; ++j) acc = mma(load8(sTk + r16 * LDW + 32 * j + 8 * g4), qf[j], acc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) lt[uu][i] = (4 * g4 + i < p.M) ? acc[i] * scale : NEG_BIG;
+              } else {
+                const int kc = kt >> 2;
+                if (kc > c - KR) {
+                  const T *kr = sKr + (kc % KR) * (CH * LDW) + (16 * (kt & 3) + r16) * LDW + 8 * g4;
+#pragma unroll
+                  for (int j = 0; j < KS; ++j) acc = mma(load8(kr + 32 * j), qf[j], acc);
+                } else {
+                  // key tile older than the LDS ring: global memory
+                  const int key = 16 * kt + r16;
+                  const bool kv = key < L;
+#pragma unroll
+                  for (int j = 0; j < KS; ++j) {
+                    const Frag<T> a = kv ? load8(Kh + (size_t)key * D + 32 * j + 8 * g4) : frag_zero<T>();
+                    acc = mma(a, qf[j], acc);
+                  }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const int kj = 16 * kt + 4 * g4 + i;
+                  lt[uu][i] = (kj <= pos && kj > pos - p.W) ? acc[i] * scale : NEG_BIG;
+                }
+              }
+            }
+          }
+          float bm = NEG_BIG;
+#pragma unroll
+          for (int uu = 0; uu < WIN_BATCH; ++uu)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bm = fmaxf(bm, lt[uu][i]);
+          bm = wave_max_cols(bm);
+          const float m_new = fmaxf(m_run, bm);
+          const float alpha = __expf(m_run - m_new);
+          l_run *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ywin[dt][i] *= alpha;
+          m_run = m_new;
+          // P V: pairs of tiles form one K = 32 step
+#pragma unroll
+          for (int pr = 0; pr < WIN_BATCH / 2; ++pr) {
+            const int ua = u0 + 2 * pr, ub = ua + 1;
+            if (ua >= n_tiles) continue;
+            float x[8];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float l = lt[2 * pr + h][i];
+                const float pv = (l > 0.5f * NEG_BIG) ? __expf(l - m_new) : 0.f;
+                x[4 * h + i] = pv;
+                l_run += pv;
+              }
+            const Frag<T> bf = frag_from<T>(x);
+            const int kta = (ua + u_first < 0) ? -1 : kt_lo + ua + u_first;
+            const int ktb = (ub >= n_tiles) ? -2 : kt_lo + ub + u_first;
+            const bool ring_a = kta >= 0 && (kta >> 2) > c - NR;
+            const bool ring_b = ktb >= 0 && (ktb >> 2) > c - NR;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+              const int dvl = 16 * dt + r16;
+              const T *pa = (kta < 0) ? sTvT + dvl * LDM + 4 * g4
+                                      : sVt + ((kta >> 2) % NR) * (DV * LDC) + dvl * LDC + 16 * (kta & 3) + 4 * g4;
+              const T *pb = (ktb < 0) ? pa : sVt + ((ktb >> 2) % NR) * (DV * LDC) + dvl * LDC + 16 * (ktb & 3) + 4 * g4;
+              Frag<T> af;
+              if ((kta < 0 || ring_a) && (ktb < 0 || ring_b)) {
+                af = load4x2(pa, pb);  // slots of a missing second tile meet P = 0
+              } else {
+                // a value tile older than the LDS ring: gather from global memory
+                float av[8];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                  const int kt = h ? ktb : kta;
+                  const bool inring = h ? ring_b : ring_a;
+                  if (kt == -2) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) av[4 * h + i] = 0.f;
+                  } else if (kt == -1 || inring) {
+                    float t4[4];
+                    load4f(h ? pb : pa, t4);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) av[4 * h + i] = t4[i];
+                  } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                      const int key = 16 * kt + 4 * g4 + i;
+                      av[4 * h + i] = (key < L) ? to_f(Vh[(size_t)key * D + dv0 + dvl]) : 0.f;
+                    }
+                  }
+                }
+                af = frag_from<T>(av);
+              }
+              ywin[dt] = mma(af, bf, ywin[dt]);
+            }
+          }
+        }
+      };
+
+      __syncthreads();  // B0
+      // ---- A: prefix sums of log gamma inside the sub-chunk; phi_q and window logits of head 0
+      float pfx[NFT][4];
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft) {
+        const Frag<T> a = (g4 < 2) ? load8(sLgT + (16 * ft + r16) * LDC + 16 * I + 8 * g4) : frag_zero<T>();
+        const f32x4 pp = mma(a, tri_pre, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pfx[ft][i] = pp[i];
+      }
+      bool safe;
+      {
+        // the sub-chunk's log decay spans at most -min_t prefix (log gamma <= 0)
+        float span = 0.f;
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) span = fmaxf(span, -pfx[ft][i]);
+        safe = wave_max_all(span) <= SPAN_MAX;
+      }
+      float qo[NFT][4];
+      query_features(pfx, qo);
+      Frag<T> pw[3];
+      float l_run = 0.f;
+      if constexpr (win_fast) window_fast_logits(pw, l_run);
+      // next chunk's first query head in flight during the rest of this one
+      if (c + 1 < c_end) {
+        const int pn = pos + CH;
+#pragma unroll
+        for (int j = 0; j < KS; ++j) pfq[j] = (pn < L) ? load8(Q0 + (size_t)pn * D + 32 * j + 8 * g4) : frag_zero<T>();
+      }
+      __syncthreads();  // B1
+
+      // ---- B: window products of head 0
+      f32x4 ywin[NDT];
+      if constexpr (win_fast)
+        window_fast_pv(pw, ywin);
+      else
+        window_general(ywin, l_run);
+      __syncthreads();  // B2
+
+      // ---- C: intra- and inter-chunk products, merge, store; later query heads in turn
+      Frag<T> kmid[KS];  // diagonal-block key operand: ko e^{p7 - tot} (reference at row 7)
+      if (safe) {
+#pragma unroll
+        for (int js = 0; js < KS; ++js) {
+          float t8[8], kv[8];
+          tab8(sENR8 + I * D, js, g4, t8);
+          const T *kr = sKown + (16 * I + r16) * LDW + 32 * js + 4 * g4;
+          const Frag<T> kk = load4x2(kr, kr + 16);
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) kv[jj] = to_f(kk.v[jj]) * t8[jj];
+          kmid[js] = frag_from<T>(kv);
+        }
+      }
+      for (int g = 0; g < G; ++g) {
+        const int hq = kvh * G + g;
+        if (g > 0) {
+          const T *Qh = Qbase + ((size_t)b * p.Hq + hq) * (size_t)L * D;
+#pragma unroll
+          for (int j = 0; j < KS; ++j) qf[j] = valid ? load8(Qh + (size_t)pos * D + 32 * j + 8 * g4) : frag_zero<T>();
+          query_features(pfx, qo);
+          if constexpr (win_fast) {
+            window_fast_logits(pw, l_run);
+            window_fast_pv(pw, ywin);
+          } else {
+            window_general(ywin, l_run);
+          }
+        }
+
+        // ---- intra-chunk scores A^T[s][t] for key sub-chunks J <= I
+        f32x4 at[4];
+#pragma unroll
+        for (int J = 0; J < 4; ++J) at[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int J = 0; J < 3; ++J) {
+          if (J < I) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int js = 0; js < KS; ++js) {
+              float x[8];
+#pragma unroll
+              for (int jj = 0; jj < 8; ++jj) x[jj] = qo[2 * js + (jj >> 2)][jj & 3];
+              // prod_{J<J'<I} e^{tot_J'} joins the two references
+#pragma unroll
+              for (int J2 = 1; J2 < 3; ++J2) {
+                if (J2 > J && J2 < I) {
+                  float t8[8];
+                  tab8(sETot + J2 * D, js, g4, t8);
+#pragma unroll
+                  for (int jj = 0; jj < 8; ++jj) x[jj] *= t8[jj];
+                }
+              }
+              const T *kr = sKown + (16 * J + r16) * LDW + 32 * js + 4 * g4;
+              acc = mma(load4x2(kr, kr + 16), frag_from<T>(x), acc);
+            }
+            at[J] = acc;
+          }
+        }
+        {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          if (safe) {
+#pragma unroll
+            for (int js = 0; js < KS; ++js) {
+              float t8[8], x[8];
+              tab8(sENP7 + I * D, js, g4, t8);
+#pragma unroll
+              for (int jj = 0; jj < 8; ++jj) x[jj] = qo[2 * js + (jj >> 2)][jj & 3] * t8[jj];
+              acc = mma(kmid[js], frag_from<T>(x), acc);
+            }
+          } else {
+            // exact: A[t][s] = sum_f phi_q[t][f] phi_k[s][f] e^{p_t[f] - p_s[f]}, with phi
+            // recomputed in fp32 (rare path: a sub-chunk whose log decay spans > SPAN_MAX)
+            float phk[NFT][4], phq[NFT][4];
+            {
+              Frag<T> kf[KS];
+#pragma unroll
+              for (int j = 0; j < KS; ++j) kf[j] = load8(sKr + kcur + (16 * I + r16) * LDW + 32 * j + 8 * g4);
+              f32x4 z[NFT];
+              feature_logits<T, D, LDW>(sWk, kf, r16, g4, z);
+              softmax_rows<NFT>(z, phk);
+              feature_logits<T, D, LDW>(sWq, qf, r16, g4, z);
+              softmax_rows<NFT>(z, phq);
+            }
+#pragma unroll 1
+            for (int s2 = 0; s2 < 16; ++s2) {
+              float part = 0.f;
+#pragma unroll
+              for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const float pk = __shfl(phk[ft][i], 16 * g4 + s2);
+                  const float bs = __shfl(pfx[ft][i], 16 * g4 + s2);
+                  const float term = phq[ft][i] * pk * __expf(pfx[ft][i] - bs);
+                  part += (s2 <= r16) ? term : 0.f;
+                }
+              part = wave_sum_cols(part);
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if ((s2 >> 2) == g4 && (s2 & 3) == i) acc[i] = part;
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] = (4 * g4 + i <= r16) ? acc[i] : 0.f;
+#pragma unroll
+          for (int J = 0; J < 4; ++J)
+            if (J == I) at[J] = acc;  // compile-time index keeps at[] in registers
+        }
+
+        // ---- Y^T = V^T A^T (intra) + S^T q~int^T (inter); lane holds Y^T[dv][t]
+        f32x4 yacc[NDT];
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) yacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int J0 = 0; J0 < 4; J0 += 2) {
+          if (J0 <= I) {
+            const bool has1 = (J0 + 1) <= I;
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              x[i] = at[J0][i];
+              x[4 + i] = has1 ? at[J0 + 1][i] : 0.f;
+            }
+            const Frag<T> bf = frag_from<T>(x);
+            const int J1 = has1 ? J0 + 1 : J0;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+              const T *vr = sVt + cur + (16 * dt + r16) * LDC + 4 * g4;
+              yacc[dt] = mma(load4x2(vr + 16 * J0, vr + 16 * J1), bf, yacc[dt]);
+            }
+          }
+        }
+#pragma unroll
+        for (int js = 0; js < KS; ++js) {
+          float x[8];
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) x[jj] = qo[2 * js + (jj >> 2)][jj & 3];
+          // prod_{J<I} e^{tot_J}: decay from the chunk start to the sub-chunk start
+#pragma unroll
+          for (int J2 = 0; J2 < 3; ++J2) {
+            if (J2 < I) {
+              float t8[8];
+              tab8(sETot + J2 * D, js, g4, t8);
+#pragma unroll
+              for (int jj = 0; jj < 8; ++jj) x[jj] *= t8[jj];
+            }
+          }
+          const Frag<T> bf = frag_from<T>(x);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            const T *sr = sSbf + (16 * dt + r16) * LDW + 32 * js + 4 * g4;
+            yacc[dt] = mma(load4x2(sr, sr + 16), bf, yacc[dt]);
+          }
+        }
+
+        const float l_tot = wave_sum_cols(l_run);
+        const float wscale = (1.f - mix) / l_tot;
+        // ---- merge and store (lane holds Y^T[dv0 + 16 dt + 4 g4 + i][pos])
+        if (valid) {
+          T *O = reinterpret_cast<T *>(p.out) + (((size_t)b * p.Hq + hq) * (size_t)L + pos) * D + dv0;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            float o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = mix * yacc[dt][i] + wscale * ywin[dt][i];
+            store4<T>(O + 16 * dt + 4 * g4, o[0], o[1], o[2], o[3]);
+          }
+        }
+      }  // g
+      __syncthreads();  // B3
+    }
+  }
+}
+
+template <typename T, int D, int DV, bool FASTWIN, bool MULTI_G>
+static hipError_t launch_split_one(const FwdParams &p, hipStream_t stream) {
+  const int grid = ((p.ngroups + 7) / 8) * 8 * p.ndvb;
+  auto kern = fwd_split_kernel<T, D, DV, FASTWIN, MULTI_G>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, p.lds.total);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(512), p.lds.total, stream, p);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int DV>
+hipError_t launch_fwd_split(const FwdParams &p, hipStream_t stream) {
+  const bool fastwin = (p.W <= CH + 1) && p.kring >= 2 && p.nring >= 2;
+  const bool multi_g = p.G > 1;
+  if (fastwin) return multi_g ? launch_split_one<T, D, DV, true, true>(p, stream)
+                              : launch_split_one<T, D, DV, true, false>(p, stream);
+  return multi_g ? launch_split_one<T, D, DV, false, true>(p, stream)
+                 : launch_split_one<T, D, DV, false, false>(p, stream);
+}
+
+template hipError_t launch_fwd_split<bf16, 64, 64>(const FwdParams &, hipStream_t);
+template hipError_t launch_fwd_split<bf16, 128, 64>(const FwdParams &, hipStream_t);
+template hipError_t launch_fwd_split<float, 64, 64>(const FwdParams &, hipStream_t);
+
+}  // namespace lz
