@@ -12,6 +12,8 @@ constexpr int CH = 64;            // chunk length
 constexpr float SPAN_MAX = 80.f;  // max |log-decay| across one 16-token sub-chunk for the
                                   // mid-reference MFMA path (e^80 ~ 5.5e34 < fp32/bf16 max)
 constexpr float NEG_BIG = -1.0e30f;
+constexpr float FAST_SPAN = 60.f; // max |log-decay| across a whole chunk for the chunk-start
+                                  // reference (keys carry e^{+60} at most, queries e^{-60})
 constexpr int LDS_LIMIT = 160 * 1024;
 constexpr int WIN_BATCH = 8;      // key tiles per online-softmax batch in the window
 
@@ -230,6 +232,20 @@ __device__ __forceinline__ void feature_logits2(const T *sW, const Frag<T> (&xa)
       zb[ft] = mma(w, xb[j], zb[ft]);
     }
   }
+}
+
+// True when every feature's log decay over the whole chunk is at most FAST_SPAN
+// in magnitude (sTot holds the four sub-chunk sums); the same value in every
+// wave of the workgroup.
+template <int D>
+__device__ __forceinline__ bool chunk_is_mild(const float *sTot, int lane) {
+  float m = 0.f;
+#pragma unroll
+  for (int q = 0; q < D / 64; ++q) {
+    const int f = lane + 64 * q;
+    m = fmaxf(m, -(sTot[f] + sTot[D + f] + sTot[2 * D + f] + sTot[3 * D + f]));
+  }
+  return wave_max_all(m) <= FAST_SPAN;
 }
 
 // Role-split forward (fwd_split.hip): 8 waves per workgroup.

@@ -12,12 +12,18 @@
 // Each role runs its own loop over the chunks; both loops pass the same four
 // workgroup barriers per chunk, so the roles stay in step:
 //   B0  chunk c's keys, values and log gamma are in LDS
-//   B1  sub-chunk totals written (key waves), log gamma consumed (both)
+//   B1  sub-chunk totals written (key waves), log gamma consumed (both); every
+//       wave then classifies the chunk: if its log decay stays within FAST_SPAN
+//       for every feature, all decays are referred to the chunk start (keys
+//       carry e^{-p_s}, queries e^{p_t}), which removes the per-block factor
+//       products; otherwise the sub-chunk references of fwd.hip are used
 //   B2  factor tables and decayed keys in LDS
 //   B3  every read of the state copy, the decayed keys and the ring slot about
 //       to be reused is done; the key waves then publish the new state copy.
 // Two waves per SIMD (512 threads, one workgroup per CU) let one role's
 // memory and matrix-core latency hide behind the other's work.
+#include <type_traits>
+
 #include "fwd_common.hpp"
 
 namespace lz {
@@ -140,7 +146,6 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
         }
       }
     }
-    const Frag<T> tri_suf = tri_frag<T>(r16, g4, false);
     ChunkRegs<T, D, DV> pf;
     load_chunk<T, D, DV>(pf, Kh, Vh, LGh, c_begin * CH, L, dv0, true, kt);
     __syncthreads();  // P2: prologue LDS writes complete
@@ -152,6 +157,9 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
                   S[ft][dt][2], S[ft][dt][3]);
 
     for (int c = c_begin; c < c_end; ++c) {
+      int lane_o = lane;
+      asm volatile("" : "+v"(lane_o));  // lane-dependent addresses are recomputed, not held live
+      const int r16 = lane_o & 15, g4 = lane_o >> 4;
       const int c0 = c * CH;
       const int kcur = (c % KR) * (CH * LDW);
       const int cur = (c % NR) * (DV * LDC);
@@ -160,16 +168,14 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
       store_lgT<T, D, DV, LDC>(pf, sLgT, kt);
       __syncthreads();  // B0
 
-      // ---- A: gate sums inside the sub-chunk, phi_k, keys decayed to the sub-chunk end
-      float pfx[NFT][4], sfx[NFT][4];
+      // ---- A: gate prefix sums inside the sub-chunk, phi_k (decayed in B)
+      float pfx[NFT][4];
 #pragma unroll
       for (int ft = 0; ft < NFT; ++ft) {
         const Frag<T> a = (g4 < 2) ? load8(sLgT + (16 * ft + r16) * LDC + 16 * I + 8 * g4) : frag_zero<T>();
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 pp = mma(a, tri_pre, zero);
-        const f32x4 ss = mma(a, tri_suf, zero);
+        const f32x4 pp = mma(a, tri_pre, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { pfx[ft][i] = pp[i]; sfx[ft][i] = ss[i]; }
+        for (int i = 0; i < 4; ++i) pfx[ft][i] = pp[i];
       }
       if (r16 == 15 || r16 == 7) {
         float *dst = (r16 == 15 ? sTot : sP7) + I * D + 4 * g4;
@@ -185,17 +191,31 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
         f32x4 z[NFT];
         feature_logits<T, D, LDW>(sWk, kf, r16, g4, z);
         softmax_rows<NFT>(z, ko);
-#pragma unroll
-        for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) ko[ft][i] *= __expf(sfx[ft][i]);
       }
       // next chunk's keys, values and log gamma in flight during the rest of this one
       if (c + 1 < c_end) load_chunk<T, D, DV>(pf, Kh, Vh, LGh, c0 + CH, L, dv0, true, kt);
       __syncthreads();  // B1
+      const bool mild = chunk_is_mild<D>(sTot, lane);
 
-      // ---- B: per-feature tables for this chunk; decayed keys -> LDS [s][f]
-      {
+      // ---- B: decayed keys -> LDS [s][f] and the per-feature tables.  Mild chunk: keys
+      //      carry e^{-p_s} (p = log decay from the chunk start), table e^{B_c}.  Otherwise
+      //      keys carry e^{tot_I - pfx} (decay to the sub-chunk end) and the sub-chunk tables.
+      if (mild) {
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft) {
+          f32x4 pI = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int J = 0; J < 3; ++J)
+            if (J < I) {
+              const f32x4 t = *reinterpret_cast<const f32x4 *>(sTot + J * D + 16 * ft + 4 * g4);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) pI[i] += t[i];
+            }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ko[ft][i] *= __expf(-(pI[i] + pfx[ft][i]));
+        }
+        if (kt < D) sETot[kt] = __expf(sTot[kt] + sTot[D + kt] + sTot[2 * D + kt] + sTot[3 * D + kt]);
+      } else {
         constexpr int PER = 4 / (256 / D);  // sub-chunks handled per thread
         const int f = kt % D, j0 = (kt / D) * PER;
 #pragma unroll
@@ -207,38 +227,58 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
           sENP7[J * D + f] = __expf(-p7);
           sENR8[J * D + f] = __expf(p7 - tt);
         }
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft) {
+          const f32x4 t = *reinterpret_cast<const f32x4 *>(sTot + I * D + 16 * ft + 4 * g4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ko[ft][i] *= __expf(t[i] - pfx[ft][i]);
+        }
       }
 #pragma unroll
       for (int ft = 0; ft < NFT; ++ft)
         store4<T>(sKown + (16 * I + r16) * LDW + 16 * ft + 4 * g4, ko[ft][0], ko[ft][1], ko[ft][2], ko[ft][3]);
       __syncthreads();  // B2
 
-      // ---- C: state update in registers: S = diag(prod_J e^{tot_J}) S + sum_s KSt[s] v_s^T with
-      //      KSt[s][f] = ko[s][f] prod_{J' > J(s)} e^{tot_J'}[f] gathered from LDS
+      // ---- C: state update in registers: S = diag(e^{B_c}) S + sum_s KSt[s] v_s^T, where
+      //      KSt[s][f] = phi_k[s][f] e^{B_c - p_s}: the decayed keys gathered from LDS times
+      //      e^{B_c} (mild) or prod_{J' > J(s)} e^{tot_J'} (sub-chunk references)
 #pragma unroll
       for (int ft = 0; ft < FTW; ++ft) {
         const int fr = 16 * (I * FTW + ft);
-        float e[4] = {1.f, 1.f, 1.f, 1.f};
+        float e[4];
+        float fac[2];
+        if (mild) {
+          const f32x4 t = *reinterpret_cast<const f32x4 *>(sETot + fr + 4 * g4);
 #pragma unroll
-        for (int J = 0; J < 4; ++J) {
-          const f32x4 t = *reinterpret_cast<const f32x4 *>(sETot + J * D + fr + 4 * g4);
+          for (int i = 0; i < 4; ++i) e[i] = t[i];
+          fac[0] = fac[1] = sETot[fr + r16];
+        } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) e[i] *= t[i];
+          for (int i = 0; i < 4; ++i) e[i] = 1.f;
+#pragma unroll
+          for (int J = 0; J < 4; ++J) {
+            const f32x4 t = *reinterpret_cast<const f32x4 *>(sETot + J * D + fr + 4 * g4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) e[i] *= t[i];
+          }
+          float et[4];
+#pragma unroll
+          for (int J = 0; J < 4; ++J) et[J] = sETot[J * D + fr + r16];
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const int J = 2 * ks + (g4 >> 1);  // rows 32ks + 8g4 .. +7 lie in sub-chunk J
+            fac[ks] = 1.f;
+#pragma unroll
+            for (int J2 = 1; J2 < 4; ++J2)
+              if (J2 > J) fac[ks] *= et[J2];
+          }
         }
-        float et[4];
-#pragma unroll
-        for (int J = 0; J < 4; ++J) et[J] = sETot[J * D + fr + r16];
         Frag<T> ka[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const int J = 2 * ks + (g4 >> 1);  // rows 32ks + 8g4 .. +7 lie in sub-chunk J
-          float fac = 1.f;
-#pragma unroll
-          for (int J2 = 1; J2 < 4; ++J2)
-            if (J2 > J) fac *= et[J2];
           float x[8];
 #pragma unroll
-          for (int jj = 0; jj < 8; ++jj) x[jj] = to_f(sKown[(32 * ks + 8 * g4 + jj) * LDW + fr + r16]) * fac;
+          for (int jj = 0; jj < 8; ++jj) x[jj] = to_f(sKown[(32 * ks + 8 * g4 + jj) * LDW + fr + r16]) * fac[ks];
           ka[ks] = frag_from<T>(x);
         }
 #pragma unroll
@@ -263,6 +303,7 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
   } else {
     // ======================================================= query waves
     const float mix = p.mix, scale = p.scale;
+    const float log_mix = __logf(mix);
     constexpr bool win_fast = FASTWIN;
     // fast window: bit 4u+i set when slot (tile u, row 4 g4 + i) is inside the window of this
     // lane's query (u = 0 meta; band tile u: kj - pos = 16u - 80 + 4 g4 + i - r16)
@@ -285,6 +326,9 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
     __syncthreads();  // P2
 
     for (int c = c_begin; c < c_end; ++c) {
+      int lane_o = lane;
+      asm volatile("" : "+v"(lane_o));  // lane-dependent addresses are recomputed, not held live
+      const int r16 = lane_o & 15, g4 = lane_o >> 4;
       const int c0 = c * CH;
       const int kcur = (c % KR) * (CH * LDW);
       const int cur = (c % NR) * (DV * LDC);
@@ -296,15 +340,18 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
 #pragma unroll
       for (int j = 0; j < KS; ++j) qf[j] = pfq[j];
 
-      // phi_q for the rows of this wave, decayed from the sub-chunk start (qo <= phi_q)
-      auto query_features = [&](const float (&pfx)[NFT][4], float (&qo)[NFT][4]) {
+      // phi_q for the rows of this wave (decayed separately, once the chunk's references are known)
+      auto query_phi = [&](float (&qo)[NFT][4]) {
         f32x4 z[NFT];
         feature_logits<T, D, LDW>(sWq, qf, r16, g4, z);
         softmax_rows<NFT>(z, qo);
+      };
+      // decay and the merge weight: qo *= mix e^{px}  (log_mix = log(mix), -inf for mix = 0)
+      auto decay_q = [&](float (&qo)[NFT][4], const float (&px)[NFT][4]) {
 #pragma unroll
         for (int ft = 0; ft < NFT; ++ft)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) qo[ft][i] *= __expf(pfx[ft][i]);
+          for (int i = 0; i < 4; ++i) qo[ft][i] *= __expf(px[ft][i] + log_mix);
       };
 
       // fast window, logits: the meta tile and the five 16-key tiles ending at this
@@ -493,6 +540,23 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
         }
       };
 
+      // whole window branch of one head, scaled for the merge: yw = (1 - mix) P V / sum(P)
+      auto window = [&](f32x4 (&yw)[NDT]) {
+        float l_run = 0.f;
+        if constexpr (win_fast) {
+          Frag<T> pw[3];
+          window_fast_logits(pw, l_run);
+          window_fast_pv(pw, yw);
+        } else {
+          window_general(yw, l_run);
+        }
+        const float ws = (1.f - mix) / wave_sum_cols(l_run);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) yw[dt][i] *= ws;
+      };
+
       __syncthreads();  // B0
       // ---- A: prefix sums of log gamma inside the sub-chunk; phi_q and window logits of head 0
       float pfx[NFT][4];
@@ -514,7 +578,7 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
         safe = wave_max_all(span) <= SPAN_MAX;
       }
       float qo[NFT][4];
-      query_features(pfx, qo);
+      query_phi(qo);
       Frag<T> pw[3];
       float l_run = 0.f;
       if constexpr (win_fast) window_fast_logits(pw, l_run);
@@ -525,183 +589,249 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
         for (int j = 0; j < KS; ++j) pfq[j] = (pn < L) ? load8(Q0 + (size_t)pn * D + 32 * j + 8 * g4) : frag_zero<T>();
       }
       __syncthreads();  // B1
+      const bool mild = chunk_is_mild<D>(sTot, lane);
+      if (mild) {
+        // chunk-start reference: the prefix grows by the totals of the earlier sub-chunks
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+          for (int J = 0; J < 3; ++J)
+            if (J < I) {
+              const f32x4 t = *reinterpret_cast<const f32x4 *>(sTot + J * D + 16 * ft + 4 * g4);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) pfx[ft][i] += t[i];
+            }
+      }
 
-      // ---- B: window products of head 0
+      // ---- B: decayed queries and window products of head 0 (scaled for the merge)
+      decay_q(qo, pfx);
       f32x4 ywin[NDT];
       if constexpr (win_fast)
         window_fast_pv(pw, ywin);
       else
         window_general(ywin, l_run);
+      {
+        const float ws = (1.f - mix) / wave_sum_cols(l_run);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ywin[dt][i] *= ws;
+      }
       __syncthreads();  // B2
 
-      // ---- C: intra- and inter-chunk products, merge, store; later query heads in turn
-      Frag<T> kmid[KS];  // diagonal-block key operand: ko e^{p7 - tot} (reference at row 7)
-      if (safe) {
+      // ---- C: intra- and inter-chunk products, merge, store; later query heads in turn.
+      //      The mild and the general case are separate instantiations so that their
+      //      registers never overlap.  yw enters holding the window output already
+      //      scaled by (1 - mix) / sum(P); the query operands carry mix, so the
+      //      products accumulate straight onto it and yw is the merged output.
+      auto heads = [&](auto mild_tag, f32x4 (&yw)[NDT]) {
+        constexpr bool MILD = decltype(mild_tag)::value;
+        Frag<T> kmid[KS];  // general case: diagonal-block key operand ko e^{p7 - tot}
+        if constexpr (!MILD) {
+          if (safe) {
 #pragma unroll
-        for (int js = 0; js < KS; ++js) {
-          float t8[8], kv[8];
-          tab8(sENR8 + I * D, js, g4, t8);
-          const T *kr = sKown + (16 * I + r16) * LDW + 32 * js + 4 * g4;
-          const Frag<T> kk = load4x2(kr, kr + 16);
+            for (int js = 0; js < KS; ++js) {
+              float t8[8], kv[8];
+              tab8(sENR8 + I * D, js, g4, t8);
+              const T *kr = sKown + (16 * I + r16) * LDW + 32 * js + 4 * g4;
+              const Frag<T> kk = load4x2(kr, kr + 16);
 #pragma unroll
-          for (int jj = 0; jj < 8; ++jj) kv[jj] = to_f(kk.v[jj]) * t8[jj];
-          kmid[js] = frag_from<T>(kv);
-        }
-      }
-      for (int g = 0; g < G; ++g) {
-        const int hq = kvh * G + g;
-        if (g > 0) {
-          const T *Qh = Qbase + ((size_t)b * p.Hq + hq) * (size_t)L * D;
-#pragma unroll
-          for (int j = 0; j < KS; ++j) qf[j] = valid ? load8(Qh + (size_t)pos * D + 32 * j + 8 * g4) : frag_zero<T>();
-          query_features(pfx, qo);
-          if constexpr (win_fast) {
-            window_fast_logits(pw, l_run);
-            window_fast_pv(pw, ywin);
-          } else {
-            window_general(ywin, l_run);
+              for (int jj = 0; jj < 8; ++jj) kv[jj] = to_f(kk.v[jj]) * t8[jj];
+              kmid[js] = frag_from<T>(kv);
+            }
           }
         }
-
-        // ---- intra-chunk scores A^T[s][t] for key sub-chunks J <= I
-        f32x4 at[4];
+        for (int g = 0; g < G; ++g) {
+          const int hq = kvh * G + g;
+          if (g > 0) {
+            const T *Qh = Qbase + ((size_t)b * p.Hq + hq) * (size_t)L * D;
 #pragma unroll
-        for (int J = 0; J < 4; ++J) at[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < KS; ++j) qf[j] = valid ? load8(Qh + (size_t)pos * D + 32 * j + 8 * g4) : frag_zero<T>();
+            query_phi(qo);
+            decay_q(qo, pfx);
+            window(yw);
+          }
+          // query operand (f-permuted K = 32 slices); mild: referred to the chunk start
+          auto qslice = [&](int js, float (&x)[8]) {
 #pragma unroll
-        for (int J = 0; J < 3; ++J) {
-          if (J < I) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int jj = 0; jj < 8; ++jj) x[jj] = qo[2 * js + (jj >> 2)][jj & 3];
+          };
+          Frag<T> qcf[KS];
+          if constexpr (MILD) {
 #pragma unroll
             for (int js = 0; js < KS; ++js) {
               float x[8];
+              qslice(js, x);
+              qcf[js] = frag_from<T>(x);
+            }
+          }
+
+          // ---- intra-chunk scores A^T[s][t] for key sub-chunks J <= I.  Mild: every block
+          //      is kown_J . qo; general: references joined by prod_{J<J'<I} e^{tot_J'}
+          f32x4 at[4];
 #pragma unroll
-              for (int jj = 0; jj < 8; ++jj) x[jj] = qo[2 * js + (jj >> 2)][jj & 3];
-              // prod_{J<J'<I} e^{tot_J'} joins the two references
+          for (int J = 0; J < 4; ++J) at[J] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-              for (int J2 = 1; J2 < 3; ++J2) {
-                if (J2 > J && J2 < I) {
+          for (int J = 0; J < 3; ++J) {
+            if (J < I) {
+              f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int js = 0; js < KS; ++js) {
+                Frag<T> bq;
+                if constexpr (MILD) {
+                  bq = qcf[js];
+                } else {
+                  float x[8];
+                  qslice(js, x);
+#pragma unroll
+                  for (int J2 = 1; J2 < 3; ++J2) {
+                    if (J2 > J && J2 < I) {
+                      float t8[8];
+                      tab8(sETot + J2 * D, js, g4, t8);
+#pragma unroll
+                      for (int jj = 0; jj < 8; ++jj) x[jj] *= t8[jj];
+                    }
+                  }
+                  bq = frag_from<T>(x);
+                }
+                const T *kr = sKown + (16 * J + r16) * LDW + 32 * js + 4 * g4;
+                acc = mma(load4x2(kr, kr + 16), bq, acc);
+              }
+              at[J] = acc;
+            }
+          }
+          {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (MILD) {
+#pragma unroll
+              for (int js = 0; js < KS; ++js) {
+                const T *kr = sKown + (16 * I + r16) * LDW + 32 * js + 4 * g4;
+                acc = mma(load4x2(kr, kr + 16), qcf[js], acc);
+              }
+            } else {
+              if (safe) {
+#pragma unroll
+                for (int js = 0; js < KS; ++js) {
+                  float t8[8], x[8];
+                  tab8(sENP7 + I * D, js, g4, t8);
+                  qslice(js, x);
+#pragma unroll
+                  for (int jj = 0; jj < 8; ++jj) x[jj] *= t8[jj];
+                  acc = mma(kmid[js], frag_from<T>(x), acc);
+                }
+              } else {
+                // exact: A[t][s] = mix sum_f phi_q[t][f] phi_k[s][f] e^{p_t[f] - p_s[f]}, with phi
+                // recomputed in fp32 (rare path: a sub-chunk whose log decay spans > SPAN_MAX).
+                // The in-sub-chunk prefix p is rebuilt from global memory so that it need not
+                // stay in registers through the common path.
+                float phk[NFT][4], phq[NFT][4], px[NFT][4];
+                {
+#pragma unroll
+                  for (int ft = 0; ft < NFT; ++ft) {
+                    float x[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                      const int t = c0 + 16 * I + 8 * g4 + j;
+                      x[j] = (g4 < 2 && t < L) ? to_f(LGh[(size_t)t * D + 16 * ft + r16]) : 0.f;
+                    }
+                    const f32x4 pp = mma(frag_from<T>(x), tri_pre, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) px[ft][i] = pp[i];
+                  }
+                  Frag<T> kf[KS];
+#pragma unroll
+                  for (int j = 0; j < KS; ++j) kf[j] = load8(sKr + kcur + (16 * I + r16) * LDW + 32 * j + 8 * g4);
+                  f32x4 z[NFT];
+                  feature_logits<T, D, LDW>(sWk, kf, r16, g4, z);
+                  softmax_rows<NFT>(z, phk);
+                  feature_logits<T, D, LDW>(sWq, qf, r16, g4, z);
+                  softmax_rows<NFT>(z, phq);
+                }
+#pragma unroll 1
+                for (int s2 = 0; s2 < 16; ++s2) {
+                  float part = 0.f;
+#pragma unroll
+                  for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                      const float pk = __shfl(phk[ft][i], 16 * g4 + s2);
+                      const float bs = __shfl(px[ft][i], 16 * g4 + s2);
+                      const float term = phq[ft][i] * pk * __expf(px[ft][i] - bs);
+                      part += (s2 <= r16) ? term : 0.f;
+                    }
+                  part = wave_sum_cols(part);
+#pragma unroll
+                  for (int i = 0; i < 4; ++i)
+                    if ((s2 >> 2) == g4 && (s2 & 3) == i) acc[i] = part * mix;
+                }
+              }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = (4 * g4 + i <= r16) ? acc[i] : 0.f;
+#pragma unroll
+            for (int J = 0; J < 4; ++J)
+              if (J == I) at[J] = acc;  // compile-time index keeps at[] in registers
+          }
+
+          // ---- Y^T += V^T A^T (intra) + S^T q~int^T (inter); lane holds Y^T[dv][t]
+#pragma unroll
+          for (int J0 = 0; J0 < 4; J0 += 2) {
+            if (J0 <= I) {
+              const bool has1 = (J0 + 1) <= I;
+              float x[8];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                x[i] = at[J0][i];
+                x[4 + i] = has1 ? at[J0 + 1][i] : 0.f;
+              }
+              const Frag<T> bf = frag_from<T>(x);
+              const int J1 = has1 ? J0 + 1 : J0;
+#pragma unroll
+              for (int dt = 0; dt < NDT; ++dt) {
+                const T *vr = sVt + cur + (16 * dt + r16) * LDC + 4 * g4;
+                yw[dt] = mma(load4x2(vr + 16 * J0, vr + 16 * J1), bf, yw[dt]);
+              }
+            }
+          }
+#pragma unroll
+          for (int js = 0; js < KS; ++js) {
+            Frag<T> bf;
+            if constexpr (MILD) {
+              bf = qcf[js];  // already referred to the chunk start
+            } else {
+              float x[8];
+              qslice(js, x);
+              // prod_{J<I} e^{tot_J}: decay from the chunk start to the sub-chunk start
+#pragma unroll
+              for (int J2 = 0; J2 < 3; ++J2) {
+                if (J2 < I) {
                   float t8[8];
                   tab8(sETot + J2 * D, js, g4, t8);
 #pragma unroll
                   for (int jj = 0; jj < 8; ++jj) x[jj] *= t8[jj];
                 }
               }
-              const T *kr = sKown + (16 * J + r16) * LDW + 32 * js + 4 * g4;
-              acc = mma(load4x2(kr, kr + 16), frag_from<T>(x), acc);
+              bf = frag_from<T>(x);
             }
-            at[J] = acc;
-          }
-        }
-        {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          if (safe) {
-#pragma unroll
-            for (int js = 0; js < KS; ++js) {
-              float t8[8], x[8];
-              tab8(sENP7 + I * D, js, g4, t8);
-#pragma unroll
-              for (int jj = 0; jj < 8; ++jj) x[jj] = qo[2 * js + (jj >> 2)][jj & 3] * t8[jj];
-              acc = mma(kmid[js], frag_from<T>(x), acc);
-            }
-          } else {
-            // exact: A[t][s] = sum_f phi_q[t][f] phi_k[s][f] e^{p_t[f] - p_s[f]}, with phi
-            // recomputed in fp32 (rare path: a sub-chunk whose log decay spans > SPAN_MAX)
-            float phk[NFT][4], phq[NFT][4];
-            {
-              Frag<T> kf[KS];
-#pragma unroll
-              for (int j = 0; j < KS; ++j) kf[j] = load8(sKr + kcur + (16 * I + r16) * LDW + 32 * j + 8 * g4);
-              f32x4 z[NFT];
-              feature_logits<T, D, LDW>(sWk, kf, r16, g4, z);
-              softmax_rows<NFT>(z, phk);
-              feature_logits<T, D, LDW>(sWq, qf, r16, g4, z);
-              softmax_rows<NFT>(z, phq);
-            }
-#pragma unroll 1
-            for (int s2 = 0; s2 < 16; ++s2) {
-              float part = 0.f;
-#pragma unroll
-              for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  const float pk = __shfl(phk[ft][i], 16 * g4 + s2);
-                  const float bs = __shfl(pfx[ft][i], 16 * g4 + s2);
-                  const float term = phq[ft][i] * pk * __expf(pfx[ft][i] - bs);
-                  part += (s2 <= r16) ? term : 0.f;
-                }
-              part = wave_sum_cols(part);
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                if ((s2 >> 2) == g4 && (s2 & 3) == i) acc[i] = part;
-            }
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i] = (4 * g4 + i <= r16) ? acc[i] : 0.f;
-#pragma unroll
-          for (int J = 0; J < 4; ++J)
-            if (J == I) at[J] = acc;  // compile-time index keeps at[] in registers
-        }
-
-        // ---- Y^T = V^T A^T (intra) + S^T q~int^T (inter); lane holds Y^T[dv][t]
-        f32x4 yacc[NDT];
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) yacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int J0 = 0; J0 < 4; J0 += 2) {
-          if (J0 <= I) {
-            const bool has1 = (J0 + 1) <= I;
-            float x[8];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              x[i] = at[J0][i];
-              x[4 + i] = has1 ? at[J0 + 1][i] : 0.f;
-            }
-            const Frag<T> bf = frag_from<T>(x);
-            const int J1 = has1 ? J0 + 1 : J0;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
-              const T *vr = sVt + cur + (16 * dt + r16) * LDC + 4 * g4;
-              yacc[dt] = mma(load4x2(vr + 16 * J0, vr + 16 * J1), bf, yacc[dt]);
+              const T *sr = sSbf + (16 * dt + r16) * LDW + 32 * js + 4 * g4;
+              yw[dt] = mma(load4x2(sr, sr + 16), bf, yw[dt]);
             }
           }
-        }
-#pragma unroll
-        for (int js = 0; js < KS; ++js) {
-          float x[8];
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) x[jj] = qo[2 * js + (jj >> 2)][jj & 3];
-          // prod_{J<I} e^{tot_J}: decay from the chunk start to the sub-chunk start
-#pragma unroll
-          for (int J2 = 0; J2 < 3; ++J2) {
-            if (J2 < I) {
-              float t8[8];
-              tab8(sETot + J2 * D, js, g4, t8);
-#pragma unroll
-              for (int jj = 0; jj < 8; ++jj) x[jj] *= t8[jj];
-            }
-          }
-          const Frag<T> bf = frag_from<T>(x);
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            const T *sr = sSbf + (16 * dt + r16) * LDW + 32 * js + 4 * g4;
-            yacc[dt] = mma(load4x2(sr, sr + 16), bf, yacc[dt]);
-          }
-        }
 
-        const float l_tot = wave_sum_cols(l_run);
-        const float wscale = (1.f - mix) / l_tot;
-        // ---- merge and store (lane holds Y^T[dv0 + 16 dt + 4 g4 + i][pos])
-        if (valid) {
-          T *O = reinterpret_cast<T *>(p.out) + (((size_t)b * p.Hq + hq) * (size_t)L + pos) * D + dv0;
+          // ---- store (lane holds Y^T[dv0 + 16 dt + 4 g4 + i][pos])
+          if (valid) {
+            T *O = reinterpret_cast<T *>(p.out) + (((size_t)b * p.Hq + hq) * (size_t)L + pos) * D + dv0;
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            float o[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = mix * yacc[dt][i] + wscale * ywin[dt][i];
-            store4<T>(O + 16 * dt + 4 * g4, o[0], o[1], o[2], o[3]);
+            for (int dt = 0; dt < NDT; ++dt) store4<T>(O + 16 * dt + 4 * g4, yw[dt][0], yw[dt][1], yw[dt][2], yw[dt][3]);
           }
-        }
-      }  // g
+        }  // g
+      };
+      if (mild)
+        heads(std::true_type{}, ywin);
+      else
+        heads(std::false_type{}, ywin);
       __syncthreads();  // B3
     }
   }
