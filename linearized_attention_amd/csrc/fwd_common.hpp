@@ -72,7 +72,9 @@ __device__ __forceinline__ void load_wT(T *dst, const T *src, int tid) {
 }
 
 // Per-thread share of one chunk: keys (row-major), values and log gamma
-// (both stored transposed, token pairs 2*tp, 2*tp+1 x 8 columns).
+// (both stored transposed, token pairs 2*tp, 2*tp+1 x 8 columns).  The 32
+// token pairs of one 8-column group sit in one half-wave, so the transposed
+// 4-byte stores of a wave cover all 64 LDS banks.
 template <typename T, int D, int DV> struct ChunkRegs {
   static constexpr int KFR = CH * D / 8 / 256;      // 8-element pieces of k per thread
   static constexpr int LFR = (CH / 2) * (D / 8) / 256;  // token-pair pieces of log gamma
@@ -92,7 +94,7 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<T, D, DV> &r, const T *Kh, 
     r.k[j] = (c0 + row < L) ? load8(Kh + (size_t)(c0 + row) * D + 8 * c8) : frag_zero<T>();
   }
   if (with_v) {
-    const int tp = tid / (DV / 8), dq = tid % (DV / 8);
+    const int dq = tid / 32, tp = tid % 32;  // one 8-column group per half-wave: conflict-free stores
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int t = c0 + 2 * tp + h;
@@ -102,7 +104,7 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<T, D, DV> &r, const T *Kh, 
 #pragma unroll
   for (int j = 0; j < ChunkRegs<T, D, DV>::LFR; ++j) {
     const int idx = tid + 256 * j;
-    const int tp = idx / (D / 8), fq = idx % (D / 8);
+    const int fq = idx / 32, tp = idx % 32;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int t = c0 + 2 * tp + h;
@@ -145,8 +147,24 @@ __device__ __forceinline__ void store_pairT(const Frag<T> &a, const Frag<T> &b, 
 
 template <typename T, int D, int DV, int LDC>
 __device__ __forceinline__ void store_values(const ChunkRegs<T, D, DV> &r, T *sVt, int tid) {
-  const int tp = tid / (DV / 8), dq = tid % (DV / 8);
+  const int dq = tid / 32, tp = tid % 32;
   store_pairT<T, LDC>(r.v[0], r.v[1], sVt + (8 * dq) * LDC + 2 * tp);
+}
+
+// The value share of load_chunk / store_values on its own (same thread mapping).
+template <typename T, int D, int DV>
+__device__ __forceinline__ void load_values(Frag<T> (&v)[2], const T *Vh, int c0, int L, int dv0, int tid) {
+  const int dq = tid / 32, tp = tid % 32;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = c0 + 2 * tp + h;
+    v[h] = (t < L) ? load8(Vh + (size_t)t * D + dv0 + 8 * dq) : frag_zero<T>();
+  }
+}
+template <typename T, int LDC>
+__device__ __forceinline__ void store_values2(const Frag<T> (&v)[2], T *sVt, int tid) {
+  const int dq = tid / 32, tp = tid % 32;
+  store_pairT<T, LDC>(v[0], v[1], sVt + (8 * dq) * LDC + 2 * tp);
 }
 
 template <typename T, int D, int DV, int LDC>
@@ -154,7 +172,7 @@ __device__ __forceinline__ void store_lgT(const ChunkRegs<T, D, DV> &r, T *sLgT,
 #pragma unroll
   for (int j = 0; j < ChunkRegs<T, D, DV>::LFR; ++j) {
     const int idx = tid + 256 * j;
-    const int tp = idx / (D / 8), fq = idx % (D / 8);
+    const int fq = idx / 32, tp = idx % 32;
     store_pairT<T, LDC>(r.lg[j][0], r.lg[j][1], sLgT + (8 * fq) * LDC + 2 * tp);
   }
 }

@@ -11,7 +11,8 @@
 //       intra- and inter-chunk products, the merge and the stores.
 // Each role runs its own loop over the chunks; both loops pass the same four
 // workgroup barriers per chunk, so the roles stay in step:
-//   B0  chunk c's keys, values and log gamma are in LDS
+//   B0  chunk c's keys and log gamma (staged by the key waves) and values
+//       (staged by the query waves) are in LDS
 //   B1  sub-chunk totals written (key waves), log gamma consumed (both); every
 //       wave then classifies the chunk: if its log decay stays within FAST_SPAN
 //       for every feature, all decays are referred to the chunk start (keys
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
       }
     }
     ChunkRegs<T, D, DV> pf;
-    load_chunk<T, D, DV>(pf, Kh, Vh, LGh, c_begin * CH, L, dv0, true, kt);
+    load_chunk<T, D, DV>(pf, Kh, Vh, LGh, c_begin * CH, L, dv0, false, kt);  // values: query waves
     __syncthreads();  // P2: prologue LDS writes complete
 #pragma unroll
     for (int ft = 0; ft < FTW; ++ft)
@@ -164,7 +165,6 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
       const int kcur = (c % KR) * (CH * LDW);
       const int cur = (c % NR) * (DV * LDC);
       store_keys<T, D, DV, LDW>(pf, sKr + kcur, kt);
-      store_values<T, D, DV, LDC>(pf, sVt + cur, kt);
       store_lgT<T, D, DV, LDC>(pf, sLgT, kt);
       __syncthreads();  // B0
 
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
         softmax_rows<NFT>(z, ko);
       }
       // next chunk's keys, values and log gamma in flight during the rest of this one
-      if (c + 1 < c_end) load_chunk<T, D, DV>(pf, Kh, Vh, LGh, c0 + CH, L, dv0, true, kt);
+      if (c + 1 < c_end) load_chunk<T, D, DV>(pf, Kh, Vh, LGh, c0 + CH, L, dv0, false, kt);
       __syncthreads();  // B1
       const bool mild = chunk_is_mild<D>(sTot, lane);
 
@@ -317,6 +317,8 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
         wmask |= (in ? 1u : 0u) << (4 * u + i);
       }
     const T *Q0 = Qbase + ((size_t)b * p.Hq + kvh * G) * (size_t)L * D;
+    Frag<T> pfv[2];  // this role stages the value chunks (the key waves stage keys and log gamma)
+    load_values<T, D, DV>(pfv, Vh, c_begin * CH, L, dv0, tid);
     Frag<T> pfq[KS];
     {
       const int pos0 = c_begin * CH + 16 * I + r16;
@@ -336,6 +338,7 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
       const int vprev = ((c + NR - 1) % NR) * (DV * LDC);
       const int pos = c0 + 16 * I + r16;
       const bool valid = pos < L;
+      store_values2<T, LDC>(pfv, sVt + cur, tid);
       Frag<T> qf[KS];
 #pragma unroll
       for (int j = 0; j < KS; ++j) qf[j] = pfq[j];
@@ -584,6 +587,7 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
       if constexpr (win_fast) window_fast_logits(pw, l_run);
       // next chunk's first query head in flight during the rest of this one
       if (c + 1 < c_end) {
+        load_values<T, D, DV>(pfv, Vh, c0 + CH, L, dv0, tid);
         const int pn = pos + CH;
 #pragma unroll
         for (int j = 0; j < KS; ++j) pfq[j] = (pn < L) ? load8(Q0 + (size_t)pn * D + 32 * j + 8 * g4) : frag_zero<T>();
