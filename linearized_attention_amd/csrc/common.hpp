@@ -127,21 +127,51 @@ template <typename T> __device__ __forceinline__ void store4(T *p, float a, floa
   }
 }
 
-__device__ __forceinline__ float wave_max_cols(float x) {
-  // max over the four lanes that share lane % 16
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+// Cross-lane reductions without the LDS crossbar: DPP moves inside each row of
+// 16 lanes, and the gfx950 permlane swaps across rows.  permlane16_swap(x, x)
+// yields, per lane l, the pair {x[l], x[l ^ 16]} (in either order) and
+// permlane32_swap(x, x) the pair {x[l], x[l ^ 32]}, so a symmetric operation
+// on the pair reduces across the rows; every lane gets the same bits.
+template <int CTRL> __device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float wave_sum_cols(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i <- 7 - i within 8
+constexpr int DPP_MIRROR = 0x140;      // lane i <- 15 - i within 16
+
+__device__ __forceinline__ float pair16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float wave_max_all(float x) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
-  return x;
+__device__ __forceinline__ float pair32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+__device__ __forceinline__ float pair16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// max / sum over the 16 lanes of a row
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dpp_f<DPP_XOR1>(x));
+  x = fmaxf(x, dpp_f<DPP_XOR2>(x));
+  x = fmaxf(x, dpp_f<DPP_HALF_MIRROR>(x));
+  return fmaxf(x, dpp_f<DPP_MIRROR>(x));
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_f<DPP_XOR1>(x);
+  x += dpp_f<DPP_XOR2>(x);
+  x += dpp_f<DPP_HALF_MIRROR>(x);
+  return x + dpp_f<DPP_MIRROR>(x);
+}
+// max / sum over the four lanes that share lane % 16 (a column of an MFMA tile)
+__device__ __forceinline__ float wave_max_cols(float x) { return pair32_max(pair16_max(x)); }
+__device__ __forceinline__ float wave_sum_cols(float x) { return pair32_sum(pair16_sum(x)); }
+__device__ __forceinline__ float wave_max_all(float x) { return wave_max_cols(row_max16(x)); }
 
 }  // namespace lz

@@ -570,16 +570,6 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) pfx[ft][i] = pp[i];
       }
-      bool safe;
-      {
-        // the sub-chunk's log decay spans at most -min_t prefix (log gamma <= 0)
-        float span = 0.f;
-#pragma unroll
-        for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) span = fmaxf(span, -pfx[ft][i]);
-        safe = wave_max_all(span) <= SPAN_MAX;
-      }
       float qo[NFT][4];
       query_phi(qo);
       Frag<T> pw[3];
@@ -594,6 +584,16 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
       }
       __syncthreads();  // B1
       const bool mild = chunk_is_mild<D>(sTot, lane);
+      bool safe = true;  // general case: mid-row reference usable on the diagonal block
+      if (!mild) {
+        // the sub-chunk's log decay spans at most -min_t prefix (log gamma <= 0)
+        float span = 0.f;
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) span = fmaxf(span, -pfx[ft][i]);
+        safe = wave_max_all(span) <= SPAN_MAX;
+      }
       if (mild) {
         // chunk-start reference: the prefix grows by the totals of the earlier sub-chunks
 #pragma unroll
