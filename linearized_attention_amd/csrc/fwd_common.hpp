@@ -190,6 +190,17 @@ __device__ __forceinline__ Frag<T> tri_frag(int r16, int g4, bool prefix) {
   return frag_from<T>(x);
 }
 
+// Constant B operand of the inclusive prefix over the whole chunk for the rows of
+// sub-chunk I: K-step ks covers chunk rows s = 32 ks + 8 kq + j, and lane
+// (t = r16, kq) holds B[s][t] = (s <= 16 I + t).
+template <typename T>
+__device__ __forceinline__ Frag<T> tri64_frag(int r16, int g4, int I, int ks) {
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = (32 * ks + 8 * g4 + j <= 16 * I + r16) ? 1.f : 0.f;
+  return frag_from<T>(x);
+}
+
 // 8 fp32 table values for the operand slots of K-step js (features
 // 32js + 4g4 + 0..3 and 32js + 16 + 4g4 + 0..3).
 __device__ __forceinline__ void tab8(const float *row, int js, int g4, float (&x)[8]) {

@@ -147,6 +147,7 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
         }
       }
     }
+    const Frag<T> tri_c0 = tri64_frag<T>(r16, g4, I, 0), tri_c1 = tri64_frag<T>(r16, g4, I, 1);
     ChunkRegs<T, D, DV> pf;
     load_chunk<T, D, DV>(pf, Kh, Vh, LGh, c_begin * CH, L, dv0, false, kt);  // values: query waves
     __syncthreads();  // P2: prologue LDS writes complete
@@ -169,13 +170,15 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
       __syncthreads();  // B0
 
       // ---- A: gate prefix sums inside the sub-chunk, phi_k (decayed in B)
-      float pfx[NFT][4];
+      float pfx[NFT][4], pc[NFT][4];  // prefix inside the sub-chunk / from the chunk start
 #pragma unroll
       for (int ft = 0; ft < NFT; ++ft) {
         const Frag<T> a = (g4 < 2) ? load8(sLgT + (16 * ft + r16) * LDC + 16 * I + 8 * g4) : frag_zero<T>();
         const f32x4 pp = mma(a, tri_pre, f32x4{0.f, 0.f, 0.f, 0.f});
+        f32x4 cc = mma(load8(sLgT + (16 * ft + r16) * LDC + 8 * g4), tri_c0, f32x4{0.f, 0.f, 0.f, 0.f});
+        cc = mma(load8(sLgT + (16 * ft + r16) * LDC + 32 + 8 * g4), tri_c1, cc);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pfx[ft][i] = pp[i];
+        for (int i = 0; i < 4; ++i) { pfx[ft][i] = pp[i]; pc[ft][i] = cc[i]; }
       }
       if (r16 == 15 || r16 == 7) {
         float *dst = (r16 == 15 ? sTot : sP7) + I * D + 4 * g4;
@@ -202,18 +205,9 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
       //      keys carry e^{tot_I - pfx} (decay to the sub-chunk end) and the sub-chunk tables.
       if (mild) {
 #pragma unroll
-        for (int ft = 0; ft < NFT; ++ft) {
-          f32x4 pI = {0.f, 0.f, 0.f, 0.f};
+        for (int ft = 0; ft < NFT; ++ft)
 #pragma unroll
-          for (int J = 0; J < 3; ++J)
-            if (J < I) {
-              const f32x4 t = *reinterpret_cast<const f32x4 *>(sTot + J * D + 16 * ft + 4 * g4);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) pI[i] += t[i];
-            }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) ko[ft][i] *= __expf(-(pI[i] + pfx[ft][i]));
-        }
+          for (int i = 0; i < 4; ++i) ko[ft][i] *= __expf(-pc[ft][i]);
         if (kt < D) sETot[kt] = __expf(sTot[kt] + sTot[D + kt] + sTot[2 * D + kt] + sTot[3 * D + kt]);
       } else {
         constexpr int PER = 4 / (256 / D);  // sub-chunks handled per thread
@@ -317,6 +311,7 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
         wmask |= (in ? 1u : 0u) << (4 * u + i);
       }
     const T *Q0 = Qbase + ((size_t)b * p.Hq + kvh * G) * (size_t)L * D;
+    const Frag<T> tri_c0 = tri64_frag<T>(r16, g4, I, 0), tri_c1 = tri64_frag<T>(r16, g4, I, 1);
     Frag<T> pfv[2];  // this role stages the value chunks (the key waves stage keys and log gamma)
     load_values<T, D, DV>(pfv, Vh, c_begin * CH, L, dv0, tid);
     Frag<T> pfq[KS];
@@ -562,13 +557,15 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
 
       __syncthreads();  // B0
       // ---- A: prefix sums of log gamma inside the sub-chunk; phi_q and window logits of head 0
+      // pfx: inclusive prefix of log gamma from the chunk start (the general case below
+      // rebases it to the sub-chunk start)
       float pfx[NFT][4];
 #pragma unroll
       for (int ft = 0; ft < NFT; ++ft) {
-        const Frag<T> a = (g4 < 2) ? load8(sLgT + (16 * ft + r16) * LDC + 16 * I + 8 * g4) : frag_zero<T>();
-        const f32x4 pp = mma(a, tri_pre, f32x4{0.f, 0.f, 0.f, 0.f});
+        f32x4 cc = mma(load8(sLgT + (16 * ft + r16) * LDC + 8 * g4), tri_c0, f32x4{0.f, 0.f, 0.f, 0.f});
+        cc = mma(load8(sLgT + (16 * ft + r16) * LDC + 32 + 8 * g4), tri_c1, cc);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pfx[ft][i] = pp[i];
+        for (int i = 0; i < 4; ++i) pfx[ft][i] = cc[i];
       }
       float qo[NFT][4];
       query_phi(qo);
@@ -586,16 +583,7 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
       const bool mild = chunk_is_mild<D>(sTot, lane);
       bool safe = true;  // general case: mid-row reference usable on the diagonal block
       if (!mild) {
-        // the sub-chunk's log decay spans at most -min_t prefix (log gamma <= 0)
-        float span = 0.f;
-#pragma unroll
-        for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) span = fmaxf(span, -pfx[ft][i]);
-        safe = wave_max_all(span) <= SPAN_MAX;
-      }
-      if (mild) {
-        // chunk-start reference: the prefix grows by the totals of the earlier sub-chunks
+        // sub-chunk start reference: subtract the totals of the earlier sub-chunks
 #pragma unroll
         for (int ft = 0; ft < NFT; ++ft)
 #pragma unroll
@@ -603,8 +591,15 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
             if (J < I) {
               const f32x4 t = *reinterpret_cast<const f32x4 *>(sTot + J * D + 16 * ft + 4 * g4);
 #pragma unroll
-              for (int i = 0; i < 4; ++i) pfx[ft][i] += t[i];
+              for (int i = 0; i < 4; ++i) pfx[ft][i] -= t[i];
             }
+        // the sub-chunk's log decay spans at most -min_t prefix (log gamma <= 0)
+        float span = 0.f;
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) span = fmaxf(span, -pfx[ft][i]);
+        safe = wave_max_all(span) <= SPAN_MAX;
       }
 
       // ---- B: decayed queries and window products of head 0 (scaled for the merge)
