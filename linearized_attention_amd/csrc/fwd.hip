@@ -777,13 +777,11 @@ static hipError_t launch_fwd_t(const FwdParams &prm, hipStream_t stream) {
       }
     }
   if (!fit) return hipErrorInvalidConfiguration;
-  // The role-split kernel keeps one W_phi_q per workgroup; a different one per grouped
-  // query head (reloaded inside the head loop) runs on the 4-wave kernel.
-  static const bool force_4wave = [] {
-    const char *e = getenv("LIZARD_FWD_KERNEL");
-    return e && strcmp(e, "4wave") == 0;
-  }();
-  if (!force_4wave && !(p.per_head_q && p.G > 1)) return launch_fwd_split<T, D, DV>(p, stream);
+  // The role-split kernel serves one query head per key/value head; grouped query heads
+  // (whose per-head work would fall on the query waves alone) run on the 4-wave kernel.
+  const char *kenv = getenv("LIZARD_FWD_KERNEL");  // "4wave": force the 4-wave kernel (tests, A/B timing)
+  const bool force_4wave = kenv && strcmp(kenv, "4wave") == 0;
+  if (!force_4wave && p.G == 1) return launch_fwd_split<T, D, DV>(p, stream);
   return launch_one<T, D, DV, false>(p, stream);
 }
 

@@ -849,11 +849,9 @@ static hipError_t launch_split_one(const FwdParams &p, hipStream_t stream) {
 
 template <typename T, int D, int DV>
 hipError_t launch_fwd_split(const FwdParams &p, hipStream_t stream) {
+  if (p.G != 1) return hipErrorInvalidValue;  // grouped query heads: the 4-wave kernel
   const bool fastwin = (p.W <= CH + 1) && p.kring >= 2 && p.nring >= 2;
-  const bool multi_g = p.G > 1;
-  if (fastwin) return multi_g ? launch_split_one<T, D, DV, true, true>(p, stream)
-                              : launch_split_one<T, D, DV, true, false>(p, stream);
-  return multi_g ? launch_split_one<T, D, DV, false, true>(p, stream)
+  return fastwin ? launch_split_one<T, D, DV, true, false>(p, stream)
                  : launch_split_one<T, D, DV, false, false>(p, stream);
 }
 
