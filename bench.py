@@ -34,7 +34,11 @@ from linearized_attention_amd.synthetic import (WORKLOADS, WORKLOAD_NAMES,  # no
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_kernel_workload1.json")
-KERNEL_SOURCES = ["linearized_attention_amd/csrc/fwd.hip", "linearized_attention_amd/csrc/common.hpp"]
+KERNEL_SOURCES = ["linearized_attention_amd/csrc/fwd_split.hip", "linearized_attention_amd/csrc/fwd_common.hpp",
+                  "linearized_attention_amd/csrc/common.hpp"]
+FWD_KERNEL = "fwd_split_kernel<bf16,128,64,true,false>"  # dominant kernel of the forward workload
+FWD_KERNEL_SYMBOL = "fwd_split_kernel"
+COPY_BYTES = 1 << 30
 
 
 def log(*a):
@@ -162,6 +166,50 @@ def cpu_baseline():
                       f"{dt:.2f} s wall"}
 
 
+def _counter_means(path: str):
+    """Per-dispatch mean of each (kernel, counter) in a rocprofv3 counter_collection.csv."""
+    import csv
+    per = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            key = (row["Kernel_Name"], row["Counter_Name"])
+            d = per.setdefault(key, {})
+            d[row["Dispatch_Id"]] = d.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+    return {k: sum(v.values()) / len(v) for k, v in per.items()}
+
+
+def write_traffic(fetch_csv: str, write_csv: str):
+    """Turn two counter passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) over
+    `bench.py --pmc-run` into HBM bytes per forward launch.  Each counter is
+    scaled by what it reads for the plain copy of COPY_BYTES in the same run."""
+    fetch, write = _counter_means(fetch_csv), _counter_means(write_csv)
+
+    def pick(means, counter, symbol):
+        vals = [v for (k, c), v in means.items() if c == counter and symbol in k]
+        if len(vals) != 1:
+            raise SystemExit(f"expected one kernel matching {symbol!r} for {counter}, found {len(vals)}")
+        return vals[0]
+    kf, kw = pick(fetch, "FETCH_SIZE", FWD_KERNEL_SYMBOL), pick(write, "WRITE_SIZE", FWD_KERNEL_SYMBOL)
+    cf, cw = pick(fetch, "FETCH_SIZE", "copyBuffer"), pick(write, "WRITE_SIZE", "copyBuffer")
+    sf, sw = COPY_BYTES / (cf * 1024.0), COPY_BYTES / (cw * 1024.0)
+    c = WORKLOADS[1]
+    nbytes, _ = fwd_algorithmic(c)
+    traffic = kf * 1024.0 * sf + kw * 1024.0 * sw
+    out = {"kernel": FWD_KERNEL, "workload": WORKLOAD_NAMES[1], "kernel_source_sha": kernel_source_sha(),
+           "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw,
+           "copy_fetch_kib": cf, "copy_write_kib": cw, "copy_bytes_each_way": COPY_BYTES,
+           "fetch_scale": sf, "write_scale": sw,
+           "traffic_bytes_per_launch": traffic, "algorithmic_bytes_per_launch": nbytes,
+           "traffic_over_algorithmic": traffic / nbytes,
+           "commands": ["rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o pmc -- python3 bench.py --pmc-run",
+                        "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o pmc -- python3 bench.py --pmc-run",
+                        "python3 bench.py --write-traffic gpurun_out/pmc_fetch/pmc_counter_collection.csv "
+                        "gpurun_out/pmc_write/pmc_counter_collection.csv"]}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def load_traffic(launch_bytes: float):
     try:
         with open(TRAFFIC_FILE) as f:
@@ -183,7 +231,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-run", action="store_true",
                     help="one forward plus a plain copy of known size, for rocprofv3 counter passes")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="(no GPU) turn the two counter_collection.csv files of the --pmc-run passes "
+                         "into profiles/traffic_fwd_kernel_workload1.json")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the forward shards by batch/head with no exchange; see the design notes).", file=sys.stderr)
@@ -195,7 +249,7 @@ def main():
 
     if args.pmc_run:
         c, inp, _, _ = bench_forward(1, 1)
-        nbytes = 1 << 30
+        nbytes = COPY_BYTES
         src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
@@ -230,7 +284,7 @@ def main():
                    "W": c["W"], "M": c["M"], "chunk": 64, "accumulation": "fp32"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "fwd_kernel<bf16,128,64,2,false>", "kernel_ms": kern_ms,
+                     "kernel": FWD_KERNEL, "kernel_ms": kern_ms,
                      "algorithmic_bytes_per_launch": nbytes},
         "mfma": {"algorithmic_flops_per_launch": flops, "achieved_tflops": mfma_tflops,
                  "peak_tflops": BF16_PEAK_TFLOPS, "frac": mfma_tflops / BF16_PEAK_TFLOPS},
