@@ -98,6 +98,43 @@ def test_fwd_matches_oracle(gpu_lib, label, kw, dtype):
     check_case(label, inp, dtype)
 
 
+def _chunk_kinds(log_gamma, chunk=64, fast_span=60.0):
+    """How many 64-token chunks have |sum log gamma| <= fast_span for every feature
+    (the kernel refers their decays to the chunk start) and how many do not."""
+    lg = log_gamma.double().numpy()
+    L = lg.shape[2]
+    mild = general = 0
+    for c0 in range(0, L, chunk):
+        tot = lg[:, :, c0:c0 + chunk, :].sum(axis=2)  # [B, H, d]
+        m = (-tot).max(axis=-1)
+        mild += int((m <= fast_span).sum())
+        general += int((m > fast_span).sum())
+    return mild, general
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+def test_fwd_mixed_chunk_references(gpu_lib, dtype, d):
+    """A gate whose chunk totals straddle the chunk-start reference bound, so one launch
+    takes both the chunk-start and the sub-chunk decay references."""
+    inp = make_fwd_inputs(B=1, Hq=2, Hkv=2, L=640, d=d, W=64, M=4, dtype=dtype, seed=77,
+                          gate="uniform:-1.6")
+    mild, general = _chunk_kinds(inp.log_gamma)
+    _say(f"      chunks: {mild} mild, {general} general")
+    assert mild > 0 and general > 0
+    check_case(f"{dtype} d{d} mixed chunk references", inp, dtype)
+
+
+@pytest.mark.parametrize("label", ["bf16 d128 ragged L200", "fp32 uniform gate -8 (mixed safe/exact diag)",
+                                   "fp32 W66 (3-chunk ring)"])
+def test_fwd_four_wave_kernel(gpu_lib, monkeypatch, label):
+    """The 4-wave kernel (used for grouped heads and the segment state pass) on single-head
+    cases as well."""
+    monkeypatch.setenv("LIZARD_FWD_KERNEL", "4wave")
+    kw, dtype = {s[0]: (s[1], s[2]) for s in SMALL}[label]
+    inp = make_fwd_inputs(dtype=dtype, seed=zlib.crc32(label.encode()) % 10000, **kw)
+    check_case(label + " [4-wave]", inp, dtype)
+
+
 @pytest.mark.parametrize("nseg", [2, 3, 5])
 def test_fwd_sequence_segments(gpu_lib, monkeypatch, nseg):
     """Segments joined through the workspace states give the same answer."""
