@@ -33,6 +33,11 @@ __device__ __forceinline__ f32x4 mma(const Frag<float> &a, const Frag<float> &b,
   return c;
 }
 
+// 2^x on the transcendental unit (v_exp_f32); exponentials are written as
+// exp2(fma(x, LOG2E, c)) so the base change costs no separate multiply.
+constexpr float LOG2E = 1.4426950408889634f;
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f(float x) { return x; }
 template <typename T> __device__ __forceinline__ T from_f(float x);

@@ -218,12 +218,13 @@ __device__ __forceinline__ void softmax_rows(const f32x4 (&z)[NFT], float (&phi)
 #pragma unroll
     for (int i = 0; i < 4; ++i) zm = fmaxf(zm, z[ft][i]);
   zm = wave_max_cols(zm);
+  const float zm2 = -zm * LOG2E;
   float zs = 0.f;
 #pragma unroll
   for (int ft = 0; ft < NFT; ++ft)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      phi[ft][i] = __expf(z[ft][i] - zm);
+      phi[ft][i] = exp2_fast(__builtin_fmaf(z[ft][i], LOG2E, zm2));
       zs += phi[ft][i];
     }
   zs = wave_sum_cols(zs);

@@ -297,7 +297,7 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
   } else {
     // ======================================================= query waves
     const float mix = p.mix, scale = p.scale;
-    const float log_mix = __logf(mix);
+    const float log2_mix = __log2f(mix);
     constexpr bool win_fast = FASTWIN;
     // fast window: bit 4u+i set when slot (tile u, row 4 g4 + i) is inside the window of this
     // lane's query (u = 0 meta; band tile u: kj - pos = 16u - 80 + 4 g4 + i - r16)
@@ -344,12 +344,12 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
         feature_logits<T, D, LDW>(sWq, qf, r16, g4, z);
         softmax_rows<NFT>(z, qo);
       };
-      // decay and the merge weight: qo *= mix e^{px}  (log_mix = log(mix), -inf for mix = 0)
+      // decay and the merge weight: qo *= mix e^{px} = 2^(px log2 e + log2 mix)  (-inf for mix = 0)
       auto decay_q = [&](float (&qo)[NFT][4], const float (&px)[NFT][4]) {
 #pragma unroll
         for (int ft = 0; ft < NFT; ++ft)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) qo[ft][i] *= __expf(px[ft][i] + log_mix);
+          for (int i = 0; i < 4; ++i) qo[ft][i] *= exp2_fast(__builtin_fmaf(px[ft][i], LOG2E, log2_mix));
       };
 
       // fast window, logits: the meta tile and the five 16-key tiles ending at this
@@ -381,6 +381,7 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) bm = fmaxf(bm, lt[u][i]);
         bm = wave_max_cols(bm);
+        const float bm2 = -bm * LOG2E;
         l_run = 0.f;
 #pragma unroll
         for (int pr = 0; pr < 3; ++pr) {
@@ -389,7 +390,7 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
           for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float pv = __expf(lt[2 * pr + h][i] - bm);  // masked: exp(-1e30) = 0
+              const float pv = exp2_fast(__builtin_fmaf(lt[2 * pr + h][i], LOG2E, bm2));  // masked: 0
               x[4 * h + i] = pv;
               l_run += pv;
             }
