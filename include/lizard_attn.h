@@ -99,6 +99,45 @@ size_t lizard_attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int L, int d,
                                        int W, lizard_dtype dtype);
 
 /*
+ * Forward as a continuation (chunked prefill feeding decode): the L new tokens
+ * of sequence b follow pos[b] earlier ones, whose effect arrives as the state
+ * and ring the decode step uses (the recurrent form of the method: arXiv page,
+ * Preliminaries; both branches: papernotes.org summary, "key designs").  The
+ * outputs equal those of one forward over all pos[b] + L tokens.  Arguments as
+ * in lizard_attn_fwd, plus (each may be NULL):
+ *   state_in   [B, Hkv, d, d] fp32: S after the earlier tokens (NULL: zero).
+ *   win_k_in, win_v_in [B, Hkv, W, d]: ring of the earlier keys / values,
+ *              token t in slot t % W (as lizard_attn_decode keeps it).  Both or
+ *              neither; require pos.  NULL: the window sees no earlier token.
+ *   pos        [B] int32 on the device: earlier tokens per sequence; advanced by
+ *              L at the end, after every read.
+ *   state_out  [B, Hkv, d, d] fp32: S after the last new token.  Must not be
+ *              state_in.
+ *   win_k_out, win_v_out [B, Hkv, W, d]: the ring after the call (may be the
+ *              ring in, updated in place).  Both or neither.
+ *   workspace  at least lizard_attn_fwd_ext_workspace_bytes() bytes: the
+ *              forward's own scratch plus the staged window history.
+ * Calls on one stream run in order; state, rings and pos of a call must not be
+ * touched by another stream meanwhile.  L = 0 launches nothing.
+ */
+lizard_status lizard_attn_fwd_ext(const void *q, const void *k, const void *v,
+                                  const void *log_gamma, const void *w_phi_q,
+                                  const void *w_phi_k, int64_t w_phi_head_stride,
+                                  const void *t_k, const void *t_v, void *out,
+                                  int B, int Hq, int Hkv, int L, int d, int W,
+                                  int M, float mix, float scale,
+                                  lizard_dtype dtype, const float *state_in,
+                                  const void *win_k_in, const void *win_v_in,
+                                  int32_t *pos, float *state_out,
+                                  void *win_k_out, void *win_v_out,
+                                  void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
+/* Workspace bytes lizard_attn_fwd_ext needs for these shapes (ring in given). */
+size_t lizard_attn_fwd_ext_workspace_bytes(int B, int Hq, int Hkv, int L,
+                                           int d, int W, lizard_dtype dtype);
+
+/*
  * One decode step: every sequence n takes one new token, in place.
  *   state       [N, Hkv, d, d] float32 (always fp32), the S matrix of the
  *               global branch; row f is key dimension f.  Updated.

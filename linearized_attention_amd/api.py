@@ -23,7 +23,8 @@ _STATUS = {0: "LIZARD_OK", 1: "LIZARD_ERR_INVALID_ARG", 2: "LIZARD_ERR_UNSUPPORT
            3: "LIZARD_ERR_WORKSPACE", 4: "LIZARD_ERR_HIP"}
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
-EXPORTED = ("lizard_attn_fwd", "lizard_attn_fwd_workspace_bytes", "lizard_attn_decode",
+EXPORTED = ("lizard_attn_fwd", "lizard_attn_fwd_workspace_bytes", "lizard_attn_fwd_ext",
+            "lizard_attn_fwd_ext_workspace_bytes", "lizard_attn_decode",
             "lizard_attn_decode_workspace_bytes", "lizard_status_string", "lizard_last_error", "lizard_version")
 
 _lock = threading.Lock()
@@ -44,6 +45,12 @@ def _declare(lib):
     lib.lizard_attn_fwd.restype = i32
     lib.lizard_attn_fwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.lizard_attn_fwd_workspace_bytes.restype = sz
+    lib.lizard_attn_fwd_ext.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp, vp, vp,
+                                        i32, i32, i32, i32, i32, i32, i32, f32, f32, i32,
+                                        vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.lizard_attn_fwd_ext.restype = i32
+    lib.lizard_attn_fwd_ext_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.lizard_attn_fwd_ext_workspace_bytes.restype = sz
     lib.lizard_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp,
                                        i32, i32, i32, i32, i32, i32, f32, f32, i32, vp, sz, vp]
     lib.lizard_attn_decode.restype = i32
@@ -145,6 +152,66 @@ def lizard_attn_fwd(q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v, *, W: int, M
         _w_stride(w_phi_q, w_phi_k, d), _ptr(t_k) if M > 0 else None, _ptr(t_v) if M > 0 else None,
         _ptr(out), B, Hq, Hkv, L, d, W, M, float(mix), float(scale), _DTYPES[dt],
         _ptr(workspace), wbytes, _stream(stream)))
+    return out
+
+
+def lizard_attn_fwd_ext_workspace_bytes(B: int, Hq: int, Hkv: int, L: int, d: int, W: int,
+                                        dtype: torch.dtype) -> int:
+    return int(load().lizard_attn_fwd_ext_workspace_bytes(B, Hq, Hkv, L, d, W, _DTYPES[dtype]))
+
+
+def lizard_attn_fwd_ext(q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v, *, W: int, M: int,
+                        mix: float = 0.5, scale: float | None = None, state_in=None, win_k_in=None,
+                        win_v_in=None, pos=None, state_out=None, win_k_out=None, win_v_out=None,
+                        out=None, workspace=None, stream=None):
+    """Forward over L new tokens that follow pos[b] earlier ones: state_in [B,Hkv,d,d] fp32,
+    rings win_k_in/win_v_in [B,Hkv,W,d] (token t in slot t % W), pos [B] int32 (advanced by L);
+    state_out, win_k_out/win_v_out receive the state and ring after the call.  Any of them may
+    be None.  Shapes otherwise as lizard_attn_fwd.  Returns out."""
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (log_gamma, "log_gamma"), (w_phi_q, "w_phi_q"),
+                 (w_phi_k, "w_phi_k")):
+        _dev(t, n, dt)
+    if M > 0:
+        _dev(t_k, "t_k", dt)
+        _dev(t_v, "t_v", dt)
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, L, d) or v.shape != k.shape or log_gamma.shape != k.shape:
+        raise ValueError("k, v, log_gamma must be [B,Hkv,L,d] matching q")
+    for t, n in ((state_in, "state_in"), (state_out, "state_out")):
+        if t is not None:
+            _dev(t, n, torch.float32)
+            if t.shape != (B, Hkv, d, d):
+                raise ValueError(f"{n} must be [B,Hkv,d,d]")
+    for t, n in ((win_k_in, "win_k_in"), (win_v_in, "win_v_in"), (win_k_out, "win_k_out"),
+                 (win_v_out, "win_v_out")):
+        if t is not None:
+            _dev(t, n, dt)
+            if t.shape != (B, Hkv, W, d):
+                raise ValueError(f"{n} must be [B,Hkv,W,d]")
+    if pos is not None:
+        _dev(pos, "pos", torch.int32)
+        if pos.shape != (B,):
+            raise ValueError("pos must be [B]")
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, "out", dt)
+    need = lizard_attn_fwd_ext_workspace_bytes(B, Hq, Hkv, L, d, W, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().lizard_attn_fwd_ext(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), _ptr(w_phi_q), _ptr(w_phi_k),
+        _w_stride(w_phi_q, w_phi_k, d), _ptr(t_k) if M > 0 else None, _ptr(t_v) if M > 0 else None,
+        _ptr(out), B, Hq, Hkv, L, d, W, M, float(mix), float(scale), _DTYPES[dt],
+        _ptr(state_in), _ptr(win_k_in), _ptr(win_v_in), _ptr(pos), _ptr(state_out), _ptr(win_k_out),
+        _ptr(win_v_out), _ptr(workspace), wbytes, _stream(stream)))
     return out
 
 

@@ -75,6 +75,109 @@ FwdPlan make_plan(int B, int Hkv, int L, int d, int W) {
   return p;
 }
 
+// State import/export of a continuation call (all optional; see lizard_attn_fwd_ext).
+struct FwdExt {
+  const float *state_in = nullptr;
+  const void *win_k_in = nullptr, *win_v_in = nullptr;
+  int32_t *pos = nullptr;
+  float *state_out = nullptr;
+  void *win_k_out = nullptr, *win_v_out = nullptr;
+};
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Rows of window history a continuation stages: W - 1 rounded up to whole chunks.
+int hist_rows_for(int W) { return W > 1 ? ((W - 1 + kChunk - 1) / kChunk) * kChunk : 0; }
+
+size_t ext_hist_bytes(int B, int Hkv, int d, int W, lizard_dtype dtype) {
+  const size_t es = dtype == LIZARD_BF16 ? 2 : 4;
+  return align256((size_t)B * Hkv * hist_rows_for(W) * d * es);
+}
+
+lizard_status fwd_impl(const void *q, const void *k, const void *v, const void *log_gamma, const void *w_phi_q,
+                       const void *w_phi_k, int64_t w_phi_head_stride, const void *t_k, const void *t_v, void *out,
+                       int B, int Hq, int Hkv, int L, int d, int W, int M, float mix, float scale,
+                       lizard_dtype dtype, void *workspace, size_t workspace_bytes, void *stream,
+                       const FwdExt *ext) {
+  if (dtype != LIZARD_F32 && dtype != LIZARD_BF16) return fail(LIZARD_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (B < 0 || L < 0) return fail(LIZARD_ERR_INVALID_ARG, "B=%d and L=%d must be >= 0", B, L);
+  if (Hq < 1 || Hkv < 1 || d < 1 || W < 1 || M < 0)
+    return fail(LIZARD_ERR_INVALID_ARG, "need Hq, Hkv, d, W >= 1 and M >= 0 (got Hq=%d Hkv=%d d=%d W=%d M=%d)", Hq,
+                Hkv, d, W, M);
+  if (Hq % Hkv != 0) return fail(LIZARD_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (w_phi_head_stride < 0) return fail(LIZARD_ERR_INVALID_ARG, "negative w_phi_head_stride");
+  if (!supported_d(d, dtype))
+    return fail(LIZARD_ERR_UNSUPPORTED, "head dim d=%d not built for %s", d, dtype == LIZARD_BF16 ? "bf16" : "fp32");
+  if (M > kMaxMeta) return fail(LIZARD_ERR_UNSUPPORTED, "M=%d meta tokens (at most %d)", M, kMaxMeta);
+  if (w_phi_head_stride != 0 && w_phi_head_stride < (int64_t)d * d)
+    return fail(LIZARD_ERR_INVALID_ARG, "w_phi_head_stride=%lld overlaps matrices of d*d elements",
+                (long long)w_phi_head_stride);
+  if (B == 0 || L == 0) return LIZARD_OK;  // empty problem
+  if (!q || !k || !v || !log_gamma || !w_phi_q || !w_phi_k || !out)
+    return fail(LIZARD_ERR_INVALID_ARG, "null tensor pointer");
+  if (M > 0 && (!t_k || !t_v)) return fail(LIZARD_ERR_INVALID_ARG, "t_k/t_v null with M=%d", M);
+  const void *ptrs[] = {q, k, v, log_gamma, w_phi_q, w_phi_k, out, t_k, t_v};
+  for (const void *ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return fail(LIZARD_ERR_INVALID_ARG, "tensor pointer %p not 16-byte aligned", ptr);
+  if ((int64_t)B * Hq * L > (int64_t)1 << 40) return fail(LIZARD_ERR_INVALID_ARG, "problem too large");
+
+  const bool history = ext && ext->pos && ext->win_k_in;  // window keys before the first token
+  if (ext) {
+    if ((ext->win_k_in == nullptr) != (ext->win_v_in == nullptr) ||
+        (ext->win_k_out == nullptr) != (ext->win_v_out == nullptr))
+      return fail(LIZARD_ERR_INVALID_ARG, "ring keys and values must be given together");
+    if (ext->win_k_in && !ext->pos) return fail(LIZARD_ERR_INVALID_ARG, "a ring in needs pos");
+    if (ext->state_out && ext->state_out == ext->state_in)
+      return fail(LIZARD_ERR_INVALID_ARG, "state_out must not be state_in");
+    const void *eptrs[] = {ext->state_in, ext->win_k_in, ext->win_v_in, ext->state_out, ext->win_k_out,
+                           ext->win_v_out};
+    for (const void *ptr : eptrs)
+      if (ptr && !aligned16(ptr)) return fail(LIZARD_ERR_INVALID_ARG, "tensor pointer %p not 16-byte aligned", ptr);
+    if (ext->pos && (reinterpret_cast<uintptr_t>(ext->pos) & 3u))
+      return fail(LIZARD_ERR_INVALID_ARG, "pos not 4-byte aligned");
+  }
+  const FwdPlan plan = make_plan(B, Hkv, L, d, W);
+  const size_t seg_bytes = plan.ws_state_bytes + plan.ws_decay_bytes;
+  const size_t hist_bytes = history ? ext_hist_bytes(B, Hkv, d, W, dtype) : 0;
+  const size_t need = (hist_bytes ? align256(seg_bytes) : seg_bytes) + 2 * hist_bytes;
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(LIZARD_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(LIZARD_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+  }
+
+  lz::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.lg = log_gamma; p.wq = w_phi_q; p.wk = w_phi_k;
+  p.tk = t_k; p.tv = t_v; p.out = out;
+  p.ws_state = need ? static_cast<float *>(workspace) : nullptr;
+  p.ws_decay = need ? reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.ws_state_bytes) : nullptr;
+  p.w_stride = w_phi_head_stride;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.L = L; p.W = W; p.M = M; p.G = Hq / Hkv;
+  p.nchunks = plan.nchunks; p.nseg = plan.nseg; p.cps = plan.cps; p.ndvb = plan.ndvb; p.nring = plan.nring;
+  p.per_head_q = w_phi_head_stride != 0;
+  p.mix = mix; p.scale = scale;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int esize = dtype == LIZARD_BF16 ? 2 : 4;
+  if (ext) {
+    p.state_in = ext->state_in;
+    p.state_out = ext->state_out;
+    p.pos = history ? ext->pos : nullptr;  // the forward reads pos only to bound the history
+    if (history) {
+      char *h = static_cast<char *>(workspace) + align256(seg_bytes);
+      p.hist_k = h;
+      p.hist_v = h + hist_bytes;
+      p.hist_rows = hist_rows_for(W);
+      hipError_t e = lz::launch_hist_stage(p, ext->win_k_in, ext->win_v_in, d, esize, st);
+      if (e != hipSuccess) return finish(e, st);
+    }
+  }
+  hipError_t e = lz::launch_fwd(p, dtype == LIZARD_BF16, d, st);
+  if (e == hipSuccess && ext && (ext->win_k_out || ext->pos))
+    e = lz::launch_ring_out(p, ext->win_k_in, ext->win_v_in, ext->win_k_out, ext->win_v_out, ext->pos, d, esize, st);
+  return finish(e, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -107,49 +210,36 @@ lizard_status lizard_attn_fwd(const void *q, const void *k, const void *v, const
                               const void *t_k, const void *t_v, void *out, int B, int Hq, int Hkv, int L,
                               int d, int W, int M, float mix, float scale, lizard_dtype dtype,
                               void *workspace, size_t workspace_bytes, void *stream) {
-  if (dtype != LIZARD_F32 && dtype != LIZARD_BF16) return fail(LIZARD_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
-  if (B < 0 || L < 0) return fail(LIZARD_ERR_INVALID_ARG, "B=%d and L=%d must be >= 0", B, L);
-  if (Hq < 1 || Hkv < 1 || d < 1 || W < 1 || M < 0)
-    return fail(LIZARD_ERR_INVALID_ARG, "need Hq, Hkv, d, W >= 1 and M >= 0 (got Hq=%d Hkv=%d d=%d W=%d M=%d)", Hq,
-                Hkv, d, W, M);
-  if (Hq % Hkv != 0) return fail(LIZARD_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
-  if (w_phi_head_stride < 0) return fail(LIZARD_ERR_INVALID_ARG, "negative w_phi_head_stride");
-  if (!supported_d(d, dtype))
-    return fail(LIZARD_ERR_UNSUPPORTED, "head dim d=%d not built for %s", d, dtype == LIZARD_BF16 ? "bf16" : "fp32");
-  if (M > kMaxMeta) return fail(LIZARD_ERR_UNSUPPORTED, "M=%d meta tokens (at most %d)", M, kMaxMeta);
-  if (w_phi_head_stride != 0 && w_phi_head_stride < (int64_t)d * d)
-    return fail(LIZARD_ERR_INVALID_ARG, "w_phi_head_stride=%lld overlaps matrices of d*d elements",
-                (long long)w_phi_head_stride);
-  if (B == 0 || L == 0) return LIZARD_OK;  // empty problem
-  if (!q || !k || !v || !log_gamma || !w_phi_q || !w_phi_k || !out)
-    return fail(LIZARD_ERR_INVALID_ARG, "null tensor pointer");
-  if (M > 0 && (!t_k || !t_v)) return fail(LIZARD_ERR_INVALID_ARG, "t_k/t_v null with M=%d", M);
-  const void *ptrs[] = {q, k, v, log_gamma, w_phi_q, w_phi_k, out, t_k, t_v};
-  for (const void *ptr : ptrs)
-    if (ptr && !aligned16(ptr)) return fail(LIZARD_ERR_INVALID_ARG, "tensor pointer %p not 16-byte aligned", ptr);
-  if ((int64_t)B * Hq * L > (int64_t)1 << 40) return fail(LIZARD_ERR_INVALID_ARG, "problem too large");
+  return fwd_impl(q, k, v, log_gamma, w_phi_q, w_phi_k, w_phi_head_stride, t_k, t_v, out, B, Hq, Hkv, L, d, W, M,
+                  mix, scale, dtype, workspace, workspace_bytes, stream, nullptr);
+}
 
-  const FwdPlan plan = make_plan(B, Hkv, L, d, W);
-  const size_t need = plan.ws_state_bytes + plan.ws_decay_bytes;
-  if (need > 0) {
-    if (!workspace || workspace_bytes < need)
-      return fail(LIZARD_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need,
-                  workspace ? workspace_bytes : (size_t)0);
-    if (!aligned16(workspace)) return fail(LIZARD_ERR_INVALID_ARG, "workspace not 16-byte aligned");
-  }
+size_t lizard_attn_fwd_ext_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int W, lizard_dtype dtype) {
+  (void)Hq;
+  if (B <= 0 || L <= 0 || Hkv <= 0 || d <= 0 || d % kDV != 0) return 0;
+  const FwdPlan p = make_plan(B, Hkv, L, d, W < 1 ? 1 : W);
+  const size_t seg = p.ws_state_bytes + p.ws_decay_bytes;
+  const size_t hist = ext_hist_bytes(B, Hkv, d, W < 1 ? 1 : W, dtype);
+  return hist ? align256(seg) + 2 * hist : seg;
+}
 
-  lz::FwdParams p{};
-  p.q = q; p.k = k; p.v = v; p.lg = log_gamma; p.wq = w_phi_q; p.wk = w_phi_k;
-  p.tk = t_k; p.tv = t_v; p.out = out;
-  p.ws_state = need ? static_cast<float *>(workspace) : nullptr;
-  p.ws_decay = need ? reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.ws_state_bytes) : nullptr;
-  p.w_stride = w_phi_head_stride;
-  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.L = L; p.W = W; p.M = M; p.G = Hq / Hkv;
-  p.nchunks = plan.nchunks; p.nseg = plan.nseg; p.cps = plan.cps; p.ndvb = plan.ndvb; p.nring = plan.nring;
-  p.per_head_q = w_phi_head_stride != 0;
-  p.mix = mix; p.scale = scale;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  return finish(lz::launch_fwd(p, dtype == LIZARD_BF16, d, st), st);
+lizard_status lizard_attn_fwd_ext(const void *q, const void *k, const void *v, const void *log_gamma,
+                                  const void *w_phi_q, const void *w_phi_k, int64_t w_phi_head_stride,
+                                  const void *t_k, const void *t_v, void *out, int B, int Hq, int Hkv, int L,
+                                  int d, int W, int M, float mix, float scale, lizard_dtype dtype,
+                                  const float *state_in, const void *win_k_in, const void *win_v_in,
+                                  int32_t *pos, float *state_out, void *win_k_out, void *win_v_out,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+  FwdExt ext;
+  ext.state_in = state_in;
+  ext.win_k_in = win_k_in;
+  ext.win_v_in = win_v_in;
+  ext.pos = pos;
+  ext.state_out = state_out;
+  ext.win_k_out = win_k_out;
+  ext.win_v_out = win_v_out;
+  return fwd_impl(q, k, v, log_gamma, w_phi_q, w_phi_k, w_phi_head_stride, t_k, t_v, out, B, Hq, Hkv, L, d, W, M,
+                  mix, scale, dtype, workspace, workspace_bytes, stream, &ext);
 }
 
 size_t lizard_attn_decode_workspace_bytes(int N, int Hq, int Hkv, int d, lizard_dtype dtype) {

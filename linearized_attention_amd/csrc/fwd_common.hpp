@@ -16,6 +16,14 @@ constexpr float FAST_SPAN = 60.f; // max |log-decay| across a whole chunk for th
                                   // reference (keys carry e^{+60} at most, queries e^{-60})
 constexpr int LDS_LIMIT = 160 * 1024;
 constexpr int WIN_BATCH = 8;      // key tiles per online-softmax batch in the window
+constexpr int KT_META = -(1 << 28);  // window tile list: the meta tile
+constexpr int KT_NONE = -(1 << 29);  // window tile list: no tile
+
+// a mod m in [0, m) for negative a too (chunk indices of the window history are < 0)
+__device__ __forceinline__ int pmod(int a, int m) {
+  const int r = a % m;
+  return r < 0 ? r + m : r;
+}
 
 template <typename T, int D, int DV> struct FwdGeom {
   static constexpr int PADE = 16 / (int)sizeof(T);

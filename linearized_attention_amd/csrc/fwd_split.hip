@@ -83,6 +83,11 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
   const T *Kh = reinterpret_cast<const T *>(p.k) + kv_off;
   const T *Vh = reinterpret_cast<const T *>(p.v) + kv_off;
   const T *LGh = reinterpret_cast<const T *>(p.lg) + kv_off;
+  // window history before the first token (continuation of earlier tokens)
+  const size_t hist_off = ((size_t)b * p.Hkv + kvh) * (size_t)p.hist_rows * D;
+  const T *Hk = reinterpret_cast<const T *>(p.hist_k) + hist_off;
+  const T *Hv = reinterpret_cast<const T *>(p.hist_v) + hist_off;
+  const int hist_avail = p.pos ? min(p.pos[b], p.W - 1) : 0;  // history tokens the window may see
   const T *Wk = reinterpret_cast<const T *>(p.wk) + (size_t)kvh * p.w_stride;
   const T *Qbase = reinterpret_cast<const T *>(p.q);
   const Frag<T> tri_pre = tri_frag<T>(r16, g4, true);
@@ -114,11 +119,14 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
     const int kt = tid - 256;
     // earlier chunks reached by the window of this segment's first chunk
     const int R = max(NR, KR);
-    for (int cc = max(0, c_begin - (R - 1)); cc < c_begin; ++cc) {
+    for (int cc = max(-(p.hist_rows / CH), c_begin - (R - 1)); cc < c_begin; ++cc) {
       ChunkRegs<T, D, DV> pre;
-      load_chunk<T, D, DV>(pre, Kh, Vh, LGh, cc * CH, L, dv0, true, kt);
-      if (cc > c_begin - KR) store_keys<T, D, DV, LDW>(pre, sKr + (cc % KR) * (CH * LDW), kt);
-      if (cc > c_begin - NR) store_values<T, D, DV, LDC>(pre, sVt + (cc % NR) * (DV * LDC), kt);
+      if (cc >= 0)
+        load_chunk<T, D, DV>(pre, Kh, Vh, LGh, cc * CH, L, dv0, true, kt);
+      else  // history rows (the log gamma slot is not used)
+        load_chunk<T, D, DV>(pre, Hk, Hv, Hk, p.hist_rows + cc * CH, p.hist_rows, dv0, true, kt);
+      if (cc > c_begin - KR) store_keys<T, D, DV, LDW>(pre, sKr + pmod(cc, KR) * (CH * LDW), kt);
+      if (cc > c_begin - NR) store_values<T, D, DV, LDC>(pre, sVt + pmod(cc, NR) * (DV * LDC), kt);
     }
     // S owned by this wave: feature tiles I*FTW .. +FTW-1, all value tiles.
     // S[ft][dt][i] = S[16*(I*FTW+ft) + 4*g4 + i][dv0 + 16*dt + r16]
@@ -127,8 +135,19 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
     for (int ft = 0; ft < FTW; ++ft)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) S[ft][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (p.state_in) {  // continuation: the state after the earlier tokens
+      const float *Si = p.state_in + ((size_t)b * p.Hkv + kvh) * D * D;
+#pragma unroll
+      for (int ft = 0; ft < FTW; ++ft)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            S[ft][dt][i] = Si[(size_t)(16 * (I * FTW + ft) + 4 * g4 + i) * D + dv0 + 16 * dt + r16];
+    }
     {
-      // start state of this segment: S = sum_j diag(prod of later decays) E_j
+      // start state of this segment: S = diag(prod of all earlier decays) S_in
+      //                                  + sum_j diag(prod of later decays) E_j
       const size_t st_per_grp = (size_t)D * DV;
       for (int j = 0; j < seg; ++j) {
         const float *E = p.ws_state + ((((size_t)b * p.Hkv + kvh) * p.ndvb + dvb) * (p.nseg - 1) + j) * st_per_grp;
@@ -294,6 +313,16 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
           store4<T>(sSbf + (16 * dt + r16) * LDW + 16 * (I * FTW + ft) + 4 * g4, S[ft][dt][0], S[ft][dt][1],
                     S[ft][dt][2], S[ft][dt][3]);
     }
+    if (p.state_out && seg == p.nseg - 1) {  // the state after the last token
+      float *So = p.state_out + ((size_t)b * p.Hkv + kvh) * D * D;
+#pragma unroll
+      for (int ft = 0; ft < FTW; ++ft)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            So[(size_t)(16 * (I * FTW + ft) + 4 * g4 + i) * D + dv0 + 16 * dt + r16] = S[ft][dt][i];
+    }
   } else {
     // ======================================================= query waves
     const float mix = p.mix, scale = p.scale;
@@ -309,6 +338,16 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
         const int dk = 16 * u - 80 + 4 * g4 + i - r16;
         const bool in = (u == 0) ? (4 * g4 + i < p.M) : (dk <= 0 && dk > -p.W);
         wmask |= (in ? 1u : 0u) << (4 * u + i);
+      }
+    // the first chunk: band slots before the first token hold history (valid only for
+    // the last hist_avail tokens; band tile u < 5 - I lies in the previous chunk)
+    uint32_t wmask0 = wmask;
+#pragma unroll
+    for (int u = 1; u < 5; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rt = I - 5 + u;
+        if (rt < 0 && 16 * rt + 4 * g4 + i < -hist_avail) wmask0 &= ~(1u << (4 * u + i));
       }
     const T *Q0 = Qbase + ((size_t)b * p.Hq + kvh * G) * (size_t)L * D;
     const Frag<T> tri_c0 = tri64_frag<T>(r16, g4, I, 0), tri_c1 = tri64_frag<T>(r16, g4, I, 1);
@@ -371,7 +410,7 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int j = 0; j < KS; ++j) acc = mma(load8(kr + 32 * j), qf[j], acc);
-          const uint32_t mu = ((c == 0) && rt < 0) ? 0u : (wmask >> (4 * u));  // no keys before 0
+          const uint32_t mu = (c == 0 ? wmask0 : wmask) >> (4 * u);
 #pragma unroll
           for (int i = 0; i < 4; ++i) lt[u][i] = ((mu >> i) & 1u) ? acc[i] * scale : NEG_BIG;
         }
@@ -423,7 +462,8 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
         float m_run = NEG_BIG;
         const int kt_hi = (c0 >> 4) + I;
         const int lo_key = c0 + 16 * I - p.W + 1;
-        const int kt_lo = lo_key <= 0 ? 0 : (lo_key >> 4);
+        const int kt_lo = max(lo_key >> 4, -((hist_avail + 15) >> 4));
+        const int kj_floor = max(pos - p.W, -hist_avail - 1);  // keys above: window and history
         // tile list: u = -1 is the meta tile (if M > 0), then kt_lo..kt_hi
         const int u_first = (p.M > 0) ? -1 : 0;
         const int n_tiles = (kt_hi - kt_lo + 1) - u_first;
@@ -434,9 +474,9 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
             const int u = u0 + uu;
             lt[uu] = f32x4{NEG_BIG, NEG_BIG, NEG_BIG, NEG_BIG};
             if (u < n_tiles) {
-              const int kt = (u + u_first < 0) ? -1 : kt_lo + u + u_first;
+              const int kt = (u + u_first < 0) ? KT_META : kt_lo + u + u_first;
               f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-              if (kt < 0) {
+              if (kt == KT_META) {
 #pragma unroll
                 for (int j = 0; j < KS; ++j) acc = mma(load8(sTk + r16 * LDW + 32 * j + 8 * g4), qf[j], acc);
 #pragma unroll
@@ -444,23 +484,26 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
               } else {
                 const int kc = kt >> 2;
                 if (kc > c - KR) {
-                  const T *kr = sKr + (kc % KR) * (CH * LDW) + (16 * (kt & 3) + r16) * LDW + 8 * g4;
+                  const T *kr = sKr + pmod(kc, KR) * (CH * LDW) + (16 * (kt & 3) + r16) * LDW + 8 * g4;
 #pragma unroll
                   for (int j = 0; j < KS; ++j) acc = mma(load8(kr + 32 * j), qf[j], acc);
                 } else {
                   // key tile older than the LDS ring: global memory
                   const int key = 16 * kt + r16;
-                  const bool kv = key < L;
+
+                  const bool kv = key < L && key >= -hist_avail;
+
+                  const T *krow = (kt >= 0 ? Kh : Hk + (size_t)p.hist_rows * D) + (ptrdiff_t)key * D;  // tiles never straddle 0
 #pragma unroll
                   for (int j = 0; j < KS; ++j) {
-                    const Frag<T> a = kv ? load8(Kh + (size_t)key * D + 32 * j + 8 * g4) : frag_zero<T>();
+                    const Frag<T> a = kv ? load8(krow + 32 * j + 8 * g4) : frag_zero<T>();
                     acc = mma(a, qf[j], acc);
                   }
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                   const int kj = 16 * kt + 4 * g4 + i;
-                  lt[uu][i] = (kj <= pos && kj > pos - p.W) ? acc[i] * scale : NEG_BIG;
+                  lt[uu][i] = (kj <= pos && kj > kj_floor) ? acc[i] * scale : NEG_BIG;
                 }
               }
             }
@@ -495,18 +538,18 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
                 l_run += pv;
               }
             const Frag<T> bf = frag_from<T>(x);
-            const int kta = (ua + u_first < 0) ? -1 : kt_lo + ua + u_first;
-            const int ktb = (ub >= n_tiles) ? -2 : kt_lo + ub + u_first;
-            const bool ring_a = kta >= 0 && (kta >> 2) > c - NR;
-            const bool ring_b = ktb >= 0 && (ktb >> 2) > c - NR;
+            const int kta = (ua + u_first < 0) ? KT_META : kt_lo + ua + u_first;
+            const int ktb = (ub >= n_tiles) ? KT_NONE : kt_lo + ub + u_first;
+            const bool ring_a = kta != KT_META && (kta >> 2) > c - NR;
+            const bool ring_b = ktb != KT_NONE && (ktb >> 2) > c - NR;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
               const int dvl = 16 * dt + r16;
-              const T *pa = (kta < 0) ? sTvT + dvl * LDM + 4 * g4
-                                      : sVt + ((kta >> 2) % NR) * (DV * LDC) + dvl * LDC + 16 * (kta & 3) + 4 * g4;
-              const T *pb = (ktb < 0) ? pa : sVt + ((ktb >> 2) % NR) * (DV * LDC) + dvl * LDC + 16 * (ktb & 3) + 4 * g4;
+              const T *pa = (kta == KT_META) ? sTvT + dvl * LDM + 4 * g4
+                                      : sVt + pmod(kta >> 2, NR) * (DV * LDC) + dvl * LDC + 16 * (kta & 3) + 4 * g4;
+              const T *pb = (ktb == KT_NONE) ? pa : sVt + pmod(ktb >> 2, NR) * (DV * LDC) + dvl * LDC + 16 * (ktb & 3) + 4 * g4;
               Frag<T> af;
-              if ((kta < 0 || ring_a) && (ktb < 0 || ring_b)) {
+              if ((kta == KT_META || ring_a) && (ktb == KT_NONE || ring_b)) {
                 af = load4x2(pa, pb);  // slots of a missing second tile meet P = 0
               } else {
                 // a value tile older than the LDS ring: gather from global memory
@@ -515,10 +558,10 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
                 for (int h = 0; h < 2; ++h) {
                   const int kt = h ? ktb : kta;
                   const bool inring = h ? ring_b : ring_a;
-                  if (kt == -2) {
+                  if (kt == KT_NONE) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) av[4 * h + i] = 0.f;
-                  } else if (kt == -1 || inring) {
+                  } else if (kt == KT_META || inring) {
                     float t4[4];
                     load4f(h ? pb : pa, t4);
 #pragma unroll
@@ -527,7 +570,9 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                       const int key = 16 * kt + 4 * g4 + i;
-                      av[4 * h + i] = (key < L) ? to_f(Vh[(size_t)key * D + dv0 + dvl]) : 0.f;
+                      av[4 * h + i] = (key < L && key >= -hist_avail)
+                        ? to_f((kt >= 0 ? Vh : Hv + (size_t)p.hist_rows * D)[(ptrdiff_t)key * D + dv0 + dvl])
+                        : 0.f;
                     }
                   }
                 }

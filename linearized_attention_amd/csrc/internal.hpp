@@ -15,6 +15,15 @@ struct FwdParams {
   void *out;
   float *ws_state;  // per-segment end states, fp32, fragment order
   float *ws_decay;  // per-segment sums of log gamma, [B][Hkv][nseg-1][d]
+  // continuation of earlier tokens (all optional): start state [B][Hkv][d][d] fp32, the
+  // window history [B][Hkv][hist_rows][d] (row hist_rows - j holds the token j places
+  // before the first one; staged from the caller's ring), its valid length per sequence
+  // min(pos[b], W - 1), and the final state [B][Hkv][d][d]
+  const float *state_in;
+  float *state_out;
+  const void *hist_k, *hist_v;
+  const int32_t *pos;
+  int hist_rows;
   int64_t w_stride;
   int B, Hq, Hkv, L, W, M, G;
   int nchunks, nseg, cps, ndvb, nring, kring, ngroups;
@@ -24,6 +33,12 @@ struct FwdParams {
 };
 
 hipError_t launch_fwd(const FwdParams &p, int dtype_bf16, int d, hipStream_t stream);
+// before the forward: window history rows from the caller's ring; after it: the ring of
+// the last W tokens and pos += L
+hipError_t launch_hist_stage(const FwdParams &p, const void *ring_k, const void *ring_v, int d, int esize,
+                             hipStream_t stream);
+hipError_t launch_ring_out(const FwdParams &p, const void *ring_k_in, const void *ring_v_in, void *ring_k_out,
+                           void *ring_v_out, int32_t *pos, int d, int esize, hipStream_t stream);
 
 struct DecParams {
   float *state;

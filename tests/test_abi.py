@@ -127,3 +127,44 @@ def test_decode_workspace_bytes_formula():
     assert lib.lizard_attn_decode_workspace_bytes(N, 3, 2, d, 1) == 0
     need = lib.lizard_attn_decode_workspace_bytes(4, 2, 2, 128, 1)
     assert _dec(lib, wsb=need - 1) == 3
+
+
+def _fwd_ext(lib, **kw):
+    a = dict(q=16, k=16, v=16, lg=16, wq=16, wk=16, stride=0, tk=16, tv=16, out=16, B=1, Hq=2, Hkv=2,
+             L=64, d=128, W=64, M=4, mix=0.5, scale=0.1, dtype=1, sin=None, rkin=None, rvin=None, pos=None,
+             sout=None, rkout=None, rvout=None, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.lizard_attn_fwd_ext(P(a["q"]), P(a["k"]), P(a["v"]), P(a["lg"]), P(a["wq"]), P(a["wk"]),
+                                   a["stride"], P(a["tk"]), P(a["tv"]), P(a["out"]), a["B"], a["Hq"],
+                                   a["Hkv"], a["L"], a["d"], a["W"], a["M"], a["mix"], a["scale"],
+                                   a["dtype"], P(a["sin"]), P(a["rkin"]), P(a["rvin"]), P(a["pos"]),
+                                   P(a["sout"]), P(a["rkout"]), P(a["rvout"]), P(a["ws"]), a["wsb"],
+                                   P(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rkin=32, rvin=32), 1),                      # a ring in needs pos
+    (dict(rkin=32, pos=64), 1),                       # keys without values
+    (dict(rkout=32), 1),                              # keys out without values
+    (dict(sin=48, sout=48), 1),                       # state_out must not be state_in
+    (dict(pos=66), 1),                                # pos misaligned
+    (dict(sout=40), 1),                               # misaligned state
+    (dict(rkin=32, rvin=32, pos=64, ws=None), 3),     # history needs workspace
+    (dict(d=96), 2),
+])
+def test_fwd_ext_validation_codes(kw, code):
+    lib = api.load()
+    assert _fwd_ext(lib, **kw) == code
+    assert lib.lizard_last_error()
+
+
+def test_fwd_ext_workspace_bytes():
+    lib = api.load()
+    B, Hkv, L, d, W = 2, 4, 256, 128, 100
+    plain = lib.lizard_attn_fwd_workspace_bytes(B, Hkv, Hkv, L, d, W, 1)
+    ext = lib.lizard_attn_fwd_ext_workspace_bytes(B, Hkv, Hkv, L, d, W, 1)
+    hist = B * Hkv * 128 * d * 2            # W - 1 = 99 rows rounded up to 128, bf16
+    assert ext >= plain + 2 * hist
+    assert _fwd_ext(lib, B=B, Hq=Hkv, Hkv=Hkv, L=L, W=W, rkin=32, rvin=32, pos=64, ws=4096, wsb=ext - 1) == 3
+    assert _fwd_ext(lib, L=0) == 0          # empty problem
