@@ -45,24 +45,32 @@ constexpr int kChunk = 64;
 constexpr int kDV = 64;       // value columns per workgroup
 constexpr int kMaxMeta = 16;
 constexpr int kTargetBlocks = 256;
+constexpr int kMaxFullCps = 16384;  // chunks per segment the whole-head kernel's LDS flags cover
 
 struct FwdPlan {
   int nchunks, nseg, cps, ndvb, nring;
+  int sss;  // whole-head kernel: state-pass pieces per segment
   size_t ws_state_bytes, ws_decay_bytes;
 };
 
-// Sequence segments are added until there are about 256 workgroups; an
-// environment override (LIZARD_FWD_SEGMENTS) exists for tests and tuning.
-FwdPlan make_plan(int B, int Hkv, int L, int d, int W) {
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Sequence segments are added until there are about 256 workgroups (one per
+// (batch, head, segment) for the whole-head kernel, one per (batch, head, 64-column
+// value block, segment) otherwise); an environment override (LIZARD_FWD_SEGMENTS)
+// exists for tests and tuning.  The segment end states are kept per 64-column
+// value block in either case (the state pass works per block).
+FwdPlan make_plan(int B, int Hkv, int L, int d, int W, bool full) {
   FwdPlan p{};
   p.nchunks = (L + kChunk - 1) / kChunk;
   p.ndvb = d / kDV;
-  const long base = (long)B * Hkv * p.ndvb;
+  const long base = (long)B * Hkv * (full ? 1 : p.ndvb);
   long nseg = (kTargetBlocks + base - 1) / base;
   if (const char *e = getenv("LIZARD_FWD_SEGMENTS")) {
     const long v = atol(e);
     if (v >= 1) nseg = v;
   }
+  if (full && nseg < (p.nchunks + kMaxFullCps - 1) / kMaxFullCps) nseg = (p.nchunks + kMaxFullCps - 1) / kMaxFullCps;
   if (nseg > p.nchunks) nseg = p.nchunks;
   if (nseg < 1) nseg = 1;
   p.cps = (int)((p.nchunks + nseg - 1) / nseg);
@@ -70,9 +78,41 @@ FwdPlan make_plan(int B, int Hkv, int L, int d, int W) {
   p.nring = (W - 1 <= kChunk) ? 2 : 3;
   if (p.nseg > 1) {
     p.ws_state_bytes = (size_t)B * Hkv * p.ndvb * (p.nseg - 1) * (size_t)d * kDV * sizeof(float);
-    p.ws_decay_bytes = (size_t)B * Hkv * (p.nseg - 1) * (size_t)d * sizeof(float);
+    p.ws_decay_bytes = align256((size_t)B * Hkv * (p.nseg - 1) * (size_t)d * sizeof(float));
+  }
+  p.sss = 1;
+  if (full && p.nseg > 1) {
+    // the state pass (all chunks before the last segment) in about kTargetBlocks pieces
+    long ss = kTargetBlocks / ((long)B * Hkv * (p.nseg - 1));
+    if (ss < 1) ss = 1;
+    if (ss > p.cps) ss = p.cps;
+    while (p.cps % ss) --ss;
+    p.sss = (int)ss;
+    p.ws_state_bytes = (size_t)B * Hkv * (p.nseg - 1) * p.sss * (size_t)d * d * sizeof(float);
+    p.ws_decay_bytes = align256((size_t)B * Hkv * (p.nseg - 1) * p.sss * (size_t)d * sizeof(float));
   }
   return p;
+}
+
+size_t plan_bytes(const FwdPlan &p) { return p.ws_state_bytes + p.ws_decay_bytes; }
+
+// The whole-head kernel serves bf16 at d = 128 with one W_phi for queries and keys,
+// one query head per key/value head and W <= 65 (LIZARD_FWD_KERNEL=split or 4wave
+// selects the value-block kernels instead, for tests and A/B timing).
+bool use_full_kernel(int Hq, int Hkv, int d, int W, lizard_dtype dtype, const void *wq, const void *wk,
+                     int64_t w_stride) {
+  const char *kenv = getenv("LIZARD_FWD_KERNEL");
+  if (kenv && (strcmp(kenv, "split") == 0 || strcmp(kenv, "4wave") == 0)) return false;
+  return dtype == LIZARD_BF16 && d == 128 && Hq == Hkv && W <= kChunk + 1 && wq == wk && w_stride == 0;
+}
+
+// Workspace for either plan (the caller does not say whether W_phi is shared).
+size_t seg_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int W, lizard_dtype dtype) {
+  const size_t sa = plan_bytes(make_plan(B, Hkv, L, d, W, false));
+  const bool maybe_full = dtype == LIZARD_BF16 && d == 128 && Hq == Hkv && W <= kChunk + 1 &&
+                          use_full_kernel(Hq, Hkv, d, W, dtype, nullptr, nullptr, 0);
+  const size_t sb = maybe_full ? plan_bytes(make_plan(B, Hkv, L, d, W, true)) : 0;
+  return sa > sb ? sa : sb;
 }
 
 // State import/export of a continuation call (all optional; see lizard_attn_fwd_ext).
@@ -83,8 +123,6 @@ struct FwdExt {
   float *state_out = nullptr;
   void *win_k_out = nullptr, *win_v_out = nullptr;
 };
-
-size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // Rows of window history a continuation stages: W - 1 rounded up to whole chunks.
 int hist_rows_for(int W) { return W > 1 ? ((W - 1 + kChunk - 1) / kChunk) * kChunk : 0; }
@@ -136,8 +174,9 @@ lizard_status fwd_impl(const void *q, const void *k, const void *v, const void *
     if (ext->pos && (reinterpret_cast<uintptr_t>(ext->pos) & 3u))
       return fail(LIZARD_ERR_INVALID_ARG, "pos not 4-byte aligned");
   }
-  const FwdPlan plan = make_plan(B, Hkv, L, d, W);
-  const size_t seg_bytes = plan.ws_state_bytes + plan.ws_decay_bytes;
+  const bool full = use_full_kernel(Hq, Hkv, d, W, dtype, w_phi_q, w_phi_k, w_phi_head_stride);
+  const FwdPlan plan = make_plan(B, Hkv, L, d, W, full);
+  const size_t seg_bytes = plan_bytes(plan);
   const size_t hist_bytes = history ? ext_hist_bytes(B, Hkv, d, W, dtype) : 0;
   const size_t need = (hist_bytes ? align256(seg_bytes) : seg_bytes) + 2 * hist_bytes;
   if (need > 0) {
@@ -156,6 +195,8 @@ lizard_status fwd_impl(const void *q, const void *k, const void *v, const void *
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.L = L; p.W = W; p.M = M; p.G = Hq / Hkv;
   p.nchunks = plan.nchunks; p.nseg = plan.nseg; p.cps = plan.cps; p.ndvb = plan.ndvb; p.nring = plan.nring;
   p.per_head_q = w_phi_head_stride != 0;
+  p.full = full ? 1 : 0;
+  p.sss = plan.sss;
   p.mix = mix; p.scale = scale;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int esize = dtype == LIZARD_BF16 ? 2 : 4;
@@ -201,8 +242,7 @@ size_t lizard_attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int
   (void)Hq;
   (void)dtype;
   if (B <= 0 || L <= 0 || Hkv <= 0 || d <= 0 || d % kDV != 0) return 0;
-  const FwdPlan p = make_plan(B, Hkv, L, d, W < 1 ? 1 : W);
-  return p.ws_state_bytes + p.ws_decay_bytes;
+  return seg_workspace_bytes(B, Hq, Hkv, L, d, W < 1 ? 1 : W, dtype);
 }
 
 lizard_status lizard_attn_fwd(const void *q, const void *k, const void *v, const void *log_gamma,
@@ -217,8 +257,7 @@ lizard_status lizard_attn_fwd(const void *q, const void *k, const void *v, const
 size_t lizard_attn_fwd_ext_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int W, lizard_dtype dtype) {
   (void)Hq;
   if (B <= 0 || L <= 0 || Hkv <= 0 || d <= 0 || d % kDV != 0) return 0;
-  const FwdPlan p = make_plan(B, Hkv, L, d, W < 1 ? 1 : W);
-  const size_t seg = p.ws_state_bytes + p.ws_decay_bytes;
+  const size_t seg = seg_workspace_bytes(B, Hq, Hkv, L, d, W < 1 ? 1 : W, dtype);
   const size_t hist = ext_hist_bytes(B, Hkv, d, W < 1 ? 1 : W, dtype);
   return hist ? align256(seg) + 2 * hist : seg;
 }

@@ -53,14 +53,14 @@
 
 namespace lz {
 
-template <typename T, int D, int DV, bool STATE_ONLY>
+template <typename T, int D, int DV, bool STATE_ONLY, bool WIDE>
 __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
-  using Gm = FwdGeom<T, D, DV>;
+  using Gm = FwdGeom<T, D, DV, WIDE>;
   constexpr int NFT = D / 16;   // 16-row tiles of the feature dimension
   constexpr int KS = D / 32;    // K = 32 steps over d (or over features)
   constexpr int NDT = DV / 16;  // 16-column tiles of this block's value columns
   constexpr int FTW = NFT / 4;  // feature tiles of S owned by each wave
-  constexpr int LDW = Gm::LDW, LDC = Gm::LDC, LDM = Gm::LDM;
+  constexpr int LDW = Gm::LDW, LDB = Gm::LDB, LDC = Gm::LDC, LDG = Gm::LDG, LDM = Gm::LDM;
   static_assert(NFT % 4 == 0, "d must be a multiple of 64");
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
     for (int ft = 0; ft < FTW; ++ft)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
-        store4<T>(sSbf + (16 * dt + r16) * LDW + 16 * (wv * FTW + ft) + 4 * g4, S[ft][dt][0], S[ft][dt][1],
+        store4<T>(sSbf + (16 * dt + r16) * LDB + 16 * (wv * FTW + ft) + 4 * g4, S[ft][dt][0], S[ft][dt][1],
                   S[ft][dt][2], S[ft][dt][3]);
   }
 
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
     // ---- this chunk's keys, values, log gamma (loaded one chunk ahead) -> LDS
     store_keys<T, D, DV, LDW>(pf, sKr + kcur, tid);
     store_values<T, D, DV, LDC>(pf, sVt + cur, tid);
-    store_lgT<T, D, DV, LDC>(pf, sLgT, tid);
+    store_lgT<T, D, DV, LDG>(pf, sLgT, tid);
     Frag<T> qf[KS];
     if constexpr (!STATE_ONLY) {
 #pragma unroll
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
     float pfx[NFT][4], sfx[NFT][4];
 #pragma unroll
     for (int ft = 0; ft < NFT; ++ft) {
-      const Frag<T> a = (g4 < 2) ? load8(sLgT + (16 * ft + r16) * LDC + 16 * I + 8 * g4) : frag_zero<T>();
+      const Frag<T> a = (g4 < 2) ? load8(sLgT + (16 * ft + r16) * LDG + 16 * I + 8 * g4) : frag_zero<T>();
       const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
       const f32x4 pp = mma(a, tri_pre, zero);
       const f32x4 ss = mma(a, tri_suf, zero);
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
     }
 #pragma unroll
     for (int ft = 0; ft < NFT; ++ft)
-      store4<T>(sKown + (16 * I + r16) * LDW + 16 * ft + 4 * g4, ko[ft][0], ko[ft][1], ko[ft][2], ko[ft][3]);
+      store4<T>(sKown + (16 * I + r16) * LDB + 16 * ft + 4 * g4, ko[ft][0], ko[ft][1], ko[ft][2], ko[ft][3]);
     __syncthreads();  // B2: tables and keys visible
 
     if constexpr (!STATE_ONLY) {
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
                   for (int jj = 0; jj < 8; ++jj) x[jj] *= t8[jj];
                 }
               }
-              const T *kr = sKown + (16 * J + r16) * LDW + 32 * js + 4 * g4;
+              const T *kr = sKown + (16 * J + r16) * LDB + 32 * js + 4 * g4;
               acc = mma(load4x2(kr, kr + 16), frag_from<T>(x), acc);
             }
             at[J] = acc;
@@ -498,7 +498,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
           const Frag<T> bf = frag_from<T>(x);
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) {
-            const T *sr = sSbf + (16 * dt + r16) * LDW + 32 * js + 4 * g4;
+            const T *sr = sSbf + (16 * dt + r16) * LDB + 32 * js + 4 * g4;
             yacc[dt] = mma(load4x2(sr, sr + 16), bf, yacc[dt]);
           }
         }
@@ -737,7 +737,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
           if (J2 > J) fac *= et[J2];
         float x[8];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) x[jj] = to_f(sKown[(32 * ks + 8 * g4 + jj) * LDW + fr + r16]) * fac;
+        for (int jj = 0; jj < 8; ++jj) x[jj] = to_f(sKown[(32 * ks + 8 * g4 + jj) * LDB + fr + r16]) * fac;
         ka[ks] = frag_from<T>(x);
       }
 #pragma unroll
@@ -748,7 +748,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
         for (int ks = 0; ks < 2; ++ks)
           S[ft][dt] = mma(ka[ks], load8(sVt + cur + (16 * dt + r16) * LDC + 32 * ks + 8 * g4), S[ft][dt]);
         if constexpr (!STATE_ONLY)
-          store4<T>(sSbf + (16 * dt + r16) * LDW + fr + 4 * g4, S[ft][dt][0], S[ft][dt][1], S[ft][dt][2],
+          store4<T>(sSbf + (16 * dt + r16) * LDB + fr + 4 * g4, S[ft][dt][0], S[ft][dt][1], S[ft][dt][2],
                     S[ft][dt][3]);
       }
     }
@@ -787,10 +787,10 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
 }
 
 // ---------------------------------------------------------------- host side
-template <typename T, int D, int DV, bool STATE_ONLY>
+template <typename T, int D, int DV, bool STATE_ONLY, bool WIDE>
 static hipError_t launch_one(const FwdParams &p, hipStream_t stream) {
   const int grid = ((p.ngroups + 7) / 8) * 8 * p.ndvb;
-  auto kern = fwd_kernel<T, D, DV, STATE_ONLY>;
+  auto kern = fwd_kernel<T, D, DV, STATE_ONLY, WIDE>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, p.lds.total);
   if (e != hipSuccess) return e;
@@ -798,38 +798,56 @@ static hipError_t launch_one(const FwdParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename T, int D, int DV>
-static hipError_t launch_fwd_t(const FwdParams &prm, hipStream_t stream) {
+// Deepest value / key rings that fit in LDS (tiles older than a ring are read from
+// global memory); false when no layout fits.
+template <typename T, int D, int DV, bool WIDE>
+static bool plan_rings(FwdParams &p, bool shared_w) {
+  for (int nr = p.nring; nr >= 2; --nr)
+    for (int kr = nr; kr >= 1; --kr) {
+      const FwdLds l = make_lds<T, D, DV, WIDE>(false, shared_w, nr, kr);
+      if (l.total <= LDS_LIMIT) {
+        p.lds = l;
+        p.nring = nr;
+        p.kring = kr;
+        return true;
+      }
+    }
+  return false;
+}
+
+template <typename T, int D, int DV, bool WIDE>
+static hipError_t launch_fwd_w(const FwdParams &prm, bool shared_w, hipStream_t stream) {
   FwdParams p = prm;
-  const bool shared_w = (p.wq == p.wk) && p.w_stride == 0;
+  if (p.full) {
+    p.ngroups = p.B * p.Hkv * p.nseg;
+    return launch_fwd_full(p, stream);
+  }
   if (p.nseg > 1) {
     FwdParams s = p;
     s.ngroups = p.B * p.Hkv * (p.nseg - 1);
     s.nring = 1;
     s.kring = 1;
-    s.lds = make_lds<T, D, DV>(true, shared_w, 1, 1);
-    hipError_t e = launch_one<T, D, DV, true>(s, stream);
+    s.lds = make_lds<T, D, DV, WIDE>(true, shared_w, 1, 1);
+    hipError_t e = launch_one<T, D, DV, true, WIDE>(s, stream);
     if (e != hipSuccess) return e;
   }
   p.ngroups = p.B * p.Hkv * p.nseg;
-  // deepest value / key rings that fit; tiles older than a ring are read from global memory
-  bool fit = false;
-  for (int nr = p.nring; nr >= 2 && !fit; --nr)
-    for (int kr = nr; kr >= 1 && !fit; --kr) {
-      p.lds = make_lds<T, D, DV>(false, shared_w, nr, kr);
-      if (p.lds.total <= LDS_LIMIT) {
-        p.nring = nr;
-        p.kring = kr;
-        fit = true;
-      }
-    }
-  if (!fit) return hipErrorInvalidConfiguration;
+  if (!plan_rings<T, D, DV, WIDE>(p, shared_w)) return hipErrorInvalidConfiguration;
   // The role-split kernel serves one query head per key/value head; grouped query heads
   // (whose per-head work would fall on the query waves alone) run on the 4-wave kernel.
   const char *kenv = getenv("LIZARD_FWD_KERNEL");  // "4wave": force the 4-wave kernel (tests, A/B timing)
   const bool force_4wave = kenv && strcmp(kenv, "4wave") == 0;
-  if (!force_4wave && p.G == 1) return launch_fwd_split<T, D, DV>(p, stream);
-  return launch_one<T, D, DV, false>(p, stream);
+  if (!force_4wave && p.G == 1) return launch_fwd_split<T, D, DV, WIDE>(p, stream);
+  return launch_one<T, D, DV, false, WIDE>(p, stream);
+}
+
+// The wide row stride when the full-depth rings fit with it, else the narrow one.
+template <typename T, int D, int DV>
+static hipError_t launch_fwd_t(const FwdParams &prm, hipStream_t stream) {
+  const bool shared_w = (prm.wq == prm.wk) && prm.w_stride == 0;
+  FwdParams probe = prm;
+  const bool wide = plan_rings<T, D, DV, true>(probe, shared_w) && probe.nring == prm.nring && probe.kring == prm.nring;
+  return wide ? launch_fwd_w<T, D, DV, true>(prm, shared_w, stream) : launch_fwd_w<T, D, DV, false>(prm, shared_w, stream);
 }
 
 hipError_t launch_fwd(const FwdParams &p, int dtype_bf16, int d, hipStream_t stream) {

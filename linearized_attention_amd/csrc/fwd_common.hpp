@@ -25,26 +25,34 @@ __device__ __forceinline__ int pmod(int a, int m) {
   return r < 0 ? r + m : r;
 }
 
-template <typename T, int D, int DV> struct FwdGeom {
-  static constexpr int PADE = 16 / (int)sizeof(T);
-  static constexpr int LDW = D + PADE;   // rows of D elements
-  static constexpr int LDC = CH + PADE;  // rows of 64 tokens
+// Row strides.  gfx950 serves 16-byte LDS reads of an MFMA fragment (16 rows x 4
+// column groups) without bank conflicts when the row stride is an odd multiple of
+// 32 bytes, and 8-byte reads when it is an odd multiple of 16 bytes (measured).
+// Rows read 16 bytes at a time (W^T, keys, meta keys, log gamma^T) take the wide
+// stride when the layout fits (WIDE), rows read 8 bytes at a time the narrow one.
+template <typename T, int D, int DV, bool WIDE> struct FwdGeom {
+  static constexpr int PADE = 16 / (int)sizeof(T);            // 16 bytes
+  static constexpr int PADW = (WIDE ? 32 : 16) / (int)sizeof(T);
+  static constexpr int LDW = D + PADW;   // rows of D elements, 16-byte reads
+  static constexpr int LDB = D + PADE;   // rows of D elements, 8-byte reads
+  static constexpr int LDC = CH + PADE;  // rows of 64 tokens, 8-byte reads
+  static constexpr int LDG = CH + PADW;  // rows of 64 tokens, 16-byte reads
   static constexpr int LDM = 16 + PADE;  // rows of 16 meta tokens
   static constexpr int SZ_W = D * LDW * (int)sizeof(T);
   static constexpr int SZ_VT = DV * LDC * (int)sizeof(T);
   static constexpr int SZ_KR = CH * LDW * (int)sizeof(T);
   // keys decayed to their sub-chunk end [s][f], overlaid on log gamma^T [f][s]
-  static constexpr int SZ_KOWN = (CH * LDW > D * LDC ? CH * LDW : D * LDC) * (int)sizeof(T);
+  static constexpr int SZ_KOWN = (CH * LDB > D * LDG ? CH * LDB : D * LDG) * (int)sizeof(T);
   static constexpr int SZ_SUB = 4 * D * (int)sizeof(float);  // one [4][D] fp32 table
-  static constexpr int SZ_SBF = DV * LDW * (int)sizeof(T);
+  static constexpr int SZ_SBF = DV * LDB * (int)sizeof(T);
   static constexpr int SZ_TVT = DV * LDM * (int)sizeof(T);
   static constexpr int SZ_TK = 16 * LDW * (int)sizeof(T);
 };
 
 // Byte offsets of the LDS regions for one launch (computed on the host).
-template <typename T, int D, int DV>
+template <typename T, int D, int DV, bool WIDE>
 static FwdLds make_lds(bool state_only, bool shared_w, int nr, int kr) {
-  using Gm = FwdGeom<T, D, DV>;
+  using Gm = FwdGeom<T, D, DV, WIDE>;
   FwdLds l{};
   int o = 0;
   l.wk = o; o += Gm::SZ_W;
@@ -286,8 +294,18 @@ __device__ __forceinline__ bool chunk_is_mild(const float *sTot, int lane) {
   return wave_max_all(m) <= FAST_SPAN;
 }
 
+// Same test when the table holds prefix sums from the chunk start (row 3 = the
+// chunk total), as in the whole-head kernel.
+template <int D>
+__device__ __forceinline__ bool chunk_is_mild_c(const float *sC, int lane) {
+  float m = 0.f;
+#pragma unroll
+  for (int q = 0; q < D / 64; ++q) m = fmaxf(m, -sC[3 * D + lane + 64 * q]);
+  return wave_max_all(m) <= FAST_SPAN;
+}
+
 // Role-split forward (fwd_split.hip): 8 waves per workgroup.
-template <typename T, int D, int DV>
+template <typename T, int D, int DV, bool WIDE>
 hipError_t launch_fwd_split(const FwdParams &p, hipStream_t stream);
 
 }  // namespace lz

@@ -1,0 +1,1038 @@
+// Lizard attention forward, whole-head variant (bf16, d = 128, window W <= 65,
+// one query head per key/value head): one workgroup per (batch, head, sequence
+// segment) computes all 128 value columns, so the feature maps, the gate sums,
+// the window logits and the intra-chunk scores are computed once per head
+// instead of once per 64-column value block.
+//
+// The arithmetic is that of the role-split kernel (fwd_split.hip), with the
+// decay references of fwd.hip: a chunk whose log decay stays within FAST_SPAN
+// for every feature refers all decays to the chunk start, other chunks use
+// 16-token sub-chunk references.  What changes is the work split and the LDS
+// layout:
+//
+//   key waves (4..7), sub-chunk I = wave - 4: stage the chunk's keys (in MFMA
+//     fragment order, straight from the loads) and log gamma^T; gate prefix
+//     sums; phi_k and the decayed keys; the per-chunk factor tables; the state
+//     update for feature rows 32I..32I+31 of S (fp32 registers, all 128 value
+//     columns) and the bf16 copy of S^T that the query waves read.
+//   query waves (0..3), sub-chunk I = wave: stage v^T; phi_q; the window; the
+//     intra- and inter-chunk products, the merge and the stores for rows
+//     16I..16I+15 and all 128 value columns.
+//
+// Only the current chunk's keys and values are in LDS (a second chunk would not
+// fit next to W_phi^T and the state copy).  The window of a query row reaches
+// back at most 64 keys, i.e. into the previous chunk, so it is split in two
+// groups combined by an online softmax: the meta tokens and the previous chunk's
+// keys (group X, computed at the top of the chunk while the previous chunk is
+// still in LDS), and the current chunk's keys (group Y).
+//
+// Operand layouts: within every 32-element group along a contraction, element
+// e = 16h + 4q + i is stored at position 8q + 4h + i ("interleaved").  An MFMA
+// accumulator holds 4 consecutive rows of two 16-row tiles in each lane, and the
+// interleaved layout turns the matching operand read into one 16-byte LDS read.
+// It is used for the features of the decayed keys and of the state copy, and for
+// the tokens of v^T.  Row strides are odd multiples of 32 bytes, which gfx950
+// serves without bank conflicts for 16-byte fragment reads.
+#include <type_traits>
+
+#include "fwd_common.hpp"
+
+namespace lz {
+namespace full {
+
+constexpr int D = 128, NFT = 8, KS = 4, NDT = 8, FTW = 2;
+constexpr int LDW = 144;  // rows of 128 elements (288 bytes)
+constexpr int LDV = 80;   // rows of 64 tokens (160 bytes)
+constexpr int LDM = 24;   // rows of 16 meta tokens (48 bytes, 8-byte reads)
+constexpr int OFF_W = 0;                        // W_phi^T [f][d]
+constexpr int OFF_K = OFF_W + D * LDW * 2;      // keys of the chunk [s][d]
+constexpr int OFF_VT = OFF_K + CH * LDW * 2;    // v^T [dv][token, interleaved]
+constexpr int OFF_KT = OFF_VT + D * LDV * 2;    // decayed keys [s][f, interleaved] / log gamma^T [f][s]
+constexpr int SZ_KT = (CH * LDW > D * LDV ? CH * LDW : D * LDV) * 2;
+constexpr int OFF_SB = OFF_KT + SZ_KT;          // S^T copy [dv][f, interleaved]
+constexpr int OFF_TAB = OFF_SB + D * LDW * 2;   // five [4][128] fp32 tables
+constexpr int OFF_TK = OFF_TAB + 5 * 4 * D * 4; // meta keys [16][d]
+constexpr int OFF_TV = OFF_TK + 16 * LDW * 2;   // meta values^T [dv][16]
+constexpr int OFF_FLAG = OFF_TV + D * LDM * 2;   // per query wave: bit k = chunk c_begin + k needs
+constexpr int FLAG_WORDS = 512;                  // the exact diagonal block (segments of at most 16384 chunks)
+constexpr int LDS_BYTES = OFF_FLAG + 4 * FLAG_WORDS * 4;
+static_assert(LDS_BYTES <= LDS_LIMIT, "whole-head layout exceeds LDS");
+
+// position of element e (0..31) of a 32-element group in the interleaved layout
+__device__ __forceinline__ int ipos(int e) { return (e & 3) | ((e >> 4) << 2) | (((e >> 2) & 3) << 3); }
+// token of slot j (0..7) of lane group kq in a 32-wide interleaved operand
+__device__ __forceinline__ int islot(int kq, int j) { return 16 * (j >> 2) + 4 * kq + (j & 3); }
+
+}  // namespace full
+
+// Exact diagonal-block scores for a sub-chunk whose log decay spans more than
+// SPAN_MAX (e.g. gamma ~ 0): A[t][s] = mix sum_f phi_q[t][f] phi_k[s][f] e^{p_t[f] - p_s[f]}
+// in fp32, p the log-gamma prefix inside the sub-chunk, phi recomputed from q and the
+// keys.  Lane (t = lane % 16, g = lane / 16) returns s = 4g .. 4g+3.
+__device__ __forceinline__ f32x4 exact_diag_scores(const bf16 *sW, const bf16 *Kh, const bf16 *LGh, const bf16 *Qh,
+                                                 int c0, int I, int L, float mix) {
+  using namespace full;
+  using T = bf16;
+  const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
+  const Frag<T> tri_pre = tri_frag<T>(r16, g4, true);
+  Frag<T> kfr[KS], qfr[KS];
+  const int t0 = c0 + 16 * I + r16;
+#pragma unroll
+  for (int j = 0; j < KS; ++j) {
+    kfr[j] = (t0 < L) ? load8(Kh + (size_t)t0 * D + 32 * j + 8 * g4) : frag_zero<T>();
+    qfr[j] = (t0 < L) ? load8(Qh + (size_t)t0 * D + 32 * j + 8 * g4) : frag_zero<T>();
+  }
+  auto logits_ft = [&](const Frag<T>(&x)[KS], int ft) {
+    f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KS; ++j) z = mma(load8(sW + (16 * ft + r16) * LDW + 32 * j + 8 * g4), x[j], z);
+    return z;
+  };
+  float mq = NEG_BIG, mk = NEG_BIG;
+  for (int ft = 0; ft < NFT; ++ft) {
+    const f32x4 zq = logits_ft(qfr, ft), zk = logits_ft(kfr, ft);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { mq = fmaxf(mq, zq[i]); mk = fmaxf(mk, zk[i]); }
+  }
+  mq = wave_max_cols(mq);
+  mk = wave_max_cols(mk);
+  float sq = 0.f, sk = 0.f;
+  for (int ft = 0; ft < NFT; ++ft) {
+    const f32x4 zq = logits_ft(qfr, ft), zk = logits_ft(kfr, ft);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { sq += __expf(zq[i] - mq); sk += __expf(zk[i] - mk); }
+  }
+  const float iq = 1.f / wave_sum_cols(sq), ik = 1.f / wave_sum_cols(sk);
+  float part[16];
+#pragma unroll
+  for (int s2 = 0; s2 < 16; ++s2) part[s2] = 0.f;
+  for (int ft = 0; ft < NFT; ++ft) {
+    const f32x4 zq = logits_ft(qfr, ft), zk = logits_ft(kfr, ft);
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = c0 + 16 * I + 8 * g4 + j;
+      x[j] = (g4 < 2 && t < L) ? to_f(LGh[(size_t)t * D + 16 * ft + r16]) : 0.f;
+    }
+    const f32x4 px = mma(frag_from<T>(x), tri_pre, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float phq = __expf(zq[i] - mq) * iq, phk = __expf(zk[i] - mk) * ik;
+#pragma unroll
+      for (int s2 = 0; s2 < 16; ++s2) {
+        const float pk = __shfl(phk, 16 * g4 + s2);
+        const float bs = __shfl(px[i], 16 * g4 + s2);
+        part[s2] += (s2 <= r16) ? phq * pk * __expf(px[i] - bs) : 0.f;
+      }
+    }
+  }
+  f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s2 = 0; s2 < 16; ++s2) {
+    const float v = wave_sum_cols(part[s2]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if ((s2 >> 2) == g4 && (s2 & 3) == i) a[i] = v * mix;
+  }
+  return a;
+}
+
+// y_t += mix sum_{s<=t} A[t][s] v_s over the 16 rows of sub-chunk I of the chunk at c0, with A
+// the exact diagonal-block scores: read-modify-write of rows this wave stored (same-wave
+// ordering makes the stores visible to the loads).
+__device__ __forceinline__ void exact_diag_fixup(const bf16 *sW, const bf16 *Kh, const bf16 *Vh, const bf16 *LGh,
+                                                 const bf16 *Qh, bf16 *Oh, int c0, int I, int L, float mix) {
+  using namespace full;
+  using T = bf16;
+  const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
+  const f32x4 a = exact_diag_scores(sW, Kh, LGh, Qh, c0, I, L, mix);
+  // lane (t, g) holds A[t][4g + i]; y_t[dv] += sum_s A[t][s] v_s[dv] for dv = 32g .. 32g+31
+  float arow[16];
+#pragma unroll
+  for (int s2 = 0; s2 < 16; ++s2) {
+    const float v = __shfl(a[s2 & 3], 16 * (s2 >> 2) + r16);
+    arow[s2] = (s2 <= r16) ? v : 0.f;
+  }
+  const int t = c0 + 16 * I + r16;
+  if (t >= L) return;
+  T *O = Oh + (size_t)t * D + 32 * g4;
+#pragma unroll 1
+  for (int q8 = 0; q8 < 4; ++q8) {
+    float y[8];
+    load8f(O + 8 * q8, y);
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2) {
+      const int sr = c0 + 16 * I + s2;
+      if (sr < L) {
+        float v8[8];
+        load8f(Vh + (size_t)sr * D + 32 * g4 + 8 * q8, v8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] += arow[s2] * v8[e];
+      }
+    }
+    store4<T>(O + 8 * q8, y[0], y[1], y[2], y[3]);
+    store4<T>(O + 8 * q8 + 4, y[4], y[5], y[6], y[7]);
+  }
+}
+
+__global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
+  using namespace full;
+  using T = bf16;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  T *sW = reinterpret_cast<T *>(smem + OFF_W);
+  T *sK = reinterpret_cast<T *>(smem + OFF_K);
+  T *sVt = reinterpret_cast<T *>(smem + OFF_VT);
+  T *sKt = reinterpret_cast<T *>(smem + OFF_KT);
+  T *sLgT = sKt;  // log gamma^T, dead before the decayed keys are written
+  T *sSb = reinterpret_cast<T *>(smem + OFF_SB);
+  float *sTot = reinterpret_cast<float *>(smem + OFF_TAB);  // C_J: prefix from the chunk start to the end of J
+  float *sP7 = sTot + 4 * D;                                // prefix from the chunk start to row 16J + 7
+  float *sETot = sP7 + 4 * D;
+  float *sENP7 = sETot + 4 * D;
+  float *sENR8 = sENP7 + 4 * D;
+  T *sTk = reinterpret_cast<T *>(smem + OFF_TK);
+  T *sTvT = reinterpret_cast<T *>(smem + OFF_TV);
+  uint32_t *sFlag = reinterpret_cast<uint32_t *>(smem + OFF_FLAG);
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const bool key_wave = wv >= 4;
+  const int I = wv & 3;
+
+  const int grp = blockIdx.x;
+  if (grp >= p.ngroups) return;
+  const int seg = grp % p.nseg;
+  const int bh = grp / p.nseg;
+  const int b = bh / p.Hkv, kvh = bh % p.Hkv;
+  const int L = p.L;
+  const int c_begin = seg * p.cps;
+  const int c_end = min(p.nchunks, c_begin + p.cps);
+
+  const size_t kv_off = ((size_t)b * p.Hkv + kvh) * (size_t)L * D;
+  const T *Kh = reinterpret_cast<const T *>(p.k) + kv_off;
+  const T *Vh = reinterpret_cast<const T *>(p.v) + kv_off;
+  const T *LGh = reinterpret_cast<const T *>(p.lg) + kv_off;
+  const T *Qh = reinterpret_cast<const T *>(p.q) + ((size_t)b * p.Hq + kvh) * (size_t)L * D;
+  T *Oh = reinterpret_cast<T *>(p.out) + ((size_t)b * p.Hq + kvh) * (size_t)L * D;
+  const size_t hist_off = ((size_t)b * p.Hkv + kvh) * (size_t)p.hist_rows * D;
+  const T *Hk = reinterpret_cast<const T *>(p.hist_k) + hist_off;
+  const T *Hv = reinterpret_cast<const T *>(p.hist_v) + hist_off;
+  const int hist_avail = p.pos ? min(p.pos[b], p.W - 1) : 0;  // history tokens the window may see
+  // key / value row x of the sequence (x < 0: history), zero outside [-hist_avail.., L)
+  auto krow = [&](int x) -> const T * { return x >= 0 ? Kh + (size_t)x * D : Hk + (ptrdiff_t)(p.hist_rows + x) * D; };
+  auto vrow = [&](int x) -> const T * { return x >= 0 ? Vh + (size_t)x * D : Hv + (ptrdiff_t)(p.hist_rows + x) * D; };
+  auto row_ok = [&](int x) { return x < L && (x >= 0 || (p.hist_rows > 0 && x >= -p.hist_rows)); };
+
+  // ---- staging helpers
+  // keys of rows c0 + 16I .. +15 in fragment order (lane (r, q): row r, d = 32j + 8q .. +7)
+  auto load_kfrag = [&](Frag<T> (&kf)[KS], int c0) {
+    const int x = c0 + 16 * I + r16;
+    const bool ok = row_ok(x);
+    const T *src = krow(ok ? x : 0);
+#pragma unroll
+    for (int j = 0; j < KS; ++j) kf[j] = ok ? load8(src + 32 * j + 8 * g4) : frag_zero<T>();
+  };
+  auto store_kfrag = [&](const Frag<T> (&kf)[KS]) {
+#pragma unroll
+    for (int j = 0; j < KS; ++j) *reinterpret_cast<bf16x8 *>(sK + (16 * I + r16) * LDW + 32 * j + 8 * g4) = kf[j].v;
+  };
+  // values: thread t (of 256) takes token pairs tp = t % 32 and 8-column groups t / 32, t / 32 + 8;
+  // each half-wave writes one column group, so the transposed 4-byte stores spread over the banks
+  auto load_vpairs = [&](Frag<T> (&vf)[2][2], int c0, int t) {
+    const int tp = t & 31;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int x = c0 + 2 * tp + h;
+      const bool ok = row_ok(x);
+      const T *src = vrow(ok ? x : 0);
+#pragma unroll
+      for (int gsel = 0; gsel < 2; ++gsel) {
+        const int gq = (t >> 5) + 8 * gsel;
+        vf[gsel][h] = ok ? load8(src + 8 * gq) : frag_zero<T>();
+      }
+    }
+  };
+  auto store_vpairs = [&](const Frag<T> (&vf)[2][2], int t) {
+    const int tp = t & 31;
+    const int pos = (2 * tp & 32) | ipos(2 * tp & 31);  // token pairs stay adjacent
+#pragma unroll
+    for (int gsel = 0; gsel < 2; ++gsel) {
+      const int gq = (t >> 5) + 8 * gsel;
+      store_pairT<T, LDV>(vf[gsel][0], vf[gsel][1], sVt + (8 * gq) * LDV + pos);
+    }
+  };
+  // log gamma^T [f][s] (natural token order): token pairs tp = t % 32, 8-feature groups t / 32, + 8
+  auto load_lgpairs = [&](Frag<T> (&lf)[2][2], int c0, int t) {
+    const int tp = t & 31;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int x = c0 + 2 * tp + h;
+      const bool ok = x < L;
+#pragma unroll
+      for (int gsel = 0; gsel < 2; ++gsel) {
+        const int fq = (t >> 5) + 8 * gsel;
+        lf[gsel][h] = ok ? load8(LGh + (size_t)x * D + 8 * fq) : frag_zero<T>();
+      }
+    }
+  };
+  auto store_lgpairs = [&](const Frag<T> (&lf)[2][2], int t) {
+    const int tp = t & 31;
+#pragma unroll
+    for (int gsel = 0; gsel < 2; ++gsel) {
+      const int fq = (t >> 5) + 8 * gsel;
+      store_pairT<T, LDV>(lf[gsel][0], lf[gsel][1], sLgT + (8 * fq) * LDV + 2 * tp);
+    }
+  };
+
+  // ---- prologue: weights, meta tokens, the chunk before the first one
+  {
+    const T *Wk = reinterpret_cast<const T *>(p.wk);
+    load_wT<T, D, LDW, 512>(sW, Wk, tid);
+    const T *Tv = reinterpret_cast<const T *>(p.tv);
+    const T *Tk = reinterpret_cast<const T *>(p.tk);
+    for (int idx = tid; idx < D * 16; idx += 512) {
+      const int dv = idx / 16, m = idx % 16;
+      sTvT[dv * LDM + m] = (m < p.M) ? Tv[((size_t)kvh * p.M + m) * D + dv] : from_f<T>(0.f);
+    }
+    for (int idx = tid; idx < 16 * D; idx += 512) {
+      const int m = idx / D, e = idx % D;
+      sTk[m * LDW + e] = (m < p.M) ? Tk[((size_t)kvh * p.M + m) * D + e] : from_f<T>(0.f);
+    }
+    for (int idx = tid; idx < 4 * FLAG_WORDS; idx += 512) sFlag[idx] = 0u;
+    // previous chunk (history or the end of the previous segment; zeros if none)
+    const int cp0 = (c_begin - 1) * CH;
+    if (key_wave) {
+      Frag<T> kf[KS];
+      load_kfrag(kf, cp0);
+      store_kfrag(kf);
+    } else {
+      Frag<T> vf[2][2];
+      load_vpairs(vf, cp0, tid);
+      store_vpairs(vf, tid);
+    }
+  }
+
+  if (key_wave) {
+    // ======================================================= key waves
+    const int kt = tid - 256;
+    // S rows owned: feature tiles 2I, 2I+1; S[ft][dt][i] = S[16(2I+ft) + 4g4 + i][16dt + r16]
+    f32x4 S[FTW][NDT];
+#pragma unroll
+    for (int ft = 0; ft < FTW; ++ft)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) S[ft][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (p.state_in) {
+      const float *Si = p.state_in + ((size_t)b * p.Hkv + kvh) * D * D;
+#pragma unroll
+      for (int ft = 0; ft < FTW; ++ft)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S[ft][dt][i] = Si[(size_t)(16 * (2 * I + ft) + 4 * g4 + i) * D + 16 * dt + r16];
+    }
+    // segment start: S = e^{D_j} S + E_j over the earlier segments (end states and log-gate
+    // sums of fwd_full_state_kernel, E in this kernel's fragment order)
+    const int nstate = (p.nseg - 1) * p.sss;  // state-pass pieces per head (p.sss per segment)
+    for (int j = 0; j < seg * p.sss; ++j) {
+      const size_t sj = (size_t)bh * nstate + j;
+      const float *Dj = p.ws_decay + sj * D;
+      const float *E = p.ws_state + sj * (size_t)(D * D);
+#pragma unroll
+      for (int ft = 0; ft < FTW; ++ft) {
+        float e[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e[i] = __expf(Dj[16 * (2 * I + ft) + 4 * g4 + i]);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const f32x4 x = *reinterpret_cast<const f32x4 *>(E + ((size_t)((2 * I + ft) * NDT + dt) * 64 + lane) * 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S[ft][dt][i] = e[i] * S[ft][dt][i] + x[i];
+        }
+      }
+    }
+    const Frag<T> tri_c0 = tri64_frag<T>(r16, g4, I, 0), tri_c1 = tri64_frag<T>(r16, g4, I, 1);
+    Frag<T> kf[KS], kf_next[KS];
+    Frag<T> lf[2][2];
+    load_kfrag(kf, c_begin * CH);
+    load_lgpairs(lf, c_begin * CH, kt);
+    // S^T copy of the start state
+    auto publish = [&]() {
+#pragma unroll
+      for (int ft = 0; ft < FTW; ++ft) {
+        const int fpos = 32 * I + 8 * g4 + 4 * ft;  // interleaved position of feature 16(2I+ft) + 4g4
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          store4<T>(sSb + (16 * dt + r16) * LDW + fpos, S[ft][dt][0], S[ft][dt][1], S[ft][dt][2], S[ft][dt][3]);
+      }
+    };
+    publish();
+    __syncthreads();  // P: prologue LDS writes complete
+
+    for (int c = c_begin; c < c_end; ++c) {
+      const int c0 = c * CH;
+      // ---- P0: phi_k of this chunk's rows (keys from registers); the query waves read the
+      //      previous chunk's keys and values from LDS meanwhile
+      float ko[NFT][4];
+      {
+        f32x4 z[NFT];
+        feature_logits<T, D, LDW>(sW, kf, r16, g4, z);
+        softmax_rows<NFT>(z, ko);
+      }
+      __syncthreads();  // B0: the previous chunk's LDS is dead
+      // ---- P1: stage this chunk's keys and log gamma^T; publish S_c; next chunk in flight
+      store_kfrag(kf);
+      store_lgpairs(lf, kt);
+      if (c > c_begin) publish();
+      if (c + 1 < c_end) {
+        load_kfrag(kf_next, c0 + CH);
+        load_lgpairs(lf, c0 + CH, kt);
+      }
+      __syncthreads();  // B1
+      // ---- P2: prefix sums from the chunk start for this sub-chunk's rows
+      float pc[NFT][4];
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft) {
+        f32x4 cc = mma(load8(sLgT + (16 * ft + r16) * LDV + 8 * g4), tri_c0, f32x4{0.f, 0.f, 0.f, 0.f});
+        cc = mma(load8(sLgT + (16 * ft + r16) * LDV + 32 + 8 * g4), tri_c1, cc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pc[ft][i] = cc[i];
+      }
+      if (r16 == 15 || r16 == 7) {
+        float *dst = (r16 == 15 ? sTot : sP7) + I * D + 4 * g4;
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft)
+          *reinterpret_cast<f32x4 *>(dst + 16 * ft) = f32x4{pc[ft][0], pc[ft][1], pc[ft][2], pc[ft][3]};
+      }
+      __syncthreads();  // B2: sub-chunk prefix ends visible; log gamma^T dead
+      const bool mild = chunk_is_mild_c<D>(sTot, lane);
+      // ---- P3: decayed keys -> LDS (interleaved features) and the factor tables.
+      //      Mild: keys carry e^{-p_s}, table e^{B_c}.  Otherwise keys carry e^{C_I - p_s}
+      //      (decay to the sub-chunk end) and the sub-chunk tables.
+      if (mild) {
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ko[ft][i] *= exp2_fast(-pc[ft][i] * LOG2E);
+        if (kt < D) sETot[kt] = __expf(sTot[3 * D + kt]);
+      } else {
+        constexpr int PER = 2;  // sub-chunks per thread (256 threads, 128 features)
+        const int f = kt % D, j0 = (kt / D) * PER;
+#pragma unroll
+        for (int jj = 0; jj < PER; ++jj) {
+          const int J = j0 + jj;
+          const float cprev = J > 0 ? sTot[(J - 1) * D + f] : 0.f;
+          const float tt = sTot[J * D + f] - cprev;
+          const float p7 = sP7[J * D + f] - cprev;
+          sETot[J * D + f] = __expf(tt);
+          sENP7[J * D + f] = __expf(-p7);
+          sENR8[J * D + f] = __expf(p7 - tt);
+        }
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft) {
+          const f32x4 t = *reinterpret_cast<const f32x4 *>(sTot + I * D + 16 * ft + 4 * g4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ko[ft][i] *= __expf(t[i] - pc[ft][i]);
+        }
+      }
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft) {
+        const int fpos = 32 * (ft >> 1) + 8 * g4 + 4 * (ft & 1);
+        store4<T>(sKt + (16 * I + r16) * LDW + fpos, ko[ft][0], ko[ft][1], ko[ft][2], ko[ft][3]);
+      }
+      __syncthreads();  // B3: decayed keys and tables visible
+      // ---- P4: S = diag(e^{B_c}) S + sum_s k~_s e^{...} v_s^T.  K = 32 steps run over the
+      //      interleaved token order of v^T; slot j of lane group g4 is token 32ks + islot(g4, j)
+#pragma unroll
+      for (int ft = 0; ft < FTW; ++ft) {
+        const int fr = 16 * (2 * I + ft);
+        const int fcol = 32 * I + ipos(16 * ft + r16);  // interleaved position of feature fr + r16
+        float e[4];
+        float fac[2][2];  // [ks][half]: factor of the keys of sub-chunk 2ks + half
+        if (mild) {
+          const f32x4 t = *reinterpret_cast<const f32x4 *>(sETot + fr + 4 * g4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) e[i] = t[i];
+          const float f0 = sETot[fr + r16];
+          fac[0][0] = fac[0][1] = fac[1][0] = fac[1][1] = f0;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) e[i] = 1.f;
+#pragma unroll
+          for (int J = 0; J < 4; ++J) {
+            const f32x4 t = *reinterpret_cast<const f32x4 *>(sETot + J * D + fr + 4 * g4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) e[i] *= t[i];
+          }
+          float et[4];
+#pragma unroll
+          for (int J = 0; J < 4; ++J) et[J] = sETot[J * D + fr + r16];
+#pragma unroll
+          for (int J = 0; J < 4; ++J) {
+            float f = 1.f;
+#pragma unroll
+            for (int J2 = 1; J2 < 4; ++J2)
+              if (J2 > J) f *= et[J2];
+            fac[J >> 1][J & 1] = f;
+          }
+        }
+        Frag<T> ka[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          float x[8];
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj)
+            x[jj] = to_f(sKt[(32 * ks + islot(g4, jj)) * LDW + fcol]) * fac[ks][jj >> 2];
+          ka[ks] = frag_from<T>(x);
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S[ft][dt][i] *= e[i];
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+            S[ft][dt] = mma(ka[ks], load8(sVt + (16 * dt + r16) * LDV + 32 * ks + 8 * g4), S[ft][dt]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < KS; ++j) kf[j] = kf_next[j];
+    }
+    if (p.state_out && seg == p.nseg - 1) {
+      float *So = p.state_out + ((size_t)b * p.Hkv + kvh) * D * D;
+#pragma unroll
+      for (int ft = 0; ft < FTW; ++ft)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) So[(size_t)(16 * (2 * I + ft) + 4 * g4 + i) * D + 16 * dt + r16] = S[ft][dt][i];
+    }
+  } else {
+    // ======================================================= query waves
+    const float mix = p.mix, scale = p.scale;
+    const float log2_mix = __log2f(mix);
+    const float sl2 = scale * LOG2E;  // window logits in base 2
+    const Frag<T> tri_c0 = tri64_frag<T>(r16, g4, I, 0), tri_c1 = tri64_frag<T>(r16, g4, I, 1);
+    Frag<T> qf[KS], qf_next[KS];
+    Frag<T> vf[2][2];
+    auto load_q = [&](Frag<T> (&f)[KS], int c0) {
+      const int t = c0 + 16 * I + r16;
+#pragma unroll
+      for (int j = 0; j < KS; ++j) f[j] = (t < L) ? load8(Qh + (size_t)t * D + 32 * j + 8 * g4) : frag_zero<T>();
+    };
+    load_q(qf, c_begin * CH);
+    load_vpairs(vf, c_begin * CH, tid);
+    bool unsafe_seen = false;
+    __syncthreads();  // P
+
+    for (int c = c_begin; c < c_end; ++c) {
+      const int c0 = c * CH;
+      const int pos = c0 + 16 * I + r16;  // query row of this lane's column
+      const bool valid = pos < L;
+      // lowest key index the window of this row may use
+      const int kmin = max(pos - p.W + 1, c == 0 ? -hist_avail : INT32_MIN / 2);
+
+      // ---- P0: window group X (meta tokens and the previous chunk's keys I..3, still in
+      //      LDS) in base-2 logits; unnormalised probabilities times values into acc
+      f32x4 acc[NDT];
+      float m_x = -1.0e20f, l_run = 0.f;
+      {
+        f32x4 lt[5];  // 0: meta; 1 + u: previous-chunk tile u (u >= I)
+        {
+          f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < KS; ++j) a = mma(load8(sTk + r16 * LDW + 32 * j + 8 * g4), qf[j], a);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lt[0][i] = (4 * g4 + i < p.M) ? a[i] * sl2 : NEG_BIG;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          lt[1 + u] = f32x4{NEG_BIG, NEG_BIG, NEG_BIG, NEG_BIG};
+          if (u >= I) {
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < KS; ++j) a = mma(load8(sK + (16 * u + r16) * LDW + 32 * j + 8 * g4), qf[j], a);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int kj = c0 - CH + 16 * u + 4 * g4 + i;
+              lt[1 + u][i] = (kj >= kmin) ? a[i] * sl2 : NEG_BIG;
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 5; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) m_x = fmaxf(m_x, lt[u][i]);
+        m_x = wave_max_cols(m_x);
+        Frag<T> pm, pp[2];
+        {
+          float x[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[i] = exp2_fast(lt[0][i] - m_x);
+            l_run += x[i];
+            x[4 + i] = 0.f;
+          }
+          pm = frag_from<T>(x);
+        }
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          float x[8];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float pv = exp2_fast(lt[1 + 2 * pr + h][i] - m_x);  // masked: 0
+              x[4 * h + i] = pv;
+              l_run += pv;
+            }
+          pp[pr] = frag_from<T>(x);
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int dvl = 16 * dt + r16;
+          const T *tv = sTvT + dvl * LDM + 4 * g4;
+          f32x4 a = mma(load4x2(tv, tv), pm, f32x4{0.f, 0.f, 0.f, 0.f});  // slots 4..7 meet P = 0
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr)
+            if (2 * pr + 1 >= I) a = mma(load8(sVt + dvl * LDV + 32 * pr + 8 * g4), pp[pr], a);
+          acc[dt] = a;
+        }
+      }
+      __syncthreads();  // B0
+      // ---- P1: stage this chunk's values; next chunk in flight
+      store_vpairs(vf, tid);
+      __syncthreads();  // B1
+      // ---- P2: prefix sums from the chunk start, phi_q, window group Y (this chunk's keys 0..I)
+      float pfx[NFT][4];
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft) {
+        f32x4 cc = mma(load8(sLgT + (16 * ft + r16) * LDV + 8 * g4), tri_c0, f32x4{0.f, 0.f, 0.f, 0.f});
+        cc = mma(load8(sLgT + (16 * ft + r16) * LDV + 32 + 8 * g4), tri_c1, cc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pfx[ft][i] = cc[i];
+      }
+      float qo[NFT][4];
+      {
+        f32x4 z[NFT];
+        feature_logits<T, D, LDW>(sW, qf, r16, g4, z);
+        softmax_rows<NFT>(z, qo);
+      }
+      {
+        f32x4 lt[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          lt[u] = f32x4{NEG_BIG, NEG_BIG, NEG_BIG, NEG_BIG};
+          if (u <= I) {
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < KS; ++j) a = mma(load8(sK + (16 * u + r16) * LDW + 32 * j + 8 * g4), qf[j], a);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int kj = c0 + 16 * u + 4 * g4 + i;
+              lt[u][i] = (kj <= pos && kj >= kmin) ? a[i] * sl2 : NEG_BIG;
+            }
+          }
+        }
+        float m_y = m_x;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) m_y = fmaxf(m_y, lt[u][i]);
+        m_y = wave_max_cols(m_y);  // >= m_x; the diagonal key is always in the window
+        const float alpha = exp2_fast(m_x - m_y);
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[dt][i] *= alpha;
+        Frag<T> pp[2];
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          float x[8];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float pv = exp2_fast(lt[2 * pr + h][i] - m_y);
+              x[4 * h + i] = pv;
+              l_run += pv;
+            }
+          pp[pr] = frag_from<T>(x);
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int dvl = 16 * dt + r16;
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr)
+            if (2 * pr <= I) acc[dt] = mma(load8(sVt + dvl * LDV + 32 * pr + 8 * g4), pp[pr], acc[dt]);
+        }
+      }
+      __syncthreads();  // B2: sub-chunk prefix ends visible
+      const bool mild = chunk_is_mild_c<D>(sTot, lane);
+      bool safe = true;  // general case: mid-row reference usable on the diagonal block
+      if (!mild) {
+        // sub-chunk start reference: subtract the prefix up to the end of sub-chunk I - 1
+        if (I > 0) {
+#pragma unroll
+          for (int ft = 0; ft < NFT; ++ft) {
+            const f32x4 t = *reinterpret_cast<const f32x4 *>(sTot + (I - 1) * D + 16 * ft + 4 * g4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pfx[ft][i] -= t[i];
+          }
+        }
+        float span = 0.f;
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) span = fmaxf(span, -pfx[ft][i]);
+        safe = wave_max_all(span) <= SPAN_MAX;
+      }
+      // sub-chunks whose diagonal block needs the exact products (added after the chunk loop)
+      const bool unsafe = !safe;
+      unsafe_seen |= unsafe;
+      if (unsafe && lane == 0) sFlag[I * FLAG_WORDS + ((c - c_begin) >> 5)] |= 1u << ((c - c_begin) & 31);
+      // next chunk's values and queries in flight from here (later than the key waves' loads:
+      // fewer registers live through the feature map and the window)
+      if (c + 1 < c_end) {
+        load_vpairs(vf, c0 + CH, tid);
+        load_q(qf_next, c0 + CH);
+      }
+      // ---- P3: decayed queries with the merge weight: qo *= mix e^{pfx}; window normalised
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qo[ft][i] *= exp2_fast(__builtin_fmaf(pfx[ft][i], LOG2E, log2_mix));
+      {
+        const float ws = (1.f - mix) / wave_sum_cols(l_run);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[dt][i] *= ws;
+      }
+      __syncthreads();  // B3: decayed keys and tables visible
+      // ---- P4: intra- and inter-chunk products onto the window output, store
+      auto finish = [&](auto mild_tag) {
+        constexpr bool MILD = decltype(mild_tag)::value;
+        // query operand in bf16 (f-interleaved K = 32 slices); the general case rescales it
+        // per feature from the tables
+        Frag<T> qcf[KS];
+#pragma unroll
+        for (int js = 0; js < KS; ++js) {
+          float x[8];
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) x[jj] = qo[2 * js + (jj >> 2)][jj & 3];
+          qcf[js] = frag_from<T>(x);
+        }
+        if constexpr (MILD) {
+          // intra-chunk scores A^T[s][t] of key sub-chunk J (masked to s <= t on the diagonal)
+          auto score = [&](int J) -> f32x4 {
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int js = 0; js < KS; ++js) a = mma(load8(sKt + (16 * J + r16) * LDW + 32 * js + 8 * g4), qcf[js], a);
+            if (J == I) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) a[i] = (4 * g4 + i <= r16) ? a[i] : 0.f;
+            }
+            return a;
+          };
+          // Y^T += V^T A^T over key sub-chunk pairs (2m, 2m+1), interleaved in v^T
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            if (2 * m <= I) {
+              const f32x4 a0 = score(2 * m);
+              const f32x4 a1 = (2 * m + 1 <= I) ? score(2 * m + 1) : f32x4{0.f, 0.f, 0.f, 0.f};
+              float x[8];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                x[i] = a0[i];
+                x[4 + i] = a1[i];
+              }
+              const Frag<T> bf = frag_from<T>(x);
+#pragma unroll
+              for (int dt = 0; dt < NDT; ++dt)
+                acc[dt] = mma(load8(sVt + (16 * dt + r16) * LDV + 32 * m + 8 * g4), bf, acc[dt]);
+            }
+          }
+          // Y^T += S^T q~^T (state at the chunk start; interleaved features)
+#pragma unroll
+          for (int js = 0; js < KS; ++js)
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+              acc[dt] = mma(load8(sSb + (16 * dt + r16) * LDW + 32 * js + 8 * g4), qcf[js], acc[dt]);
+        } else {
+          // Sub-chunk references (rare: a chunk whose log decay exceeds FAST_SPAN).  One key
+          // sub-chunk at a time, register-light: the query operand of K-step js times the tables
+          // e^{tot_J2} of the sub-chunks J2 in [lo, hi)
+          auto qscaled = [&](int js, int lo, int hi) {
+            float x[8];
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) x[jj] = to_f(qcf[js].v[jj]);
+#pragma unroll 1
+            for (int J2 = lo; J2 < hi; ++J2) {
+              float t8[8];
+              tab8(sETot + J2 * D, js, g4, t8);
+#pragma unroll
+              for (int jj = 0; jj < 8; ++jj) x[jj] *= t8[jj];
+            }
+            return frag_from<T>(x);
+          };
+#pragma unroll 1
+          for (int J = 0; J <= I; ++J) {
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+            if (J < I) {
+#pragma unroll
+              for (int js = 0; js < KS; ++js)
+                a = mma(load8(sKt + (16 * J + r16) * LDW + 32 * js + 8 * g4), qscaled(js, J + 1, I), a);
+            } else if (safe) {
+              // mid-row reference: (k~ e^{p7 - tot}) . (q e^{-p7})
+#pragma unroll
+              for (int js = 0; js < KS; ++js) {
+                float t8[8], kv[8], x[8];
+                const Frag<T> kk = load8(sKt + (16 * I + r16) * LDW + 32 * js + 8 * g4);
+                tab8(sENR8 + I * D, js, g4, t8);
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) kv[jj] = to_f(kk.v[jj]) * t8[jj];
+                tab8(sENP7 + I * D, js, g4, t8);
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) x[jj] = to_f(qcf[js].v[jj]) * t8[jj];
+                a = mma(frag_from<T>(kv), frag_from<T>(x), a);
+              }
+            } else {
+              a = f32x4{0.f, 0.f, 0.f, 0.f};  // exact block added after the chunk loop
+            }
+            if (J == I) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) a[i] = (4 * g4 + i <= r16) ? a[i] : 0.f;
+            }
+            // tile J sits in slots 4 (J & 1) .. +3 of the interleaved pair (J & ~1, J | 1)
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              x[i] = (J & 1) ? 0.f : a[i];
+              x[4 + i] = (J & 1) ? a[i] : 0.f;
+            }
+            const Frag<T> bf = frag_from<T>(x);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+              acc[dt] = mma(load8(sVt + (16 * dt + r16) * LDV + 32 * (J >> 1) + 8 * g4), bf, acc[dt]);
+          }
+#pragma unroll
+          for (int js = 0; js < KS; ++js) {
+            const Frag<T> bf = qscaled(js, 0, I);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+              acc[dt] = mma(load8(sSb + (16 * dt + r16) * LDW + 32 * js + 8 * g4), bf, acc[dt]);
+          }
+        }
+        if (valid) {
+          T *O = Oh + (size_t)pos * D;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) store4<T>(O + 16 * dt + 4 * g4, acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+        }
+      };
+      if (mild)
+        finish(std::true_type{});
+      else
+        finish(std::false_type{});
+#pragma unroll
+      for (int j = 0; j < KS; ++j) qf[j] = qf_next[j];
+    }
+    // Exact diagonal blocks of this wave's flagged sub-chunks, added to the rows it stored
+    // (few registers are live after the loop)
+    if (unsafe_seen) {
+      for (int c = c_begin; c < c_end; ++c) {
+        if (!((sFlag[I * FLAG_WORDS + ((c - c_begin) >> 5)] >> ((c - c_begin) & 31)) & 1u)) continue;
+        exact_diag_fixup(sW, Kh, Vh, LGh, Qh, Oh, c * CH, I, L, mix);
+      }
+    }
+  }
+}
+
+// State pass of a segmented sequence: the chunks before the last segment in pieces (p.sss per
+// segment); for each piece the end state E_j of its tokens alone (from S = 0) and the sum of
+// its log gates D_j, so that the whole-head kernel can start a segment from
+// sum_{i<j} diag(e^{D_{i+1} + ... + D_{j-1}}) E_i over the pieces before it (the recurrence
+// is associative in (D, E)).  Four waves, each the key side of one sub-chunk,
+// with the arithmetic of the key waves above; 80 KB of LDS, so two workgroups share a CU.
+namespace full {
+constexpr int ST_OFF_W = 0;
+constexpr int ST_OFF_VT = ST_OFF_W + D * LDW * 2;
+constexpr int ST_OFF_KT = ST_OFF_VT + D * LDV * 2;
+constexpr int ST_OFF_TAB = ST_OFF_KT + SZ_KT;
+constexpr int ST_LDS_BYTES = ST_OFF_TAB + 2 * 4 * D * 4;
+static_assert(2 * ST_LDS_BYTES <= LDS_LIMIT, "state pass: two workgroups per CU");
+}  // namespace full
+
+__global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
+  using namespace full;
+  using T = bf16;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  T *sW = reinterpret_cast<T *>(smem + ST_OFF_W);
+  T *sVt = reinterpret_cast<T *>(smem + ST_OFF_VT);
+  T *sKt = reinterpret_cast<T *>(smem + ST_OFF_KT);
+  T *sLgT = sKt;
+  float *sTot = reinterpret_cast<float *>(smem + ST_OFF_TAB);
+  float *sP7 = sTot + 4 * D;
+
+  const int tid = threadIdx.x, lane = tid & 63, I = tid >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int nsp = (p.nseg - 1) * p.sss;  // pieces of p.cps / p.sss chunks before the last segment
+  const int grp = blockIdx.x;
+  if (grp >= p.B * p.Hkv * nsp) return;
+  const int piece = grp % nsp, bh = grp / nsp;
+  const int L = p.L;
+  const int cpp = p.cps / p.sss;
+  const int c_begin = piece * cpp, c_end = c_begin + cpp;  // never in the last segment: full chunks
+  const size_t kv_off = (size_t)bh * (size_t)L * D;
+  const T *Kh = reinterpret_cast<const T *>(p.k) + kv_off;
+  const T *Vh = reinterpret_cast<const T *>(p.v) + kv_off;
+  const T *LGh = reinterpret_cast<const T *>(p.lg) + kv_off;
+
+  load_wT<T, D, LDW, 256>(sW, reinterpret_cast<const T *>(p.wk), tid);
+  auto load_k = [&](Frag<T> (&kf)[KS], int c0) {
+    const T *src = Kh + (size_t)(c0 + 16 * I + r16) * D;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) kf[j] = load8(src + 32 * j + 8 * g4);
+  };
+  // values and log gamma, token pairs tp = tid % 32, 8-column groups tid / 32 + 8 gsel (4 per thread)
+  auto load_pairs = [&](Frag<T> (&f)[2][2], const T *base, int c0) {
+    const int tp = tid & 31;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int gsel = 0; gsel < 2; ++gsel) f[gsel][h] = load8(base + (size_t)(c0 + 2 * tp + h) * D + 8 * ((tid >> 5) + 8 * gsel));
+  };
+  Frag<T> kf[KS], vf[2][2], lf[2][2];
+  load_k(kf, c_begin * CH);
+  load_pairs(vf, Vh, c_begin * CH);
+  load_pairs(lf, LGh, c_begin * CH);
+  f32x4 S[FTW][NDT];
+#pragma unroll
+  for (int ft = 0; ft < FTW; ++ft)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) S[ft][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float dsum = 0.f;  // thread tid < D: sum of log gamma of feature tid
+  const Frag<T> tri_c0 = tri64_frag<T>(r16, g4, I, 0), tri_c1 = tri64_frag<T>(r16, g4, I, 1);
+  __syncthreads();
+
+  for (int c = c_begin; c < c_end; ++c) {
+    float ko[NFT][4];
+    {
+      f32x4 z[NFT];
+      feature_logits<T, D, LDW>(sW, kf, r16, g4, z);
+      softmax_rows<NFT>(z, ko);
+    }
+    {
+      const int tp = tid & 31;
+      const int vpos = (2 * tp & 32) | ipos(2 * tp & 31);
+#pragma unroll
+      for (int gsel = 0; gsel < 2; ++gsel) {
+        const int gq = (tid >> 5) + 8 * gsel;
+        store_pairT<T, LDV>(vf[gsel][0], vf[gsel][1], sVt + (8 * gq) * LDV + vpos);
+        store_pairT<T, LDV>(lf[gsel][0], lf[gsel][1], sLgT + (8 * gq) * LDV + 2 * tp);
+      }
+    }
+    if (c + 1 < c_end) {
+      load_k(kf, (c + 1) * CH);
+      load_pairs(vf, Vh, (c + 1) * CH);
+      load_pairs(lf, LGh, (c + 1) * CH);
+    }
+    __syncthreads();
+    float pc[NFT][4];
+#pragma unroll
+    for (int ft = 0; ft < NFT; ++ft) {
+      f32x4 cc = mma(load8(sLgT + (16 * ft + r16) * LDV + 8 * g4), tri_c0, f32x4{0.f, 0.f, 0.f, 0.f});
+      cc = mma(load8(sLgT + (16 * ft + r16) * LDV + 32 + 8 * g4), tri_c1, cc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pc[ft][i] = cc[i];
+    }
+    if (r16 == 15 || r16 == 7) {
+      float *dst = (r16 == 15 ? sTot : sP7) + I * D + 4 * g4;
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft)
+        *reinterpret_cast<f32x4 *>(dst + 16 * ft) = f32x4{pc[ft][0], pc[ft][1], pc[ft][2], pc[ft][3]};
+    }
+    __syncthreads();
+    if (tid < D) dsum += sTot[3 * D + tid];
+    const bool mild = chunk_is_mild_c<D>(sTot, lane);
+    if (mild) {
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ko[ft][i] *= exp2_fast(-pc[ft][i] * LOG2E);
+    } else {
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft) {
+        const f32x4 t = *reinterpret_cast<const f32x4 *>(sTot + I * D + 16 * ft + 4 * g4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ko[ft][i] *= __expf(t[i] - pc[ft][i]);
+      }
+    }
+#pragma unroll
+    for (int ft = 0; ft < NFT; ++ft) {
+      const int fpos = 32 * (ft >> 1) + 8 * g4 + 4 * (ft & 1);
+      store4<T>(sKt + (16 * I + r16) * LDW + fpos, ko[ft][0], ko[ft][1], ko[ft][2], ko[ft][3]);
+    }
+    __syncthreads();
+    // S = diag(e^{C_3}) S + sum_s k~_s e^{...} v_s^T (factors from the prefix table)
+#pragma unroll
+    for (int ft = 0; ft < FTW; ++ft) {
+      const int fr = 16 * (2 * I + ft);
+      const int fcol = 32 * I + ipos(16 * ft + r16);
+      const f32x4 c3 = *reinterpret_cast<const f32x4 *>(sTot + 3 * D + fr + 4 * g4);
+      float e[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e[i] = __expf(c3[i]);
+      float fac[2][2];
+      const float c3r = sTot[3 * D + fr + r16];
+      if (mild) {
+        fac[0][0] = fac[0][1] = fac[1][0] = fac[1][1] = __expf(c3r);
+      } else {
+#pragma unroll
+        for (int J = 0; J < 4; ++J) fac[J >> 1][J & 1] = __expf(c3r - sTot[J * D + fr + r16]);
+      }
+      Frag<T> ka[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        float x[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) x[jj] = to_f(sKt[(32 * ks + islot(g4, jj)) * LDW + fcol]) * fac[ks][jj >> 2];
+        ka[ks] = frag_from<T>(x);
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[ft][dt][i] *= e[i];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          S[ft][dt] = mma(ka[ks], load8(sVt + (16 * dt + r16) * LDV + 32 * ks + 8 * g4), S[ft][dt]);
+      }
+    }
+    __syncthreads();
+  }
+  float *E = p.ws_state + (size_t)grp * (D * D);
+#pragma unroll
+  for (int ft = 0; ft < FTW; ++ft)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+      *reinterpret_cast<f32x4 *>(E + ((size_t)((2 * I + ft) * NDT + dt) * 64 + lane) * 4) = S[ft][dt];
+  if (tid < D) p.ws_decay[(size_t)grp * D + tid] = dsum;
+}
+
+hipError_t launch_fwd_full(const FwdParams &p, hipStream_t stream) {
+  hipError_t e;
+  if (p.nseg > 1) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(fwd_full_state_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, full::ST_LDS_BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fwd_full_state_kernel, dim3(p.B * p.Hkv * (p.nseg - 1) * p.sss), dim3(256), full::ST_LDS_BYTES,
+                       stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  e = hipFuncSetAttribute(reinterpret_cast<const void *>(fwd_full_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, full::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fwd_full_kernel, dim3(p.ngroups), dim3(512), full::LDS_BYTES, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace lz

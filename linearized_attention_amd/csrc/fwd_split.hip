@@ -32,14 +32,14 @@ namespace lz {
 // FASTWIN: W <= 65 with two chunks in each ring (the window is exactly six 16-key
 // tiles); MULTI_G: more than one query head per key/value head.  Both are known
 // on the host; fixing them at compile time keeps each variant within 256 VGPRs.
-template <typename T, int D, int DV, bool FASTWIN, bool MULTI_G>
+template <typename T, int D, int DV, bool FASTWIN, bool MULTI_G, bool WIDE>
 __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
-  using Gm = FwdGeom<T, D, DV>;
+  using Gm = FwdGeom<T, D, DV, WIDE>;
   constexpr int NFT = D / 16;   // 16-row tiles of the feature dimension
   constexpr int KS = D / 32;    // K = 32 steps over d (or over features)
   constexpr int NDT = DV / 16;  // 16-column tiles of this block's value columns
   constexpr int FTW = NFT / 4;  // feature tiles of S owned by each key wave
-  constexpr int LDW = Gm::LDW, LDC = Gm::LDC, LDM = Gm::LDM;
+  constexpr int LDW = Gm::LDW, LDB = Gm::LDB, LDC = Gm::LDC, LDG = Gm::LDG, LDM = Gm::LDM;
   static_assert(NFT % 4 == 0, "d must be a multiple of 64");
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
     for (int ft = 0; ft < FTW; ++ft)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
-        store4<T>(sSbf + (16 * dt + r16) * LDW + 16 * (I * FTW + ft) + 4 * g4, S[ft][dt][0], S[ft][dt][1],
+        store4<T>(sSbf + (16 * dt + r16) * LDB + 16 * (I * FTW + ft) + 4 * g4, S[ft][dt][0], S[ft][dt][1],
                   S[ft][dt][2], S[ft][dt][3]);
 
     for (int c = c_begin; c < c_end; ++c) {
@@ -185,17 +185,17 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
       const int kcur = (c % KR) * (CH * LDW);
       const int cur = (c % NR) * (DV * LDC);
       store_keys<T, D, DV, LDW>(pf, sKr + kcur, kt);
-      store_lgT<T, D, DV, LDC>(pf, sLgT, kt);
+      store_lgT<T, D, DV, LDG>(pf, sLgT, kt);
       __syncthreads();  // B0
 
       // ---- A: gate prefix sums inside the sub-chunk, phi_k (decayed in B)
       float pfx[NFT][4], pc[NFT][4];  // prefix inside the sub-chunk / from the chunk start
 #pragma unroll
       for (int ft = 0; ft < NFT; ++ft) {
-        const Frag<T> a = (g4 < 2) ? load8(sLgT + (16 * ft + r16) * LDC + 16 * I + 8 * g4) : frag_zero<T>();
+        const Frag<T> a = (g4 < 2) ? load8(sLgT + (16 * ft + r16) * LDG + 16 * I + 8 * g4) : frag_zero<T>();
         const f32x4 pp = mma(a, tri_pre, f32x4{0.f, 0.f, 0.f, 0.f});
-        f32x4 cc = mma(load8(sLgT + (16 * ft + r16) * LDC + 8 * g4), tri_c0, f32x4{0.f, 0.f, 0.f, 0.f});
-        cc = mma(load8(sLgT + (16 * ft + r16) * LDC + 32 + 8 * g4), tri_c1, cc);
+        f32x4 cc = mma(load8(sLgT + (16 * ft + r16) * LDG + 8 * g4), tri_c0, f32x4{0.f, 0.f, 0.f, 0.f});
+        cc = mma(load8(sLgT + (16 * ft + r16) * LDG + 32 + 8 * g4), tri_c1, cc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) { pfx[ft][i] = pp[i]; pc[ft][i] = cc[i]; }
       }
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
       }
 #pragma unroll
       for (int ft = 0; ft < NFT; ++ft)
-        store4<T>(sKown + (16 * I + r16) * LDW + 16 * ft + 4 * g4, ko[ft][0], ko[ft][1], ko[ft][2], ko[ft][3]);
+        store4<T>(sKown + (16 * I + r16) * LDB + 16 * ft + 4 * g4, ko[ft][0], ko[ft][1], ko[ft][2], ko[ft][3]);
       __syncthreads();  // B2
 
       // ---- C: state update in registers: S = diag(e^{B_c}) S + sum_s KSt[s] v_s^T, where
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
         for (int ks = 0; ks < 2; ++ks) {
           float x[8];
 #pragma unroll
-          for (int jj = 0; jj < 8; ++jj) x[jj] = to_f(sKown[(32 * ks + 8 * g4 + jj) * LDW + fr + r16]) * fac[ks];
+          for (int jj = 0; jj < 8; ++jj) x[jj] = to_f(sKown[(32 * ks + 8 * g4 + jj) * LDB + fr + r16]) * fac[ks];
           ka[ks] = frag_from<T>(x);
         }
 #pragma unroll
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
       for (int ft = 0; ft < FTW; ++ft)
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
-          store4<T>(sSbf + (16 * dt + r16) * LDW + 16 * (I * FTW + ft) + 4 * g4, S[ft][dt][0], S[ft][dt][1],
+          store4<T>(sSbf + (16 * dt + r16) * LDB + 16 * (I * FTW + ft) + 4 * g4, S[ft][dt][0], S[ft][dt][1],
                     S[ft][dt][2], S[ft][dt][3]);
     }
     if (p.state_out && seg == p.nseg - 1) {  // the state after the last token
@@ -608,8 +608,8 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
       float pfx[NFT][4];
 #pragma unroll
       for (int ft = 0; ft < NFT; ++ft) {
-        f32x4 cc = mma(load8(sLgT + (16 * ft + r16) * LDC + 8 * g4), tri_c0, f32x4{0.f, 0.f, 0.f, 0.f});
-        cc = mma(load8(sLgT + (16 * ft + r16) * LDC + 32 + 8 * g4), tri_c1, cc);
+        f32x4 cc = mma(load8(sLgT + (16 * ft + r16) * LDG + 8 * g4), tri_c0, f32x4{0.f, 0.f, 0.f, 0.f});
+        cc = mma(load8(sLgT + (16 * ft + r16) * LDG + 32 + 8 * g4), tri_c1, cc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) pfx[ft][i] = cc[i];
       }
@@ -678,7 +678,7 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
             for (int js = 0; js < KS; ++js) {
               float t8[8], kv[8];
               tab8(sENR8 + I * D, js, g4, t8);
-              const T *kr = sKown + (16 * I + r16) * LDW + 32 * js + 4 * g4;
+              const T *kr = sKown + (16 * I + r16) * LDB + 32 * js + 4 * g4;
               const Frag<T> kk = load4x2(kr, kr + 16);
 #pragma unroll
               for (int jj = 0; jj < 8; ++jj) kv[jj] = to_f(kk.v[jj]) * t8[jj];
@@ -739,7 +739,7 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
                   }
                   bq = frag_from<T>(x);
                 }
-                const T *kr = sKown + (16 * J + r16) * LDW + 32 * js + 4 * g4;
+                const T *kr = sKown + (16 * J + r16) * LDB + 32 * js + 4 * g4;
                 acc = mma(load4x2(kr, kr + 16), bq, acc);
               }
               at[J] = acc;
@@ -750,7 +750,7 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
             if constexpr (MILD) {
 #pragma unroll
               for (int js = 0; js < KS; ++js) {
-                const T *kr = sKown + (16 * I + r16) * LDW + 32 * js + 4 * g4;
+                const T *kr = sKown + (16 * I + r16) * LDB + 32 * js + 4 * g4;
                 acc = mma(load4x2(kr, kr + 16), qcf[js], acc);
               }
             } else {
@@ -860,7 +860,7 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
             }
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
-              const T *sr = sSbf + (16 * dt + r16) * LDW + 32 * js + 4 * g4;
+              const T *sr = sSbf + (16 * dt + r16) * LDB + 32 * js + 4 * g4;
               yw[dt] = mma(load4x2(sr, sr + 16), bf, yw[dt]);
             }
           }
@@ -882,10 +882,10 @@ __global__ __launch_bounds__(512, 1) void fwd_split_kernel(FwdParams p) {
   }
 }
 
-template <typename T, int D, int DV, bool FASTWIN, bool MULTI_G>
+template <typename T, int D, int DV, bool FASTWIN, bool MULTI_G, bool WIDE>
 static hipError_t launch_split_one(const FwdParams &p, hipStream_t stream) {
   const int grid = ((p.ngroups + 7) / 8) * 8 * p.ndvb;
-  auto kern = fwd_split_kernel<T, D, DV, FASTWIN, MULTI_G>;
+  auto kern = fwd_split_kernel<T, D, DV, FASTWIN, MULTI_G, WIDE>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, p.lds.total);
   if (e != hipSuccess) return e;
@@ -893,16 +893,19 @@ static hipError_t launch_split_one(const FwdParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename T, int D, int DV>
+template <typename T, int D, int DV, bool WIDE>
 hipError_t launch_fwd_split(const FwdParams &p, hipStream_t stream) {
   if (p.G != 1) return hipErrorInvalidValue;  // grouped query heads: the 4-wave kernel
   const bool fastwin = (p.W <= CH + 1) && p.kring >= 2 && p.nring >= 2;
-  return fastwin ? launch_split_one<T, D, DV, true, false>(p, stream)
-                 : launch_split_one<T, D, DV, false, false>(p, stream);
+  return fastwin ? launch_split_one<T, D, DV, true, false, WIDE>(p, stream)
+                 : launch_split_one<T, D, DV, false, false, WIDE>(p, stream);
 }
 
-template hipError_t launch_fwd_split<bf16, 64, 64>(const FwdParams &, hipStream_t);
-template hipError_t launch_fwd_split<bf16, 128, 64>(const FwdParams &, hipStream_t);
-template hipError_t launch_fwd_split<float, 64, 64>(const FwdParams &, hipStream_t);
+template hipError_t launch_fwd_split<bf16, 64, 64, true>(const FwdParams &, hipStream_t);
+template hipError_t launch_fwd_split<bf16, 128, 64, true>(const FwdParams &, hipStream_t);
+template hipError_t launch_fwd_split<float, 64, 64, true>(const FwdParams &, hipStream_t);
+template hipError_t launch_fwd_split<bf16, 64, 64, false>(const FwdParams &, hipStream_t);
+template hipError_t launch_fwd_split<bf16, 128, 64, false>(const FwdParams &, hipStream_t);
+template hipError_t launch_fwd_split<float, 64, 64, false>(const FwdParams &, hipStream_t);
 
 }  // namespace lz

@@ -29,10 +29,15 @@ struct FwdParams {
   int nchunks, nseg, cps, ndvb, nring, kring, ngroups;
   FwdLds lds;
   int per_head_q;
+  int full;  // whole-head kernel (fwd_full.hip)
+  int sss;   // whole-head kernel: state-pass pieces per segment (divides cps)
   float mix, scale;
 };
 
 hipError_t launch_fwd(const FwdParams &p, int dtype_bf16, int d, hipStream_t stream);
+// whole-head forward kernel (bf16, d = 128, shared W_phi, one query head per key/value
+// head, W <= 65); the state pass of launch_fwd runs first when the sequence is segmented
+hipError_t launch_fwd_full(const FwdParams &p, hipStream_t stream);
 // before the forward: window history rows from the caller's ring; after it: the ring of
 // the last W tokens and pos += L
 hipError_t launch_hist_stage(const FwdParams &p, const void *ring_k, const void *ring_v, int d, int esize,

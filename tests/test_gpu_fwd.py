@@ -146,6 +146,30 @@ def test_fwd_sequence_segments(gpu_lib, monkeypatch, nseg):
     check_case(f"bf16 gqa {nseg} segments", inp, "bf16")
 
 
+@pytest.mark.parametrize("nseg", [1, 2, 3, 5])
+def test_fwd_whole_head_segments(gpu_lib, monkeypatch, nseg):
+    """The whole-head kernel (bf16, d = 128, one query head per key/value head, W <= 65) over
+    sequence segments joined through its state pass: a gate that mixes both decay
+    references with a ragged tail, and gamma = 0 (exact diagonal blocks from the fixup
+    kernel) across segment boundaries."""
+    monkeypatch.setenv("LIZARD_FWD_SEGMENTS", str(nseg))
+    inp = make_fwd_inputs(B=1, Hq=2, Hkv=2, L=650, d=128, W=65, M=16, dtype="bf16", seed=90 + nseg,
+                          gate="uniform:-1.6")
+    check_case(f"bf16 whole-head {nseg} segments, mixed references", inp, "bf16")
+    inp = make_fwd_inputs(B=2, Hq=1, Hkv=1, L=300, d=128, W=64, M=4, dtype="bf16", seed=95 + nseg, gate="zero")
+    check_case(f"bf16 whole-head {nseg} segments, gamma=0", inp, "bf16")
+
+
+@pytest.mark.parametrize("label", ["bf16 d128 ragged L200", "bf16 gamma=0 (exact diag)", "bf16 gamma=1"])
+def test_fwd_value_block_kernel(gpu_lib, monkeypatch, label):
+    """The value-block (role-split) kernel on cases the whole-head kernel would otherwise take
+    (it still serves separate or per-head W_phi and grouped heads)."""
+    monkeypatch.setenv("LIZARD_FWD_KERNEL", "split")
+    kw, dtype = {s[0]: (s[1], s[2]) for s in SMALL}[label]
+    inp = make_fwd_inputs(dtype=dtype, seed=zlib.crc32(label.encode()) % 10000, **kw)
+    check_case(label + " [value blocks]", inp, dtype)
+
+
 def _sampled_check(index, heads, label):
     inp = workload_fwd_inputs(index)
     dtype = "bf16"
