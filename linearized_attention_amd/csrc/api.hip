@@ -45,6 +45,7 @@ constexpr int kChunk = 64;
 constexpr int kDV = 64;       // value columns per workgroup
 constexpr int kMaxMeta = 16;
 constexpr int kTargetBlocks = 256;
+constexpr int kStateBlocks = 512;  // state-pass pieces (two 80 KB workgroups fit a CU)
 constexpr int kMaxFullCps = 16384;  // chunks per segment the whole-head kernel's LDS flags cover
 
 struct FwdPlan {
@@ -60,11 +61,11 @@ size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 // value block, segment) otherwise); an environment override (LIZARD_FWD_SEGMENTS)
 // exists for tests and tuning.  The segment end states are kept per 64-column
 // value block in either case (the state pass works per block).
-FwdPlan make_plan(int B, int Hkv, int L, int d, int W, bool full) {
+FwdPlan make_plan(int B, int Hq, int Hkv, int L, int d, int W, bool full) {
   FwdPlan p{};
   p.nchunks = (L + kChunk - 1) / kChunk;
   p.ndvb = d / kDV;
-  const long base = (long)B * Hkv * (full ? 1 : p.ndvb);
+  const long base = full ? (long)B * Hq : (long)B * Hkv * p.ndvb;
   long nseg = (kTargetBlocks + base - 1) / base;
   if (const char *e = getenv("LIZARD_FWD_SEGMENTS")) {
     const long v = atol(e);
@@ -82,8 +83,8 @@ FwdPlan make_plan(int B, int Hkv, int L, int d, int W, bool full) {
   }
   p.sss = 1;
   if (full && p.nseg > 1) {
-    // the state pass (all chunks before the last segment) in about kTargetBlocks pieces
-    long ss = kTargetBlocks / ((long)B * Hkv * (p.nseg - 1));
+    // the state pass (all chunks before the last segment) in about kStateBlocks pieces
+    long ss = kStateBlocks / ((long)B * Hkv * (p.nseg - 1));
     if (ss < 1) ss = 1;
     if (ss > p.cps) ss = p.cps;
     while (p.cps % ss) --ss;
@@ -96,22 +97,23 @@ FwdPlan make_plan(int B, int Hkv, int L, int d, int W, bool full) {
 
 size_t plan_bytes(const FwdPlan &p) { return p.ws_state_bytes + p.ws_decay_bytes; }
 
-// The whole-head kernel serves bf16 at d = 128 with one W_phi for queries and keys,
-// one query head per key/value head and W <= 65 (LIZARD_FWD_KERNEL=split or 4wave
+// The whole-head kernel serves bf16 at d = 128 with one W_phi for queries and keys
+// (any grouping of query heads) and W <= 65 (LIZARD_FWD_KERNEL=split or 4wave
 // selects the value-block kernels instead, for tests and A/B timing).
 bool use_full_kernel(int Hq, int Hkv, int d, int W, lizard_dtype dtype, const void *wq, const void *wk,
                      int64_t w_stride) {
   const char *kenv = getenv("LIZARD_FWD_KERNEL");
   if (kenv && (strcmp(kenv, "split") == 0 || strcmp(kenv, "4wave") == 0)) return false;
-  return dtype == LIZARD_BF16 && d == 128 && Hq == Hkv && W <= kChunk + 1 && wq == wk && w_stride == 0;
+  (void)Hq;
+  (void)Hkv;
+  return dtype == LIZARD_BF16 && d == 128 && W <= kChunk + 1 && wq == wk && w_stride == 0;
 }
 
 // Workspace for either plan (the caller does not say whether W_phi is shared).
 size_t seg_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int W, lizard_dtype dtype) {
-  const size_t sa = plan_bytes(make_plan(B, Hkv, L, d, W, false));
-  const bool maybe_full = dtype == LIZARD_BF16 && d == 128 && Hq == Hkv && W <= kChunk + 1 &&
-                          use_full_kernel(Hq, Hkv, d, W, dtype, nullptr, nullptr, 0);
-  const size_t sb = maybe_full ? plan_bytes(make_plan(B, Hkv, L, d, W, true)) : 0;
+  const size_t sa = plan_bytes(make_plan(B, Hq, Hkv, L, d, W, false));
+  const bool maybe_full = use_full_kernel(Hq, Hkv, d, W, dtype, nullptr, nullptr, 0);
+  const size_t sb = maybe_full ? plan_bytes(make_plan(B, Hq, Hkv, L, d, W, true)) : 0;
   return sa > sb ? sa : sb;
 }
 
@@ -175,7 +177,7 @@ lizard_status fwd_impl(const void *q, const void *k, const void *v, const void *
       return fail(LIZARD_ERR_INVALID_ARG, "pos not 4-byte aligned");
   }
   const bool full = use_full_kernel(Hq, Hkv, d, W, dtype, w_phi_q, w_phi_k, w_phi_head_stride);
-  const FwdPlan plan = make_plan(B, Hkv, L, d, W, full);
+  const FwdPlan plan = make_plan(B, Hq, Hkv, L, d, W, full);
   const size_t seg_bytes = plan_bytes(plan);
   const size_t hist_bytes = history ? ext_hist_bytes(B, Hkv, d, W, dtype) : 0;
   const size_t need = (hist_bytes ? align256(seg_bytes) : seg_bytes) + 2 * hist_bytes;

@@ -1,8 +1,10 @@
-// Lizard attention forward, whole-head variant (bf16, d = 128, window W <= 65,
-// one query head per key/value head): one workgroup per (batch, head, sequence
+// Lizard attention forward, whole-head variant (bf16, d = 128, window W <= 65, one
+// W_phi for queries and keys): one workgroup per (batch, query head, sequence
 // segment) computes all 128 value columns, so the feature maps, the gate sums,
 // the window logits and the intra-chunk scores are computed once per head
-// instead of once per 64-column value block.
+// instead of once per 64-column value block.  With grouped query heads the G
+// workgroups of a key/value head each run its key side (on one XCD, so k, v and
+// log gamma come from L2 after the first read).
 //
 // The arithmetic is that of the role-split kernel (fwd_split.hip), with the
 // decay references of fwd.hip: a chunk whose log decay stays within FAST_SPAN
@@ -199,11 +201,16 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
   const bool key_wave = wv >= 4;
   const int I = wv & 3;
 
-  const int grp = blockIdx.x;
+  // block -> (batch, key/value head, segment) group and query head g of the group; the G
+  // blocks of a group are 8 apart, so they run on one XCD and share its L2 for k, v, log gamma
+  const int G = p.G;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int grp = (slot / G) * 8 + xcd, g = slot % G;
   if (grp >= p.ngroups) return;
   const int seg = grp % p.nseg;
   const int bh = grp / p.nseg;
   const int b = bh / p.Hkv, kvh = bh % p.Hkv;
+  const int hq = kvh * G + g;
   const int L = p.L;
   const int c_begin = seg * p.cps;
   const int c_end = min(p.nchunks, c_begin + p.cps);
@@ -212,8 +219,8 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
   const T *Kh = reinterpret_cast<const T *>(p.k) + kv_off;
   const T *Vh = reinterpret_cast<const T *>(p.v) + kv_off;
   const T *LGh = reinterpret_cast<const T *>(p.lg) + kv_off;
-  const T *Qh = reinterpret_cast<const T *>(p.q) + ((size_t)b * p.Hq + kvh) * (size_t)L * D;
-  T *Oh = reinterpret_cast<T *>(p.out) + ((size_t)b * p.Hq + kvh) * (size_t)L * D;
+  const T *Qh = reinterpret_cast<const T *>(p.q) + ((size_t)b * p.Hq + hq) * (size_t)L * D;
+  T *Oh = reinterpret_cast<T *>(p.out) + ((size_t)b * p.Hq + hq) * (size_t)L * D;
   const size_t hist_off = ((size_t)b * p.Hkv + kvh) * (size_t)p.hist_rows * D;
   const T *Hk = reinterpret_cast<const T *>(p.hist_k) + hist_off;
   const T *Hv = reinterpret_cast<const T *>(p.hist_v) + hist_off;
@@ -496,7 +503,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
 #pragma unroll
       for (int j = 0; j < KS; ++j) kf[j] = kf_next[j];
     }
-    if (p.state_out && seg == p.nseg - 1) {
+    if (p.state_out && seg == p.nseg - 1 && g == 0) {
       float *So = p.state_out + ((size_t)b * p.Hkv + kvh) * D * D;
 #pragma unroll
       for (int ft = 0; ft < FTW; ++ft)
@@ -1031,7 +1038,7 @@ hipError_t launch_fwd_full(const FwdParams &p, hipStream_t stream) {
   e = hipFuncSetAttribute(reinterpret_cast<const void *>(fwd_full_kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, full::LDS_BYTES);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fwd_full_kernel, dim3(p.ngroups), dim3(512), full::LDS_BYTES, stream, p);
+  hipLaunchKernelGGL(fwd_full_kernel, dim3(((p.ngroups + 7) / 8) * 8 * p.G), dim3(512), full::LDS_BYTES, stream, p);
   return hipGetLastError();
 }
 

@@ -124,7 +124,7 @@ def test_fwd_mixed_chunk_references(gpu_lib, dtype, d):
     check_case(f"{dtype} d{d} mixed chunk references", inp, dtype)
 
 
-@pytest.mark.parametrize("label", ["bf16 d128 ragged L200", "fp32 uniform gate -8 (mixed safe/exact diag)",
+@pytest.mark.parametrize("label", ["bf16 d128 ragged L200", "bf16 gqa 4:2 shared W", "fp32 uniform gate -8 (mixed safe/exact diag)",
                                    "fp32 W66 (3-chunk ring)"])
 def test_fwd_four_wave_kernel(gpu_lib, monkeypatch, label):
     """The 4-wave kernel (used for grouped heads and the segment state pass) on single-head
