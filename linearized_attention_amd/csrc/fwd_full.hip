@@ -44,19 +44,22 @@ namespace full {
 
 constexpr int D = 128, NFT = 8, KS = 4, NDT = 8, FTW = 2;
 constexpr int LDW = 144;  // rows of 128 elements (288 bytes)
+constexpr int LDWW = 136; // W_phi^T rows (272 bytes: LDS is too short for 288)
+constexpr int LDQ = 136;  // decayed-query rows (272 bytes)
 constexpr int LDV = 80;   // rows of 64 tokens (160 bytes)
-constexpr int LDM = 24;   // rows of 16 meta tokens (48 bytes, 8-byte reads)
+constexpr int LDM = 16;   // rows of 16 meta tokens (32 bytes, 8-byte reads)
 constexpr int OFF_W = 0;                        // W_phi^T [f][d]
-constexpr int OFF_K = OFF_W + D * LDW * 2;      // keys of the chunk [s][d]
+constexpr int OFF_K = OFF_W + D * LDWW * 2;     // keys of the chunk [s][d]
 constexpr int OFF_VT = OFF_K + CH * LDW * 2;    // v^T [dv][token, interleaved]
 constexpr int OFF_KT = OFF_VT + D * LDV * 2;    // decayed keys [s][f, interleaved] / log gamma^T [f][s]
 constexpr int SZ_KT = (CH * LDW > D * LDV ? CH * LDW : D * LDV) * 2;
 constexpr int OFF_SB = OFF_KT + SZ_KT;          // S^T copy [dv][f, interleaved]
-constexpr int OFF_TAB = OFF_SB + D * LDW * 2;   // five [4][128] fp32 tables
-constexpr int OFF_TK = OFF_TAB + 5 * 4 * D * 4; // meta keys [16][d]
+constexpr int OFF_Q = OFF_SB + D * LDW * 2;     // decayed queries [t][f, interleaved]
+constexpr int OFF_TAB = OFF_Q + CH * LDQ * 2;   // prefix ends C_J and prefix to row 16J + 7, [4][128] fp32 each
+constexpr int OFF_TK = OFF_TAB + 2 * 4 * D * 4; // meta keys [16][d]
 constexpr int OFF_TV = OFF_TK + 16 * LDW * 2;   // meta values^T [dv][16]
-constexpr int OFF_FLAG = OFF_TV + D * LDM * 2;   // per query wave: bit k = chunk c_begin + k needs
-constexpr int FLAG_WORDS = 512;                  // the exact diagonal block (segments of at most 16384 chunks)
+constexpr int OFF_FLAG = OFF_TV + D * LDM * 2;  // per query wave: bit k = chunk c_begin + k needs
+constexpr int FLAG_WORDS = 128;                 // the exact diagonal block (segments of at most 4096 chunks)
 constexpr int LDS_BYTES = OFF_FLAG + 4 * FLAG_WORDS * 4;
 static_assert(LDS_BYTES <= LDS_LIMIT, "whole-head layout exceeds LDS");
 
@@ -87,7 +90,7 @@ __device__ __forceinline__ f32x4 exact_diag_scores(const bf16 *sW, const bf16 *K
   auto logits_ft = [&](const Frag<T>(&x)[KS], int ft) {
     f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < KS; ++j) z = mma(load8(sW + (16 * ft + r16) * LDW + 32 * j + 8 * g4), x[j], z);
+    for (int j = 0; j < KS; ++j) z = mma(load8(sW + (16 * ft + r16) * LDWW + 32 * j + 8 * g4), x[j], z);
     return z;
   };
   float mq = NEG_BIG, mk = NEG_BIG;
@@ -187,16 +190,17 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
   T *sKt = reinterpret_cast<T *>(smem + OFF_KT);
   T *sLgT = sKt;  // log gamma^T, dead before the decayed keys are written
   T *sSb = reinterpret_cast<T *>(smem + OFF_SB);
+  T *sQ = reinterpret_cast<T *>(smem + OFF_Q);
   float *sTot = reinterpret_cast<float *>(smem + OFF_TAB);  // C_J: prefix from the chunk start to the end of J
   float *sP7 = sTot + 4 * D;                                // prefix from the chunk start to row 16J + 7
-  float *sETot = sP7 + 4 * D;
-  float *sENP7 = sETot + 4 * D;
-  float *sENR8 = sENP7 + 4 * D;
   T *sTk = reinterpret_cast<T *>(smem + OFF_TK);
   T *sTvT = reinterpret_cast<T *>(smem + OFF_TV);
   uint32_t *sFlag = reinterpret_cast<uint32_t *>(smem + OFF_FLAG);
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // lane id from mbcnt and the wave index as a scalar: both can be rebuilt anywhere, so the
+  // register allocator recomputes lane-derived values instead of keeping (or spilling) them
+  const int tid = threadIdx.x, lane = __lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g4 = lane >> 4;
   const bool key_wave = wv >= 4;
   const int I = wv & 3;
@@ -291,10 +295,47 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
     }
   };
 
+  // queries of rows c0 + 16I .. +15 in fragment order
+  auto load_q = [&](Frag<T> (&f)[KS], int c0) {
+    const int t = c0 + 16 * I + r16;
+    const unsigned off = (unsigned)(t * D + 8 * g4);
+#pragma unroll
+    for (int j = 0; j < KS; ++j) f[j] = (t < L) ? load8(Qh + off + 32 * j) : frag_zero<T>();
+  };
+  // Loads inside the chunk loop (rows >= 0): a uniform base and a 32-bit per-lane offset
+  // recomputed from the lane id each time, so no 64-bit lane addresses are held (or spilled)
+  // across the loop; a reloaded spill would also wait for every load in flight.
+  auto kfrag_in = [&](Frag<T> (&kf)[KS], int c0, int ln) {
+    const int x = c0 + 16 * I + (ln & 15);
+    const unsigned off = (unsigned)(x * D + 8 * (ln >> 4));
+#pragma unroll
+    for (int j = 0; j < KS; ++j) kf[j] = (x < L) ? load8(Kh + off + 32 * j) : frag_zero<T>();
+  };
+  auto q_in = [&](Frag<T> (&f)[KS], int c0, int ln) {
+    const int t = c0 + 16 * I + (ln & 15);
+    const unsigned off = (unsigned)(t * D + 8 * (ln >> 4));
+#pragma unroll
+    for (int j = 0; j < KS; ++j) f[j] = (t < L) ? load8(Qh + off + 32 * j) : frag_zero<T>();
+  };
+  // token pairs (2 tp, 2 tp + 1) x 8-column groups t / 32 and t / 32 + 8 of a [L][D] tensor
+  auto pairs_in = [&](Frag<T> (&f)[2][2], const T *base, int c0, int t) {
+    const int tp = t & 31;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int x = c0 + 2 * tp + h;
+#pragma unroll
+      for (int gsel = 0; gsel < 2; ++gsel) {
+        const unsigned off = (unsigned)(x * D + 8 * ((t >> 5) + 8 * gsel));
+        f[gsel][h] = (x < L) ? load8(base + off) : frag_zero<T>();
+      }
+    }
+  };
+  const float mix = p.mix, log2_mix = __log2f(p.mix);
+
   // ---- prologue: weights, meta tokens, the chunk before the first one
   {
     const T *Wk = reinterpret_cast<const T *>(p.wk);
-    load_wT<T, D, LDW, 512>(sW, Wk, tid);
+    load_wT<T, D, LDWW, 512>(sW, Wk, tid);
     const T *Tv = reinterpret_cast<const T *>(p.tv);
     const T *Tk = reinterpret_cast<const T *>(p.tk);
     for (int idx = tid; idx < D * 16; idx += 512) {
@@ -358,9 +399,10 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
       }
     }
     const Frag<T> tri_c0 = tri64_frag<T>(r16, g4, I, 0), tri_c1 = tri64_frag<T>(r16, g4, I, 1);
-    Frag<T> kf[KS], kf_next[KS];
+    Frag<T> kf[KS], kf_next[KS], qf[KS], qf_next[KS];
     Frag<T> lf[2][2];
     load_kfrag(kf, c_begin * CH);
+    load_q(qf, c_begin * CH);
     load_lgpairs(lf, c_begin * CH, kt);
     // S^T copy of the start state
     auto publish = [&]() {
@@ -377,22 +419,32 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
 
     for (int c = c_begin; c < c_end; ++c) {
       const int c0 = c * CH;
-      // ---- P0: phi_k of this chunk's rows (keys from registers); the query waves read the
-      //      previous chunk's keys and values from LDS meanwhile
-      float ko[NFT][4];
+      // ---- P0: phi_k and phi_q of this chunk's rows (keys and queries from registers, each
+      //      W_phi^T fragment read once for both); the query waves read the previous chunk's
+      //      keys and values from LDS meanwhile
+      float ko[NFT][4], qo[NFT][4];
       {
-        f32x4 z[NFT];
-        feature_logits<T, D, LDW>(sW, kf, r16, g4, z);
+        f32x4 z[NFT], zq[NFT];
+        feature_logits2<T, D, LDWW>(sW, kf, qf, r16, g4, z, zq);
         softmax_rows<NFT>(z, ko);
+        softmax_rows<NFT>(zq, qo);
       }
       __syncthreads();  // B0: the previous chunk's LDS is dead
-      // ---- P1: stage this chunk's keys and log gamma^T; publish S_c; next chunk in flight
+      // ---- P1: stage this chunk's keys, log gamma^T and phi_q; publish S_c; next chunk in flight
       store_kfrag(kf);
       store_lgpairs(lf, kt);
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft) {  // phi_q, decayed in P2 (interleaved features)
+        const int fpos = 32 * (ft >> 1) + 8 * g4 + 4 * (ft & 1);
+        store4<T>(sQ + (16 * I + r16) * LDQ + fpos, qo[ft][0], qo[ft][1], qo[ft][2], qo[ft][3]);
+      }
       if (c > c_begin) publish();
       if (c + 1 < c_end) {
-        load_kfrag(kf_next, c0 + CH);
-        load_lgpairs(lf, c0 + CH, kt);
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        kfrag_in(kf_next, c0 + CH, ln);
+        q_in(qf_next, c0 + CH, ln);
+        pairs_in(lf, LGh, c0 + CH, ln + 64 * (wv - 4));
       }
       __syncthreads();  // B1
       // ---- P2: prefix sums from the chunk start for this sub-chunk's rows
@@ -410,7 +462,22 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
         for (int ft = 0; ft < NFT; ++ft)
           *reinterpret_cast<f32x4 *>(dst + 16 * ft) = f32x4{pc[ft][0], pc[ft][1], pc[ft][2], pc[ft][3]};
       }
-      __syncthreads();  // B2: sub-chunk prefix ends visible; log gamma^T dead
+      // decayed queries with the merge weight, chunk-start reference: mix e^{p_t} phi_q (<= 1
+      // for any gate), in place; a chunk on the sub-chunk references has the query waves
+      // rebuild theirs
+#pragma unroll
+      for (int js = 0; js < KS; ++js) {
+        T *qp = sQ + (16 * I + r16) * LDQ + 32 * js + 8 * g4;
+        const Frag<T> ph = load8(qp);
+        float x[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int ft = 2 * js + (jj >> 2), i = jj & 3;
+          x[jj] = to_f(ph.v[jj]) * exp2_fast(__builtin_fmaf(pc[ft][i], LOG2E, log2_mix));
+        }
+        *reinterpret_cast<bf16x8 *>(qp) = frag_from<T>(x).v;
+      }
+      __syncthreads();  // B2: sub-chunk prefix ends and decayed queries visible; log gamma^T dead
       const bool mild = chunk_is_mild_c<D>(sTot, lane);
       // ---- P3: decayed keys -> LDS (interleaved features) and the factor tables.
       //      Mild: keys carry e^{-p_s}, table e^{B_c}.  Otherwise keys carry e^{C_I - p_s}
@@ -420,20 +487,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
         for (int ft = 0; ft < NFT; ++ft)
 #pragma unroll
           for (int i = 0; i < 4; ++i) ko[ft][i] *= exp2_fast(-pc[ft][i] * LOG2E);
-        if (kt < D) sETot[kt] = __expf(sTot[3 * D + kt]);
       } else {
-        constexpr int PER = 2;  // sub-chunks per thread (256 threads, 128 features)
-        const int f = kt % D, j0 = (kt / D) * PER;
-#pragma unroll
-        for (int jj = 0; jj < PER; ++jj) {
-          const int J = j0 + jj;
-          const float cprev = J > 0 ? sTot[(J - 1) * D + f] : 0.f;
-          const float tt = sTot[J * D + f] - cprev;
-          const float p7 = sP7[J * D + f] - cprev;
-          sETot[J * D + f] = __expf(tt);
-          sENP7[J * D + f] = __expf(-p7);
-          sENR8[J * D + f] = __expf(p7 - tt);
-        }
 #pragma unroll
         for (int ft = 0; ft < NFT; ++ft) {
           const f32x4 t = *reinterpret_cast<const f32x4 *>(sTot + I * D + 16 * ft + 4 * g4);
@@ -453,34 +507,17 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
       for (int ft = 0; ft < FTW; ++ft) {
         const int fr = 16 * (2 * I + ft);
         const int fcol = 32 * I + ipos(16 * ft + r16);  // interleaved position of feature fr + r16
+        // row decay e^{B_c} = e^{C_3}; key factors e^{C_3} (mild: keys carry e^{-p_s}) or
+        // e^{C_3 - C_J} (keys carry e^{C_J - p_s})
         float e[4];
         float fac[2][2];  // [ks][half]: factor of the keys of sub-chunk 2ks + half
-        if (mild) {
-          const f32x4 t = *reinterpret_cast<const f32x4 *>(sETot + fr + 4 * g4);
+        {
+          const f32x4 c3 = *reinterpret_cast<const f32x4 *>(sTot + 3 * D + fr + 4 * g4);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) e[i] = t[i];
-          const float f0 = sETot[fr + r16];
-          fac[0][0] = fac[0][1] = fac[1][0] = fac[1][1] = f0;
-        } else {
+          for (int i = 0; i < 4; ++i) e[i] = __expf(c3[i]);
+          const float c3r = sTot[3 * D + fr + r16];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) e[i] = 1.f;
-#pragma unroll
-          for (int J = 0; J < 4; ++J) {
-            const f32x4 t = *reinterpret_cast<const f32x4 *>(sETot + J * D + fr + 4 * g4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) e[i] *= t[i];
-          }
-          float et[4];
-#pragma unroll
-          for (int J = 0; J < 4; ++J) et[J] = sETot[J * D + fr + r16];
-#pragma unroll
-          for (int J = 0; J < 4; ++J) {
-            float f = 1.f;
-#pragma unroll
-            for (int J2 = 1; J2 < 4; ++J2)
-              if (J2 > J) f *= et[J2];
-            fac[J >> 1][J & 1] = f;
-          }
+          for (int J = 0; J < 4; ++J) fac[J >> 1][J & 1] = __expf(mild ? c3r : c3r - sTot[J * D + fr + r16]);
         }
         Frag<T> ka[2];
 #pragma unroll
@@ -501,7 +538,10 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
         }
       }
 #pragma unroll
-      for (int j = 0; j < KS; ++j) kf[j] = kf_next[j];
+      for (int j = 0; j < KS; ++j) {
+        kf[j] = kf_next[j];
+        qf[j] = qf_next[j];
+      }
     }
     if (p.state_out && seg == p.nseg - 1 && g == 0) {
       float *So = p.state_out + ((size_t)b * p.Hkv + kvh) * D * D;
@@ -514,17 +554,9 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
     }
   } else {
     // ======================================================= query waves
-    const float mix = p.mix, scale = p.scale;
-    const float log2_mix = __log2f(mix);
-    const float sl2 = scale * LOG2E;  // window logits in base 2
-    const Frag<T> tri_c0 = tri64_frag<T>(r16, g4, I, 0), tri_c1 = tri64_frag<T>(r16, g4, I, 1);
+    const float sl2 = p.scale * LOG2E;  // window logits in base 2
     Frag<T> qf[KS], qf_next[KS];
     Frag<T> vf[2][2];
-    auto load_q = [&](Frag<T> (&f)[KS], int c0) {
-      const int t = c0 + 16 * I + r16;
-#pragma unroll
-      for (int j = 0; j < KS; ++j) f[j] = (t < L) ? load8(Qh + (size_t)t * D + 32 * j + 8 * g4) : frag_zero<T>();
-    };
     load_q(qf, c_begin * CH);
     load_vpairs(vf, c_begin * CH, tid);
     bool unsafe_seen = false;
@@ -605,24 +637,11 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
         }
       }
       __syncthreads();  // B0
-      // ---- P1: stage this chunk's values; next chunk in flight
+      // ---- P1: stage this chunk's values
       store_vpairs(vf, tid);
       __syncthreads();  // B1
-      // ---- P2: prefix sums from the chunk start, phi_q, window group Y (this chunk's keys 0..I)
-      float pfx[NFT][4];
-#pragma unroll
-      for (int ft = 0; ft < NFT; ++ft) {
-        f32x4 cc = mma(load8(sLgT + (16 * ft + r16) * LDV + 8 * g4), tri_c0, f32x4{0.f, 0.f, 0.f, 0.f});
-        cc = mma(load8(sLgT + (16 * ft + r16) * LDV + 32 + 8 * g4), tri_c1, cc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pfx[ft][i] = cc[i];
-      }
-      float qo[NFT][4];
-      {
-        f32x4 z[NFT];
-        feature_logits<T, D, LDW>(sW, qf, r16, g4, z);
-        softmax_rows<NFT>(z, qo);
-      }
+      // ---- P2: window group Y (this chunk's keys 0..I); the key waves compute the decayed queries
+      Frag<T> qcf[KS];  // query operand of the intra and inter products (f-interleaved K = 32 slices)
       {
         f32x4 lt[4];
 #pragma unroll
@@ -677,21 +696,42 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
       const bool mild = chunk_is_mild_c<D>(sTot, lane);
       bool safe = true;  // general case: mid-row reference usable on the diagonal block
       if (!mild) {
-        // sub-chunk start reference: subtract the prefix up to the end of sub-chunk I - 1
-        if (I > 0) {
-#pragma unroll
-          for (int ft = 0; ft < NFT; ++ft) {
-            const f32x4 t = *reinterpret_cast<const f32x4 *>(sTot + (I - 1) * D + 16 * ft + 4 * g4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pfx[ft][i] -= t[i];
-          }
+        // sub-chunk start reference: q~ = mix e^{px_t} phi_q with px the prefix inside the
+        // sub-chunk, rebuilt from q and log gamma in global memory (log gamma^T in LDS is being
+        // overwritten by the decayed keys)
+        Frag<T> qfr[KS];
+        load_q(qfr, c0);
+        float phq[NFT][4];
+        {
+          f32x4 z[NFT];
+          feature_logits<T, D, LDWW>(sW, qfr, r16, g4, z);
+          softmax_rows<NFT>(z, phq);
         }
+        const Frag<T> tri_pre = tri_frag<T>(r16, g4, true);
         float span = 0.f;
 #pragma unroll
-        for (int ft = 0; ft < NFT; ++ft)
+        for (int ft = 0; ft < NFT; ++ft) {
+          float x[8];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) span = fmaxf(span, -pfx[ft][i]);
+          for (int j = 0; j < 8; ++j) {
+            const int t = c0 + 16 * I + 8 * g4 + j;
+            x[j] = (g4 < 2 && t < L) ? to_f(LGh[(size_t)t * D + 16 * ft + r16]) : 0.f;
+          }
+          const f32x4 px = mma(frag_from<T>(x), tri_pre, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            span = fmaxf(span, -px[i]);
+            phq[ft][i] *= exp2_fast(__builtin_fmaf(px[i], LOG2E, log2_mix));
+          }
+        }
         safe = wave_max_all(span) <= SPAN_MAX;
+#pragma unroll
+        for (int js = 0; js < KS; ++js) {
+          float x[8];
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) x[jj] = phq[2 * js + (jj >> 2)][jj & 3];
+          qcf[js] = frag_from<T>(x);
+        }
       }
       // sub-chunks whose diagonal block needs the exact products (added after the chunk loop)
       const bool unsafe = !safe;
@@ -700,14 +740,12 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
       // next chunk's values and queries in flight from here (later than the key waves' loads:
       // fewer registers live through the feature map and the window)
       if (c + 1 < c_end) {
-        load_vpairs(vf, c0 + CH, tid);
-        load_q(qf_next, c0 + CH);
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        pairs_in(vf, Vh, c0 + CH, ln + 64 * wv);
+        q_in(qf_next, c0 + CH, ln);
       }
-      // ---- P3: decayed queries with the merge weight: qo *= mix e^{pfx}; window normalised
-#pragma unroll
-      for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) qo[ft][i] *= exp2_fast(__builtin_fmaf(pfx[ft][i], LOG2E, log2_mix));
+      // ---- P3: window output normalised and scaled for the merge
       {
         const float ws = (1.f - mix) / wave_sum_cols(l_run);
 #pragma unroll
@@ -719,16 +757,6 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
       // ---- P4: intra- and inter-chunk products onto the window output, store
       auto finish = [&](auto mild_tag) {
         constexpr bool MILD = decltype(mild_tag)::value;
-        // query operand in bf16 (f-interleaved K = 32 slices); the general case rescales it
-        // per feature from the tables
-        Frag<T> qcf[KS];
-#pragma unroll
-        for (int js = 0; js < KS; ++js) {
-          float x[8];
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) x[jj] = qo[2 * js + (jj >> 2)][jj & 3];
-          qcf[js] = frag_from<T>(x);
-        }
         if constexpr (MILD) {
           // intra-chunk scores A^T[s][t] of key sub-chunk J (masked to s <= t on the diagonal)
           auto score = [&](int J) -> f32x4 {
@@ -769,17 +797,15 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
           // Sub-chunk references (rare: a chunk whose log decay exceeds FAST_SPAN).  One key
           // sub-chunk at a time, register-light: the query operand of K-step js times the tables
           // e^{tot_J2} of the sub-chunks J2 in [lo, hi)
+          // the query operand of K-step js times prod_{lo <= J2 < hi} e^{tot_J2} = e^{C_{hi-1} - C_{lo-1}}
           auto qscaled = [&](int js, int lo, int hi) {
-            float x[8];
+            float x[8], a8[8], b8[8];
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) x[jj] = to_f(qcf[js].v[jj]);
-#pragma unroll 1
-            for (int J2 = lo; J2 < hi; ++J2) {
-              float t8[8];
-              tab8(sETot + J2 * D, js, g4, t8);
+            for (int jj = 0; jj < 8; ++jj) { a8[jj] = 0.f; b8[jj] = 0.f; }
+            if (hi > 0) tab8(sTot + (hi - 1) * D, js, g4, a8);
+            if (lo > 0) tab8(sTot + (lo - 1) * D, js, g4, b8);
 #pragma unroll
-              for (int jj = 0; jj < 8; ++jj) x[jj] *= t8[jj];
-            }
+            for (int jj = 0; jj < 8; ++jj) x[jj] = to_f(qcf[js].v[jj]) * __expf(a8[jj] - b8[jj]);
             return frag_from<T>(x);
           };
 #pragma unroll 1
@@ -793,14 +819,19 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
               // mid-row reference: (k~ e^{p7 - tot}) . (q e^{-p7})
 #pragma unroll
               for (int js = 0; js < KS; ++js) {
-                float t8[8], kv[8], x[8];
+                // keys carry e^{C_I - p_s}, queries e^{p_t - C_{I-1}}: k e^{P7 - C_I}, q e^{C_{I-1} - P7}
+                float p8[8], c8[8], cp8[8], kv[8], x[8];
                 const Frag<T> kk = load8(sKt + (16 * I + r16) * LDW + 32 * js + 8 * g4);
-                tab8(sENR8 + I * D, js, g4, t8);
+                tab8(sP7 + I * D, js, g4, p8);
+                tab8(sTot + I * D, js, g4, c8);
 #pragma unroll
-                for (int jj = 0; jj < 8; ++jj) kv[jj] = to_f(kk.v[jj]) * t8[jj];
-                tab8(sENP7 + I * D, js, g4, t8);
+                for (int jj = 0; jj < 8; ++jj) cp8[jj] = 0.f;
+                if (I > 0) tab8(sTot + (I - 1) * D, js, g4, cp8);
 #pragma unroll
-                for (int jj = 0; jj < 8; ++jj) x[jj] = to_f(qcf[js].v[jj]) * t8[jj];
+                for (int jj = 0; jj < 8; ++jj) {
+                  kv[jj] = to_f(kk.v[jj]) * __expf(p8[jj] - c8[jj]);
+                  x[jj] = to_f(qcf[js].v[jj]) * __expf(cp8[jj] - p8[jj]);
+                }
                 a = mma(frag_from<T>(kv), frag_from<T>(x), a);
               }
             } else {
@@ -836,10 +867,13 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
           for (int dt = 0; dt < NDT; ++dt) store4<T>(O + 16 * dt + 4 * g4, acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
         }
       };
-      if (mild)
+      if (mild) {
+#pragma unroll
+        for (int js = 0; js < KS; ++js) qcf[js] = load8(sQ + (16 * I + r16) * LDQ + 32 * js + 8 * g4);
         finish(std::true_type{});
-      else
+      } else {
         finish(std::false_type{});
+      }
 #pragma unroll
       for (int j = 0; j < KS; ++j) qf[j] = qf_next[j];
     }
