@@ -55,8 +55,8 @@ constexpr int OFF_KT = OFF_VT + D * LDV * 2;    // decayed keys [s][f, interleav
 constexpr int SZ_KT = (CH * LDW > D * LDV ? CH * LDW : D * LDV) * 2;
 constexpr int OFF_SB = OFF_KT + SZ_KT;          // S^T copy [dv][f, interleaved]
 constexpr int OFF_Q = OFF_SB + D * LDW * 2;     // decayed queries [t][f, interleaved]
-constexpr int OFF_TAB = OFF_Q + CH * LDQ * 2;   // prefix ends C_J and prefix to row 16J + 7, [4][128] fp32 each
-constexpr int OFF_TK = OFF_TAB + 2 * 4 * D * 4; // meta keys [16][d]
+constexpr int OFF_TAB = OFF_Q + CH * LDQ * 2;   // prefix ends C_J, [4][128] fp32
+constexpr int OFF_TK = OFF_TAB + 4 * D * 4;     // meta keys [16][d]
 constexpr int OFF_TV = OFF_TK + 16 * LDW * 2;   // meta values^T [dv][16]
 constexpr int OFF_FLAG = OFF_TV + D * LDM * 2;  // per query wave: bit k = chunk c_begin + k needs
 constexpr int FLAG_WORDS = 128;                 // the exact diagonal block (segments of at most 4096 chunks)
@@ -192,7 +192,6 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
   T *sSb = reinterpret_cast<T *>(smem + OFF_SB);
   T *sQ = reinterpret_cast<T *>(smem + OFF_Q);
   float *sTot = reinterpret_cast<float *>(smem + OFF_TAB);  // C_J: prefix from the chunk start to the end of J
-  float *sP7 = sTot + 4 * D;                                // prefix from the chunk start to row 16J + 7
   T *sTk = reinterpret_cast<T *>(smem + OFF_TK);
   T *sTvT = reinterpret_cast<T *>(smem + OFF_TV);
   uint32_t *sFlag = reinterpret_cast<uint32_t *>(smem + OFF_FLAG);
@@ -448,40 +447,82 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
       }
       __syncthreads();  // B1
       // ---- P2: prefix sums from the chunk start for this sub-chunk's rows
+      // (LDS addresses from a lane id the compiler cannot hoist: kept across the loop they
+      // would be spilled, and a reloaded spill waits for the loads in flight)
+      int ln2 = lane;
+      asm volatile("" : "+v"(ln2));
+      const T *lgrow = sLgT + (ln2 & 15) * LDV + 8 * (ln2 >> 4);
+      const float *tabcol = sTot + 4 * (ln2 >> 4);  // + J * D + 16 ft: C_J of features 16 ft + 4 g4 ..
+      // pc: prefix from the chunk start; the chunk totals (all-ones operand, the same products
+      // as row 15 of sub-chunk 3) decide the references here, before the tables are shared
       float pc[NFT][4];
+      float span_c = 0.f;
+      {
+        Frag<T> ones;
 #pragma unroll
-      for (int ft = 0; ft < NFT; ++ft) {
-        f32x4 cc = mma(load8(sLgT + (16 * ft + r16) * LDV + 8 * g4), tri_c0, f32x4{0.f, 0.f, 0.f, 0.f});
-        cc = mma(load8(sLgT + (16 * ft + r16) * LDV + 32 + 8 * g4), tri_c1, cc);
+        for (int j = 0; j < 8; ++j) ones.v[j] = from_f<T>(1.f);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pc[ft][i] = cc[i];
+        for (int ft = 0; ft < NFT; ++ft) {
+          const Frag<T> a0 = load8(lgrow + 16 * ft * LDV), a1 = load8(lgrow + 16 * ft * LDV + 32);
+          f32x4 cc = mma(a0, tri_c0, f32x4{0.f, 0.f, 0.f, 0.f});
+          cc = mma(a1, tri_c1, cc);
+          f32x4 tt = mma(a0, ones, f32x4{0.f, 0.f, 0.f, 0.f});
+          tt = mma(a1, ones, tt);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pc[ft][i] = cc[i];
+            span_c = fmaxf(span_c, -tt[i]);
+          }
+        }
       }
-      if (r16 == 15 || r16 == 7) {
-        float *dst = (r16 == 15 ? sTot : sP7) + I * D + 4 * g4;
+      const bool mild = wave_max_all(span_c) <= FAST_SPAN;
+      if (r16 == 15) {
 #pragma unroll
         for (int ft = 0; ft < NFT; ++ft)
-          *reinterpret_cast<f32x4 *>(dst + 16 * ft) = f32x4{pc[ft][0], pc[ft][1], pc[ft][2], pc[ft][3]};
+          *reinterpret_cast<f32x4 *>(sTot + I * D + 16 * ft + 4 * g4) = f32x4{pc[ft][0], pc[ft][1], pc[ft][2], pc[ft][3]};
       }
-      // decayed queries with the merge weight, chunk-start reference: mix e^{p_t} phi_q (<= 1
-      // for any gate), in place; a chunk on the sub-chunk references has the query waves
-      // rebuild theirs
+      // decayed queries with the merge weight, in place.  Mild chunk: mix e^{p_t} phi_q
+      // (chunk-start reference).  Otherwise mix e^{p_t - C_{I-1}} phi_q (sub-chunk start, the
+      // prefix inside sub-chunk I from a masked triangle); the query waves apply the factors
+      // between sub-chunks.  Both are at most mix.
+      {
+        float px[NFT][4];
+        if (mild) {
 #pragma unroll
-      for (int js = 0; js < KS; ++js) {
-        T *qp = sQ + (16 * I + r16) * LDQ + 32 * js + 8 * g4;
-        const Frag<T> ph = load8(qp);
-        float x[8];
+          for (int ft = 0; ft < NFT; ++ft)
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int ft = 2 * js + (jj >> 2), i = jj & 3;
-          x[jj] = to_f(ph.v[jj]) * exp2_fast(__builtin_fmaf(pc[ft][i], LOG2E, log2_mix));
+            for (int i = 0; i < 4; ++i) px[ft][i] = pc[ft][i];
+        } else {
+          float x[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int sr = 32 * (I >> 1) + 8 * g4 + j;
+            x[j] = (sr >= 16 * I && sr <= 16 * I + r16) ? 1.f : 0.f;
+          }
+          const Frag<T> tri_sub = frag_from<T>(x);
+#pragma unroll
+          for (int ft = 0; ft < NFT; ++ft) {
+            const f32x4 cc = mma(load8(lgrow + 16 * ft * LDV + 32 * (I >> 1)), tri_sub, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int i = 0; i < 4; ++i) px[ft][i] = cc[i];
+          }
         }
-        *reinterpret_cast<bf16x8 *>(qp) = frag_from<T>(x).v;
+#pragma unroll
+        for (int js = 0; js < KS; ++js) {
+          T *qp = sQ + (16 * I + r16) * LDQ + 32 * js + 8 * g4;
+          const Frag<T> ph = load8(qp);
+          float x[8];
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            const int ft = 2 * js + (jj >> 2), i = jj & 3;
+            x[jj] = to_f(ph.v[jj]) * exp2_fast(__builtin_fmaf(px[ft][i], LOG2E, log2_mix));
+          }
+          *reinterpret_cast<bf16x8 *>(qp) = frag_from<T>(x).v;
+        }
       }
       __syncthreads();  // B2: sub-chunk prefix ends and decayed queries visible; log gamma^T dead
-      const bool mild = chunk_is_mild_c<D>(sTot, lane);
-      // ---- P3: decayed keys -> LDS (interleaved features) and the factor tables.
-      //      Mild: keys carry e^{-p_s}, table e^{B_c}.  Otherwise keys carry e^{C_I - p_s}
-      //      (decay to the sub-chunk end) and the sub-chunk tables.
+      // ---- P3: decayed keys -> LDS (interleaved features).  Mild: keys carry e^{-p_s}.
+      //      Otherwise e^{C_I - p_s} (decay to the sub-chunk end).
       if (mild) {
 #pragma unroll
         for (int ft = 0; ft < NFT; ++ft)
@@ -490,7 +531,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
       } else {
 #pragma unroll
         for (int ft = 0; ft < NFT; ++ft) {
-          const f32x4 t = *reinterpret_cast<const f32x4 *>(sTot + I * D + 16 * ft + 4 * g4);
+          const f32x4 t = *reinterpret_cast<const f32x4 *>(tabcol + I * D + 16 * ft);
 #pragma unroll
           for (int i = 0; i < 4; ++i) ko[ft][i] *= __expf(t[i] - pc[ft][i]);
         }
@@ -500,7 +541,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
         const int fpos = 32 * (ft >> 1) + 8 * g4 + 4 * (ft & 1);
         store4<T>(sKt + (16 * I + r16) * LDW + fpos, ko[ft][0], ko[ft][1], ko[ft][2], ko[ft][3]);
       }
-      __syncthreads();  // B3: decayed keys and tables visible
+      __syncthreads();  // B3: decayed keys visible
       // ---- P4: S = diag(e^{B_c}) S + sum_s k~_s e^{...} v_s^T.  K = 32 steps run over the
       //      interleaved token order of v^T; slot j of lane group g4 is token 32ks + islot(g4, j)
 #pragma unroll
@@ -694,44 +735,17 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
       }
       __syncthreads();  // B2: sub-chunk prefix ends visible
       const bool mild = chunk_is_mild_c<D>(sTot, lane);
-      bool safe = true;  // general case: mid-row reference usable on the diagonal block
+      // general case: the diagonal block on the sub-chunk references needs the log decay across
+      // sub-chunk I, C_{I-1} - C_I, within SPAN_MAX for every feature
+      bool safe = true;
       if (!mild) {
-        // sub-chunk start reference: q~ = mix e^{px_t} phi_q with px the prefix inside the
-        // sub-chunk, rebuilt from q and log gamma in global memory (log gamma^T in LDS is being
-        // overwritten by the decayed keys)
-        Frag<T> qfr[KS];
-        load_q(qfr, c0);
-        float phq[NFT][4];
-        {
-          f32x4 z[NFT];
-          feature_logits<T, D, LDWW>(sW, qfr, r16, g4, z);
-          softmax_rows<NFT>(z, phq);
-        }
-        const Frag<T> tri_pre = tri_frag<T>(r16, g4, true);
         float span = 0.f;
 #pragma unroll
-        for (int ft = 0; ft < NFT; ++ft) {
-          float x[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int t = c0 + 16 * I + 8 * g4 + j;
-            x[j] = (g4 < 2 && t < L) ? to_f(LGh[(size_t)t * D + 16 * ft + r16]) : 0.f;
-          }
-          const f32x4 px = mma(frag_from<T>(x), tri_pre, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            span = fmaxf(span, -px[i]);
-            phq[ft][i] *= exp2_fast(__builtin_fmaf(px[i], LOG2E, log2_mix));
-          }
+        for (int q = 0; q < D / 64; ++q) {
+          const int f = lane + 64 * q;
+          span = fmaxf(span, (I > 0 ? sTot[(I - 1) * D + f] : 0.f) - sTot[I * D + f]);
         }
         safe = wave_max_all(span) <= SPAN_MAX;
-#pragma unroll
-        for (int js = 0; js < KS; ++js) {
-          float x[8];
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) x[jj] = phq[2 * js + (jj >> 2)][jj & 3];
-          qcf[js] = frag_from<T>(x);
-        }
       }
       // sub-chunks whose diagonal block needs the exact products (added after the chunk loop)
       const bool unsafe = !safe;
@@ -794,10 +808,11 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
             for (int dt = 0; dt < NDT; ++dt)
               acc[dt] = mma(load8(sSb + (16 * dt + r16) * LDW + 32 * js + 8 * g4), qcf[js], acc[dt]);
         } else {
-          // Sub-chunk references (rare: a chunk whose log decay exceeds FAST_SPAN).  One key
-          // sub-chunk at a time, register-light: the query operand of K-step js times the tables
-          // e^{tot_J2} of the sub-chunks J2 in [lo, hi)
-          // the query operand of K-step js times prod_{lo <= J2 < hi} e^{tot_J2} = e^{C_{hi-1} - C_{lo-1}}
+          // Sub-chunk references (a chunk whose log decay exceeds FAST_SPAN): queries carry
+          // e^{p_t - C_{I-1}}, keys e^{C_J - p_s}.  Key sub-chunk J < I - 1 meets the factor
+          // e^{C_{I-1} - C_J} <= 1 on the query operand, the diagonal block e^{C_{I-1} - C_I}
+          // (at most e^{SPAN_MAX}) on the key operand, the state e^{C_{I-1}}.
+          // The query operand of K-step js times e^{C_{hi-1} - C_{lo-1}} (C_{-1} = 0)
           auto qscaled = [&](int js, int lo, int hi) {
             float x[8], a8[8], b8[8];
 #pragma unroll
@@ -811,28 +826,25 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
 #pragma unroll 1
           for (int J = 0; J <= I; ++J) {
             f32x4 a = {0.f, 0.f, 0.f, 0.f};
-            if (J < I) {
+            if (J + 1 == I) {
+#pragma unroll
+              for (int js = 0; js < KS; ++js) a = mma(load8(sKt + (16 * J + r16) * LDW + 32 * js + 8 * g4), qcf[js], a);
+            } else if (J < I) {
 #pragma unroll
               for (int js = 0; js < KS; ++js)
                 a = mma(load8(sKt + (16 * J + r16) * LDW + 32 * js + 8 * g4), qscaled(js, J + 1, I), a);
             } else if (safe) {
-              // mid-row reference: (k~ e^{p7 - tot}) . (q e^{-p7})
 #pragma unroll
               for (int js = 0; js < KS; ++js) {
-                // keys carry e^{C_I - p_s}, queries e^{p_t - C_{I-1}}: k e^{P7 - C_I}, q e^{C_{I-1} - P7}
-                float p8[8], c8[8], cp8[8], kv[8], x[8];
+                float c8[8], cp8[8], kv[8];
                 const Frag<T> kk = load8(sKt + (16 * I + r16) * LDW + 32 * js + 8 * g4);
-                tab8(sP7 + I * D, js, g4, p8);
                 tab8(sTot + I * D, js, g4, c8);
 #pragma unroll
                 for (int jj = 0; jj < 8; ++jj) cp8[jj] = 0.f;
                 if (I > 0) tab8(sTot + (I - 1) * D, js, g4, cp8);
 #pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                  kv[jj] = to_f(kk.v[jj]) * __expf(p8[jj] - c8[jj]);
-                  x[jj] = to_f(qcf[js].v[jj]) * __expf(cp8[jj] - p8[jj]);
-                }
-                a = mma(frag_from<T>(kv), frag_from<T>(x), a);
+                for (int jj = 0; jj < 8; ++jj) kv[jj] = to_f(kk.v[jj]) * __expf(cp8[jj] - c8[jj]);
+                a = mma(frag_from<T>(kv), qcf[js], a);
               }
             } else {
               a = f32x4{0.f, 0.f, 0.f, 0.f};  // exact block added after the chunk loop
@@ -855,7 +867,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
           }
 #pragma unroll
           for (int js = 0; js < KS; ++js) {
-            const Frag<T> bf = qscaled(js, 0, I);
+            const Frag<T> bf = I > 0 ? qscaled(js, 0, I) : qcf[js];
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
               acc[dt] = mma(load8(sSb + (16 * dt + r16) * LDW + 32 * js + 8 * g4), bf, acc[dt]);
@@ -867,13 +879,10 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
           for (int dt = 0; dt < NDT; ++dt) store4<T>(O + 16 * dt + 4 * g4, acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
         }
       };
-      if (mild) {
 #pragma unroll
-        for (int js = 0; js < KS; ++js) qcf[js] = load8(sQ + (16 * I + r16) * LDQ + 32 * js + 8 * g4);
-        finish(std::true_type{});
-      } else {
-        finish(std::false_type{});
-      }
+      for (int js = 0; js < KS; ++js) qcf[js] = load8(sQ + (16 * I + r16) * LDQ + 32 * js + 8 * g4);
+      if (mild) finish(std::true_type{});
+      else finish(std::false_type{});
 #pragma unroll
       for (int j = 0; j < KS; ++j) qf[j] = qf_next[j];
     }
@@ -899,7 +908,7 @@ constexpr int ST_OFF_W = 0;
 constexpr int ST_OFF_VT = ST_OFF_W + D * LDW * 2;
 constexpr int ST_OFF_KT = ST_OFF_VT + D * LDV * 2;
 constexpr int ST_OFF_TAB = ST_OFF_KT + SZ_KT;
-constexpr int ST_LDS_BYTES = ST_OFF_TAB + 2 * 4 * D * 4;
+constexpr int ST_LDS_BYTES = ST_OFF_TAB + 4 * D * 4;
 static_assert(2 * ST_LDS_BYTES <= LDS_LIMIT, "state pass: two workgroups per CU");
 }  // namespace full
 
@@ -912,7 +921,6 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
   T *sKt = reinterpret_cast<T *>(smem + ST_OFF_KT);
   T *sLgT = sKt;
   float *sTot = reinterpret_cast<float *>(smem + ST_OFF_TAB);
-  float *sP7 = sTot + 4 * D;
 
   const int tid = threadIdx.x, lane = tid & 63, I = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
@@ -986,11 +994,10 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) pc[ft][i] = cc[i];
     }
-    if (r16 == 15 || r16 == 7) {
-      float *dst = (r16 == 15 ? sTot : sP7) + I * D + 4 * g4;
+    if (r16 == 15) {
 #pragma unroll
       for (int ft = 0; ft < NFT; ++ft)
-        *reinterpret_cast<f32x4 *>(dst + 16 * ft) = f32x4{pc[ft][0], pc[ft][1], pc[ft][2], pc[ft][3]};
+        *reinterpret_cast<f32x4 *>(sTot + I * D + 16 * ft + 4 * g4) = f32x4{pc[ft][0], pc[ft][1], pc[ft][2], pc[ft][3]};
     }
     __syncthreads();
     if (tid < D) dsum += sTot[3 * D + tid];
