@@ -106,7 +106,7 @@ bool use_full_kernel(int Hq, int Hkv, int d, int W, lizard_dtype dtype, const vo
   if (kenv && (strcmp(kenv, "split") == 0 || strcmp(kenv, "4wave") == 0)) return false;
   (void)Hq;
   (void)Hkv;
-  return dtype == LIZARD_BF16 && d == 128 && W <= kChunk + 1 && wq == wk && w_stride == 0;
+  return dtype == LIZARD_BF16 && d == 128 && W <= 2 * kChunk + 1 && wq == wk && w_stride == 0;
 }
 
 // Workspace for either plan (the caller does not say whether W_phi is shared).

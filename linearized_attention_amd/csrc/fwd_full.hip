@@ -180,6 +180,8 @@ __device__ __forceinline__ void exact_diag_fixup(const bf16 *sW, const bf16 *Kh,
   }
 }
 
+// ZW: windows of 66..129 keys, which reach into the chunk two back (window group Z)
+template <bool ZW>
 __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
   using namespace full;
   using T = bf16;
@@ -346,22 +348,24 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
       sTk[m * LDW + e] = (m < p.M) ? Tk[((size_t)kvh * p.M + m) * D + e] : from_f<T>(0.f);
     }
     for (int idx = tid; idx < 4 * FLAG_WORDS; idx += 512) sFlag[idx] = 0u;
-    // previous chunk (history or the end of the previous segment; zeros if none)
-    const int cp0 = (c_begin - 1) * CH;
-    if (key_wave) {
-      Frag<T> kf[KS];
-      load_kfrag(kf, cp0);
-      store_kfrag(kf);
-    } else {
-      Frag<T> vf[2][2];
-      load_vpairs(vf, cp0, tid);
-      store_vpairs(vf, tid);
-    }
   }
+  // The chunks before the first one (history or the end of the previous segment; zeros if
+  // none) are staged by the roles below: keys by the key waves, values by the query waves.
 
   if (key_wave) {
     // ======================================================= key waves
     const int kt = tid - 256;
+    {
+      Frag<T> kf[KS];
+      if constexpr (ZW) {
+        load_kfrag(kf, (c_begin - 2) * CH);
+        store_kfrag(kf);
+        __syncthreads();  // Z0: the chunk two back staged
+        __syncthreads();  // Z1: the query waves' group Z of the first chunk done
+      }
+      load_kfrag(kf, (c_begin - 1) * CH);
+      store_kfrag(kf);
+    }
     // S rows owned: feature tiles 2I, 2I+1; S[ft][dt][i] = S[16(2I+ft) + 4g4 + i][16dt + r16]
     f32x4 S[FTW][NDT];
 #pragma unroll
@@ -596,9 +600,75 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
   } else {
     // ======================================================= query waves
     const float sl2 = p.scale * LOG2E;  // window logits in base 2
-    Frag<T> qf[KS], qf_next[KS];
+    // Window group Z (ZW only): the keys of the chunk two back, tiles I..3, for the queries qz of
+    // the chunk at cz0.  It runs at the top of the chunk before (the chunk two back is then the
+    // previous chunk, still in LDS) and is carried into group X as (az, mz, lz): unnormalised
+    // probabilities times values, the base-2 max per query row, this lane's part of the sum.
+    auto window_z = [&](const Frag<T> (&qz)[KS], int cz0, f32x4 (&az)[NDT], float &mz, float &lz) {
+      const int kminz = max(cz0 + 16 * I + r16 - p.W + 1, -hist_avail);
+      f32x4 lt[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        lt[u] = f32x4{NEG_BIG, NEG_BIG, NEG_BIG, NEG_BIG};
+        if (u >= I) {
+          f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < KS; ++j) a = mma(load8(sK + (16 * u + r16) * LDW + 32 * j + 8 * g4), qz[j], a);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kj = cz0 - 2 * CH + 16 * u + 4 * g4 + i;
+            lt[u][i] = (kj >= kminz) ? a[i] * sl2 : NEG_BIG;
+          }
+        }
+      }
+      float m = -1.0e20f, l = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, lt[u][i]);
+      m = wave_max_cols(m);
+      Frag<T> pp[2];
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        float x[8];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pv = exp2_fast(lt[2 * pr + h][i] - m);  // masked: 0
+            x[4 * h + i] = pv;
+            l += pv;
+          }
+        pp[pr] = frag_from<T>(x);
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr)
+          if (2 * pr + 1 >= I) a = mma(load8(sVt + (16 * dt + r16) * LDV + 32 * pr + 8 * g4), pp[pr], a);
+        az[dt] = a;
+      }
+      mz = m;
+      lz = l;
+    };
+    Frag<T> qf[KS], qf_next[KS], qf_next2[KS];
     Frag<T> vf[2][2];
+    f32x4 accz[NDT];
+    float m_z = -1.0e20f, l_z = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) accz[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     load_q(qf, c_begin * CH);
+    if constexpr (ZW) {
+      load_vpairs(vf, (c_begin - 2) * CH, tid);
+      store_vpairs(vf, tid);
+      __syncthreads();  // Z0
+      window_z(qf, c_begin * CH, accz, m_z, l_z);
+      __syncthreads();  // Z1
+      load_q(qf_next, (c_begin + 1) * CH);
+    }
+    load_vpairs(vf, (c_begin - 1) * CH, tid);
+    store_vpairs(vf, tid);
     load_vpairs(vf, c_begin * CH, tid);
     bool unsafe_seen = false;
     __syncthreads();  // P
@@ -608,14 +678,15 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
       const int pos = c0 + 16 * I + r16;  // query row of this lane's column
       const bool valid = pos < L;
       // lowest key index the window of this row may use
-      const int kmin = max(pos - p.W + 1, c == 0 ? -hist_avail : INT32_MIN / 2);
+      const int kmin = max(pos - p.W + 1, -hist_avail);
 
-      // ---- P0: window group X (meta tokens and the previous chunk's keys I..3, still in
-      //      LDS) in base-2 logits; unnormalised probabilities times values into acc
+      // ---- P0: window group X (meta tokens and the previous chunk's keys, still in LDS: tiles
+      //      I..3, all four with ZW) in base-2 logits, merged with group Z; unnormalised
+      //      probabilities times values into acc.  Then (ZW) group Z of the next chunk.
       f32x4 acc[NDT];
-      float m_x = -1.0e20f, l_run = 0.f;
+      float m_x = m_z, l_run = 0.f;
       {
-        f32x4 lt[5];  // 0: meta; 1 + u: previous-chunk tile u (u >= I)
+        f32x4 lt[5];  // 0: meta; 1 + u: previous-chunk tile u
         {
           f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -626,7 +697,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           lt[1 + u] = f32x4{NEG_BIG, NEG_BIG, NEG_BIG, NEG_BIG};
-          if (u >= I) {
+          if (ZW || u >= I) {
             f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < KS; ++j) a = mma(load8(sK + (16 * u + r16) * LDW + 32 * j + 8 * g4), qf[j], a);
@@ -642,6 +713,8 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) m_x = fmaxf(m_x, lt[u][i]);
         m_x = wave_max_cols(m_x);
+        const float alpha_z = exp2_fast(m_z - m_x);  // group Z rescaled to the joint max
+        l_run = l_z * alpha_z;
         Frag<T> pm, pp[2];
         {
           float x[8];
@@ -670,12 +743,20 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
         for (int dt = 0; dt < NDT; ++dt) {
           const int dvl = 16 * dt + r16;
           const T *tv = sTvT + dvl * LDM + 4 * g4;
-          f32x4 a = mma(load4x2(tv, tv), pm, f32x4{0.f, 0.f, 0.f, 0.f});  // slots 4..7 meet P = 0
+          f32x4 a0 = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (ZW) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a0[i] = accz[dt][i] * alpha_z;
+          }
+          f32x4 a = mma(load4x2(tv, tv), pm, a0);  // slots 4..7 meet P = 0
 #pragma unroll
           for (int pr = 0; pr < 2; ++pr)
-            if (2 * pr + 1 >= I) a = mma(load8(sVt + dvl * LDV + 32 * pr + 8 * g4), pp[pr], a);
+            if (ZW || 2 * pr + 1 >= I) a = mma(load8(sVt + dvl * LDV + 32 * pr + 8 * g4), pp[pr], a);
           acc[dt] = a;
         }
+      }
+      if constexpr (ZW) {
+        if (c + 1 < c_end) window_z(qf_next, c0 + CH, accz, m_z, l_z);
       }
       __syncthreads();  // B0
       // ---- P1: stage this chunk's values
@@ -757,7 +838,8 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
         int ln = lane;
         asm volatile("" : "+v"(ln));
         pairs_in(vf, Vh, c0 + CH, ln + 64 * wv);
-        q_in(qf_next, c0 + CH, ln);
+        if constexpr (ZW) q_in(qf_next2, c0 + 2 * CH, ln);
+        else q_in(qf_next, c0 + CH, ln);
       }
       // ---- P3: window output normalised and scaled for the merge
       {
@@ -884,7 +966,10 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
       if (mild) finish(std::true_type{});
       else finish(std::false_type{});
 #pragma unroll
-      for (int j = 0; j < KS; ++j) qf[j] = qf_next[j];
+      for (int j = 0; j < KS; ++j) {
+        qf[j] = qf_next[j];
+        if constexpr (ZW) qf_next[j] = qf_next2[j];
+      }
     }
     // Exact diagonal blocks of this wave's flagged sub-chunks, added to the rows it stored
     // (few registers are live after the loop)
@@ -1076,10 +1161,13 @@ hipError_t launch_fwd_full(const FwdParams &p, hipStream_t stream) {
                        stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  e = hipFuncSetAttribute(reinterpret_cast<const void *>(fwd_full_kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, full::LDS_BYTES);
+  const void *kern = p.W > CH + 1 ? reinterpret_cast<const void *>(fwd_full_kernel<true>)
+                                  : reinterpret_cast<const void *>(fwd_full_kernel<false>);
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, full::LDS_BYTES);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fwd_full_kernel, dim3(((p.ngroups + 7) / 8) * 8 * p.G), dim3(512), full::LDS_BYTES, stream, p);
+  const dim3 grid(((p.ngroups + 7) / 8) * 8 * p.G);
+  if (p.W > CH + 1) hipLaunchKernelGGL(fwd_full_kernel<true>, grid, dim3(512), full::LDS_BYTES, stream, p);
+  else hipLaunchKernelGGL(fwd_full_kernel<false>, grid, dim3(512), full::LDS_BYTES, stream, p);
   return hipGetLastError();
 }
 

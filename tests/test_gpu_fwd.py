@@ -148,7 +148,7 @@ def test_fwd_sequence_segments(gpu_lib, monkeypatch, nseg):
 
 @pytest.mark.parametrize("nseg", [1, 2, 3, 5])
 def test_fwd_whole_head_segments(gpu_lib, monkeypatch, nseg):
-    """The whole-head kernel (bf16, d = 128, one query head per key/value head, W <= 65) over
+    """The whole-head kernel (bf16, d = 128, one W_phi for queries and keys) over
     sequence segments joined through its state pass: a gate that mixes both decay
     references with a ragged tail, and gamma = 0 (exact diagonal blocks from the fixup
     kernel) across segment boundaries."""
@@ -158,6 +158,25 @@ def test_fwd_whole_head_segments(gpu_lib, monkeypatch, nseg):
     check_case(f"bf16 whole-head {nseg} segments, mixed references", inp, "bf16")
     inp = make_fwd_inputs(B=2, Hq=1, Hkv=1, L=300, d=128, W=64, M=4, dtype="bf16", seed=95 + nseg, gate="zero")
     check_case(f"bf16 whole-head {nseg} segments, gamma=0", inp, "bf16")
+
+
+WIDE = [
+    ("W66 M1 ragged, mixed references", dict(B=1, Hq=2, Hkv=2, L=300, d=128, W=66, M=1, gate="uniform:-1.6"), 1),
+    ("W100 M8 gqa 4:2", dict(B=2, Hq=4, Hkv=2, L=400, d=128, W=100, M=8), 1),
+    ("W128 M8 uniform gate, 3 segments", dict(B=1, Hq=2, Hkv=2, L=650, d=128, W=128, M=8, gate="uniform"), 3),
+    ("W129 M16 ragged, 2 segments", dict(B=2, Hq=1, Hkv=1, L=201, d=128, W=129, M=16), 2),
+    ("W128 M0 L100 (full causal softmax)", dict(B=1, Hq=2, Hkv=2, L=100, d=128, W=128, M=0), 1),
+    ("W128 gamma=0 (exact diag)", dict(B=1, Hq=2, Hkv=2, L=260, d=128, W=128, M=4, gate="zero"), 2),
+]
+
+
+@pytest.mark.parametrize("label,kw,nseg", WIDE, ids=[c[0] for c in WIDE])
+def test_fwd_whole_head_wide_window(gpu_lib, monkeypatch, label, kw, nseg):
+    """The whole-head kernel with windows of 66..129 keys: the window reaches into the chunk
+    two back (computed one chunk early and carried), with segments and grouped heads."""
+    monkeypatch.setenv("LIZARD_FWD_SEGMENTS", str(nseg))
+    inp = make_fwd_inputs(dtype="bf16", seed=zlib.crc32(label.encode()) % 10000, **kw)
+    check_case(f"bf16 whole-head {label}", inp, "bf16")
 
 
 @pytest.mark.parametrize("label", ["bf16 d128 ragged L200", "bf16 gamma=0 (exact diag)", "bf16 gamma=1"])

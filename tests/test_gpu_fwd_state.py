@@ -49,6 +49,10 @@ CASES = [
     ("fp32 d64 W200 split 190 (history past the rings)", dict(B=1, Hq=1, Hkv=1, L=400, d=64, W=200, M=3),
      190, "f32"),
     ("bf16 gqa 4:2 split 100", dict(B=1, Hq=4, Hkv=2, L=260, d=128, W=64, M=4), 100, "bf16"),
+    ("bf16 d128 W128 split 150 (window two chunks back)", dict(B=1, Hq=2, Hkv=2, L=330, d=128, W=128, M=8),
+     150, "bf16"),
+    ("bf16 d128 W100 split 40 (history shorter than the window)",
+     dict(B=1, Hq=2, Hkv=2, L=230, d=128, W=100, M=4, gate="uniform:-1"), 40, "bf16"),
     ("fp32 d64 uniform gate split 70", dict(B=1, Hq=2, Hkv=2, L=250, d=64, W=64, M=4, gate="uniform"), 70, "f32"),
 ]
 
