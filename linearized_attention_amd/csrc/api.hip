@@ -98,7 +98,7 @@ FwdPlan make_plan(int B, int Hq, int Hkv, int L, int d, int W, bool full) {
 size_t plan_bytes(const FwdPlan &p) { return p.ws_state_bytes + p.ws_decay_bytes; }
 
 // The whole-head kernel serves bf16 at d = 128 with one W_phi for queries and keys
-// (any grouping of query heads) and W <= 65 (LIZARD_FWD_KERNEL=split or 4wave
+// (any grouping of query heads) and W <= 129 (LIZARD_FWD_KERNEL=split or 4wave
 // selects the value-block kernels instead, for tests and A/B timing).
 bool use_full_kernel(int Hq, int Hkv, int d, int W, lizard_dtype dtype, const void *wq, const void *wk,
                      int64_t w_stride) {

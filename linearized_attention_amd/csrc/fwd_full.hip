@@ -1,4 +1,4 @@
-// Lizard attention forward, whole-head variant (bf16, d = 128, window W <= 65, one
+// Lizard attention forward, whole-head variant (bf16, d = 128, window W <= 129, one
 // W_phi for queries and keys): one workgroup per (batch, query head, sequence
 // segment) computes all 128 value columns, so the feature maps, the gate sums,
 // the window logits and the intra-chunk scores are computed once per head
@@ -14,19 +14,22 @@
 //
 //   key waves (4..7), sub-chunk I = wave - 4: stage the chunk's keys (in MFMA
 //     fragment order, straight from the loads) and log gamma^T; gate prefix
-//     sums; phi_k and the decayed keys; the per-chunk factor tables; the state
-//     update for feature rows 32I..32I+31 of S (fp32 registers, all 128 value
-//     columns) and the bf16 copy of S^T that the query waves read.
-//   query waves (0..3), sub-chunk I = wave: stage v^T; phi_q; the window; the
-//     intra- and inter-chunk products, the merge and the stores for rows
-//     16I..16I+15 and all 128 value columns.
+//     sums and the choice of decay references; phi_k and phi_q (one pass over
+//     the W_phi^T fragments) and their decayed forms; the state update for
+//     feature rows 32I..32I+31 of S (fp32 registers, all 128 value columns) and
+//     the bf16 copy of S^T that the query waves read.
+//   query waves (0..3), sub-chunk I = wave: stage v^T; the window; the intra-
+//     and inter-chunk products, the merge and the stores for rows 16I..16I+15
+//     and all 128 value columns.
 //
 // Only the current chunk's keys and values are in LDS (a second chunk would not
-// fit next to W_phi^T and the state copy).  The window of a query row reaches
-// back at most 64 keys, i.e. into the previous chunk, so it is split in two
+// fit next to W_phi^T and the state copy).  The window of a query row is split in
 // groups combined by an online softmax: the meta tokens and the previous chunk's
 // keys (group X, computed at the top of the chunk while the previous chunk is
-// still in LDS), and the current chunk's keys (group Y).
+// still in LDS), and the current chunk's keys (group Y).  A window of more than
+// 65 keys also reaches into the chunk two back (group Z): that part is computed
+// at the top of the previous chunk, when the chunk two back is the one in LDS,
+// for the next chunk's queries, and carried in registers as a partial softmax.
 //
 // Operand layouts: within every 32-element group along a contraction, element
 // e = 16h + 4q + i is stored at position 8q + 4h + i ("interleaved").  An MFMA

@@ -83,12 +83,18 @@ def test_fwd_workspace_required_when_segmented():
 
 def test_workspace_bytes_matches_plan_formula():
     lib = api.load()
-    # B*Hkv*ndvb = 64 groups -> 4 segments of 512/4 = 128 chunks each
     B, Hkv, L, d = 1, 32, 32768, 128
     got = lib.lizard_attn_fwd_workspace_bytes(B, Hkv, Hkv, L, d, 128, 1)
+    # value-block plan: B*Hkv*ndvb = 64 groups -> 4 segments of 128 chunks, end states per
+    # 64-column block
     nseg = 4
-    want = B * Hkv * 2 * (nseg - 1) * d * 64 * 4 + B * Hkv * (nseg - 1) * d * 4
-    assert got == want
+    split = B * Hkv * 2 * (nseg - 1) * d * 64 * 4 + B * Hkv * (nseg - 1) * d * 4
+    # whole-head plan (bf16, d = 128, W <= 129): B*Hq = 32 blocks -> 8 segments of 64 chunks;
+    # the state pass in 512 // (32 * 7) = 2 pieces per segment, full d x d states
+    nseg, sss = 8, 2
+    pieces = B * Hkv * (nseg - 1) * sss
+    full = pieces * d * d * 4 + -(-pieces * d * 4 // 256) * 256
+    assert got == max(split, full)
 
 
 def _dec(lib, **kw):
