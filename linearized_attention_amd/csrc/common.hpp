@@ -37,6 +37,9 @@ __device__ __forceinline__ f32x4 mma(const Frag<float> &a, const Frag<float> &b,
 // exp2(fma(x, LOG2E, c)) so the base change costs no separate multiply.
 constexpr float LOG2E = 1.4426950408889634f;
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+// Materialise a value at this point (an empty asm that reads and writes it).  Used before a
+// barrier to keep the compiler from sinking arithmetic into the next phase.
+__device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
 
 __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f(float x) { return x; }

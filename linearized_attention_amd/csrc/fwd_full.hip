@@ -435,6 +435,15 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
         softmax_rows<NFT>(z, ko);
         softmax_rows<NFT>(zq, qo);
       }
+      // finish the feature maps here: left to itself the compiler sinks the softmax past the
+      // barrier into the next phase, where the query waves have nothing to do
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pin(ko[ft][i]);
+          pin(qo[ft][i]);
+        }
       __syncthreads();  // B0: the previous chunk's LDS is dead
       // ---- P1: stage this chunk's keys, log gamma^T and phi_q; publish S_c; next chunk in flight
       store_kfrag(kf);
