@@ -183,6 +183,34 @@ __device__ __forceinline__ void exact_diag_fixup(const bf16 *sW, const bf16 *Kh,
   }
 }
 
+// Feature logits of two row sets (keys and queries) against W_phi^T in LDS, with the W_phi^T
+// fragments of feature tile ft + 1 loaded while tile ft is multiplied (the compiler otherwise
+// waits for each fragment right before its products).
+__device__ __forceinline__ void feature_logits2_pipe(const bf16 *sW, const Frag<bf16> (&xa)[full::KS],
+                                                     const Frag<bf16> (&xb)[full::KS], int r16, int g4,
+                                                     f32x4 (&za)[full::NFT], f32x4 (&zb)[full::NFT]) {
+  using namespace full;
+  const bf16 *wrow = sW + r16 * LDWW + 8 * g4;
+  Frag<bf16> w[2][KS];
+#pragma unroll
+  for (int j = 0; j < KS; ++j) w[0][j] = load8(wrow + 32 * j);
+#pragma unroll
+  for (int ft = 0; ft < NFT; ++ft) {
+    if (ft + 1 < NFT) {
+#pragma unroll
+      for (int j = 0; j < KS; ++j) w[(ft + 1) & 1][j] = load8(wrow + 16 * (ft + 1) * LDWW + 32 * j);
+    }
+    f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      a = mma(w[ft & 1][j], xa[j], a);
+      b = mma(w[ft & 1][j], xb[j], b);
+    }
+    za[ft] = a;
+    zb[ft] = b;
+  }
+}
+
 // ZW: windows of 66..129 keys, which reach into the chunk two back (window group Z)
 template <bool ZW>
 __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
@@ -431,7 +459,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
       float ko[NFT][4], qo[NFT][4];
       {
         f32x4 z[NFT], zq[NFT];
-        feature_logits2<T, D, LDWW>(sW, kf, qf, r16, g4, z, zq);
+        feature_logits2_pipe(sW, kf, qf, r16, g4, z, zq);
         softmax_rows<NFT>(z, ko);
         softmax_rows<NFT>(zq, qo);
       }
@@ -560,38 +588,49 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
       __syncthreads();  // B3: decayed keys visible
       // ---- P4: S = diag(e^{B_c}) S + sum_s k~_s e^{...} v_s^T.  K = 32 steps run over the
       //      interleaved token order of v^T; slot j of lane group g4 is token 32ks + islot(g4, j)
+      {
+        Frag<T> ka[FTW][2];  // [ft][ks]: decayed keys^T of feature tile 2I + ft, tokens of K-step ks
+        float e[FTW][4];     // row decay e^{B_c} = e^{C_3}
 #pragma unroll
-      for (int ft = 0; ft < FTW; ++ft) {
-        const int fr = 16 * (2 * I + ft);
-        const int fcol = 32 * I + ipos(16 * ft + r16);  // interleaved position of feature fr + r16
-        // row decay e^{B_c} = e^{C_3}; key factors e^{C_3} (mild: keys carry e^{-p_s}) or
-        // e^{C_3 - C_J} (keys carry e^{C_J - p_s})
-        float e[4];
-        float fac[2][2];  // [ks][half]: factor of the keys of sub-chunk 2ks + half
-        {
+        for (int ft = 0; ft < FTW; ++ft) {
+          const int fr = 16 * (2 * I + ft);
+          const int fcol = 32 * I + ipos(16 * ft + r16);  // interleaved position of feature fr + r16
+          // key factors e^{C_3} (mild: keys carry e^{-p_s}) or e^{C_3 - C_J} (keys carry e^{C_J - p_s})
+          float fac[2][2];  // [ks][half]: factor of the keys of sub-chunk 2ks + half
           const f32x4 c3 = *reinterpret_cast<const f32x4 *>(sTot + 3 * D + fr + 4 * g4);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) e[i] = __expf(c3[i]);
+          for (int i = 0; i < 4; ++i) e[ft][i] = __expf(c3[i]);
           const float c3r = sTot[3 * D + fr + r16];
 #pragma unroll
           for (int J = 0; J < 4; ++J) fac[J >> 1][J & 1] = __expf(mild ? c3r : c3r - sTot[J * D + fr + r16]);
-        }
-        Frag<T> ka[2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          float x[8];
+          for (int ks = 0; ks < 2; ++ks) {
+            float x[8];
 #pragma unroll
-          for (int jj = 0; jj < 8; ++jj)
-            x[jj] = to_f(sKt[(32 * ks + islot(g4, jj)) * LDW + fcol]) * fac[ks][jj >> 2];
-          ka[ks] = frag_from<T>(x);
+            for (int jj = 0; jj < 8; ++jj)
+              x[jj] = to_f(sKt[(32 * ks + islot(g4, jj)) * LDW + fcol]) * fac[ks][jj >> 2];
+            ka[ft][ks] = frag_from<T>(x);
+          }
         }
+        // each v^T fragment serves both feature tiles; the next value tile's fragments are
+        // loaded while this one is multiplied
+        const T *vrow = sVt + r16 * LDV + 8 * g4;
+        Frag<T> vb[2][2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) vb[0][ks] = load8(vrow + 32 * ks);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
+          if (dt + 1 < NDT) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) S[ft][dt][i] *= e[i];
+            for (int ks = 0; ks < 2; ++ks) vb[(dt + 1) & 1][ks] = load8(vrow + 16 * (dt + 1) * LDV + 32 * ks);
+          }
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-            S[ft][dt] = mma(ka[ks], load8(sVt + (16 * dt + r16) * LDV + 32 * ks + 8 * g4), S[ft][dt]);
+          for (int ft = 0; ft < FTW; ++ft) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[ft][dt][i] *= e[ft][i];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) S[ft][dt] = mma(ka[ft][ks], vb[dt & 1][ks], S[ft][dt]);
+          }
         }
       }
 #pragma unroll
@@ -863,6 +902,24 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
       }
       __syncthreads();  // B3: decayed keys and tables visible
       // ---- P4: intra- and inter-chunk products onto the window output, store
+      // Y^T += S^T qop^T over the 32 S^T fragments, four loaded ahead of their products
+      auto inter = [&](const Frag<T> (&qop)[KS]) {
+        const T *srow = sSb + r16 * LDW + 8 * g4;
+        Frag<T> sb[2][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sb[0][u] = load8(srow + 16 * u * LDW);
+#pragma unroll
+        for (int st = 0; st < 2 * KS; ++st) {  // step st: K-step st / 2, value tiles 4 (st % 2) ..
+          if (st + 1 < 2 * KS) {
+            const int js1 = (st + 1) >> 1, dh1 = (st + 1) & 1;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) sb[(st + 1) & 1][u] = load8(srow + 16 * (4 * dh1 + u) * LDW + 32 * js1);
+          }
+          const int js = st >> 1, dh = st & 1;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[4 * dh + u] = mma(sb[st & 1][u], qop[js], acc[4 * dh + u]);
+        }
+      };
       auto finish = [&](auto mild_tag) {
         constexpr bool MILD = decltype(mild_tag)::value;
         if constexpr (MILD) {
@@ -896,11 +953,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
             }
           }
           // Y^T += S^T q~^T (state at the chunk start; interleaved features)
-#pragma unroll
-          for (int js = 0; js < KS; ++js)
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-              acc[dt] = mma(load8(sSb + (16 * dt + r16) * LDW + 32 * js + 8 * g4), qcf[js], acc[dt]);
+          inter(qcf);
         } else {
           // Sub-chunk references (a chunk whose log decay exceeds FAST_SPAN): queries carry
           // e^{p_t - C_{I-1}}, keys e^{C_J - p_s}.  Key sub-chunk J < I - 1 meets the factor
