@@ -183,12 +183,11 @@ __device__ __forceinline__ void exact_diag_fixup(const bf16 *sW, const bf16 *Kh,
   }
 }
 
-// Feature logits of two row sets (keys and queries) against W_phi^T in LDS, with the W_phi^T
-// fragments of feature tile ft + 1 loaded while tile ft is multiplied (the compiler otherwise
-// waits for each fragment right before its products).
-__device__ __forceinline__ void feature_logits2_pipe(const bf16 *sW, const Frag<bf16> (&xa)[full::KS],
-                                                     const Frag<bf16> (&xb)[full::KS], int r16, int g4,
-                                                     f32x4 (&za)[full::NFT], f32x4 (&zb)[full::NFT]) {
+// Feature logits of the wave's 16 rows against W_phi^T in LDS, with the W_phi^T fragments of
+// feature tile ft + 1 loaded while tile ft is multiplied (the compiler otherwise waits for each
+// fragment right before its products).
+__device__ __forceinline__ void feature_logits_pipe(const bf16 *sW, const Frag<bf16> (&xa)[full::KS], int r16, int g4,
+                                                    f32x4 (&za)[full::NFT]) {
   using namespace full;
   const bf16 *wrow = sW + r16 * LDWW + 8 * g4;
   Frag<bf16> w[2][KS];
@@ -200,14 +199,10 @@ __device__ __forceinline__ void feature_logits2_pipe(const bf16 *sW, const Frag<
 #pragma unroll
       for (int j = 0; j < KS; ++j) w[(ft + 1) & 1][j] = load8(wrow + 16 * (ft + 1) * LDWW + 32 * j);
     }
-    f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < KS; ++j) {
-      a = mma(w[ft & 1][j], xa[j], a);
-      b = mma(w[ft & 1][j], xb[j], b);
-    }
+    for (int j = 0; j < KS; ++j) a = mma(w[ft & 1][j], xa[j], a);
     za[ft] = a;
-    zb[ft] = b;
   }
 }
 
@@ -433,10 +428,9 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
       }
     }
     const Frag<T> tri_c0 = tri64_frag<T>(r16, g4, I, 0), tri_c1 = tri64_frag<T>(r16, g4, I, 1);
-    Frag<T> kf[KS], kf_next[KS], qf[KS], qf_next[KS];
+    Frag<T> kf[KS], kf_next[KS];
     Frag<T> lf[2][2];
     load_kfrag(kf, c_begin * CH);
-    load_q(qf, c_begin * CH);
     load_lgpairs(lf, c_begin * CH, kt);
     // S^T copy of the start state
     auto publish = [&]() {
@@ -453,40 +447,30 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
 
     for (int c = c_begin; c < c_end; ++c) {
       const int c0 = c * CH;
-      // ---- P0: phi_k and phi_q of this chunk's rows (keys and queries from registers, each
-      //      W_phi^T fragment read once for both); the query waves read the previous chunk's
-      //      keys and values from LDS meanwhile
-      float ko[NFT][4], qo[NFT][4];
+      // ---- P0: phi_k of this chunk's rows (keys from registers); the query waves read the
+      //      previous chunk's keys and values from LDS meanwhile
+      float ko[NFT][4];
       {
-        f32x4 z[NFT], zq[NFT];
-        feature_logits2_pipe(sW, kf, qf, r16, g4, z, zq);
+        f32x4 z[NFT];
+        feature_logits_pipe(sW, kf, r16, g4, z);
         softmax_rows<NFT>(z, ko);
-        softmax_rows<NFT>(zq, qo);
       }
-      // finish the feature maps here: left to itself the compiler sinks the softmax past the
-      // barrier into the next phase, where the query waves have nothing to do
+      // finish the feature map here: left to itself the compiler sinks the softmax past the
+      // barrier into the next phase
 #pragma unroll
       for (int ft = 0; ft < NFT; ++ft)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pin(ko[ft][i]);
-          pin(qo[ft][i]);
-        }
+        for (int i = 0; i < 4; ++i) pin(ko[ft][i]);
       __syncthreads();  // B0: the previous chunk's LDS is dead
-      // ---- P1: stage this chunk's keys, log gamma^T and phi_q; publish S_c; next chunk in flight
+      // ---- P1: stage this chunk's keys and log gamma^T; publish S_c; next chunk in flight (the
+      //      query waves compute phi_q meanwhile)
       store_kfrag(kf);
       store_lgpairs(lf, kt);
-#pragma unroll
-      for (int ft = 0; ft < NFT; ++ft) {  // phi_q, decayed in P2 (interleaved features)
-        const int fpos = 32 * (ft >> 1) + 8 * g4 + 4 * (ft & 1);
-        store4<T>(sQ + (16 * I + r16) * LDQ + fpos, qo[ft][0], qo[ft][1], qo[ft][2], qo[ft][3]);
-      }
       if (c > c_begin) publish();
       if (c + 1 < c_end) {
         int ln = lane;
         asm volatile("" : "+v"(ln));
         kfrag_in(kf_next, c0 + CH, ln);
-        q_in(qf_next, c0 + CH, ln);
         pairs_in(lf, LGh, c0 + CH, ln + 64 * (wv - 4));
       }
       __syncthreads();  // B1
@@ -634,10 +618,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
         }
       }
 #pragma unroll
-      for (int j = 0; j < KS; ++j) {
-        kf[j] = kf_next[j];
-        qf[j] = qf_next[j];
-      }
+      for (int j = 0; j < KS; ++j) kf[j] = kf_next[j];
     }
     if (p.state_out && seg == p.nseg - 1 && g == 0) {
       float *So = p.state_out + ((size_t)b * p.Hkv + kvh) * D * D;
@@ -810,8 +791,22 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
         if (c + 1 < c_end) window_z(qf_next, c0 + CH, accz, m_z, l_z);
       }
       __syncthreads();  // B0
-      // ---- P1: stage this chunk's values
+      // ---- P1: stage this chunk's values; phi_q of this wave's rows into LDS (the key waves
+      //      decay it in place)
       store_vpairs(vf, tid);
+      {
+        f32x4 zq[NFT];
+        float qo[NFT][4];
+        // (the wide-window variant carries group Z through here: no registers for prefetching)
+        if constexpr (ZW) feature_logits<T, D, LDWW>(sW, qf, r16, g4, zq);
+        else feature_logits_pipe(sW, qf, r16, g4, zq);
+        softmax_rows<NFT>(zq, qo);
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft) {  // interleaved features
+          const int fpos = 32 * (ft >> 1) + 8 * g4 + 4 * (ft & 1);
+          store4<T>(sQ + (16 * I + r16) * LDQ + fpos, qo[ft][0], qo[ft][1], qo[ft][2], qo[ft][3]);
+        }
+      }
       __syncthreads();  // B1
       // ---- P2: window group Y (this chunk's keys 0..I); the key waves compute the decayed queries
       Frag<T> qcf[KS];  // query operand of the intra and inter products (f-interleaved K = 32 slices)
