@@ -14,13 +14,13 @@
 //
 //   key waves (4..7), sub-chunk I = wave - 4: stage the chunk's keys (in MFMA
 //     fragment order, straight from the loads) and log gamma^T; gate prefix
-//     sums and the choice of decay references; phi_k and phi_q (one pass over
-//     the W_phi^T fragments) and their decayed forms; the state update for
-//     feature rows 32I..32I+31 of S (fp32 registers, all 128 value columns) and
-//     the bf16 copy of S^T that the query waves read.
-//   query waves (0..3), sub-chunk I = wave: stage v^T; the window; the intra-
-//     and inter-chunk products, the merge and the stores for rows 16I..16I+15
-//     and all 128 value columns.
+//     sums and the choice of decay references; phi_k and the decayed keys; the
+//     decay of phi_q in LDS; the state update for feature rows 32I..32I+31 of S
+//     (fp32 registers, all 128 value columns) and the bf16 copy of S^T that the
+//     query waves read.
+//   query waves (0..3), sub-chunk I = wave: stage v^T; phi_q (while the key
+//     waves stage); the window; the intra- and inter-chunk products, the merge
+//     and the stores for rows 16I..16I+15 and all 128 value columns.
 //
 // Only the current chunk's keys and values are in LDS (a second chunk would not
 // fit next to W_phi^T and the state copy).  The window of a query row is split in
