@@ -1050,7 +1050,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
 // with the arithmetic of the key waves above; 80 KB of LDS, so two workgroups share a CU.
 namespace full {
 constexpr int ST_OFF_W = 0;
-constexpr int ST_OFF_VT = ST_OFF_W + D * LDW * 2;
+constexpr int ST_OFF_VT = ST_OFF_W + D * LDWW * 2;
 constexpr int ST_OFF_KT = ST_OFF_VT + D * LDV * 2;
 constexpr int ST_OFF_TAB = ST_OFF_KT + SZ_KT;
 constexpr int ST_LDS_BYTES = ST_OFF_TAB + 4 * D * 4;
@@ -1081,7 +1081,7 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
   const T *Vh = reinterpret_cast<const T *>(p.v) + kv_off;
   const T *LGh = reinterpret_cast<const T *>(p.lg) + kv_off;
 
-  load_wT<T, D, LDW, 256>(sW, reinterpret_cast<const T *>(p.wk), tid);
+  load_wT<T, D, LDWW, 256>(sW, reinterpret_cast<const T *>(p.wk), tid);
   auto load_k = [&](Frag<T> (&kf)[KS], int c0) {
     const T *src = Kh + (size_t)(c0 + 16 * I + r16) * D;
 #pragma unroll
@@ -1112,7 +1112,7 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
     float ko[NFT][4];
     {
       f32x4 z[NFT];
-      feature_logits<T, D, LDW>(sW, kf, r16, g4, z);
+      feature_logits_pipe(sW, kf, r16, g4, z);
       softmax_rows<NFT>(z, ko);
     }
     {
@@ -1167,37 +1167,46 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
     }
     __syncthreads();
     // S = diag(e^{C_3}) S + sum_s k~_s e^{...} v_s^T (factors from the prefix table)
+    {
+      Frag<T> ka[FTW][2];
+      float e[FTW][4];
 #pragma unroll
-    for (int ft = 0; ft < FTW; ++ft) {
-      const int fr = 16 * (2 * I + ft);
-      const int fcol = 32 * I + ipos(16 * ft + r16);
-      const f32x4 c3 = *reinterpret_cast<const f32x4 *>(sTot + 3 * D + fr + 4 * g4);
-      float e[4];
+      for (int ft = 0; ft < FTW; ++ft) {
+        const int fr = 16 * (2 * I + ft);
+        const int fcol = 32 * I + ipos(16 * ft + r16);
+        const f32x4 c3 = *reinterpret_cast<const f32x4 *>(sTot + 3 * D + fr + 4 * g4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) e[i] = __expf(c3[i]);
-      float fac[2][2];
-      const float c3r = sTot[3 * D + fr + r16];
-      if (mild) {
-        fac[0][0] = fac[0][1] = fac[1][0] = fac[1][1] = __expf(c3r);
-      } else {
+        for (int i = 0; i < 4; ++i) e[ft][i] = __expf(c3[i]);
+        float fac[2][2];
+        const float c3r = sTot[3 * D + fr + r16];
 #pragma unroll
-        for (int J = 0; J < 4; ++J) fac[J >> 1][J & 1] = __expf(c3r - sTot[J * D + fr + r16]);
+        for (int J = 0; J < 4; ++J) fac[J >> 1][J & 1] = __expf(mild ? c3r : c3r - sTot[J * D + fr + r16]);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          float x[8];
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) x[jj] = to_f(sKt[(32 * ks + islot(g4, jj)) * LDW + fcol]) * fac[ks][jj >> 2];
+          ka[ft][ks] = frag_from<T>(x);
+        }
       }
-      Frag<T> ka[2];
+      // each v^T fragment serves both feature tiles; the next value tile's are loaded ahead
+      const T *vrow = sVt + r16 * LDV + 8 * g4;
+      Frag<T> vb[2][2];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        float x[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) x[jj] = to_f(sKt[(32 * ks + islot(g4, jj)) * LDW + fcol]) * fac[ks][jj >> 2];
-        ka[ks] = frag_from<T>(x);
-      }
+      for (int ks = 0; ks < 2; ++ks) vb[0][ks] = load8(vrow + 32 * ks);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
+        if (dt + 1 < NDT) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[ft][dt][i] *= e[i];
+          for (int ks = 0; ks < 2; ++ks) vb[(dt + 1) & 1][ks] = load8(vrow + 16 * (dt + 1) * LDV + 32 * ks);
+        }
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          S[ft][dt] = mma(ka[ks], load8(sVt + (16 * dt + r16) * LDV + 32 * ks + 8 * g4), S[ft][dt]);
+        for (int ft = 0; ft < FTW; ++ft) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S[ft][dt][i] *= e[ft][i];
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) S[ft][dt] = mma(ka[ft][ks], vb[dt & 1][ks], S[ft][dt]);
+        }
       }
     }
     __syncthreads();
