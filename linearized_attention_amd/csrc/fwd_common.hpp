@@ -14,6 +14,8 @@ constexpr float SPAN_MAX = 80.f;  // max |log-decay| across one 16-token sub-chu
 constexpr float NEG_BIG = -1.0e30f;
 constexpr float FAST_SPAN = 60.f; // max |log-decay| across a whole chunk for the chunk-start
                                   // reference (keys carry e^{+60} at most, queries e^{-60})
+constexpr float SKIP_LOG = 40.f;  // the state pass drops chunks that reach their segment's end
+                                  // decayed below e^{-40} in every feature
 constexpr int LDS_LIMIT = 160 * 1024;
 constexpr int WIN_BATCH = 8;      // key tiles per online-softmax batch in the window
 constexpr int KT_META = -(1 << 28);  // window tile list: the meta tile

@@ -1069,19 +1069,82 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, I = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
-  const int nsp = (p.nseg - 1) * p.sss;  // pieces of p.cps / p.sss chunks before the last segment
+  const int nsp = (p.nseg - 1) * p.sss;  // pieces: p.sss per segment before the last one
   const int grp = blockIdx.x;
   if (grp >= p.B * p.Hkv * nsp) return;
   const int piece = grp % nsp, bh = grp / nsp;
   const int L = p.L;
-  const int cpp = p.cps / p.sss;
-  const int c_begin = piece * cpp, c_end = c_begin + cpp;  // never in the last segment: full chunks
   const size_t kv_off = (size_t)bh * (size_t)L * D;
   const T *Kh = reinterpret_cast<const T *>(p.k) + kv_off;
   const T *Vh = reinterpret_cast<const T *>(p.v) + kv_off;
   const T *LGh = reinterpret_cast<const T *>(p.lg) + kv_off;
 
   load_wT<T, D, LDWW, 256>(sW, reinterpret_cast<const T *>(p.wk), tid);
+
+  // The block of chunks [b0, b1) is one segment (never the last: full chunks).  A chunk c whose
+  // tokens reach the block end decayed by less than e^{-SKIP_LOG} in every feature (the log-gate
+  // sum over chunks c + 1 .. b1 - 1 below -SKIP_LOG) adds nothing the fp32 state can hold
+  // (below 4e-18 of its own size), and neither do the chunks before it.  So the block's state
+  // starts from zero at c_start, the first chunk that is not dropped, and the p.sss pieces split
+  // [c_start, b1).  The scan goes backwards in batches of 8 chunks: threads (row slot rs, feature
+  // group fq) add up 8 features over rows rs + 16 r of each chunk.
+  const int blk = piece / p.sss, pp = piece % p.sss;
+  const int b0 = blk * p.cps, b1 = b0 + p.cps;
+  int c_start = b0;
+  {
+    constexpr int NB = 8;
+    const int fq = lane & 15, rs = 4 * I + (lane >> 4);
+    float* red = reinterpret_cast<float *>(smem + ST_OFF_VT);  // [4 waves][NB][D] chunk sums (free here)
+    int *vote = reinterpret_cast<int *>(smem + ST_OFF_TAB);     // [2]: per feature wave, chunks all-below
+    float suf = 0.f;  // thread tid < D: log-gate sum of feature tid over the chunks scanned so far
+    for (int top = b1 - 1; top > b0; top -= NB) {
+      float part[NB][8];
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part[u][e] = 0.f;
+        const int cc = top - u;
+        if (cc > b0) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float x[8];
+            load8f(LGh + (size_t)(cc * CH + rs + 16 * r) * D + 8 * fq, x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part[u][e] += x[e];
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NB; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = wave_sum_cols(part[u][e]);
+          if (lane < 16) red[(I * NB + u) * D + 8 * fq + e] = v;
+        }
+      __syncthreads();
+      int bits = 0;  // bit u: the scanned sum through chunk top - u is below -SKIP_LOG
+      if (tid < D) {
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+          if (top - u > b0) suf += red[u * D + tid] + red[(NB + u) * D + tid] + red[(2 * NB + u) * D + tid] + red[(3 * NB + u) * D + tid];
+          bits |= (top - u > b0 && suf < -SKIP_LOG) ? 1 << u : 0;
+        }
+        int all = 0;
+#pragma unroll
+        for (int u = 0; u < NB; ++u) all |= __all((bits >> u) & 1) ? 1 << u : 0;
+        if (lane == 0) vote[I] = all;
+      }
+      __syncthreads();
+      const int both = vote[0] & vote[1];
+      __syncthreads();  // red and vote are rewritten by the next batch
+      if (both) {
+        c_start = top - (__ffs(both) - 1);  // the latest chunk through which every feature is below
+        break;
+      }
+    }
+  }
+  const int nneed = b1 - c_start, len = (nneed + p.sss - 1) / p.sss;
+  const int c_begin = min(c_start + pp * len, b1), c_end = min(c_begin + len, b1);
   auto load_k = [&](Frag<T> (&kf)[KS], int c0) {
     const T *src = Kh + (size_t)(c0 + 16 * I + r16) * D;
 #pragma unroll
@@ -1096,9 +1159,11 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
       for (int gsel = 0; gsel < 2; ++gsel) f[gsel][h] = load8(base + (size_t)(c0 + 2 * tp + h) * D + 8 * ((tid >> 5) + 8 * gsel));
   };
   Frag<T> kf[KS], vf[2][2], lf[2][2];
-  load_k(kf, c_begin * CH);
-  load_pairs(vf, Vh, c_begin * CH);
-  load_pairs(lf, LGh, c_begin * CH);
+  if (c_begin < c_end) {
+    load_k(kf, c_begin * CH);
+    load_pairs(vf, Vh, c_begin * CH);
+    load_pairs(lf, LGh, c_begin * CH);
+  }
   f32x4 S[FTW][NDT];
 #pragma unroll
   for (int ft = 0; ft < FTW; ++ft)
@@ -1217,7 +1282,8 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
       *reinterpret_cast<f32x4 *>(E + ((size_t)((2 * I + ft) * NDT + dt) * 64 + lane) * 4) = S[ft][dt];
-  if (tid < D) p.ws_decay[(size_t)grp * D + tid] = dsum;
+  // the state carried into a block that starts late is dropped with the chunks before c_start
+  if (tid < D) p.ws_decay[(size_t)grp * D + tid] = (pp == 0 && c_start > b0) ? NEG_BIG : dsum;
 }
 
 hipError_t launch_fwd_full(const FwdParams &p, hipStream_t stream) {

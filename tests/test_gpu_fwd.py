@@ -179,6 +179,17 @@ def test_fwd_whole_head_wide_window(gpu_lib, monkeypatch, label, kw, nseg):
     check_case(f"bf16 whole-head {label}", inp, "bf16")
 
 
+@pytest.mark.parametrize("gate", ["one", "const:-0.1", "const:-0.5", "logsigmoid"])
+def test_fwd_whole_head_state_pass_drops_decayed_chunks(gpu_lib, monkeypatch, gate):
+    """The state pass leaves out the chunks of a segment that reach its end decayed below
+    e^-40 in every feature (with -0.1 per token: all but the last 7 of 13 chunks; -0.5: the
+    last 2), and splits the rest over its pieces; gamma = 1 keeps everything."""
+    monkeypatch.setenv("LIZARD_FWD_SEGMENTS", "2")
+    inp = make_fwd_inputs(B=2, Hq=2, Hkv=2, L=1600, d=128, W=64, M=4, dtype="bf16",
+                          seed=zlib.crc32(gate.encode()) % 10000, gate=gate)
+    check_case(f"bf16 whole-head 2 segments, gate {gate}", inp, "bf16")
+
+
 @pytest.mark.parametrize("label", ["bf16 d128 ragged L200", "bf16 gamma=0 (exact diag)", "bf16 gamma=1"])
 def test_fwd_value_block_kernel(gpu_lib, monkeypatch, label):
     """The value-block (role-split) kernel on cases the whole-head kernel would otherwise take
