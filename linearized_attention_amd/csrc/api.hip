@@ -46,7 +46,7 @@ constexpr int kDV = 64;       // value columns per workgroup
 constexpr int kMaxMeta = 16;
 constexpr int kTargetBlocks = 256;
 constexpr int kStateBlocks = 512;  // state-pass pieces (two 80 KB workgroups fit a CU)
-constexpr int kMaxFullCps = 4096;   // chunks per segment the whole-head kernel's LDS flags cover
+constexpr int kMaxFullCps = 1024;   // chunks per segment the whole-head kernel's LDS flags cover
 
 struct FwdPlan {
   int nchunks, nseg, cps, ndvb, nring;

@@ -47,8 +47,8 @@ namespace full {
 
 constexpr int D = 128, NFT = 8, KS = 4, NDT = 8, FTW = 2;
 constexpr int LDW = 144;  // rows of 128 elements (288 bytes)
-constexpr int LDWW = 136; // W_phi^T rows (272 bytes: LDS is too short for 288)
-constexpr int LDQ = 136;  // decayed-query rows (272 bytes)
+constexpr int LDWW = 144; // W_phi^T rows (288 bytes)
+constexpr int LDQ = 144;  // decayed-query rows (288 bytes)
 constexpr int LDV = 80;   // rows of 64 tokens (160 bytes)
 constexpr int LDM = 16;   // rows of 16 meta tokens (32 bytes, 8-byte reads)
 constexpr int OFF_W = 0;                        // W_phi^T [f][d]
@@ -62,7 +62,7 @@ constexpr int OFF_TAB = OFF_Q + CH * LDQ * 2;   // prefix ends C_J, [4][128] fp3
 constexpr int OFF_TK = OFF_TAB + 4 * D * 4;     // meta keys [16][d]
 constexpr int OFF_TV = OFF_TK + 16 * LDW * 2;   // meta values^T [dv][16]
 constexpr int OFF_FLAG = OFF_TV + D * LDM * 2;  // per query wave: bit k = chunk c_begin + k needs
-constexpr int FLAG_WORDS = 128;                 // the exact diagonal block (segments of at most 4096 chunks)
+constexpr int FLAG_WORDS = 32;                  // the exact diagonal block (segments of at most 1024 chunks)
 constexpr int LDS_BYTES = OFF_FLAG + 4 * FLAG_WORDS * 4;
 static_assert(LDS_BYTES <= LDS_LIMIT, "whole-head layout exceeds LDS");
 
