@@ -206,6 +206,25 @@ __device__ __forceinline__ void feature_logits_pipe(const bf16 *sW, const Frag<b
   }
 }
 
+// The state update's A operand, decayed keys^T: feature 32 I + 16 ft + r16 for the 8 tokens of
+// lane group g4 in K-step ks (slots 0..3: tokens 32 ks + 4 g4 + j, slots 4..7: the same + 16), from
+// sKt rows (tokens, interleaved features) by two transposed LDS reads (ds_read_b64_tr_b16): in a
+// group of 16 lanes, lane m reads the 4 features 32 I + 16 ft + 4 (m % 4) .. + 3 (contiguous in the
+// interleaved order) of token 32 ks + 4 g4 + m / 4, and lane i receives feature i of the 4 tokens
+// that lanes 4 j + i / 4 read (j = 0..3).
+__device__ __forceinline__ void keysT_tr(const bf16 *sKt, int I, int ft, int ks, int r16, int g4, float (&x)[8]) {
+  using namespace full;
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const bf16 *src = sKt + (32 * ks + 4 * g4 + (r16 >> 2)) * LDW + 32 * I + 8 * (r16 & 3) + 4 * ft;
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(src));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(src + 16 * LDW));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[j] = __uint_as_float((uint32_t)(uint16_t)lo[j] << 16);
+    x[4 + j] = __uint_as_float((uint32_t)(uint16_t)hi[j] << 16);
+  }
+}
+
 // ZW: windows of 66..129 keys, which reach into the chunk two back (window group Z)
 template <bool ZW>
 __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
@@ -578,7 +597,6 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
 #pragma unroll
         for (int ft = 0; ft < FTW; ++ft) {
           const int fr = 16 * (2 * I + ft);
-          const int fcol = 32 * I + ipos(16 * ft + r16);  // interleaved position of feature fr + r16
           // key factors e^{C_3} (mild: keys carry e^{-p_s}) or e^{C_3 - C_J} (keys carry e^{C_J - p_s})
           float fac[2][2];  // [ks][half]: factor of the keys of sub-chunk 2ks + half
           const f32x4 c3 = *reinterpret_cast<const f32x4 *>(sTot + 3 * D + fr + 4 * g4);
@@ -590,9 +608,9 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
             float x[8];
+            keysT_tr(sKt, I, ft, ks, r16, g4, x);
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj)
-              x[jj] = to_f(sKt[(32 * ks + islot(g4, jj)) * LDW + fcol]) * fac[ks][jj >> 2];
+            for (int jj = 0; jj < 8; ++jj) x[jj] *= fac[ks][jj >> 2];
             ka[ft][ks] = frag_from<T>(x);
           }
         }
@@ -1238,7 +1256,6 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
 #pragma unroll
       for (int ft = 0; ft < FTW; ++ft) {
         const int fr = 16 * (2 * I + ft);
-        const int fcol = 32 * I + ipos(16 * ft + r16);
         const f32x4 c3 = *reinterpret_cast<const f32x4 *>(sTot + 3 * D + fr + 4 * g4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) e[ft][i] = __expf(c3[i]);
@@ -1249,8 +1266,9 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           float x[8];
+          keysT_tr(sKt, I, ft, ks, r16, g4, x);
 #pragma unroll
-          for (int jj = 0; jj < 8; ++jj) x[jj] = to_f(sKt[(32 * ks + islot(g4, jj)) * LDW + fcol]) * fac[ks][jj >> 2];
+          for (int jj = 0; jj < 8; ++jj) x[jj] *= fac[ks][jj >> 2];
           ka[ft][ks] = frag_from<T>(x);
         }
       }
