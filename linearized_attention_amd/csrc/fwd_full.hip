@@ -351,28 +351,41 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
   // Loads inside the chunk loop (rows >= 0): a uniform base and a 32-bit per-lane offset
   // recomputed from the lane id each time, so no 64-bit lane addresses are held (or spilled)
   // across the loop; a reloaded spill would also wait for every load in flight.
+  // (a chunk that lies inside the sequence, every chunk but a ragged last one, skips the
+  // per-lane bounds checks and the exec-mask branches they cost)
   auto kfrag_in = [&](Frag<T> (&kf)[KS], int c0, int ln) {
     const int x = c0 + 16 * I + (ln & 15);
     const unsigned off = (unsigned)(x * D + 8 * (ln >> 4));
+    if (c0 + CH <= L) {
 #pragma unroll
-    for (int j = 0; j < KS; ++j) kf[j] = (x < L) ? load8(Kh + off + 32 * j) : frag_zero<T>();
+      for (int j = 0; j < KS; ++j) kf[j] = load8(Kh + off + 32 * j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < KS; ++j) kf[j] = (x < L) ? load8(Kh + off + 32 * j) : frag_zero<T>();
+    }
   };
   auto q_in = [&](Frag<T> (&f)[KS], int c0, int ln) {
     const int t = c0 + 16 * I + (ln & 15);
     const unsigned off = (unsigned)(t * D + 8 * (ln >> 4));
+    if (c0 + CH <= L) {
 #pragma unroll
-    for (int j = 0; j < KS; ++j) f[j] = (t < L) ? load8(Qh + off + 32 * j) : frag_zero<T>();
+      for (int j = 0; j < KS; ++j) f[j] = load8(Qh + off + 32 * j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < KS; ++j) f[j] = (t < L) ? load8(Qh + off + 32 * j) : frag_zero<T>();
+    }
   };
   // token pairs (2 tp, 2 tp + 1) x 8-column groups t / 32 and t / 32 + 8 of a [L][D] tensor
   auto pairs_in = [&](Frag<T> (&f)[2][2], const T *base, int c0, int t) {
     const int tp = t & 31;
+    const bool inside = c0 + CH <= L;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int x = c0 + 2 * tp + h;
 #pragma unroll
       for (int gsel = 0; gsel < 2; ++gsel) {
         const unsigned off = (unsigned)(x * D + 8 * ((t >> 5) + 8 * gsel));
-        f[gsel][h] = (x < L) ? load8(base + off) : frag_zero<T>();
+        f[gsel][h] = (inside || x < L) ? load8(base + off) : frag_zero<T>();
       }
     }
   };
