@@ -225,6 +225,32 @@ __device__ __forceinline__ void keysT_tr(const bf16 *sKt, int I, int ft, int ks,
   }
 }
 
+// W_phi^T [f][d] into LDS (row stride LDWW) from W_phi [d][f] in global memory, by NT threads:
+// each thread takes row pairs (d, d + 1) x 8 features, all its loads in flight before the
+// transposed 4-byte stores of the pairs.
+template <int NT>
+__device__ __forceinline__ void load_wT_pairs(bf16 *dst, const bf16 *src, int tid) {
+  using namespace full;
+  constexpr int IT = (D / 2) * (D / 8) / NT;
+  static_assert(IT * NT == (D / 2) * (D / 8), "thread count must divide the row pairs");
+  Frag<bf16> a[IT], b[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = tid + it * NT, dd = 2 * (idx / (D / 8)), f0 = (idx % (D / 8)) * 8;
+    a[it] = load8(src + (size_t)dd * D + f0);
+    b[it] = load8(src + (size_t)(dd + 1) * D + f0);
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = tid + it * NT, dd = 2 * (idx / (D / 8)), f0 = (idx % (D / 8)) * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      bf16 pair[2] = {a[it].v[j], b[it].v[j]};
+      *reinterpret_cast<uint32_t *>(dst + (f0 + j) * LDWW + dd) = *reinterpret_cast<const uint32_t *>(pair);
+    }
+  }
+}
+
 // ZW: windows of 66..129 keys, which reach into the chunk two back (window group Z)
 template <bool ZW>
 __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
@@ -394,7 +420,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
   // ---- prologue: weights, meta tokens, the chunk before the first one
   {
     const T *Wk = reinterpret_cast<const T *>(p.wk);
-    load_wT<T, D, LDWW, 512>(sW, Wk, tid);
+    load_wT_pairs<512>(sW, Wk, tid);
     const T *Tv = reinterpret_cast<const T *>(p.tv);
     const T *Tk = reinterpret_cast<const T *>(p.tk);
     for (int idx = tid; idx < D * 16; idx += 512) {
@@ -1110,7 +1136,7 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
   const T *Vh = reinterpret_cast<const T *>(p.v) + kv_off;
   const T *LGh = reinterpret_cast<const T *>(p.lg) + kv_off;
 
-  load_wT<T, D, LDWW, 256>(sW, reinterpret_cast<const T *>(p.wk), tid);
+  load_wT_pairs<256>(sW, reinterpret_cast<const T *>(p.wk), tid);
 
   // The block of chunks [b0, b1) is one segment (never the last: full chunks).  A chunk c whose
   // tokens reach the block end decayed by less than e^{-SKIP_LOG} in every feature (the log-gate
