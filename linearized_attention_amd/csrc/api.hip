@@ -45,7 +45,8 @@ constexpr int kChunk = 64;
 constexpr int kDV = 64;       // value columns per workgroup
 constexpr int kMaxMeta = 16;
 constexpr int kTargetBlocks = 256;
-constexpr int kStateBlocks = 512;  // state-pass pieces (two 80 KB workgroups fit a CU)
+constexpr int kStateBlocks = 256;  // state-pass pieces (two 80 KB workgroups fit a CU; with
+                                    // the decayed chunks left out, 256 timed better than 512)
 constexpr int kMaxFullCps = 1024;   // chunks per segment the whole-head kernel's LDS flags cover
 
 struct FwdPlan {

@@ -90,8 +90,8 @@ def test_workspace_bytes_matches_plan_formula():
     nseg = 4
     split = B * Hkv * 2 * (nseg - 1) * d * 64 * 4 + B * Hkv * (nseg - 1) * d * 4
     # whole-head plan (bf16, d = 128, W <= 129): B*Hq = 32 blocks -> 8 segments of 64 chunks;
-    # the state pass in 512 // (32 * 7) = 2 pieces per segment, full d x d states
-    nseg, sss = 8, 2
+    # the state pass in max(1, 256 // (32 * 7)) = 1 piece per segment, full d x d states
+    nseg, sss = 8, 1
     pieces = B * Hkv * (nseg - 1) * sss
     full = pieces * d * d * 4 + -(-pieces * d * 4 // 256) * 256
     assert got == max(split, full)
