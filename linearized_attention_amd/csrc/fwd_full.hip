@@ -1022,47 +1022,50 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
             for (int jj = 0; jj < 8; ++jj) x[jj] = to_f(qcf[js].v[jj]) * __expf(a8[jj] - b8[jj]);
             return frag_from<T>(x);
           };
+          // scores of the key sub-chunk pair (2m, 2m + 1), then one product with their v^T
 #pragma unroll 1
-          for (int J = 0; J <= I; ++J) {
-            f32x4 a = {0.f, 0.f, 0.f, 0.f};
-            if (J + 1 == I) {
+          for (int m = 0; 2 * m <= I; ++m) {
+            f32x4 sc[2];
 #pragma unroll
-              for (int js = 0; js < KS; ++js) a = mma(load8(sKt + (16 * J + r16) * LDW + 32 * js + 8 * g4), qcf[js], a);
-            } else if (J < I) {
+            for (int h = 0; h < 2; ++h) {
+              const int J = 2 * m + h;
+              f32x4 a = {0.f, 0.f, 0.f, 0.f};
+              if (J + 1 == I) {
 #pragma unroll
-              for (int js = 0; js < KS; ++js)
-                a = mma(load8(sKt + (16 * J + r16) * LDW + 32 * js + 8 * g4), qscaled(js, J + 1, I), a);
-            } else if (safe) {
+                for (int js = 0; js < KS; ++js) a = mma(load8(sKt + (16 * J + r16) * LDW + 32 * js + 8 * g4), qcf[js], a);
+              } else if (J < I) {
 #pragma unroll
-              for (int js = 0; js < KS; ++js) {
-                float c8[8], cp8[8], kv[8];
-                const Frag<T> kk = load8(sKt + (16 * I + r16) * LDW + 32 * js + 8 * g4);
-                tab8(sTot + I * D, js, g4, c8);
+                for (int js = 0; js < KS; ++js)
+                  a = mma(load8(sKt + (16 * J + r16) * LDW + 32 * js + 8 * g4), qscaled(js, J + 1, I), a);
+              } else if (J == I && safe) {
 #pragma unroll
-                for (int jj = 0; jj < 8; ++jj) cp8[jj] = 0.f;
-                if (I > 0) tab8(sTot + (I - 1) * D, js, g4, cp8);
+                for (int js = 0; js < KS; ++js) {
+                  float c8[8], cp8[8], kv[8];
+                  const Frag<T> kk = load8(sKt + (16 * I + r16) * LDW + 32 * js + 8 * g4);
+                  tab8(sTot + I * D, js, g4, c8);
 #pragma unroll
-                for (int jj = 0; jj < 8; ++jj) kv[jj] = to_f(kk.v[jj]) * __expf(cp8[jj] - c8[jj]);
-                a = mma(frag_from<T>(kv), qcf[js], a);
+                  for (int jj = 0; jj < 8; ++jj) cp8[jj] = 0.f;
+                  if (I > 0) tab8(sTot + (I - 1) * D, js, g4, cp8);
+#pragma unroll
+                  for (int jj = 0; jj < 8; ++jj) kv[jj] = to_f(kk.v[jj]) * __expf(cp8[jj] - c8[jj]);
+                  a = mma(frag_from<T>(kv), qcf[js], a);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a[i] = (4 * g4 + i <= r16) ? a[i] : 0.f;
               }
-            } else {
-              a = f32x4{0.f, 0.f, 0.f, 0.f};  // exact block added after the chunk loop
+              // (an unsafe diagonal block stays zero: its exact products are added after the loop)
+              sc[h] = a;
             }
-            if (J == I) {
-#pragma unroll
-              for (int i = 0; i < 4; ++i) a[i] = (4 * g4 + i <= r16) ? a[i] : 0.f;
-            }
-            // tile J sits in slots 4 (J & 1) .. +3 of the interleaved pair (J & ~1, J | 1)
             float x[8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              x[i] = (J & 1) ? 0.f : a[i];
-              x[4 + i] = (J & 1) ? a[i] : 0.f;
+              x[i] = sc[0][i];
+              x[4 + i] = sc[1][i];
             }
             const Frag<T> bf = frag_from<T>(x);
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
-              acc[dt] = mma(load8(sVt + (16 * dt + r16) * LDV + 32 * (J >> 1) + 8 * g4), bf, acc[dt]);
+              acc[dt] = mma(load8(sVt + (16 * dt + r16) * LDV + 32 * m + 8 * g4), bf, acc[dt]);
           }
 #pragma unroll
           for (int js = 0; js < KS; ++js) {
