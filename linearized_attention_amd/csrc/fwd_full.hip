@@ -1139,8 +1139,6 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
   const T *Vh = reinterpret_cast<const T *>(p.v) + kv_off;
   const T *LGh = reinterpret_cast<const T *>(p.lg) + kv_off;
 
-  load_wT_pairs<256>(sW, reinterpret_cast<const T *>(p.wk), tid);
-
   // The block of chunks [b0, b1) is one segment (never the last: full chunks).  A chunk c whose
   // tokens reach the block end decayed by less than e^{-SKIP_LOG} in every feature (the log-gate
   // sum over chunks c + 1 .. b1 - 1 below -SKIP_LOG) adds nothing the fp32 state can hold
@@ -1157,23 +1155,26 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
     float* red = reinterpret_cast<float *>(smem + ST_OFF_VT);  // [4 waves][NB][D] chunk sums (free here)
     int *vote = reinterpret_cast<int *>(smem + ST_OFF_TAB);     // [2]: per feature wave, chunks all-below
     float suf = 0.f;  // thread tid < D: log-gate sum of feature tid over the chunks scanned so far
+    bool staged = false;
     for (int top = b1 - 1; top > b0; top -= NB) {
-      float part[NB][8];
+      Frag<T> raw[NB][4];
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) part[u][e] = 0.f;
         const int cc = top - u;
-        if (cc > b0) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float x[8];
-            load8f(LGh + (size_t)(cc * CH + rs + 16 * r) * D + 8 * fq, x);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) part[u][e] += x[e];
-          }
-        }
+        for (int r = 0; r < 4; ++r)
+          raw[u][r] = cc > b0 ? load8(LGh + (size_t)(cc * CH + rs + 16 * r) * D + 8 * fq) : frag_zero<T>();
       }
+      if (!staged) {  // W_phi^T staging overlaps the first batch's loads
+        load_wT_pairs<256>(sW, reinterpret_cast<const T *>(p.wk), tid);
+        staged = true;
+      }
+      float part[NB][8];
+#pragma unroll
+      for (int u = 0; u < NB; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          part[u][e] = (to_f(raw[u][0].v[e]) + to_f(raw[u][1].v[e])) + (to_f(raw[u][2].v[e]) + to_f(raw[u][3].v[e]));
 #pragma unroll
       for (int u = 0; u < NB; ++u)
 #pragma unroll
@@ -1203,6 +1204,7 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
       }
     }
   }
+  if (c_start == b0 && b1 - 1 <= b0) load_wT_pairs<256>(sW, reinterpret_cast<const T *>(p.wk), tid);  // no scan ran
   const int nneed = b1 - c_start, len = (nneed + p.sss - 1) / p.sss;
   const int c_begin = min(c_start + pp * len, b1), c_end = min(c_begin + len, b1);
   auto load_k = [&](Frag<T> (&kf)[KS], int c0) {
