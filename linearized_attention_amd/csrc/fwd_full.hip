@@ -944,7 +944,9 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
         if constexpr (ZW) q_in(qf_next2, c0 + 2 * CH, ln);
         else q_in(qf_next, c0 + CH, ln);
       }
-      // ---- P3: window output normalised and scaled for the merge
+      // ---- P3: window output normalised and scaled for the merge; for strong-decay chunks the
+      //      inter-chunk product (decayed queries and prefix ends are visible since B2, the state
+      //      copy since B1)
       {
         const float ws = (1.f - mix) / wave_sum_cols(l_run);
 #pragma unroll
@@ -952,8 +954,6 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[dt][i] *= ws;
       }
-      __syncthreads();  // B3: decayed keys and tables visible
-      // ---- P4: intra- and inter-chunk products onto the window output, store
       // Y^T += S^T qop^T over the 32 S^T fragments, four loaded ahead of their products
       auto inter = [&](const Frag<T> (&qop)[KS]) {
         const T *srow = sSb + r16 * LDW + 8 * g4;
@@ -972,6 +972,28 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
           for (int u = 0; u < 4; ++u) acc[4 * dh + u] = mma(sb[st & 1][u], qop[js], acc[4 * dh + u]);
         }
       };
+#pragma unroll
+      for (int js = 0; js < KS; ++js) qcf[js] = load8(sQ + (16 * I + r16) * LDQ + 32 * js + 8 * g4);
+      if (mild || ZW) {
+        // (mild chunks: the inter product stays with the intra products after B3, where it
+        // timed better; the wide-window variant has no registers to spare here)
+      } else if (I == 0) {
+        inter(qcf);
+      } else {
+        // sub-chunk references: the queries carry e^{p_t - C_{I-1}}; the state needs e^{p_t}
+        Frag<T> qs[KS];
+#pragma unroll
+        for (int js = 0; js < KS; ++js) {
+          float x[8], c8[8];
+          tab8(sTot + (I - 1) * D, js, g4, c8);
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) x[jj] = to_f(qcf[js].v[jj]) * __expf(c8[jj]);
+          qs[js] = frag_from<T>(x);
+        }
+        inter(qs);
+      }
+      __syncthreads();  // B3: decayed keys and tables visible
+      // ---- P4: intra- and inter-chunk products onto the window output, store
       auto finish = [&](auto mild_tag) {
         constexpr bool MILD = decltype(mild_tag)::value;
         if constexpr (MILD) {
@@ -1067,12 +1089,14 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
             for (int dt = 0; dt < NDT; ++dt)
               acc[dt] = mma(load8(sVt + (16 * dt + r16) * LDV + 32 * m + 8 * g4), bf, acc[dt]);
           }
+          if constexpr (ZW) {  // the inter-chunk product (the other variant ran it before B3)
 #pragma unroll
-          for (int js = 0; js < KS; ++js) {
-            const Frag<T> bf = I > 0 ? qscaled(js, 0, I) : qcf[js];
+            for (int js = 0; js < KS; ++js) {
+              const Frag<T> bf = I > 0 ? qscaled(js, 0, I) : qcf[js];
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-              acc[dt] = mma(load8(sSb + (16 * dt + r16) * LDW + 32 * js + 8 * g4), bf, acc[dt]);
+              for (int dt = 0; dt < NDT; ++dt)
+                acc[dt] = mma(load8(sSb + (16 * dt + r16) * LDW + 32 * js + 8 * g4), bf, acc[dt]);
+            }
           }
         }
         if (valid) {
@@ -1081,8 +1105,6 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
           for (int dt = 0; dt < NDT; ++dt) store4<T>(O + 16 * dt + 4 * g4, acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
         }
       };
-#pragma unroll
-      for (int js = 0; js < KS; ++js) qcf[js] = load8(sQ + (16 * I + r16) * LDQ + 32 * js + 8 * g4);
       if (mild) finish(std::true_type{});
       else finish(std::false_type{});
 #pragma unroll
