@@ -97,6 +97,17 @@ def test_workspace_bytes_matches_plan_formula():
     assert got == max(split, full)
 
 
+def test_whole_head_segments_cover_at_most_1024_chunks():
+    """The whole-head kernel keeps one LDS flag bit per chunk of its segment (1024 at most): a
+    sequence of 2048 chunks over 256 (batch, head) pairs, which would otherwise run as one
+    segment, is split in two and needs the state-pass workspace; 1024 chunks need none."""
+    lib = api.load()
+    assert lib.lizard_attn_fwd_workspace_bytes(8, 32, 32, 1024 * 64, 128, 64, 1) == 0
+    need = lib.lizard_attn_fwd_workspace_bytes(8, 32, 32, 2048 * 64, 128, 64, 1)
+    pieces = 8 * 32 * 1 * 1  # B*Hkv*(nseg - 1)*sss with nseg = 2, sss = 256 // 256
+    assert need == pieces * 128 * 128 * 4 + pieces * 128 * 4
+
+
 def _dec(lib, **kw):
     a = dict(state=16, wk=16, wv=16, pos=16, q=16, k=16, v=16, lg=16, wq=16, wkm=16, stride=0, tk=16,
              tv=16, out=16, N=4, Hq=2, Hkv=2, d=128, W=64, M=4, mix=0.5, scale=0.1, dtype=1, ws=16,
