@@ -694,7 +694,12 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
     // previous chunk, still in LDS) and is carried into group X as (az, mz, lz): unnormalised
     // probabilities times values, the base-2 max per query row, this lane's part of the sum.
     auto window_z = [&](const Frag<T> (&qz)[KS], int cz0, f32x4 (&az)[NDT], float &mz, float &lz) {
-      const int kminz = max(cz0 + 16 * I + r16 - p.W + 1, -hist_avail);
+      // mask offsets from a lane id the compiler cannot hoist out of the chunk loop (kept
+      // across it they were spilled)
+      int lnz = lane;
+      asm volatile("" : "+v"(lnz));
+      const int kminz = max(cz0 + 16 * I + (lnz & 15) - p.W + 1, -hist_avail);
+      const int kz0 = cz0 - 2 * CH + 4 * (lnz >> 4);
       f32x4 lt[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -705,8 +710,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
           for (int j = 0; j < KS; ++j) a = mma(load8(sK + (16 * u + r16) * LDW + 32 * j + 8 * g4), qz[j], a);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int kj = cz0 - 2 * CH + 16 * u + 4 * g4 + i;
-            lt[u][i] = (kj >= kminz) ? a[i] * sl2 : NEG_BIG;
+            lt[u][i] = (kz0 + 16 * u + i >= kminz) ? a[i] * sl2 : NEG_BIG;
           }
         }
       }
@@ -1124,18 +1128,30 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
   }
 }
 
-// State pass of a segmented sequence: the chunks before the last segment in pieces (p.sss per
-// segment); for each piece the end state E_j of its tokens alone (from S = 0) and the sum of
-// its log gates D_j, so that the whole-head kernel can start a segment from
-// sum_{i<j} diag(e^{D_{i+1} + ... + D_{j-1}}) E_i over the pieces before it (the recurrence
-// is associative in (D, E)).  Four waves, each the key side of one sub-chunk,
-// with the arithmetic of the key waves above; 80 KB of LDS, so two workgroups share a CU.
+// State pass of a segmented sequence: every segment but the last is a block of chunks
+// [b0, b1), split into p.sss pieces.  Piece pp of a block walks the block backwards from its
+// end, keeps the log-gate sums of the chunks after the current one (the suffix s), and adds the
+// chunks c with (b1 - 1 - c) % p.sss == pp decayed to the block end:
+//   E_pp = sum_c diag(e^{s_c}) sum_{t in c} diag(e^{C(c) - p_t}) phi_k(k_t) v_t^T,
+// where p_t is the prefix sum inside chunk c through t and C(c) its total.  The pieces of a block
+// thus add up to the block's state from S = 0 (the recurrence is linear in the added terms).
+// Piece 0 also carries the block's log-gate sum D, the others D = 0, so that the whole-head
+// kernel's fold S = e^{D_j} S + E_j over the pieces in order gives every segment its start state.
+// Once the suffix is below -SKIP_LOG in every feature, the chunks before reach the block end
+// decayed by less than e^{-SKIP_LOG} (below 4e-18 of their size, nothing the fp32 state can
+// hold): the walk stops there, and piece 0 sets D = NEG_BIG, dropping the state carried in.
+// Every piece reads the log gates of all the chunks it walks (the suffix) and the keys and
+// values of its own.  Four waves, each the key side of one sub-chunk, with the arithmetic of
+// the key waves above; 80 KB of LDS, so two workgroups share a CU.  The pieces of a block run
+// 8 workgroups apart, on one XCD, and share its L2 for the log gates they all read.
 namespace full {
 constexpr int ST_OFF_W = 0;
 constexpr int ST_OFF_VT = ST_OFF_W + D * LDWW * 2;
 constexpr int ST_OFF_KT = ST_OFF_VT + D * LDV * 2;
 constexpr int ST_OFF_TAB = ST_OFF_KT + SZ_KT;
-constexpr int ST_LDS_BYTES = ST_OFF_TAB + 4 * D * 4;
+constexpr int ST_OFF_SUF = ST_OFF_TAB + 4 * D * 4;  // [2][D] suffix sums (alternating chunks)
+constexpr int ST_OFF_VOTE = ST_OFF_SUF + 2 * D * 4;
+constexpr int ST_LDS_BYTES = ST_OFF_VOTE + 16;
 static_assert(2 * ST_LDS_BYTES <= LDS_LIMIT, "state pass: two workgroups per CU");
 }  // namespace full
 
@@ -1148,87 +1164,26 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
   T *sKt = reinterpret_cast<T *>(smem + ST_OFF_KT);
   T *sLgT = sKt;
   float *sTot = reinterpret_cast<float *>(smem + ST_OFF_TAB);
+  float *sSuf = reinterpret_cast<float *>(smem + ST_OFF_SUF);
+  int *sVote = reinterpret_cast<int *>(smem + ST_OFF_VOTE);
 
   const int tid = threadIdx.x, lane = tid & 63, I = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
-  const int nsp = (p.nseg - 1) * p.sss;  // pieces: p.sss per segment before the last one
-  const int grp = blockIdx.x;
-  if (grp >= p.B * p.Hkv * nsp) return;
-  const int piece = grp % nsp, bh = grp / nsp;
+  const int sss = p.sss;
+  const int nblk = p.B * p.Hkv * (p.nseg - 1);  // blocks: every segment but the last, per head
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int bg = (slot / sss) * 8 + xcd, pp = slot % sss;
+  if (bg >= nblk) return;
+  const int bh = bg / (p.nseg - 1), blk = bg % (p.nseg - 1);
+  const int grp = bg * sss + pp;  // workspace slot: piece pp of block blk of head bh
   const int L = p.L;
   const size_t kv_off = (size_t)bh * (size_t)L * D;
   const T *Kh = reinterpret_cast<const T *>(p.k) + kv_off;
   const T *Vh = reinterpret_cast<const T *>(p.v) + kv_off;
   const T *LGh = reinterpret_cast<const T *>(p.lg) + kv_off;
+  const int b0 = blk * p.cps, b1 = b0 + p.cps;  // never the last segment: full chunks
+  auto own = [&](int c) { return (b1 - 1 - c) % sss == pp; };
 
-  // The block of chunks [b0, b1) is one segment (never the last: full chunks).  A chunk c whose
-  // tokens reach the block end decayed by less than e^{-SKIP_LOG} in every feature (the log-gate
-  // sum over chunks c + 1 .. b1 - 1 below -SKIP_LOG) adds nothing the fp32 state can hold
-  // (below 4e-18 of its own size), and neither do the chunks before it.  So the block's state
-  // starts from zero at c_start, the first chunk that is not dropped, and the p.sss pieces split
-  // [c_start, b1).  The scan goes backwards in batches of 8 chunks: threads (row slot rs, feature
-  // group fq) add up 8 features over rows rs + 16 r of each chunk.
-  const int blk = piece / p.sss, pp = piece % p.sss;
-  const int b0 = blk * p.cps, b1 = b0 + p.cps;
-  int c_start = b0;
-  {
-    constexpr int NB = 8;
-    const int fq = lane & 15, rs = 4 * I + (lane >> 4);
-    float* red = reinterpret_cast<float *>(smem + ST_OFF_VT);  // [4 waves][NB][D] chunk sums (free here)
-    int *vote = reinterpret_cast<int *>(smem + ST_OFF_TAB);     // [2]: per feature wave, chunks all-below
-    float suf = 0.f;  // thread tid < D: log-gate sum of feature tid over the chunks scanned so far
-    bool staged = false;
-    for (int top = b1 - 1; top > b0; top -= NB) {
-      Frag<T> raw[NB][4];
-#pragma unroll
-      for (int u = 0; u < NB; ++u) {
-        const int cc = top - u;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          raw[u][r] = cc > b0 ? load8(LGh + (size_t)(cc * CH + rs + 16 * r) * D + 8 * fq) : frag_zero<T>();
-      }
-      if (!staged) {  // W_phi^T staging overlaps the first batch's loads
-        load_wT_pairs<256>(sW, reinterpret_cast<const T *>(p.wk), tid);
-        staged = true;
-      }
-      float part[NB][8];
-#pragma unroll
-      for (int u = 0; u < NB; ++u)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          part[u][e] = (to_f(raw[u][0].v[e]) + to_f(raw[u][1].v[e])) + (to_f(raw[u][2].v[e]) + to_f(raw[u][3].v[e]));
-#pragma unroll
-      for (int u = 0; u < NB; ++u)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float v = wave_sum_cols(part[u][e]);
-          if (lane < 16) red[(I * NB + u) * D + 8 * fq + e] = v;
-        }
-      __syncthreads();
-      int bits = 0;  // bit u: the scanned sum through chunk top - u is below -SKIP_LOG
-      if (tid < D) {
-#pragma unroll
-        for (int u = 0; u < NB; ++u) {
-          if (top - u > b0) suf += red[u * D + tid] + red[(NB + u) * D + tid] + red[(2 * NB + u) * D + tid] + red[(3 * NB + u) * D + tid];
-          bits |= (top - u > b0 && suf < -SKIP_LOG) ? 1 << u : 0;
-        }
-        int all = 0;
-#pragma unroll
-        for (int u = 0; u < NB; ++u) all |= __all((bits >> u) & 1) ? 1 << u : 0;
-        if (lane == 0) vote[I] = all;
-      }
-      __syncthreads();
-      const int both = vote[0] & vote[1];
-      __syncthreads();  // red and vote are rewritten by the next batch
-      if (both) {
-        c_start = top - (__ffs(both) - 1);  // the latest chunk through which every feature is below
-        break;
-      }
-    }
-  }
-  if (c_start == b0 && b1 - 1 <= b0) load_wT_pairs<256>(sW, reinterpret_cast<const T *>(p.wk), tid);  // no scan ran
-  const int nneed = b1 - c_start, len = (nneed + p.sss - 1) / p.sss;
-  const int c_begin = min(c_start + pp * len, b1), c_end = min(c_begin + len, b1);
   auto load_k = [&](Frag<T> (&kf)[KS], int c0) {
     const T *src = Kh + (size_t)(c0 + 16 * I + r16) * D;
 #pragma unroll
@@ -1243,23 +1198,26 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
       for (int gsel = 0; gsel < 2; ++gsel) f[gsel][h] = load8(base + (size_t)(c0 + 2 * tp + h) * D + 8 * ((tid >> 5) + 8 * gsel));
   };
   Frag<T> kf[KS], vf[2][2], lf[2][2];
-  if (c_begin < c_end) {
-    load_k(kf, c_begin * CH);
-    load_pairs(vf, Vh, c_begin * CH);
-    load_pairs(lf, LGh, c_begin * CH);
-  }
+  int c = b1 - 1;
+  load_pairs(lf, LGh, c * CH);
+  load_k(kf, (c - pp) * CH);  // this piece's first chunk (p.sss <= p.cps)
+  load_pairs(vf, Vh, (c - pp) * CH);
+  load_wT_pairs<256>(sW, reinterpret_cast<const T *>(p.wk), tid);  // overlaps the first loads
   f32x4 S[FTW][NDT];
 #pragma unroll
   for (int ft = 0; ft < FTW; ++ft)
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) S[ft][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float dsum = 0.f;  // thread tid < D: sum of log gamma of feature tid
+  float suf = 0.f;  // thread tid < D: log-gate sum of feature tid over the chunks walked so far
+  if (tid < D) sSuf[tid] = 0.f;
   const Frag<T> tri_c0 = tri64_frag<T>(r16, g4, I, 0), tri_c1 = tri64_frag<T>(r16, g4, I, 1);
+  bool stopped = false;
   __syncthreads();
 
-  for (int c = c_begin; c < c_end; ++c) {
+  for (int par = 0;; par ^= 1, --c) {
+    const bool mine = own(c);
     float ko[NFT][4];
-    {
+    if (mine) {
       f32x4 z[NFT];
       feature_logits_pipe(sW, kf, r16, g4, z);
       softmax_rows<NFT>(z, ko);
@@ -1270,14 +1228,16 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
 #pragma unroll
       for (int gsel = 0; gsel < 2; ++gsel) {
         const int gq = (tid >> 5) + 8 * gsel;
-        store_pairT<T, LDV>(vf[gsel][0], vf[gsel][1], sVt + (8 * gq) * LDV + vpos);
+        if (mine) store_pairT<T, LDV>(vf[gsel][0], vf[gsel][1], sVt + (8 * gq) * LDV + vpos);
         store_pairT<T, LDV>(lf[gsel][0], lf[gsel][1], sLgT + (8 * gq) * LDV + 2 * tp);
       }
     }
-    if (c + 1 < c_end) {
-      load_k(kf, (c + 1) * CH);
-      load_pairs(vf, Vh, (c + 1) * CH);
-      load_pairs(lf, LGh, (c + 1) * CH);
+    // in flight from here: the log gates of the next chunk back, the keys and values of this
+    // piece's next chunk (p.sss chunks back: the walk's cheap chunks in between hide the loads)
+    if (c > b0) load_pairs(lf, LGh, (c - 1) * CH);
+    if (mine && c - sss >= b0) {
+      load_k(kf, (c - sss) * CH);
+      load_pairs(vf, Vh, (c - sss) * CH);
     }
     __syncthreads();
     float pc[NFT][4];
@@ -1294,41 +1254,48 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
         *reinterpret_cast<f32x4 *>(sTot + I * D + 16 * ft + 4 * g4) = f32x4{pc[ft][0], pc[ft][1], pc[ft][2], pc[ft][3]};
     }
     __syncthreads();
-    if (tid < D) dsum += sTot[3 * D + tid];
-    const bool mild = chunk_is_mild_c<D>(sTot, lane);
-    if (mild) {
+    // suffix through this chunk, for the next chunk back; stop once every feature is below
+    if (tid < D) {
+      suf += sTot[3 * D + tid];
+      sSuf[(par ^ 1) * D + tid] = suf;
+      const bool below = __all(suf < -SKIP_LOG);
+      if (lane == 0) sVote[I] = below;
+    }
+    const bool mild = mine && chunk_is_mild_c<D>(sTot, lane);
+    if (mine) {
+      // decayed keys: mild chunk e^{-p_t} (chunk-start reference), else e^{C_I - p_t}
+      if (mild) {
 #pragma unroll
-      for (int ft = 0; ft < NFT; ++ft)
+        for (int ft = 0; ft < NFT; ++ft)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ko[ft][i] *= exp2_fast(-pc[ft][i] * LOG2E);
-    } else {
+          for (int i = 0; i < 4; ++i) ko[ft][i] *= exp2_fast(-pc[ft][i] * LOG2E);
+      } else {
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft) {
+          const f32x4 t = *reinterpret_cast<const f32x4 *>(sTot + I * D + 16 * ft + 4 * g4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ko[ft][i] *= __expf(t[i] - pc[ft][i]);
+        }
+      }
 #pragma unroll
       for (int ft = 0; ft < NFT; ++ft) {
-        const f32x4 t = *reinterpret_cast<const f32x4 *>(sTot + I * D + 16 * ft + 4 * g4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ko[ft][i] *= __expf(t[i] - pc[ft][i]);
+        const int fpos = 32 * (ft >> 1) + 8 * g4 + 4 * (ft & 1);
+        store4<T>(sKt + (16 * I + r16) * LDW + fpos, ko[ft][0], ko[ft][1], ko[ft][2], ko[ft][3]);
       }
     }
-#pragma unroll
-    for (int ft = 0; ft < NFT; ++ft) {
-      const int fpos = 32 * (ft >> 1) + 8 * g4 + 4 * (ft & 1);
-      store4<T>(sKt + (16 * I + r16) * LDW + fpos, ko[ft][0], ko[ft][1], ko[ft][2], ko[ft][3]);
-    }
     __syncthreads();
-    // S = diag(e^{C_3}) S + sum_s k~_s e^{...} v_s^T (factors from the prefix table)
-    {
+    const bool stop = sVote[0] && sVote[1];
+    if (mine) {
+      // S += sum_t k~_t e^{s + ...} v_t^T: key factors e^{s + C_3} (mild) or e^{s + C_3 - C_J}
+      // for sub-chunk J, s = the suffix after this chunk (feature of the key row)
       Frag<T> ka[FTW][2];
-      float e[FTW][4];
 #pragma unroll
       for (int ft = 0; ft < FTW; ++ft) {
         const int fr = 16 * (2 * I + ft);
-        const f32x4 c3 = *reinterpret_cast<const f32x4 *>(sTot + 3 * D + fr + 4 * g4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) e[ft][i] = __expf(c3[i]);
         float fac[2][2];
-        const float c3r = sTot[3 * D + fr + r16];
+        const float c3s = sTot[3 * D + fr + r16] + sSuf[par * D + fr + r16];
 #pragma unroll
-        for (int J = 0; J < 4; ++J) fac[J >> 1][J & 1] = __expf(mild ? c3r : c3r - sTot[J * D + fr + r16]);
+        for (int J = 0; J < 4; ++J) fac[J >> 1][J & 1] = __expf(mild ? c3s : c3s - sTot[J * D + fr + r16]);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           float x[8];
@@ -1350,15 +1317,17 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
           for (int ks = 0; ks < 2; ++ks) vb[(dt + 1) & 1][ks] = load8(vrow + 16 * (dt + 1) * LDV + 32 * ks);
         }
 #pragma unroll
-        for (int ft = 0; ft < FTW; ++ft) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) S[ft][dt][i] *= e[ft][i];
+        for (int ft = 0; ft < FTW; ++ft)
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) S[ft][dt] = mma(ka[ft][ks], vb[dt & 1][ks], S[ft][dt]);
-        }
       }
     }
-    __syncthreads();
+    if (stop || c == b0) {
+      stopped = stop && c > b0;
+      break;
+    }
+    if (mine) __syncthreads();  // keys and values read before the next chunk is staged (the
+                                // other chunks' LDS reads all came before the last barrier)
   }
   float *E = p.ws_state + (size_t)grp * (D * D);
 #pragma unroll
@@ -1366,8 +1335,7 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
       *reinterpret_cast<f32x4 *>(E + ((size_t)((2 * I + ft) * NDT + dt) * 64 + lane) * 4) = S[ft][dt];
-  // the state carried into a block that starts late is dropped with the chunks before c_start
-  if (tid < D) p.ws_decay[(size_t)grp * D + tid] = (pp == 0 && c_start > b0) ? NEG_BIG : dsum;
+  if (tid < D) p.ws_decay[(size_t)grp * D + tid] = pp > 0 ? 0.f : (stopped ? NEG_BIG : suf);
 }
 
 hipError_t launch_fwd_full(const FwdParams &p, hipStream_t stream) {
@@ -1376,7 +1344,8 @@ hipError_t launch_fwd_full(const FwdParams &p, hipStream_t stream) {
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(fwd_full_state_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, full::ST_LDS_BYTES);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fwd_full_state_kernel, dim3(p.B * p.Hkv * (p.nseg - 1) * p.sss), dim3(256), full::ST_LDS_BYTES,
+    const int nblk = p.B * p.Hkv * (p.nseg - 1);  // pieces of a block 8 workgroups apart
+    hipLaunchKernelGGL(fwd_full_state_kernel, dim3(((nblk + 7) / 8) * 8 * p.sss), dim3(256), full::ST_LDS_BYTES,
                        stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
