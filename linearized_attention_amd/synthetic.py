@@ -102,7 +102,8 @@ def make_fwd_inputs(*, B: int, Hq: int, Hkv: int, L: int, d: int, W: int, M: int
                     dtype: str = "bf16", seed: int = 0, gate: str = "logsigmoid",
                     mix: float = 0.5, scale: float | None = None,
                     per_head_w: bool = False, separate_wk: bool = False,
-                    q_var: float = 1.0, k_var: float = 1.0) -> FwdInputs:
+                    q_var: float = 1.0, k_var: float = 1.0,
+                    phi_cols: int | None = None) -> FwdInputs:
     """Draw one forward problem.
 
     gate: "logsigmoid" (config recipe), "uniform" (U[-5,-1e-4]), "one"
@@ -110,9 +111,12 @@ def make_fwd_inputs(*, B: int, Hq: int, Hkv: int, L: int, d: int, W: int, M: int
     "const:<x>" (every entry equal to x), or "uniform:<lo>" (U[lo, -1e-4]).
     per_head_w: one W_phi per head ([Hq,d,d] / [Hkv,d,d]) instead of a shared one.
     separate_wk: draw an independent key-side W_phi (otherwise W_phi_k = W_phi_q).
+    phi_cols: columns of W_phi (default d).  The Hedgehog map exp(xW) (+) exp(-xW)
+    takes d // 2 columns, so that its feature dimension is d again.
     """
     rng = np.random.Generator(np.random.PCG64(seed))
-    wshape = (Hq, d, d) if per_head_w else (d, d)
+    cols = d if phi_cols is None else phi_cols
+    wshape = (Hq, d, cols) if per_head_w else (d, cols)
     w_phi = _normal(rng, wshape, 1.0 / d)
     kshape = (B, Hkv, L, d)
     if gate == "logsigmoid":
@@ -136,7 +140,7 @@ def make_fwd_inputs(*, B: int, Hq: int, Hkv: int, L: int, d: int, W: int, M: int
     tk = _normal(rng, (Hkv, M, d))
     tv = _normal(rng, (Hkv, M, d))
     if separate_wk:
-        wk = _normal(rng, (Hkv, d, d) if per_head_w else (d, d), 1.0 / d)
+        wk = _normal(rng, (Hkv, d, cols) if per_head_w else (d, cols), 1.0 / d)
     elif per_head_w:
         G = Hq // Hkv
         wk = w_phi[::G].copy()
@@ -178,9 +182,11 @@ class DecodeInputs:
 def make_decode_inputs(*, N: int, Hq: int, Hkv: int, d: int, W: int, M: int, steps: int,
                        pos0: int, dtype: str = "bf16", seed: int = 0,
                        state_var: float = 0.1, zero_state: bool = False,
-                       mix: float = 0.5, gate: str = "logsigmoid") -> DecodeInputs:
+                       mix: float = 0.5, gate: str = "logsigmoid",
+                       phi_cols: int | None = None) -> DecodeInputs:
+    """Draw one decode problem (phi_cols as in make_fwd_inputs)."""
     rng = np.random.Generator(np.random.PCG64(seed))
-    w_phi = _normal(rng, (d, d), 1.0 / d)
+    w_phi = _normal(rng, (d, d if phi_cols is None else phi_cols), 1.0 / d)
     w_gamma = _normal(rng, (d, d), 1.0 / d)
     tk = _normal(rng, (Hkv, M, d))
     tv = _normal(rng, (Hkv, M, d))

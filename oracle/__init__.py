@@ -51,11 +51,11 @@ def _load():
             i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
             lib.oracle_lizard_fwd.argtypes = [dp, dp, dp, dp, dp, dp, i64, dp, dp,
                                               i32, i32, i32, i32, i32, i32, i32, i32,
-                                              f64, f64, dp, dp, dp, dp]
+                                              f64, f64, i32, dp, dp, dp, dp]
             lib.oracle_lizard_fwd.restype = i32
             lib.oracle_lizard_decode.argtypes = [dp, dp, dp, ip, dp, dp, dp, dp, dp, dp,
                                                  i64, dp, dp, i32, i32, i32, i32, i32,
-                                                 i32, i32, f64, f64, dp, dp, dp]
+                                                 i32, i32, f64, f64, i32, dp, dp, dp]
             lib.oracle_lizard_decode.restype = i32
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = i32
@@ -84,30 +84,46 @@ def num_threads() -> int:
     return int(_load().oracle_num_threads())
 
 
+_FMAPS = {"softmax": 0, "hedgehog": 1}
+
+
+def _fmap_code(feature_map: str) -> int:
+    if feature_map not in _FMAPS:
+        raise ValueError(f"unknown feature map {feature_map!r}")
+    return _FMAPS[feature_map]
+
+
 def lizard_fwd(q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v, *, W: int, M: int,
                mix: float, scale: float, w_shared: bool | None = None,
-               return_branches: bool = False, return_state: bool = False):
+               return_branches: bool = False, return_state: bool = False,
+               feature_map: str = "softmax"):
     """Lizard attention forward in fp64.
 
     q [B,Hq,L,d]; k, v [B,Hkv,L,d]; log_gamma [B,Hkv,L,df];
-    w_phi_q, w_phi_k: [d,df] shared by all heads, or [Hq,d,df] / [Hkv,d,df];
+    w_phi_q, w_phi_k: [d,c] shared by all heads, or [Hq,d,c] / [Hkv,d,c], with
+    c = df for feature_map "softmax" and c = df/2 for "hedgehog"
+    (phi(x) = exp(xW) concatenated with exp(-xW));
     t_k, t_v [Hkv,M,d].  Returns y [B,Hq,L,d] (float64), plus (y_gla, y_win)
     and/or the final state [B,Hkv,df,d] when asked.
     """
+    fm = _fmap_code(feature_map)
     q, k, v, lg = _f64(q), _f64(k), _f64(v), _f64(log_gamma)
     wq, wk = _f64(w_phi_q), _f64(w_phi_k)
     tk, tv = _f64(t_k), _f64(t_v)
     B, Hq, L, d = q.shape
     Hkv = k.shape[1]
     df = lg.shape[-1]
+    cols = df // 2 if fm == 1 else df
+    if wq.shape[-2:] != (d, cols) or wk.shape[-2:] != (d, cols):
+        raise ValueError(f"W_phi must end in [{d},{cols}] for this feature map")
     if wq.ndim == 2:
         stride = 0
         if wk.ndim != 2:
             raise ValueError("w_phi_q and w_phi_k must both be shared or both per head")
     else:
         if wq.shape[0] != Hq or wk.shape[0] != Hkv:
-            raise ValueError("per-head W_phi must be [Hq,d,df] and [Hkv,d,df]")
-        stride = d * df
+            raise ValueError("per-head W_phi must be [Hq,d,c] and [Hkv,d,c]")
+        stride = d * cols
     if M == 0:
         tk = np.zeros((Hkv, 1, d))
         tv = np.zeros((Hkv, 1, d))
@@ -118,7 +134,7 @@ def lizard_fwd(q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v, *, W: int, M: int
     nul = ctypes.POINTER(ctypes.c_double)()
     rc = _load().oracle_lizard_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(lg), _ptr(wq), _ptr(wk), stride, _ptr(tk), _ptr(tv),
-        B, Hq, Hkv, L, d, df, W, M, float(mix), float(scale), _ptr(y),
+        B, Hq, Hkv, L, d, df, W, M, float(mix), float(scale), fm, _ptr(y),
         _ptr(yg) if yg is not None else nul, _ptr(yw) if yw is not None else nul,
         _ptr(st) if st is not None else nul)
     if rc != 0:
@@ -133,12 +149,14 @@ def lizard_fwd(q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v, *, W: int, M: int
 
 def lizard_decode(state, ring_k, ring_v, pos, q, k, v, log_gamma, w_phi_q, w_phi_k,
                   t_k, t_v, *, M: int, mix: float, scale: float,
-                  return_branches: bool = False):
+                  return_branches: bool = False, feature_map: str = "softmax"):
     """One decode step in fp64.  Returns (out, state, ring_k, ring_v, pos) as new
     float64/int32 arrays (inputs are not modified), plus (y_gla, y_win) if asked.
 
     state [N,Hkv,df,d]; ring_k/ring_v [N,Hkv,W,d]; pos [N] (tokens seen so far);
-    q [N,Hq,d]; k, v [N,Hkv,d]; log_gamma [N,Hkv,df]."""
+    q [N,Hq,d]; k, v [N,Hkv,d]; log_gamma [N,Hkv,df]; W_phi and feature_map
+    as in lizard_fwd."""
+    fm = _fmap_code(feature_map)
     st, rk, rv = _f64(state).copy(), _f64(ring_k).copy(), _f64(ring_v).copy()
     try:
         import torch
@@ -153,7 +171,10 @@ def lizard_decode(state, ring_k, ring_v, pos, q, k, v, log_gamma, w_phi_q, w_phi
     Hkv = k.shape[1]
     df = lg.shape[-1]
     W = rk.shape[2]
-    stride = 0 if wq.ndim == 2 else d * df
+    cols = df // 2 if fm == 1 else df
+    if wq.shape[-2:] != (d, cols) or wk.shape[-2:] != (d, cols):
+        raise ValueError(f"W_phi must end in [{d},{cols}] for this feature map")
+    stride = 0 if wq.ndim == 2 else d * cols
     if M == 0:
         tk = np.zeros((Hkv, 1, d))
         tv = np.zeros((Hkv, 1, d))
@@ -164,7 +185,7 @@ def lizard_decode(state, ring_k, ring_v, pos, q, k, v, log_gamma, w_phi_q, w_phi
     rc = _load().oracle_lizard_decode(
         _ptr(st), _ptr(rk), _ptr(rv), ps.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
         _ptr(q), _ptr(k), _ptr(v), _ptr(lg), _ptr(wq), _ptr(wk), stride, _ptr(tk), _ptr(tv),
-        N, Hq, Hkv, d, df, W, M, float(mix), float(scale), _ptr(out),
+        N, Hq, Hkv, d, df, W, M, float(mix), float(scale), fm, _ptr(out),
         _ptr(yg) if yg is not None else nul, _ptr(yw) if yw is not None else nul)
     if rc != 0:
         raise ValueError("oracle_lizard_decode rejected the shapes")

@@ -8,12 +8,14 @@
  *
  * What it computes, and where the pages define it:
  *
- *   Feature map        phi(x) = softmax over features of (x . W_phi)
+ *   Feature map        fmap 0: phi(x) = softmax over features of (x . W_phi)
  *                      (the softmax-over-features map of the synthetic
- *                      workloads; the Lizard paper's own map is the
- *                      exp(xW) (+) exp(-xW) "Hedgehog" map, arXiv page,
- *                      Method section, hardware-efficient reparameterization
- *                      paragraph).
+ *                      workloads), W_phi [d, df].
+ *                      fmap 1: the Lizard paper's own "Hedgehog" map,
+ *                      phi(x) = exp(x . W_phi) (+) exp(-x . W_phi), the two
+ *                      halves concatenated, W_phi [d, df/2], df even
+ *                      (arXiv page, Method section, hardware-efficient
+ *                      reparameterization paragraph).  No normalisation.
  *   Global branch      h_i = gamma_i (.) h_{i-1} + phi(k_i) v_i^T,
  *                      y_i = phi(q_i)^T h_i, with a per-key-dimension gate
  *                      gamma_i = exp(log_gamma_i) that scales every row of h
@@ -36,9 +38,21 @@
 #include <stdlib.h>
 #include <string.h>
 
-/* phi = softmax_f( sum_i x[i] * w[i*df + f] ), max subtracted first. */
+/* fmap 0: phi = softmax_f( sum_i x[i] * w[i*df + f] ), max subtracted first.
+ * fmap 1: z_j = sum_i x[i] * w[i*(df/2) + j]; phi_j = exp(z_j) and
+ *         phi_{df/2 + j} = exp(-z_j) for j < df/2. */
 static void feature_map(const double *x, const double *w, int d, int df,
-                        double *z, double *phi) {
+                        int fmap, double *z, double *phi) {
+  if (fmap == 1) {
+    const int h = df / 2;
+    for (int j = 0; j < h; ++j) {
+      double acc = 0.0;
+      for (int i = 0; i < d; ++i) acc += x[i] * w[(int64_t)i * h + j];
+      phi[j] = exp(acc);
+      phi[h + j] = exp(-acc);
+    }
+    return;
+  }
   double zmax = -INFINITY;
   for (int f = 0; f < df; ++f) {
     double acc = 0.0;
@@ -63,8 +77,10 @@ static double dot(const double *a, const double *b, int n) {
 /*
  * Forward over whole sequences.
  *   q [B,Hq,L,d]; k, v [B,Hkv,L,d]; lg (log gamma) [B,Hkv,L,df]
- *   wq, wk: W_phi for query / key side, [.,d,df]; head h uses w + h*w_stride
- *           (w_stride = 0: one matrix shared by all heads)
+ *   wq, wk: W_phi for query / key side, [.,d,df] (fmap 0) or [.,d,df/2]
+ *           (fmap 1); head h uses w + h*w_stride (w_stride = 0: one matrix
+ *           shared by all heads)
+ *   fmap    feature map: 0 softmax over features, 1 Hedgehog (see above)
  *   tk, tv  [Hkv,M,d] meta-memory keys / values
  *   y, y_gla, y_win [B,Hq,L,d] (y_gla / y_win may be NULL)
  *   state_out [B,Hkv,df,d] final h (may be NULL)
@@ -75,10 +91,10 @@ int oracle_lizard_fwd(const double *q, const double *k, const double *v,
                       const double *lg, const double *wq, const double *wk,
                       int64_t w_stride, const double *tk, const double *tv,
                       int B, int Hq, int Hkv, int L, int d, int df, int W,
-                      int M, double mix, double scale, double *y,
+                      int M, double mix, double scale, int fmap, double *y,
                       double *y_gla, double *y_win, double *state_out) {
   if (B < 1 || Hq < 1 || Hkv < 1 || L < 0 || d < 1 || df < 1 || W < 1 ||
-      M < 0 || Hq % Hkv != 0)
+      M < 0 || Hq % Hkv != 0 || fmap < 0 || fmap > 1 || (fmap == 1 && df % 2))
     return -1;
   const int G = Hq / Hkv;
   const int nb = B * Hq;
@@ -106,8 +122,8 @@ int oracle_lizard_fwd(const double *q, const double *k, const double *v,
       const double *vi = vh + (int64_t)i * d;
       const double *gi = gh + (int64_t)i * df;
       /* global branch: decay every key-dimension row, then add phi(k) v^T */
-      feature_map(ki, wkh, d, df, z, phk);
-      feature_map(qi, wqh, d, df, z, phq);
+      feature_map(ki, wkh, d, df, fmap, z, phk);
+      feature_map(qi, wqh, d, df, fmap, z, phq);
       for (int f = 0; f < df; ++f) {
         const double gam = exp(gi[f]);
         double *row = S + (int64_t)f * d;
@@ -167,6 +183,7 @@ int oracle_lizard_fwd(const double *q, const double *k, const double *v,
  *   pos [N]                      tokens already seen (index of the new token);
  *                                incremented
  *   q [N,Hq,d]; k, v [N,Hkv,d]; lg [N,Hkv,df]; out, y_gla, y_win [N,Hq,d]
+ *   wq, wk, w_stride, fmap: as in the forward
  * The per-token arithmetic is the forward's: decay then add, read out, and a
  * softmax over the M meta keys and the min(pos+1, W) newest keys.
  */
@@ -176,9 +193,9 @@ int oracle_lizard_decode(double *state, double *ring_k, double *ring_v,
                          const double *wk, int64_t w_stride, const double *tk,
                          const double *tv, int N, int Hq, int Hkv, int d,
                          int df, int W, int M, double mix, double scale,
-                         double *out, double *y_gla, double *y_win) {
+                         int fmap, double *out, double *y_gla, double *y_win) {
   if (N < 1 || Hq < 1 || Hkv < 1 || d < 1 || df < 1 || W < 1 || M < 0 ||
-      Hq % Hkv != 0)
+      Hq % Hkv != 0 || fmap < 0 || fmap > 1 || (fmap == 1 && df % 2))
     return -1;
   for (int n = 0; n < N; ++n)
     if (pos[n] < 0) return -1;
@@ -197,7 +214,7 @@ int oracle_lizard_decode(double *state, double *ring_k, double *ring_v,
       const int64_t nh = (int64_t)n * Hkv + hk;
       const double *kt = k + nh * d, *vt = v + nh * d, *gt = lg + nh * df;
       double *S = state + nh * df * d;
-      feature_map(kt, wk + (int64_t)hk * w_stride, d, df, z, phi);
+      feature_map(kt, wk + (int64_t)hk * w_stride, d, df, fmap, z, phi);
       for (int f = 0; f < df; ++f) {
         const double gam = exp(gt[f]);
         for (int e = 0; e < d; ++e)
@@ -211,7 +228,7 @@ int oracle_lizard_decode(double *state, double *ring_k, double *ring_v,
       const int64_t nh = (int64_t)n * Hkv + hk;
       const double *qt = q + ((int64_t)n * Hq + hq) * d;
       const double *S = state + nh * df * d;
-      feature_map(qt, wq + (int64_t)hq * w_stride, d, df, z, phi);
+      feature_map(qt, wq + (int64_t)hq * w_stride, d, df, fmap, z, phi);
       for (int e = 0; e < d; ++e) yg[e] = 0.0;
       for (int f = 0; f < df; ++f)
         for (int e = 0; e < d; ++e) yg[e] += phi[f] * S[(int64_t)f * d + e];

@@ -92,3 +92,54 @@ def test_pins_catch_mutant(name, orig, mut, tmp_path, monkeypatch):
         except AssertionError:
             failures += 1
     assert failures > 0, f"no pin caught mutant {name!r}"
+
+
+# Mutants of the Hedgehog feature map, against its own pins.
+import tests.test_oracle_hedgehog as hh_pins  # noqa: E402
+
+HH_MUTANTS = [
+    ("hedgehog halves swapped",
+     "phi[j] = exp(acc);\n      phi[h + j] = exp(-acc);",
+     "phi[j] = exp(-acc);\n      phi[h + j] = exp(acc);"),
+    ("hedgehog second half not negated",
+     "phi[h + j] = exp(-acc);",
+     "phi[h + j] = exp(acc);"),
+    ("hedgehog weights read transposed",
+     "acc += x[i] * w[(int64_t)i * h + j];",
+     "acc += x[i] * w[(int64_t)j * d + i];"),
+    ("hedgehog normalised like softmax",
+     "phi[h + j] = exp(-acc);\n    }\n    return;",
+     "phi[h + j] = exp(-acc);\n    }\n    for (int f = 0; f < df; ++f) phi[f] /= df;\n    return;"),
+]
+
+HH_PIN_FUNCS = [
+    lambda: hh_pins.test_gamma_one_is_a_causal_cosh_kernel_sum(False),
+    lambda: hh_pins.test_gamma_one_is_a_causal_cosh_kernel_sum(True),
+    hh_pins.test_zero_weights_give_unit_features_and_a_geometric_gate,
+    hh_pins.test_sign_flip_swaps_the_halves,
+    hh_pins.test_gate_halves_fix_the_order_of_the_halves,
+]
+
+
+@pytest.mark.parametrize("name,orig,mut", HH_MUTANTS, ids=[m[0] for m in HH_MUTANTS])
+def test_hedgehog_pins_catch_mutant(name, orig, mut, tmp_path, monkeypatch):
+    src = open(SRC).read()
+    assert src.count(orig) >= 1, f"mutation anchor for {name!r} not found"
+    cpath = tmp_path / "mut.c"
+    cpath.write_text(src.replace(orig, mut, 1))
+    so = tmp_path / "libmut.so"
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-std=c99", str(cpath),
+                    "-o", str(so), "-lm"], check=True)
+    real = oracle._load()
+    lib = ctypes.CDLL(str(so))
+    for fn in ("oracle_lizard_fwd", "oracle_lizard_decode", "oracle_num_threads"):
+        getattr(lib, fn).argtypes = getattr(real, fn).argtypes
+        getattr(lib, fn).restype = getattr(real, fn).restype
+    monkeypatch.setattr(oracle, "_lib", lib)
+    failures = 0
+    for fn in HH_PIN_FUNCS:
+        try:
+            fn()
+        except AssertionError:
+            failures += 1
+    assert failures > 0, f"no pin caught mutant {name!r}"
