@@ -46,7 +46,9 @@
  *     log_gamma <= 0 (gamma in (0,1]; use a large finite negative value such
  *     as -1e4 for gamma = 0, never -inf); outputs do not alias inputs.
  *   - Supported head dimensions: d = 64 or 128 for bf16, d = 64 for fp32.
- *     The feature dimension equals d.  Meta tokens: 0 <= M <= 16.
+ *     The feature dimension equals d for both feature maps (the softmax map
+ *     above, and the Hedgehog map of the *_hedgehog entry points, whose
+ *     W_phi is [d, d/2]).  Meta tokens: 0 <= M <= 16.
  */
 #ifndef LIZARD_ATTN_H
 #define LIZARD_ATTN_H
@@ -94,9 +96,35 @@ lizard_status lizard_attn_fwd(const void *q, const void *k, const void *v,
                               lizard_dtype dtype, void *workspace,
                               size_t workspace_bytes, void *stream);
 
-/* Workspace bytes lizard_attn_fwd needs for these shapes (0 if none). */
+/* Workspace bytes lizard_attn_fwd needs for these shapes (0 if none).  It
+ * also covers lizard_attn_fwd_hedgehog. */
 size_t lizard_attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int L, int d,
                                        int W, lizard_dtype dtype);
+
+/*
+ * Forward with the Lizard paper's own feature map, the Hedgehog map
+ *   phi(x) = exp(x . W_phi) (+) exp(-x . W_phi)
+ * (the two halves concatenated, exp(xW) first, no normalisation; arXiv page,
+ * Method section, the hardware-efficient reparameterization paragraph), in
+ * place of the softmax over features.  W_phi is [d, d/2], so that the
+ * feature dimension -- the rows of the state and the entries of log_gamma per
+ * token -- is d: feature f < d/2 is exp((xW)_f), feature d/2 + f is
+ * exp(-(xW)_f).  Everything else as in lizard_attn_fwd, with the same
+ * workspace.  Built for bf16, d = 128, W <= 129, and one W_phi shared by
+ * queries, keys and heads (w_phi_q == w_phi_k, w_phi_head_stride = 0); other
+ * requests return LIZARD_ERR_UNSUPPORTED.  Precondition, not checked: the
+ * logits x . W_phi stay within about +-80, where exp is finite in fp32.
+ */
+lizard_status lizard_attn_fwd_hedgehog(const void *q, const void *k,
+                                       const void *v, const void *log_gamma,
+                                       const void *w_phi_q, const void *w_phi_k,
+                                       int64_t w_phi_head_stride,
+                                       const void *t_k, const void *t_v,
+                                       void *out, int B, int Hq, int Hkv,
+                                       int L, int d, int W, int M, float mix,
+                                       float scale, lizard_dtype dtype,
+                                       void *workspace, size_t workspace_bytes,
+                                       void *stream);
 
 /*
  * Forward as a continuation (chunked prefill feeding decode): the L new tokens
@@ -175,6 +203,28 @@ lizard_status lizard_attn_decode(float *state, void *win_k, void *win_v,
  * 0 for an empty or invalid shape. */
 size_t lizard_attn_decode_workspace_bytes(int N, int Hq, int Hkv, int d,
                                           lizard_dtype dtype);
+
+/*
+ * One decode step with the Hedgehog feature map (see lizard_attn_fwd_hedgehog):
+ * W_phi is [d, d/2] per matrix (w_phi_head_stride = 0, or at least d*d/2
+ * elements between heads' matrices), the state's rows are the d features
+ * exp(xW) (+) exp(-xW).  Everything else, the workspace included, as in
+ * lizard_attn_decode, for the same dtypes and head dimensions.  Running L
+ * steps from a zero state reproduces lizard_attn_fwd_hedgehog on those tokens.
+ */
+lizard_status lizard_attn_decode_hedgehog(float *state, void *win_k,
+                                          void *win_v, int32_t *pos,
+                                          const void *q, const void *k,
+                                          const void *v, const void *log_gamma,
+                                          const void *w_phi_q,
+                                          const void *w_phi_k,
+                                          int64_t w_phi_head_stride,
+                                          const void *t_k, const void *t_v,
+                                          void *out, int N, int Hq, int Hkv,
+                                          int d, int W, int M, float mix,
+                                          float scale, lizard_dtype dtype,
+                                          void *workspace,
+                                          size_t workspace_bytes, void *stream);
 
 /* Static text for a status code. */
 const char *lizard_status_string(lizard_status s);

@@ -23,9 +23,10 @@ _STATUS = {0: "LIZARD_OK", 1: "LIZARD_ERR_INVALID_ARG", 2: "LIZARD_ERR_UNSUPPORT
            3: "LIZARD_ERR_WORKSPACE", 4: "LIZARD_ERR_HIP"}
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
-EXPORTED = ("lizard_attn_fwd", "lizard_attn_fwd_workspace_bytes", "lizard_attn_fwd_ext",
-            "lizard_attn_fwd_ext_workspace_bytes", "lizard_attn_decode",
-            "lizard_attn_decode_workspace_bytes", "lizard_status_string", "lizard_last_error", "lizard_version")
+EXPORTED = ("lizard_attn_fwd", "lizard_attn_fwd_workspace_bytes", "lizard_attn_fwd_hedgehog",
+            "lizard_attn_fwd_ext", "lizard_attn_fwd_ext_workspace_bytes", "lizard_attn_decode",
+            "lizard_attn_decode_hedgehog", "lizard_attn_decode_workspace_bytes",
+            "lizard_status_string", "lizard_last_error", "lizard_version")
 
 _lock = threading.Lock()
 _lib = None
@@ -54,6 +55,10 @@ def _declare(lib):
     lib.lizard_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp,
                                        i32, i32, i32, i32, i32, i32, f32, f32, i32, vp, sz, vp]
     lib.lizard_attn_decode.restype = i32
+    lib.lizard_attn_fwd_hedgehog.argtypes = lib.lizard_attn_fwd.argtypes
+    lib.lizard_attn_fwd_hedgehog.restype = i32
+    lib.lizard_attn_decode_hedgehog.argtypes = lib.lizard_attn_decode.argtypes
+    lib.lizard_attn_decode_hedgehog.restype = i32
     lib.lizard_attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.lizard_attn_decode_workspace_bytes.restype = sz
     lib.lizard_status_string.argtypes = [i32]
@@ -108,12 +113,15 @@ def lizard_attn_fwd_workspace_bytes(B: int, Hq: int, Hkv: int, L: int, d: int, W
     return int(load().lizard_attn_fwd_workspace_bytes(B, Hq, Hkv, L, d, W, _DTYPES[dtype]))
 
 
-def _w_stride(w_q, w_k, d):
+def _w_stride(w_q, w_k, d, cols=None):
+    cols = d if cols is None else cols
+    if w_q.shape[-2:] != (d, cols) or w_k.shape[-2:] != (d, cols):
+        raise ValueError(f"w_phi_q and w_phi_k must end in [{d},{cols}] for this feature map")
     if w_q.dim() == 2 and w_k.dim() == 2:
         return 0
     if w_q.dim() == 3 and w_k.dim() == 3:
-        return d * d
-    raise ValueError("w_phi_q and w_phi_k must both be [d,d] (shared) or both per head")
+        return d * cols
+    raise ValueError("w_phi_q and w_phi_k must both be shared or both per head")
 
 
 def lizard_attn_fwd(q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v, *, W: int, M: int,
@@ -122,6 +130,23 @@ def lizard_attn_fwd(q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v, *, W: int, M
     """Lizard attention forward on the GPU.  Shapes: q [B,Hq,L,d]; k, v, log_gamma
     [B,Hkv,L,d]; w_phi_q/w_phi_k [d,d] or [Hq|Hkv,d,d]; t_k, t_v [Hkv,M,d].
     Returns out [B,Hq,L,d] in the input dtype."""
+    return _fwd(load().lizard_attn_fwd, q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v, W=W, M=M,
+                mix=mix, scale=scale, out=out, workspace=workspace, stream=stream, cols=q.shape[-1])
+
+
+def lizard_attn_fwd_hedgehog(q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v, *, W: int, M: int,
+                             mix: float = 0.5, scale: float | None = None, out=None,
+                             workspace=None, stream=None):
+    """Forward with the Hedgehog map phi(x) = exp(xW) (+) exp(-xW): w_phi_q/w_phi_k [d, d/2]
+    (the library takes one matrix shared by both sides and all heads).  Otherwise as
+    lizard_attn_fwd."""
+    return _fwd(load().lizard_attn_fwd_hedgehog, q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v,
+                W=W, M=M, mix=mix, scale=scale, out=out, workspace=workspace, stream=stream,
+                cols=q.shape[-1] // 2)
+
+
+def _fwd(fn, q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v, *, W, M, mix, scale, out,
+         workspace, stream, cols):
     dt = q.dtype
     if dt not in _DTYPES:
         raise ValueError(f"unsupported dtype {dt}")
@@ -147,9 +172,9 @@ def lizard_attn_fwd(q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v, *, W: int, M
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(load().lizard_attn_fwd(
+    _check(fn(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), _ptr(w_phi_q), _ptr(w_phi_k),
-        _w_stride(w_phi_q, w_phi_k, d), _ptr(t_k) if M > 0 else None, _ptr(t_v) if M > 0 else None,
+        _w_stride(w_phi_q, w_phi_k, d, cols), _ptr(t_k) if M > 0 else None, _ptr(t_v) if M > 0 else None,
         _ptr(out), B, Hq, Hkv, L, d, W, M, float(mix), float(scale), _DTYPES[dt],
         _ptr(workspace), wbytes, _stream(stream)))
     return out
@@ -224,6 +249,23 @@ def lizard_attn_decode(state, win_k, win_v, pos, q, k, v, log_gamma, w_phi_q, w_
                        workspace=None, stream=None):
     """One decode step, in place on state [N,Hkv,d,d] fp32, win_k/win_v [N,Hkv,W,d],
     pos [N] int32.  q [N,Hq,d]; k, v, log_gamma [N,Hkv,d].  Returns out [N,Hq,d]."""
+    return _decode(load().lizard_attn_decode, state, win_k, win_v, pos, q, k, v, log_gamma,
+                   w_phi_q, w_phi_k, t_k, t_v, M=M, mix=mix, scale=scale, out=out,
+                   workspace=workspace, stream=stream, cols=q.shape[-1])
+
+
+def lizard_attn_decode_hedgehog(state, win_k, win_v, pos, q, k, v, log_gamma, w_phi_q, w_phi_k,
+                                t_k, t_v, *, M: int, mix: float = 0.5, scale: float | None = None,
+                                out=None, workspace=None, stream=None):
+    """One decode step with the Hedgehog map: w_phi_q/w_phi_k [d, d/2] or [Hq|Hkv, d, d/2].
+    Otherwise as lizard_attn_decode."""
+    return _decode(load().lizard_attn_decode_hedgehog, state, win_k, win_v, pos, q, k, v,
+                   log_gamma, w_phi_q, w_phi_k, t_k, t_v, M=M, mix=mix, scale=scale, out=out,
+                   workspace=workspace, stream=stream, cols=q.shape[-1] // 2)
+
+
+def _decode(fn, state, win_k, win_v, pos, q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v, *, M,
+            mix, scale, out, workspace, stream, cols):
     dt = q.dtype
     if dt not in _DTYPES:
         raise ValueError(f"unsupported dtype {dt}")
@@ -252,9 +294,9 @@ def lizard_attn_decode(state, win_k, win_v, pos, q, k, v, log_gamma, w_phi_q, w_
         need = lizard_attn_decode_workspace_bytes(N, Hq, Hkv, d, dt)
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     wbytes = workspace.numel() * workspace.element_size()
-    _check(load().lizard_attn_decode(
+    _check(fn(
         _ptr(state), _ptr(win_k), _ptr(win_v), _ptr(pos), _ptr(q), _ptr(k), _ptr(v),
-        _ptr(log_gamma), _ptr(w_phi_q), _ptr(w_phi_k), _w_stride(w_phi_q, w_phi_k, d),
+        _ptr(log_gamma), _ptr(w_phi_q), _ptr(w_phi_k), _w_stride(w_phi_q, w_phi_k, d, cols),
         _ptr(t_k) if M > 0 else None, _ptr(t_v) if M > 0 else None, _ptr(out),
         N, Hq, Hkv, d, W, M, float(mix), float(scale), _DTYPES[dt], _ptr(workspace), wbytes,
         _stream(stream)))

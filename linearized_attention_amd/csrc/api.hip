@@ -139,7 +139,7 @@ lizard_status fwd_impl(const void *q, const void *k, const void *v, const void *
                        const void *w_phi_k, int64_t w_phi_head_stride, const void *t_k, const void *t_v, void *out,
                        int B, int Hq, int Hkv, int L, int d, int W, int M, float mix, float scale,
                        lizard_dtype dtype, void *workspace, size_t workspace_bytes, void *stream,
-                       const FwdExt *ext) {
+                       const FwdExt *ext, bool hedgehog = false) {
   if (dtype != LIZARD_F32 && dtype != LIZARD_BF16) return fail(LIZARD_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
   if (B < 0 || L < 0) return fail(LIZARD_ERR_INVALID_ARG, "B=%d and L=%d must be >= 0", B, L);
   if (Hq < 1 || Hkv < 1 || d < 1 || W < 1 || M < 0)
@@ -153,6 +153,10 @@ lizard_status fwd_impl(const void *q, const void *k, const void *v, const void *
   if (w_phi_head_stride != 0 && w_phi_head_stride < (int64_t)d * d)
     return fail(LIZARD_ERR_INVALID_ARG, "w_phi_head_stride=%lld overlaps matrices of d*d elements",
                 (long long)w_phi_head_stride);
+  if (hedgehog && !use_full_kernel(Hq, Hkv, d, W, dtype, w_phi_q, w_phi_k, w_phi_head_stride))
+    return fail(LIZARD_ERR_UNSUPPORTED,
+                "the Hedgehog map is built for bf16, d = 128, W <= %d and one W_phi for queries, keys and "
+                "heads (w_phi_q == w_phi_k, stride 0)", 2 * kChunk + 1);
   if (B == 0 || L == 0) return LIZARD_OK;  // empty problem
   if (!q || !k || !v || !log_gamma || !w_phi_q || !w_phi_k || !out)
     return fail(LIZARD_ERR_INVALID_ARG, "null tensor pointer");
@@ -200,6 +204,7 @@ lizard_status fwd_impl(const void *q, const void *k, const void *v, const void *
   p.per_head_q = w_phi_head_stride != 0;
   p.full = full ? 1 : 0;
   p.sss = plan.sss;
+  p.hh = hedgehog ? 1 : 0;
   p.mix = mix; p.scale = scale;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int esize = dtype == LIZARD_BF16 ? 2 : 4;
@@ -257,6 +262,15 @@ lizard_status lizard_attn_fwd(const void *q, const void *k, const void *v, const
                   mix, scale, dtype, workspace, workspace_bytes, stream, nullptr);
 }
 
+lizard_status lizard_attn_fwd_hedgehog(const void *q, const void *k, const void *v, const void *log_gamma,
+                                       const void *w_phi_q, const void *w_phi_k, int64_t w_phi_head_stride,
+                                       const void *t_k, const void *t_v, void *out, int B, int Hq, int Hkv, int L,
+                                       int d, int W, int M, float mix, float scale, lizard_dtype dtype,
+                                       void *workspace, size_t workspace_bytes, void *stream) {
+  return fwd_impl(q, k, v, log_gamma, w_phi_q, w_phi_k, w_phi_head_stride, t_k, t_v, out, B, Hq, Hkv, L, d, W, M,
+                  mix, scale, dtype, workspace, workspace_bytes, stream, nullptr, true);
+}
+
 size_t lizard_attn_fwd_ext_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int W, lizard_dtype dtype) {
   (void)Hq;
   if (B <= 0 || L <= 0 || Hkv <= 0 || d <= 0 || d % kDV != 0) return 0;
@@ -290,11 +304,11 @@ size_t lizard_attn_decode_workspace_bytes(int N, int Hq, int Hkv, int d, lizard_
   return lz::decode_workspace_bytes(N, Hq, Hkv, d);
 }
 
-lizard_status lizard_attn_decode(float *state, void *win_k, void *win_v, int32_t *pos, const void *q, const void *k,
+static lizard_status decode_impl(float *state, void *win_k, void *win_v, int32_t *pos, const void *q, const void *k,
                                  const void *v, const void *log_gamma, const void *w_phi_q, const void *w_phi_k,
                                  int64_t w_phi_head_stride, const void *t_k, const void *t_v, void *out, int N, int Hq,
                                  int Hkv, int d, int W, int M, float mix, float scale, lizard_dtype dtype,
-                                 void *workspace, size_t workspace_bytes, void *stream) {
+                                 void *workspace, size_t workspace_bytes, void *stream, bool hedgehog) {
   if (dtype != LIZARD_F32 && dtype != LIZARD_BF16) return fail(LIZARD_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
   if (N < 0) return fail(LIZARD_ERR_INVALID_ARG, "N=%d must be >= 0", N);
   if (Hq < 1 || Hkv < 1 || d < 1 || W < 1 || M < 0)
@@ -307,9 +321,10 @@ lizard_status lizard_attn_decode(float *state, void *win_k, void *win_v, int32_t
   if (M > kMaxMeta) return fail(LIZARD_ERR_UNSUPPORTED, "M=%d meta tokens (at most %d)", M, kMaxMeta);
   if (W > lz::decode_max_window())
     return fail(LIZARD_ERR_UNSUPPORTED, "decode window W=%d (at most %d)", W, lz::decode_max_window());
-  if (w_phi_head_stride != 0 && w_phi_head_stride < (int64_t)d * d)
-    return fail(LIZARD_ERR_INVALID_ARG, "w_phi_head_stride=%lld overlaps matrices of d*d elements",
-                (long long)w_phi_head_stride);
+  const int64_t wsize = (int64_t)d * (hedgehog ? d / 2 : d);  // elements of one W_phi
+  if (w_phi_head_stride != 0 && w_phi_head_stride < wsize)
+    return fail(LIZARD_ERR_INVALID_ARG, "w_phi_head_stride=%lld overlaps matrices of %lld elements",
+                (long long)w_phi_head_stride, (long long)wsize);
   if (N == 0) return LIZARD_OK;
   if (!state || !win_k || !win_v || !pos || !q || !k || !v || !log_gamma || !w_phi_q || !w_phi_k || !out)
     return fail(LIZARD_ERR_INVALID_ARG, "null tensor pointer");
@@ -331,8 +346,28 @@ lizard_status lizard_attn_decode(float *state, void *win_k, void *win_v, int32_t
   p.ws_phi = static_cast<float *>(workspace);
   p.ws_count = reinterpret_cast<int *>(p.ws_phi + (size_t)N * Hq * d + (size_t)N * Hkv * d);  // after phi
   p.N = N; p.Hq = Hq; p.Hkv = Hkv; p.W = W; p.M = M; p.G = Hq / Hkv; p.mix = mix; p.scale = scale;
+  p.hh = hedgehog ? 1 : 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
   return finish(lz::launch_decode(p, dtype == LIZARD_BF16, d, st), st);
+}
+
+lizard_status lizard_attn_decode(float *state, void *win_k, void *win_v, int32_t *pos, const void *q, const void *k,
+                                 const void *v, const void *log_gamma, const void *w_phi_q, const void *w_phi_k,
+                                 int64_t w_phi_head_stride, const void *t_k, const void *t_v, void *out, int N, int Hq,
+                                 int Hkv, int d, int W, int M, float mix, float scale, lizard_dtype dtype,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
+  return decode_impl(state, win_k, win_v, pos, q, k, v, log_gamma, w_phi_q, w_phi_k, w_phi_head_stride, t_k, t_v,
+                     out, N, Hq, Hkv, d, W, M, mix, scale, dtype, workspace, workspace_bytes, stream, false);
+}
+
+lizard_status lizard_attn_decode_hedgehog(float *state, void *win_k, void *win_v, int32_t *pos, const void *q,
+                                          const void *k, const void *v, const void *log_gamma, const void *w_phi_q,
+                                          const void *w_phi_k, int64_t w_phi_head_stride, const void *t_k,
+                                          const void *t_v, void *out, int N, int Hq, int Hkv, int d, int W, int M,
+                                          float mix, float scale, lizard_dtype dtype, void *workspace,
+                                          size_t workspace_bytes, void *stream) {
+  return decode_impl(state, win_k, win_v, pos, q, k, v, log_gamma, w_phi_q, w_phi_k, w_phi_head_stride, t_k, t_v,
+                     out, N, Hq, Hkv, d, W, M, mix, scale, dtype, workspace, workspace_bytes, stream, true);
 }
 
 }  // extern "C"

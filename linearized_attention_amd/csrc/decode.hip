@@ -15,7 +15,8 @@
 //   decode_phi   every feature map of the step as one small GEMM on the matrix
 //                cores: rows are the new keys (per key/value head) and queries
 //                (per query head) of 64 sequences, times W_phi staged
-//                transposed in LDS, then the softmax over features.  fp32
+//                transposed in LDS, then the softmax over features (or the
+//                Hedgehog map's exponential).  fp32
 //                results go to the workspace.
 //   decode_step  one workgroup per (sequence, key/value head), bound by HBM
 //                traffic.  It issues its loads in the order it consumes them
@@ -53,7 +54,9 @@ template <typename T> __device__ __forceinline__ void opaque(Frag<T> &f) {
 
 // grid (ceil(N / 64), Hkv + Hq): y < Hkv is the key side of key/value head y,
 // otherwise query head y - Hkv.  Wave w owns rows 16w .. 16w+15 of the tile.
-template <typename T, int D>
+// HH: the Hedgehog map, phi(x) = exp(xW) (+) exp(-xW) with W_phi [D][D/2] (W^T staged with its
+// negation below it, so the logits of the D features are (xW, -xW)); no normalisation.
+template <typename T, int D, bool HH>
 __global__ __launch_bounds__(256) void decode_phi_kernel(DecParams p) {
   constexpr int LDW = D + 16 / (int)sizeof(T);  // padded row of W^T (elements)
   constexpr int NC = D / 16;                    // 16-column output tiles
@@ -70,11 +73,15 @@ __global__ __launch_bounds__(256) void decode_phi_kernel(DecParams p) {
   if (hs == 0 && tid < DEC_ROWS && n0 + tid < N) p.ws_count[n0 + tid] = 0;
 
   const T *Wsrc = reinterpret_cast<const T *>(key ? p.wk : p.wq) + (size_t)h * p.w_stride;
-  for (int idx = tid; idx < D * (D / 8); idx += 256) {  // W[i][f] -> wt[f][i]
-    const int i = idx / (D / 8), f0 = (idx % (D / 8)) * 8;
-    const Frag<T> w = load8(Wsrc + (size_t)i * D + f0);
+  constexpr int FC = HH ? D / 2 : D;  // columns of W_phi
+  for (int idx = tid; idx < D * (FC / 8); idx += 256) {  // W[i][f] -> wt[f][i] (and -W -> wt[FC + f][i])
+    const int i = idx / (FC / 8), f0 = (idx % (FC / 8)) * 8;
+    const Frag<T> w = load8(Wsrc + (size_t)i * FC + f0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) wt[(f0 + j) * LDW + i] = w.v[j];
+    for (int j = 0; j < 8; ++j) {
+      wt[(f0 + j) * LDW + i] = w.v[j];
+      if constexpr (HH) wt[(FC + f0 + j) * LDW + i] = -w.v[j];
+    }
   }
 
   // A fragments straight from global: row n = n0 + 16*wv + r
@@ -98,20 +105,26 @@ __global__ __launch_bounds__(256) void decode_phi_kernel(DecParams p) {
   const int sub = key ? 0 : 1 + h % G;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    float m = DEC_NEG;
+    float inv = 1.f;
+    if constexpr (HH) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) m = fmaxf(m, acc[c][i]);
+      for (int c = 0; c < NC; ++c) acc[c][i] = __expf(acc[c][i]);
+    } else {
+      float m = DEC_NEG;
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-    float s = 0.f;
+      for (int c = 0; c < NC; ++c) m = fmaxf(m, acc[c][i]);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      acc[c][i] = __expf(acc[c][i] - m);
-      s += acc[c][i];
+      for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+      float s = 0.f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        acc[c][i] = __expf(acc[c][i] - m);
+        s += acc[c][i];
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
+      inv = 1.f / s;
     }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
-    const float inv = 1.f / s;
     const int nr = n0 + 16 * wv + 4 * kq + i;
     if (nr < N) {
       float *dst = p.ws_phi + (((size_t)nr * Hkv + hk) * (1 + G) + sub) * D;
@@ -415,8 +428,9 @@ __global__ __launch_bounds__(256, 2) void decode_step_kernel(DecParams p) {
 
 template <typename T, int D>
 static hipError_t launch_dec_t(const DecParams &p, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_phi_kernel<T, D>), dim3((p.N + DEC_ROWS - 1) / DEC_ROWS, p.Hkv + p.Hq), dim3(256),
-                     0, stream, p);
+  const dim3 pgrid((p.N + DEC_ROWS - 1) / DEC_ROWS, p.Hkv + p.Hq);
+  if (p.hh) hipLaunchKernelGGL((decode_phi_kernel<T, D, true>), pgrid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL((decode_phi_kernel<T, D, false>), pgrid, dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.G == 1)

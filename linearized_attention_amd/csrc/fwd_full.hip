@@ -77,6 +77,7 @@ __device__ __forceinline__ int islot(int kq, int j) { return 16 * (j >> 2) + 4 *
 // SPAN_MAX (e.g. gamma ~ 0): A[t][s] = mix sum_f phi_q[t][f] phi_k[s][f] e^{p_t[f] - p_s[f]}
 // in fp32, p the log-gamma prefix inside the sub-chunk, phi recomputed from q and the
 // keys.  Lane (t = lane % 16, g = lane / 16) returns s = 4g .. 4g+3.
+template <bool HH>
 __device__ __forceinline__ f32x4 exact_diag_scores(const bf16 *sW, const bf16 *Kh, const bf16 *LGh, const bf16 *Qh,
                                                  int c0, int I, int L, float mix) {
   using namespace full;
@@ -96,21 +97,27 @@ __device__ __forceinline__ f32x4 exact_diag_scores(const bf16 *sW, const bf16 *K
     for (int j = 0; j < KS; ++j) z = mma(load8(sW + (16 * ft + r16) * LDWW + 32 * j + 8 * g4), x[j], z);
     return z;
   };
-  float mq = NEG_BIG, mk = NEG_BIG;
-  for (int ft = 0; ft < NFT; ++ft) {
-    const f32x4 zq = logits_ft(qfr, ft), zk = logits_ft(kfr, ft);
+  // softmax map: max and normaliser per row; the Hedgehog map is the plain exponential
+  float mq = 0.f, mk = 0.f, iq = 1.f, ik = 1.f;
+  if constexpr (!HH) {
+    mq = NEG_BIG;
+    mk = NEG_BIG;
+    for (int ft = 0; ft < NFT; ++ft) {
+      const f32x4 zq = logits_ft(qfr, ft), zk = logits_ft(kfr, ft);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { mq = fmaxf(mq, zq[i]); mk = fmaxf(mk, zk[i]); }
-  }
-  mq = wave_max_cols(mq);
-  mk = wave_max_cols(mk);
-  float sq = 0.f, sk = 0.f;
-  for (int ft = 0; ft < NFT; ++ft) {
-    const f32x4 zq = logits_ft(qfr, ft), zk = logits_ft(kfr, ft);
+      for (int i = 0; i < 4; ++i) { mq = fmaxf(mq, zq[i]); mk = fmaxf(mk, zk[i]); }
+    }
+    mq = wave_max_cols(mq);
+    mk = wave_max_cols(mk);
+    float sq = 0.f, sk = 0.f;
+    for (int ft = 0; ft < NFT; ++ft) {
+      const f32x4 zq = logits_ft(qfr, ft), zk = logits_ft(kfr, ft);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { sq += __expf(zq[i] - mq); sk += __expf(zk[i] - mk); }
+      for (int i = 0; i < 4; ++i) { sq += __expf(zq[i] - mq); sk += __expf(zk[i] - mk); }
+    }
+    iq = 1.f / wave_sum_cols(sq);
+    ik = 1.f / wave_sum_cols(sk);
   }
-  const float iq = 1.f / wave_sum_cols(sq), ik = 1.f / wave_sum_cols(sk);
   float part[16];
 #pragma unroll
   for (int s2 = 0; s2 < 16; ++s2) part[s2] = 0.f;
@@ -148,12 +155,13 @@ __device__ __forceinline__ f32x4 exact_diag_scores(const bf16 *sW, const bf16 *K
 // y_t += mix sum_{s<=t} A[t][s] v_s over the 16 rows of sub-chunk I of the chunk at c0, with A
 // the exact diagonal-block scores: read-modify-write of rows this wave stored (same-wave
 // ordering makes the stores visible to the loads).
+template <bool HH>
 __device__ __forceinline__ void exact_diag_fixup(const bf16 *sW, const bf16 *Kh, const bf16 *Vh, const bf16 *LGh,
                                                  const bf16 *Qh, bf16 *Oh, int c0, int I, int L, float mix) {
   using namespace full;
   using T = bf16;
   const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
-  const f32x4 a = exact_diag_scores(sW, Kh, LGh, Qh, c0, I, L, mix);
+  const f32x4 a = exact_diag_scores<HH>(sW, Kh, LGh, Qh, c0, I, L, mix);
   // lane (t, g) holds A[t][4g + i]; y_t[dv] += sum_s A[t][s] v_s[dv] for dv = 32g .. 32g+31
   float arow[16];
 #pragma unroll
@@ -227,32 +235,51 @@ __device__ __forceinline__ void keysT_tr(const bf16 *sKt, int I, int ft, int ks,
 
 // W_phi^T [f][d] into LDS (row stride LDWW) from W_phi [d][f] in global memory, by NT threads:
 // each thread takes row pairs (d, d + 1) x 8 features, all its loads in flight before the
-// transposed 4-byte stores of the pairs.
-template <int NT>
+// transposed 4-byte stores of the pairs.  HH (Hedgehog map): W_phi is [d][D/2], and rows
+// D/2 + f receive -W_phi^T (a sign flip, exact in bf16), so that the logits of the D features
+// are (xW, -xW).
+template <int NT, bool HH = false>
 __device__ __forceinline__ void load_wT_pairs(bf16 *dst, const bf16 *src, int tid) {
   using namespace full;
-  constexpr int IT = (D / 2) * (D / 8) / NT;
-  static_assert(IT * NT == (D / 2) * (D / 8), "thread count must divide the row pairs");
+  constexpr int FC = HH ? D / 2 : D;  // columns of W_phi
+  constexpr int IT = (D / 2) * (FC / 8) / NT;
+  static_assert(IT * NT == (D / 2) * (FC / 8), "thread count must divide the row pairs");
   Frag<bf16> a[IT], b[IT];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
-    const int idx = tid + it * NT, dd = 2 * (idx / (D / 8)), f0 = (idx % (D / 8)) * 8;
-    a[it] = load8(src + (size_t)dd * D + f0);
-    b[it] = load8(src + (size_t)(dd + 1) * D + f0);
+    const int idx = tid + it * NT, dd = 2 * (idx / (FC / 8)), f0 = (idx % (FC / 8)) * 8;
+    a[it] = load8(src + (size_t)dd * FC + f0);
+    b[it] = load8(src + (size_t)(dd + 1) * FC + f0);
   }
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
-    const int idx = tid + it * NT, dd = 2 * (idx / (D / 8)), f0 = (idx % (D / 8)) * 8;
+    const int idx = tid + it * NT, dd = 2 * (idx / (FC / 8)), f0 = (idx % (FC / 8)) * 8;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       bf16 pair[2] = {a[it].v[j], b[it].v[j]};
-      *reinterpret_cast<uint32_t *>(dst + (f0 + j) * LDWW + dd) = *reinterpret_cast<const uint32_t *>(pair);
+      const uint32_t u = *reinterpret_cast<const uint32_t *>(pair);
+      *reinterpret_cast<uint32_t *>(dst + (f0 + j) * LDWW + dd) = u;
+      if constexpr (HH) *reinterpret_cast<uint32_t *>(dst + (FC + f0 + j) * LDWW + dd) = u ^ 0x80008000u;
     }
   }
 }
 
+// The feature map of the wave's rows from their logits z: softmax over the D features (max
+// subtracted), or for the Hedgehog map (logits (xW, -xW)) the plain exponential.
+template <bool HH, int NFT>
+__device__ __forceinline__ void feature_map_rows(const f32x4 (&z)[NFT], float (&phi)[NFT][4]) {
+  if constexpr (HH) {
+#pragma unroll
+    for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) phi[ft][i] = exp2_fast(z[ft][i] * LOG2E);
+  } else {
+    softmax_rows<NFT>(z, phi);
+  }
+}
+
 // ZW: windows of 66..129 keys, which reach into the chunk two back (window group Z)
-template <bool ZW>
+template <bool ZW, bool HH>
 __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
   using namespace full;
   using T = bf16;
@@ -420,7 +447,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
   // ---- prologue: weights, meta tokens, the chunk before the first one
   {
     const T *Wk = reinterpret_cast<const T *>(p.wk);
-    load_wT_pairs<512>(sW, Wk, tid);
+    load_wT_pairs<512, HH>(sW, Wk, tid);
     const T *Tv = reinterpret_cast<const T *>(p.tv);
     const T *Tk = reinterpret_cast<const T *>(p.tk);
     for (int idx = tid; idx < D * 16; idx += 512) {
@@ -511,7 +538,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
       {
         f32x4 z[NFT];
         feature_logits_pipe(sW, kf, r16, g4, z);
-        softmax_rows<NFT>(z, ko);
+        feature_map_rows<HH>(z, ko);
       }
       // finish the feature map here: left to itself the compiler sinks the softmax past the
       // barrier into the next phase
@@ -861,7 +888,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
         // (the wide-window variant carries group Z through here: no registers for prefetching)
         if constexpr (ZW) feature_logits<T, D, LDWW>(sW, qf, r16, g4, zq);
         else feature_logits_pipe(sW, qf, r16, g4, zq);
-        softmax_rows<NFT>(zq, qo);
+        feature_map_rows<HH>(zq, qo);
 #pragma unroll
         for (int ft = 0; ft < NFT; ++ft) {  // interleaved features
           const int fpos = 32 * (ft >> 1) + 8 * g4 + 4 * (ft & 1);
@@ -1122,7 +1149,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
     if (unsafe_seen) {
       for (int c = c_begin; c < c_end; ++c) {
         if (!((sFlag[I * FLAG_WORDS + ((c - c_begin) >> 5)] >> ((c - c_begin) & 31)) & 1u)) continue;
-        exact_diag_fixup(sW, Kh, Vh, LGh, Qh, Oh, c * CH, I, L, mix);
+        exact_diag_fixup<HH>(sW, Kh, Vh, LGh, Qh, Oh, c * CH, I, L, mix);
       }
     }
   }
@@ -1155,6 +1182,7 @@ constexpr int ST_LDS_BYTES = ST_OFF_VOTE + 16;
 static_assert(2 * ST_LDS_BYTES <= LDS_LIMIT, "state pass: two workgroups per CU");
 }  // namespace full
 
+template <bool HH>
 __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
   using namespace full;
   using T = bf16;
@@ -1202,7 +1230,7 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
   load_pairs(lf, LGh, c * CH);
   load_k(kf, (c - pp) * CH);  // this piece's first chunk (p.sss <= p.cps)
   load_pairs(vf, Vh, (c - pp) * CH);
-  load_wT_pairs<256>(sW, reinterpret_cast<const T *>(p.wk), tid);  // overlaps the first loads
+  load_wT_pairs<256, HH>(sW, reinterpret_cast<const T *>(p.wk), tid);  // overlaps the first loads
   f32x4 S[FTW][NDT];
 #pragma unroll
   for (int ft = 0; ft < FTW; ++ft)
@@ -1220,7 +1248,7 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
     if (mine) {
       f32x4 z[NFT];
       feature_logits_pipe(sW, kf, r16, g4, z);
-      softmax_rows<NFT>(z, ko);
+      feature_map_rows<HH>(z, ko);
     }
     {
       const int tp = tid & 31;
@@ -1338,25 +1366,31 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
   if (tid < D) p.ws_decay[(size_t)grp * D + tid] = pp > 0 ? 0.f : (stopped ? NEG_BIG : suf);
 }
 
-hipError_t launch_fwd_full(const FwdParams &p, hipStream_t stream) {
+template <bool HH>
+static hipError_t launch_fwd_full_t(const FwdParams &p, hipStream_t stream) {
   hipError_t e;
   if (p.nseg > 1) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(fwd_full_state_kernel),
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(fwd_full_state_kernel<HH>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, full::ST_LDS_BYTES);
     if (e != hipSuccess) return e;
     const int nblk = p.B * p.Hkv * (p.nseg - 1);  // pieces of a block 8 workgroups apart
-    hipLaunchKernelGGL(fwd_full_state_kernel, dim3(((nblk + 7) / 8) * 8 * p.sss), dim3(256), full::ST_LDS_BYTES,
+    hipLaunchKernelGGL(fwd_full_state_kernel<HH>, dim3(((nblk + 7) / 8) * 8 * p.sss), dim3(256), full::ST_LDS_BYTES,
                        stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  const void *kern = p.W > CH + 1 ? reinterpret_cast<const void *>(fwd_full_kernel<true>)
-                                  : reinterpret_cast<const void *>(fwd_full_kernel<false>);
+  const bool zw = p.W > CH + 1;
+  const void *kern = zw ? reinterpret_cast<const void *>(fwd_full_kernel<true, HH>)
+                        : reinterpret_cast<const void *>(fwd_full_kernel<false, HH>);
   e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, full::LDS_BYTES);
   if (e != hipSuccess) return e;
   const dim3 grid(((p.ngroups + 7) / 8) * 8 * p.G);
-  if (p.W > CH + 1) hipLaunchKernelGGL(fwd_full_kernel<true>, grid, dim3(512), full::LDS_BYTES, stream, p);
-  else hipLaunchKernelGGL(fwd_full_kernel<false>, grid, dim3(512), full::LDS_BYTES, stream, p);
+  if (zw) hipLaunchKernelGGL((fwd_full_kernel<true, HH>), grid, dim3(512), full::LDS_BYTES, stream, p);
+  else hipLaunchKernelGGL((fwd_full_kernel<false, HH>), grid, dim3(512), full::LDS_BYTES, stream, p);
   return hipGetLastError();
+}
+
+hipError_t launch_fwd_full(const FwdParams &p, hipStream_t stream) {
+  return p.hh ? launch_fwd_full_t<true>(p, stream) : launch_fwd_full_t<false>(p, stream);
 }
 
 }  // namespace lz

@@ -31,6 +31,7 @@ struct FwdParams {
   int per_head_q;
   int full;  // whole-head kernel (fwd_full.hip)
   int sss;   // whole-head kernel: state-pass pieces per segment (divides cps)
+  int hh;    // whole-head kernel: Hedgehog feature map (W_phi [d][d/2]) instead of the softmax
   float mix, scale;
 };
 
@@ -55,6 +56,7 @@ struct DecParams {
   int *ws_count;   // [N]: workgroups of the step that have read pos[n]
   int64_t w_stride;
   int N, Hq, Hkv, W, M, G;
+  int hh;  // Hedgehog feature map (W_phi [d][d/2]) instead of the softmax
   float mix, scale;
 };
 

@@ -39,12 +39,12 @@ def test_status_strings_and_version():
     assert b"gfx950" in lib.lizard_version()
 
 
-def _fwd(lib, **kw):
+def _fwd(lib, fn="lizard_attn_fwd", **kw):
     a = dict(q=16, k=16, v=16, lg=16, wq=16, wk=16, stride=0, tk=16, tv=16, out=16, B=1, Hq=2, Hkv=2,
              L=64, d=128, W=64, M=4, mix=0.5, scale=0.1, dtype=1, ws=None, wsb=0, stream=None)
     a.update(kw)
     P = lambda x: None if x is None else ctypes.c_void_p(x)
-    return lib.lizard_attn_fwd(P(a["q"]), P(a["k"]), P(a["v"]), P(a["lg"]), P(a["wq"]), P(a["wk"]),
+    return getattr(lib, fn)(P(a["q"]), P(a["k"]), P(a["v"]), P(a["lg"]), P(a["wq"]), P(a["wk"]),
                                a["stride"], P(a["tk"]), P(a["tv"]), P(a["out"]), a["B"], a["Hq"],
                                a["Hkv"], a["L"], a["d"], a["W"], a["M"], a["mix"], a["scale"],
                                a["dtype"], P(a["ws"]), a["wsb"], P(a["stream"]))
@@ -62,6 +62,23 @@ def test_fwd_validation_codes(kw, code):
     lib = api.load()
     assert _fwd(lib, **kw) == code
     assert lib.lizard_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(Hq=3, Hkv=2), 1), (dict(stride=100), 1),
+    (dict(d=64), 2), (dict(d=64, dtype=0), 2),            # only bf16, d = 128
+    (dict(W=130), 2),                                       # windows of at most 129 keys
+    (dict(wk=32), 2), (dict(stride=128 * 128), 2),          # one W_phi for both sides and all heads
+])
+def test_fwd_hedgehog_validation_codes(kw, code):
+    lib = api.load()
+    assert _fwd(lib, fn="lizard_attn_fwd_hedgehog", **kw) == code
+    assert lib.lizard_last_error()
+
+
+def test_fwd_hedgehog_empty_problem_is_ok():
+    lib = api.load()
+    assert _fwd(lib, fn="lizard_attn_fwd_hedgehog", B=0) == 0
 
 
 def test_fwd_empty_problem_is_ok_without_launch():
@@ -108,13 +125,13 @@ def test_whole_head_segments_cover_at_most_1024_chunks():
     assert need == pieces * 128 * 128 * 4 + pieces * 128 * 4
 
 
-def _dec(lib, **kw):
+def _dec(lib, fn="lizard_attn_decode", **kw):
     a = dict(state=16, wk=16, wv=16, pos=16, q=16, k=16, v=16, lg=16, wq=16, wkm=16, stride=0, tk=16,
              tv=16, out=16, N=4, Hq=2, Hkv=2, d=128, W=64, M=4, mix=0.5, scale=0.1, dtype=1, ws=16,
              wsb=1 << 30, stream=None)
     a.update(kw)
     P = lambda x: None if x is None else ctypes.c_void_p(x)
-    return lib.lizard_attn_decode(P(a["state"]), P(a["wk"]), P(a["wv"]), P(a["pos"]), P(a["q"]),
+    return getattr(lib, fn)(P(a["state"]), P(a["wk"]), P(a["wv"]), P(a["pos"]), P(a["q"]),
                                   P(a["k"]), P(a["v"]), P(a["lg"]), P(a["wq"]), P(a["wkm"]),
                                   a["stride"], P(a["tk"]), P(a["tv"]), P(a["out"]), a["N"], a["Hq"],
                                   a["Hkv"], a["d"], a["W"], a["M"], a["mix"], a["scale"], a["dtype"],
@@ -129,6 +146,14 @@ def _dec(lib, **kw):
 def test_decode_validation_codes(kw, code):
     lib = api.load()
     assert _dec(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(state=None), 1), (dict(d=32), 2), (dict(W=257), 2), (dict(ws=None), 3),
+    (dict(stride=128 * 64 - 1), 1),                         # W_phi [d, d/2]: d*d/2 elements apart
+])
+def test_decode_hedgehog_validation_codes(kw, code):
+    assert _dec(api.load(), fn="lizard_attn_decode_hedgehog", **kw) == code
 
 
 def test_decode_empty_is_ok():
