@@ -28,7 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from linearized_attention_amd import api  # noqa: E402
-from linearized_attention_amd.synthetic import (WORKLOADS, WORKLOAD_NAMES,  # noqa: E402
+from linearized_attention_amd.synthetic import (WORKLOADS, WORKLOAD_NAMES, make_fwd_inputs,  # noqa: E402
                                                 workload_decode_inputs, workload_fwd_inputs)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
@@ -119,6 +119,29 @@ def bench_forward(steps: int, warmup: int):
     log(f"[bench] forward: {warmup} warmup done, timing {steps} steps")
     total_ms, per = time_launches(step, steps)
     return c, inp, total_ms, per
+
+
+def bench_forward_hedgehog(steps: int, warmup: int):
+    """The same layer shape with the Hedgehog feature map (W_phi [d, d/2])."""
+    c = WORKLOADS[1]
+    log("[bench] generating the forward workload with the Hedgehog map")
+    inp = make_fwd_inputs(B=c["B"], Hq=c["Hq"], Hkv=c["Hkv"], L=c["L"], d=c["d"], W=c["W"], M=c["M"],
+                          dtype=c["dtype"], seed=1001, gate=c["gate"], phi_cols=c["d"] // 2)
+    g = inp.to("cuda")
+    out = torch.empty_like(g.q)
+    need = api.lizard_attn_fwd_workspace_bytes(c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], c["W"], g.q.dtype)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+
+    def step():
+        api.lizard_attn_fwd_hedgehog(g.q, g.k, g.v, g.log_gamma, g.w_phi_q, g.w_phi_k, g.t_k, g.t_v,
+                                     W=inp.W, M=inp.M, mix=inp.mix, scale=inp.scale, out=out, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] hedgehog forward: {warmup} warmup done, timing {steps} steps")
+    total_ms, per = time_launches(step, steps)
+    return c, total_ms, per
 
 
 def bench_decode(steps: int, warmup: int):
@@ -232,6 +255,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-hedgehog", action="store_true",
+                    help="skip the Hedgehog-map forward on the same shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-run", action="store_true",
                     help="one forward plus a plain copy of known size, for rocprofv3 counter passes")
@@ -295,6 +320,19 @@ def main():
     }
     del inp
     torch.cuda.empty_cache()
+    if not args.no_hedgehog:
+        hc, htot, hper = bench_forward_hedgehog(max(args.steps // 2, 1), args.warmup)
+        hms = sum(hper) / len(hper)
+        hach = nbytes / (hms * 1e-3) / 1e9
+        result["hedgehog"] = {
+            "workload": WORKLOAD_NAMES[1] + " hedgehog-map W_phi[128,64]",
+            "steps": len(hper), "ms_per_step": htot / len(hper),
+            "tokens_per_s": tokens / (htot / len(hper) * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": hach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": hach / HBM_PEAK_GBS, "kernel_ms": hms,
+                         "algorithmic_bytes_per_launch": nbytes},
+        }
+        torch.cuda.empty_cache()
     if not args.no_decode:
         dc, dtot, dper = bench_decode(args.decode_steps, 4)
         dbytes = decode_bytes_per_step(dc)

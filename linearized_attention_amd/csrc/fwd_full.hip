@@ -1213,9 +1213,13 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
   auto own = [&](int c) { return (b1 - 1 - c) % sss == pp; };
 
   auto load_k = [&](Frag<T> (&kf)[KS], int c0) {
-    const T *src = Kh + (size_t)(c0 + 16 * I + r16) * D;
+    // lane offsets rebuilt here from a lane id the compiler cannot hoist (a per-lane row
+    // pointer kept across the loop was spilled, and its reload waits for the loads in flight)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const T *src = Kh + (size_t)(c0 + 16 * I + (ln & 15)) * D;
 #pragma unroll
-    for (int j = 0; j < KS; ++j) kf[j] = load8(src + 32 * j + 8 * g4);
+    for (int j = 0; j < KS; ++j) kf[j] = load8(src + 32 * j + 8 * (ln >> 4));
   };
   // values and log gamma, token pairs tp = tid % 32, 8-column groups tid / 32 + 8 gsel (4 per thread)
   auto load_pairs = [&](Frag<T> (&f)[2][2], const T *base, int c0) {
