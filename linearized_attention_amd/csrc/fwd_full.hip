@@ -274,7 +274,31 @@ __device__ __forceinline__ void feature_map_rows(const f32x4 (&z)[NFT], float (&
 #pragma unroll
       for (int i = 0; i < 4; ++i) phi[ft][i] = exp2_fast(z[ft][i] * LOG2E);
   } else {
-    softmax_rows<NFT>(z, phi);
+    // softmax over the D features of the row (4 lanes x NFT x 4 values): max and sum as trees
+    // rather than one chain through all NFT x 4 values
+    float mt[NFT], st[NFT];
+#pragma unroll
+    for (int ft = 0; ft < NFT; ++ft) mt[ft] = fmaxf(fmaxf(z[ft][0], z[ft][1]), fmaxf(z[ft][2], z[ft][3]));
+#pragma unroll
+    for (int w = NFT / 2; w >= 1; w /= 2)
+#pragma unroll
+      for (int ft = 0; ft < w; ++ft) mt[ft] = fmaxf(mt[ft], mt[ft + w]);
+    const float zm2 = -wave_max_cols(mt[0]) * LOG2E;
+#pragma unroll
+    for (int ft = 0; ft < NFT; ++ft) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) phi[ft][i] = exp2_fast(__builtin_fmaf(z[ft][i], LOG2E, zm2));
+      st[ft] = (phi[ft][0] + phi[ft][1]) + (phi[ft][2] + phi[ft][3]);
+    }
+#pragma unroll
+    for (int w = NFT / 2; w >= 1; w /= 2)
+#pragma unroll
+      for (int ft = 0; ft < w; ++ft) st[ft] += st[ft + w];
+    const float inv = 1.f / wave_sum_cols(st[0]);
+#pragma unroll
+    for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) phi[ft][i] *= inv;
   }
 }
 
