@@ -205,6 +205,23 @@ lizard_status fwd_impl(const void *q, const void *k, const void *v, const void *
   p.full = full ? 1 : 0;
   p.sss = plan.sss;
   p.hh = hedgehog ? 1 : 0;
+  // Two segments on the whole-head path: the second one's workgroups walk the chunks before it
+  // themselves (no state pass), and the first segment takes a few chunks more to even out the
+  // walk.  Not with a start state or window history (the walk starts from zero at chunk 0).
+  // The shift is estimated in the kernel from the gates (LIZARD_FWD_SPLIT_SHIFT=n fixes it at n
+  // chunks; a negative value turns the split off: state pass instead).
+  p.split = 0;
+  const char *shift_env = getenv("LIZARD_FWD_SPLIT_SHIFT");
+  const int shift_fixed = shift_env ? atoi(shift_env) : -1;
+  if (full && plan.nseg == 2 && !(ext && (ext->state_in || history)) && !(shift_env && shift_fixed < 0) &&
+      plan.cps < plan.nchunks && plan.cps <= kMaxFullCps) {
+    int smax = plan.cps / 4;
+    if (smax > plan.nchunks - 1 - plan.cps) smax = plan.nchunks - 1 - plan.cps;
+    if (smax > kMaxFullCps - plan.cps) smax = kMaxFullCps - plan.cps;
+    p.split = plan.cps;
+    p.split_shift = shift_fixed;
+    p.split_max = smax;
+  }
   p.mix = mix; p.scale = scale;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int esize = dtype == LIZARD_BF16 ? 2 : 4;

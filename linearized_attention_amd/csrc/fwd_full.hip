@@ -302,6 +302,245 @@ __device__ __forceinline__ void feature_map_rows(const f32x4 (&z)[NFT], float (&
   }
 }
 
+// Chunks the first of two segments takes beyond the even split at chunk b, so that both end
+// together.  The second segment first walks back from its start until every feature has decayed
+// by e^{-SKIP_LOG}, about n = SKIP_LOG / r chunks for the slowest feature's log decay r per
+// chunk (at most b).  Measured on MI355X, a walk costs about 3 + 3.7 n us and a chunk of the
+// main loop 6.5 us, so the first segment takes (3 + 3.7 n) / 13 chunks more.  r comes from the
+// last four chunks before b: wave w < 4 sums chunk b - 1 - w per feature into part[w][D]
+// (shared memory), and after the barrier that follows every wave reads the four rows and
+// reduces them the same way.  Every workgroup of the head runs this on the same data with the
+// same code, so the two segments agree without communicating.
+__device__ __forceinline__ void split_shift_part(const bf16 *LGh, int b, int wv, int lane, float *part) {
+  using namespace full;
+  const int c = b - 1 - wv;
+  if (wv >= 4 || c < 0) return;
+  const int fg = lane & 15, tg = lane >> 4;  // features 8 fg .. 8 fg + 7 of tokens tg + 4 i
+  float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+  for (int i0 = 0; i0 < 16; i0 += 4) {  // four rows in flight at a time (few registers here)
+    Frag<bf16> x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = load8(LGh + (size_t)(c * CH + tg + 4 * (i0 + i)) * D + 8 * fg);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] += to_f(x[i].v[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float t = wave_sum_cols(a[e]);
+    if (tg == 0) part[wv * D + 8 * fg + e] = t;
+  }
+}
+__device__ __forceinline__ int split_shift(const float *part, int b, int lane) {
+  using namespace full;
+  const int nc = b < 4 ? b : 4;
+  float r = 1.0e30f;  // the slowest feature's log decay per chunk (log gamma <= 0)
+#pragma unroll
+  for (int q = 0; q < D / 64; ++q) {
+    float a = 0.f;
+    for (int w = 0; w < nc; ++w) a += part[w * D + lane + 64 * q];
+    r = fminf(r, -a);
+  }
+  r = -wave_max_all(-r) / (float)nc;
+  const float n = fminf(SKIP_LOG / fmaxf(r, 1.0e-6f), (float)b);
+  return (int)((3.f + 3.7f * n) / 13.f + 0.5f);
+}
+
+// The backward walk of the segment state pass (see fwd_full_state_kernel below).
+// LDS of one backward walk: W_phi^T (staged and visible before the walk starts, or staged by
+// the stage_w callback the walk runs after its first loads), v^T, the log gamma^T / decayed key
+// rows, the prefix table, the suffix sums [2][D] and four vote words.
+struct WalkLds {
+  const bf16 *sW;
+  bf16 *sVt, *sKt;
+  float *sTot, *sSuf;
+  int *sVote;
+};
+
+// Backward walk over the chunks [b0, b1) of one head (b1 - b0 full chunks), piece pp of sss:
+// adds the chunks c with (b1 - 1 - c) % sss == pp, decayed to b1, to S (which it zeroes first).
+// WORKER threads wt = 0..255 are four waves (sub-chunk I = wt / 64) that do the work; the other
+// threads of the workgroup (WORKER = false) only take part in its barriers.  Returns whether the
+// walk stopped before b0; the workers wt < D hold in suf the log-gate sum of the chunks walked.
+// Ends with a barrier: the LDS it used is free for the caller.
+template <bool HH, bool WORKER, typename StageW>
+__device__ __forceinline__ bool walk_back(const WalkLds &lds, const bf16 *Kh, const bf16 *Vh, const bf16 *LGh,
+                                          int b0, int b1, int pp, int sss, int wt, f32x4 (&S)[full::FTW][full::NDT],
+                                          float &suf, StageW stage_w) {
+  using namespace full;
+  using T = bf16;
+  const bf16 *sW = lds.sW;
+  T *sVt = lds.sVt, *sKt = lds.sKt, *sLgT = lds.sKt;
+  float *sTot = lds.sTot, *sSuf = lds.sSuf;
+  int *sVote = lds.sVote;
+  const int lane = wt & 63, I = wt >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  auto own = [&](int c) { return (b1 - 1 - c) % sss == pp; };
+
+  auto load_k = [&](Frag<T> (&kf)[KS], int c0) {
+    // lane offsets rebuilt here from a lane id the compiler cannot hoist (a per-lane row
+    // pointer kept across the loop was spilled, and its reload waits for the loads in flight)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const T *src = Kh + (size_t)(c0 + 16 * I + (ln & 15)) * D;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) kf[j] = load8(src + 32 * j + 8 * (ln >> 4));
+  };
+  // values and log gamma, token pairs tp = wt % 32, 8-column groups wt / 32 + 8 gsel (4 per thread)
+  // (offsets from an opaque copy of wt, for the reason given in load_k)
+  auto load_pairs = [&](Frag<T> (&f)[2][2], const T *base, int c0) {
+    int w = wt;
+    asm volatile("" : "+v"(w));
+    const int tp = w & 31;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int gsel = 0; gsel < 2; ++gsel) f[gsel][h] = load8(base + (size_t)(c0 + 2 * tp + h) * D + 8 * ((w >> 5) + 8 * gsel));
+  };
+  Frag<T> kf[KS], vf[2][2], lf[2][2];
+  int c = b1 - 1;
+  if constexpr (WORKER) {
+    load_pairs(lf, LGh, c * CH);
+    load_k(kf, (c - pp) * CH);  // this piece's first chunk (sss <= b1 - b0)
+    load_pairs(vf, Vh, (c - pp) * CH);
+  }
+  stage_w();  // overlaps the first loads
+#pragma unroll
+  for (int ft = 0; ft < FTW; ++ft)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) S[ft][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  suf = 0.f;  // thread wt < D: log-gate sum of feature wt over the chunks walked so far
+  if (WORKER && wt < D) sSuf[wt] = 0.f;
+  const Frag<T> tri_c0 = tri64_frag<T>(r16, g4, I, 0), tri_c1 = tri64_frag<T>(r16, g4, I, 1);
+  bool stopped = false;
+  __syncthreads();
+
+  for (int par = 0;; par ^= 1, --c) {
+    const bool mine = own(c);
+    float ko[NFT][4];
+    if (WORKER && mine) {
+      f32x4 z[NFT];
+      feature_logits_pipe(sW, kf, r16, g4, z);
+      feature_map_rows<HH>(z, ko);
+    }
+    if constexpr (WORKER) {
+      const int tp = wt & 31;
+      const int vpos = (2 * tp & 32) | ipos(2 * tp & 31);
+#pragma unroll
+      for (int gsel = 0; gsel < 2; ++gsel) {
+        const int gq = (wt >> 5) + 8 * gsel;
+        if (mine) store_pairT<T, LDV>(vf[gsel][0], vf[gsel][1], sVt + (8 * gq) * LDV + vpos);
+        store_pairT<T, LDV>(lf[gsel][0], lf[gsel][1], sLgT + (8 * gq) * LDV + 2 * tp);
+      }
+      // in flight from here: the log gates of the next chunk back, the keys and values of this
+      // piece's next chunk (sss chunks back: the walk's cheap chunks in between hide the loads)
+      if (c > b0) load_pairs(lf, LGh, (c - 1) * CH);
+      if (mine && c - sss >= b0) {
+        load_k(kf, (c - sss) * CH);
+        load_pairs(vf, Vh, (c - sss) * CH);
+      }
+    }
+    __syncthreads();
+    float pc[NFT][4];
+    if constexpr (WORKER) {
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft) {
+        f32x4 cc = mma(load8(sLgT + (16 * ft + r16) * LDV + 8 * g4), tri_c0, f32x4{0.f, 0.f, 0.f, 0.f});
+        cc = mma(load8(sLgT + (16 * ft + r16) * LDV + 32 + 8 * g4), tri_c1, cc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pc[ft][i] = cc[i];
+      }
+      if (r16 == 15) {
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft)
+          *reinterpret_cast<f32x4 *>(sTot + I * D + 16 * ft + 4 * g4) = f32x4{pc[ft][0], pc[ft][1], pc[ft][2], pc[ft][3]};
+      }
+    }
+    __syncthreads();
+    bool mild = false;
+    if constexpr (WORKER) {
+      // suffix through this chunk, for the next chunk back; stop once every feature is below
+      if (wt < D) {
+        suf += sTot[3 * D + wt];
+        sSuf[(par ^ 1) * D + wt] = suf;
+        const bool below = __all(suf < -SKIP_LOG);
+        if (lane == 0) sVote[I] = below;
+      }
+      mild = mine && chunk_is_mild_c<D>(sTot, lane);
+      if (mine) {
+        // decayed keys: mild chunk e^{-p_t} (chunk-start reference), else e^{C_I - p_t}
+        if (mild) {
+#pragma unroll
+          for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ko[ft][i] *= exp2_fast(-pc[ft][i] * LOG2E);
+        } else {
+#pragma unroll
+          for (int ft = 0; ft < NFT; ++ft) {
+            const f32x4 t = *reinterpret_cast<const f32x4 *>(sTot + I * D + 16 * ft + 4 * g4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ko[ft][i] *= __expf(t[i] - pc[ft][i]);
+          }
+        }
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft) {
+          const int fpos = 32 * (ft >> 1) + 8 * g4 + 4 * (ft & 1);
+          store4<T>(sKt + (16 * I + r16) * LDW + fpos, ko[ft][0], ko[ft][1], ko[ft][2], ko[ft][3]);
+        }
+      }
+    }
+    __syncthreads();
+    const bool stop = sVote[0] && sVote[1];
+    if (WORKER && mine) {
+      // S += sum_t k~_t e^{s + ...} v_t^T: key factors e^{s + C_3} (mild) or e^{s + C_3 - C_J}
+      // for sub-chunk J, s = the suffix after this chunk (feature of the key row)
+      Frag<T> ka[FTW][2];
+#pragma unroll
+      for (int ft = 0; ft < FTW; ++ft) {
+        const int fr = 16 * (2 * I + ft);
+        float fac[2][2];
+        const float c3s = sTot[3 * D + fr + r16] + sSuf[par * D + fr + r16];
+#pragma unroll
+        for (int J = 0; J < 4; ++J) fac[J >> 1][J & 1] = __expf(mild ? c3s : c3s - sTot[J * D + fr + r16]);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          float x[8];
+          keysT_tr(sKt, I, ft, ks, r16, g4, x);
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) x[jj] *= fac[ks][jj >> 2];
+          ka[ft][ks] = frag_from<T>(x);
+        }
+      }
+      // each v^T fragment serves both feature tiles; the next value tile's are loaded ahead
+      const T *vrow = sVt + r16 * LDV + 8 * g4;
+      Frag<T> vb[2][2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) vb[0][ks] = load8(vrow + 32 * ks);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        if (dt + 1 < NDT) {
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) vb[(dt + 1) & 1][ks] = load8(vrow + 16 * (dt + 1) * LDV + 32 * ks);
+        }
+#pragma unroll
+        for (int ft = 0; ft < FTW; ++ft)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) S[ft][dt] = mma(ka[ft][ks], vb[dt & 1][ks], S[ft][dt]);
+      }
+    }
+    if (stop || c == b0) {
+      stopped = stop && c > b0;
+      break;
+    }
+    if (mine) __syncthreads();  // keys and values read before the next chunk is staged (the
+                                // other chunks' LDS reads all came before the last barrier)
+  }
+  __syncthreads();
+  return stopped;
+}
+
 // ZW: windows of 66..129 keys, which reach into the chunk two back (window group Z)
 template <bool ZW, bool HH>
 __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
@@ -319,6 +558,10 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
   T *sTk = reinterpret_cast<T *>(smem + OFF_TK);
   T *sTvT = reinterpret_cast<T *>(smem + OFF_TV);
   uint32_t *sFlag = reinterpret_cast<uint32_t *>(smem + OFF_FLAG);
+  // a self-started segment walks the chunks before it with the regions of the chunk loop; its
+  // suffix sums and votes sit in the decayed-query rows, unused until the loop
+  const WalkLds wlds{sW, sVt, sKt, sTot, reinterpret_cast<float *>(smem + OFF_Q),
+                     reinterpret_cast<int *>(smem + OFF_Q + 2 * D * 4)};
 
   // lane id from mbcnt and the wave index as a scalar: both can be rebuilt anywhere, so the
   // register allocator recomputes lane-derived values instead of keeping (or spilling) them
@@ -339,8 +582,6 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
   const int b = bh / p.Hkv, kvh = bh % p.Hkv;
   const int hq = kvh * G + g;
   const int L = p.L;
-  const int c_begin = seg * p.cps;
-  const int c_end = min(p.nchunks, c_begin + p.cps);
 
   const size_t kv_off = ((size_t)b * p.Hkv + kvh) * (size_t)L * D;
   const T *Kh = reinterpret_cast<const T *>(p.k) + kv_off;
@@ -356,6 +597,21 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
   auto krow = [&](int x) -> const T * { return x >= 0 ? Kh + (size_t)x * D : Hk + (ptrdiff_t)(p.hist_rows + x) * D; };
   auto vrow = [&](int x) -> const T * { return x >= 0 ? Vh + (size_t)x * D : Hv + (ptrdiff_t)(p.hist_rows + x) * D; };
   auto row_ok = [&](int x) { return x < L && (x >= 0 || (p.hist_rows > 0 && x >= -p.hist_rows)); };
+
+  // p.split > 0: two segments, the second starting at chunk p.split + shift and walking the
+  // chunks before it for its start state (no state pass).  The shift is computed here from the
+  // gates, by every workgroup of the head alike, so both segments agree on it.
+  int bsplit = 0;
+  if (p.split) {
+    float *part = reinterpret_cast<float *>(smem + OFF_Q + 2 * D * 4 + 16);  // after the walk's words
+    if (p.split_shift < 0) split_shift_part(LGh, p.split, wv, lane, part);
+    __syncthreads();
+    const int sh = p.split_shift >= 0 ? p.split_shift : split_shift(part, p.split, lane);
+    bsplit = p.split + min(sh, p.split_max);
+  }
+  const int c_begin = p.split ? (seg ? bsplit : 0) : seg * p.cps;
+  const int c_end = p.split ? (seg ? p.nchunks : bsplit) : min(p.nchunks, c_begin + p.cps);
+  const bool self_start = p.split && seg == 1;
 
   // ---- staging helpers
   // keys of rows c0 + 16I .. +15 in fragment order (lane (r, q): row r, d = 32j + 8q .. +7)
@@ -490,6 +746,12 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
   if (key_wave) {
     // ======================================================= key waves
     const int kt = tid - 256;
+    // S rows owned: feature tiles 2I, 2I+1; S[ft][dt][i] = S[16(2I+ft) + 4g4 + i][16dt + r16]
+    f32x4 S[FTW][NDT];
+    if (self_start) {  // the state at the split: the chunks before it walked backwards
+      float suf;
+      walk_back<HH, true>(wlds, Kh, Vh, LGh, 0, c_begin, 0, 1, kt, S, suf, [] {});
+    }
     {
       Frag<T> kf[KS];
       if constexpr (ZW) {
@@ -501,8 +763,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
       load_kfrag(kf, (c_begin - 1) * CH);
       store_kfrag(kf);
     }
-    // S rows owned: feature tiles 2I, 2I+1; S[ft][dt][i] = S[16(2I+ft) + 4g4 + i][16dt + r16]
-    f32x4 S[FTW][NDT];
+    if (!self_start) {
 #pragma unroll
     for (int ft = 0; ft < FTW; ++ft)
 #pragma unroll
@@ -535,6 +796,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
           for (int i = 0; i < 4; ++i) S[ft][dt][i] = e[i] * S[ft][dt][i] + x[i];
         }
       }
+    }
     }
     const Frag<T> tri_c0 = tri64_frag<T>(r16, g4, I, 0), tri_c1 = tri64_frag<T>(r16, g4, I, 1);
     Frag<T> kf[KS], kf_next[KS];
@@ -739,6 +1001,11 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
     }
   } else {
     // ======================================================= query waves
+    if (self_start) {  // the key waves walk the chunks before the split; same barriers here
+      f32x4 Sd[FTW][NDT];
+      float sd;
+      walk_back<HH, false>(wlds, Kh, Vh, LGh, 0, c_begin, 0, 1, tid, Sd, sd, [] {});
+    }
     const float sl2 = p.scale * LOG2E;  // window logits in base 2
     // Window group Z (ZW only): the keys of the chunk two back, tiles I..3, for the queries qz of
     // the chunk at cz0.  It runs at the top of the chunk before (the chunk two back is then the
@@ -979,9 +1246,11 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
       bool safe = true;
       if (!mild) {
         float span = 0.f;
+        int ln = lane;  // (table addresses from an opaque lane id: kept across the loop, spilled)
+        asm volatile("" : "+v"(ln));
 #pragma unroll
         for (int q = 0; q < D / 64; ++q) {
-          const int f = lane + 64 * q;
+          const int f = ln + 64 * q;
           span = fmaxf(span, (I > 0 ? sTot[(I - 1) * D + f] : 0.f) - sTot[I * D + f]);
         }
         safe = wave_max_all(span) <= SPAN_MAX;
@@ -1195,6 +1464,9 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
 // values of its own.  Four waves, each the key side of one sub-chunk, with the arithmetic of
 // the key waves above; 80 KB of LDS, so two workgroups share a CU.  The pieces of a block run
 // 8 workgroups apart, on one XCD, and share its L2 for the log gates they all read.
+//
+// The walk itself (walk_back) also starts the second of two segments inside the whole-head
+// kernel, without a state pass (fwd_full_kernel, p.split).
 namespace full {
 constexpr int ST_OFF_W = 0;
 constexpr int ST_OFF_VT = ST_OFF_W + D * LDWW * 2;
@@ -1212,15 +1484,10 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
   using T = bf16;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   T *sW = reinterpret_cast<T *>(smem + ST_OFF_W);
-  T *sVt = reinterpret_cast<T *>(smem + ST_OFF_VT);
-  T *sKt = reinterpret_cast<T *>(smem + ST_OFF_KT);
-  T *sLgT = sKt;
-  float *sTot = reinterpret_cast<float *>(smem + ST_OFF_TAB);
-  float *sSuf = reinterpret_cast<float *>(smem + ST_OFF_SUF);
-  int *sVote = reinterpret_cast<int *>(smem + ST_OFF_VOTE);
-
+  const WalkLds lds{sW, reinterpret_cast<T *>(smem + ST_OFF_VT), reinterpret_cast<T *>(smem + ST_OFF_KT),
+                    reinterpret_cast<float *>(smem + ST_OFF_TAB), reinterpret_cast<float *>(smem + ST_OFF_SUF),
+                    reinterpret_cast<int *>(smem + ST_OFF_VOTE)};
   const int tid = threadIdx.x, lane = tid & 63, I = tid >> 6;
-  const int r16 = lane & 15, g4 = lane >> 4;
   const int sss = p.sss;
   const int nblk = p.B * p.Hkv * (p.nseg - 1);  // blocks: every segment but the last, per head
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -1228,163 +1495,16 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
   if (bg >= nblk) return;
   const int bh = bg / (p.nseg - 1), blk = bg % (p.nseg - 1);
   const int grp = bg * sss + pp;  // workspace slot: piece pp of block blk of head bh
-  const int L = p.L;
-  const size_t kv_off = (size_t)bh * (size_t)L * D;
+  const size_t kv_off = (size_t)bh * (size_t)p.L * D;
   const T *Kh = reinterpret_cast<const T *>(p.k) + kv_off;
   const T *Vh = reinterpret_cast<const T *>(p.v) + kv_off;
   const T *LGh = reinterpret_cast<const T *>(p.lg) + kv_off;
   const int b0 = blk * p.cps, b1 = b0 + p.cps;  // never the last segment: full chunks
-  auto own = [&](int c) { return (b1 - 1 - c) % sss == pp; };
-
-  auto load_k = [&](Frag<T> (&kf)[KS], int c0) {
-    // lane offsets rebuilt here from a lane id the compiler cannot hoist (a per-lane row
-    // pointer kept across the loop was spilled, and its reload waits for the loads in flight)
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const T *src = Kh + (size_t)(c0 + 16 * I + (ln & 15)) * D;
-#pragma unroll
-    for (int j = 0; j < KS; ++j) kf[j] = load8(src + 32 * j + 8 * (ln >> 4));
-  };
-  // values and log gamma, token pairs tp = tid % 32, 8-column groups tid / 32 + 8 gsel (4 per thread)
-  auto load_pairs = [&](Frag<T> (&f)[2][2], const T *base, int c0) {
-    const int tp = tid & 31;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int gsel = 0; gsel < 2; ++gsel) f[gsel][h] = load8(base + (size_t)(c0 + 2 * tp + h) * D + 8 * ((tid >> 5) + 8 * gsel));
-  };
-  Frag<T> kf[KS], vf[2][2], lf[2][2];
-  int c = b1 - 1;
-  load_pairs(lf, LGh, c * CH);
-  load_k(kf, (c - pp) * CH);  // this piece's first chunk (p.sss <= p.cps)
-  load_pairs(vf, Vh, (c - pp) * CH);
-  load_wT_pairs<256, HH>(sW, reinterpret_cast<const T *>(p.wk), tid);  // overlaps the first loads
   f32x4 S[FTW][NDT];
-#pragma unroll
-  for (int ft = 0; ft < FTW; ++ft)
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) S[ft][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float suf = 0.f;  // thread tid < D: log-gate sum of feature tid over the chunks walked so far
-  if (tid < D) sSuf[tid] = 0.f;
-  const Frag<T> tri_c0 = tri64_frag<T>(r16, g4, I, 0), tri_c1 = tri64_frag<T>(r16, g4, I, 1);
-  bool stopped = false;
-  __syncthreads();
-
-  for (int par = 0;; par ^= 1, --c) {
-    const bool mine = own(c);
-    float ko[NFT][4];
-    if (mine) {
-      f32x4 z[NFT];
-      feature_logits_pipe(sW, kf, r16, g4, z);
-      feature_map_rows<HH>(z, ko);
-    }
-    {
-      const int tp = tid & 31;
-      const int vpos = (2 * tp & 32) | ipos(2 * tp & 31);
-#pragma unroll
-      for (int gsel = 0; gsel < 2; ++gsel) {
-        const int gq = (tid >> 5) + 8 * gsel;
-        if (mine) store_pairT<T, LDV>(vf[gsel][0], vf[gsel][1], sVt + (8 * gq) * LDV + vpos);
-        store_pairT<T, LDV>(lf[gsel][0], lf[gsel][1], sLgT + (8 * gq) * LDV + 2 * tp);
-      }
-    }
-    // in flight from here: the log gates of the next chunk back, the keys and values of this
-    // piece's next chunk (p.sss chunks back: the walk's cheap chunks in between hide the loads)
-    if (c > b0) load_pairs(lf, LGh, (c - 1) * CH);
-    if (mine && c - sss >= b0) {
-      load_k(kf, (c - sss) * CH);
-      load_pairs(vf, Vh, (c - sss) * CH);
-    }
-    __syncthreads();
-    float pc[NFT][4];
-#pragma unroll
-    for (int ft = 0; ft < NFT; ++ft) {
-      f32x4 cc = mma(load8(sLgT + (16 * ft + r16) * LDV + 8 * g4), tri_c0, f32x4{0.f, 0.f, 0.f, 0.f});
-      cc = mma(load8(sLgT + (16 * ft + r16) * LDV + 32 + 8 * g4), tri_c1, cc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pc[ft][i] = cc[i];
-    }
-    if (r16 == 15) {
-#pragma unroll
-      for (int ft = 0; ft < NFT; ++ft)
-        *reinterpret_cast<f32x4 *>(sTot + I * D + 16 * ft + 4 * g4) = f32x4{pc[ft][0], pc[ft][1], pc[ft][2], pc[ft][3]};
-    }
-    __syncthreads();
-    // suffix through this chunk, for the next chunk back; stop once every feature is below
-    if (tid < D) {
-      suf += sTot[3 * D + tid];
-      sSuf[(par ^ 1) * D + tid] = suf;
-      const bool below = __all(suf < -SKIP_LOG);
-      if (lane == 0) sVote[I] = below;
-    }
-    const bool mild = mine && chunk_is_mild_c<D>(sTot, lane);
-    if (mine) {
-      // decayed keys: mild chunk e^{-p_t} (chunk-start reference), else e^{C_I - p_t}
-      if (mild) {
-#pragma unroll
-        for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) ko[ft][i] *= exp2_fast(-pc[ft][i] * LOG2E);
-      } else {
-#pragma unroll
-        for (int ft = 0; ft < NFT; ++ft) {
-          const f32x4 t = *reinterpret_cast<const f32x4 *>(sTot + I * D + 16 * ft + 4 * g4);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) ko[ft][i] *= __expf(t[i] - pc[ft][i]);
-        }
-      }
-#pragma unroll
-      for (int ft = 0; ft < NFT; ++ft) {
-        const int fpos = 32 * (ft >> 1) + 8 * g4 + 4 * (ft & 1);
-        store4<T>(sKt + (16 * I + r16) * LDW + fpos, ko[ft][0], ko[ft][1], ko[ft][2], ko[ft][3]);
-      }
-    }
-    __syncthreads();
-    const bool stop = sVote[0] && sVote[1];
-    if (mine) {
-      // S += sum_t k~_t e^{s + ...} v_t^T: key factors e^{s + C_3} (mild) or e^{s + C_3 - C_J}
-      // for sub-chunk J, s = the suffix after this chunk (feature of the key row)
-      Frag<T> ka[FTW][2];
-#pragma unroll
-      for (int ft = 0; ft < FTW; ++ft) {
-        const int fr = 16 * (2 * I + ft);
-        float fac[2][2];
-        const float c3s = sTot[3 * D + fr + r16] + sSuf[par * D + fr + r16];
-#pragma unroll
-        for (int J = 0; J < 4; ++J) fac[J >> 1][J & 1] = __expf(mild ? c3s : c3s - sTot[J * D + fr + r16]);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          float x[8];
-          keysT_tr(sKt, I, ft, ks, r16, g4, x);
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) x[jj] *= fac[ks][jj >> 2];
-          ka[ft][ks] = frag_from<T>(x);
-        }
-      }
-      // each v^T fragment serves both feature tiles; the next value tile's are loaded ahead
-      const T *vrow = sVt + r16 * LDV + 8 * g4;
-      Frag<T> vb[2][2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) vb[0][ks] = load8(vrow + 32 * ks);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        if (dt + 1 < NDT) {
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) vb[(dt + 1) & 1][ks] = load8(vrow + 16 * (dt + 1) * LDV + 32 * ks);
-        }
-#pragma unroll
-        for (int ft = 0; ft < FTW; ++ft)
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) S[ft][dt] = mma(ka[ft][ks], vb[dt & 1][ks], S[ft][dt]);
-      }
-    }
-    if (stop || c == b0) {
-      stopped = stop && c > b0;
-      break;
-    }
-    if (mine) __syncthreads();  // keys and values read before the next chunk is staged (the
-                                // other chunks' LDS reads all came before the last barrier)
-  }
+  float suf;
+  const bool stopped = walk_back<HH, true>(lds, Kh, Vh, LGh, b0, b1, pp, sss, tid, S, suf, [&]() {
+    load_wT_pairs<256, HH>(sW, reinterpret_cast<const T *>(p.wk), tid);
+  });
   float *E = p.ws_state + (size_t)grp * (D * D);
 #pragma unroll
   for (int ft = 0; ft < FTW; ++ft)
@@ -1397,7 +1517,7 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
 template <bool HH>
 static hipError_t launch_fwd_full_t(const FwdParams &p, hipStream_t stream) {
   hipError_t e;
-  if (p.nseg > 1) {
+  if (p.nseg > 1 && !p.split) {
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(fwd_full_state_kernel<HH>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, full::ST_LDS_BYTES);
     if (e != hipSuccess) return e;

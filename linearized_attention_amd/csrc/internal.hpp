@@ -32,6 +32,10 @@ struct FwdParams {
   int full;  // whole-head kernel (fwd_full.hip)
   int sss;   // whole-head kernel: state-pass pieces per segment (divides cps)
   int hh;    // whole-head kernel: Hedgehog feature map (W_phi [d][d/2]) instead of the softmax
+  int split; // whole-head kernel, two segments: > 0 puts the second segment's start at this chunk
+             // plus a shift and has its workgroups walk the chunks before it (no state pass)
+  int split_shift;  // the shift: < 0 estimated from the gates in the kernel, else this many chunks
+  int split_max;    // largest shift allowed
   float mix, scale;
 };
 

@@ -185,9 +185,28 @@ def test_fwd_whole_head_state_pass_drops_decayed_chunks(gpu_lib, monkeypatch, ga
     e^-40 in every feature (with -0.1 per token: all but the last 7 of 13 chunks; -0.5: the
     last 2), and splits the rest over its pieces; gamma = 1 keeps everything."""
     monkeypatch.setenv("LIZARD_FWD_SEGMENTS", "2")
+    monkeypatch.setenv("LIZARD_FWD_SPLIT_SHIFT", "-1")  # the state pass, not the self-started split
     inp = make_fwd_inputs(B=2, Hq=2, Hkv=2, L=1600, d=128, W=64, M=4, dtype="bf16",
                           seed=zlib.crc32(gate.encode()) % 10000, gate=gate)
     check_case(f"bf16 whole-head 2 segments, gate {gate}", inp, "bf16")
+
+
+@pytest.mark.parametrize("shift", [None, "-1", "0", "2", "100"])
+def test_fwd_whole_head_two_segment_split(gpu_lib, monkeypatch, shift):
+    """Two segments on the whole-head path: the second one's workgroups walk the chunks before
+    its start themselves (no state pass), and the first takes `shift` chunks beyond the even
+    split (None: estimated from the gates in the kernel; 100 is capped at a quarter segment;
+    -1: the state pass instead).  Gates with long, short and no decay, a ragged tail, GQA."""
+    monkeypatch.setenv("LIZARD_FWD_SEGMENTS", "2")
+    if shift is None:
+        monkeypatch.delenv("LIZARD_FWD_SPLIT_SHIFT", raising=False)
+    else:
+        monkeypatch.setenv("LIZARD_FWD_SPLIT_SHIFT", shift)
+    for gate, kw in (("logsigmoid", dict(B=1, Hq=4, Hkv=2, L=1650)), ("uniform:-1.6", dict(B=2, Hq=1, Hkv=1, L=900)),
+                     ("one", dict(B=1, Hq=2, Hkv=2, L=1000))):
+        inp = make_fwd_inputs(d=128, W=64, M=4, dtype="bf16", seed=zlib.crc32(f"{gate}{shift}".encode()) % 10000,
+                              gate=gate, **kw)
+        check_case(f"bf16 whole-head 2 segments, shift {shift}, gate {gate}", inp, "bf16")
 
 
 @pytest.mark.parametrize("label", ["bf16 d128 ragged L200", "bf16 gamma=0 (exact diag)", "bf16 gamma=1"])
