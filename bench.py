@@ -36,9 +36,9 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_full_workload1.json")
 KERNEL_SOURCES = ["linearized_attention_amd/csrc/fwd_full.hip", "linearized_attention_amd/csrc/fwd_common.hpp",
                   "linearized_attention_amd/csrc/common.hpp", "linearized_attention_amd/csrc/api.hip"]
-# The forward call on this workload launches the segment state pass and the whole-head kernel
-# (the dominant one); timings, rooflines and traffic refer to the call, i.e. both.
-FWD_KERNEL = "fwd_full_state_kernel + fwd_full_kernel"
+# The forward call on this workload launches one whole-head kernel (two segments per head, the
+# second walking its own start state); timings, rooflines and traffic refer to the call.
+FWD_KERNEL = "fwd_full_kernel"
 FWD_KERNEL_SYMBOL = "fwd_full"
 COPY_BYTES = 1 << 30
 
