@@ -541,6 +541,181 @@ __device__ __forceinline__ bool walk_back(const WalkLds &lds, const bf16 *Kh, co
   return stopped;
 }
 
+// The same walk over [0, b1) for the workgroup of a self-started segment, split between its two
+// roles and pipelined by one chunk: the query waves (Q, wt = tid) stage chunk c, take its feature
+// map, prefix sums, suffix and decayed keys, while the key waves (K, wt = tid - 256) add chunk
+// c + 1, whose results sit in the other of two LDS buffers, to S.  Three barriers per chunk; K
+// adds the last chunk after the loop.  S and suf as in walk_back (S in the key waves only).
+struct PipeLds {
+  const bf16 *sW;
+  bf16 *sVt0, *sVt1, *sKt0, *sKt1;  // the two buffers (named, not indexed: an indexed pointer
+  float *sTot0, *sTot1, *sSuf;      // array would live in scratch memory)
+  int *sVote;
+  __device__ bf16 *vt(int b) const { return b ? sVt1 : sVt0; }
+  __device__ bf16 *kt(int b) const { return b ? sKt1 : sKt0; }
+  __device__ float *tot(int b) const { return b ? sTot1 : sTot0; }
+};
+template <bool HH, bool QROLE>
+__device__ __forceinline__ void walk_pipe(const PipeLds &lds, const bf16 *Kh, const bf16 *Vh, const bf16 *LGh,
+                                          int b1, int wt, f32x4 (&S)[full::FTW][full::NDT]) {
+  using namespace full;
+  using T = bf16;
+  const int lane = wt & 63, I = wt >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  auto load_k = [&](Frag<T> (&kf)[KS], int c0) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const T *src = Kh + (size_t)(c0 + 16 * I + (ln & 15)) * D;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) kf[j] = load8(src + 32 * j + 8 * (ln >> 4));
+  };
+  auto load_pairs = [&](Frag<T> (&f)[2][2], const T *base, int c0) {
+    int w = wt;
+    asm volatile("" : "+v"(w));
+    const int tp = w & 31;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int gsel = 0; gsel < 2; ++gsel) f[gsel][h] = load8(base + (size_t)(c0 + 2 * tp + h) * D + 8 * ((w >> 5) + 8 * gsel));
+  };
+  // K: S += chunk c's decayed keys^T (buffer bj) times its v^T, keys scaled by e^{s_c + C_3 (- C_J)}
+  auto add_chunk = [&](int bj) {
+    const T *sKt = lds.kt(bj), *sVt = lds.vt(bj);
+    const float *sTot = lds.tot(bj), *suf_c = lds.sSuf + bj * D;
+    const bool mild = chunk_is_mild_c<D>(sTot, lane);
+    Frag<T> ka[FTW][2];
+#pragma unroll
+    for (int ft = 0; ft < FTW; ++ft) {
+      const int fr = 16 * (2 * I + ft);
+      float fac[2][2];
+      const float c3s = sTot[3 * D + fr + r16] + suf_c[fr + r16];
+#pragma unroll
+      for (int J = 0; J < 4; ++J) fac[J >> 1][J & 1] = __expf(mild ? c3s : c3s - sTot[J * D + fr + r16]);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        float x[8];
+        keysT_tr(sKt, I, ft, ks, r16, g4, x);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) x[jj] *= fac[ks][jj >> 2];
+        ka[ft][ks] = frag_from<T>(x);
+      }
+    }
+    const T *vrow = sVt + r16 * LDV + 8 * g4;
+    Frag<T> vb[2][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) vb[0][ks] = load8(vrow + 32 * ks);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      if (dt + 1 < NDT) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) vb[(dt + 1) & 1][ks] = load8(vrow + 16 * (dt + 1) * LDV + 32 * ks);
+      }
+#pragma unroll
+      for (int ft = 0; ft < FTW; ++ft)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) S[ft][dt] = mma(ka[ft][ks], vb[dt & 1][ks], S[ft][dt]);
+    }
+  };
+
+  Frag<T> kf[KS], vf[2][2], lf[2][2];
+  float suf = 0.f;  // Q, wt < D: log-gate sum of feature wt over the chunks walked so far
+  int c = b1 - 1;
+  if constexpr (QROLE) {
+    load_pairs(lf, LGh, c * CH);
+    load_k(kf, c * CH);
+    load_pairs(vf, Vh, c * CH);
+    if (wt < D) lds.sSuf[wt] = 0.f;  // s of the last chunk (buffer 0)
+  } else {
+#pragma unroll
+    for (int ft = 0; ft < FTW; ++ft)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) S[ft][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const Frag<T> tri_c0 = tri64_frag<T>(r16, g4, I, 0), tri_c1 = tri64_frag<T>(r16, g4, I, 1);
+  __syncthreads();
+  for (int j = 0;; ++j, --c) {
+    const int bj = j & 1;
+    float ko[NFT][4];
+    if constexpr (QROLE) {
+      T *sKt = lds.kt(bj), *sVt = lds.vt(bj);
+      {
+        f32x4 z[NFT];
+        feature_logits_pipe(lds.sW, kf, r16, g4, z);
+        feature_map_rows<HH>(z, ko);
+      }
+      const int tp = wt & 31;
+      const int vpos = (2 * tp & 32) | ipos(2 * tp & 31);
+#pragma unroll
+      for (int gsel = 0; gsel < 2; ++gsel) {
+        const int gq = (wt >> 5) + 8 * gsel;
+        store_pairT<T, LDV>(vf[gsel][0], vf[gsel][1], sVt + (8 * gq) * LDV + vpos);
+        store_pairT<T, LDV>(lf[gsel][0], lf[gsel][1], sKt + (8 * gq) * LDV + 2 * tp);  // log gamma^T
+      }
+      if (c > 0) {
+        load_pairs(lf, LGh, (c - 1) * CH);
+        load_k(kf, (c - 1) * CH);
+        load_pairs(vf, Vh, (c - 1) * CH);
+      }
+    } else {
+      if (j > 0) add_chunk(bj ^ 1);  // the previous (later) chunk
+    }
+    __syncthreads();  // W1: log gamma^T and v^T of chunk c staged
+    float pc[NFT][4];
+    if constexpr (QROLE) {
+      const T *sLgT = lds.kt(bj);
+      float *sTot = lds.tot(bj);
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft) {
+        f32x4 cc = mma(load8(sLgT + (16 * ft + r16) * LDV + 8 * g4), tri_c0, f32x4{0.f, 0.f, 0.f, 0.f});
+        cc = mma(load8(sLgT + (16 * ft + r16) * LDV + 32 + 8 * g4), tri_c1, cc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pc[ft][i] = cc[i];
+      }
+      if (r16 == 15) {
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft)
+          *reinterpret_cast<f32x4 *>(sTot + I * D + 16 * ft + 4 * g4) = f32x4{pc[ft][0], pc[ft][1], pc[ft][2], pc[ft][3]};
+      }
+    }
+    __syncthreads();  // W2: prefix ends of chunk c visible
+    if constexpr (QROLE) {
+      const float *sTot = lds.tot(bj);
+      T *sKt = lds.kt(bj);
+      if (wt < D) {  // suffix through chunk c: s of the next chunk back (other buffer's slot)
+        suf += sTot[3 * D + wt];
+        lds.sSuf[(bj ^ 1) * D + wt] = suf;
+        const bool below = __all(suf < -SKIP_LOG);
+        if (lane == 0) lds.sVote[I] = below;
+      }
+      if (chunk_is_mild_c<D>(sTot, lane)) {
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ko[ft][i] *= exp2_fast(-pc[ft][i] * LOG2E);
+      } else {
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft) {
+          const f32x4 t = *reinterpret_cast<const f32x4 *>(sTot + I * D + 16 * ft + 4 * g4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ko[ft][i] *= __expf(t[i] - pc[ft][i]);
+        }
+      }
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft) {
+        const int fpos = 32 * (ft >> 1) + 8 * g4 + 4 * (ft & 1);
+        store4<T>(sKt + (16 * I + r16) * LDW + fpos, ko[ft][0], ko[ft][1], ko[ft][2], ko[ft][3]);
+      }
+    }
+    __syncthreads();  // W3: decayed keys, suffix and votes of chunk c visible
+    const bool stop = lds.sVote[0] && lds.sVote[1];
+    if (stop || c == 0) {
+      if constexpr (!QROLE) add_chunk(bj);
+      break;
+    }
+  }
+  __syncthreads();
+}
+
 // ZW: windows of 66..129 keys, which reach into the chunk two back (window group Z)
 template <bool ZW, bool HH>
 __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
@@ -558,10 +733,17 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
   T *sTk = reinterpret_cast<T *>(smem + OFF_TK);
   T *sTvT = reinterpret_cast<T *>(smem + OFF_TV);
   uint32_t *sFlag = reinterpret_cast<uint32_t *>(smem + OFF_FLAG);
-  // a self-started segment walks the chunks before it with the regions of the chunk loop; its
-  // suffix sums and votes sit in the decayed-query rows, unused until the loop
-  const WalkLds wlds{sW, sVt, sKt, sTot, reinterpret_cast<float *>(smem + OFF_Q),
-                     reinterpret_cast<int *>(smem + OFF_Q + 2 * D * 4)};
+  // A self-started segment walks the chunks before it (walk_pipe) in two LDS buffers: the
+  // regions of the chunk loop, and copies of them in the S^T-copy and decayed-query rows (unused
+  // until the loop), where the suffix sums, votes and the split estimate follow.
+  constexpr int SC_VT = 0, SC_KT = SC_VT + D * LDV * 2, SC_TAB = SC_KT + SZ_KT;
+  constexpr int SC_SUF = SC_TAB + 4 * D * 4, SC_VOTE = SC_SUF + 2 * D * 4, SC_PART = SC_VOTE + 64;
+  static_assert(OFF_Q == OFF_SB + D * LDW * 2, "scratch spans the S^T copy and the decayed queries");
+  static_assert(SC_PART + 4 * D * 4 <= D * LDW * 2 + CH * LDQ * 2, "walk scratch exceeds its rows");
+  char *scr = smem + OFF_SB;
+  const PipeLds plds{sW, sVt, reinterpret_cast<T *>(scr + SC_VT), sKt, reinterpret_cast<T *>(scr + SC_KT),
+                     sTot, reinterpret_cast<float *>(scr + SC_TAB), reinterpret_cast<float *>(scr + SC_SUF),
+                     reinterpret_cast<int *>(scr + SC_VOTE)};
 
   // lane id from mbcnt and the wave index as a scalar: both can be rebuilt anywhere, so the
   // register allocator recomputes lane-derived values instead of keeping (or spilling) them
@@ -603,7 +785,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
   // gates, by every workgroup of the head alike, so both segments agree on it.
   int bsplit = 0;
   if (p.split) {
-    float *part = reinterpret_cast<float *>(smem + OFF_Q + 2 * D * 4 + 16);  // after the walk's words
+    float *part = reinterpret_cast<float *>(scr + SC_PART);
     if (p.split_shift < 0) split_shift_part(LGh, p.split, wv, lane, part);
     __syncthreads();
     const int sh = p.split_shift >= 0 ? p.split_shift : split_shift(part, p.split, lane);
@@ -748,10 +930,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
     const int kt = tid - 256;
     // S rows owned: feature tiles 2I, 2I+1; S[ft][dt][i] = S[16(2I+ft) + 4g4 + i][16dt + r16]
     f32x4 S[FTW][NDT];
-    if (self_start) {  // the state at the split: the chunks before it walked backwards
-      float suf;
-      walk_back<HH, true>(wlds, Kh, Vh, LGh, 0, c_begin, 0, 1, kt, S, suf, [] {});
-    }
+    if (self_start) walk_pipe<HH, false>(plds, Kh, Vh, LGh, c_begin, kt, S);  // the state at the split
     {
       Frag<T> kf[KS];
       if constexpr (ZW) {
@@ -1001,10 +1180,9 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
     }
   } else {
     // ======================================================= query waves
-    if (self_start) {  // the key waves walk the chunks before the split; same barriers here
+    if (self_start) {  // the query waves' part of the walk to the split
       f32x4 Sd[FTW][NDT];
-      float sd;
-      walk_back<HH, false>(wlds, Kh, Vh, LGh, 0, c_begin, 0, 1, tid, Sd, sd, [] {});
+      walk_pipe<HH, true>(plds, Kh, Vh, LGh, c_begin, tid, Sd);
     }
     const float sl2 = p.scale * LOG2E;  // window logits in base 2
     // Window group Z (ZW only): the keys of the chunk two back, tiles I..3, for the queries qz of
