@@ -209,6 +209,17 @@ def test_fwd_whole_head_two_segment_split(gpu_lib, monkeypatch, shift):
         check_case(f"bf16 whole-head 2 segments, shift {shift}, gate {gate}", inp, "bf16")
 
 
+@pytest.mark.parametrize("L", [65, 100, 129, 190])
+def test_fwd_whole_head_two_segment_split_short(gpu_lib, monkeypatch, L):
+    """Two self-started segments on 2-3 chunks: a one-chunk walk, a ragged last chunk, a last
+    segment of one token (L = 129), and no room for a shift."""
+    monkeypatch.setenv("LIZARD_FWD_SEGMENTS", "2")
+    monkeypatch.delenv("LIZARD_FWD_SPLIT_SHIFT", raising=False)
+    for gate in ("logsigmoid", "one"):
+        inp = make_fwd_inputs(B=2, Hq=2, Hkv=1, L=L, d=128, W=64, M=4, dtype="bf16", seed=L, gate=gate)
+        check_case(f"bf16 whole-head 2 segments, L={L}, gate {gate}", inp, "bf16")
+
+
 @pytest.mark.parametrize("label", ["bf16 d128 ragged L200", "bf16 gamma=0 (exact diag)", "bf16 gamma=1"])
 def test_fwd_value_block_kernel(gpu_lib, monkeypatch, label):
     """The value-block (role-split) kernel on cases the whole-head kernel would otherwise take
