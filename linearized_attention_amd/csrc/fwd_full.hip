@@ -38,6 +38,11 @@
 // It is used for the features of the decayed keys and of the state copy, and for
 // the tokens of v^T.  Row strides are odd multiples of 32 bytes, which gfx950
 // serves without bank conflicts for 16-byte fragment reads.
+//
+// A sequence may be split into segments (one workgroup each) to fill the chip.  A segment's start
+// state comes from the state pass (fwd_full_state_kernel, three or more segments), or, for the
+// second of two segments, from a backward walk over the chunks before it that its own workgroup
+// runs first (walk_pipe); the first segment then takes a few chunks more (split_shift).
 #include <type_traits>
 
 #include "fwd_common.hpp"
@@ -545,7 +550,7 @@ __device__ __forceinline__ bool walk_back(const WalkLds &lds, const bf16 *Kh, co
 // roles and pipelined by one chunk: the query waves (Q, wt = tid) stage chunk c, take its feature
 // map, prefix sums, suffix and decayed keys, while the key waves (K, wt = tid - 256) add chunk
 // c + 1, whose results sit in the other of two LDS buffers, to S.  Three barriers per chunk; K
-// adds the last chunk after the loop.  S and suf as in walk_back (S in the key waves only).
+// adds the last chunk after the loop.  S as in walk_back (in the key waves only).
 struct PipeLds {
   const bf16 *sW;
   bf16 *sVt0, *sVt1, *sKt0, *sKt1;  // the two buffers (named, not indexed: an indexed pointer
@@ -1643,8 +1648,8 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
 // the key waves above; 80 KB of LDS, so two workgroups share a CU.  The pieces of a block run
 // 8 workgroups apart, on one XCD, and share its L2 for the log gates they all read.
 //
-// The walk itself (walk_back) also starts the second of two segments inside the whole-head
-// kernel, without a state pass (fwd_full_kernel, p.split).
+// The same walk, split between the two roles of the whole-head kernel (walk_pipe), starts the
+// second of two segments there without a state pass (fwd_full_kernel, p.split).
 namespace full {
 constexpr int ST_OFF_W = 0;
 constexpr int ST_OFF_VT = ST_OFF_W + D * LDWW * 2;
