@@ -310,8 +310,9 @@ __device__ __forceinline__ void feature_map_rows(const f32x4 (&z)[NFT], float (&
 // Chunks the first of two segments takes beyond the even split at chunk b, so that both end
 // together.  The second segment first walks back from its start until every feature has decayed
 // by e^{-SKIP_LOG}, about n = SKIP_LOG / r chunks for the slowest feature's log decay r per
-// chunk (at most b).  Measured on MI355X, a walk costs about 3 + 3.7 n us and a chunk of the
-// main loop 6.5 us, so the first segment takes (3 + 3.7 n) / 13 chunks more.  r comes from the
+// chunk (at most b).  Measured on MI355X, the walk with its set-up costs about 6 + 3.2 n us and
+// a chunk of the main loop 6.5 us, so the first segment takes (6 + 3.2 n) / 13 chunks more (fitted
+// over gates whose walks last 1, 7, 14 and all chunks).  r comes from the
 // last four chunks before b: wave w < 4 sums chunk b - 1 - w per feature into part[w][D]
 // (shared memory), and after the barrier that follows every wave reads the four rows and
 // reduces them the same way.  Every workgroup of the head runs this on the same data with the
@@ -350,7 +351,7 @@ __device__ __forceinline__ int split_shift(const float *part, int b, int lane) {
   }
   r = -wave_max_all(-r) / (float)nc;
   const float n = fminf(SKIP_LOG / fmaxf(r, 1.0e-6f), (float)b);
-  return (int)((3.f + 3.7f * n) / 13.f + 0.5f);
+  return (int)((6.f + 3.2f * n) / 13.f + 0.5f);
 }
 
 // The backward walk of the segment state pass (see fwd_full_state_kernel below).
