@@ -170,3 +170,14 @@ def test_ext_with_segments(gpu_lib, monkeypatch):
     monkeypatch.setenv("LIZARD_FWD_SEGMENTS", "3")
     test_chunked_prefill_matches_one_forward(gpu_lib, "fp32 3 segments", dict(B=1, Hq=2, Hkv=2, L=400, d=64,
                                                                                 W=64, M=4), 100, "f32")
+
+
+@pytest.mark.parametrize("nseg", [2, 3])
+def test_ext_whole_head_with_segments(gpu_lib, monkeypatch, nseg):
+    """The whole-head path in a continuation: the first call (no state in, no history: with two
+    segments its second one starts itself) exports state and ring, the second imports them
+    (the state pass then, since the walk starts from zero)."""
+    monkeypatch.setenv("LIZARD_FWD_SEGMENTS", str(nseg))
+    monkeypatch.delenv("LIZARD_FWD_SPLIT_SHIFT", raising=False)
+    test_chunked_prefill_matches_one_forward(gpu_lib, f"bf16 whole-head {nseg} segments",
+                                             dict(B=2, Hq=2, Hkv=1, L=900, d=128, W=64, M=4), 600, "bf16")
