@@ -100,10 +100,10 @@ def time_launches(fn, steps: int):
     return t_start.elapsed_time(t_end), per
 
 
-def bench_forward(steps: int, warmup: int):
-    c = WORKLOADS[1]
-    log("[bench] generating forward workload:", WORKLOAD_NAMES[1])
-    inp = workload_fwd_inputs(1)
+def bench_forward(steps: int, warmup: int, idx: int = 1):
+    c = WORKLOADS[idx]
+    log("[bench] generating forward workload:", WORKLOAD_NAMES[idx])
+    inp = workload_fwd_inputs(idx)
     g = inp.to("cuda")
     out = torch.empty_like(g.q)
     need = api.lizard_attn_fwd_workspace_bytes(c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], c["W"], g.q.dtype)
@@ -255,6 +255,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--workload", type=int, default=1, choices=(1, 2, 4),
+                    help="forward workload to time (2: 32K stress, 4: GQA); other than 1, only that "
+                         "forward is timed and reported")
     ap.add_argument("--no-hedgehog", action="store_true",
                     help="skip the Hedgehog-map forward on the same shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -287,7 +290,7 @@ def main():
         log(f"[bench] pmc run: one forward, then a copy of {nbytes} bytes read + {nbytes} bytes written")
         return
 
-    c, inp, total_ms, per = bench_forward(args.steps, args.warmup)
+    c, inp, total_ms, per = bench_forward(args.steps, args.warmup, args.workload)
     ms_per_step = total_ms / args.steps
     tokens = c["B"] * c["L"]
     value = tokens / (ms_per_step * 1e-3)
@@ -295,7 +298,7 @@ def main():
     kern_ms = sum(per) / len(per)
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
     mfma_tflops = flops / (kern_ms * 1e-3) / 1e12
-    traffic = load_traffic(nbytes)
+    traffic = load_traffic(nbytes) if args.workload == 1 else None
     result = {
         "metric": "Lizard-attn fwd tokens/sec at L=4096,H=32,d=128; % MFMA peak; decode % HBM BW",
         "value": value,
@@ -309,17 +312,21 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_NAMES[1], "B": c["B"], "H": c["Hq"], "L": c["L"], "d": c["d"],
+        "config": {"workload": WORKLOAD_NAMES[args.workload], "B": c["B"], "H": c["Hq"], "Hkv": c["Hkv"], "L": c["L"], "d": c["d"],
                    "W": c["W"], "M": c["M"], "chunk": 64, "accumulation": "fp32"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": FWD_KERNEL, "kernel_ms": kern_ms,
+                     "kernel": FWD_KERNEL if args.workload == 1 else "fwd_full_state_kernel + fwd_full_kernel",
+                     "kernel_ms": kern_ms,
                      "algorithmic_bytes_per_launch": nbytes},
         "mfma": {"algorithmic_flops_per_launch": flops, "achieved_tflops": mfma_tflops,
                  "peak_tflops": BF16_PEAK_TFLOPS, "frac": mfma_tflops / BF16_PEAK_TFLOPS},
     }
     del inp
     torch.cuda.empty_cache()
+    if args.workload != 1:
+        print(json.dumps(result), flush=True)
+        return
     if not args.no_hedgehog:
         hc, htot, hper = bench_forward_hedgehog(max(args.steps // 2, 1), args.warmup)
         hms = sum(hper) / len(hper)
