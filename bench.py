@@ -6,10 +6,21 @@ A step is one forward pass (feature maps, chunk-local gate sums, intra- and
 inter-chunk products, state scan, anchor window, merge) over the
 Llama-3-8B-shaped layer: B=4, H=32, L=4096, d=128, W=64, M=4, bf16 inputs with
 fp32 accumulation, seeded synthetic data.  Inputs are resident in HBM before
-the timed region.  The JSON line also carries the decode step (N=256
-sequences, H=32, d=128, fp32 state, W=64, M=4; 128 consecutive steps) with its
-own HBM roofline, and the fp64 oracle timed on the host cores on a bounded
-sample of the forward workload.
+the timed region.
+
+Timing.  After the W requested warm-up calls, warm-up continues until at least
+CLOCK_WARMUP_MS of back-to-back forward calls have run (the GPU's clocks take
+some 50-100 ms of steady work to settle); the line states the warm-up actually
+run.  Then K calls are timed back to back, bracketed by two synchronisations
+(`ms_per_step`, `value`).  The roofline figures come from a second pass of K
+calls, each preceded by a 512 MB write that flushes the 256 MB MALL, timed one
+by one with HIP events on the launch stream: the median and the mean are
+reported, `achieved` uses the median.
+
+The JSON line also carries the decode step (N=256 sequences, H=32, d=128, fp32
+state, W=64, M=4; 128 consecutive steps) with its own HBM roofline, the
+forward with the Hedgehog feature map, and the fp64 oracle timed on the host
+cores over the whole forward workload (about 1.5 s of wall time on 16 threads).
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -19,6 +30,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -34,6 +46,9 @@ from linearized_attention_amd.synthetic import (WORKLOADS, WORKLOAD_NAMES, make_
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_full_workload1.json")
+COUNTER_FILE = os.path.join(ROOT, "profiles", "counters_fwd_full_workload{}.json")
+CLOCK_WARMUP_MS = 400.0        # minimum of steady forward calls before the timed region
+FLUSH_BYTES = 512 << 20        # written before each flushed launch (MALL is 256 MB)
 KERNEL_SOURCES = ["linearized_attention_amd/csrc/fwd_full.hip", "linearized_attention_amd/csrc/fwd_common.hpp",
                   "linearized_attention_amd/csrc/common.hpp", "linearized_attention_amd/csrc/api.hip"]
 # The forward call on this workload launches one whole-head kernel (two segments per head, the
@@ -59,16 +74,18 @@ def fwd_algorithmic(c) -> tuple[float, float]:
     """Algorithmic bytes and flops of one forward over workload c.
 
     Bytes: q, k, v, log gamma read once and out written once (per-KV tensors
-    counted once); weights and meta tokens are negligible.  Flops per query
-    token-head: feature maps 4 d d_f (key side counted per query head here,
-    as in the layer without grouping), intra-chunk (C+1)(d_f+d_v), inter-chunk
-    read-out 2 d_f d_v, state update 2 d_f d_v, window 2 (M + W) (d + d_v)."""
+    counted once); weights and meta tokens are negligible.  Flops: per query
+    token-head the query feature map 2 d d_f, intra-chunk (C+1)(d_f+d_v),
+    inter-chunk read-out 2 d_f d_v and window 2 (M + W) (d + d_v); per key
+    token-head (once per key/value head) the key feature map 2 d d_f and the
+    state update 2 d_f d_v."""
     B, Hq, Hkv, L, d, W, M = c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], c["W"], c["M"]
     e = 2 if c["dtype"] == "bf16" else 4
     nbytes = e * d * (2 * B * Hq * L + 3 * B * Hkv * L)
     C = 64
-    per = 4 * d * d + (C + 1) * (2 * d) + 2 * d * d + 2 * d * d + 2 * (M + W) * (2 * d)
-    return float(nbytes), float(per) * B * Hq * L
+    per_q = 2 * d * d + (C + 1) * (2 * d) + 2 * d * d + 2 * (M + W) * (2 * d)
+    per_k = 2 * d * d + 2 * d * d
+    return float(nbytes), float(per_q) * B * Hq * L + float(per_k) * B * Hkv * L
 
 
 def decode_bytes_per_step(c) -> float:
@@ -79,6 +96,44 @@ def decode_bytes_per_step(c) -> float:
     per_kv = 2 * d * d * 4 + 2 * W * d * e + 2 * d * e + 3 * d * e
     per_q = 2 * d * e
     return float(N * (Hkv * per_kv + Hq * per_q))
+
+
+def clock_warmup(fn, calls: int, min_ms: float = CLOCK_WARMUP_MS):
+    """Run fn `calls` times, then on until at least min_ms of wall time of back-to-back calls
+    has passed.  Returns (calls run, ms)."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    for _ in range(calls):
+        fn()
+        n += 1
+    torch.cuda.synchronize()
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        for _ in range(10):
+            fn()
+        n += 10
+        torch.cuda.synchronize()
+    return n, (time.perf_counter() - t0) * 1e3
+
+
+def time_launches_flushed(fn, steps: int, flush: torch.Tensor):
+    """Per-launch HIP-event durations of `steps` calls of fn, each after a write of the whole
+    flush buffer (out of the timed interval) so that no input is left in the MALL."""
+    st = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        flush.fill_(i & 0xFF)
+        a.record(st)
+        fn()
+        b.record(st)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def launch_stats(per):
+    return {"median_ms": statistics.median(per), "mean_ms": sum(per) / len(per), "min_ms": min(per),
+            "max_ms": max(per), "launches": len(per)}
 
 
 def time_launches(fn, steps: int):
@@ -113,12 +168,13 @@ def bench_forward(steps: int, warmup: int, idx: int = 1):
         api.lizard_attn_fwd(g.q, g.k, g.v, g.log_gamma, g.w_phi_q, g.w_phi_k, g.t_k, g.t_v, W=inp.W,
                             M=inp.M, mix=inp.mix, scale=inp.scale, out=out, workspace=ws)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"[bench] forward: {warmup} warmup done, timing {steps} steps")
+    wcalls, wms = clock_warmup(step, warmup)
+    log(f"[bench] forward: {wcalls} warm-up calls in {wms:.0f} ms, timing {steps} steps")
     total_ms, per = time_launches(step, steps)
-    return c, inp, total_ms, per
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    per_flushed = time_launches_flushed(step, steps, flush)
+    del flush
+    return c, inp, total_ms, per, per_flushed, (wcalls, wms)
 
 
 def bench_forward_hedgehog(steps: int, warmup: int):
@@ -136,10 +192,8 @@ def bench_forward_hedgehog(steps: int, warmup: int):
         api.lizard_attn_fwd_hedgehog(g.q, g.k, g.v, g.log_gamma, g.w_phi_q, g.w_phi_k, g.t_k, g.t_v,
                                      W=inp.W, M=inp.M, mix=inp.mix, scale=inp.scale, out=out, workspace=ws)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"[bench] hedgehog forward: {warmup} warmup done, timing {steps} steps")
+    wcalls, wms = clock_warmup(step, warmup)
+    log(f"[bench] hedgehog forward: {wcalls} warm-up calls in {wms:.0f} ms, timing {steps} steps")
     total_ms, per = time_launches(step, steps)
     return c, total_ms, per
 
@@ -172,9 +226,21 @@ def bench_decode(steps: int, warmup: int):
     return c, total_ms, per
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline():
     """The fp64 oracle on the host cores over the whole forward workload (128
-    heads x 4096 tokens; about 20 thread-seconds of fp64 work)."""
+    heads x 4096 tokens; about 20 thread-seconds of fp64 work, 1-2 s of wall
+    time on 16 threads)."""
     import oracle
     c = WORKLOADS[1]
     inp = workload_fwd_inputs(1)
@@ -187,6 +253,7 @@ def cpu_baseline():
     dt = time.perf_counter() - t0
     tokens = c["B"] * c["L"]
     return {"value": tokens / dt, "unit": "tokens/s", "cores": min(threads, heads), "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"the whole forward workload ({c['B']} x {c['Hq']} heads x {c['L']} tokens), fp64, "
                       f"{dt:.2f} s wall"}
 
@@ -203,41 +270,97 @@ def _counter_means(path: str):
     return {k: sum(v.values()) / len(v) for k, v in per.items()}
 
 
-def write_traffic(fetch_csv: str, write_csv: str):
-    """Turn two counter passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) over
-    `bench.py --pmc-run` into HBM bytes per forward launch.  Each counter is
-    scaled by what it reads for the plain copy of COPY_BYTES in the same run."""
-    fetch, write = _counter_means(fetch_csv), _counter_means(write_csv)
+def _pick(means, counter, symbol, exclude=()):
+    vals = [v for (k, c), v in means.items() if c == counter and symbol in k and not any(x in k for x in exclude)]
+    if not vals:
+        raise SystemExit(f"no kernel matching {symbol!r} for {counter}")
+    return sum(vals)  # every kernel of one forward call
 
-    def pick(means, counter, symbol):
-        vals = [v for (k, c), v in means.items() if c == counter and symbol in k]
-        if not vals:
-            raise SystemExit(f"no kernel matching {symbol!r} for {counter}")
-        return sum(vals)  # every kernel of one forward call
-    kf, kw = pick(fetch, "FETCH_SIZE", FWD_KERNEL_SYMBOL), pick(write, "WRITE_SIZE", FWD_KERNEL_SYMBOL)
-    cf, cw = pick(fetch, "FETCH_SIZE", "copyBuffer"), pick(write, "WRITE_SIZE", "copyBuffer")
+
+def write_traffic(fetch_csv: str, write_csv: str, idx: int):
+    """Turn two counter passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) over
+    `bench.py --pmc-run --workload idx` into HBM bytes per forward call.  Each
+    counter is scaled by what it reads for the plain copy of COPY_BYTES in the
+    same run."""
+    fetch, write = _counter_means(fetch_csv), _counter_means(write_csv)
+    kf, kw = _pick(fetch, "FETCH_SIZE", FWD_KERNEL_SYMBOL), _pick(write, "WRITE_SIZE", FWD_KERNEL_SYMBOL)
+    cf, cw = _pick(fetch, "FETCH_SIZE", "copyBuffer"), _pick(write, "WRITE_SIZE", "copyBuffer")
     sf, sw = COPY_BYTES / (cf * 1024.0), COPY_BYTES / (cw * 1024.0)
-    c = WORKLOADS[1]
+    c = WORKLOADS[idx]
     nbytes, _ = fwd_algorithmic(c)
     traffic = kf * 1024.0 * sf + kw * 1024.0 * sw
-    out = {"kernel": FWD_KERNEL, "workload": WORKLOAD_NAMES[1], "kernel_source_sha": kernel_source_sha(),
+    out = {"kernel": FWD_KERNEL, "workload": WORKLOAD_NAMES[idx], "kernel_source_sha": kernel_source_sha(),
            "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw,
            "copy_fetch_kib": cf, "copy_write_kib": cw, "copy_bytes_each_way": COPY_BYTES,
            "fetch_scale": sf, "write_scale": sw,
            "traffic_bytes_per_launch": traffic, "algorithmic_bytes_per_launch": nbytes,
            "traffic_over_algorithmic": traffic / nbytes,
-           "commands": ["rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o pmc -- python3 bench.py --pmc-run",
-                        "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o pmc -- python3 bench.py --pmc-run",
-                        "python3 bench.py --write-traffic gpurun_out/pmc_fetch/pmc_counter_collection.csv "
+           "commands": [f"rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o pmc -- python3 bench.py "
+                        f"--pmc-run --workload {idx}",
+                        f"rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o pmc -- python3 bench.py "
+                        f"--pmc-run --workload {idx}",
+                        f"python3 bench.py --workload {idx} --write-traffic "
+                        "gpurun_out/pmc_fetch/pmc_counter_collection.csv "
                         "gpurun_out/pmc_write/pmc_counter_collection.csv"]}
-    with open(TRAFFIC_FILE, "w") as f:
+    path = TRAFFIC_FILE if idx == 1 else TRAFFIC_FILE.replace("workload1", f"workload{idx}")
+    with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
 
 
-def load_traffic(launch_bytes: float):
+GEMM_N = 8192  # the bf16 GEMM of --pmc-run: 2 N^3 flops, calibrates the MFMA counter
+
+
+def write_counters(csvs, idx: int):
+    """Per-call means of every SQ/GRBM counter collected over `bench.py --pmc-run --workload idx`
+    (one counter pass per file), summed over the kernels of one forward call, with the executed
+    bf16 MFMA flops: SQ_INSTS_VALU_MFMA_MOPS_BF16 scaled by 2 N^3 / (its value for the N^3 bf16
+    GEMM of the same run)."""
+    means = {}
+    for p in csvs:
+        means.update(_counter_means(p))
+    names = sorted({cn for (_, cn) in means})
+    fwd = {}
+    for cn in names:
+        try:
+            fwd[cn] = _pick(means, cn, FWD_KERNEL_SYMBOL)
+        except SystemExit:
+            pass
+    out = {"kernel": FWD_KERNEL, "workload": WORKLOAD_NAMES[idx], "kernel_source_sha": kernel_source_sha(),
+           "per_call": fwd}
+    mops = "SQ_INSTS_VALU_MFMA_MOPS_BF16"
+    if mops in fwd:
+        gemm = [v for (k, cn), v in means.items() if cn == mops and "lz::" not in k and "fwd_full" not in k]
+        g = max(gemm) if gemm else 0.0
+        if g > 0:
+            per_mop = 2.0 * GEMM_N ** 3 / g
+            _, algo = fwd_algorithmic(WORKLOADS[idx])
+            out["mfma_flops_per_mop"] = per_mop
+            out["executed_mfma_flops_per_call"] = fwd[mops] * per_mop
+            out["algorithmic_flops_per_call"] = algo
+            out["executed_over_algorithmic"] = fwd[mops] * per_mop / algo
+    out["commands"] = [f"rocprofv3 --pmc <counters> -f csv -d gpurun_out/pmc_<pass> -o pmc -- python3 bench.py "
+                       f"--pmc-run --workload {idx}", f"python3 bench.py --workload {idx} --write-counters <csv files>"]
+    with open(COUNTER_FILE.format(idx), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def load_counters(idx: int):
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(COUNTER_FILE.format(idx)) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t
+
+
+def load_traffic(idx: int = 1):
+    path = TRAFFIC_FILE if idx == 1 else TRAFFIC_FILE.replace("workload1", f"workload{idx}")
+    try:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -249,10 +372,11 @@ def load_traffic(launch_bytes: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # The GPU's clocks settle after some 50-100 ms of steady work: with 3 warm-up calls the timed
-    # calls of workload 1 ran about 15% slower than with 200 or more (measured on MI355X).
+    # Warm-up calls before the timed ones; the warm-up then continues until CLOCK_WARMUP_MS of
+    # steady calls have run (with 3 warm-up calls the timed calls of workload 1 ran about 15%
+    # slower than with 200 or more: the clocks had not settled).
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--workload", type=int, default=1, choices=(1, 2, 4),
@@ -262,13 +386,20 @@ def main():
                     help="skip the Hedgehog-map forward on the same shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-run", action="store_true",
-                    help="one forward plus a plain copy of known size, for rocprofv3 counter passes")
+                    help="a few forward calls, a plain copy of known size and a bf16 GEMM of known flops, "
+                         "for rocprofv3 counter passes")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="(no GPU) turn the two counter_collection.csv files of the --pmc-run passes "
-                         "into profiles/traffic_fwd_kernel_workload1.json")
+                         "into profiles/traffic_fwd_full_workload<N>.json")
+    ap.add_argument("--write-counters", nargs="+", metavar="CSV",
+                    help="(no GPU) turn counter_collection.csv files of --pmc-run passes into "
+                         "profiles/counters_fwd_full_workload<N>.json")
     args = ap.parse_args()
     if args.write_traffic:
-        write_traffic(*args.write_traffic)
+        write_traffic(*args.write_traffic, args.workload)
+        return
+    if args.write_counters:
+        write_counters(args.write_counters, args.workload)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -280,25 +411,40 @@ def main():
     api.load()
 
     if args.pmc_run:
-        c, inp, _, _ = bench_forward(1, 1)
+        bench_forward(2, 1, args.workload)
         nbytes = COPY_BYTES
         src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
+        del src, dst
+        a = torch.full((GEMM_N, GEMM_N), 0.5, dtype=torch.bfloat16, device="cuda")
+        b = torch.full((GEMM_N, GEMM_N), 0.25, dtype=torch.bfloat16, device="cuda")
+        torch.matmul(a, b)
         torch.cuda.synchronize()
-        log(f"[bench] pmc run: one forward, then a copy of {nbytes} bytes read + {nbytes} bytes written")
+        log(f"[bench] pmc run: forward calls, then a copy of {nbytes} bytes each way, then a "
+            f"{GEMM_N}^3 bf16 GEMM")
         return
 
-    c, inp, total_ms, per = bench_forward(args.steps, args.warmup, args.workload)
+    c, inp, total_ms, per, per_fl, (wcalls, wms) = bench_forward(args.steps, args.warmup, args.workload)
     ms_per_step = total_ms / args.steps
     tokens = c["B"] * c["L"]
     value = tokens / (ms_per_step * 1e-3)
     nbytes, flops = fwd_algorithmic(c)
-    kern_ms = sum(per) / len(per)
+    st = launch_stats(per_fl)
+    kern_ms = st["median_ms"]
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
     mfma_tflops = flops / (kern_ms * 1e-3) / 1e12
-    traffic = load_traffic(nbytes) if args.workload == 1 else None
+    traffic = load_traffic(args.workload)
+    counters = load_counters(args.workload)
+    mfma = {"algorithmic_flops_per_launch": flops, "achieved_tflops": mfma_tflops,
+            "peak_tflops": BF16_PEAK_TFLOPS, "frac": mfma_tflops / BF16_PEAK_TFLOPS,
+            "executed_flops_per_launch": None, "executed_tflops": None, "executed_frac": None}
+    if counters and counters.get("executed_mfma_flops_per_call"):
+        ex = counters["executed_mfma_flops_per_call"]
+        mfma.update(executed_flops_per_launch=ex, executed_tflops=ex / (kern_ms * 1e-3) / 1e12,
+                    executed_frac=ex / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                    executed_source=os.path.relpath(COUNTER_FILE.format(args.workload), ROOT))
     result = {
         "metric": "Lizard-attn fwd tokens/sec at L=4096,H=32,d=128; % MFMA peak; decode % HBM BW",
         "value": value,
@@ -306,21 +452,22 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_warmup": {"calls": wcalls, "ms": wms, "min_ms": CLOCK_WARMUP_MS},
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_NAMES[args.workload], "B": c["B"], "H": c["Hq"], "Hkv": c["Hkv"], "L": c["L"], "d": c["d"],
-                   "W": c["W"], "M": c["M"], "chunk": 64, "accumulation": "fp32"},
+        "config": {"workload": WORKLOAD_NAMES[args.workload], "B": c["B"], "H": c["Hq"], "Hkv": c["Hkv"],
+                   "L": c["L"], "d": c["d"], "W": c["W"], "M": c["M"], "chunk": 64, "accumulation": "fp32"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": FWD_KERNEL if args.workload == 1 else "fwd_full_state_kernel + fwd_full_kernel",
-                     "kernel_ms": kern_ms,
+                     "kernel_ms": kern_ms, "launches": {**st, "mall_flushed": True},
+                     "back_to_back_launch_mean_ms": sum(per) / len(per),
                      "algorithmic_bytes_per_launch": nbytes},
-        "mfma": {"algorithmic_flops_per_launch": flops, "achieved_tflops": mfma_tflops,
-                 "peak_tflops": BF16_PEAK_TFLOPS, "frac": mfma_tflops / BF16_PEAK_TFLOPS},
+        "mfma": mfma,
     }
     del inp
     torch.cuda.empty_cache()
@@ -329,7 +476,7 @@ def main():
         return
     if not args.no_hedgehog:
         hc, htot, hper = bench_forward_hedgehog(max(args.steps // 2, 1), args.warmup)
-        hms = sum(hper) / len(hper)
+        hms = statistics.median(hper)
         hach = nbytes / (hms * 1e-3) / 1e9
         result["hedgehog"] = {
             "workload": WORKLOAD_NAMES[1] + " hedgehog-map W_phi[128,64]",
@@ -343,7 +490,7 @@ def main():
     if not args.no_decode:
         dc, dtot, dper = bench_decode(args.decode_steps, 4)
         dbytes = decode_bytes_per_step(dc)
-        dms = sum(dper) / len(dper)
+        dms = statistics.median(dper)
         dach = dbytes / (dms * 1e-3) / 1e9
         result["decode"] = {
             "workload": WORKLOAD_NAMES[3], "steps": args.decode_steps,

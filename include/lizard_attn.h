@@ -33,7 +33,8 @@
  *     (except where a type is spelled out).  The caller owns every buffer.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *     enqueue work on it and return; nothing synchronises the host unless the
- *     environment variable LIZARD_DEBUG_SYNC=1 is set.
+ *     option "debug_sync" is set (lizard_set_option, or LIZARD_DEBUG_SYNC=1 in
+ *     the environment when the library is loaded).
  *   - The library allocates no device memory.  Scratch space comes from the
  *     caller's `workspace` argument.
  *   - Errors are reported only through the return value.  On any status other
@@ -82,7 +83,10 @@ typedef enum { LIZARD_F32 = 0, LIZARD_BF16 = 1 } lizard_dtype;
  *   out        [B, Hq, L, d]     written
  *   Hq must be a multiple of Hkv.  B = 0 or L = 0 is an empty problem: OK,
  *   nothing launched.  `scale` multiplies the window logits (1/sqrt(d) gives
- *   standard scaled dot-product attention).
+ *   standard scaled dot-product attention); it must be finite.  `mix` weighs
+ *   the global branch and 1 - mix the window: finite and >= 0 (mix > 1 is
+ *   allowed and gives the window a negative weight), else
+ *   LIZARD_ERR_INVALID_ARG.
  *   workspace  device scratch of at least lizard_attn_fwd_workspace_bytes()
  *              bytes for the same shapes (may be NULL when that is 0); its
  *              contents on entry do not matter and are clobbered.
@@ -166,7 +170,13 @@ size_t lizard_attn_fwd_ext_workspace_bytes(int B, int Hq, int Hkv, int L,
                                            int d, int W, lizard_dtype dtype);
 
 /*
- * One decode step: every sequence n takes one new token, in place.
+ * One decode step: every sequence n takes one new token, in place.  This is the
+ * recurrent (constant-memory) form of the same attention: the global branch
+ * carries its d x d state from token to token (arXiv page, Preliminaries, the
+ * recurrent view of linear attention; Experiments, "Generation Efficiency":
+ * memory and throughput stay constant with the length generated), and the
+ * window keeps only its last W keys and values (papernotes.org summary, "key
+ * designs", Anchor Window Attention item).
  *   state       [N, Hkv, d, d] float32 (always fp32), the S matrix of the
  *               global branch; row f is key dimension f.  Updated.
  *   win_k, win_v [N, Hkv, W, d] ring buffers of the last W keys / values; the
@@ -177,7 +187,7 @@ size_t lizard_attn_fwd_ext_workspace_bytes(int B, int Hq, int Hkv, int L,
  *               pos[n] + 1 < W.  Incremented by one.
  *   q [N, Hq, d]; k, v, log_gamma [N, Hkv, d]; out [N, Hq, d] (written)
  *   w_phi_q, w_phi_k, w_phi_head_stride, t_k, t_v, M, mix, scale: as in the
- *   forward.  The per-token arithmetic is the forward's: decay, add, read out;
+ *   forward (the same ranges of mix and scale).  The per-token arithmetic is the forward's: decay, add, read out;
  *   then a softmax over the M meta keys and the min(pos+1, W) newest keys.
  *   Running L steps from a zero state, pos = 0, reproduces the forward on
  *   those L tokens.
@@ -232,8 +242,30 @@ const char *lizard_status_string(lizard_status s);
 /* Thread-local detail of the last non-OK status returned on this thread. */
 const char *lizard_last_error(void);
 
-/* Library version string, e.g. "lizard_attn 0.1.0 gfx950". */
+/* Library version string, e.g. "lizard_attn 0.2.0 gfx950". */
 const char *lizard_version(void);
+
+/*
+ * Tuning and test options of the forward's launch plan (process-wide; they do
+ * not change any result beyond rounding):
+ *   "debug_sync"      1: synchronise the stream after every call (errors then
+ *                     surface at the call).
+ *   "fwd_kernel"      0: kernel chosen by shape; 1: the role-split value-block
+ *                     kernel; 2: the 4-wave value-block kernel.
+ *   "fwd_segments"    0: segments per sequence chosen by shape; n > 0: n.
+ *   "fwd_split_shift" with two segments: n >= 0 chunks moved to the first
+ *                     segment; a negative value runs the state pass instead of
+ *                     the self-started second segment; -1000000 (the start
+ *                     value): the shift is estimated from the gates.
+ * Start values come from the environment when the library is loaded
+ * (LIZARD_DEBUG_SYNC, LIZARD_FWD_KERNEL=split|4wave, LIZARD_FWD_SEGMENTS,
+ * LIZARD_FWD_SPLIT_SHIFT).  Calls read the options when they start; changing
+ * one while another thread is inside a call affects that call or the next.
+ * Unknown names or out-of-range values return LIZARD_ERR_INVALID_ARG.
+ */
+lizard_status lizard_set_option(const char *name, int value);
+/* Current value of an option (0 for an unknown name). */
+int lizard_get_option(const char *name);
 
 #ifdef __cplusplus
 }

@@ -26,7 +26,8 @@ _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 EXPORTED = ("lizard_attn_fwd", "lizard_attn_fwd_workspace_bytes", "lizard_attn_fwd_hedgehog",
             "lizard_attn_fwd_ext", "lizard_attn_fwd_ext_workspace_bytes", "lizard_attn_decode",
             "lizard_attn_decode_hedgehog", "lizard_attn_decode_workspace_bytes",
-            "lizard_status_string", "lizard_last_error", "lizard_version")
+            "lizard_status_string", "lizard_last_error", "lizard_version", "lizard_set_option",
+            "lizard_get_option")
 
 _lock = threading.Lock()
 _lib = None
@@ -67,6 +68,10 @@ def _declare(lib):
     lib.lizard_last_error.restype = ctypes.c_char_p
     lib.lizard_version.argtypes = []
     lib.lizard_version.restype = ctypes.c_char_p
+    lib.lizard_set_option.argtypes = [ctypes.c_char_p, i32]
+    lib.lizard_set_option.restype = i32
+    lib.lizard_get_option.argtypes = [ctypes.c_char_p]
+    lib.lizard_get_option.restype = i32
     return lib
 
 
@@ -113,15 +118,54 @@ def lizard_attn_fwd_workspace_bytes(B: int, Hq: int, Hkv: int, L: int, d: int, W
     return int(load().lizard_attn_fwd_workspace_bytes(B, Hq, Hkv, L, d, W, _DTYPES[dtype]))
 
 
-def _w_stride(w_q, w_k, d, cols=None):
+def set_option(name: str, value: int) -> None:
+    """Set a tuning / test option of the library (see lizard_set_option in the header)."""
+    _check(load().lizard_set_option(name.encode(), int(value)))
+
+
+def get_option(name: str) -> int:
+    return int(load().lizard_get_option(name.encode()))
+
+
+def _w_stride(w_q, w_k, d, Hq, Hkv, cols=None):
     cols = d if cols is None else cols
     if w_q.shape[-2:] != (d, cols) or w_k.shape[-2:] != (d, cols):
         raise ValueError(f"w_phi_q and w_phi_k must end in [{d},{cols}] for this feature map")
     if w_q.dim() == 2 and w_k.dim() == 2:
         return 0
     if w_q.dim() == 3 and w_k.dim() == 3:
+        if w_q.shape[0] != Hq or w_k.shape[0] != Hkv:
+            raise ValueError(f"per-head w_phi_q must be [{Hq},{d},{cols}] and w_phi_k [{Hkv},{d},{cols}]")
         return d * cols
     raise ValueError("w_phi_q and w_phi_k must both be shared or both per head")
+
+
+def _out(out, like, name="out"):
+    if out is None:
+        return torch.empty_like(like)
+    _dev(out, name, like.dtype)
+    if out.shape != like.shape or out.device != like.device:
+        raise ValueError(f"{name} must be {tuple(like.shape)} on {like.device}")
+    return out
+
+
+def _workspace(workspace, need, device):
+    """The caller's workspace (a uint8 GPU tensor of at least `need` bytes on `device`), or a
+    new one when None and `need` > 0."""
+    if workspace is None:
+        return None if need == 0 else torch.empty(need, dtype=torch.uint8, device=device)
+    _dev(workspace, "workspace", torch.uint8)
+    if workspace.device != device:
+        raise ValueError(f"workspace must be on {device}")
+    if workspace.numel() < need:
+        raise ValueError(f"workspace of {need} bytes needed, got {workspace.numel()}")
+    return workspace
+
+
+def _same_device(dev, *named):
+    for t, n in named:
+        if t is not None and t.device != dev:
+            raise ValueError(f"{n} must be on {dev}")
 
 
 def lizard_attn_fwd(q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v, *, W: int, M: int,
@@ -162,19 +206,18 @@ def _fwd(fn, q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v, *, W, M, mix, scale
         raise ValueError("k, v, log_gamma must be [B,Hkv,L,d] matching q")
     if M > 0 and (t_k.shape != (Hkv, M, d) or t_v.shape != (Hkv, M, d)):
         raise ValueError("t_k, t_v must be [Hkv,M,d]")
+    _same_device(q.device, (k, "k"), (v, "v"), (log_gamma, "log_gamma"), (w_phi_q, "w_phi_q"),
+                 (w_phi_k, "w_phi_k"), (t_k if M > 0 else None, "t_k"), (t_v if M > 0 else None, "t_v"))
+    wstride = _w_stride(w_phi_q, w_phi_k, d, Hq, Hkv, cols)
     if scale is None:
         scale = d ** -0.5
-    if out is None:
-        out = torch.empty_like(q)
-    else:
-        _dev(out, "out", dt)
+    out = _out(out, q)
     need = lizard_attn_fwd_workspace_bytes(B, Hq, Hkv, L, d, W, dt)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(fn(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), _ptr(w_phi_q), _ptr(w_phi_k),
-        _w_stride(w_phi_q, w_phi_k, d, cols), _ptr(t_k) if M > 0 else None, _ptr(t_v) if M > 0 else None,
+        wstride, _ptr(t_k) if M > 0 else None, _ptr(t_v) if M > 0 else None,
         _ptr(out), B, Hq, Hkv, L, d, W, M, float(mix), float(scale), _DTYPES[dt],
         _ptr(workspace), wbytes, _stream(stream)))
     return out
@@ -221,19 +264,22 @@ def lizard_attn_fwd_ext(q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v, *, W: in
         _dev(pos, "pos", torch.int32)
         if pos.shape != (B,):
             raise ValueError("pos must be [B]")
+    if M > 0 and (t_k.shape != (Hkv, M, d) or t_v.shape != (Hkv, M, d)):
+        raise ValueError("t_k, t_v must be [Hkv,M,d]")
+    _same_device(q.device, (k, "k"), (v, "v"), (log_gamma, "log_gamma"), (w_phi_q, "w_phi_q"),
+                 (w_phi_k, "w_phi_k"), (t_k if M > 0 else None, "t_k"), (t_v if M > 0 else None, "t_v"),
+                 (state_in, "state_in"), (state_out, "state_out"), (win_k_in, "win_k_in"),
+                 (win_v_in, "win_v_in"), (win_k_out, "win_k_out"), (win_v_out, "win_v_out"), (pos, "pos"))
+    wstride = _w_stride(w_phi_q, w_phi_k, d, Hq, Hkv)
     if scale is None:
         scale = d ** -0.5
-    if out is None:
-        out = torch.empty_like(q)
-    else:
-        _dev(out, "out", dt)
+    out = _out(out, q)
     need = lizard_attn_fwd_ext_workspace_bytes(B, Hq, Hkv, L, d, W, dt)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().lizard_attn_fwd_ext(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), _ptr(w_phi_q), _ptr(w_phi_k),
-        _w_stride(w_phi_q, w_phi_k, d), _ptr(t_k) if M > 0 else None, _ptr(t_v) if M > 0 else None,
+        wstride, _ptr(t_k) if M > 0 else None, _ptr(t_v) if M > 0 else None,
         _ptr(out), B, Hq, Hkv, L, d, W, M, float(mix), float(scale), _DTYPES[dt],
         _ptr(state_in), _ptr(win_k_in), _ptr(win_v_in), _ptr(pos), _ptr(state_out), _ptr(win_k_out),
         _ptr(win_v_out), _ptr(workspace), wbytes, _stream(stream)))
@@ -284,19 +330,21 @@ def _decode(fn, state, win_k, win_v, pos, q, k, v, log_gamma, w_phi_q, w_phi_k, 
         raise ValueError("state [N,Hkv,d,d] and win_k/win_v [N,Hkv,W,d] expected")
     if k.shape != (N, Hkv, d) or v.shape != k.shape or log_gamma.shape != k.shape or pos.shape != (N,):
         raise ValueError("k, v, log_gamma must be [N,Hkv,d] and pos [N]")
+    if M > 0 and (t_k.shape != (Hkv, M, d) or t_v.shape != (Hkv, M, d)):
+        raise ValueError("t_k, t_v must be [Hkv,M,d]")
+    _same_device(q.device, (state, "state"), (win_k, "win_k"), (win_v, "win_v"), (pos, "pos"), (k, "k"),
+                 (v, "v"), (log_gamma, "log_gamma"), (w_phi_q, "w_phi_q"), (w_phi_k, "w_phi_k"),
+                 (t_k if M > 0 else None, "t_k"), (t_v if M > 0 else None, "t_v"))
+    wstride = _w_stride(w_phi_q, w_phi_k, d, Hq, Hkv, cols)
     if scale is None:
         scale = d ** -0.5
-    if out is None:
-        out = torch.empty_like(q)
-    else:
-        _dev(out, "out", dt)
-    if workspace is None:
-        need = lizard_attn_decode_workspace_bytes(N, Hq, Hkv, d, dt)
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    out = _out(out, q)
+    need = lizard_attn_decode_workspace_bytes(N, Hq, Hkv, d, dt)
+    workspace = _workspace(workspace, max(need, 16), q.device)
     wbytes = workspace.numel() * workspace.element_size()
     _check(fn(
         _ptr(state), _ptr(win_k), _ptr(win_v), _ptr(pos), _ptr(q), _ptr(k), _ptr(v),
-        _ptr(log_gamma), _ptr(w_phi_q), _ptr(w_phi_k), _w_stride(w_phi_q, w_phi_k, d, cols),
+        _ptr(log_gamma), _ptr(w_phi_q), _ptr(w_phi_k), wstride,
         _ptr(t_k) if M > 0 else None, _ptr(t_v) if M > 0 else None, _ptr(out),
         N, Hq, Hkv, d, W, M, float(mix), float(scale), _DTYPES[dt], _ptr(workspace), wbytes,
         _stream(stream)))

@@ -7,6 +7,8 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <atomic>
+#include <cmath>
 
 #include "../../include/lizard_attn.h"
 #include "internal.hpp"
@@ -25,13 +27,30 @@ lizard_status fail(lizard_status s, const char *fmt, ...) {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool debug_sync() {
-  static const int v = [] {
-    const char *e = getenv("LIZARD_DEBUG_SYNC");
-    return (e && e[0] == '1') ? 1 : 0;
-  }();
-  return v != 0;
-}
+// Tuning and test options.  Their start values come from the environment, read once when the
+// library is loaded (LIZARD_DEBUG_SYNC=1, LIZARD_FWD_KERNEL=split|4wave, LIZARD_FWD_SEGMENTS=n,
+// LIZARD_FWD_SPLIT_SHIFT=n); lizard_set_option() changes them afterwards.  Calls only read them.
+struct Options {
+  std::atomic<int> debug_sync{0};
+  std::atomic<int> fwd_kernel{0};   // 0: chosen by shape, 1: role-split, 2: 4-wave
+  std::atomic<int> segments{0};     // 0: chosen by shape, else this many segments
+  std::atomic<int> split_shift{kShiftAuto};  // kShiftAuto: estimated; < 0: no self-started split
+  static constexpr int kShiftAuto = -1000000;
+  Options() {
+    if (const char *e = getenv("LIZARD_DEBUG_SYNC")) debug_sync = (e[0] == '1');
+    if (const char *e = getenv("LIZARD_FWD_KERNEL")) fwd_kernel = kernel_code(e);
+    if (const char *e = getenv("LIZARD_FWD_SEGMENTS")) segments = atoi(e) > 0 ? atoi(e) : 0;
+    if (const char *e = getenv("LIZARD_FWD_SPLIT_SHIFT")) split_shift = atoi(e);
+  }
+  static int kernel_code(const char *e) {
+    if (strcmp(e, "split") == 0) return 1;
+    if (strcmp(e, "4wave") == 0) return 2;
+    return 0;
+  }
+};
+Options g_opt;
+
+bool debug_sync() { return g_opt.debug_sync.load(std::memory_order_relaxed) != 0; }
 
 lizard_status finish(hipError_t e, hipStream_t stream) {
   if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(stream);
@@ -59,8 +78,8 @@ size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // Sequence segments are added until there are about 256 workgroups (one per
 // (batch, head, segment) for the whole-head kernel, one per (batch, head, 64-column
-// value block, segment) otherwise); an environment override (LIZARD_FWD_SEGMENTS)
-// exists for tests and tuning.  The segment end states are kept per 64-column
+// value block, segment) otherwise); the option "fwd_segments" overrides the count for tests
+// and tuning.  The segment end states are kept per 64-column
 // value block in either case (the state pass works per block).
 FwdPlan make_plan(int B, int Hq, int Hkv, int L, int d, int W, bool full) {
   FwdPlan p{};
@@ -68,10 +87,7 @@ FwdPlan make_plan(int B, int Hq, int Hkv, int L, int d, int W, bool full) {
   p.ndvb = d / kDV;
   const long base = full ? (long)B * Hq : (long)B * Hkv * p.ndvb;
   long nseg = (kTargetBlocks + base - 1) / base;
-  if (const char *e = getenv("LIZARD_FWD_SEGMENTS")) {
-    const long v = atol(e);
-    if (v >= 1) nseg = v;
-  }
+  if (const int v = g_opt.segments.load(std::memory_order_relaxed)) nseg = v;
   if (full && nseg < (p.nchunks + kMaxFullCps - 1) / kMaxFullCps) nseg = (p.nchunks + kMaxFullCps - 1) / kMaxFullCps;
   if (nseg > p.nchunks) nseg = p.nchunks;
   if (nseg < 1) nseg = 1;
@@ -99,12 +115,11 @@ FwdPlan make_plan(int B, int Hq, int Hkv, int L, int d, int W, bool full) {
 size_t plan_bytes(const FwdPlan &p) { return p.ws_state_bytes + p.ws_decay_bytes; }
 
 // The whole-head kernel serves bf16 at d = 128 with one W_phi for queries and keys
-// (any grouping of query heads) and W <= 129 (LIZARD_FWD_KERNEL=split or 4wave
-// selects the value-block kernels instead, for tests and A/B timing).
+// (any grouping of query heads) and W <= 129 (the option "fwd_kernel" = 1 or 2 selects the
+// value-block kernels instead, for tests and A/B timing).
 bool use_full_kernel(int Hq, int Hkv, int d, int W, lizard_dtype dtype, const void *wq, const void *wk,
                      int64_t w_stride) {
-  const char *kenv = getenv("LIZARD_FWD_KERNEL");
-  if (kenv && (strcmp(kenv, "split") == 0 || strcmp(kenv, "4wave") == 0)) return false;
+  if (g_opt.fwd_kernel.load(std::memory_order_relaxed) != 0) return false;
   (void)Hq;
   (void)Hkv;
   return dtype == LIZARD_BF16 && d == 128 && W <= 2 * kChunk + 1 && wq == wk && w_stride == 0;
@@ -147,6 +162,8 @@ lizard_status fwd_impl(const void *q, const void *k, const void *v, const void *
                 Hkv, d, W, M);
   if (Hq % Hkv != 0) return fail(LIZARD_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
   if (w_phi_head_stride < 0) return fail(LIZARD_ERR_INVALID_ARG, "negative w_phi_head_stride");
+  if (!(std::isfinite(mix) && mix >= 0.f) || !std::isfinite(scale))
+    return fail(LIZARD_ERR_INVALID_ARG, "mix=%g must be finite and >= 0, scale=%g finite", (double)mix, (double)scale);
   if (!supported_d(d, dtype))
     return fail(LIZARD_ERR_UNSUPPORTED, "head dim d=%d not built for %s", d, dtype == LIZARD_BF16 ? "bf16" : "fp32");
   if (M > kMaxMeta) return fail(LIZARD_ERR_UNSUPPORTED, "M=%d meta tokens (at most %d)", M, kMaxMeta);
@@ -203,17 +220,19 @@ lizard_status fwd_impl(const void *q, const void *k, const void *v, const void *
   p.nchunks = plan.nchunks; p.nseg = plan.nseg; p.cps = plan.cps; p.ndvb = plan.ndvb; p.nring = plan.nring;
   p.per_head_q = w_phi_head_stride != 0;
   p.full = full ? 1 : 0;
+  p.force_4wave = g_opt.fwd_kernel.load(std::memory_order_relaxed) == 2 ? 1 : 0;
   p.sss = plan.sss;
   p.hh = hedgehog ? 1 : 0;
   // Two segments on the whole-head path: the second one's workgroups walk the chunks before it
   // themselves (no state pass), and the first segment takes a few chunks more to even out the
   // walk.  Not with a start state or window history (the walk starts from zero at chunk 0).
-  // The shift is estimated in the kernel from the gates (LIZARD_FWD_SPLIT_SHIFT=n fixes it at n
-  // chunks; a negative value turns the split off: state pass instead).
+  // The shift is estimated in the kernel from the gates (the option "fwd_split_shift" = n >= 0
+  // fixes it at n chunks; a negative value turns the split off: state pass instead).
   p.split = 0;
-  const char *shift_env = getenv("LIZARD_FWD_SPLIT_SHIFT");
-  const int shift_fixed = shift_env ? atoi(shift_env) : -1;
-  if (full && plan.nseg == 2 && !(ext && (ext->state_in || history)) && !(shift_env && shift_fixed < 0) &&
+  const int shift_opt = g_opt.split_shift.load(std::memory_order_relaxed);
+  const bool shift_auto = shift_opt == Options::kShiftAuto;
+  const int shift_fixed = shift_auto ? -1 : shift_opt;
+  if (full && plan.nseg == 2 && !(ext && (ext->state_in || history)) && (shift_auto || shift_fixed >= 0) &&
       plan.cps < plan.nchunks && plan.cps <= kMaxFullCps) {
     int smax = plan.cps / 4;
     if (smax > plan.nchunks - 1 - plan.cps) smax = plan.nchunks - 1 - plan.cps;
@@ -261,7 +280,34 @@ const char *lizard_status_string(lizard_status s) {
 
 const char *lizard_last_error(void) { return g_err; }
 
-const char *lizard_version(void) { return "lizard_attn 0.1.0 gfx950"; }
+const char *lizard_version(void) { return "lizard_attn 0.2.0 gfx950"; }
+
+lizard_status lizard_set_option(const char *name, int value) {
+  if (!name) return fail(LIZARD_ERR_INVALID_ARG, "null option name");
+  if (strcmp(name, "debug_sync") == 0) {
+    g_opt.debug_sync = value != 0;
+  } else if (strcmp(name, "fwd_kernel") == 0) {
+    if (value < 0 || value > 2) return fail(LIZARD_ERR_INVALID_ARG, "fwd_kernel=%d (0, 1 or 2)", value);
+    g_opt.fwd_kernel = value;
+  } else if (strcmp(name, "fwd_segments") == 0) {
+    if (value < 0) return fail(LIZARD_ERR_INVALID_ARG, "fwd_segments=%d must be >= 0", value);
+    g_opt.segments = value;
+  } else if (strcmp(name, "fwd_split_shift") == 0) {
+    g_opt.split_shift = value;
+  } else {
+    return fail(LIZARD_ERR_INVALID_ARG, "unknown option '%s'", name);
+  }
+  return LIZARD_OK;
+}
+
+int lizard_get_option(const char *name) {
+  if (!name) return 0;
+  if (strcmp(name, "debug_sync") == 0) return g_opt.debug_sync;
+  if (strcmp(name, "fwd_kernel") == 0) return g_opt.fwd_kernel;
+  if (strcmp(name, "fwd_segments") == 0) return g_opt.segments;
+  if (strcmp(name, "fwd_split_shift") == 0) return g_opt.split_shift;
+  return 0;
+}
 
 size_t lizard_attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int W, lizard_dtype dtype) {
   (void)Hq;
@@ -333,6 +379,8 @@ static lizard_status decode_impl(float *state, void *win_k, void *win_v, int32_t
                 Hkv, d, W, M);
   if (Hq % Hkv != 0) return fail(LIZARD_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
   if (w_phi_head_stride < 0) return fail(LIZARD_ERR_INVALID_ARG, "negative w_phi_head_stride");
+  if (!(std::isfinite(mix) && mix >= 0.f) || !std::isfinite(scale))
+    return fail(LIZARD_ERR_INVALID_ARG, "mix=%g must be finite and >= 0, scale=%g finite", (double)mix, (double)scale);
   if (!supported_d(d, dtype))
     return fail(LIZARD_ERR_UNSUPPORTED, "head dim d=%d not built for %s", d, dtype == LIZARD_BF16 ? "bf16" : "fp32");
   if (M > kMaxMeta) return fail(LIZARD_ERR_UNSUPPORTED, "M=%d meta tokens (at most %d)", M, kMaxMeta);

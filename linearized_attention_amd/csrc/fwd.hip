@@ -835,9 +835,7 @@ static hipError_t launch_fwd_w(const FwdParams &prm, bool shared_w, hipStream_t 
   if (!plan_rings<T, D, DV, WIDE>(p, shared_w)) return hipErrorInvalidConfiguration;
   // The role-split kernel serves one query head per key/value head; grouped query heads
   // (whose per-head work would fall on the query waves alone) run on the 4-wave kernel.
-  const char *kenv = getenv("LIZARD_FWD_KERNEL");  // "4wave": force the 4-wave kernel (tests, A/B timing)
-  const bool force_4wave = kenv && strcmp(kenv, "4wave") == 0;
-  if (!force_4wave && p.G == 1) return launch_fwd_split<T, D, DV, WIDE>(p, stream);
+  if (!p.force_4wave && p.G == 1) return launch_fwd_split<T, D, DV, WIDE>(p, stream);
   return launch_one<T, D, DV, false, WIDE>(p, stream);
 }
 

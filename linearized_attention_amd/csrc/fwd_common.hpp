@@ -16,6 +16,14 @@ constexpr float FAST_SPAN = 60.f; // max |log-decay| across a whole chunk for th
                                   // reference (keys carry e^{+60} at most, queries e^{-60})
 constexpr float SKIP_LOG = 40.f;  // the state pass drops chunks that reach their segment's end
                                   // decayed below e^{-40} in every feature
+// The same cutoff for a feature map whose values are not bounded by one: the Hedgehog map's
+// features lie in [e^{-LOGIT_MAX}, e^{LOGIT_MAX}] under its documented logit bound, so a chunk is
+// dropped only once its largest possible term, decayed, is below e^{-SKIP_LOG} times the smallest
+// possible term of the same feature row: suffix < -(SKIP_LOG + 2 LOGIT_MAX).
+constexpr float HH_LOGIT_MAX = 80.f;
+template <bool HH> __host__ __device__ constexpr float skip_log() {
+  return HH ? SKIP_LOG + 2.f * HH_LOGIT_MAX : SKIP_LOG;
+}
 constexpr int LDS_LIMIT = 160 * 1024;
 constexpr int WIN_BATCH = 8;      // key tiles per online-softmax batch in the window
 constexpr int KT_META = -(1 << 28);  // window tile list: the meta tile

@@ -309,7 +309,7 @@ __device__ __forceinline__ void feature_map_rows(const f32x4 (&z)[NFT], float (&
 
 // Chunks the first of two segments takes beyond the even split at chunk b, so that both end
 // together.  The second segment first walks back from its start until every feature has decayed
-// by e^{-SKIP_LOG}, about n = SKIP_LOG / r chunks for the slowest feature's log decay r per
+// by e^{-skip_log}, about n = skip_log / r chunks for the slowest feature's log decay r per
 // chunk (at most b).  Measured on MI355X, the walk with its set-up costs about 6 + 3.2 n us and
 // a chunk of the main loop 6.5 us, so the first segment takes (6 + 3.2 n) / 13 chunks more (fitted
 // over gates whose walks last 1, 7, 14 and all chunks).  r comes from the
@@ -339,6 +339,7 @@ __device__ __forceinline__ void split_shift_part(const bf16 *LGh, int b, int wv,
     if (tg == 0) part[wv * D + 8 * fg + e] = t;
   }
 }
+template <bool HH>
 __device__ __forceinline__ int split_shift(const float *part, int b, int lane) {
   using namespace full;
   const int nc = b < 4 ? b : 4;
@@ -350,7 +351,7 @@ __device__ __forceinline__ int split_shift(const float *part, int b, int lane) {
     r = fminf(r, -a);
   }
   r = -wave_max_all(-r) / (float)nc;
-  const float n = fminf(SKIP_LOG / fmaxf(r, 1.0e-6f), (float)b);
+  const float n = fminf(skip_log<HH>() / fmaxf(r, 1.0e-6f), (float)b);
   return (int)((6.f + 3.2f * n) / 13.f + 0.5f);
 }
 
@@ -471,7 +472,7 @@ __device__ __forceinline__ bool walk_back(const WalkLds &lds, const bf16 *Kh, co
       if (wt < D) {
         suf += sTot[3 * D + wt];
         sSuf[(par ^ 1) * D + wt] = suf;
-        const bool below = __all(suf < -SKIP_LOG);
+        const bool below = __all(suf < -skip_log<HH>());
         if (lane == 0) sVote[I] = below;
       }
       mild = mine && chunk_is_mild_c<D>(sTot, lane);
@@ -690,7 +691,7 @@ __device__ __forceinline__ void walk_pipe(const PipeLds &lds, const bf16 *Kh, co
       if (wt < D) {  // suffix through chunk c: s of the next chunk back (other buffer's slot)
         suf += sTot[3 * D + wt];
         lds.sSuf[(bj ^ 1) * D + wt] = suf;
-        const bool below = __all(suf < -SKIP_LOG);
+        const bool below = __all(suf < -skip_log<HH>());
         if (lane == 0) lds.sVote[I] = below;
       }
       if (chunk_is_mild_c<D>(sTot, lane)) {
@@ -794,7 +795,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
     float *part = reinterpret_cast<float *>(scr + SC_PART);
     if (p.split_shift < 0) split_shift_part(LGh, p.split, wv, lane, part);
     __syncthreads();
-    const int sh = p.split_shift >= 0 ? p.split_shift : split_shift(part, p.split, lane);
+    const int sh = p.split_shift >= 0 ? p.split_shift : split_shift<HH>(part, p.split, lane);
     bsplit = p.split + min(sh, p.split_max);
   }
   const int c_begin = p.split ? (seg ? bsplit : 0) : seg * p.cps;
@@ -1644,6 +1645,9 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
 // Once the suffix is below -SKIP_LOG in every feature, the chunks before reach the block end
 // decayed by less than e^{-SKIP_LOG} (below 4e-18 of their size, nothing the fp32 state can
 // hold): the walk stops there, and piece 0 sets D = NEG_BIG, dropping the state carried in.
+// With the Hedgehog map (features up to e^{HH_LOGIT_MAX}, not bounded by one) the cutoff is
+// -(SKIP_LOG + 2 HH_LOGIT_MAX), which bounds a dropped term relative to the smallest term any
+// token of the same feature row can add (skip_log).
 // Every piece reads the log gates of all the chunks it walks (the suffix) and the keys and
 // values of its own.  Four waves, each the key side of one sub-chunk, with the arithmetic of
 // the key waves above; 80 KB of LDS, so two workgroups share a CU.  The pieces of a block run

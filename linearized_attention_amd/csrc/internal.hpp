@@ -29,6 +29,7 @@ struct FwdParams {
   int nchunks, nseg, cps, ndvb, nring, kring, ngroups;
   FwdLds lds;
   int per_head_q;
+  int force_4wave;  // value-block path: the 4-wave kernel also for one query head per KV head
   int full;  // whole-head kernel (fwd_full.hip)
   int sss;   // whole-head kernel: state-pass pieces per segment (divides cps)
   int hh;    // whole-head kernel: Hedgehog feature map (W_phi [d][d/2]) instead of the softmax

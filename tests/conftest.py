@@ -22,3 +22,20 @@ def gpu_lib():
     from linearized_attention_amd import api
     api.load()
     return api
+
+
+SHIFT_AUTO = -1000000  # the library's "estimate the split shift" value of fwd_split_shift
+
+
+@pytest.fixture
+def lz_opts(gpu_lib):
+    """Sets library options (lizard_set_option) for one test and restores their values after it."""
+    names = ("fwd_kernel", "fwd_segments", "fwd_split_shift", "debug_sync")
+    saved = {n: gpu_lib.get_option(n) for n in names}
+
+    def set_opt(name, value):
+        gpu_lib.set_option(name, value)
+
+    yield set_opt
+    for n, v in saved.items():
+        gpu_lib.set_option(n, v)

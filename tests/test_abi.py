@@ -57,6 +57,8 @@ def _fwd(lib, fn="lizard_attn_fwd", **kw):
     (dict(stride=-1), 1), (dict(stride=100), 1),
     (dict(d=96), 2), (dict(d=128, dtype=0), 2), (dict(M=17), 2),
     (dict(tk=None), 1),
+    (dict(mix=-0.25), 1), (dict(mix=float("nan")), 1), (dict(mix=float("inf")), 1),
+    (dict(scale=float("nan")), 1), (dict(mix=-0.25, B=0), 1),   # checked before the empty case
 ])
 def test_fwd_validation_codes(kw, code):
     lib = api.load()
@@ -142,6 +144,7 @@ def _dec(lib, fn="lizard_attn_decode", **kw):
     (dict(state=None), 1), (dict(pos=None), 1), (dict(Hq=3), 1), (dict(W=0), 1), (dict(N=-1), 1),
     (dict(d=32), 2), (dict(W=257), 2), (dict(M=20), 2), (dict(q=8), 1), (dict(pos=18), 1),
     (dict(ws=None), 3), (dict(wsb=100), 3), (dict(ws=24), 1),
+    (dict(mix=-1.0), 1), (dict(mix=float("nan")), 1), (dict(scale=float("inf")), 1),
 ])
 def test_decode_validation_codes(kw, code):
     lib = api.load()
@@ -210,3 +213,49 @@ def test_fwd_ext_workspace_bytes():
     assert ext >= plain + 2 * hist
     assert _fwd_ext(lib, B=B, Hq=Hkv, Hkv=Hkv, L=L, W=W, rkin=32, rvin=32, pos=64, ws=4096, wsb=ext - 1) == 3
     assert _fwd_ext(lib, L=0) == 0          # empty problem
+
+
+def test_mix_range_accepts_zero_and_above_one():
+    """mix = 0 (window only) and mix > 1 (negative window weight) pass validation: an empty
+    problem returns OK without launching anything."""
+    lib = api.load()
+    assert _fwd(lib, mix=0.0, B=0) == 0
+    assert _fwd(lib, mix=1.5, B=0) == 0
+    assert _dec(lib, mix=0.0, N=0) == 0
+
+
+def test_options_set_get_and_reject():
+    lib = api.load()
+    saved = {n: lib.lizard_get_option(n.encode()) for n in ("fwd_kernel", "fwd_segments", "fwd_split_shift")}
+    try:
+        assert lib.lizard_set_option(b"fwd_segments", 3) == 0
+        assert lib.lizard_get_option(b"fwd_segments") == 3
+        assert lib.lizard_set_option(b"fwd_kernel", 2) == 0
+        assert lib.lizard_get_option(b"fwd_kernel") == 2
+        assert lib.lizard_set_option(b"fwd_kernel", 3) == 1
+        assert lib.lizard_set_option(b"fwd_segments", -1) == 1
+        assert lib.lizard_set_option(b"no_such_option", 1) == 1
+        assert lib.lizard_set_option(None, 1) == 1
+        assert lib.lizard_get_option(b"no_such_option") == 0
+    finally:
+        for n, v in saved.items():
+            assert lib.lizard_set_option(n.encode(), v) == 0
+
+
+def test_segment_option_changes_the_plan():
+    """A 4 x 32 x 4096 forward is planned in two segments on the whole-head path, whose state
+    pass (when the second segment does not start itself) needs workspace; one forced segment
+    needs none.  Both two and three segments keep 256 state-pass pieces of one 128 x 128 fp32
+    state and 128 log-gate sums each."""
+    lib = api.load()
+    saved = lib.lizard_get_option(b"fwd_segments")
+    try:
+        lib.lizard_set_option(b"fwd_segments", 0)
+        base = lib.lizard_attn_fwd_workspace_bytes(4, 32, 32, 4096, 128, 64, 1)
+        lib.lizard_set_option(b"fwd_segments", 1)
+        assert lib.lizard_attn_fwd_workspace_bytes(4, 32, 32, 4096, 128, 64, 1) == 0
+        lib.lizard_set_option(b"fwd_segments", 3)
+        more = lib.lizard_attn_fwd_workspace_bytes(4, 32, 32, 4096, 128, 64, 1)
+        assert base == more == 256 * (128 * 128 * 4 + 128 * 4)
+    finally:
+        lib.lizard_set_option(b"fwd_segments", saved)

@@ -14,6 +14,7 @@ import torch
 import oracle
 from linearized_attention_amd import api
 from linearized_attention_amd.synthetic import make_fwd_inputs, workload_fwd_inputs
+from tests.conftest import SHIFT_AUTO
 
 pytestmark = pytest.mark.gpu
 
@@ -126,19 +127,19 @@ def test_fwd_mixed_chunk_references(gpu_lib, dtype, d):
 
 @pytest.mark.parametrize("label", ["bf16 d128 ragged L200", "bf16 gqa 4:2 shared W", "fp32 uniform gate -8 (mixed safe/exact diag)",
                                    "fp32 W66 (3-chunk ring)"])
-def test_fwd_four_wave_kernel(gpu_lib, monkeypatch, label):
+def test_fwd_four_wave_kernel(gpu_lib, lz_opts, label):
     """The 4-wave kernel (used for grouped heads and the segment state pass) on single-head
     cases as well."""
-    monkeypatch.setenv("LIZARD_FWD_KERNEL", "4wave")
+    lz_opts("fwd_kernel", 2)
     kw, dtype = {s[0]: (s[1], s[2]) for s in SMALL}[label]
     inp = make_fwd_inputs(dtype=dtype, seed=zlib.crc32(label.encode()) % 10000, **kw)
     check_case(label + " [4-wave]", inp, dtype)
 
 
 @pytest.mark.parametrize("nseg", [2, 3, 5])
-def test_fwd_sequence_segments(gpu_lib, monkeypatch, nseg):
+def test_fwd_sequence_segments(gpu_lib, lz_opts, nseg):
     """Segments joined through the workspace states give the same answer."""
-    monkeypatch.setenv("LIZARD_FWD_SEGMENTS", str(nseg))
+    lz_opts("fwd_segments", nseg)
     inp = make_fwd_inputs(B=1, Hq=2, Hkv=2, L=330, d=64, W=70, M=4, dtype="f32", seed=31,
                           gate="uniform:-1")
     check_case(f"fp32 {nseg} segments", inp, "f32")
@@ -147,12 +148,12 @@ def test_fwd_sequence_segments(gpu_lib, monkeypatch, nseg):
 
 
 @pytest.mark.parametrize("nseg", [1, 2, 3, 5])
-def test_fwd_whole_head_segments(gpu_lib, monkeypatch, nseg):
+def test_fwd_whole_head_segments(gpu_lib, lz_opts, nseg):
     """The whole-head kernel (bf16, d = 128, one W_phi for queries and keys) over
     sequence segments joined through its state pass: a gate that mixes both decay
     references with a ragged tail, and gamma = 0 (exact diagonal blocks from the fixup
     kernel) across segment boundaries."""
-    monkeypatch.setenv("LIZARD_FWD_SEGMENTS", str(nseg))
+    lz_opts("fwd_segments", nseg)
     inp = make_fwd_inputs(B=1, Hq=2, Hkv=2, L=650, d=128, W=65, M=16, dtype="bf16", seed=90 + nseg,
                           gate="uniform:-1.6")
     check_case(f"bf16 whole-head {nseg} segments, mixed references", inp, "bf16")
@@ -171,37 +172,37 @@ WIDE = [
 
 
 @pytest.mark.parametrize("label,kw,nseg", WIDE, ids=[c[0] for c in WIDE])
-def test_fwd_whole_head_wide_window(gpu_lib, monkeypatch, label, kw, nseg):
+def test_fwd_whole_head_wide_window(gpu_lib, lz_opts, label, kw, nseg):
     """The whole-head kernel with windows of 66..129 keys: the window reaches into the chunk
     two back (computed one chunk early and carried), with segments and grouped heads."""
-    monkeypatch.setenv("LIZARD_FWD_SEGMENTS", str(nseg))
+    lz_opts("fwd_segments", nseg)
     inp = make_fwd_inputs(dtype="bf16", seed=zlib.crc32(label.encode()) % 10000, **kw)
     check_case(f"bf16 whole-head {label}", inp, "bf16")
 
 
 @pytest.mark.parametrize("gate", ["one", "const:-0.1", "const:-0.5", "logsigmoid"])
-def test_fwd_whole_head_state_pass_drops_decayed_chunks(gpu_lib, monkeypatch, gate):
+def test_fwd_whole_head_state_pass_drops_decayed_chunks(gpu_lib, lz_opts, gate):
     """The state pass leaves out the chunks of a segment that reach its end decayed below
     e^-40 in every feature (with -0.1 per token: all but the last 7 of 13 chunks; -0.5: the
     last 2), and splits the rest over its pieces; gamma = 1 keeps everything."""
-    monkeypatch.setenv("LIZARD_FWD_SEGMENTS", "2")
-    monkeypatch.setenv("LIZARD_FWD_SPLIT_SHIFT", "-1")  # the state pass, not the self-started split
+    lz_opts("fwd_segments", 2)
+    lz_opts("fwd_split_shift", -1)  # the state pass, not the self-started split
     inp = make_fwd_inputs(B=2, Hq=2, Hkv=2, L=1600, d=128, W=64, M=4, dtype="bf16",
                           seed=zlib.crc32(gate.encode()) % 10000, gate=gate)
     check_case(f"bf16 whole-head 2 segments, gate {gate}", inp, "bf16")
 
 
 @pytest.mark.parametrize("shift", [None, "-1", "0", "2", "100"])
-def test_fwd_whole_head_two_segment_split(gpu_lib, monkeypatch, shift):
+def test_fwd_whole_head_two_segment_split(gpu_lib, lz_opts, shift):
     """Two segments on the whole-head path: the second one's workgroups walk the chunks before
     its start themselves (no state pass), and the first takes `shift` chunks beyond the even
     split (None: estimated from the gates in the kernel; 100 is capped at a quarter segment;
     -1: the state pass instead).  Gates with long, short and no decay, a ragged tail, GQA."""
-    monkeypatch.setenv("LIZARD_FWD_SEGMENTS", "2")
+    lz_opts("fwd_segments", 2)
     if shift is None:
-        monkeypatch.delenv("LIZARD_FWD_SPLIT_SHIFT", raising=False)
+        lz_opts("fwd_split_shift", SHIFT_AUTO)
     else:
-        monkeypatch.setenv("LIZARD_FWD_SPLIT_SHIFT", shift)
+        lz_opts("fwd_split_shift", int(shift))
     for gate, kw in (("logsigmoid", dict(B=1, Hq=4, Hkv=2, L=1650)), ("uniform:-1.6", dict(B=2, Hq=1, Hkv=1, L=900)),
                      ("one", dict(B=1, Hq=2, Hkv=2, L=1000))):
         inp = make_fwd_inputs(d=128, W=64, M=4, dtype="bf16", seed=zlib.crc32(f"{gate}{shift}".encode()) % 10000,
@@ -210,21 +211,21 @@ def test_fwd_whole_head_two_segment_split(gpu_lib, monkeypatch, shift):
 
 
 @pytest.mark.parametrize("L", [65, 100, 129, 190])
-def test_fwd_whole_head_two_segment_split_short(gpu_lib, monkeypatch, L):
+def test_fwd_whole_head_two_segment_split_short(gpu_lib, lz_opts, L):
     """Two self-started segments on 2-3 chunks: a one-chunk walk, a ragged last chunk, a last
     segment of one token (L = 129), and no room for a shift."""
-    monkeypatch.setenv("LIZARD_FWD_SEGMENTS", "2")
-    monkeypatch.delenv("LIZARD_FWD_SPLIT_SHIFT", raising=False)
+    lz_opts("fwd_segments", 2)
+    lz_opts("fwd_split_shift", SHIFT_AUTO)
     for gate in ("logsigmoid", "one"):
         inp = make_fwd_inputs(B=2, Hq=2, Hkv=1, L=L, d=128, W=64, M=4, dtype="bf16", seed=L, gate=gate)
         check_case(f"bf16 whole-head 2 segments, L={L}, gate {gate}", inp, "bf16")
 
 
 @pytest.mark.parametrize("label", ["bf16 d128 ragged L200", "bf16 gamma=0 (exact diag)", "bf16 gamma=1"])
-def test_fwd_value_block_kernel(gpu_lib, monkeypatch, label):
+def test_fwd_value_block_kernel(gpu_lib, lz_opts, label):
     """The value-block (role-split) kernel on cases the whole-head kernel would otherwise take
     (it still serves separate or per-head W_phi and grouped heads)."""
-    monkeypatch.setenv("LIZARD_FWD_KERNEL", "split")
+    lz_opts("fwd_kernel", 1)
     kw, dtype = {s[0]: (s[1], s[2]) for s in SMALL}[label]
     inp = make_fwd_inputs(dtype=dtype, seed=zlib.crc32(label.encode()) % 10000, **kw)
     check_case(label + " [value blocks]", inp, dtype)

@@ -19,6 +19,7 @@ import torch
 import oracle
 from linearized_attention_amd import api
 from linearized_attention_amd.synthetic import make_decode_inputs, make_fwd_inputs
+from tests.conftest import SHIFT_AUTO
 
 pytestmark = pytest.mark.gpu
 TOL = {"f32": 1e-4, "bf16": 2e-2}
@@ -165,19 +166,19 @@ def test_prefill_then_decode(gpu_lib):
     assert pos.cpu().tolist() == [Lp + n] * B
 
 
-def test_ext_with_segments(gpu_lib, monkeypatch):
+def test_ext_with_segments(gpu_lib, lz_opts):
     """Sequence segments of the continuation call combine with the imported state."""
-    monkeypatch.setenv("LIZARD_FWD_SEGMENTS", "3")
+    lz_opts("fwd_segments", 3)
     test_chunked_prefill_matches_one_forward(gpu_lib, "fp32 3 segments", dict(B=1, Hq=2, Hkv=2, L=400, d=64,
                                                                                 W=64, M=4), 100, "f32")
 
 
 @pytest.mark.parametrize("nseg", [2, 3])
-def test_ext_whole_head_with_segments(gpu_lib, monkeypatch, nseg):
+def test_ext_whole_head_with_segments(gpu_lib, lz_opts, nseg):
     """The whole-head path in a continuation: the first call (no state in, no history: with two
     segments its second one starts itself) exports state and ring, the second imports them
     (the state pass then, since the walk starts from zero)."""
-    monkeypatch.setenv("LIZARD_FWD_SEGMENTS", str(nseg))
-    monkeypatch.delenv("LIZARD_FWD_SPLIT_SHIFT", raising=False)
+    lz_opts("fwd_segments", nseg)
+    lz_opts("fwd_split_shift", SHIFT_AUTO)
     test_chunked_prefill_matches_one_forward(gpu_lib, f"bf16 whole-head {nseg} segments",
                                              dict(B=2, Hq=2, Hkv=1, L=900, d=128, W=64, M=4), 600, "bf16")

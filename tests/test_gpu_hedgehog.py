@@ -76,9 +76,40 @@ CASES = [
 
 
 @pytest.mark.parametrize("label,kw,nseg", CASES, ids=[c[0] for c in CASES])
-def test_fwd_hedgehog_matches_oracle(gpu_lib, monkeypatch, label, kw, nseg):
-    monkeypatch.setenv("LIZARD_FWD_SEGMENTS", str(nseg))
+def test_fwd_hedgehog_matches_oracle(gpu_lib, lz_opts, label, kw, nseg):
+    lz_opts("fwd_segments", nseg)
     check_case(label, hh_inputs(label, **kw))
+
+
+@pytest.mark.parametrize("nseg,big_chunk,last", [(2, 7, 640), (3, 9, 768)])
+def test_fwd_hedgehog_large_features_beyond_the_decay_cutoff(gpu_lib, lz_opts, nseg, big_chunk, last):
+    """The unnormalised Hedgehog features can reach e^60 (logits up to the documented bound of
+    about 80).  A chunk whose keys carry such features and that reaches the next segment decayed
+    by about e^-45 still dominates its outputs (e^15 against O(e^3) terms), so the segment walks
+    must not drop it at the softmax map's cutoff of e^-40.  Gate -0.35 per token (22.4 per chunk),
+    16 chunks; the last four keys of chunk `big_chunk` point along one column of W_phi so that
+    one logit is 60.  With two segments the second starts at chunk 10 (split shift 2) and walks
+    back; with three the state pass walks the middle block.  The global branch (mix = 1) of the
+    last segment's rows is compared with the oracle: without those chunks it would be off by
+    about 100% (checked on the CPU with the oracle when the case was written)."""
+    lz_opts("fwd_segments", nseg)
+    inp = make_fwd_inputs(B=1, Hq=1, Hkv=1, L=1024, d=128, W=64, M=4, dtype="bf16", seed=77 + nseg,
+                          gate="const:-0.35", phi_cols=64)
+    w = inp.w_phi_k.double().numpy()
+    col = w[:, int(np.argmax((w ** 2).sum(0)))]
+    k = inp.k.double().numpy().copy()
+    t1 = (big_chunk + 1) * 64
+    k[0, 0, t1 - 4:t1] = col * (60.0 / (col @ col))
+    inp.k = torch.tensor(k).to(torch.bfloat16)
+    _say(f"[hedgehog fwd] large features beyond the cutoff, {nseg} segments, chunk {big_chunk}")
+    _, yg, _ = oracle.lizard_fwd(*inp.tensors(), W=inp.W, M=inp.M, mix=1.0, scale=inp.scale,
+                                 return_branches=True, feature_map="hedgehog")
+    got = gpu_fwd_hh(inp.to("cuda"), inp, 1.0).double().cpu().numpy()
+    assert np.isfinite(got).all()
+    e = float(rel_l2(got[:, :, last:], yg[:, :, last:], axes=(-2, -1)).max())
+    e_all = float(rel_l2(got, yg, axes=(-2, -1)).max())
+    _say(f"      rel-L2 of the last segment's rows {e:.3e}, all rows {e_all:.3e}")
+    assert e <= TOL and e_all <= TOL
 
 
 def test_fwd_hedgehog_full_size_sampled_heads(gpu_lib):
