@@ -236,6 +236,34 @@ lizard_status lizard_attn_decode_hedgehog(float *state, void *win_k,
                                           void *workspace,
                                           size_t workspace_bytes, void *stream);
 
+/*
+ * lizard_attn_decode without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Arguments and results as lizard_attn_decode (softmax
+ * feature map).  The step's scratch (4 * (N*Hkv*(1 + Hq/Hkv)*d + N) bytes: the
+ * feature maps and one counter per sequence) lives in a static device array of
+ * 32 MiB that each GPU the library runs on holds until the process ends; the
+ * call allocates nothing.  Shapes that need more scratch return
+ * LIZARD_ERR_UNSUPPORTED (e.g. N = 256, Hq = Hkv = 32, d = 128 needs 8.4 MB;
+ * N*Hkv*(1 + Hq/Hkv)*d must stay below about 8.3 million).  Every call on one
+ * GPU uses that GPU's one array: calls that overlap on a GPU (different
+ * streams, or host threads) race and give wrong results; calls in order on one
+ * stream are safe.  The scratch needs no clearing between calls (the step's
+ * first kernel resets its counters).
+ */
+lizard_status lizard_attn_decode_noalloc(float *state, void *win_k, void *win_v,
+                                         int32_t *pos, const void *q,
+                                         const void *k, const void *v,
+                                         const void *log_gamma,
+                                         const void *w_phi_q,
+                                         const void *w_phi_k,
+                                         int64_t w_phi_head_stride,
+                                         const void *t_k, const void *t_v,
+                                         void *out, int N, int Hq, int Hkv,
+                                         int d, int W, int M, float mix,
+                                         float scale, lizard_dtype dtype,
+                                         void *stream);
+
 /* Static text for a status code. */
 const char *lizard_status_string(lizard_status s);
 

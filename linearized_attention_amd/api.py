@@ -27,7 +27,7 @@ EXPORTED = ("lizard_attn_fwd", "lizard_attn_fwd_workspace_bytes", "lizard_attn_f
             "lizard_attn_fwd_ext", "lizard_attn_fwd_ext_workspace_bytes", "lizard_attn_decode",
             "lizard_attn_decode_hedgehog", "lizard_attn_decode_workspace_bytes",
             "lizard_status_string", "lizard_last_error", "lizard_version", "lizard_set_option",
-            "lizard_get_option")
+            "lizard_get_option", "lizard_attn_decode_noalloc")
 
 _lock = threading.Lock()
 _lib = None
@@ -60,6 +60,9 @@ def _declare(lib):
     lib.lizard_attn_fwd_hedgehog.restype = i32
     lib.lizard_attn_decode_hedgehog.argtypes = lib.lizard_attn_decode.argtypes
     lib.lizard_attn_decode_hedgehog.restype = i32
+    lib.lizard_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp,
+                                               i32, i32, i32, i32, i32, i32, f32, f32, i32, vp]
+    lib.lizard_attn_decode_noalloc.restype = i32
     lib.lizard_attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.lizard_attn_decode_workspace_bytes.restype = sz
     lib.lizard_status_string.argtypes = [i32]
@@ -300,6 +303,16 @@ def lizard_attn_decode(state, win_k, win_v, pos, q, k, v, log_gamma, w_phi_q, w_
                    workspace=workspace, stream=stream, cols=q.shape[-1])
 
 
+def lizard_attn_decode_noalloc(state, win_k, win_v, pos, q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v,
+                               *, M: int, mix: float = 0.5, scale: float | None = None, out=None,
+                               stream=None):
+    """lizard_attn_decode without a workspace: the library's static per-GPU scratch serves the
+    step (calls that overlap on one GPU race).  Arguments and results as lizard_attn_decode."""
+    return _decode(load().lizard_attn_decode_noalloc, state, win_k, win_v, pos, q, k, v, log_gamma,
+                   w_phi_q, w_phi_k, t_k, t_v, M=M, mix=mix, scale=scale, out=out, workspace=None,
+                   stream=stream, cols=q.shape[-1], noalloc=True)
+
+
 def lizard_attn_decode_hedgehog(state, win_k, win_v, pos, q, k, v, log_gamma, w_phi_q, w_phi_k,
                                 t_k, t_v, *, M: int, mix: float = 0.5, scale: float | None = None,
                                 out=None, workspace=None, stream=None):
@@ -311,7 +324,7 @@ def lizard_attn_decode_hedgehog(state, win_k, win_v, pos, q, k, v, log_gamma, w_
 
 
 def _decode(fn, state, win_k, win_v, pos, q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v, *, M,
-            mix, scale, out, workspace, stream, cols):
+            mix, scale, out, workspace, stream, cols, noalloc=False):
     dt = q.dtype
     if dt not in _DTYPES:
         raise ValueError(f"unsupported dtype {dt}")
@@ -339,15 +352,17 @@ def _decode(fn, state, win_k, win_v, pos, q, k, v, log_gamma, w_phi_q, w_phi_k, 
     if scale is None:
         scale = d ** -0.5
     out = _out(out, q)
+    args = [_ptr(state), _ptr(win_k), _ptr(win_v), _ptr(pos), _ptr(q), _ptr(k), _ptr(v),
+            _ptr(log_gamma), _ptr(w_phi_q), _ptr(w_phi_k), wstride,
+            _ptr(t_k) if M > 0 else None, _ptr(t_v) if M > 0 else None, _ptr(out),
+            N, Hq, Hkv, d, W, M, float(mix), float(scale), _DTYPES[dt]]
+    if noalloc:
+        _check(fn(*args, _stream(stream)))
+        return out
     need = lizard_attn_decode_workspace_bytes(N, Hq, Hkv, d, dt)
     workspace = _workspace(workspace, max(need, 16), q.device)
     wbytes = workspace.numel() * workspace.element_size()
-    _check(fn(
-        _ptr(state), _ptr(win_k), _ptr(win_v), _ptr(pos), _ptr(q), _ptr(k), _ptr(v),
-        _ptr(log_gamma), _ptr(w_phi_q), _ptr(w_phi_k), wstride,
-        _ptr(t_k) if M > 0 else None, _ptr(t_v) if M > 0 else None, _ptr(out),
-        N, Hq, Hkv, d, W, M, float(mix), float(scale), _DTYPES[dt], _ptr(workspace), wbytes,
-        _stream(stream)))
+    _check(fn(*args, _ptr(workspace), wbytes, _stream(stream)))
     return out
 
 

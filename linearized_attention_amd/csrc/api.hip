@@ -9,6 +9,7 @@
 #include <cstring>
 #include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "../../include/lizard_attn.h"
 #include "internal.hpp"
@@ -367,11 +368,50 @@ size_t lizard_attn_decode_workspace_bytes(int N, int Hq, int Hkv, int d, lizard_
   return lz::decode_workspace_bytes(N, Hq, Hkv, d);
 }
 
+// Scratch of lizard_attn_decode_noalloc: the step's feature maps and per-sequence counters (what
+// lizard_attn_decode keeps in the caller's workspace), in a static device array.  Every GPU the
+// library runs on holds its own copy at its own address until the process ends; host code
+// reaches it only through that address (the array's name is a host-side stand-in).
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the scratch on the stream's GPU, looked up once per device
+// (hipGetSymbolAddress with that device current).
+lizard_status scratch_for_stream(hipStream_t st, void **out) {
+  int dev = -1;
+  hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(LIZARD_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(LIZARD_ERR_UNSUPPORTED, "device %d (at most %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return fail(LIZARD_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(LIZARD_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess || !ptr)
+      return fail(LIZARD_ERR_HIP, "scratch address on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return LIZARD_OK;
+}
+
 static lizard_status decode_impl(float *state, void *win_k, void *win_v, int32_t *pos, const void *q, const void *k,
                                  const void *v, const void *log_gamma, const void *w_phi_q, const void *w_phi_k,
                                  int64_t w_phi_head_stride, const void *t_k, const void *t_v, void *out, int N, int Hq,
                                  int Hkv, int d, int W, int M, float mix, float scale, lizard_dtype dtype,
-                                 void *workspace, size_t workspace_bytes, void *stream, bool hedgehog) {
+                                 void *workspace, size_t workspace_bytes, void *stream, bool hedgehog,
+                                 bool static_scratch = false) {
   if (dtype != LIZARD_F32 && dtype != LIZARD_BF16) return fail(LIZARD_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
   if (N < 0) return fail(LIZARD_ERR_INVALID_ARG, "N=%d must be >= 0", N);
   if (Hq < 1 || Hkv < 1 || d < 1 || W < 1 || M < 0)
@@ -399,6 +439,16 @@ static lizard_status decode_impl(float *state, void *win_k, void *win_v, int32_t
     if (ptr && !aligned16(ptr)) return fail(LIZARD_ERR_INVALID_ARG, "tensor pointer %p not 16-byte aligned", ptr);
   if (reinterpret_cast<uintptr_t>(pos) & 3u) return fail(LIZARD_ERR_INVALID_ARG, "pos not 4-byte aligned");
   const size_t need = lz::decode_workspace_bytes(N, Hq, Hkv, d);
+  if (static_scratch) {
+    if (need > kDecodeScratchBytes)
+      return fail(LIZARD_ERR_UNSUPPORTED,
+                  "lizard_attn_decode_noalloc: N=%d, Hkv=%d, Hq/Hkv=%d, d=%d need %zu bytes of scratch; the static "
+                  "scratch holds %zu (use lizard_attn_decode with a workspace)", N, Hkv, Hq / Hkv, d, need,
+                  kDecodeScratchBytes);
+    const lizard_status s = scratch_for_stream(static_cast<hipStream_t>(stream), &workspace);
+    if (s != LIZARD_OK) return s;
+    workspace_bytes = kDecodeScratchBytes;
+  }
   if (!workspace || workspace_bytes < need)
     return fail(LIZARD_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -433,6 +483,15 @@ lizard_status lizard_attn_decode_hedgehog(float *state, void *win_k, void *win_v
                                           size_t workspace_bytes, void *stream) {
   return decode_impl(state, win_k, win_v, pos, q, k, v, log_gamma, w_phi_q, w_phi_k, w_phi_head_stride, t_k, t_v,
                      out, N, Hq, Hkv, d, W, M, mix, scale, dtype, workspace, workspace_bytes, stream, true);
+}
+
+lizard_status lizard_attn_decode_noalloc(float *state, void *win_k, void *win_v, int32_t *pos, const void *q,
+                                         const void *k, const void *v, const void *log_gamma, const void *w_phi_q,
+                                         const void *w_phi_k, int64_t w_phi_head_stride, const void *t_k,
+                                         const void *t_v, void *out, int N, int Hq, int Hkv, int d, int W, int M,
+                                         float mix, float scale, lizard_dtype dtype, void *stream) {
+  return decode_impl(state, win_k, win_v, pos, q, k, v, log_gamma, w_phi_q, w_phi_k, w_phi_head_stride, t_k, t_v,
+                     out, N, Hq, Hkv, d, W, M, mix, scale, dtype, nullptr, 0, stream, false, true);
 }
 
 }  // extern "C"

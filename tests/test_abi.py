@@ -259,3 +259,31 @@ def test_segment_option_changes_the_plan():
         assert base == more == 256 * (128 * 128 * 4 + 128 * 4)
     finally:
         lib.lizard_set_option(b"fwd_segments", saved)
+
+
+def _dec_noalloc(lib, **kw):
+    a = dict(state=16, wk=16, wv=16, pos=16, q=16, k=16, v=16, lg=16, wq=16, wkm=16, stride=0, tk=16,
+             tv=16, out=16, N=4, Hq=2, Hkv=2, d=128, W=64, M=4, mix=0.5, scale=0.1, dtype=1, stream=None)
+    a.update(kw)
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.lizard_attn_decode_noalloc(P(a["state"]), P(a["wk"]), P(a["wv"]), P(a["pos"]), P(a["q"]),
+                                          P(a["k"]), P(a["v"]), P(a["lg"]), P(a["wq"]), P(a["wkm"]),
+                                          a["stride"], P(a["tk"]), P(a["tv"]), P(a["out"]), a["N"], a["Hq"],
+                                          a["Hkv"], a["d"], a["W"], a["M"], a["mix"], a["scale"], a["dtype"],
+                                          P(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(state=None), 1), (dict(Hq=3), 1), (dict(d=32), 2), (dict(W=257), 2), (dict(mix=-1.0), 1),
+    (dict(N=4100, Hq=8, Hkv=8), 2),          # 4100 * 8 * 2 * 128 floats exceed the 32 MiB scratch
+    (dict(N=32641, Hq=1, Hkv=1, d=128), 2),  # 4 * 32641 * (2 * 128 + 1) bytes: just over 32 MiB
+])
+def test_decode_noalloc_validation_codes(kw, code):
+    """Host-side checks of the workspace-free decode step, all before any HIP call."""
+    lib = api.load()
+    assert _dec_noalloc(lib, **kw) == code
+    assert lib.lizard_last_error()
+
+
+def test_decode_noalloc_empty_is_ok():
+    assert _dec_noalloc(api.load(), N=0) == 0
