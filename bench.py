@@ -13,7 +13,7 @@ CLOCK_WARMUP_MS of back-to-back forward calls have run (the GPU's clocks take
 some 50-100 ms of steady work to settle); the line states the warm-up actually
 run.  Then K calls are timed back to back, bracketed by two synchronisations
 (`ms_per_step`, `value`).  The roofline figures come from a second pass of K
-calls, each preceded by a 512 MB write that flushes the 256 MB MALL, timed one
+calls, each preceded by a 512 MB read that flushes the 256 MB MALL, timed one
 by one with HIP events on the launch stream: the median and the mean are
 reported, `achieved` uses the median.
 
@@ -48,7 +48,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_full_workload1.json")
 COUNTER_FILE = os.path.join(ROOT, "profiles", "counters_fwd_full_workload{}.json")
 CLOCK_WARMUP_MS = 400.0        # minimum of steady forward calls before the timed region
-FLUSH_BYTES = 512 << 20        # written before each flushed launch (MALL is 256 MB)
+FLUSH_BYTES = 512 << 20        # read before each flushed launch (MALL is 256 MB)
 KERNEL_SOURCES = ["linearized_attention_amd/csrc/fwd_full.hip", "linearized_attention_amd/csrc/fwd_common.hpp",
                   "linearized_attention_amd/csrc/common.hpp", "linearized_attention_amd/csrc/api.hip"]
 # The forward call on this workload launches one whole-head kernel (two segments per head, the
@@ -117,13 +117,15 @@ def clock_warmup(fn, calls: int, min_ms: float = CLOCK_WARMUP_MS):
 
 
 def time_launches_flushed(fn, steps: int, flush: torch.Tensor):
-    """Per-launch HIP-event durations of `steps` calls of fn, each after a write of the whole
-    flush buffer (out of the timed interval) so that no input is left in the MALL."""
+    """Per-launch HIP-event durations of `steps` calls of fn, each after a read of the whole
+    flush buffer (out of the timed interval) so that no input is left in the MALL.  A read, not
+    a write: a written buffer leaves dirty lines whose write-back would fall into the timed
+    launch."""
     st = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
-    for i, (a, b) in enumerate(evs):
-        flush.fill_(i & 0xFF)
+    for a, b in evs:
+        flush.sum()  # fp32 reduction: reads the buffer, writes one value
         a.record(st)
         fn()
         b.record(st)
@@ -155,7 +157,8 @@ def time_launches(fn, steps: int):
     return t_start.elapsed_time(t_end), per
 
 
-def bench_forward(steps: int, warmup: int, idx: int = 1):
+def bench_forward(steps: int, warmup: int, idx: int = 1, min_warm_ms: float = CLOCK_WARMUP_MS,
+                  flushed: bool = True):
     c = WORKLOADS[idx]
     log("[bench] generating forward workload:", WORKLOAD_NAMES[idx])
     inp = workload_fwd_inputs(idx)
@@ -168,12 +171,14 @@ def bench_forward(steps: int, warmup: int, idx: int = 1):
         api.lizard_attn_fwd(g.q, g.k, g.v, g.log_gamma, g.w_phi_q, g.w_phi_k, g.t_k, g.t_v, W=inp.W,
                             M=inp.M, mix=inp.mix, scale=inp.scale, out=out, workspace=ws)
 
-    wcalls, wms = clock_warmup(step, warmup)
+    wcalls, wms = clock_warmup(step, warmup, min_warm_ms)
     log(f"[bench] forward: {wcalls} warm-up calls in {wms:.0f} ms, timing {steps} steps")
     total_ms, per = time_launches(step, steps)
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
-    per_flushed = time_launches_flushed(step, steps, flush)
-    del flush
+    per_flushed = None
+    if flushed:
+        flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        per_flushed = time_launches_flushed(step, steps, flush)
+        del flush
     return c, inp, total_ms, per, per_flushed, (wcalls, wms)
 
 
@@ -258,8 +263,9 @@ def cpu_baseline():
                       f"{dt:.2f} s wall"}
 
 
-def _counter_means(path: str):
-    """Per-dispatch mean of each (kernel, counter) in a rocprofv3 counter_collection.csv."""
+def _counter_dispatches(path: str):
+    """Per-dispatch values of each (kernel, counter) in a rocprofv3 counter_collection.csv
+    (rows of one dispatch and counter summed over their dimensions)."""
     import csv
     per = {}
     with open(path, newline="") as f:
@@ -267,7 +273,21 @@ def _counter_means(path: str):
             key = (row["Kernel_Name"], row["Counter_Name"])
             d = per.setdefault(key, {})
             d[row["Dispatch_Id"]] = d.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
-    return {k: sum(v.values()) / len(v) for k, v in per.items()}
+    return per
+
+
+def _counter_means(path: str):
+    """Per-dispatch mean of each (kernel, counter) in a rocprofv3 counter_collection.csv."""
+    return {k: sum(v.values()) / len(v) for k, v in _counter_dispatches(path).items()}
+
+
+def _copy_value(path: str, counter: str):
+    """The counter of the largest copyBuffer dispatch: the plain copy of COPY_BYTES (input
+    uploads are copies too, and much smaller)."""
+    vals = [max(v.values()) for (k, c), v in _counter_dispatches(path).items() if c == counter and "copyBuffer" in k]
+    if not vals:
+        raise SystemExit(f"no copyBuffer dispatch for {counter}")
+    return max(vals)
 
 
 def _pick(means, counter, symbol, exclude=()):
@@ -284,7 +304,7 @@ def write_traffic(fetch_csv: str, write_csv: str, idx: int):
     same run."""
     fetch, write = _counter_means(fetch_csv), _counter_means(write_csv)
     kf, kw = _pick(fetch, "FETCH_SIZE", FWD_KERNEL_SYMBOL), _pick(write, "WRITE_SIZE", FWD_KERNEL_SYMBOL)
-    cf, cw = _pick(fetch, "FETCH_SIZE", "copyBuffer"), _pick(write, "WRITE_SIZE", "copyBuffer")
+    cf, cw = _copy_value(fetch_csv, "FETCH_SIZE"), _copy_value(write_csv, "WRITE_SIZE")
     sf, sw = COPY_BYTES / (cf * 1024.0), COPY_BYTES / (cw * 1024.0)
     c = WORKLOADS[idx]
     nbytes, _ = fwd_algorithmic(c)
@@ -411,7 +431,7 @@ def main():
     api.load()
 
     if args.pmc_run:
-        bench_forward(2, 1, args.workload)
+        bench_forward(2, 1, args.workload, min_warm_ms=0.0, flushed=False)
         nbytes = COPY_BYTES
         src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
@@ -465,7 +485,7 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": FWD_KERNEL if args.workload == 1 else "fwd_full_state_kernel + fwd_full_kernel",
                      "kernel_ms": kern_ms, "launches": {**st, "mall_flushed": True},
-                     "back_to_back_launch_mean_ms": sum(per) / len(per),
+                     "back_to_back_launches": launch_stats(per),
                      "algorithmic_bytes_per_launch": nbytes},
         "mfma": mfma,
     }
