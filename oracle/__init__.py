@@ -57,6 +57,10 @@ def _load():
                                                  i64, dp, dp, i32, i32, i32, i32, i32,
                                                  i32, i32, f64, f64, i32, dp, dp, dp]
             lib.oracle_lizard_decode.restype = i32
+            lib.oracle_lizard_bwd.argtypes = [dp, dp, dp, dp, dp, dp, i64, dp, dp, dp,
+                                              i32, i32, i32, i32, i32, i32, i32, i32,
+                                              f64, f64, i32, dp, dp, dp, dp, dp, dp, dp, dp]
+            lib.oracle_lizard_bwd.restype = i32
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = i32
             _lib = lib
@@ -193,3 +197,50 @@ def lizard_decode(state, ring_k, ring_v, pos, q, k, v, log_gamma, w_phi_q, w_phi
     if return_branches:
         res = res + (yg, yw)
     return res
+
+
+def lizard_bwd(q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v, dy, *, W: int, M: int,
+               mix: float, scale: float, feature_map: str = "softmax"):
+    """Gradients of sum(dy * y) through lizard_fwd, in fp64 (the chain rule through the
+    literal recurrence and window softmax; see oracle_lizard_bwd in lizard_oracle.c).
+
+    Same inputs as lizard_fwd plus dy [B,Hq,L,d].  Returns a dict of float64 arrays:
+    dq, dk, dv, dlg (shapes of q, k, v, log_gamma), dwq, dwk (shapes of w_phi_q and
+    w_phi_k; kept apart even when one matrix serves both sides: its gradient is then
+    dwq + dwk), dtk, dtv (shapes of t_k, t_v; [Hkv,0,d] when M = 0).
+    The forward states of one (batch, head) pair are all kept: L * df * d doubles per
+    OpenMP thread."""
+    fm = _fmap_code(feature_map)
+    q, k, v, lg, dy = _f64(q), _f64(k), _f64(v), _f64(log_gamma), _f64(dy)
+    wq, wk = _f64(w_phi_q), _f64(w_phi_k)
+    tk, tv = _f64(t_k), _f64(t_v)
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    df = lg.shape[-1]
+    cols = df // 2 if fm == 1 else df
+    if wq.shape[-2:] != (d, cols) or wk.shape[-2:] != (d, cols):
+        raise ValueError(f"W_phi must end in [{d},{cols}] for this feature map")
+    if (wq.ndim == 2) != (wk.ndim == 2):
+        raise ValueError("w_phi_q and w_phi_k must both be shared or both per head")
+    if wq.ndim == 3 and (wq.shape[0] != Hq or wk.shape[0] != Hkv):
+        raise ValueError("per-head W_phi must be [Hq,d,c] and [Hkv,d,c]")
+    stride = 0 if wq.ndim == 2 else d * cols
+    if dy.shape != q.shape:
+        raise ValueError("dy must have the shape of q")
+    Mc = max(M, 1)
+    if M == 0:
+        tk = np.zeros((Hkv, 1, d))
+        tv = np.zeros((Hkv, 1, d))
+    out = {"dq": np.zeros(q.shape), "dk": np.zeros(k.shape), "dv": np.zeros(v.shape),
+           "dlg": np.zeros(lg.shape), "dwq": np.zeros(wq.shape), "dwk": np.zeros(wk.shape),
+           "dtk": np.zeros((Hkv, Mc, d)), "dtv": np.zeros((Hkv, Mc, d))}
+    rc = _load().oracle_lizard_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(lg), _ptr(wq), _ptr(wk), stride, _ptr(tk), _ptr(tv), _ptr(dy),
+        B, Hq, Hkv, L, d, df, W, M, float(mix), float(scale), fm,
+        _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlg"]), _ptr(out["dwq"]),
+        _ptr(out["dwk"]), _ptr(out["dtk"]), _ptr(out["dtv"]))
+    if rc != 0:
+        raise ValueError("oracle_lizard_bwd rejected the shapes")
+    out["dtk"] = out["dtk"][:, :M]
+    out["dtv"] = out["dtv"][:, :M]
+    return out

@@ -32,6 +32,14 @@
  * It is deliberately the literal token-by-token recurrence and a brute-force
  * window softmax, in double precision, with no blocking, chunking or
  * reordering.  OpenMP runs independent (batch, query head) pairs in parallel.
+ *
+ * The backward pass (oracle_lizard_bwd) is the chain rule taken through those
+ * same steps in reverse order: the states S_i of the forward recurrence are
+ * kept, the recurrence is walked from the last token to the first carrying
+ * dL/dS, each window softmax is differentiated on its own, and the feature
+ * maps last.  The gradients are those the pages' training needs (arXiv page,
+ * Experiments: the first stage trains the feature maps and the gate; the
+ * Introduction's throughput claim is a training number).
  */
 #include <math.h>
 #include <stdint.h>
@@ -269,6 +277,233 @@ int oracle_lizard_decode(double *state, double *ring_k, double *ring_v,
     pos[n] = p + 1;
     free(phi); free(z); free(logit); free(yg); free(yw);
   }
+  return 0;
+}
+
+/* Backward of feature_map: given x, phi(x) and dL/dphi, add dL/dx to dx and
+ * dL/dW to dw (same layout as w).  fmap 0: dz_f = phi_f (dphi_f - sum_g
+ * phi_g dphi_g); fmap 1: dz_j = phi_j dphi_j - phi_{h+j} dphi_{h+j}.  Then
+ * dx_i = sum_f W[i][f] dz_f and dW[i][f] += x_i dz_f. */
+static void feature_map_bwd(const double *x, const double *w, int d, int df,
+                            int fmap, const double *phi, const double *dphi,
+                            double *dz, double *dx, double *dw) {
+  int cols = df;
+  if (fmap == 1) {
+    cols = df / 2;
+    for (int j = 0; j < cols; ++j)
+      dz[j] = phi[j] * dphi[j] - phi[cols + j] * dphi[cols + j];
+  } else {
+    double inner = 0.0;
+    for (int f = 0; f < df; ++f) inner += phi[f] * dphi[f];
+    for (int f = 0; f < df; ++f) dz[f] = phi[f] * (dphi[f] - inner);
+  }
+  for (int i = 0; i < d; ++i) {
+    double acc = 0.0;
+    for (int c = 0; c < cols; ++c) {
+      acc += w[(int64_t)i * cols + c] * dz[c];
+      dw[(int64_t)i * cols + c] += x[i] * dz[c];
+    }
+    dx[i] += acc;
+  }
+}
+
+/*
+ * Gradients of a scalar loss through oracle_lizard_fwd, given dy = dL/dy
+ * [B,Hq,L,d].  Outputs (overwritten): dq [B,Hq,L,d]; dk, dv [B,Hkv,L,d];
+ * dlg [B,Hkv,L,df]; dwq and dwk shaped like wq and wk (one matrix when
+ * w_stride = 0, else one per query / key-value head; w_stride must then be
+ * d * cols); dtk, dtv [Hkv,M,d].  dwq and dwk are kept apart even when the
+ * caller passes one matrix as both: its gradient is then their sum.
+ *
+ * For each (b, query head) the forward recurrence is run first, keeping every
+ * S_i (L * df * d doubles).  Then, from i = L-1 down to 0, with G = dL/dS_i:
+ *   G += phi_q(q_i) (mix dy_i)^T            (y_gla_i = phi_q^T S_i)
+ *   dphi_q(q_i) = S_i (mix dy_i)
+ *   dphi_k(k_i) = G v_i,  dv_i += G^T phi_k(k_i)   (S_i gets phi_k v_i^T)
+ *   dlg_i[f] = gamma_i[f] sum_e G[f][e] S_{i-1}[f][e]
+ *   G = diag(gamma_i) G                       (S_i = diag(gamma_i) S_{i-1} ...)
+ * and the window softmax of token i is differentiated with (1 - mix) dy_i:
+ *   dp_a = dy_w . value_a, ds_a = p_a (dp_a - sum_b p_b dp_b),
+ *   dq_i += scale sum_a ds_a key_a, dkey_a += scale ds_a q_i,
+ *   dvalue_a += p_a dy_w  (keys / values: meta tokens or k_j, v_j).
+ * Returns 0, or -1 on a shape it cannot take.
+ */
+int oracle_lizard_bwd(const double *q, const double *k, const double *v,
+                      const double *lg, const double *wq, const double *wk,
+                      int64_t w_stride, const double *tk, const double *tv,
+                      const double *dy, int B, int Hq, int Hkv, int L, int d,
+                      int df, int W, int M, double mix, double scale, int fmap,
+                      double *dq, double *dk, double *dv, double *dlg,
+                      double *dwq, double *dwk, double *dtk, double *dtv) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || L < 0 || d < 1 || df < 1 || W < 1 ||
+      M < 0 || Hq % Hkv != 0 || fmap < 0 || fmap > 1 || (fmap == 1 && df % 2))
+    return -1;
+  const int cols = fmap == 1 ? df / 2 : df;
+  const int64_t wsz = (int64_t)d * cols;
+  if (w_stride != 0 && w_stride != wsz) return -1;
+  const int G = Hq / Hkv;
+  const int nwq = w_stride ? Hq : 1, nwk = w_stride ? Hkv : 1;
+  memset(dq, 0, sizeof(double) * (size_t)B * Hq * L * d);
+  memset(dk, 0, sizeof(double) * (size_t)B * Hkv * L * d);
+  memset(dv, 0, sizeof(double) * (size_t)B * Hkv * L * d);
+  memset(dlg, 0, sizeof(double) * (size_t)B * Hkv * L * df);
+  memset(dwq, 0, sizeof(double) * (size_t)nwq * wsz);
+  memset(dwk, 0, sizeof(double) * (size_t)nwk * wsz);
+  if (M > 0) {
+    memset(dtk, 0, sizeof(double) * (size_t)Hkv * M * d);
+    memset(dtv, 0, sizeof(double) * (size_t)Hkv * M * d);
+  }
+  const int ntask = B * Hkv;
+  /* per task (b, kv head): private sums of the gradients shared between tasks */
+  double *pwq = calloc((size_t)ntask * nwq * wsz, sizeof(double));
+  double *pwk = calloc((size_t)ntask * nwk * wsz, sizeof(double));
+  double *ptk = calloc((size_t)ntask * (M > 0 ? M : 1) * d, sizeof(double));
+  double *ptv = calloc((size_t)ntask * (M > 0 ? M : 1) * d, sizeof(double));
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int task = 0; task < ntask; ++task) {
+    const int b = task / Hkv, hk = task % Hkv;
+    const int64_t kvo = ((int64_t)b * Hkv + hk) * L;
+    const double *kh = k + kvo * d, *vh = v + kvo * d, *gh = lg + kvo * df;
+    double *dkh = dk + kvo * d, *dvh = dv + kvo * d, *dgh = dlg + kvo * df;
+    const double *wkh = wk + (int64_t)hk * w_stride;
+    double *dwkh = pwk + (int64_t)task * nwk * wsz + (w_stride ? (int64_t)hk * wsz : 0);
+    const double *tkh = tk + (int64_t)hk * M * d, *tvh = tv + (int64_t)hk * M * d;
+    double *dtkh = ptk + (int64_t)task * (M > 0 ? M : 1) * d;
+    double *dtvh = ptv + (int64_t)task * (M > 0 ? M : 1) * d;
+    double *S = malloc(sizeof(double) * (size_t)(L + 1) * df * d); /* S[i+1] = S_i */
+    double *Gr = malloc(sizeof(double) * (size_t)df * d);
+    double *phq = malloc(sizeof(double) * (size_t)L * df);
+    double *phk = malloc(sizeof(double) * (size_t)L * df);
+    double *dphq = malloc(sizeof(double) * df);
+    double *dphk = malloc(sizeof(double) * df);
+    double *z = malloc(sizeof(double) * df);
+    double *dz = malloc(sizeof(double) * df);
+    double *p = malloc(sizeof(double) * (M + (W < L ? W : L) + 1));
+    double *dp = malloc(sizeof(double) * (M + (W < L ? W : L) + 1));
+    double *ydg = malloc(sizeof(double) * d);
+    for (int i = 0; i < L; ++i) feature_map(kh + (int64_t)i * d, wkh, d, df, fmap, z, phk + (int64_t)i * df);
+    for (int g = 0; g < G; ++g) {
+      const int hq = hk * G + g;
+      const int64_t qo = ((int64_t)b * Hq + hq) * L;
+      const double *qh = q + qo * d, *dyh = dy + qo * d;
+      double *dqh = dq + qo * d;
+      const double *wqh = wq + (int64_t)hq * w_stride;
+      double *dwqh = pwq + (int64_t)task * nwq * wsz + (w_stride ? (int64_t)hq * wsz : 0);
+      for (int i = 0; i < L; ++i) feature_map(qh + (int64_t)i * d, wqh, d, df, fmap, z, phq + (int64_t)i * df);
+      /* forward recurrence, every state kept */
+      memset(S, 0, sizeof(double) * (size_t)df * d);
+      for (int i = 0; i < L; ++i) {
+        const double *prev = S + (int64_t)i * df * d;
+        double *cur = S + (int64_t)(i + 1) * df * d;
+        for (int f = 0; f < df; ++f) {
+          const double gam = exp(gh[(int64_t)i * df + f]);
+          for (int e = 0; e < d; ++e)
+            cur[(int64_t)f * d + e] = gam * prev[(int64_t)f * d + e] +
+                                      phk[(int64_t)i * df + f] * vh[(int64_t)i * d + e];
+        }
+      }
+      /* reverse sweep of the global branch */
+      memset(Gr, 0, sizeof(double) * (size_t)df * d);
+      for (int i = L - 1; i >= 0; --i) {
+        const double *Si = S + (int64_t)(i + 1) * df * d, *Sp = S + (int64_t)i * df * d;
+        const double *vi = vh + (int64_t)i * d, *pq = phq + (int64_t)i * df, *pk = phk + (int64_t)i * df;
+        for (int e = 0; e < d; ++e) ydg[e] = mix * dyh[(int64_t)i * d + e];
+        for (int f = 0; f < df; ++f) {
+          double a = 0.0;
+          for (int e = 0; e < d; ++e) {
+            Gr[(int64_t)f * d + e] += pq[f] * ydg[e];
+            a += Si[(int64_t)f * d + e] * ydg[e];
+          }
+          dphq[f] = a;
+        }
+        for (int f = 0; f < df; ++f) {
+          double a = 0.0, c = 0.0;
+          for (int e = 0; e < d; ++e) {
+            a += Gr[(int64_t)f * d + e] * vi[e];
+            c += Gr[(int64_t)f * d + e] * Sp[(int64_t)f * d + e];
+          }
+          dphk[f] = a;
+          const double gam = exp(gh[(int64_t)i * df + f]);
+          dgh[(int64_t)i * df + f] += gam * c;
+        }
+        for (int e = 0; e < d; ++e) {
+          double a = 0.0;
+          for (int f = 0; f < df; ++f) a += Gr[(int64_t)f * d + e] * pk[f];
+          dvh[(int64_t)i * d + e] += a;
+        }
+        for (int f = 0; f < df; ++f) {
+          const double gam = exp(gh[(int64_t)i * df + f]);
+          for (int e = 0; e < d; ++e) Gr[(int64_t)f * d + e] *= gam;
+        }
+        feature_map_bwd(qh + (int64_t)i * d, wqh, d, df, fmap, pq, dphq, dz, dqh + (int64_t)i * d, dwqh);
+        feature_map_bwd(kh + (int64_t)i * d, wkh, d, df, fmap, pk, dphk, dz, dkh + (int64_t)i * d, dwkh);
+      }
+      /* window branch, token by token */
+      for (int i = 0; i < L; ++i) {
+        const double *qi = qh + (int64_t)i * d;
+        const double *dyi = dyh + (int64_t)i * d;
+        const int lo = i - W + 1 > 0 ? i - W + 1 : 0;
+        int n = 0;
+        double mx = -INFINITY;
+        for (int m = 0; m < M; ++m, ++n) {
+          p[n] = scale * dot(qi, tkh + (int64_t)m * d, d);
+          if (p[n] > mx) mx = p[n];
+        }
+        for (int j = lo; j <= i; ++j, ++n) {
+          p[n] = scale * dot(qi, kh + (int64_t)j * d, d);
+          if (p[n] > mx) mx = p[n];
+        }
+        double zsum = 0.0;
+        for (int a = 0; a < n; ++a) {
+          p[a] = exp(p[a] - mx);
+          zsum += p[a];
+        }
+        double inner = 0.0;
+        n = 0;
+        for (int m = 0; m < M; ++m, ++n) {
+          p[n] /= zsum;
+          dp[n] = (1.0 - mix) * dot(dyi, tvh + (int64_t)m * d, d);
+          inner += p[n] * dp[n];
+        }
+        for (int j = lo; j <= i; ++j, ++n) {
+          p[n] /= zsum;
+          dp[n] = (1.0 - mix) * dot(dyi, vh + (int64_t)j * d, d);
+          inner += p[n] * dp[n];
+        }
+        n = 0;
+        for (int m = 0; m < M; ++m, ++n) {
+          const double ds = p[n] * (dp[n] - inner);
+          for (int e = 0; e < d; ++e) {
+            dqh[(int64_t)i * d + e] += scale * ds * tkh[(int64_t)m * d + e];
+            dtkh[(int64_t)m * d + e] += scale * ds * qi[e];
+            dtvh[(int64_t)m * d + e] += p[n] * (1.0 - mix) * dyi[e];
+          }
+        }
+        for (int j = lo; j <= i; ++j, ++n) {
+          const double ds = p[n] * (dp[n] - inner);
+          for (int e = 0; e < d; ++e) {
+            dqh[(int64_t)i * d + e] += scale * ds * kh[(int64_t)j * d + e];
+            dkh[(int64_t)j * d + e] += scale * ds * qi[e];
+            dvh[(int64_t)j * d + e] += p[n] * (1.0 - mix) * dyi[e];
+          }
+        }
+      }
+    }
+    free(S); free(Gr); free(phq); free(phk); free(dphq); free(dphk); free(z); free(dz);
+    free(p); free(dp); free(ydg);
+  }
+  for (int task = 0; task < ntask; ++task) {
+    for (int64_t x = 0; x < (int64_t)nwq * wsz; ++x) dwq[x] += pwq[(int64_t)task * nwq * wsz + x];
+    for (int64_t x = 0; x < (int64_t)nwk * wsz; ++x) dwk[x] += pwk[(int64_t)task * nwk * wsz + x];
+    if (M > 0) {
+      const int hk = task % Hkv;
+      for (int64_t x = 0; x < (int64_t)M * d; ++x) {
+        dtk[(int64_t)hk * M * d + x] += ptk[(int64_t)task * M * d + x];
+        dtv[(int64_t)hk * M * d + x] += ptv[(int64_t)task * M * d + x];
+      }
+    }
+  }
+  free(pwq); free(pwk); free(ptk); free(ptv);
   return 0;
 }
 

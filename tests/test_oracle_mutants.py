@@ -143,3 +143,70 @@ def test_hedgehog_pins_catch_mutant(name, orig, mut, tmp_path, monkeypatch):
         except AssertionError:
             failures += 1
     assert failures > 0, f"no pin caught mutant {name!r}"
+
+
+# Mutants of the backward pass, against its pins (finite differences, autograd).
+import tests.test_oracle_bwd as bwd_pins  # noqa: E402
+
+BWD_MUTANTS = [
+    ("bwd gate gradient without gamma",
+     "dgh[(int64_t)i * df + f] += gam * c;",
+     "dgh[(int64_t)i * df + f] += c;"),
+    ("bwd state gradient not decayed",
+     "for (int e = 0; e < d; ++e) Gr[(int64_t)f * d + e] *= gam;",
+     "for (int e = 0; e < d; ++e) Gr[(int64_t)f * d + e] *= 1.0;"),
+    ("bwd query features read the previous state",
+     "a += Si[(int64_t)f * d + e] * ydg[e];",
+     "a += Sp[(int64_t)f * d + e] * ydg[e];"),
+    ("bwd softmax map without its inner product",
+     "for (int f = 0; f < df; ++f) dz[f] = phi[f] * (dphi[f] - inner);",
+     "for (int f = 0; f < df; ++f) dz[f] = phi[f] * dphi[f];"),
+    ("bwd window dq without the scale",
+     "dqh[(int64_t)i * d + e] += scale * ds * kh[(int64_t)j * d + e];",
+     "dqh[(int64_t)i * d + e] += ds * kh[(int64_t)j * d + e];"),
+    ("bwd window dv without the merge weight",
+     "dvh[(int64_t)j * d + e] += p[n] * (1.0 - mix) * dyi[e];",
+     "dvh[(int64_t)j * d + e] += p[n] * dyi[e];"),
+    ("bwd hedgehog halves added",
+     "dz[j] = phi[j] * dphi[j] - phi[cols + j] * dphi[cols + j];",
+     "dz[j] = phi[j] * dphi[j] + phi[cols + j] * dphi[cols + j];"),
+    ("bwd weight gradient transposed",
+     "dw[(int64_t)i * cols + c] += x[i] * dz[c];",
+     "dw[(int64_t)c * d + i] += x[i] * dz[c];"),
+    ("bwd value gradient with the query features",
+     "for (int f = 0; f < df; ++f) a += Gr[(int64_t)f * d + e] * pk[f];",
+     "for (int f = 0; f < df; ++f) a += Gr[(int64_t)f * d + e] * pq[f];"),
+    ("bwd window ignores the meta-token mean",
+     "for (int m = 0; m < M; ++m, ++n) {\n          p[n] /= zsum;\n          dp[n] = (1.0 - mix) * dot(dyi, tvh + (int64_t)m * d, d);\n          inner += p[n] * dp[n];",
+     "for (int m = 0; m < M; ++m, ++n) {\n          p[n] /= zsum;\n          dp[n] = (1.0 - mix) * dot(dyi, tvh + (int64_t)m * d, d);"),
+]
+
+BWD_PIN_FUNCS = [
+    lambda: bwd_pins.check_fd(*bwd_pins.FD_CASES[0]),
+    lambda: bwd_pins.check_fd(*bwd_pins.FD_CASES[4]),
+    lambda: bwd_pins.test_bwd_matches_autograd_of_explicit_products(*bwd_pins.AG_CASES[0]),
+]
+
+
+@pytest.mark.parametrize("name,orig,mut", BWD_MUTANTS, ids=[m[0] for m in BWD_MUTANTS])
+def test_bwd_pins_catch_mutant(name, orig, mut, tmp_path, monkeypatch):
+    src = open(SRC).read()
+    assert src.count(orig) >= 1, f"mutation anchor for {name!r} not found"
+    cpath = tmp_path / "mut.c"
+    cpath.write_text(src.replace(orig, mut, 1))
+    so = tmp_path / "libmut.so"
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-std=c99", str(cpath),
+                    "-o", str(so), "-lm"], check=True)
+    real = oracle._load()
+    lib = ctypes.CDLL(str(so))
+    for fn in ("oracle_lizard_fwd", "oracle_lizard_decode", "oracle_lizard_bwd", "oracle_num_threads"):
+        getattr(lib, fn).argtypes = getattr(real, fn).argtypes
+        getattr(lib, fn).restype = getattr(real, fn).restype
+    monkeypatch.setattr(oracle, "_lib", lib)
+    failures = 0
+    for fn in BWD_PIN_FUNCS:
+        try:
+            fn()
+        except AssertionError:
+            failures += 1
+    assert failures > 0, f"no pin caught mutant {name!r}"
