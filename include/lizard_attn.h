@@ -237,6 +237,68 @@ lizard_status lizard_attn_decode_hedgehog(float *state, void *win_k,
                                           size_t workspace_bytes, void *stream);
 
 /*
+ * Backward pass of lizard_attn_fwd: given dy = dL/dy [B, Hq, L, d] for a scalar
+ * loss L, the gradients of L with respect to every input of the forward.  The
+ * pages train the feature maps, the gate and the meta-memory tokens (arXiv
+ * page, Experiments: the first training stage; the Introduction's +32%
+ * figure is a training-throughput number), which needs these gradients.
+ * Inputs q, k, v, log_gamma, w_phi_q, w_phi_k, w_phi_head_stride, t_k, t_v, W,
+ * M, mix, scale, dtype exactly as given to the forward; w_phi_head_stride must
+ * be 0 (one matrix for every head) or d*d (one per head).  Outputs (device
+ * pointers, overwritten):
+ *   dq [B, Hq, L, d]; dk, dv, dlog_gamma [B, Hkv, L, d]   in `dtype`
+ *   dw_phi_q, dw_phi_k   fp32, shaped like w_phi_q / w_phi_k ([d, d], or
+ *                        [Hq, d, d] / [Hkv, d, d] per head).  They are kept
+ *                        apart even when one matrix serves both sides (pass the
+ *                        same pointer twice to the forward): its gradient is
+ *                        then dw_phi_q + dw_phi_k.
+ *   dt_k, dt_v [Hkv, M, d] fp32 (may be NULL when M = 0)
+ * The window keys' and values' gradients sum over the query heads of their
+ * group, as do the meta tokens' and the key side's feature-map gradients.
+ * Built for the forward's dtypes and head dimensions (bf16 d = 64 or 128, fp32
+ * d = 64), any W, M <= 16, any grouping.  workspace: at least
+ * lizard_attn_bwd_workspace_bytes() bytes (16-byte aligned), clobbered.
+ * B = 0 or L = 0 launches nothing and writes nothing.
+ */
+lizard_status lizard_attn_bwd(const void *q, const void *k, const void *v,
+                              const void *log_gamma, const void *w_phi_q,
+                              const void *w_phi_k, int64_t w_phi_head_stride,
+                              const void *t_k, const void *t_v, const void *dy,
+                              void *dq, void *dk, void *dv, void *dlog_gamma,
+                              float *dw_phi_q, float *dw_phi_k, float *dt_k,
+                              float *dt_v, int B, int Hq, int Hkv, int L, int d,
+                              int W, int M, float mix, float scale,
+                              lizard_dtype dtype, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* Workspace bytes lizard_attn_bwd (and lizard_attn_bwd_hedgehog) needs: about
+ * 24 * B * (Hq + Hkv) * L * d bytes (the feature maps, fp32 feature-map and
+ * window gradients) plus partial sums; 0 for an empty or invalid shape. */
+size_t lizard_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int d,
+                                       int M, lizard_dtype dtype);
+
+/*
+ * Backward pass of lizard_attn_fwd_hedgehog (the Hedgehog map exp(xW) (+)
+ * exp(-xW), W_phi [d, d/2]): arguments as lizard_attn_bwd, with dw_phi_q /
+ * dw_phi_k shaped like the [d, d/2] (or per-head [H, d, d/2]) matrices and
+ * w_phi_head_stride 0 or d*d/2.  Unlike the Hedgehog forward it takes separate
+ * and per-head matrices, every built dtype and head dimension, and any W.
+ */
+lizard_status lizard_attn_bwd_hedgehog(const void *q, const void *k,
+                                       const void *v, const void *log_gamma,
+                                       const void *w_phi_q, const void *w_phi_k,
+                                       int64_t w_phi_head_stride,
+                                       const void *t_k, const void *t_v,
+                                       const void *dy, void *dq, void *dk,
+                                       void *dv, void *dlog_gamma,
+                                       float *dw_phi_q, float *dw_phi_k,
+                                       float *dt_k, float *dt_v, int B, int Hq,
+                                       int Hkv, int L, int d, int W, int M,
+                                       float mix, float scale,
+                                       lizard_dtype dtype, void *workspace,
+                                       size_t workspace_bytes, void *stream);
+
+/*
  * lizard_attn_decode without a workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc).  Arguments and results as lizard_attn_decode (softmax

@@ -27,7 +27,8 @@ EXPORTED = ("lizard_attn_fwd", "lizard_attn_fwd_workspace_bytes", "lizard_attn_f
             "lizard_attn_fwd_ext", "lizard_attn_fwd_ext_workspace_bytes", "lizard_attn_decode",
             "lizard_attn_decode_hedgehog", "lizard_attn_decode_workspace_bytes",
             "lizard_status_string", "lizard_last_error", "lizard_version", "lizard_set_option",
-            "lizard_get_option", "lizard_attn_decode_noalloc")
+            "lizard_get_option", "lizard_attn_decode_noalloc", "lizard_attn_bwd",
+            "lizard_attn_bwd_hedgehog", "lizard_attn_bwd_workspace_bytes")
 
 _lock = threading.Lock()
 _lib = None
@@ -63,6 +64,13 @@ def _declare(lib):
     lib.lizard_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp,
                                                i32, i32, i32, i32, i32, i32, f32, f32, i32, vp]
     lib.lizard_attn_decode_noalloc.restype = i32
+    lib.lizard_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                    i32, i32, i32, i32, i32, i32, i32, f32, f32, i32, vp, sz, vp]
+    lib.lizard_attn_bwd.restype = i32
+    lib.lizard_attn_bwd_hedgehog.argtypes = lib.lizard_attn_bwd.argtypes
+    lib.lizard_attn_bwd_hedgehog.restype = i32
+    lib.lizard_attn_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.lizard_attn_bwd_workspace_bytes.restype = sz
     lib.lizard_attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.lizard_attn_decode_workspace_bytes.restype = sz
     lib.lizard_status_string.argtypes = [i32]
@@ -363,6 +371,66 @@ def _decode(fn, state, win_k, win_v, pos, q, k, v, log_gamma, w_phi_q, w_phi_k, 
     workspace = _workspace(workspace, max(need, 16), q.device)
     wbytes = workspace.numel() * workspace.element_size()
     _check(fn(*args, _ptr(workspace), wbytes, _stream(stream)))
+    return out
+
+
+def lizard_attn_bwd_workspace_bytes(B: int, Hq: int, Hkv: int, L: int, d: int, M: int,
+                                    dtype: torch.dtype) -> int:
+    return int(load().lizard_attn_bwd_workspace_bytes(B, Hq, Hkv, L, d, M, _DTYPES[dtype]))
+
+
+def lizard_attn_bwd(q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v, dy, *, W: int, M: int,
+                    mix: float = 0.5, scale: float | None = None, feature_map: str = "softmax",
+                    workspace=None, stream=None):
+    """Backward of lizard_attn_fwd (feature_map "softmax") or lizard_attn_fwd_hedgehog
+    ("hedgehog"): gradients of a loss with dL/dy = dy [B,Hq,L,d].  Returns a dict: dq, dk, dv,
+    dlg in the input dtype; dwq, dwk (shaped like w_phi_q / w_phi_k; kept apart even when one
+    matrix serves both sides), dtk, dtv ([Hkv,M,d]) in fp32."""
+    if feature_map not in ("softmax", "hedgehog"):
+        raise ValueError(f"unknown feature map {feature_map!r}")
+    hh = feature_map == "hedgehog"
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (log_gamma, "log_gamma"), (w_phi_q, "w_phi_q"),
+                 (w_phi_k, "w_phi_k"), (dy, "dy")):
+        _dev(t, n, dt)
+    if M > 0:
+        _dev(t_k, "t_k", dt)
+        _dev(t_v, "t_v", dt)
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, L, d) or v.shape != k.shape or log_gamma.shape != k.shape:
+        raise ValueError("k, v, log_gamma must be [B,Hkv,L,d] matching q")
+    if dy.shape != q.shape:
+        raise ValueError("dy must have the shape of q")
+    if M > 0 and (t_k.shape != (Hkv, M, d) or t_v.shape != (Hkv, M, d)):
+        raise ValueError("t_k, t_v must be [Hkv,M,d]")
+    _same_device(q.device, (k, "k"), (v, "v"), (log_gamma, "log_gamma"), (w_phi_q, "w_phi_q"),
+                 (w_phi_k, "w_phi_k"), (dy, "dy"), (t_k if M > 0 else None, "t_k"),
+                 (t_v if M > 0 else None, "t_v"))
+    cols = d // 2 if hh else d
+    wstride = _w_stride(w_phi_q, w_phi_k, d, Hq, Hkv, cols)
+    if scale is None:
+        scale = d ** -0.5
+    dev = q.device
+    out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+           "dlg": torch.empty_like(log_gamma),
+           "dwq": torch.empty(w_phi_q.shape, dtype=torch.float32, device=dev),
+           "dwk": torch.empty(w_phi_k.shape, dtype=torch.float32, device=dev),
+           "dtk": torch.empty((Hkv, M, d), dtype=torch.float32, device=dev),
+           "dtv": torch.empty((Hkv, M, d), dtype=torch.float32, device=dev)}
+    need = lizard_attn_bwd_workspace_bytes(B, Hq, Hkv, L, d, M, dt)
+    workspace = _workspace(workspace, need, dev)
+    wbytes = 0 if workspace is None else workspace.numel()
+    fn = load().lizard_attn_bwd_hedgehog if hh else load().lizard_attn_bwd
+    _check(fn(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), _ptr(w_phi_q), _ptr(w_phi_k), wstride,
+        _ptr(t_k) if M > 0 else None, _ptr(t_v) if M > 0 else None, _ptr(dy),
+        _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlg"]), _ptr(out["dwq"]),
+        _ptr(out["dwk"]), _ptr(out["dtk"]) if M > 0 else None, _ptr(out["dtv"]) if M > 0 else None,
+        B, Hq, Hkv, L, d, W, M, float(mix), float(scale), _DTYPES[dt], _ptr(workspace), wbytes,
+        _stream(stream)))
     return out
 
 

@@ -485,6 +485,90 @@ lizard_status lizard_attn_decode_hedgehog(float *state, void *win_k, void *win_v
                      out, N, Hq, Hkv, d, W, M, mix, scale, dtype, workspace, workspace_bytes, stream, true);
 }
 
+size_t lizard_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int M, lizard_dtype dtype) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0 || d <= 0 || M < 0 || Hq % Hkv != 0) return 0;
+  return lz::bwd_workspace_layout(B, Hq, Hkv, L, d, M, dtype == LIZARD_BF16, nullptr);
+}
+
+static lizard_status bwd_impl(const void *q, const void *k, const void *v, const void *log_gamma,
+                              const void *w_phi_q, const void *w_phi_k, int64_t w_phi_head_stride, const void *t_k,
+                              const void *t_v, const void *dy, void *dq, void *dk, void *dv, void *dlog_gamma,
+                              float *dw_phi_q, float *dw_phi_k, float *dt_k, float *dt_v, int B, int Hq, int Hkv,
+                              int L, int d, int W, int M, float mix, float scale, lizard_dtype dtype,
+                              void *workspace, size_t workspace_bytes, void *stream, bool hedgehog) {
+  if (dtype != LIZARD_F32 && dtype != LIZARD_BF16) return fail(LIZARD_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (B < 0 || L < 0) return fail(LIZARD_ERR_INVALID_ARG, "B=%d and L=%d must be >= 0", B, L);
+  if (Hq < 1 || Hkv < 1 || d < 1 || W < 1 || M < 0)
+    return fail(LIZARD_ERR_INVALID_ARG, "need Hq, Hkv, d, W >= 1 and M >= 0 (got Hq=%d Hkv=%d d=%d W=%d M=%d)", Hq,
+                Hkv, d, W, M);
+  if (Hq % Hkv != 0) return fail(LIZARD_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (!(std::isfinite(mix) && mix >= 0.f) || !std::isfinite(scale))
+    return fail(LIZARD_ERR_INVALID_ARG, "mix=%g must be finite and >= 0, scale=%g finite", (double)mix, (double)scale);
+  if (!supported_d(d, dtype))
+    return fail(LIZARD_ERR_UNSUPPORTED, "head dim d=%d not built for %s", d, dtype == LIZARD_BF16 ? "bf16" : "fp32");
+  if (M > kMaxMeta) return fail(LIZARD_ERR_UNSUPPORTED, "M=%d meta tokens (at most %d)", M, kMaxMeta);
+  const int64_t wsize = (int64_t)d * (hedgehog ? d / 2 : d);
+  if (w_phi_head_stride != 0 && w_phi_head_stride != wsize)
+    return fail(LIZARD_ERR_INVALID_ARG, "w_phi_head_stride=%lld: 0 (shared) or %lld (one matrix per head)",
+                (long long)w_phi_head_stride, (long long)wsize);
+  if ((int64_t)B * Hq * L > (int64_t)1 << 34) return fail(LIZARD_ERR_INVALID_ARG, "problem too large");
+  if (B == 0 || L == 0) return LIZARD_OK;  // empty problem: nothing is written
+  if (!q || !k || !v || !log_gamma || !w_phi_q || !w_phi_k || !dy || !dq || !dk || !dv || !dlog_gamma ||
+      !dw_phi_q || !dw_phi_k)
+    return fail(LIZARD_ERR_INVALID_ARG, "null tensor pointer");
+  if (M > 0 && (!t_k || !t_v || !dt_k || !dt_v)) return fail(LIZARD_ERR_INVALID_ARG, "t_k/t_v/dt_k/dt_v null with M=%d", M);
+  const void *ptrs[] = {q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v, dy, dq, dk, dv, dlog_gamma,
+                        dw_phi_q, dw_phi_k, dt_k, dt_v};
+  for (const void *ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return fail(LIZARD_ERR_INVALID_ARG, "tensor pointer %p not 16-byte aligned", ptr);
+  lz::BwdWs ws{};
+  const size_t need = lz::bwd_workspace_layout(B, Hq, Hkv, L, d, M, dtype == LIZARD_BF16, &ws);
+  if (!workspace || workspace_bytes < need)
+    return fail(LIZARD_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(LIZARD_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+  char *w = static_cast<char *>(workspace);
+  lz::BwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.lg = log_gamma; p.wq = w_phi_q; p.wk = w_phi_k; p.tk = t_k; p.tv = t_v; p.dy = dy;
+  p.dq = dq; p.dk = dk; p.dvo = dv; p.dlg = dlog_gamma;
+  p.dwq = dw_phi_q; p.dwk = dw_phi_k; p.dtk = dt_k; p.dtv = dt_v;
+  p.phq = reinterpret_cast<float *>(w + ws.phq); p.phk = reinterpret_cast<float *>(w + ws.phk);
+  p.dphq = reinterpret_cast<float *>(w + ws.dphq); p.dphk = reinterpret_cast<float *>(w + ws.dphk);
+  p.dvg = reinterpret_cast<float *>(w + ws.dvg); p.dqw = reinterpret_cast<float *>(w + ws.dqw);
+  p.dkw = reinterpret_cast<float *>(w + ws.dkw); p.dvw = reinterpret_cast<float *>(w + ws.dvw);
+  p.wstat = reinterpret_cast<float *>(w + ws.wstat); p.dw_part = reinterpret_cast<float *>(w + ws.dw_part);
+  p.dtk_part = reinterpret_cast<float *>(w + ws.dtk_part); p.dtv_part = reinterpret_cast<float *>(w + ws.dtv_part);
+  p.w_stride = w_phi_head_stride;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.L = L; p.W = W; p.M = M; p.G = Hq / Hkv;
+  p.hh = hedgehog ? 1 : 0;
+  p.mix = mix; p.scale = scale;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return finish(lz::launch_bwd(p, dtype == LIZARD_BF16, d, st), st);
+}
+
+lizard_status lizard_attn_bwd(const void *q, const void *k, const void *v, const void *log_gamma,
+                              const void *w_phi_q, const void *w_phi_k, int64_t w_phi_head_stride, const void *t_k,
+                              const void *t_v, const void *dy, void *dq, void *dk, void *dv, void *dlog_gamma,
+                              float *dw_phi_q, float *dw_phi_k, float *dt_k, float *dt_v, int B, int Hq, int Hkv,
+                              int L, int d, int W, int M, float mix, float scale, lizard_dtype dtype,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+  return bwd_impl(q, k, v, log_gamma, w_phi_q, w_phi_k, w_phi_head_stride, t_k, t_v, dy, dq, dk, dv, dlog_gamma,
+                  dw_phi_q, dw_phi_k, dt_k, dt_v, B, Hq, Hkv, L, d, W, M, mix, scale, dtype, workspace,
+                  workspace_bytes, stream, false);
+}
+
+lizard_status lizard_attn_bwd_hedgehog(const void *q, const void *k, const void *v, const void *log_gamma,
+                                       const void *w_phi_q, const void *w_phi_k, int64_t w_phi_head_stride,
+                                       const void *t_k, const void *t_v, const void *dy, void *dq, void *dk,
+                                       void *dv, void *dlog_gamma, float *dw_phi_q, float *dw_phi_k, float *dt_k,
+                                       float *dt_v, int B, int Hq, int Hkv, int L, int d, int W, int M, float mix,
+                                       float scale, lizard_dtype dtype, void *workspace, size_t workspace_bytes,
+                                       void *stream) {
+  return bwd_impl(q, k, v, log_gamma, w_phi_q, w_phi_k, w_phi_head_stride, t_k, t_v, dy, dq, dk, dv, dlog_gamma,
+                  dw_phi_q, dw_phi_k, dt_k, dt_v, B, Hq, Hkv, L, d, W, M, mix, scale, dtype, workspace,
+                  workspace_bytes, stream, true);
+}
+
 lizard_status lizard_attn_decode_noalloc(float *state, void *win_k, void *win_v, int32_t *pos, const void *q,
                                          const void *k, const void *v, const void *log_gamma, const void *w_phi_q,
                                          const void *w_phi_k, int64_t w_phi_head_stride, const void *t_k,

@@ -1,0 +1,1138 @@
+// Lizard attention backward: gradients of a loss L through the forward (softmax or Hedgehog
+// feature map, gated linear attention, anchor window, merge) given dL/dy.
+//
+// Decomposition (every kernel here; the host sequence is launch_bwd at the end):
+//   1. bwd_phi_kernel       phi_q = fmap(q W_q), phi_k = fmap(k W_k) into the workspace.
+//   2. bwd_sweep_kernel     role F (one wave per batch, query head, 16-feature tile): forward over
+//                           16-token steps with its columns of the state S in registers:
+//                               dphi_q[t] = mix * S_t dy_t
+//                           role V (one wave per batch, key/value head, 16-column tile of v):
+//                           backward over the steps with its columns of dL/dS in registers:
+//                               dv_gla[s] = mix * dS_s^T phi_k[s]
+//   3. bwd_sweep_kernel     role R (one wave per batch, key/value head, 16-feature tile): backward
+//                           with its rows of dL/dS:  dphi_k[s] = mix * dS_s v_s, and the log-gate
+//                           gradient dlg_j = sum_{t >= j} (sum_g phi_q phi_q-grad - phi_k phi_k-grad)
+//   4. bwd_win_q_kernel     window softmax statistics, dq of the window, meta-token gradients.
+//   5. bwd_win_k_kernel     dk and dv of the window.
+//   6. bwd_fb_kernel        feature-map backward, dq = dz_q W_q^T (+ window part), dk likewise,
+//                           dv = both parts, dW partial sums.
+//   7. bwd_reduce_kernel    dW and dT from their partial sums.
+//
+// Where the recurrence lives.  S_t = diag(gamma_t) S_{t-1} + phi_k(k_t) v_t^T and y_t = phi_q^T S_t
+// (papernotes.org summary, "key designs", Gated Linear Attention item).  Inside a 16-token step
+// with p_t the log-gate prefix from the step start (inclusive) and P its total,
+//   S_t = diag(e^{p_t}) S_in + sum_{s <= t} diag(e^{p_t - p_s}) phi_k[s] v_s^T.
+// A step is "mild" when P >= -60 for the features a wave handles: the exponentials then split
+// into e^{p_t} <= 1 and e^{-p_s} <= e^60 factors on the MFMA operands.  Otherwise the in-step
+// products are taken per element in fp32 (e.g. gamma ~ 0).  Every state update uses e^{P - p_s}
+// <= 1 and needs no split.
+//
+// MFMA conventions (common.hpp): x32 fragments for contractions over d; K = 16 fragments (F4) for
+// contractions over the 16 tokens of a step: lane (r, kq) holds A[m = r][k = 4kq + j] and
+// B[k = 4kq + j][n = r], j = 0..3, and the accumulator D[m = 4kq + i][n = r].  "Interleaved" rows:
+// slot j of lane group kq in K-step ks holds column 32 ks + 16 (j >> 2) + 4 kq + (j & 3), the order
+// in which an accumulator tile pair (16 dt.. , 16 dt + 16..) lists its rows, so that accumulators
+// of the states serve as MFMA operands straight from registers.
+#include "fwd_common.hpp"
+
+namespace lz {
+namespace bwd {
+
+constexpr int TS = 16;              // tokens per sweep step / window tile
+constexpr float MILD_SPAN = 60.f;   // -P at most this for the split exponentials
+constexpr int QPW = 16;             // query tiles per wave in the window-q kernel
+
+template <typename T> struct F4;
+template <> struct F4<bf16> { bf16x4 v; };
+template <> struct F4<float> { float v[4]; };
+
+template <typename T> __device__ __forceinline__ F4<T> f4_from(const float (&x)[4]) {
+  F4<T> f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f.v[j] = from_f<T>(x[j]);
+  return f;
+}
+template <typename T> __device__ __forceinline__ float f4_at(const F4<T> &f, int j) { return to_f(f.v[j]); }
+
+__device__ __forceinline__ f32x4 mma16(const F4<bf16> &a, const F4<bf16> &b, f32x4 c) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, a.v), __builtin_bit_cast(s4, b.v), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(const F4<float> &a, const F4<float> &b, f32x4 c) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], c, 0, 0, 0);
+  return c;
+}
+// fp32 operands regardless of T (exact sums of fp32 values)
+__device__ __forceinline__ f32x4 mma16_f32(const float (&a)[4], const float (&b)[4], f32x4 c) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
+  return c;
+}
+
+// Rows r0 .. r0+3 of column c0 + (lane % 16) of a row-major tile in LDS (ld elements per row,
+// a multiple of 4; c0 a multiple of 4).  bf16: one transposed read (ds_read_b64_tr_b16: lane m of
+// each group of 16 reads 4 elements of row r0 + m / 4 from column c0 + 4 (m % 4), lane i receives
+// column c0 + i of the 4 rows).
+template <typename T> __device__ __forceinline__ F4<T> lds_col4(const T *tile, int ld, int r0, int c0) {
+  const int m = threadIdx.x & 15;
+  F4<T> f;
+  if constexpr (sizeof(T) == 2) {
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    const T *src = tile + (r0 + (m >> 2)) * ld + c0 + 4 * (m & 3);
+    const s4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4 *)(src));
+    f.v = __builtin_bit_cast(bf16x4, x);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.v[j] = tile[(r0 + j) * ld + c0 + m];
+  }
+  return f;
+}
+
+// Interleaved row fragment of K-step ks from row `row` of a [rows][D] tensor (zero when !ok).
+template <typename T> __device__ __forceinline__ Frag<T> row_il(const T *base, int ks, int kq, bool ok) {
+  if (!ok) return frag_zero<T>();
+  return load4x2(base + 32 * ks + 4 * kq, base + 32 * ks + 16 + 4 * kq);
+}
+// The same fragment written into a row-major LDS tile row (natural column order).
+template <typename T> __device__ __forceinline__ void store_il(T *row, const Frag<T> &f, int ks, int kq) {
+  if constexpr (sizeof(T) == 2) {
+    bf16x4 a, b;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { a[j] = f.v[j]; b[j] = f.v[4 + j]; }
+    *reinterpret_cast<bf16x4 *>(row + 32 * ks + 4 * kq) = a;
+    *reinterpret_cast<bf16x4 *>(row + 32 * ks + 16 + 4 * kq) = b;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { row[32 * ks + 4 * kq + j] = f.v[j]; row[32 * ks + 16 + 4 * kq + j] = f.v[4 + j]; }
+  }
+}
+// Natural row fragment (columns 32 ks + 8 kq .. + 7) of row `row`.
+template <typename T> __device__ __forceinline__ Frag<T> row_nat(const T *base, int ks, int kq, bool ok) {
+  return ok ? load8(base + 32 * ks + 8 * kq) : frag_zero<T>();
+}
+// Column fragment: rows r0 + j (j = 0..3, zero at or beyond L) of column `col`.
+template <typename T> __device__ __forceinline__ F4<T> col_g(const T *base, int D, int r0, int col, int L) {
+  F4<T> f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f.v[j] = (r0 + j < L) ? base[(size_t)(r0 + j) * D + col] : from_f<T>(0.f);
+  return f;
+}
+__device__ __forceinline__ void colf_g(const float *base, int D, int r0, int col, int L, float (&x)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x[j] = (r0 + j < L) ? base[(size_t)(r0 + j) * D + col] : 0.f;
+}
+
+// Conversions between operand types.
+template <typename T> __device__ __forceinline__ Frag<float> to32(const Frag<T> &f) {
+  Frag<float> o;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o.v[j] = to_f(f.v[j]);
+  return o;
+}
+template <typename T> __device__ __forceinline__ F4<float> to32(const F4<T> &f) {
+  F4<float> o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o.v[j] = to_f(f.v[j]);
+  return o;
+}
+template <typename T> __device__ __forceinline__ Frag<T> from32(const Frag<float> &f) {
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = f.v[j];
+  return frag_from<T>(x);
+}
+
+// Constant triangles of the in-step prefix sums: lane (r, kq) slot j -> (4 kq + j <= r).
+template <typename T> __device__ __forceinline__ F4<T> tri_le(int r, int kq) {
+  float x[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x[j] = (4 * kq + j <= r) ? 1.f : 0.f;
+  return f4_from<T>(x);
+}
+
+}  // namespace bwd
+
+using namespace bwd;
+
+// ======================================================================== 1. feature maps
+// One wave per 16 rows of q (blocks < nq) or k: phi = softmax(x W) or exp(xW) (+) exp(-xW), stored
+// in fp32 (the log-gate gradient sums products of phi with its gradient over the whole sequence,
+// and those sums cancel to zero overall: their terms need fp32 accuracy); W^T staged in LDS.
+template <typename T, int D, bool HH>
+__global__ __launch_bounds__(256) void bwd_phi_kernel(BwdParams p) {
+  constexpr int NFT = D / 16, KS = D / 32, LDW = D + 16 / (int)sizeof(T);
+  constexpr int FC = HH ? D / 2 : D;
+  __shared__ __align__(16) T sW[D * LDW];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, kq = lane >> 4;
+  const int ntile = (p.L + 63) / 64;
+  const int nq = p.B * p.Hq * ntile;
+  const bool qside = (int)blockIdx.x < nq;
+  const int bid = qside ? blockIdx.x : blockIdx.x - nq;
+  const int H = qside ? p.Hq : p.Hkv;
+  const int bh = bid / ntile, c0 = (bid % ntile) * 64 + 16 * w;
+  const int h = bh % H;
+  const T *Wsrc = reinterpret_cast<const T *>(qside ? p.wq : p.wk) + (size_t)h * p.w_stride;
+  for (int idx = tid; idx < D * FC; idx += 256) {  // W[i][c] -> sW[c][i] (and -W -> sW[FC + c][i])
+    const int i = idx / FC, c = idx % FC;
+    const T x = Wsrc[(size_t)i * FC + c];
+    sW[c * LDW + i] = x;
+    if constexpr (HH) sW[(FC + c) * LDW + i] = from_f<T>(-to_f(x));
+  }
+  __syncthreads();
+  const T *X = reinterpret_cast<const T *>(qside ? p.q : p.k) + (size_t)bh * p.L * D;
+  float *PH = (qside ? p.phq : p.phk) + (size_t)bh * p.L * D;
+  const int t = c0 + r;
+  Frag<T> xf[KS];
+#pragma unroll
+  for (int j = 0; j < KS; ++j) xf[j] = row_nat(X + (size_t)t * D, j, kq, t < p.L);
+  f32x4 z[NFT];
+  feature_logits<T, D, LDW>(sW, xf, r, kq, z);  // z^T[f][t]: lane (t = r, kq) holds f = 16 ft + 4 kq + i
+  float ph[NFT][4];
+  if constexpr (HH) {
+#pragma unroll
+    for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ph[ft][i] = __expf(z[ft][i]);
+  } else {
+    softmax_rows<NFT>(z, ph);
+  }
+  if (t < p.L) {
+#pragma unroll
+    for (int ft = 0; ft < NFT; ++ft)
+      *reinterpret_cast<f32x4 *>(PH + (size_t)t * D + 16 * ft + 4 * kq) = f32x4{ph[ft][0], ph[ft][1], ph[ft][2], ph[ft][3]};
+  }
+}
+
+// ======================================================================== 2/3. sweeps
+// Wave-private LDS tiles of a step: T rows of 16 tokens (8-byte aligned transposed reads), and
+// fp32 tables of the exact path (16 tokens x the features the wave handles).
+template <typename T, int D> struct LdsF {
+  static constexpr int LD = D + 4, LDF = 20;
+  float a[TS * LD];      // rows of v
+  float pf[TS * LDF];    // p[s][f - f0]
+  float ph1[TS * LDF];   // phi_k[s][f - f0]
+};
+template <typename T, int D> struct LdsR {
+  static constexpr int LD = D + 4, LDF = 20;
+  float a[TS * LD];      // rows of dy
+  float pf[TS * LDF];    // p[t][f - f0]
+  float ph1[TS * LDF];   // phi_q[t][f - f0]
+  float ph2[TS * LDF];   // in-step sums of the exact path
+  float dd[TS * 17];     // E[t][s] = dy_t . v_s
+};
+template <typename T, int D> struct LdsV {
+  static constexpr int LD = D + 8, LDF = D + 4;
+  T a[TS * LD];          // rows of dy
+  T b[TS * LD];          // rows of phi_q
+  T c[TS * LD];          // rows of log gamma
+  float pf[TS * LDF];    // exact path: p[t][f]
+  float ph1[TS * LDF];   // exact path: phi_q[t][f]
+  float ph2[TS * LDF];   // exact path: phi_k[s][f]
+};
+
+// Role F: dphi_q for features f0 .. f0 + 15 of query head hq (see the top of the file).
+template <typename T, int D>
+__device__ void sweep_f(const BwdParams &p, LdsF<T, D> &sm, int b, int hq, int ft0) {
+  constexpr int NDT = D / 16, NKS = D / 32, LD = LdsF<T, D>::LD, LDF = LdsF<T, D>::LDF;
+  const int lane = threadIdx.x & 63, r = lane & 15, kq = lane >> 4;
+  const int L = p.L, hk = hq / p.G, f0 = 16 * ft0;
+  const size_t kvo = ((size_t)b * p.Hkv + hk) * L * D, qo = ((size_t)b * p.Hq + hq) * L * D;
+  const T *V = reinterpret_cast<const T *>(p.v) + kvo;
+  const T *LG = reinterpret_cast<const T *>(p.lg) + kvo;
+  const float *PK = p.phk + kvo;
+  const T *DY = reinterpret_cast<const T *>(p.dy) + qo;
+  float *DPQ = p.dphq + qo;
+  f32x4 S[NDT];  // S^T[dv = 16 dt + 4 kq + i][f = f0 + r]
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) S[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const F4<float> tri = tri_le<float>(r, kq);  // the sweep runs on fp32 operands
+  for (int c0 = 0; c0 < L; c0 += TS) {
+    // ---- loads: dy and v rows c0 + r (interleaved), log gamma and phi_k columns f0 + r
+    Frag<float> dyf[NKS], vf[NKS];
+    const bool rok = c0 + r < L;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      dyf[ks] = to32(row_il(DY + (size_t)(c0 + r) * D, ks, kq, rok));
+      vf[ks] = to32(row_il(V + (size_t)(c0 + r) * D, ks, kq, rok));
+    }
+    const F4<float> lgc = to32(col_g(LG, D, c0 + 4 * kq, f0 + r, L));
+    const F4<float> pkc = col_g(PK, D, c0 + 4 * kq, f0 + r, L);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) store_il(sm.a + r * LD, vf[ks], ks, kq);
+    // ---- prefix sums: pK (lane (f = f0 + r, kq): s = 4 kq + i), pQ (lane (t = r, kq): f = f0 + 4 kq + i)
+    const f32x4 pK = mma16(tri, lgc, f32x4{0.f, 0.f, 0.f, 0.f});
+    const f32x4 pQ = mma16(lgc, tri, f32x4{0.f, 0.f, 0.f, 0.f});
+    const float Pf = __shfl(pK[3], 48 + r);  // chunk total of feature f0 + r
+    const bool mild = wave_max_all(-Pf) <= MILD_SPAN;
+    // ---- D^T[s][t] = v_s . dy_t (lane (t = r, kq): s = 4 kq + i), masked to s <= t
+    f32x4 dT = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) dT = mma(vf[ks], dyf[ks], dT);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dT[i] = (4 * kq + i <= r) ? dT[i] : 0.f;
+    // ---- inter: Out^T[f][t] = sum_dv S[f][dv] dy_t[dv]
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = S[2 * ks + (j >> 2)][j & 3];
+      o = mma(frag_from<float>(x), dyf[ks], o);
+    }
+    if (mild) {
+      float kt[4], dm[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kt[j] = f4_at(pkc, j) * __expf(-pK[j]);
+        dm[j] = dT[j];
+      }
+      o = mma16(f4_from<float>(kt), f4_from<float>(dm), o);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] *= __expf(pQ[i]);
+    } else {
+      // exact: o = e^{p_t} o_inter + sum_{s <= t} D[t][s] phi_k[s][f] e^{p_t[f] - p_s[f]}
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sm.pf[(4 * kq + i) * LDF + r] = pK[i];
+        sm.ph1[(4 * kq + i) * LDF + r] = f4_at(pkc, i);
+      }
+      __syncthreads();
+      float dts[16];
+#pragma unroll
+      for (int s = 0; s < 16; ++s) dts[s] = __shfl(dT[s & 3], r + 16 * (s >> 2));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int fl = 4 * kq + i;
+        float a = o[i] * __expf(pQ[i]);
+        for (int s = 0; s <= r; ++s) a += dts[s] * sm.ph1[s * LDF + fl] * __expf(pQ[i] - sm.pf[s * LDF + fl]);
+        o[i] = a;
+      }
+      __syncthreads();
+    }
+    if (rok) {
+      *reinterpret_cast<f32x4 *>(DPQ + (size_t)(c0 + r) * D + f0 + 4 * kq) =
+          f32x4{p.mix * o[0], p.mix * o[1], p.mix * o[2], p.mix * o[3]};
+    }
+    // ---- state: S^T = e^{P} S^T + V^T Kbar, Kbar[s][f] = phi_k[s][f] e^{P - p_s[f]}
+    float kb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kb[j] = f4_at(pkc, j) * __expf(Pf - pK[j]);
+    const F4<float> kbf = f4_from<float>(kb);
+    const float eP = __expf(Pf);
+    __syncthreads();  // v rows staged
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[dt][i] *= eP;
+      S[dt] = mma16(lds_col4(sm.a, LD, 4 * kq, 16 * dt), kbf, S[dt]);
+    }
+    __syncthreads();  // v rows read before the next step overwrites them
+  }
+}
+
+// Role V: dv_gla for value columns dv0 .. dv0 + 15 of key/value head hk (sum over its query heads).
+template <typename T, int D>
+__device__ void sweep_v(const BwdParams &p, LdsV<T, D> &sm, int b, int hk, int dt0) {
+  constexpr int NFT = D / 16, NKS = D / 32, LD = LdsV<T, D>::LD, LDF = LdsV<T, D>::LDF;
+  const int lane = threadIdx.x & 63, r = lane & 15, kq = lane >> 4;
+  const int L = p.L, G = p.G, dv0 = 16 * dt0;
+  const size_t kvo = ((size_t)b * p.Hkv + hk) * L * D;
+  const T *LG = reinterpret_cast<const T *>(p.lg) + kvo;
+  const float *PK = p.phk + kvo;
+  float *DVG = p.dvg + kvo;
+  f32x4 dS[NFT];  // dS[f = 16 ft + 4 kq + i][dv = dv0 + r]
+#pragma unroll
+  for (int ft = 0; ft < NFT; ++ft) dS[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const F4<T> tri = tri_le<T>(r, kq);
+  const int nstep = (L + TS - 1) / TS;
+  for (int st = nstep - 1; st >= 0; --st) {
+    const int c0 = st * TS;
+    const bool rok = c0 + r < L;
+    // log gamma rows into LDS, then the prefix sums of every feature tile in both layouts
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) store_il(sm.c + r * LD, row_il(LG + (size_t)(c0 + r) * D, ks, kq, rok), ks, kq);
+    Frag<float> pkf[NKS];  // phi_k rows (interleaved)
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) pkf[ks] = row_il(PK + (size_t)(c0 + r) * D, ks, kq, rok);  // fp32 rows
+    __syncthreads();
+    f32x4 pQ[NFT], pK[NFT];  // pQ: lane (t = r, kq) f = 16 ft + 4 kq + i; pK: lane (f = 16 ft + r, kq) t = 4 kq + i
+    float spn = 0.f;
+#pragma unroll
+    for (int ft = 0; ft < NFT; ++ft) {
+      const F4<T> lc = lds_col4(sm.c, LD, 4 * kq, 16 * ft);
+      pQ[ft] = mma16(lc, tri, f32x4{0.f, 0.f, 0.f, 0.f});
+      pK[ft] = mma16(tri, lc, f32x4{0.f, 0.f, 0.f, 0.f});
+      spn = fmaxf(spn, -pK[ft][3]);
+    }
+    const bool mild = wave_max_all(spn) <= MILD_SPAN;
+    float Pq[NFT][4];  // every lane: P[f = 16 ft + 4 kq + i]
+#pragma unroll
+    for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Pq[ft][i] = __shfl(pQ[ft][i], 15 + 16 * kq);
+    // ---- inter: dV[s][dv] = sum_f Kbar[s][f] dS[f][dv], Kbar = phi_k e^{P - p_s}
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};  // lane (dv = dv0 + r, kq): s = 4 kq + i
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      float ka[8], sb[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int ft = 2 * ks + (j >> 2), i = j & 3;
+        ka[j] = pkf[ks].v[j] * __expf(Pq[ft][i] - pQ[ft][i]);
+        sb[j] = dS[ft][i];
+      }
+      acc = mma(frag_from<T>(ka), frag_from<T>(sb), acc);
+    }
+    if (!mild) {
+      // exact path tables: p and phi_k of the step, fp32
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.pf[r * LDF + 16 * ft + 4 * kq + i] = pQ[ft][i];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sm.ph2[r * LDF + 32 * ks + 16 * (j >> 2) + 4 * kq + (j & 3)] = pkf[ks].v[j];
+    }
+    // ---- per query head of the group: intra part, then the state update
+    for (int g = 0; g < G; ++g) {
+      const int hq = hk * G + g;
+      const size_t qo = ((size_t)b * p.Hq + hq) * L * D;
+      const float *PQ = p.phq + qo;
+      const T *DY = reinterpret_cast<const T *>(p.dy) + qo;
+      Frag<float> pqf[NKS];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        pqf[ks] = row_il(PQ + (size_t)(c0 + r) * D, ks, kq, rok);
+        store_il(sm.a + r * LD, row_il(DY + (size_t)(c0 + r) * D, ks, kq, rok), ks, kq);
+        store_il(sm.b + r * LD, from32<T>(pqf[ks]), ks, kq);
+      }
+      __syncthreads();
+      // A[t][s] (lane (s = r, kq): t = 4 kq + i), masked to t >= s
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+      if (mild) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          float qa[8], kb[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int ft = 2 * ks + (j >> 2), i = j & 3;
+            qa[j] = pqf[ks].v[j] * __expf(pQ[ft][i]);
+            kb[j] = pkf[ks].v[j] * __expf(-pQ[ft][i]);
+          }
+          a = mma(frag_from<T>(qa), frag_from<T>(kb), a);
+        }
+      } else {
+        // exact: A[t][s] = sum_f phi_q[t][f] phi_k[s][f] e^{p_t[f] - p_s[f]}
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sm.ph1[r * LDF + 32 * ks + 16 * (j >> 2) + 4 * kq + (j & 3)] = pqf[ks].v[j];
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 4 * kq + i;
+          float x = 0.f;
+          if (t >= r)
+            for (int f = 0; f < D; ++f)
+              x += sm.ph1[t * LDF + f] * sm.ph2[r * LDF + f] * __expf(sm.pf[t * LDF + f] - sm.pf[r * LDF + f]);
+          a[i] = x;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = (4 * kq + i >= r) ? a[i] : 0.f;
+      // dV[s][dv] += sum_t A[t][s] dy_t[dv]
+      const F4<T> dyc = lds_col4(sm.a, LD, 4 * kq, dv0);
+      {
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = a[i];
+        acc = mma16(f4_from<T>(x), dyc, acc);
+      }
+      // dS[f][dv] (contribution of this head, added below after the decay): Qt^T dY
+      // Qt[t][f] = phi_q[t][f] e^{p_t[f]}: columns from LDS, prefix in the pK layout
+      if (g == 0) {
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dS[ft][i] *= __expf(Pq[ft][i]);
+      }
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft) {
+        const F4<T> qc = lds_col4(sm.b, LD, 4 * kq, 16 * ft);
+        float qt[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qt[j] = f4_at(qc, j) * __expf(pK[ft][j]);
+        dS[ft] = mma16(f4_from<T>(qt), dyc, dS[ft]);
+      }
+      __syncthreads();
+    }
+    // store dV (lane (dv = dv0 + r, kq): s = c0 + 4 kq + i)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = c0 + 4 * kq + i;
+      if (s < L) DVG[(size_t)s * D + dv0 + r] = p.mix * acc[i];
+    }
+  }
+}
+
+// Role R: dphi_k for features f0 .. f0 + 15 of key/value head hk and dlg of those features.
+template <typename T, int D>
+__device__ void sweep_r(const BwdParams &p, LdsR<T, D> &sm, int b, int hk, int ft0) {
+  constexpr int NDT = D / 16, NKS = D / 32, LD = LdsR<T, D>::LD, LDF = LdsR<T, D>::LDF;
+  const int lane = threadIdx.x & 63, r = lane & 15, kq = lane >> 4;
+  const int L = p.L, G = p.G, f0 = 16 * ft0;
+  const size_t kvo = ((size_t)b * p.Hkv + hk) * L * D;
+  const T *V = reinterpret_cast<const T *>(p.v) + kvo;
+  const T *LG = reinterpret_cast<const T *>(p.lg) + kvo;
+  const float *PK = p.phk + kvo;
+  float *DPK = p.dphk + kvo;
+  T *DLG = reinterpret_cast<T *>(p.dlg) + kvo;
+  f32x4 dS[NDT];  // dS^T[dv = 16 dt + 4 kq + i][f = f0 + r]
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) dS[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const F4<float> tri = tri_le<float>(r, kq);  // the sweep runs on fp32 operands
+  float ufs[4];  // U[t][t'] = (t' >= t): lane (t = r, kq) slot j -> (4 kq + j >= r)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ufs[j] = (4 * kq + j >= r) ? 1.f : 0.f;
+  float rsum = 0.f;  // dlg of feature f0 + r summed over the later steps
+  const int nstep = (L + TS - 1) / TS;
+  for (int st = nstep - 1; st >= 0; --st) {
+    const int c0 = st * TS;
+    const bool rok = c0 + r < L;
+    Frag<float> vf[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) vf[ks] = to32(row_il(V + (size_t)(c0 + r) * D, ks, kq, rok));
+    const F4<float> lgc = to32(col_g(LG, D, c0 + 4 * kq, f0 + r, L));
+    const F4<float> pkc = col_g(PK, D, c0 + 4 * kq, f0 + r, L);
+    const f32x4 pK = mma16(tri, lgc, f32x4{0.f, 0.f, 0.f, 0.f});  // lane (f0 + r, kq): s = 4 kq + i
+    const float Pf = __shfl(pK[3], 48 + r);
+    const bool mild = wave_max_all(-Pf) <= MILD_SPAN;
+    // ---- inter: X[s][f] = sum_dv v_s[dv] dS[f][dv] (lane (f0 + r, kq): s = 4 kq + i)
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = dS[2 * ks + (j >> 2)][j & 3];
+      o = mma(vf[ks], frag_from<float>(x), o);
+    }
+    const float eP = __expf(Pf);
+    if (mild) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] *= eP;  // times e^{-p_s} below: e^{P - p_s} in all
+    }
+    float gq[4] = {0.f, 0.f, 0.f, 0.f};  // sum_g phi_q dphi_q at (t = 4 kq + i, f0 + r)
+    if (!mild) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.pf[(4 * kq + i) * LDF + r] = pK[i];
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dS[dt][i] *= eP;
+    for (int g = 0; g < G; ++g) {
+      const int hq = hk * G + g;
+      const size_t qo = ((size_t)b * p.Hq + hq) * L * D;
+      const float *PQ = p.phq + qo;
+      const T *DY = reinterpret_cast<const T *>(p.dy) + qo;
+      const float *DPQ = p.dphq + qo;
+      Frag<float> dyf[NKS];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        dyf[ks] = to32(row_il(DY + (size_t)(c0 + r) * D, ks, kq, rok));
+        store_il(sm.a + r * LD, dyf[ks], ks, kq);
+      }
+      const F4<float> pqc = col_g(PQ, D, c0 + 4 * kq, f0 + r, L);
+      float dq4[4];
+      colf_g(DPQ, D, c0 + 4 * kq, f0 + r, L, dq4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) gq[j] += f4_at(pqc, j) * dq4[j];
+      // E[t][s] = dy_t . v_s (lane (s = r, kq): t = 4 kq + i), masked to t >= s
+      f32x4 e = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) e = mma(dyf[ks], vf[ks], e);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e[i] = (4 * kq + i >= r) ? e[i] : 0.f;
+      // Qt[t][f] = phi_q[t][f] e^{p_t[f]} (lane (f0 + r, kq): t = 4 kq + j)
+      float qt[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qt[j] = f4_at(pqc, j) * __expf(pK[j]);
+      const F4<float> qtf = f4_from<float>(qt);
+      if (mild) {
+        float ea[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ea[i] = e[i];
+        // sum_t E[t][s] Qt[t][f]; times e^{-p_s} below
+        o = mma16(f4_from<float>(ea), qtf, o);
+      } else {
+        // exact: sum_{t >= s} E[t][s] phi_q[t][f] e^{p_t[f] - p_s[f]}, one exponent per term,
+        // summed over the group's query heads in ph2
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.ph1[(4 * kq + i) * LDF + r] = f4_at(pqc, i);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.dd[(4 * kq + i) * 17 + r] = e[i];
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s = 4 * kq + i;
+          float x = 0.f;
+          for (int t = s; t < TS; ++t)
+            x += sm.dd[t * 17 + s] * sm.ph1[t * LDF + r] * __expf(sm.pf[t * LDF + r] - sm.pf[s * LDF + r]);
+          sm.ph2[s * LDF + r] = (g == 0 ? 0.f : sm.ph2[s * LDF + r]) + x;
+        }
+        __syncthreads();
+      }
+      // dS^T[dv][f] += sum_t dy_t[dv] Qt[t][f]
+      __syncthreads();  // dy rows staged
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) dS[dt] = mma16(lds_col4(sm.a, LD, 4 * kq, 16 * dt), qtf, dS[dt]);
+      __syncthreads();
+    }
+    // ---- dphi_k[s][f] = mix e^{-p_s} (e^{P} X + sum_g intra)   (lane (f0 + r, kq): s = 4 kq + i)
+    float dpk[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (mild) {
+        dpk[i] = p.mix * o[i] * __expf(-pK[i]);
+      } else {  // o: the unscaled inter term
+        dpk[i] = p.mix * (o[i] * __expf(Pf - pK[i]) + sm.ph2[(4 * kq + i) * LDF + r]);
+      }
+    }
+    // ---- dlg: db[t][f] = sum_g phi_q dphi_q - phi_k dphi_k; reverse cumsum in the step (fp32 MFMA)
+    float db[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) db[i] = gq[i] - f4_at(pkc, i) * dpk[i];
+    const f32x4 cs = mma16_f32(ufs, db, f32x4{0.f, 0.f, 0.f, 0.f});  // lane (f0 + r, kq): t = 4 kq + i
+    const float tot = __shfl(cs[0], r);                              // t = 0: the step's total
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = c0 + 4 * kq + i;
+      if (s < L) {
+        DPK[(size_t)s * D + f0 + r] = dpk[i];
+        DLG[(size_t)s * D + f0 + r] = from_f<T>(cs[i] + rsum);
+      }
+    }
+    rsum += tot;
+    if (!mild) __syncthreads();
+  }
+}
+
+// One wave per block; ROLE 0: F (blocks: batch, query head, feature tile), 1: V (batch, key/value
+// head, value tile), 2: R (batch, key/value head, feature tile).
+template <typename T, int D, int ROLE>
+__global__ __launch_bounds__(64) void bwd_sweep_kernel(BwdParams p) {
+  constexpr int NT = D / 16;
+  const int tile = blockIdx.x % NT, bh = blockIdx.x / NT;
+  if constexpr (ROLE == 0) {
+    __shared__ LdsF<T, D> sm;
+    sweep_f<T, D>(p, sm, bh / p.Hq, bh % p.Hq, tile);
+  } else if constexpr (ROLE == 1) {
+    __shared__ LdsV<T, D> sm;
+    sweep_v<T, D>(p, sm, bh / p.Hkv, bh % p.Hkv, tile);
+  } else {
+    __shared__ LdsR<T, D> sm;
+    sweep_r<T, D>(p, sm, bh / p.Hkv, bh % p.Hkv, tile);
+  }
+}
+
+// ======================================================================== 4. window, query side
+// One wave per (batch, query head, run of QPW 16-query tiles).  Per tile: online max / sum over the
+// meta tile and the key tiles of the band, then D_t = sum_j p dp, ds = p (dp - D_t),
+// dq_t = scale sum_j ds K_j; the meta keys' and values' gradients accumulate over the run.
+// Logit layout: lane (t = r, kq) holds s[j = 16 u + 4 kq + i][t].
+template <typename T, int D> struct WinQLds {
+  static constexpr int LD = D + 8;
+  T k[TS * LD];    // the key tile (or meta keys), rows
+  T q[TS * LD];    // the query tile, rows
+  T dy[TS * LD];   // (1 - mix) dy of the query tile, rows
+  T pm[TS * 20];   // meta probabilities [m][t]
+  T dm[TS * 20];   // meta ds [m][t]
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void bwd_win_q_kernel(BwdParams p) {
+  constexpr int NDT = D / 16, KS = D / 32, LD = WinQLds<T, D>::LD;
+  __shared__ WinQLds<T, D> sm;
+  const int lane = threadIdx.x & 63, r = lane & 15, kq = lane >> 4;
+  const int L = p.L, W = p.W, M = p.M;
+  const int ntile = (L + TS - 1) / TS, nrun = (ntile + QPW - 1) / QPW;
+  const int bh = blockIdx.x / nrun, run = blockIdx.x % nrun;
+  const int b = bh / p.Hq, hq = bh % p.Hq, hk = hq / p.G;
+  const size_t kvo = ((size_t)b * p.Hkv + hk) * L * D, qo = (size_t)bh * L * D;
+  const T *K = reinterpret_cast<const T *>(p.k) + kvo;
+  const T *V = reinterpret_cast<const T *>(p.v) + kvo;
+  const T *Q = reinterpret_cast<const T *>(p.q) + qo;
+  const T *DY = reinterpret_cast<const T *>(p.dy) + qo;
+  const T *TK = reinterpret_cast<const T *>(p.tk) + (size_t)hk * M * D;
+  const T *TV = reinterpret_cast<const T *>(p.tv) + (size_t)hk * M * D;
+  const float sl = p.scale, wmix = 1.f - p.mix;
+  f32x4 dtk[NDT], dtv[NDT];  // meta gradients (m = 4 kq + i, e = 16 et + r)
+#pragma unroll
+  for (int et = 0; et < NDT; ++et) { dtk[et] = f32x4{0.f, 0.f, 0.f, 0.f}; dtv[et] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+  Frag<T> tkf[KS], tvf[KS];  // meta keys / values as rows m = r
+#pragma unroll
+  for (int j = 0; j < KS; ++j) {
+    tkf[j] = row_nat(TK + (size_t)r * D, j, kq, r < M);
+    tvf[j] = row_nat(TV + (size_t)r * D, j, kq, r < M);
+  }
+  for (int qt = run * QPW; qt < min(ntile, (run + 1) * QPW); ++qt) {
+    const int t0 = qt * TS, t = t0 + r;
+    const bool tok = t < L;
+    Frag<T> qf[KS], dyf[KS];
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      qf[j] = row_nat(Q + (size_t)t * D, j, kq, tok);
+      Frag<T> f = row_nat(DY + (size_t)t * D, j, kq, tok);
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = wmix * to_f(f.v[e]);
+      dyf[j] = frag_from<T>(x);
+      *reinterpret_cast<Frag<T> *>(sm.q + r * LD + 32 * j + 8 * kq) = qf[j];
+      *reinterpret_cast<Frag<T> *>(sm.dy + r * LD + 32 * j + 8 * kq) = dyf[j];
+    }
+    const int jlo = max(0, t0 - W + 1), ulo = jlo / TS, uhi = qt;
+    // logits of tile u (u = -1: meta), masked
+    auto logits = [&](int u, f32x4 &s) {
+      s = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (u < 0) {
+#pragma unroll
+        for (int j = 0; j < KS; ++j) s = mma(tkf[j], qf[j], s);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[i] = (4 * kq + i < M) ? s[i] * sl : -1.0e30f;
+      } else {
+        const int jr = TS * u + r;
+#pragma unroll
+        for (int j = 0; j < KS; ++j) s = mma(row_nat(K + (size_t)jr * D, j, kq, jr < L), qf[j], s);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int jj = TS * u + 4 * kq + i;
+          s[i] = (jj <= t && jj > t - W && jj < L) ? s[i] * sl : -1.0e30f;
+        }
+      }
+    };
+    auto dots = [&](int u, f32x4 &dp) {  // dp[j][t] = v_j . dy_w[t]
+      dp = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (u < 0) {
+#pragma unroll
+        for (int j = 0; j < KS; ++j) dp = mma(tvf[j], dyf[j], dp);
+      } else {
+        const int jr = TS * u + r;
+#pragma unroll
+        for (int j = 0; j < KS; ++j) dp = mma(row_nat(V + (size_t)jr * D, j, kq, jr < L), dyf[j], dp);
+      }
+    };
+    // pass 1: max and sum
+    float mx = -1.0e30f, sum = 0.f;
+    for (int u = -1; u <= uhi; ++u) {
+      if (u >= 0 && u < ulo) continue;
+      f32x4 s;
+      logits(u, s);
+      float m2 = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+      m2 = fmaxf(mx, wave_max_cols(m2));
+      sum *= __expf(mx - m2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sum += (s[i] > -1.0e29f) ? __expf(s[i] - m2) : 0.f;
+      mx = m2;
+    }
+    sum = wave_sum_cols(sum);
+    const float inv = 1.f / sum;
+    // pass 2: D_t = sum_j p dp
+    float dsum = 0.f;
+    for (int u = -1; u <= uhi; ++u) {
+      if (u >= 0 && u < ulo) continue;
+      f32x4 s, dp;
+      logits(u, s);
+      dots(u, dp);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dsum += (s[i] > -1.0e29f) ? __expf(s[i] - mx) * inv * dp[i] : 0.f;
+    }
+    dsum = wave_sum_cols(dsum);
+    if (tok) {
+      float *st = p.wstat + ((size_t)bh * L + t) * 4;
+      if (kq == 0) *reinterpret_cast<f32x4 *>(st) = f32x4{mx, inv, dsum, 0.f};
+    }
+    // pass 3: ds, dq, meta gradients
+    f32x4 dq[NDT];  // lane (e = 16 et + r, kq): t = 4 kq + i
+#pragma unroll
+    for (int et = 0; et < NDT; ++et) dq[et] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = -1; u <= uhi; ++u) {
+      if (u >= 0 && u < ulo) continue;
+      f32x4 s, dp;
+      logits(u, s);
+      dots(u, dp);
+      float pr[4], ds[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pr[i] = (s[i] > -1.0e29f) ? __expf(s[i] - mx) * inv : 0.f;
+        ds[i] = pr[i] * (dp[i] - dsum);
+      }
+      // the key tile's rows into LDS for the transposed operand
+      const int jr = TS * u + r;
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+        const Frag<T> kf = (u < 0) ? tkf[j] : row_nat(K + (size_t)jr * D, j, kq, jr < L);
+        *reinterpret_cast<Frag<T> *>(sm.k + r * LD + 32 * j + 8 * kq) = kf;
+      }
+      __syncthreads();
+      // dq[t][e] += scale sum_j ds[t][j] K[j][e]: A = ds (lane (t = r, kq): j = 4 kq + i)
+      const F4<T> dsa = f4_from<T>(ds);
+#pragma unroll
+      for (int et = 0; et < NDT; ++et) dq[et] = mma16(dsa, lds_col4(sm.k, LD, 4 * kq, 16 * et), dq[et]);
+      if (u < 0 && M > 0) {
+        // meta: dTk[m][e] += scale sum_t ds[m][t] q_t[e], dTv[m][e] += sum_t p[m][t] dyw_t[e]
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sm.dm[(4 * kq + i) * 20 + r] = from_f<T>(ds[i]);
+          sm.pm[(4 * kq + i) * 20 + r] = from_f<T>(pr[i]);
+        }
+        __syncthreads();
+        F4<T> da, pa;  // rows m = r, t = 4 kq + j
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { da.v[j] = sm.dm[r * 20 + 4 * kq + j]; pa.v[j] = sm.pm[r * 20 + 4 * kq + j]; }
+#pragma unroll
+        for (int et = 0; et < NDT; ++et) {
+          dtk[et] = mma16(da, lds_col4(sm.q, LD, 4 * kq, 16 * et), dtk[et]);
+          dtv[et] = mma16(pa, lds_col4(sm.dy, LD, 4 * kq, 16 * et), dtv[et]);
+        }
+      }
+      __syncthreads();
+    }
+    float *DQW = p.dqw + qo;
+#pragma unroll
+    for (int et = 0; et < NDT; ++et)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tt = t0 + 4 * kq + i;
+        if (tt < L) DQW[(size_t)tt * D + 16 * et + r] = sl * dq[et][i];
+      }
+  }
+  if (M > 0) {
+    float *PT = p.dtk_part + (size_t)blockIdx.x * 16 * D;
+    float *PV = p.dtv_part + (size_t)blockIdx.x * 16 * D;
+#pragma unroll
+    for (int et = 0; et < NDT; ++et)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        PT[(4 * kq + i) * D + 16 * et + r] = sl * dtk[et][i];
+        PV[(4 * kq + i) * D + 16 * et + r] = dtv[et][i];
+      }
+  }
+}
+
+// ======================================================================== 5. window, key side
+// One wave per (batch, key/value head, 16-key tile): for every query head of the group and every
+// query tile that sees these keys, p from the stored statistics, ds = p (dp - D_t), then
+// dk_j += scale sum_t ds[t][j] q_t and dv_j += sum_t p[t][j] dyw_t.
+// Logit layout: lane (j = r, kq) holds s[t = 16 u + 4 kq + i][j].
+template <typename T, int D>
+__global__ __launch_bounds__(64) void bwd_win_k_kernel(BwdParams p) {
+  constexpr int NDT = D / 16, KS = D / 32, LD = D + 8;
+  __shared__ __align__(16) T sq[TS * LD];
+  __shared__ __align__(16) T sdy[TS * LD];
+  const int lane = threadIdx.x & 63, r = lane & 15, kq = lane >> 4;
+  const int L = p.L, W = p.W, G = p.G;
+  const int ntile = (L + TS - 1) / TS;
+  const int bh = blockIdx.x / ntile, kt = blockIdx.x % ntile;
+  const int b = bh / p.Hkv, hk = bh % p.Hkv;
+  const size_t kvo = (size_t)bh * L * D;
+  const T *K = reinterpret_cast<const T *>(p.k) + kvo;
+  const T *V = reinterpret_cast<const T *>(p.v) + kvo;
+  const int j0 = kt * TS, j = j0 + r;
+  Frag<T> kf[KS], vf[KS];
+#pragma unroll
+  for (int x = 0; x < KS; ++x) {
+    kf[x] = row_nat(K + (size_t)j * D, x, kq, j < L);
+    vf[x] = row_nat(V + (size_t)j * D, x, kq, j < L);
+  }
+  const float sl = p.scale, wmix = 1.f - p.mix;
+  f32x4 dk[NDT], dv[NDT];  // lane (e = 16 et + r, kq): j = 4 kq + i
+#pragma unroll
+  for (int et = 0; et < NDT; ++et) { dk[et] = f32x4{0.f, 0.f, 0.f, 0.f}; dv[et] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+  const int uhi = min(ntile - 1, (j0 + TS - 1 + W - 1) / TS);
+  for (int g = 0; g < G; ++g) {
+    const int hq = hk * G + g;
+    const size_t qo = ((size_t)b * p.Hq + hq) * L * D;
+    const T *Q = reinterpret_cast<const T *>(p.q) + qo;
+    const T *DY = reinterpret_cast<const T *>(p.dy) + qo;
+    const float *ST = p.wstat + ((size_t)b * p.Hq + hq) * L * 4;
+    for (int u = kt; u <= uhi; ++u) {
+      const int t0 = u * TS, tr = t0 + r;
+      Frag<T> qf[KS], dyf[KS];
+#pragma unroll
+      for (int x = 0; x < KS; ++x) {
+        qf[x] = row_nat(Q + (size_t)tr * D, x, kq, tr < L);
+        const Frag<T> f = row_nat(DY + (size_t)tr * D, x, kq, tr < L);
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = wmix * to_f(f.v[e]);
+        dyf[x] = frag_from<T>(y);
+        *reinterpret_cast<Frag<T> *>(sq + r * LD + 32 * x + 8 * kq) = qf[x];
+        *reinterpret_cast<Frag<T> *>(sdy + r * LD + 32 * x + 8 * kq) = dyf[x];
+      }
+      f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int x = 0; x < KS; ++x) {
+        s = mma(qf[x], kf[x], s);   // s[t][j]: lane (j = r, kq) t = 4 kq + i
+        dp = mma(dyf[x], vf[x], dp);
+      }
+      float ds[4], pr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 4 * kq + i;
+        const bool ok = t < L && j < L && j <= t && j > t - W;
+        float mx = 0.f, inv = 0.f, dd = 0.f;
+        if (t < L) {
+          const f32x4 stt = *reinterpret_cast<const f32x4 *>(ST + (size_t)t * 4);
+          mx = stt[0]; inv = stt[1]; dd = stt[2];
+        }
+        pr[i] = ok ? __expf(s[i] * sl - mx) * inv : 0.f;
+        ds[i] = pr[i] * (dp[i] - dd);
+      }
+      __syncthreads();
+      const F4<T> dsa = f4_from<T>(ds), pa = f4_from<T>(pr);
+#pragma unroll
+      for (int et = 0; et < NDT; ++et) {
+        dk[et] = mma16(dsa, lds_col4(sq, LD, 4 * kq, 16 * et), dk[et]);
+        dv[et] = mma16(pa, lds_col4(sdy, LD, 4 * kq, 16 * et), dv[et]);
+      }
+      __syncthreads();
+    }
+  }
+  float *DKW = p.dkw + kvo, *DVW = p.dvw + kvo;
+#pragma unroll
+  for (int et = 0; et < NDT; ++et)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int jj = j0 + 4 * kq + i;
+      if (jj < L) {
+        DKW[(size_t)jj * D + 16 * et + r] = sl * dk[et][i];
+        DVW[(size_t)jj * D + 16 * et + r] = dv[et][i];
+      }
+    }
+}
+
+// ======================================================================== 6. feature-map backward
+// One block (4 waves) per (batch, head) of the query side (first B*Hq blocks) or the key side.
+// Per 64-row chunk: dz = phi (dphi - <phi, dphi>) (softmax) or phi_j dphi_j - phi_{h+j} dphi_{h+j}
+// (Hedgehog), dx = dz W^T + window part; the dW partial sum sum_t x_t^T dz_t accumulates over the
+// chunks in registers (wave w: rows 16 (NIT w) .. of W).  The key side also writes dv.
+template <typename T, int D, bool HH>
+__global__ __launch_bounds__(256) void bwd_fb_kernel(BwdParams p) {
+  constexpr int KS = D / 32, FC = HH ? D / 2 : D, NCT = FC / 16, NIT = D / 64, LDW = FC + 16 / (int)sizeof(T);
+  constexpr int LDX = D + 8, LDZ = FC + 8;
+  __shared__ __align__(16) T sW[D * LDW];   // W [i][c] rows
+  __shared__ __align__(16) T sX[64 * LDX];  // x rows of the chunk
+  __shared__ __align__(16) T sZ[64 * LDZ];  // dz rows of the chunk
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, kq = lane >> 4;
+  const int L = p.L;
+  const bool qside = (int)blockIdx.x < p.B * p.Hq;
+  const int bh = qside ? blockIdx.x : blockIdx.x - p.B * p.Hq;
+  const int H = qside ? p.Hq : p.Hkv, h = bh % H;
+  const T *Wsrc = reinterpret_cast<const T *>(qside ? p.wq : p.wk) + (size_t)h * p.w_stride;
+  for (int idx = tid; idx < D * FC; idx += 256) sW[(idx / FC) * LDW + idx % FC] = Wsrc[idx];
+  const size_t o = (size_t)bh * L * D;
+  const T *X = reinterpret_cast<const T *>(qside ? p.q : p.k) + o;
+  const float *PH = (qside ? p.phq : p.phk) + o;
+  const float *DPH = (qside ? p.dphq : p.dphk) + o;
+  const float *DXW = (qside ? p.dqw : p.dkw) + o;
+  T *DX = reinterpret_cast<T *>(qside ? p.dq : p.dk) + o;
+  f32x4 dw[NIT][NCT];  // dW[i = 16 (NIT w + it) + 4 kq + ii][c = 16 ct + r]
+#pragma unroll
+  for (int it = 0; it < NIT; ++it)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) dw[it][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+  for (int c0 = 0; c0 < L; c0 += 64) {
+    const int t = c0 + 16 * w + r;
+    const bool tok = t < L;
+    // phi and dphi of row t, natural columns 32 ks + 8 kq .. + 7
+    float ph[KS][8], dph[KS][8];
+    float dot = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const Frag<float> f = row_nat(PH + (size_t)t * D, ks, kq, tok);
+      const Frag<T> xf = row_nat(X + (size_t)t * D, ks, kq, tok);
+      *reinterpret_cast<Frag<T> *>(sX + (16 * w + r) * LDX + 32 * ks + 8 * kq) = xf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ph[ks][e] = f.v[e];
+        dph[ks][e] = tok ? DPH[(size_t)t * D + 32 * ks + 8 * kq + e] : 0.f;
+        dot += ph[ks][e] * dph[ks][e];
+      }
+    }
+    // dz rows (natural columns of W's FC columns)
+    Frag<T> dzf[FC / 32];
+    if constexpr (HH) {
+#pragma unroll
+      for (int ks = 0; ks < FC / 32; ++ks) {
+        float z[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] = ph[ks][e] * dph[ks][e] - ph[ks + FC / 32][e] * dph[ks + FC / 32][e];
+        dzf[ks] = frag_from<T>(z);
+      }
+    } else {
+      dot = wave_sum_cols(dot);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        float z[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] = ph[ks][e] * (dph[ks][e] - dot);
+        dzf[ks] = frag_from<T>(z);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < FC / 32; ++ks) *reinterpret_cast<Frag<T> *>(sZ + (16 * w + r) * LDZ + 32 * ks + 8 * kq) = dzf[ks];
+    // dx[t][i] = sum_c dz[t][c] W[i][c] (lane (i = 16 it + r, kq): t = 16 w + 4 kq + ii)
+#pragma unroll
+    for (int it = 0; it < D / 16; ++it) {
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < FC / 32; ++ks) a = mma(dzf[ks], load8(sW + (16 * it + r) * LDW + 32 * ks + 8 * kq), a);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int tt = c0 + 16 * w + 4 * kq + ii;
+        if (tt < L) DX[(size_t)tt * D + 16 * it + r] = from_f<T>(a[ii] + DXW[(size_t)tt * D + 16 * it + r]);
+      }
+    }
+    __syncthreads();  // x and dz rows of the chunk staged
+    // dW[i][c] += sum_t x[t][i] dz[t][c]: K = 64 rows in 16-row steps
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+      F4<T> za[NCT];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) za[ct] = lds_col4(sZ, LDZ, 16 * k4 + 4 * kq, 16 * ct);
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const F4<T> xa = lds_col4(sX, LDX, 16 * k4 + 4 * kq, 16 * (NIT * w + it));
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) dw[it][ct] = mma16(xa, za[ct], dw[it][ct]);
+      }
+    }
+    if (!qside) {  // dv = dv_gla + dv_window for the chunk's rows
+      const float *DVG = p.dvg + o, *DVW = p.dvw + o;
+      T *DV = reinterpret_cast<T *>(p.dvo) + o;
+      for (int idx = tid; idx < 64 * D; idx += 256) {
+        const int tt = c0 + idx / D;
+        if (tt < L) DV[(size_t)c0 * D + idx] = from_f<T>(DVG[(size_t)c0 * D + idx] + DVW[(size_t)c0 * D + idx]);
+      }
+    }
+    __syncthreads();
+  }
+  float *part = p.dw_part + (size_t)blockIdx.x * D * FC;
+#pragma unroll
+  for (int it = 0; it < NIT; ++it)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) part[(size_t)(16 * (NIT * w + it) + 4 * kq + ii) * FC + 16 * ct + r] = dw[it][ct][ii];
+}
+
+// ======================================================================== 7. reductions
+// dW_q (and dW_k): sum of the per-(batch, head) partials over the heads that share a matrix;
+// dT_k, dT_v: sum of the window-q partials of the key/value head's query heads.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p, int D, int FC) {
+  const size_t wsz = (size_t)D * FC;
+  const int nwq = p.w_stride ? p.Hq : 1, nwk = p.w_stride ? p.Hkv : 1;
+  const size_t nw = (size_t)(nwq + nwk) * wsz;
+  const int ntile = (p.L + TS - 1) / TS, nrun = (ntile + QPW - 1) / QPW;
+  const size_t nt = p.M > 0 ? (size_t)p.Hkv * p.M * D : 0;
+  for (size_t x = (size_t)blockIdx.x * 256 + threadIdx.x; x < nw + 2 * nt; x += (size_t)gridDim.x * 256) {
+    if (x < nw) {
+      const bool qs = x < (size_t)nwq * wsz;
+      const size_t y = qs ? x : x - (size_t)nwq * wsz;
+      const int mat = (int)(y / wsz);
+      const size_t e = y % wsz;
+      const int H = qs ? p.Hq : p.Hkv;
+      const size_t base = qs ? 0 : (size_t)p.B * p.Hq;
+      float acc = 0.f;
+      for (int b = 0; b < p.B; ++b)
+        for (int h = 0; h < H; ++h)
+          if (!p.w_stride || h == mat) acc += p.dw_part[(base + (size_t)b * H + h) * wsz + e];
+      (qs ? p.dwq : p.dwk)[y] = acc;
+    } else {
+      const size_t y = x - nw;
+      const bool kpart = y < nt;
+      const size_t z = kpart ? y : y - nt;
+      const int hk = (int)(z / ((size_t)p.M * D));
+      const int m = (int)(z / D % p.M), e = (int)(z % D);
+      float acc = 0.f;
+      for (int b = 0; b < p.B; ++b)
+        for (int g = 0; g < p.G; ++g)
+          for (int run = 0; run < nrun; ++run) {
+            const size_t blk = ((size_t)b * p.Hq + hk * p.G + g) * nrun + run;
+            acc += (kpart ? p.dtk_part : p.dtv_part)[(blk * 16 + m) * D + e];
+          }
+      (kpart ? p.dtk : p.dtv)[z] = acc;
+    }
+  }
+}
+
+// ======================================================================== host side
+size_t bwd_workspace_layout(int B, int Hq, int Hkv, int L, int d, int M, int dtype_bf16, BwdWs *ws) {
+  (void)dtype_bf16;  // every workspace array is fp32
+  const size_t nq = (size_t)B * Hq * L * d, nk = (size_t)B * Hkv * L * d;
+  const int ntile = (L + TS - 1) / TS, nrun = (ntile + QPW - 1) / QPW;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  BwdWs w{};
+  w.phq = take(nq * 4);
+  w.phk = take(nk * 4);
+  w.dphq = take(nq * 4);
+  w.dphk = take(nk * 4);
+  w.dvg = take(nk * 4);
+  w.dqw = take(nq * 4);
+  w.dkw = take(nk * 4);
+  w.dvw = take(nk * 4);
+  w.wstat = take((size_t)B * Hq * L * 16);
+  w.dw_part = take((size_t)(B * Hq + B * Hkv) * d * d * 4);
+  const size_t ntp = M > 0 ? (size_t)B * Hq * nrun * 16 * d * 4 : 0;
+  w.dtk_part = take(ntp);
+  w.dtv_part = take(ntp);
+  if (ws) *ws = w;
+  return off;
+}
+
+template <typename T, int D>
+static hipError_t launch_bwd_t(const BwdParams &p, hipStream_t st) {
+  const int ntile64 = (p.L + 63) / 64;
+  if (p.hh) hipLaunchKernelGGL((bwd_phi_kernel<T, D, true>), dim3((p.B * p.Hq + p.B * p.Hkv) * ntile64), dim3(256), 0, st, p);
+  else hipLaunchKernelGGL((bwd_phi_kernel<T, D, false>), dim3((p.B * p.Hq + p.B * p.Hkv) * ntile64), dim3(256), 0, st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nft = D / 16;
+  hipLaunchKernelGGL((bwd_sweep_kernel<T, D, 0>), dim3(p.B * p.Hq * nft), dim3(64), 0, st, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_sweep_kernel<T, D, 1>), dim3(p.B * p.Hkv * nft), dim3(64), 0, st, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int ntile = (p.L + TS - 1) / TS, nrun = (ntile + QPW - 1) / QPW;
+  hipLaunchKernelGGL((bwd_win_q_kernel<T, D>), dim3(p.B * p.Hq * nrun), dim3(64), 0, st, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_sweep_kernel<T, D, 2>), dim3(p.B * p.Hkv * nft), dim3(64), 0, st, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_win_k_kernel<T, D>), dim3(p.B * p.Hkv * ntile), dim3(64), 0, st, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (p.hh) hipLaunchKernelGGL((bwd_fb_kernel<T, D, true>), dim3(p.B * p.Hq + p.B * p.Hkv), dim3(256), 0, st, p);
+  else hipLaunchKernelGGL((bwd_fb_kernel<T, D, false>), dim3(p.B * p.Hq + p.B * p.Hkv), dim3(256), 0, st, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int FC = p.hh ? D / 2 : D;
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(512), dim3(256), 0, st, p, D, FC);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdParams &p, int dtype_bf16, int d, hipStream_t stream) {
+  if (dtype_bf16) {
+    if (d == 64) return launch_bwd_t<bf16, 64>(p, stream);
+    if (d == 128) return launch_bwd_t<bf16, 128>(p, stream);
+  } else {
+    if (d == 64) return launch_bwd_t<float, 64>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lz

@@ -72,4 +72,25 @@ hipError_t launch_decode(const DecParams &p, int dtype_bf16, int d, hipStream_t 
 namespace lz {
 int decode_max_window();
 size_t decode_workspace_bytes(int N, int Hq, int Hkv, int d);
+
+// Backward pass (bwd.hip).  Inputs as the forward's plus dy; outputs dq [B,Hq,L,d], dk, dvo,
+// dlg [B,Hkv,L,d] in the input type, dwq / dwk (shaped like W_phi) and dtk / dtv [Hkv,M,d] in fp32.
+// The workspace holds the feature maps, the fp32 feature-map gradients, the window parts and the
+// partial sums (offsets from bwd_workspace_layout).
+struct BwdParams {
+  const void *q, *k, *v, *lg, *wq, *wk, *tk, *tv, *dy;
+  void *dq, *dk, *dvo, *dlg;
+  float *dwq, *dwk, *dtk, *dtv;
+  float *phq, *phk;  // feature maps, fp32
+  float *dphq, *dphk, *dvg, *dqw, *dkw, *dvw, *wstat, *dw_part, *dtk_part, *dtv_part;
+  int64_t w_stride;  // elements between heads' W_phi; 0: one shared matrix
+  int B, Hq, Hkv, L, W, M, G;
+  int hh;            // Hedgehog feature map (W_phi [d][d/2])
+  float mix, scale;
+};
+struct BwdWs {
+  size_t phq, phk, dphq, dphk, dvg, dqw, dkw, dvw, wstat, dw_part, dtk_part, dtv_part;
+};
+size_t bwd_workspace_layout(int B, int Hq, int Hkv, int L, int d, int M, int dtype_bf16, BwdWs *ws);
+hipError_t launch_bwd(const BwdParams &p, int dtype_bf16, int d, hipStream_t stream);
 }
