@@ -231,6 +231,35 @@ def bench_decode(steps: int, warmup: int):
     return c, total_ms, per
 
 
+def bwd_algorithmic_bytes(c) -> float:
+    """Algorithmic HBM bytes of one backward call: q, dy (per query head) and k, v, log gamma (per
+    key/value head) read once; dq and dk, dv, dlog gamma written once.  Weights, meta tokens and
+    their fp32 gradients are negligible."""
+    B, Hq, Hkv, L, d = c["B"], c["Hq"], c["Hkv"], c["L"], c["d"]
+    e = 2 if c["dtype"] == "bf16" else 4
+    return float(e * d * L * B * (3 * Hq + 6 * Hkv))
+
+
+def bench_backward(steps: int, warmup: int, idx: int = 1):
+    """The backward pass over the same layer shape (dy seeded N(0, 1) in bf16)."""
+    c = WORKLOADS[idx]
+    log("[bench] generating the backward workload:", WORKLOAD_NAMES[idx])
+    inp = workload_fwd_inputs(idx)
+    g = inp.to("cuda")
+    dy = torch.randn(g.q.shape, generator=torch.Generator().manual_seed(7)).to(g.q.dtype).to("cuda")
+    need = api.lizard_attn_bwd_workspace_bytes(c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], c["M"], g.q.dtype)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+
+    def step():
+        api.lizard_attn_bwd(g.q, g.k, g.v, g.log_gamma, g.w_phi_q, g.w_phi_k, g.t_k, g.t_v, dy, W=inp.W,
+                            M=inp.M, mix=inp.mix, scale=inp.scale, workspace=ws)
+
+    wcalls, wms = clock_warmup(step, warmup)
+    log(f"[bench] backward: {wcalls} warm-up calls in {wms:.0f} ms, timing {steps} steps")
+    total_ms, per = time_launches(step, steps)
+    return c, total_ms, per, need
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -405,6 +434,7 @@ def main():
     ap.add_argument("--no-hedgehog", action="store_true",
                     help="skip the Hedgehog-map forward on the same shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward pass on the same shape")
     ap.add_argument("--pmc-run", action="store_true",
                     help="a few forward calls, a plain copy of known size and a bf16 GEMM of known flops, "
                          "for rocprofv3 counter passes")
@@ -505,6 +535,20 @@ def main():
             "roofline": {"bound": "hbm", "achieved": hach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": hach / HBM_PEAK_GBS, "kernel_ms": hms,
                          "algorithmic_bytes_per_launch": nbytes},
+        }
+        torch.cuda.empty_cache()
+    if not args.no_backward:
+        bc, btot, bper, bws = bench_backward(max(args.steps // 2, 1), args.warmup)
+        bms = statistics.median(bper)
+        bbytes = bwd_algorithmic_bytes(bc)
+        result["backward"] = {
+            "workload": WORKLOAD_NAMES[1] + " backward (dq, dk, dv, dlog_gamma, dW_phi, dT)",
+            "steps": len(bper), "ms_per_step": btot / len(bper),
+            "tokens_per_s": tokens / (btot / len(bper) * 1e-3),
+            "workspace_bytes": bws,
+            "roofline": {"bound": "hbm", "achieved": bbytes / (bms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": bbytes / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, "kernel_ms": bms,
+                         "algorithmic_bytes_per_launch": bbytes},
         }
         torch.cuda.empty_cache()
     if not args.no_decode:

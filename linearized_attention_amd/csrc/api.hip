@@ -538,6 +538,7 @@ static lizard_status bwd_impl(const void *q, const void *k, const void *v, const
   p.dkw = reinterpret_cast<float *>(w + ws.dkw); p.dvw = reinterpret_cast<float *>(w + ws.dvw);
   p.wstat = reinterpret_cast<float *>(w + ws.wstat); p.dw_part = reinterpret_cast<float *>(w + ws.dw_part);
   p.dtk_part = reinterpret_cast<float *>(w + ws.dtk_part); p.dtv_part = reinterpret_cast<float *>(w + ws.dtv_part);
+  p.dw_tmp = reinterpret_cast<float *>(w + ws.dw_tmp);
   p.w_stride = w_phi_head_stride;
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.L = L; p.W = W; p.M = M; p.G = Hq / Hkv;
   p.hh = hedgehog ? 1 : 0;

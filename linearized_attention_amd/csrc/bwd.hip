@@ -27,6 +27,11 @@
 // products are taken per element in fp32 (e.g. gamma ~ 0).  Every state update uses e^{P - p_s}
 // <= 1 and needs no split.
 //
+// Precision: roles F and R compute with products of about 16 significant bits (the hi / lo
+// bf16 split of mmx_ft and its kin; fp32 MFMAs for fp32 inputs): the log-gate gradient is a sum
+// over the whole sequence of terms whose total is exactly zero, so their errors must stay far
+// below bf16 rounding.  The feature maps are kept in fp32 for the same reason.
+//
 // MFMA conventions (common.hpp): x32 fragments for contractions over d; K = 16 fragments (F4) for
 // contractions over the 16 tokens of a step: lane (r, kq) holds A[m = r][k = 4kq + j] and
 // B[k = 4kq + j][n = r], j = 0..3, and the accumulator D[m = 4kq + i][n = r].  "Interleaved" rows:
@@ -41,6 +46,7 @@ namespace bwd {
 constexpr int TS = 16;              // tokens per sweep step / window tile
 constexpr float MILD_SPAN = 60.f;   // -P at most this for the split exponentials
 constexpr int QPW = 16;             // query tiles per wave in the window-q kernel
+constexpr int FB_CHUNKS = 8;        // 64-row chunks per block of the feature-map backward
 
 template <typename T> struct F4;
 template <> struct F4<bf16> { bf16x4 v; };
@@ -143,6 +149,58 @@ template <typename T> __device__ __forceinline__ Frag<T> from32(const Frag<float
   return frag_from<T>(x);
 }
 
+// Products where one or both operands are fp32 values that a bf16 operand would round too coarsely
+// (the sweeps' states and decayed feature maps: the log-gate gradient sums products of the sweeps'
+// outputs over whole sequences, and those sums cancel to zero overall).  With T = bf16 an fp32
+// value x is split into hi = bf16(x) and lo = bf16(x - hi), about 16 significant bits: one fp32
+// operand against an exact T operand takes two MFMAs, two fp32 operands three (the lo * lo term is
+// below 2^-16 of the product).  With T = fp32 the products are fp32 MFMAs.
+__device__ __forceinline__ bf16 hi_bf16(float x) { return (bf16)x; }
+__device__ __forceinline__ bf16 lo_bf16(float x) { return (bf16)(x - (float)(bf16)x); }
+template <typename T> __device__ __forceinline__ f32x4 mmx_ft(const float (&a)[8], const Frag<T> &b, f32x4 c) {
+  if constexpr (sizeof(T) == 2) {
+    Frag<bf16> h, l;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { h.v[j] = hi_bf16(a[j]); l.v[j] = lo_bf16(a[j]); }
+    return mma(l, b, mma(h, b, c));
+  } else {
+    return mma(frag_from<float>(a), b, c);
+  }
+}
+template <typename T> __device__ __forceinline__ f32x4 mmx_tf(const Frag<T> &a, const float (&b)[8], f32x4 c) {
+  if constexpr (sizeof(T) == 2) {
+    Frag<bf16> h, l;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { h.v[j] = hi_bf16(b[j]); l.v[j] = lo_bf16(b[j]); }
+    return mma(a, l, mma(a, h, c));
+  } else {
+    return mma(a, frag_from<float>(b), c);
+  }
+}
+template <typename T> __device__ __forceinline__ f32x4 m16_tf(const F4<T> &a, const float (&b)[4], f32x4 c) {
+  if constexpr (sizeof(T) == 2) {
+    F4<bf16> h, l;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { h.v[j] = hi_bf16(b[j]); l.v[j] = lo_bf16(b[j]); }
+    return mma16(a, l, mma16(a, h, c));
+  } else {
+    return mma16(a, f4_from<float>(b), c);
+  }
+}
+template <typename T> __device__ __forceinline__ f32x4 m16_ff(const float (&a)[4], const float (&b)[4], f32x4 c) {
+  if constexpr (sizeof(T) == 2) {
+    F4<bf16> ah, al, bh, bl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ah.v[j] = hi_bf16(a[j]); al.v[j] = lo_bf16(a[j]);
+      bh.v[j] = hi_bf16(b[j]); bl.v[j] = lo_bf16(b[j]);
+    }
+    return mma16(al, bh, mma16(ah, bl, mma16(ah, bh, c)));
+  } else {
+    return mma16(f4_from<float>(a), f4_from<float>(b), c);
+  }
+}
+
 // Constant triangles of the in-step prefix sums: lane (r, kq) slot j -> (4 kq + j <= r).
 template <typename T> __device__ __forceinline__ F4<T> tri_le(int r, int kq) {
   float x[4];
@@ -208,14 +266,14 @@ __global__ __launch_bounds__(256) void bwd_phi_kernel(BwdParams p) {
 // Wave-private LDS tiles of a step: T rows of 16 tokens (8-byte aligned transposed reads), and
 // fp32 tables of the exact path (16 tokens x the features the wave handles).
 template <typename T, int D> struct LdsF {
-  static constexpr int LD = D + 4, LDF = 20;
-  float a[TS * LD];      // rows of v
+  static constexpr int LD = D + 8, LDF = 20;
+  T a[TS * LD];          // rows of v
   float pf[TS * LDF];    // p[s][f - f0]
   float ph1[TS * LDF];   // phi_k[s][f - f0]
 };
 template <typename T, int D> struct LdsR {
-  static constexpr int LD = D + 4, LDF = 20;
-  float a[TS * LD];      // rows of dy
+  static constexpr int LD = D + 8, LDF = 20;
+  T a[TS * LD];          // rows of dy
   float pf[TS * LDF];    // p[t][f - f0]
   float ph1[TS * LDF];   // phi_q[t][f - f0]
   float ph2[TS * LDF];   // in-step sums of the exact path
@@ -246,18 +304,34 @@ __device__ void sweep_f(const BwdParams &p, LdsF<T, D> &sm, int b, int hq, int f
   f32x4 S[NDT];  // S^T[dv = 16 dt + 4 kq + i][f = f0 + r]
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) S[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const F4<float> tri = tri_le<float>(r, kq);  // the sweep runs on fp32 operands
+  const F4<T> tri = tri_le<T>(r, kq);
+  // a step's loads: dy and v rows c0 + r (interleaved), log gamma and phi_k columns f0 + r; the
+  // next step's are in flight while this one is computed
+  Frag<T> dyr[NKS], vr[NKS];
+  F4<T> lgr;
+  F4<float> pkr;
+  auto load_step = [&](int c0) {
+    const bool ok = c0 + r < L;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      dyr[ks] = row_il(DY + (size_t)(c0 + r) * D, ks, kq, ok);
+      vr[ks] = row_il(V + (size_t)(c0 + r) * D, ks, kq, ok);
+    }
+    lgr = col_g(LG, D, c0 + 4 * kq, f0 + r, L);
+    pkr = col_g(PK, D, c0 + 4 * kq, f0 + r, L);
+  };
+  load_step(0);
   for (int c0 = 0; c0 < L; c0 += TS) {
-    // ---- loads: dy and v rows c0 + r (interleaved), log gamma and phi_k columns f0 + r
-    Frag<float> dyf[NKS], vf[NKS];
+    Frag<T> dyf[NKS], vf[NKS];
     const bool rok = c0 + r < L;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      dyf[ks] = to32(row_il(DY + (size_t)(c0 + r) * D, ks, kq, rok));
-      vf[ks] = to32(row_il(V + (size_t)(c0 + r) * D, ks, kq, rok));
+      dyf[ks] = dyr[ks];
+      vf[ks] = vr[ks];
     }
-    const F4<float> lgc = to32(col_g(LG, D, c0 + 4 * kq, f0 + r, L));
-    const F4<float> pkc = col_g(PK, D, c0 + 4 * kq, f0 + r, L);
+    const F4<T> lgc = lgr;
+    const F4<float> pkc = pkr;
+    if (c0 + TS < L) load_step(c0 + TS);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) store_il(sm.a + r * LD, vf[ks], ks, kq);
     // ---- prefix sums: pK (lane (f = f0 + r, kq): s = 4 kq + i), pQ (lane (t = r, kq): f = f0 + 4 kq + i)
@@ -278,7 +352,7 @@ __device__ void sweep_f(const BwdParams &p, LdsF<T, D> &sm, int b, int hq, int f
       float x[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) x[j] = S[2 * ks + (j >> 2)][j & 3];
-      o = mma(frag_from<float>(x), dyf[ks], o);
+      o = mmx_ft<T>(x, dyf[ks], o);
     }
     if (mild) {
       float kt[4], dm[4];
@@ -287,7 +361,7 @@ __device__ void sweep_f(const BwdParams &p, LdsF<T, D> &sm, int b, int hq, int f
         kt[j] = f4_at(pkc, j) * __expf(-pK[j]);
         dm[j] = dT[j];
       }
-      o = mma16(f4_from<float>(kt), f4_from<float>(dm), o);
+      o = m16_ff<T>(kt, dm, o);
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] *= __expf(pQ[i]);
     } else {
@@ -318,14 +392,13 @@ __device__ void sweep_f(const BwdParams &p, LdsF<T, D> &sm, int b, int hq, int f
     float kb[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) kb[j] = f4_at(pkc, j) * __expf(Pf - pK[j]);
-    const F4<float> kbf = f4_from<float>(kb);
     const float eP = __expf(Pf);
     __syncthreads();  // v rows staged
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) S[dt][i] *= eP;
-      S[dt] = mma16(lds_col4(sm.a, LD, 4 * kq, 16 * dt), kbf, S[dt]);
+      S[dt] = m16_tf<T>(lds_col4(sm.a, LD, 4 * kq, 16 * dt), kb, S[dt]);
     }
     __syncthreads();  // v rows read before the next step overwrites them
   }
@@ -492,20 +565,42 @@ __device__ void sweep_r(const BwdParams &p, LdsR<T, D> &sm, int b, int hk, int f
   f32x4 dS[NDT];  // dS^T[dv = 16 dt + 4 kq + i][f = f0 + r]
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) dS[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const F4<float> tri = tri_le<float>(r, kq);  // the sweep runs on fp32 operands
+  const F4<T> tri = tri_le<T>(r, kq);
   float ufs[4];  // U[t][t'] = (t' >= t): lane (t = r, kq) slot j -> (4 kq + j >= r)
 #pragma unroll
   for (int j = 0; j < 4; ++j) ufs[j] = (4 * kq + j >= r) ? 1.f : 0.f;
   float rsum = 0.f;  // dlg of feature f0 + r summed over the later steps
   const int nstep = (L + TS - 1) / TS;
+  // loads of a step (v rows, log gamma and phi_k columns) and of a (step, query head) pair (dy
+  // rows, phi_q and dphi_q columns): the next ones are in flight while the current ones are used
+  Frag<T> vr[NKS], dyr[NKS];
+  F4<T> lgr;
+  F4<float> pkr, pqr;
+  float dqr[4];
+  auto load_step = [&](int c0) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) vr[ks] = row_il(V + (size_t)(c0 + r) * D, ks, kq, c0 + r < L);
+    lgr = col_g(LG, D, c0 + 4 * kq, f0 + r, L);
+    pkr = col_g(PK, D, c0 + 4 * kq, f0 + r, L);
+  };
+  auto load_head = [&](int c0, int g) {
+    const size_t qo = ((size_t)b * p.Hq + hk * G + g) * L * D;
+    const T *DY = reinterpret_cast<const T *>(p.dy) + qo;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) dyr[ks] = row_il(DY + (size_t)(c0 + r) * D, ks, kq, c0 + r < L);
+    pqr = col_g(p.phq + qo, D, c0 + 4 * kq, f0 + r, L);
+    colf_g(p.dphq + qo, D, c0 + 4 * kq, f0 + r, L, dqr);
+  };
+  load_step((nstep - 1) * TS);
+  load_head((nstep - 1) * TS, 0);
   for (int st = nstep - 1; st >= 0; --st) {
     const int c0 = st * TS;
-    const bool rok = c0 + r < L;
-    Frag<float> vf[NKS];
+    Frag<T> vf[NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) vf[ks] = to32(row_il(V + (size_t)(c0 + r) * D, ks, kq, rok));
-    const F4<float> lgc = to32(col_g(LG, D, c0 + 4 * kq, f0 + r, L));
-    const F4<float> pkc = col_g(PK, D, c0 + 4 * kq, f0 + r, L);
+    for (int ks = 0; ks < NKS; ++ks) vf[ks] = vr[ks];
+    const F4<T> lgc = lgr;
+    const F4<float> pkc = pkr;
+    if (st > 0) load_step(c0 - TS);
     const f32x4 pK = mma16(tri, lgc, f32x4{0.f, 0.f, 0.f, 0.f});  // lane (f0 + r, kq): s = 4 kq + i
     const float Pf = __shfl(pK[3], 48 + r);
     const bool mild = wave_max_all(-Pf) <= MILD_SPAN;
@@ -516,7 +611,7 @@ __device__ void sweep_r(const BwdParams &p, LdsR<T, D> &sm, int b, int hk, int f
       float x[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) x[j] = dS[2 * ks + (j >> 2)][j & 3];
-      o = mma(vf[ks], frag_from<float>(x), o);
+      o = mmx_tf<T>(vf[ks], x, o);
     }
     const float eP = __expf(Pf);
     if (mild) {
@@ -533,20 +628,18 @@ __device__ void sweep_r(const BwdParams &p, LdsR<T, D> &sm, int b, int hk, int f
 #pragma unroll
       for (int i = 0; i < 4; ++i) dS[dt][i] *= eP;
     for (int g = 0; g < G; ++g) {
-      const int hq = hk * G + g;
-      const size_t qo = ((size_t)b * p.Hq + hq) * L * D;
-      const float *PQ = p.phq + qo;
-      const T *DY = reinterpret_cast<const T *>(p.dy) + qo;
-      const float *DPQ = p.dphq + qo;
-      Frag<float> dyf[NKS];
+      Frag<T> dyf[NKS];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        dyf[ks] = to32(row_il(DY + (size_t)(c0 + r) * D, ks, kq, rok));
+        dyf[ks] = dyr[ks];
         store_il(sm.a + r * LD, dyf[ks], ks, kq);
       }
-      const F4<float> pqc = col_g(PQ, D, c0 + 4 * kq, f0 + r, L);
+      const F4<float> pqc = pqr;
       float dq4[4];
-      colf_g(DPQ, D, c0 + 4 * kq, f0 + r, L, dq4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dq4[j] = dqr[j];
+      if (g + 1 < G) load_head(c0, g + 1);
+      else if (st > 0) load_head(c0 - TS, 0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) gq[j] += f4_at(pqc, j) * dq4[j];
       // E[t][s] = dy_t . v_s (lane (s = r, kq): t = 4 kq + i), masked to t >= s
@@ -559,13 +652,12 @@ __device__ void sweep_r(const BwdParams &p, LdsR<T, D> &sm, int b, int hk, int f
       float qt[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) qt[j] = f4_at(pqc, j) * __expf(pK[j]);
-      const F4<float> qtf = f4_from<float>(qt);
       if (mild) {
         float ea[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) ea[i] = e[i];
         // sum_t E[t][s] Qt[t][f]; times e^{-p_s} below
-        o = mma16(f4_from<float>(ea), qtf, o);
+        o = m16_ff<T>(ea, qt, o);
       } else {
         // exact: sum_{t >= s} E[t][s] phi_q[t][f] e^{p_t[f] - p_s[f]}, one exponent per term,
         // summed over the group's query heads in ph2
@@ -587,7 +679,7 @@ __device__ void sweep_r(const BwdParams &p, LdsR<T, D> &sm, int b, int hk, int f
       // dS^T[dv][f] += sum_t dy_t[dv] Qt[t][f]
       __syncthreads();  // dy rows staged
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) dS[dt] = mma16(lds_col4(sm.a, LD, 4 * kq, 16 * dt), qtf, dS[dt]);
+      for (int dt = 0; dt < NDT; ++dt) dS[dt] = m16_tf<T>(lds_col4(sm.a, LD, 4 * kq, 16 * dt), qt, dS[dt]);
       __syncthreads();
     }
     // ---- dphi_k[s][f] = mix e^{-p_s} (e^{P} X + sum_g intra)   (lane (f0 + r, kq): s = 4 kq + i)
@@ -914,10 +1006,11 @@ __global__ __launch_bounds__(64) void bwd_win_k_kernel(BwdParams p) {
 }
 
 // ======================================================================== 6. feature-map backward
-// One block (4 waves) per (batch, head) of the query side (first B*Hq blocks) or the key side.
-// Per 64-row chunk: dz = phi (dphi - <phi, dphi>) (softmax) or phi_j dphi_j - phi_{h+j} dphi_{h+j}
-// (Hedgehog), dx = dz W^T + window part; the dW partial sum sum_t x_t^T dz_t accumulates over the
-// chunks in registers (wave w: rows 16 (NIT w) .. of W).  The key side also writes dv.
+// One block (4 waves) per (batch, head, run of FB_CHUNKS 64-row chunks) of the query side (first
+// B*Hq*nsplit blocks) or the key side.  Per chunk: dz = phi (dphi - <phi, dphi>) (softmax) or
+// phi_j dphi_j - phi_{h+j} dphi_{h+j} (Hedgehog), dx = dz W^T + window part; the dW partial sum
+// sum_t x_t^T dz_t accumulates over the run in registers (wave w: rows 16 (NIT w) .. of W) and is
+// written per block.  The key side also writes dv.
 template <typename T, int D, bool HH>
 __global__ __launch_bounds__(256) void bwd_fb_kernel(BwdParams p) {
   constexpr int KS = D / 32, FC = HH ? D / 2 : D, NCT = FC / 16, NIT = D / 64, LDW = FC + 16 / (int)sizeof(T);
@@ -927,8 +1020,10 @@ __global__ __launch_bounds__(256) void bwd_fb_kernel(BwdParams p) {
   __shared__ __align__(16) T sZ[64 * LDZ];  // dz rows of the chunk
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, kq = lane >> 4;
   const int L = p.L;
-  const bool qside = (int)blockIdx.x < p.B * p.Hq;
-  const int bh = qside ? blockIdx.x : blockIdx.x - p.B * p.Hq;
+  const int nsplit = (L + 64 * FB_CHUNKS - 1) / (64 * FB_CHUNKS);
+  const bool qside = (int)blockIdx.x < p.B * p.Hq * nsplit;
+  const int bid = qside ? blockIdx.x : blockIdx.x - p.B * p.Hq * nsplit;
+  const int bh = bid / nsplit, split = bid % nsplit;
   const int H = qside ? p.Hq : p.Hkv, h = bh % H;
   const T *Wsrc = reinterpret_cast<const T *>(qside ? p.wq : p.wk) + (size_t)h * p.w_stride;
   for (int idx = tid; idx < D * FC; idx += 256) sW[(idx / FC) * LDW + idx % FC] = Wsrc[idx];
@@ -944,7 +1039,7 @@ __global__ __launch_bounds__(256) void bwd_fb_kernel(BwdParams p) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) dw[it][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   __syncthreads();
-  for (int c0 = 0; c0 < L; c0 += 64) {
+  for (int c0 = 64 * FB_CHUNKS * split; c0 < min(L, 64 * FB_CHUNKS * (split + 1)); c0 += 64) {
     const int t = c0 + 16 * w + r;
     const bool tok = t < L;
     // phi and dphi of row t, natural columns 32 ks + 8 kq .. + 7
@@ -953,12 +1048,13 @@ __global__ __launch_bounds__(256) void bwd_fb_kernel(BwdParams p) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const Frag<float> f = row_nat(PH + (size_t)t * D, ks, kq, tok);
+      const Frag<float> df = row_nat(DPH + (size_t)t * D, ks, kq, tok);
       const Frag<T> xf = row_nat(X + (size_t)t * D, ks, kq, tok);
       *reinterpret_cast<Frag<T> *>(sX + (16 * w + r) * LDX + 32 * ks + 8 * kq) = xf;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         ph[ks][e] = f.v[e];
-        dph[ks][e] = tok ? DPH[(size_t)t * D + 32 * ks + 8 * kq + e] : 0.f;
+        dph[ks][e] = df.v[e];
         dot += ph[ks][e] * dph[ks][e];
       }
     }
@@ -1010,12 +1106,16 @@ __global__ __launch_bounds__(256) void bwd_fb_kernel(BwdParams p) {
         for (int ct = 0; ct < NCT; ++ct) dw[it][ct] = mma16(xa, za[ct], dw[it][ct]);
       }
     }
-    if (!qside) {  // dv = dv_gla + dv_window for the chunk's rows
+    if (!qside) {  // dv = dv_gla + dv_window for the chunk's rows, 4 elements per thread and step
       const float *DVG = p.dvg + o, *DVW = p.dvw + o;
       T *DV = reinterpret_cast<T *>(p.dvo) + o;
-      for (int idx = tid; idx < 64 * D; idx += 256) {
+      for (int idx = 4 * tid; idx < 64 * D; idx += 4 * 256) {
         const int tt = c0 + idx / D;
-        if (tt < L) DV[(size_t)c0 * D + idx] = from_f<T>(DVG[(size_t)c0 * D + idx] + DVW[(size_t)c0 * D + idx]);
+        if (tt < L) {
+          const f32x4 a = *reinterpret_cast<const f32x4 *>(DVG + (size_t)c0 * D + idx);
+          const f32x4 bb = *reinterpret_cast<const f32x4 *>(DVW + (size_t)c0 * D + idx);
+          store4<T>(DV + (size_t)c0 * D + idx, a[0] + bb[0], a[1] + bb[1], a[2] + bb[2], a[3] + bb[3]);
+        }
       }
     }
     __syncthreads();
@@ -1030,27 +1130,44 @@ __global__ __launch_bounds__(256) void bwd_fb_kernel(BwdParams p) {
 }
 
 // ======================================================================== 7. reductions
-// dW_q (and dW_k): sum of the per-(batch, head) partials over the heads that share a matrix;
-// dT_k, dT_v: sum of the window-q partials of the key/value head's query heads.
-__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p, int D, int FC) {
+// dW_q (and dW_k): sum of the per-block partials over the heads that share a matrix, in two stages
+// with a fixed order (deterministic): stage 0 sums the partials of group g (partial index % RG == g)
+// into tmp[g], stage 1 sums tmp over the groups.  dT_k, dT_v (stage 1): sum of the window-q
+// partials of the key/value head's query heads.
+constexpr int RG = 32;
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p, int D, int FC, int stage) {
   const size_t wsz = (size_t)D * FC;
   const int nwq = p.w_stride ? p.Hq : 1, nwk = p.w_stride ? p.Hkv : 1;
   const size_t nw = (size_t)(nwq + nwk) * wsz;
   const int ntile = (p.L + TS - 1) / TS, nrun = (ntile + QPW - 1) / QPW;
+  const int nsplit = (p.L + 64 * FB_CHUNKS - 1) / (64 * FB_CHUNKS);
   const size_t nt = p.M > 0 ? (size_t)p.Hkv * p.M * D : 0;
+  if (stage == 0) {
+    const size_t x = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const int grp = blockIdx.y;
+    if (x >= nw) return;
+    const bool qs = x < (size_t)nwq * wsz;
+    const size_t y = qs ? x : x - (size_t)nwq * wsz;
+    const int mat = (int)(y / wsz);
+    const size_t e = y % wsz;
+    const int H = qs ? p.Hq : p.Hkv;
+    const size_t base = qs ? 0 : (size_t)p.B * p.Hq * nsplit;
+    const int hlo = p.w_stride ? mat : 0, hhi = p.w_stride ? mat + 1 : H;
+    float acc = 0.f;
+    int idx = 0;  // running index of the partials of this output element
+    for (int b = 0; b < p.B; ++b)
+      for (int h = hlo; h < hhi; ++h)
+        for (int sp = 0; sp < nsplit; ++sp, ++idx)
+          if (idx % RG == grp) acc += p.dw_part[(base + ((size_t)b * H + h) * nsplit + sp) * wsz + e];
+    p.dw_tmp[(size_t)grp * nw + x] = acc;
+    return;
+  }
   for (size_t x = (size_t)blockIdx.x * 256 + threadIdx.x; x < nw + 2 * nt; x += (size_t)gridDim.x * 256) {
     if (x < nw) {
-      const bool qs = x < (size_t)nwq * wsz;
-      const size_t y = qs ? x : x - (size_t)nwq * wsz;
-      const int mat = (int)(y / wsz);
-      const size_t e = y % wsz;
-      const int H = qs ? p.Hq : p.Hkv;
-      const size_t base = qs ? 0 : (size_t)p.B * p.Hq;
       float acc = 0.f;
-      for (int b = 0; b < p.B; ++b)
-        for (int h = 0; h < H; ++h)
-          if (!p.w_stride || h == mat) acc += p.dw_part[(base + (size_t)b * H + h) * wsz + e];
-      (qs ? p.dwq : p.dwk)[y] = acc;
+      for (int g = 0; g < RG; ++g) acc += p.dw_tmp[(size_t)g * nw + x];
+      if (x < (size_t)nwq * wsz) p.dwq[x] = acc;
+      else p.dwk[x - (size_t)nwq * wsz] = acc;
     } else {
       const size_t y = x - nw;
       const bool kpart = y < nt;
@@ -1090,10 +1207,12 @@ size_t bwd_workspace_layout(int B, int Hq, int Hkv, int L, int d, int M, int dty
   w.dkw = take(nk * 4);
   w.dvw = take(nk * 4);
   w.wstat = take((size_t)B * Hq * L * 16);
-  w.dw_part = take((size_t)(B * Hq + B * Hkv) * d * d * 4);
+  const int nsplit = (L + 64 * FB_CHUNKS - 1) / (64 * FB_CHUNKS);
+  w.dw_part = take((size_t)(B * Hq + B * Hkv) * nsplit * d * d * 4);
   const size_t ntp = M > 0 ? (size_t)B * Hq * nrun * 16 * d * 4 : 0;
   w.dtk_part = take(ntp);
   w.dtv_part = take(ntp);
+  w.dw_tmp = take((size_t)RG * (Hq + Hkv) * d * d * 4);  // (per-head W_phi: the larger layout)
   if (ws) *ws = w;
   return off;
 }
@@ -1117,11 +1236,16 @@ static hipError_t launch_bwd_t(const BwdParams &p, hipStream_t st) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_win_k_kernel<T, D>), dim3(p.B * p.Hkv * ntile), dim3(64), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (p.hh) hipLaunchKernelGGL((bwd_fb_kernel<T, D, true>), dim3(p.B * p.Hq + p.B * p.Hkv), dim3(256), 0, st, p);
-  else hipLaunchKernelGGL((bwd_fb_kernel<T, D, false>), dim3(p.B * p.Hq + p.B * p.Hkv), dim3(256), 0, st, p);
+  const int nsplit = (p.L + 64 * FB_CHUNKS - 1) / (64 * FB_CHUNKS);
+  const dim3 fbgrid((p.B * p.Hq + p.B * p.Hkv) * nsplit);
+  if (p.hh) hipLaunchKernelGGL((bwd_fb_kernel<T, D, true>), fbgrid, dim3(256), 0, st, p);
+  else hipLaunchKernelGGL((bwd_fb_kernel<T, D, false>), fbgrid, dim3(256), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int FC = p.hh ? D / 2 : D;
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(512), dim3(256), 0, st, p, D, FC);
+  const size_t nw = (size_t)((p.w_stride ? p.Hq : 1) + (p.w_stride ? p.Hkv : 1)) * D * FC;
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((nw + 255) / 256), RG), dim3(256), 0, st, p, D, FC, 0);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(512), dim3(256), 0, st, p, D, FC, 1);
   return hipGetLastError();
 }
 

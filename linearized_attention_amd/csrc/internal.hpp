@@ -82,14 +82,14 @@ struct BwdParams {
   void *dq, *dk, *dvo, *dlg;
   float *dwq, *dwk, *dtk, *dtv;
   float *phq, *phk;  // feature maps, fp32
-  float *dphq, *dphk, *dvg, *dqw, *dkw, *dvw, *wstat, *dw_part, *dtk_part, *dtv_part;
+  float *dphq, *dphk, *dvg, *dqw, *dkw, *dvw, *wstat, *dw_part, *dtk_part, *dtv_part, *dw_tmp;
   int64_t w_stride;  // elements between heads' W_phi; 0: one shared matrix
   int B, Hq, Hkv, L, W, M, G;
   int hh;            // Hedgehog feature map (W_phi [d][d/2])
   float mix, scale;
 };
 struct BwdWs {
-  size_t phq, phk, dphq, dphk, dvg, dqw, dkw, dvw, wstat, dw_part, dtk_part, dtv_part;
+  size_t phq, phk, dphq, dphk, dvg, dqw, dkw, dvw, wstat, dw_part, dtk_part, dtv_part, dw_tmp;
 };
 size_t bwd_workspace_layout(int B, int Hq, int Hkv, int L, int d, int M, int dtype_bf16, BwdWs *ws);
 hipError_t launch_bwd(const BwdParams &p, int dtype_bf16, int d, hipStream_t stream);
