@@ -260,6 +260,26 @@ def bench_backward(steps: int, warmup: int, idx: int = 1):
     return c, total_ms, per, need
 
 
+def bench_gla(steps: int, warmup: int, idx: int = 1):
+    """The global branch alone (lizard_gla_fwd) over the same layer shape in both intra-chunk
+    forms: the standard secondary-chunked one with fp32 diagonal blocks and the reparameterized
+    one.  Returns per-mode (total ms, per-launch ms)."""
+    c = WORKLOADS[idx]
+    log("[bench] generating the GLA-only workload:", WORKLOAD_NAMES[idx])
+    inp = workload_fwd_inputs(idx)
+    g = inp.to("cuda")
+    out = torch.empty_like(g.q)
+    res = {}
+    for mode in ("standard", "reparam"):
+        def step(mode=mode):
+            api.lizard_gla_fwd(g.q, g.k, g.v, g.log_gamma, g.w_phi_q, mode=mode, out=out)
+
+        wcalls, wms = clock_warmup(step, warmup)
+        log(f"[bench] gla {mode}: {wcalls} warm-up calls in {wms:.0f} ms, timing {steps} steps")
+        res[mode] = time_launches(step, steps)
+    return c, res
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -435,6 +455,8 @@ def main():
                     help="skip the Hedgehog-map forward on the same shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward pass on the same shape")
+    ap.add_argument("--no-gla", action="store_true",
+                    help="skip the standard / reparameterized GLA-only forwards on the same shape")
     ap.add_argument("--pmc-run", action="store_true",
                     help="a few forward calls, a plain copy of known size and a bf16 GEMM of known flops, "
                          "for rocprofv3 counter passes")
@@ -535,6 +557,21 @@ def main():
             "roofline": {"bound": "hbm", "achieved": hach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": hach / HBM_PEAK_GBS, "kernel_ms": hms,
                          "algorithmic_bytes_per_launch": nbytes},
+        }
+        torch.cuda.empty_cache()
+    if not args.no_gla:
+        gc, gres = bench_gla(max(args.steps // 2, 1), args.warmup)
+        fwd_ms = statistics.median(per)
+        gms = {m: statistics.median(p) for m, (t, p) in gres.items()}
+        result["gla"] = {
+            "workload": WORKLOAD_NAMES[1] + " global branch only (mix = 1, no window)",
+            "steps": len(gres["standard"][1]),
+            "standard_ms": gms["standard"], "reparam_ms": gms["reparam"], "lizard_fwd_ms": fwd_ms,
+            "standard_tokens_per_s": tokens / (gms["standard"] * 1e-3),
+            "reparam_tokens_per_s": tokens / (gms["reparam"] * 1e-3),
+            "standard_over_reparam": gms["standard"] / gms["reparam"],
+            "standard_over_lizard_fwd": gms["standard"] / fwd_ms,
+            "timing": "median per-launch HIP-event time, inputs resident, after a clock warm-up",
         }
         torch.cuda.empty_cache()
     if not args.no_backward:

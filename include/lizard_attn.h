@@ -357,6 +357,36 @@ lizard_status lizard_set_option(const char *name, int value);
 /* Current value of an option (0 for an unknown name). */
 int lizard_get_option(const char *name);
 
+/*
+ * The global (gated-linear-attention) branch alone, for measuring the Lizard
+ * paper's reparameterization against the standard chunked algorithm on the
+ * same hardware (arXiv page, Method: the standard parallel form keeps its
+ * per-element decays in fp32 and so off the matrix cores; Efficiency: the
+ * reparameterized forward is reported 32-36% faster):
+ *   out_t = sum_{s <= t} sum_f phi(q_t)_f phi(k_s)_f
+ *           exp(sum_{s < u <= t} log_gamma_u,f) v_s,
+ * the recurrence h_t = gamma_t (.) h_{t-1} + phi(k_t) v_t^T, out_t = phi(q_t)^T h_t
+ * of lizard_attn_fwd without the window (its output at mix = 1).
+ *   q [B, Hq, L, d]; k, v, log_gamma [B, Hkv, L, d]; out [B, Hq, L, d]
+ *   w_phi      [d, d], one matrix for queries, keys and heads; the softmax
+ *              over features of x . W_phi
+ *   mode       0: standard -- 16-token sub-chunks; blocks below the diagonal
+ *              on bf16 matrix products with decays referred to sub-chunk
+ *              ends (all factors <= 1), the diagonal blocks element by element
+ *              in fp32, one exponential per (query, key, feature);
+ *              1: reparameterized -- decays referred to the 64-token chunk
+ *              start, the whole masked intra-chunk product on bf16 matrix
+ *              products (a chunk whose log decay passes 60 in some feature is
+ *              done the standard way).
+ * Built for bf16 and d = 128 only (else LIZARD_ERR_UNSUPPORTED); Hq a multiple
+ * of Hkv; all pointers device memory, 16-byte aligned, owned by the caller;
+ * no workspace.  B = 0 or L = 0: OK, nothing launched.
+ */
+lizard_status lizard_gla_fwd(const void *q, const void *k, const void *v,
+                             const void *log_gamma, const void *w_phi,
+                             void *out, int B, int Hq, int Hkv, int L, int d,
+                             int mode, lizard_dtype dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ EXPORTED = ("lizard_attn_fwd", "lizard_attn_fwd_workspace_bytes", "lizard_attn_f
             "lizard_attn_decode_hedgehog", "lizard_attn_decode_workspace_bytes",
             "lizard_status_string", "lizard_last_error", "lizard_version", "lizard_set_option",
             "lizard_get_option", "lizard_attn_decode_noalloc", "lizard_attn_bwd",
-            "lizard_attn_bwd_hedgehog", "lizard_attn_bwd_workspace_bytes")
+            "lizard_attn_bwd_hedgehog", "lizard_attn_bwd_workspace_bytes", "lizard_gla_fwd")
 
 _lock = threading.Lock()
 _lib = None
@@ -71,6 +71,8 @@ def _declare(lib):
     lib.lizard_attn_bwd_hedgehog.restype = i32
     lib.lizard_attn_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.lizard_attn_bwd_workspace_bytes.restype = sz
+    lib.lizard_gla_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
+    lib.lizard_gla_fwd.restype = i32
     lib.lizard_attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.lizard_attn_decode_workspace_bytes.restype = sz
     lib.lizard_status_string.argtypes = [i32]
@@ -431,6 +433,34 @@ def lizard_attn_bwd(q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v, dy, *, W: in
         _ptr(out["dwk"]), _ptr(out["dtk"]) if M > 0 else None, _ptr(out["dtv"]) if M > 0 else None,
         B, Hq, Hkv, L, d, W, M, float(mix), float(scale), _DTYPES[dt], _ptr(workspace), wbytes,
         _stream(stream)))
+    return out
+
+
+GLA_MODES = {"standard": 0, "reparam": 1}
+
+
+def lizard_gla_fwd(q, k, v, log_gamma, w_phi, *, mode: str = "standard", out=None, stream=None):
+    """The gated-linear-attention branch alone (lizard_attn_fwd's output at mix = 1): q
+    [B,Hq,L,d]; k, v, log_gamma [B,Hkv,L,d]; w_phi [d,d] shared by queries, keys and heads.
+    mode "standard": secondary chunking with fp32 diagonal blocks; "reparam": the whole
+    intra-chunk product on matrix cores.  bf16, d = 128."""
+    if mode not in GLA_MODES:
+        raise ValueError(f"mode must be one of {sorted(GLA_MODES)}")
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (log_gamma, "log_gamma"), (w_phi, "w_phi")):
+        _dev(t, n, dt)
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, L, d) or v.shape != k.shape or log_gamma.shape != k.shape:
+        raise ValueError("k, v, log_gamma must be [B,Hkv,L,d] matching q")
+    if w_phi.shape != (d, d):
+        raise ValueError(f"w_phi must be [{d},{d}]")
+    _same_device(q.device, (k, "k"), (v, "v"), (log_gamma, "log_gamma"), (w_phi, "w_phi"))
+    out = _out(out, q)
+    _check(load().lizard_gla_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), _ptr(w_phi), _ptr(out),
+                                 B, Hq, Hkv, L, d, GLA_MODES[mode], _DTYPES[dt], _stream(stream)))
     return out
 
 

@@ -570,6 +570,31 @@ lizard_status lizard_attn_bwd_hedgehog(const void *q, const void *k, const void 
                   workspace_bytes, stream, true);
 }
 
+lizard_status lizard_gla_fwd(const void *q, const void *k, const void *v, const void *log_gamma, const void *w_phi,
+                             void *out, int B, int Hq, int Hkv, int L, int d, int mode, lizard_dtype dtype,
+                             void *stream) {
+  if (dtype != LIZARD_F32 && dtype != LIZARD_BF16) return fail(LIZARD_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (B < 0 || L < 0) return fail(LIZARD_ERR_INVALID_ARG, "B=%d and L=%d must be >= 0", B, L);
+  if (Hq < 1 || Hkv < 1 || d < 1)
+    return fail(LIZARD_ERR_INVALID_ARG, "need Hq, Hkv, d >= 1 (got Hq=%d Hkv=%d d=%d)", Hq, Hkv, d);
+  if (Hq % Hkv != 0) return fail(LIZARD_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (mode != 0 && mode != 1) return fail(LIZARD_ERR_INVALID_ARG, "mode=%d (0 standard, 1 reparameterized)", mode);
+  if (dtype != LIZARD_BF16 || d != 128)
+    return fail(LIZARD_ERR_UNSUPPORTED, "GLA forward built for bf16, d=128 (got %s, d=%d)",
+                dtype == LIZARD_BF16 ? "bf16" : "fp32", d);
+  if ((int64_t)B * Hq * L > (int64_t)1 << 40) return fail(LIZARD_ERR_INVALID_ARG, "problem too large");
+  if (B == 0 || L == 0) return LIZARD_OK;
+  if (!q || !k || !v || !log_gamma || !w_phi || !out) return fail(LIZARD_ERR_INVALID_ARG, "null tensor pointer");
+  const void *ptrs[] = {q, k, v, log_gamma, w_phi, out};
+  for (const void *ptr : ptrs)
+    if (!aligned16(ptr)) return fail(LIZARD_ERR_INVALID_ARG, "tensor pointer %p not 16-byte aligned", ptr);
+  lz::GlaParams p{};
+  p.q = q; p.k = k; p.v = v; p.lg = log_gamma; p.w = w_phi; p.out = out;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.L = L; p.mode = mode;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return finish(lz::launch_gla(p, st), st);
+}
+
 lizard_status lizard_attn_decode_noalloc(float *state, void *win_k, void *win_v, int32_t *pos, const void *q,
                                          const void *k, const void *v, const void *log_gamma, const void *w_phi_q,
                                          const void *w_phi_k, int64_t w_phi_head_stride, const void *t_k,

@@ -94,3 +94,16 @@ struct BwdWs {
 size_t bwd_workspace_layout(int B, int Hq, int Hkv, int L, int d, int M, int dtype_bf16, BwdWs *ws);
 hipError_t launch_bwd(const BwdParams &p, int dtype_bf16, int d, hipStream_t stream);
 }
+
+namespace lz {
+// Gated-linear-attention forward alone (gla.hip): bf16, d = 128, one W_phi [d][d] for queries,
+// keys and heads, the softmax feature map.  mode 0: standard secondary-chunked form with fp32
+// diagonal blocks; mode 1: chunk-start reference with the whole intra-chunk product on MFMA.
+struct GlaParams {
+  const void *q, *k, *v, *lg, *w;
+  void *out;
+  int B, Hq, Hkv, L;
+  int mode;
+};
+hipError_t launch_gla(const GlaParams &p, hipStream_t stream);
+}

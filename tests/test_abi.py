@@ -287,3 +287,29 @@ def test_decode_noalloc_validation_codes(kw, code):
 
 def test_decode_noalloc_empty_is_ok():
     assert _dec_noalloc(api.load(), N=0) == 0
+
+
+def _gla(lib, **kw):
+    a = dict(q=16, k=16, v=16, lg=16, w=16, out=16, B=1, Hq=2, Hkv=2, L=64, d=128, mode=0, dtype=1, stream=None)
+    a.update(kw)
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.lizard_gla_fwd(P(a["q"]), P(a["k"]), P(a["v"]), P(a["lg"]), P(a["w"]), P(a["out"]), a["B"],
+                              a["Hq"], a["Hkv"], a["L"], a["d"], a["mode"], a["dtype"], P(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(w=None), 1), (dict(out=24), 1), (dict(Hq=3), 1), (dict(Hkv=0), 1),
+    (dict(L=-1), 1), (dict(mode=2), 1), (dict(mode=-1), 1), (dict(dtype=5), 1),
+    (dict(d=64), 2), (dict(dtype=0), 2),      # bf16, d = 128 only
+    (dict(mode=7, B=0), 1),                   # checked before the empty case
+])
+def test_gla_fwd_validation_codes(kw, code):
+    lib = api.load()
+    assert _gla(lib, **kw) == code
+    assert lib.lizard_last_error()
+
+
+def test_gla_fwd_empty_is_ok():
+    lib = api.load()
+    assert _gla(lib, B=0) == 0
+    assert _gla(lib, L=0, q=None) == 0
