@@ -49,8 +49,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_full_workload1.json")
 COUNTER_FILE = os.path.join(ROOT, "profiles", "counters_fwd_full_workload{}.json")
 CLOCK_WARMUP_MS = 400.0        # minimum of steady forward calls before the timed region
 FLUSH_BYTES = 512 << 20        # read before each flushed launch (MALL is 256 MB)
-KERNEL_SOURCES = ["linearized_attention_amd/csrc/fwd_full.hip", "linearized_attention_amd/csrc/fwd_common.hpp",
-                  "linearized_attention_amd/csrc/common.hpp", "linearized_attention_amd/csrc/api.hip"]
+KERNEL_SOURCES = ["linearized_attention_amd/csrc/fwd_full.hip", "linearized_attention_amd/csrc/fwd_full.hpp",
+                  "linearized_attention_amd/csrc/fwd_common.hpp", "linearized_attention_amd/csrc/common.hpp",
+                  "linearized_attention_amd/csrc/api.hip"]
 # The forward call on this workload launches one whole-head kernel (two segments per head, the
 # second walking its own start state); timings, rooflines and traffic refer to the call.
 FWD_KERNEL = "fwd_full_kernel"
@@ -201,6 +202,28 @@ def bench_forward_hedgehog(steps: int, warmup: int):
     log(f"[bench] hedgehog forward: {wcalls} warm-up calls in {wms:.0f} ms, timing {steps} steps")
     total_ms, per = time_launches(step, steps)
     return c, total_ms, per
+
+
+def bench_forward_separate_w(steps: int, warmup: int):
+    """The same layer with a W_phi per query head and per key/value head (separate matrices for
+    the two sides): the query feature maps come from a pass of their own."""
+    c = WORKLOADS[1]
+    log("[bench] generating the forward workload with per-head, separate W_phi")
+    inp = make_fwd_inputs(B=c["B"], Hq=c["Hq"], Hkv=c["Hkv"], L=c["L"], d=c["d"], W=c["W"], M=c["M"],
+                          dtype=c["dtype"], seed=1001, gate=c["gate"], per_head_w=True, separate_wk=True)
+    g = inp.to("cuda")
+    out = torch.empty_like(g.q)
+    need = api.lizard_attn_fwd_workspace_bytes(c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], c["W"], g.q.dtype)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+
+    def step():
+        api.lizard_attn_fwd(g.q, g.k, g.v, g.log_gamma, g.w_phi_q, g.w_phi_k, g.t_k, g.t_v, W=inp.W,
+                            M=inp.M, mix=inp.mix, scale=inp.scale, out=out, workspace=ws)
+
+    wcalls, wms = clock_warmup(step, warmup)
+    log(f"[bench] separate-W forward: {wcalls} warm-up calls in {wms:.0f} ms, timing {steps} steps")
+    total_ms, per = time_launches(step, steps)
+    return total_ms, per
 
 
 def bench_decode(steps: int, warmup: int):
@@ -455,6 +478,8 @@ def main():
                     help="skip the Hedgehog-map forward on the same shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward pass on the same shape")
+    ap.add_argument("--no-separate-w", action="store_true",
+                    help="skip the forward with per-head, separate W_phi on the same shape")
     ap.add_argument("--no-gla", action="store_true",
                     help="skip the standard / reparameterized GLA-only forwards on the same shape")
     ap.add_argument("--pmc-run", action="store_true",
@@ -557,6 +582,16 @@ def main():
             "roofline": {"bound": "hbm", "achieved": hach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": hach / HBM_PEAK_GBS, "kernel_ms": hms,
                          "algorithmic_bytes_per_launch": nbytes},
+        }
+        torch.cuda.empty_cache()
+    if not args.no_separate_w:
+        stot, sper = bench_forward_separate_w(max(args.steps // 2, 1), args.warmup)
+        sms = statistics.median(sper)
+        result["separate_w"] = {
+            "workload": WORKLOAD_NAMES[1] + " with W_phi per query head and per key/value head",
+            "steps": len(sper), "ms_per_step": stot / len(sper), "kernel_ms": sms,
+            "tokens_per_s": tokens / (stot / len(sper) * 1e-3),
+            "over_shared_w": sms / statistics.median(per),
         }
         torch.cuda.empty_cache()
     if not args.no_gla:

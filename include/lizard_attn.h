@@ -114,10 +114,11 @@ size_t lizard_attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int L, int d,
  * feature dimension -- the rows of the state and the entries of log_gamma per
  * token -- is d: feature f < d/2 is exp((xW)_f), feature d/2 + f is
  * exp(-(xW)_f).  Everything else as in lizard_attn_fwd, with the same
- * workspace.  Built for bf16, d = 128, W <= 129, and one W_phi shared by
- * queries, keys and heads (w_phi_q == w_phi_k, w_phi_head_stride = 0); other
- * requests return LIZARD_ERR_UNSUPPORTED.  Precondition, not checked: the
- * logits x . W_phi stay within about +-80, where exp is finite in fp32.
+ * workspace: W_phi shared, separate for queries and keys, or one per head
+ * (w_phi_head_stride >= d * d/2 elements).  Built for bf16, d = 128 and
+ * W <= 129; other requests return LIZARD_ERR_UNSUPPORTED.  Precondition, not
+ * checked: the logits x . W_phi stay within about +-80, where exp is finite in
+ * fp32.
  */
 lizard_status lizard_attn_fwd_hedgehog(const void *q, const void *k,
                                        const void *v, const void *log_gamma,

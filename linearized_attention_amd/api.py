@@ -194,9 +194,8 @@ def lizard_attn_fwd(q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v, *, W: int, M
 def lizard_attn_fwd_hedgehog(q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v, *, W: int, M: int,
                              mix: float = 0.5, scale: float | None = None, out=None,
                              workspace=None, stream=None):
-    """Forward with the Hedgehog map phi(x) = exp(xW) (+) exp(-xW): w_phi_q/w_phi_k [d, d/2]
-    (the library takes one matrix shared by both sides and all heads).  Otherwise as
-    lizard_attn_fwd."""
+    """Forward with the Hedgehog map phi(x) = exp(xW) (+) exp(-xW): w_phi_q/w_phi_k [d, d/2] or
+    per head [Hq|Hkv, d, d/2].  Otherwise as lizard_attn_fwd."""
     return _fwd(load().lizard_attn_fwd_hedgehog, q, k, v, log_gamma, w_phi_q, w_phi_k, t_k, t_v,
                 W=W, M=M, mix=mix, scale=scale, out=out, workspace=workspace, stream=stream,
                 cols=q.shape[-1] // 2)

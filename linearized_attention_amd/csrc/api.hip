@@ -115,21 +115,25 @@ FwdPlan make_plan(int B, int Hq, int Hkv, int L, int d, int W, bool full) {
 
 size_t plan_bytes(const FwdPlan &p) { return p.ws_state_bytes + p.ws_decay_bytes; }
 
-// The whole-head kernel serves bf16 at d = 128 with one W_phi for queries and keys
-// (any grouping of query heads) and W <= 129 (the option "fwd_kernel" = 1 or 2 selects the
-// value-block kernels instead, for tests and A/B timing).
-bool use_full_kernel(int Hq, int Hkv, int d, int W, lizard_dtype dtype, const void *wq, const void *wk,
-                     int64_t w_stride) {
+// The whole-head kernel serves bf16 at d = 128 with W <= 129, any grouping of query heads and
+// any W_phi arrangement (the option "fwd_kernel" = 1 or 2 selects the value-block kernels
+// instead, for tests and A/B timing).
+bool use_full_kernel(int d, int W, lizard_dtype dtype) {
   if (g_opt.fwd_kernel.load(std::memory_order_relaxed) != 0) return false;
-  (void)Hq;
-  (void)Hkv;
-  return dtype == LIZARD_BF16 && d == 128 && W <= 2 * kChunk + 1 && wq == wk && w_stride == 0;
+  return dtype == LIZARD_BF16 && d == 128 && W <= 2 * kChunk + 1;
+}
+
+// Whether the query side needs a W_phi of its own on the whole-head path: separate matrices, or
+// per-head ones with grouped query heads (with G = 1 and one pointer, query head h and key/value
+// head h use the same matrix).
+bool query_w_differs(const void *wq, const void *wk, int64_t w_stride, int G) {
+  return wq != wk || (w_stride != 0 && G > 1);
 }
 
 // Workspace for either plan (the caller does not say whether W_phi is shared).
 size_t seg_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int W, lizard_dtype dtype) {
   const size_t sa = plan_bytes(make_plan(B, Hq, Hkv, L, d, W, false));
-  const bool maybe_full = use_full_kernel(Hq, Hkv, d, W, dtype, nullptr, nullptr, 0);
+  const bool maybe_full = use_full_kernel(d, W, dtype);
   const size_t sb = maybe_full ? plan_bytes(make_plan(B, Hq, Hkv, L, d, W, true)) : 0;
   return sa > sb ? sa : sb;
 }
@@ -168,13 +172,12 @@ lizard_status fwd_impl(const void *q, const void *k, const void *v, const void *
   if (!supported_d(d, dtype))
     return fail(LIZARD_ERR_UNSUPPORTED, "head dim d=%d not built for %s", d, dtype == LIZARD_BF16 ? "bf16" : "fp32");
   if (M > kMaxMeta) return fail(LIZARD_ERR_UNSUPPORTED, "M=%d meta tokens (at most %d)", M, kMaxMeta);
-  if (w_phi_head_stride != 0 && w_phi_head_stride < (int64_t)d * d)
-    return fail(LIZARD_ERR_INVALID_ARG, "w_phi_head_stride=%lld overlaps matrices of d*d elements",
-                (long long)w_phi_head_stride);
-  if (hedgehog && !use_full_kernel(Hq, Hkv, d, W, dtype, w_phi_q, w_phi_k, w_phi_head_stride))
-    return fail(LIZARD_ERR_UNSUPPORTED,
-                "the Hedgehog map is built for bf16, d = 128, W <= %d and one W_phi for queries, keys and "
-                "heads (w_phi_q == w_phi_k, stride 0)", 2 * kChunk + 1);
+  const int64_t wsize = (int64_t)d * (hedgehog ? d / 2 : d);  // elements of one W_phi
+  if (w_phi_head_stride != 0 && w_phi_head_stride < wsize)
+    return fail(LIZARD_ERR_INVALID_ARG, "w_phi_head_stride=%lld overlaps matrices of %lld elements",
+                (long long)w_phi_head_stride, (long long)wsize);
+  if (hedgehog && !use_full_kernel(d, W, dtype))
+    return fail(LIZARD_ERR_UNSUPPORTED, "the Hedgehog map is built for bf16, d = 128, W <= %d", 2 * kChunk + 1);
   if (B == 0 || L == 0) return LIZARD_OK;  // empty problem
   if (!q || !k || !v || !log_gamma || !w_phi_q || !w_phi_k || !out)
     return fail(LIZARD_ERR_INVALID_ARG, "null tensor pointer");
@@ -199,7 +202,7 @@ lizard_status fwd_impl(const void *q, const void *k, const void *v, const void *
     if (ext->pos && (reinterpret_cast<uintptr_t>(ext->pos) & 3u))
       return fail(LIZARD_ERR_INVALID_ARG, "pos not 4-byte aligned");
   }
-  const bool full = use_full_kernel(Hq, Hkv, d, W, dtype, w_phi_q, w_phi_k, w_phi_head_stride);
+  const bool full = use_full_kernel(d, W, dtype);
   const FwdPlan plan = make_plan(B, Hq, Hkv, L, d, W, full);
   const size_t seg_bytes = plan_bytes(plan);
   const size_t hist_bytes = history ? ext_hist_bytes(B, Hkv, d, W, dtype) : 0;
@@ -224,6 +227,7 @@ lizard_status fwd_impl(const void *q, const void *k, const void *v, const void *
   p.force_4wave = g_opt.fwd_kernel.load(std::memory_order_relaxed) == 2 ? 1 : 0;
   p.sss = plan.sss;
   p.hh = hedgehog ? 1 : 0;
+  p.qphi = full && query_w_differs(w_phi_q, w_phi_k, w_phi_head_stride, Hq / Hkv) ? 1 : 0;
   // Two segments on the whole-head path: the second one's workgroups walk the chunks before it
   // themselves (no state pass), and the first segment takes a few chunks more to even out the
   // walk.  Not with a start state or window history (the walk starts from zero at chunk 0).

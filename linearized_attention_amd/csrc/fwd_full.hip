@@ -45,46 +45,19 @@
 // runs first (walk_pipe); the first segment then takes a few chunks more (split_shift).
 #include <type_traits>
 
-#include "fwd_common.hpp"
+#include "fwd_full.hpp"
 
 namespace lz {
-namespace full {
-
-constexpr int D = 128, NFT = 8, KS = 4, NDT = 8, FTW = 2;
-constexpr int LDW = 144;  // rows of 128 elements (288 bytes)
-constexpr int LDWW = 144; // W_phi^T rows (288 bytes)
-constexpr int LDQ = 144;  // decayed-query rows (288 bytes)
-constexpr int LDV = 80;   // rows of 64 tokens (160 bytes)
-constexpr int LDM = 16;   // rows of 16 meta tokens (32 bytes, 8-byte reads)
-constexpr int OFF_W = 0;                        // W_phi^T [f][d]
-constexpr int OFF_K = OFF_W + D * LDWW * 2;     // keys of the chunk [s][d]
-constexpr int OFF_VT = OFF_K + CH * LDW * 2;    // v^T [dv][token, interleaved]
-constexpr int OFF_KT = OFF_VT + D * LDV * 2;    // decayed keys [s][f, interleaved] / log gamma^T [f][s]
-constexpr int SZ_KT = (CH * LDW > D * LDV ? CH * LDW : D * LDV) * 2;
-constexpr int OFF_SB = OFF_KT + SZ_KT;          // S^T copy [dv][f, interleaved]
-constexpr int OFF_Q = OFF_SB + D * LDW * 2;     // decayed queries [t][f, interleaved]
-constexpr int OFF_TAB = OFF_Q + CH * LDQ * 2;   // prefix ends C_J, [4][128] fp32
-constexpr int OFF_TK = OFF_TAB + 4 * D * 4;     // meta keys [16][d]
-constexpr int OFF_TV = OFF_TK + 16 * LDW * 2;   // meta values^T [dv][16]
-constexpr int OFF_FLAG = OFF_TV + D * LDM * 2;  // per query wave: bit k = chunk c_begin + k needs
-constexpr int FLAG_WORDS = 32;                  // the exact diagonal block (segments of at most 1024 chunks)
-constexpr int LDS_BYTES = OFF_FLAG + 4 * FLAG_WORDS * 4;
-static_assert(LDS_BYTES <= LDS_LIMIT, "whole-head layout exceeds LDS");
-
-// position of element e (0..31) of a 32-element group in the interleaved layout
-__device__ __forceinline__ int ipos(int e) { return (e & 3) | ((e >> 4) << 2) | (((e >> 2) & 3) << 3); }
-// token of slot j (0..7) of lane group kq in a 32-wide interleaved operand
-__device__ __forceinline__ int islot(int kq, int j) { return 16 * (j >> 2) + 4 * kq + (j & 3); }
-
-}  // namespace full
 
 // Exact diagonal-block scores for a sub-chunk whose log decay spans more than
 // SPAN_MAX (e.g. gamma ~ 0): A[t][s] = mix sum_f phi_q[t][f] phi_k[s][f] e^{p_t[f] - p_s[f]}
 // in fp32, p the log-gamma prefix inside the sub-chunk, phi recomputed from q and the
 // keys.  Lane (t = lane % 16, g = lane / 16) returns s = 4g .. 4g+3.
-template <bool HH>
-__device__ __forceinline__ f32x4 exact_diag_scores(const bf16 *sW, const bf16 *Kh, const bf16 *LGh, const bf16 *Qh,
-                                                 int c0, int I, int L, float mix) {
+// Wq (QPHI): the query side's W_phi [d][D or D/2] in global memory when it differs from the key
+// side's W_phi^T in LDS; its W^T fragments are gathered element by element (a rare path).
+template <bool HH, bool QPHI>
+__device__ __forceinline__ f32x4 exact_diag_scores(const bf16 *sW, const bf16 *Wq, const bf16 *Kh, const bf16 *LGh,
+                                                 const bf16 *Qh, int c0, int I, int L, float mix) {
   using namespace full;
   using T = bf16;
   const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
@@ -102,32 +75,66 @@ __device__ __forceinline__ f32x4 exact_diag_scores(const bf16 *sW, const bf16 *K
     for (int j = 0; j < KS; ++j) z = mma(load8(sW + (16 * ft + r16) * LDWW + 32 * j + 8 * g4), x[j], z);
     return z;
   };
+  // query logits: W_phi^T in LDS, or (QPHI) W_phi_q^T[f][d] = W_q[d][f] gathered, with the
+  // Hedgehog map's rows D/2 + f taking -W_q[d][f]
+  auto logits_q = [&](int ft) {
+    if constexpr (!QPHI) {
+      return logits_ft(qfr, ft);
+    } else {
+      constexpr int FC = HH ? D / 2 : D;
+      const int f = 16 * ft + r16;
+      const bool neg = HH && f >= FC;
+      const int col = neg ? f - FC : f;
+      f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+        Frag<T> w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const T x = Wq[(size_t)(32 * j + 8 * g4 + e) * FC + col];
+          w.v[e] = neg ? -x : x;
+        }
+        z = mma(w, qfr[j], z);
+      }
+      return z;
+    }
+  };
+  // loop over the feature tiles (kept rolled with the gathered query weights, whose unrolled
+  // loads would not fit the registers)
+  auto for_ft = [&](auto body) {
+    if constexpr (QPHI) {
+#pragma unroll 1
+      for (int ft = 0; ft < NFT; ++ft) body(ft);
+    } else {
+      for (int ft = 0; ft < NFT; ++ft) body(ft);
+    }
+  };
   // softmax map: max and normaliser per row; the Hedgehog map is the plain exponential
   float mq = 0.f, mk = 0.f, iq = 1.f, ik = 1.f;
   if constexpr (!HH) {
     mq = NEG_BIG;
     mk = NEG_BIG;
-    for (int ft = 0; ft < NFT; ++ft) {
-      const f32x4 zq = logits_ft(qfr, ft), zk = logits_ft(kfr, ft);
+    for_ft([&](int ft) {
+      const f32x4 zq = logits_q(ft), zk = logits_ft(kfr, ft);
 #pragma unroll
       for (int i = 0; i < 4; ++i) { mq = fmaxf(mq, zq[i]); mk = fmaxf(mk, zk[i]); }
-    }
+    });
     mq = wave_max_cols(mq);
     mk = wave_max_cols(mk);
     float sq = 0.f, sk = 0.f;
-    for (int ft = 0; ft < NFT; ++ft) {
-      const f32x4 zq = logits_ft(qfr, ft), zk = logits_ft(kfr, ft);
+    for_ft([&](int ft) {
+      const f32x4 zq = logits_q(ft), zk = logits_ft(kfr, ft);
 #pragma unroll
       for (int i = 0; i < 4; ++i) { sq += __expf(zq[i] - mq); sk += __expf(zk[i] - mk); }
-    }
+    });
     iq = 1.f / wave_sum_cols(sq);
     ik = 1.f / wave_sum_cols(sk);
   }
   float part[16];
 #pragma unroll
   for (int s2 = 0; s2 < 16; ++s2) part[s2] = 0.f;
-  for (int ft = 0; ft < NFT; ++ft) {
-    const f32x4 zq = logits_ft(qfr, ft), zk = logits_ft(kfr, ft);
+  for_ft([&](int ft) {
+    const f32x4 zq = logits_q(ft), zk = logits_ft(kfr, ft);
     float x[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -145,7 +152,7 @@ __device__ __forceinline__ f32x4 exact_diag_scores(const bf16 *sW, const bf16 *K
         part[s2] += (s2 <= r16) ? phq * pk * __expf(px[i] - bs) : 0.f;
       }
     }
-  }
+  });
   f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s2 = 0; s2 < 16; ++s2) {
@@ -160,13 +167,14 @@ __device__ __forceinline__ f32x4 exact_diag_scores(const bf16 *sW, const bf16 *K
 // y_t += mix sum_{s<=t} A[t][s] v_s over the 16 rows of sub-chunk I of the chunk at c0, with A
 // the exact diagonal-block scores: read-modify-write of rows this wave stored (same-wave
 // ordering makes the stores visible to the loads).
-template <bool HH>
-__device__ __forceinline__ void exact_diag_fixup(const bf16 *sW, const bf16 *Kh, const bf16 *Vh, const bf16 *LGh,
-                                                 const bf16 *Qh, bf16 *Oh, int c0, int I, int L, float mix) {
+template <bool HH, bool QPHI>
+__device__ __forceinline__ void exact_diag_fixup(const bf16 *sW, const bf16 *Wq, const bf16 *Kh, const bf16 *Vh,
+                                                 const bf16 *LGh, const bf16 *Qh, bf16 *Oh, int c0, int I, int L,
+                                                 float mix) {
   using namespace full;
   using T = bf16;
   const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
-  const f32x4 a = exact_diag_scores<HH>(sW, Kh, LGh, Qh, c0, I, L, mix);
+  const f32x4 a = exact_diag_scores<HH, QPHI>(sW, Wq, Kh, LGh, Qh, c0, I, L, mix);
   // lane (t, g) holds A[t][4g + i]; y_t[dv] += sum_s A[t][s] v_s[dv] for dv = 32g .. 32g+31
   float arow[16];
 #pragma unroll
@@ -235,75 +243,6 @@ __device__ __forceinline__ void keysT_tr(const bf16 *sKt, int I, int ft, int ks,
   for (int j = 0; j < 4; ++j) {
     x[j] = __uint_as_float((uint32_t)(uint16_t)lo[j] << 16);
     x[4 + j] = __uint_as_float((uint32_t)(uint16_t)hi[j] << 16);
-  }
-}
-
-// W_phi^T [f][d] into LDS (row stride LDWW) from W_phi [d][f] in global memory, by NT threads:
-// each thread takes row pairs (d, d + 1) x 8 features, all its loads in flight before the
-// transposed 4-byte stores of the pairs.  HH (Hedgehog map): W_phi is [d][D/2], and rows
-// D/2 + f receive -W_phi^T (a sign flip, exact in bf16), so that the logits of the D features
-// are (xW, -xW).
-template <int NT, bool HH = false>
-__device__ __forceinline__ void load_wT_pairs(bf16 *dst, const bf16 *src, int tid) {
-  using namespace full;
-  constexpr int FC = HH ? D / 2 : D;  // columns of W_phi
-  constexpr int IT = (D / 2) * (FC / 8) / NT;
-  static_assert(IT * NT == (D / 2) * (FC / 8), "thread count must divide the row pairs");
-  Frag<bf16> a[IT], b[IT];
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int idx = tid + it * NT, dd = 2 * (idx / (FC / 8)), f0 = (idx % (FC / 8)) * 8;
-    a[it] = load8(src + (size_t)dd * FC + f0);
-    b[it] = load8(src + (size_t)(dd + 1) * FC + f0);
-  }
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int idx = tid + it * NT, dd = 2 * (idx / (FC / 8)), f0 = (idx % (FC / 8)) * 8;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      bf16 pair[2] = {a[it].v[j], b[it].v[j]};
-      const uint32_t u = *reinterpret_cast<const uint32_t *>(pair);
-      *reinterpret_cast<uint32_t *>(dst + (f0 + j) * LDWW + dd) = u;
-      if constexpr (HH) *reinterpret_cast<uint32_t *>(dst + (FC + f0 + j) * LDWW + dd) = u ^ 0x80008000u;
-    }
-  }
-}
-
-// The feature map of the wave's rows from their logits z: softmax over the D features (max
-// subtracted), or for the Hedgehog map (logits (xW, -xW)) the plain exponential.
-template <bool HH, int NFT>
-__device__ __forceinline__ void feature_map_rows(const f32x4 (&z)[NFT], float (&phi)[NFT][4]) {
-  if constexpr (HH) {
-#pragma unroll
-    for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) phi[ft][i] = exp2_fast(z[ft][i] * LOG2E);
-  } else {
-    // softmax over the D features of the row (4 lanes x NFT x 4 values): max and sum as trees
-    // rather than one chain through all NFT x 4 values
-    float mt[NFT], st[NFT];
-#pragma unroll
-    for (int ft = 0; ft < NFT; ++ft) mt[ft] = fmaxf(fmaxf(z[ft][0], z[ft][1]), fmaxf(z[ft][2], z[ft][3]));
-#pragma unroll
-    for (int w = NFT / 2; w >= 1; w /= 2)
-#pragma unroll
-      for (int ft = 0; ft < w; ++ft) mt[ft] = fmaxf(mt[ft], mt[ft + w]);
-    const float zm2 = -wave_max_cols(mt[0]) * LOG2E;
-#pragma unroll
-    for (int ft = 0; ft < NFT; ++ft) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) phi[ft][i] = exp2_fast(__builtin_fmaf(z[ft][i], LOG2E, zm2));
-      st[ft] = (phi[ft][0] + phi[ft][1]) + (phi[ft][2] + phi[ft][3]);
-    }
-#pragma unroll
-    for (int w = NFT / 2; w >= 1; w /= 2)
-#pragma unroll
-      for (int ft = 0; ft < w; ++ft) st[ft] += st[ft + w];
-    const float inv = 1.f / wave_sum_cols(st[0]);
-#pragma unroll
-    for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) phi[ft][i] *= inv;
   }
 }
 
@@ -723,8 +662,11 @@ __device__ __forceinline__ void walk_pipe(const PipeLds &lds, const bf16 *Kh, co
   __syncthreads();
 }
 
-// ZW: windows of 66..129 keys, which reach into the chunk two back (window group Z)
-template <bool ZW, bool HH>
+// ZW: windows of 66..129 keys, which reach into the chunk two back (window group Z).
+// QPHI: the query side's W_phi differs from the key side's (separate or per-head matrices): the
+// query feature maps were written into the output rows by fwd_full_phiq_kernel, the query waves
+// copy them into LDS, and W_phi^T in LDS is the key side's (of this key/value head).
+template <bool ZW, bool HH, bool QPHI>
 __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
   using namespace full;
   using T = bf16;
@@ -915,7 +857,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
 
   // ---- prologue: weights, meta tokens, the chunk before the first one
   {
-    const T *Wk = reinterpret_cast<const T *>(p.wk);
+    const T *Wk = reinterpret_cast<const T *>(p.wk) + (size_t)kvh * p.w_stride;
     load_wT_pairs<512, HH>(sW, Wk, tid);
     const T *Tv = reinterpret_cast<const T *>(p.tv);
     const T *Tk = reinterpret_cast<const T *>(p.tk);
@@ -1267,14 +1209,30 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
     store_vpairs(vf, tid);
     load_vpairs(vf, c_begin * CH, tid);
     bool unsafe_seen = false;
+    // QPHI: this wave's phi_q rows of chunk c (in the output rows, which it overwrites only in P4
+    // of chunk c), stored there in the interleaved feature order of the LDS rows.  Loaded one
+    // chunk ahead, after B2 (the wide-window variant, short of registers, loads them at the top
+    // of the chunk).
+    Frag<T> pq[QPHI ? KS : 1];
+    auto load_pq = [&](int c0q) {
+      if constexpr (QPHI) {
+        const int t = c0q + 16 * I + r16;
+        const T *src = Oh + (size_t)(t < L ? t : 0) * D + 8 * g4;
+#pragma unroll
+        for (int js = 0; js < KS; ++js) pq[js] = t < L ? load8(src + 32 * js) : frag_zero<T>();
+      }
+    };
+    if constexpr (QPHI && !ZW) load_pq(c_begin * CH);
     __syncthreads();  // P
 
     for (int c = c_begin; c < c_end; ++c) {
       const int c0 = c * CH;
       const int pos = c0 + 16 * I + r16;  // query row of this lane's column
       const bool valid = pos < L;
+
       // lowest key index the window of this row may use
       const int kmin = max(pos - p.W + 1, -hist_avail);
+      if constexpr (QPHI && ZW) load_pq(c0);
 
       // ---- P0: window group X (meta tokens and the previous chunk's keys, still in LDS: tiles
       //      I..3, all four with ZW) in base-2 logits, merged with group Z; unnormalised
@@ -1358,7 +1316,10 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
       // ---- P1: stage this chunk's values; phi_q of this wave's rows into LDS (the key waves
       //      decay it in place)
       store_vpairs(vf, tid);
-      {
+      if constexpr (QPHI) {
+#pragma unroll
+        for (int js = 0; js < KS; ++js) *reinterpret_cast<bf16x8 *>(sQ + (16 * I + r16) * LDQ + 32 * js + 8 * g4) = pq[js].v;
+      } else {
         f32x4 zq[NFT];
         float qo[NFT][4];
         // (the wide-window variant carries group Z through here: no registers for prefetching)
@@ -1452,6 +1413,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
         pairs_in(vf, Vh, c0 + CH, ln + 64 * wv);
         if constexpr (ZW) q_in(qf_next2, c0 + 2 * CH, ln);
         else q_in(qf_next, c0 + CH, ln);
+        if constexpr (QPHI && !ZW) load_pq(c0 + CH);
       }
       // ---- P3: window output normalised and scaled for the merge; for strong-decay chunks the
       //      inter-chunk product (decayed queries and prefix ends are visible since B2, the state
@@ -1627,7 +1589,8 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
     if (unsafe_seen) {
       for (int c = c_begin; c < c_end; ++c) {
         if (!((sFlag[I * FLAG_WORDS + ((c - c_begin) >> 5)] >> ((c - c_begin) & 31)) & 1u)) continue;
-        exact_diag_fixup<HH>(sW, Kh, Vh, LGh, Qh, Oh, c * CH, I, L, mix);
+        const T *Wq = QPHI ? reinterpret_cast<const T *>(p.wq) + (size_t)hq * p.w_stride : nullptr;
+        exact_diag_fixup<HH, QPHI>(sW, Wq, Kh, Vh, LGh, Qh, Oh, c * CH, I, L, mix);
       }
     }
   }
@@ -1691,7 +1654,7 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
   f32x4 S[FTW][NDT];
   float suf;
   const bool stopped = walk_back<HH, true>(lds, Kh, Vh, LGh, b0, b1, pp, sss, tid, S, suf, [&]() {
-    load_wT_pairs<256, HH>(sW, reinterpret_cast<const T *>(p.wk), tid);
+    load_wT_pairs<256, HH>(sW, reinterpret_cast<const T *>(p.wk) + (size_t)(bh % p.Hkv) * p.w_stride, tid);
   });
   float *E = p.ws_state + (size_t)grp * (D * D);
 #pragma unroll
@@ -1700,6 +1663,16 @@ __global__ __launch_bounds__(256, 2) void fwd_full_state_kernel(FwdParams p) {
     for (int dt = 0; dt < NDT; ++dt)
       *reinterpret_cast<f32x4 *>(E + ((size_t)((2 * I + ft) * NDT + dt) * 64 + lane) * 4) = S[ft][dt];
   if (tid < D) p.ws_decay[(size_t)grp * D + tid] = pp > 0 ? 0.f : (stopped ? NEG_BIG : suf);
+}
+
+template <bool ZW, bool HH, bool QPHI>
+static hipError_t launch_main(const FwdParams &p, hipStream_t stream) {
+  const void *kern = reinterpret_cast<const void *>(fwd_full_kernel<ZW, HH, QPHI>);
+  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, full::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  const dim3 grid(((p.ngroups + 7) / 8) * 8 * p.G);
+  hipLaunchKernelGGL((fwd_full_kernel<ZW, HH, QPHI>), grid, dim3(512), full::LDS_BYTES, stream, p);
+  return hipGetLastError();
 }
 
 template <bool HH>
@@ -1714,15 +1687,10 @@ static hipError_t launch_fwd_full_t(const FwdParams &p, hipStream_t stream) {
                        stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  if (p.qphi && (e = launch_fwd_full_phiq(p, stream)) != hipSuccess) return e;
   const bool zw = p.W > CH + 1;
-  const void *kern = zw ? reinterpret_cast<const void *>(fwd_full_kernel<true, HH>)
-                        : reinterpret_cast<const void *>(fwd_full_kernel<false, HH>);
-  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, full::LDS_BYTES);
-  if (e != hipSuccess) return e;
-  const dim3 grid(((p.ngroups + 7) / 8) * 8 * p.G);
-  if (zw) hipLaunchKernelGGL((fwd_full_kernel<true, HH>), grid, dim3(512), full::LDS_BYTES, stream, p);
-  else hipLaunchKernelGGL((fwd_full_kernel<false, HH>), grid, dim3(512), full::LDS_BYTES, stream, p);
-  return hipGetLastError();
+  return zw ? (p.qphi ? launch_main<true, HH, true>(p, stream) : launch_main<true, HH, false>(p, stream))
+            : (p.qphi ? launch_main<false, HH, true>(p, stream) : launch_main<false, HH, false>(p, stream));
 }
 
 hipError_t launch_fwd_full(const FwdParams &p, hipStream_t stream) {

@@ -33,6 +33,8 @@ struct FwdParams {
   int full;  // whole-head kernel (fwd_full.hip)
   int sss;   // whole-head kernel: state-pass pieces per segment (divides cps)
   int hh;    // whole-head kernel: Hedgehog feature map (W_phi [d][d/2]) instead of the softmax
+  int qphi;  // whole-head kernel: the query side's W_phi differs from the key side's (separate or
+             // per-head matrices); phi_q is computed by a pass of its own into the output rows
   int split; // whole-head kernel, two segments: > 0 puts the second segment's start at this chunk
              // plus a shift and has its workgroups walk the chunks before it (no state pass)
   int split_shift;  // the shift: < 0 estimated from the gates in the kernel, else this many chunks
@@ -44,6 +46,8 @@ hipError_t launch_fwd(const FwdParams &p, int dtype_bf16, int d, hipStream_t str
 // whole-head forward kernel (bf16, d = 128, shared W_phi, one query head per key/value
 // head, W <= 65); the state pass of launch_fwd runs first when the sequence is segmented
 hipError_t launch_fwd_full(const FwdParams &p, hipStream_t stream);
+// its query feature maps on their own (p.qphi), written into the output rows
+hipError_t launch_fwd_full_phiq(const FwdParams &p, hipStream_t stream);
 // before the forward: window history rows from the caller's ring; after it: the ring of
 // the last W tokens and pos += L
 hipError_t launch_hist_stage(const FwdParams &p, const void *ring_k, const void *ring_v, int d, int esize,

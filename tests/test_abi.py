@@ -68,9 +68,9 @@ def test_fwd_validation_codes(kw, code):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), 1), (dict(Hq=3, Hkv=2), 1), (dict(stride=100), 1),
+    (dict(stride=128 * 64 - 1), 1),                          # overlaps matrices of d x d/2 elements
     (dict(d=64), 2), (dict(d=64, dtype=0), 2),            # only bf16, d = 128
     (dict(W=130), 2),                                       # windows of at most 129 keys
-    (dict(wk=32), 2), (dict(stride=128 * 128), 2),          # one W_phi for both sides and all heads
 ])
 def test_fwd_hedgehog_validation_codes(kw, code):
     lib = api.load()
