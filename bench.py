@@ -15,12 +15,17 @@ run.  Then K calls are timed back to back, bracketed by two synchronisations
 (`ms_per_step`, `value`).  The roofline figures come from a second pass of K
 calls, each preceded by a 512 MB read that flushes the 256 MB MALL, timed one
 by one with HIP events on the launch stream: the median and the mean are
-reported, `achieved` uses the median.
+reported, `achieved` uses the mean (the average launch duration, the figure a
+rocprofv3 kernel trace of the same launches averages to).
 
-The JSON line also carries the decode step (N=256 sequences, H=32, d=128, fp32
-state, W=64, M=4; 128 consecutive steps) with its own HBM roofline, the
-forward with the Hedgehog feature map, and the fp64 oracle timed on the host
-cores over the whole forward workload (about 1.5 s of wall time on 16 threads).
+The JSON line also carries, on the same layer shape: the forward with the
+Hedgehog feature map, the forward with per-head separate W_phi, the global
+branch alone in its standard and reparameterized forms, and the backward pass
+(each the median of per-launch HIP-event times after a clock warm-up); the
+decode step (N=256 sequences, H=32, d=128, fp32 state, W=64, M=4; 128
+consecutive steps) with its own HBM roofline; and the fp64 oracle timed on the
+host cores over the whole forward workload (about 1.5 s of wall time on 16
+threads).
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -529,7 +534,7 @@ def main():
     value = tokens / (ms_per_step * 1e-3)
     nbytes, flops = fwd_algorithmic(c)
     st = launch_stats(per_fl)
-    kern_ms = st["median_ms"]
+    kern_ms = st["mean_ms"]  # the average launch duration (the kernel-trace summary's figure)
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
     mfma_tflops = flops / (kern_ms * 1e-3) / 1e12
     traffic = load_traffic(args.workload)

@@ -132,3 +132,20 @@ def test_decode_workload3_full_size_sampled(gpu_lib):
     _say(f"      out rel-L2 {err:.3e}  state rel-L2 {serr:.3e}")
     assert err <= TOL["bf16"] and serr <= TOL["bf16"]
     assert (pg.numpy() == 4098).all()
+
+
+def test_decode_workload3_128_steps_sampled(gpu_lib):
+    """The benchmark's decode run: N=256 sequences, H=32, d=128, 128 consecutive steps on the
+    GPU from the seeded start (pos 4096); six sequences followed through all 128 steps in fp64,
+    every step's output and the final state compared."""
+    _say("[decode] workload 3 full size, 128 consecutive steps")
+    dec = workload_decode_inputs(3, steps=128)
+    yg, sg, rkg, _, pg = run_gpu_steps(dec)
+    seqs = np.array([0, 5, 99, 160, 223, 255])
+    yo, so, rko, _, po = run_oracle_steps(dec, seqs=torch.from_numpy(seqs))
+    err = rel_l2(yg[seqs], yo, axes=(0, 2, 3)).max()
+    serr = rel_l2(sg[seqs], so, axes=(0, 2, 3)).max()
+    _say(f"      out rel-L2 (per head, all 128 steps) {err:.3e}  final state rel-L2 {serr:.3e}")
+    assert err <= TOL["bf16"] and serr <= TOL["bf16"]
+    assert (pg.numpy() == 4096 + 128).all()
+    assert torch.equal(rkg[torch.from_numpy(seqs)], torch.from_numpy(np.asarray(rko)).to(rkg.dtype))
