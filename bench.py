@@ -12,11 +12,16 @@ Timing.  After the W requested warm-up calls, warm-up continues until at least
 CLOCK_WARMUP_MS of back-to-back forward calls have run (the GPU's clocks take
 some 50-100 ms of steady work to settle); the line states the warm-up actually
 run.  Then K calls are timed back to back, bracketed by two synchronisations
-(`ms_per_step`, `value`).  The roofline figures come from a second pass of K
-calls, each preceded by a 512 MB read that flushes the 256 MB MALL, timed one
-by one with HIP events on the launch stream: the median and the mean are
-reported, `achieved` uses the mean (the average launch duration, the figure a
-rocprofv3 kernel trace of the same launches averages to).
+(`ms_per_step`, `value`).  Each of those launches is also timed on its own
+with HIP events on the launch stream; `roofline.achieved` divides the
+algorithmic bytes by their mean (the average launch duration, the figure a
+rocprofv3 kernel trace of the same launches averages to).  A second pass of K
+calls, each preceded by a 512 MB read that flushes the 256 MB MALL, is
+reported beside it (`mall_flushed_launches`): across runs it came out from 1%
+faster to 20% slower than the back-to-back launches, with the same spread when
+the flush was replaced by an idle gap or by compute-only work, so what it
+measures is the clock state after a pause, not inputs left in the MALL (the
+inputs and output, 671 MB, are 2.6 times its size).
 
 The JSON line also carries, on the same layer shape: the forward with the
 Hedgehog feature map, the forward with per-head separate W_phi, the global
@@ -533,7 +538,7 @@ def main():
     tokens = c["B"] * c["L"]
     value = tokens / (ms_per_step * 1e-3)
     nbytes, flops = fwd_algorithmic(c)
-    st = launch_stats(per_fl)
+    st = launch_stats(per)
     kern_ms = st["mean_ms"]  # the average launch duration (the kernel-trace summary's figure)
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
     mfma_tflops = flops / (kern_ms * 1e-3) / 1e12
@@ -566,8 +571,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": FWD_KERNEL if args.workload == 1 else "fwd_full_state_kernel + fwd_full_kernel",
-                     "kernel_ms": kern_ms, "launches": {**st, "mall_flushed": True},
-                     "back_to_back_launches": launch_stats(per),
+                     "kernel_ms": kern_ms, "launches": {**st, "mall_flushed": False},
+                     "mall_flushed_launches": launch_stats(per_fl),
                      "algorithmic_bytes_per_launch": nbytes},
         "mfma": mfma,
     }
