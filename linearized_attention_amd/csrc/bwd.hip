@@ -6,8 +6,10 @@
 //   2. bwd_sweep_kernel     role F (one wave per batch, query head, 16-feature tile): forward over
 //                           16-token steps with its columns of the state S in registers:
 //                               dphi_q[t] = mix * S_t dy_t
-//                           role V (one wave per batch, key/value head, 16-column tile of v):
-//                           backward over the steps with its columns of dL/dS in registers:
+//                           bwd_v_kernel, role V (workgroups of D / 32 waves, one wave per 16-column
+//                           tile of v, two workgroups per batch and key/value head, the step's
+//                           decayed operands shared in LDS): backward over the steps with its
+//                           columns of dL/dS in registers:
 //                               dv_gla[s] = mix * dS_s^T phi_k[s]
 //   3. bwd_sweep_kernel     role R (one wave per batch, key/value head, 16-feature tile): backward
 //                           with its rows of dL/dS:  dphi_k[s] = mix * dS_s v_s, and the log-gate
@@ -279,15 +281,6 @@ template <typename T, int D> struct LdsR {
   float ph2[TS * LDF];   // in-step sums of the exact path
   float dd[TS * 17];     // E[t][s] = dy_t . v_s
 };
-template <typename T, int D> struct LdsV {
-  static constexpr int LD = D + 8, LDF = D + 4;
-  T a[TS * LD];          // rows of dy
-  T b[TS * LD];          // rows of phi_q
-  T c[TS * LD];          // rows of log gamma
-  float pf[TS * LDF];    // exact path: p[t][f]
-  float ph1[TS * LDF];   // exact path: phi_q[t][f]
-  float ph2[TS * LDF];   // exact path: phi_k[s][f]
-};
 
 // Role F: dphi_q for features f0 .. f0 + 15 of query head hq (see the top of the file).
 template <typename T, int D>
@@ -401,152 +394,6 @@ __device__ void sweep_f(const BwdParams &p, LdsF<T, D> &sm, int b, int hq, int f
       S[dt] = m16_tf<T>(lds_col4(sm.a, LD, 4 * kq, 16 * dt), kb, S[dt]);
     }
     __syncthreads();  // v rows read before the next step overwrites them
-  }
-}
-
-// Role V: dv_gla for value columns dv0 .. dv0 + 15 of key/value head hk (sum over its query heads).
-template <typename T, int D>
-__device__ void sweep_v(const BwdParams &p, LdsV<T, D> &sm, int b, int hk, int dt0) {
-  constexpr int NFT = D / 16, NKS = D / 32, LD = LdsV<T, D>::LD, LDF = LdsV<T, D>::LDF;
-  const int lane = threadIdx.x & 63, r = lane & 15, kq = lane >> 4;
-  const int L = p.L, G = p.G, dv0 = 16 * dt0;
-  const size_t kvo = ((size_t)b * p.Hkv + hk) * L * D;
-  const T *LG = reinterpret_cast<const T *>(p.lg) + kvo;
-  const float *PK = p.phk + kvo;
-  float *DVG = p.dvg + kvo;
-  f32x4 dS[NFT];  // dS[f = 16 ft + 4 kq + i][dv = dv0 + r]
-#pragma unroll
-  for (int ft = 0; ft < NFT; ++ft) dS[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const F4<T> tri = tri_le<T>(r, kq);
-  const int nstep = (L + TS - 1) / TS;
-  for (int st = nstep - 1; st >= 0; --st) {
-    const int c0 = st * TS;
-    const bool rok = c0 + r < L;
-    // log gamma rows into LDS, then the prefix sums of every feature tile in both layouts
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) store_il(sm.c + r * LD, row_il(LG + (size_t)(c0 + r) * D, ks, kq, rok), ks, kq);
-    Frag<float> pkf[NKS];  // phi_k rows (interleaved)
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) pkf[ks] = row_il(PK + (size_t)(c0 + r) * D, ks, kq, rok);  // fp32 rows
-    __syncthreads();
-    f32x4 pQ[NFT], pK[NFT];  // pQ: lane (t = r, kq) f = 16 ft + 4 kq + i; pK: lane (f = 16 ft + r, kq) t = 4 kq + i
-    float spn = 0.f;
-#pragma unroll
-    for (int ft = 0; ft < NFT; ++ft) {
-      const F4<T> lc = lds_col4(sm.c, LD, 4 * kq, 16 * ft);
-      pQ[ft] = mma16(lc, tri, f32x4{0.f, 0.f, 0.f, 0.f});
-      pK[ft] = mma16(tri, lc, f32x4{0.f, 0.f, 0.f, 0.f});
-      spn = fmaxf(spn, -pK[ft][3]);
-    }
-    const bool mild = wave_max_all(spn) <= MILD_SPAN;
-    float Pq[NFT][4];  // every lane: P[f = 16 ft + 4 kq + i]
-#pragma unroll
-    for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Pq[ft][i] = __shfl(pQ[ft][i], 15 + 16 * kq);
-    // ---- inter: dV[s][dv] = sum_f Kbar[s][f] dS[f][dv], Kbar = phi_k e^{P - p_s}
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};  // lane (dv = dv0 + r, kq): s = 4 kq + i
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      float ka[8], sb[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int ft = 2 * ks + (j >> 2), i = j & 3;
-        ka[j] = pkf[ks].v[j] * __expf(Pq[ft][i] - pQ[ft][i]);
-        sb[j] = dS[ft][i];
-      }
-      acc = mma(frag_from<T>(ka), frag_from<T>(sb), acc);
-    }
-    if (!mild) {
-      // exact path tables: p and phi_k of the step, fp32
-#pragma unroll
-      for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sm.pf[r * LDF + 16 * ft + 4 * kq + i] = pQ[ft][i];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) sm.ph2[r * LDF + 32 * ks + 16 * (j >> 2) + 4 * kq + (j & 3)] = pkf[ks].v[j];
-    }
-    // ---- per query head of the group: intra part, then the state update
-    for (int g = 0; g < G; ++g) {
-      const int hq = hk * G + g;
-      const size_t qo = ((size_t)b * p.Hq + hq) * L * D;
-      const float *PQ = p.phq + qo;
-      const T *DY = reinterpret_cast<const T *>(p.dy) + qo;
-      Frag<float> pqf[NKS];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        pqf[ks] = row_il(PQ + (size_t)(c0 + r) * D, ks, kq, rok);
-        store_il(sm.a + r * LD, row_il(DY + (size_t)(c0 + r) * D, ks, kq, rok), ks, kq);
-        store_il(sm.b + r * LD, from32<T>(pqf[ks]), ks, kq);
-      }
-      __syncthreads();
-      // A[t][s] (lane (s = r, kq): t = 4 kq + i), masked to t >= s
-      f32x4 a = {0.f, 0.f, 0.f, 0.f};
-      if (mild) {
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          float qa[8], kb[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int ft = 2 * ks + (j >> 2), i = j & 3;
-            qa[j] = pqf[ks].v[j] * __expf(pQ[ft][i]);
-            kb[j] = pkf[ks].v[j] * __expf(-pQ[ft][i]);
-          }
-          a = mma(frag_from<T>(qa), frag_from<T>(kb), a);
-        }
-      } else {
-        // exact: A[t][s] = sum_f phi_q[t][f] phi_k[s][f] e^{p_t[f] - p_s[f]}
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) sm.ph1[r * LDF + 32 * ks + 16 * (j >> 2) + 4 * kq + (j & 3)] = pqf[ks].v[j];
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 4 * kq + i;
-          float x = 0.f;
-          if (t >= r)
-            for (int f = 0; f < D; ++f)
-              x += sm.ph1[t * LDF + f] * sm.ph2[r * LDF + f] * __expf(sm.pf[t * LDF + f] - sm.pf[r * LDF + f]);
-          a[i] = x;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = (4 * kq + i >= r) ? a[i] : 0.f;
-      // dV[s][dv] += sum_t A[t][s] dy_t[dv]
-      const F4<T> dyc = lds_col4(sm.a, LD, 4 * kq, dv0);
-      {
-        float x[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = a[i];
-        acc = mma16(f4_from<T>(x), dyc, acc);
-      }
-      // dS[f][dv] (contribution of this head, added below after the decay): Qt^T dY
-      // Qt[t][f] = phi_q[t][f] e^{p_t[f]}: columns from LDS, prefix in the pK layout
-      if (g == 0) {
-#pragma unroll
-        for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) dS[ft][i] *= __expf(Pq[ft][i]);
-      }
-#pragma unroll
-      for (int ft = 0; ft < NFT; ++ft) {
-        const F4<T> qc = lds_col4(sm.b, LD, 4 * kq, 16 * ft);
-        float qt[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) qt[j] = f4_at(qc, j) * __expf(pK[ft][j]);
-        dS[ft] = mma16(f4_from<T>(qt), dyc, dS[ft]);
-      }
-      __syncthreads();
-    }
-    // store dV (lane (dv = dv0 + r, kq): s = c0 + 4 kq + i)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int s = c0 + 4 * kq + i;
-      if (s < L) DVG[(size_t)s * D + dv0 + r] = p.mix * acc[i];
-    }
   }
 }
 
@@ -711,8 +558,8 @@ __device__ void sweep_r(const BwdParams &p, LdsR<T, D> &sm, int b, int hk, int f
   }
 }
 
-// One wave per block; ROLE 0: F (blocks: batch, query head, feature tile), 1: V (batch, key/value
-// head, value tile), 2: R (batch, key/value head, feature tile).
+// One wave per block; ROLE 0: F (blocks: batch, query head, feature tile), 2: R (batch, key/value
+// head, feature tile).  Role V runs in bwd_v_kernel below.
 template <typename T, int D, int ROLE>
 __global__ __launch_bounds__(64) void bwd_sweep_kernel(BwdParams p) {
   constexpr int NT = D / 16;
@@ -720,12 +567,213 @@ __global__ __launch_bounds__(64) void bwd_sweep_kernel(BwdParams p) {
   if constexpr (ROLE == 0) {
     __shared__ LdsF<T, D> sm;
     sweep_f<T, D>(p, sm, bh / p.Hq, bh % p.Hq, tile);
-  } else if constexpr (ROLE == 1) {
-    __shared__ LdsV<T, D> sm;
-    sweep_v<T, D>(p, sm, bh / p.Hkv, bh % p.Hkv, tile);
   } else {
     __shared__ LdsR<T, D> sm;
     sweep_r<T, D>(p, sm, bh / p.Hkv, bh % p.Hkv, tile);
+  }
+}
+
+// Role V: dv_gla[s] = mix dS_s^T phi_k-part for value columns of key/value head hk, summed over its
+// query heads, backward over the 16-token steps with dL/dS for the wave's 16 value columns in
+// registers:  dv[s] = sum_f Kbar[s][f] dS[f] + sum_{t >= s} A[t][s] dy_t,  then
+// dS <- diag(e^P) dS + Qtil^T dY  with Kbar = phi_k e^{P - p_s}, Qtil = phi_q e^{p_t} and, on a mild
+// step, A = Qtil Ktil^T, Ktil = phi_k e^{-p_s} (otherwise A per element in fp32).
+// Every value column needs the same decayed operands, so the waves of a workgroup share them: the
+// NW = D / 32 waves take value tiles h NW + w of one (batch, key/value head), h = 0, 1 the two
+// workgroups of the head (8 launch slots apart: one XCD, so the second reads the head's inputs from
+// L2), and wave w builds the operands for features 32 w .. 32 w + 31 of every step into LDS.
+template <typename T, int D> struct LdsV2 {
+  static constexpr int NW = D / 32;
+  static constexpr int LD = D + 8;   // T rows of the shared operands (natural feature order)
+  static constexpr int LDL = 40;     // T rows of a wave's log-gamma slice (32 features)
+  static constexpr int LDX = 36;     // fp32 rows of a wave's exact-path slice
+  T kb[TS * LD], kt[TS * LD], qt[TS * LD];  // Kbar, Ktil, Qtil of the step [token][feature]
+  float ep[D];                              // e^{P[f]}
+  float span[NW];                           // per slice: max over its features of -P
+  T lg[NW][TS * LDL];                       // per wave: log gamma of its slice
+  float xp[NW][TS * LDX], xq[NW][TS * LDX], xk[NW][TS * LDX];  // per wave: p, phi_q, phi_k (exact path)
+  float part[NW][TS * 17];                  // exact path: per slice, partial A[t][s]
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(64 * (D / 32)) void bwd_v_kernel(BwdParams p) {
+  using S = LdsV2<T, D>;
+  constexpr int NW = S::NW, NFT = D / 16, NKS = D / 32, LD = S::LD, LDL = S::LDL, LDX = S::LDX;
+  __shared__ S sm;
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, kq = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bh = (blockIdx.x >> 4) * 8 + (blockIdx.x & 7), half = (blockIdx.x >> 3) & 1;
+  if (bh >= p.B * p.Hkv) return;  // padding of the launch to whole XCD pairs
+  const int hk = bh % p.Hkv, b = bh / p.Hkv;
+  const int L = p.L, G = p.G, dv0 = 16 * (half * NW + w);
+  const size_t kvo = (size_t)bh * L * D;
+  const T *LG = reinterpret_cast<const T *>(p.lg) + kvo;
+  const float *PK = p.phk + kvo;
+  float *DVG = p.dvg + kvo;
+  T *lgs = sm.lg[w];
+  float *xp = sm.xp[w], *xq = sm.xq[w], *xk = sm.xk[w];
+  f32x4 dS[NFT];  // dS[f = 16 ft + 4 kq + i][dv = dv0 + r]
+#pragma unroll
+  for (int ft = 0; ft < NFT; ++ft) dS[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const F4<T> tri = tri_le<T>(r, kq);
+  auto qrow = [&](int g) { return ((size_t)b * p.Hq + hk * G + g) * L * D; };
+  // the slice rows (token c0 + r, features 32 w + slot) and this wave's dy column of a step
+  auto load_step = [&](int c0, Frag<T> &lgf, Frag<float> &pkf, Frag<float> &pqf, F4<T> &dyc, int g) {
+    const bool rok = c0 + r < L;
+    lgf = row_il(LG + (size_t)(c0 + r) * D, w, kq, rok);
+    pkf = row_il(PK + (size_t)(c0 + r) * D, w, kq, rok);
+    pqf = row_il(p.phq + qrow(g) + (size_t)(c0 + r) * D, w, kq, rok);
+    dyc = col_g(reinterpret_cast<const T *>(p.dy) + qrow(g), D, c0 + 4 * kq, dv0 + r, L);
+  };
+  auto load_head = [&](int c0, Frag<float> &pqf, F4<T> &dyc, int g) {
+    pqf = row_il(p.phq + qrow(g) + (size_t)(c0 + r) * D, w, kq, c0 + r < L);
+    dyc = col_g(reinterpret_cast<const T *>(p.dy) + qrow(g), D, c0 + 4 * kq, dv0 + r, L);
+  };
+  const int nstep = (L + TS - 1) / TS;
+  Frag<T> lgf;
+  Frag<float> pkf, pqf;
+  F4<T> dyc;
+  load_step((nstep - 1) * TS, lgf, pkf, pqf, dyc, 0);
+  for (int st = nstep - 1; st >= 0; --st) {
+    const int c0 = st * TS;
+    // ---- the slice's prefix sums (lane (t = r, kq): feature 32 w + 16 h + 4 kq + i) and totals
+    store_il(lgs + r * LDL, lgf, 0, kq);
+    __builtin_amdgcn_wave_barrier();
+    f32x4 pq[2];
+    float P[2][4];
+    float spn = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      pq[h] = mma16(lds_col4(lgs, LDL, 4 * kq, 16 * h), tri, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        P[h][i] = __shfl(pq[h][i], 15 + 16 * kq);
+        spn = fmaxf(spn, -P[h][i]);
+      }
+    }
+    spn = wave_max_all(spn);
+    // ---- the slice's operands: Kbar = phi_k e^{P - p}, Ktil = phi_k e^{-p} (used on mild steps
+    //      only, where -p <= 60), Qtil = phi_q e^{p} of the first query head, e^{P}; exact-path rows
+    {
+      float kb[8], kt[8], qt[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int h = j >> 2, i = j & 3;
+        const float pv = pq[h][i];
+        kb[j] = pkf.v[j] * __expf(P[h][i] - pv);
+        kt[j] = pkf.v[j] * __expf(fminf(-pv, MILD_SPAN));
+        qt[j] = pqf.v[j] * __expf(pv);
+        const int col = 16 * h + 4 * kq + i;
+        xp[r * LDX + col] = pv;
+        xk[r * LDX + col] = pkf.v[j];
+        xq[r * LDX + col] = pqf.v[j];
+      }
+      store_il(sm.kb + r * LD, frag_from<T>(kb), w, kq);
+      store_il(sm.kt + r * LD, frag_from<T>(kt), w, kq);
+      store_il(sm.qt + r * LD, frag_from<T>(qt), w, kq);
+      if (r == 0) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sm.ep[32 * w + 16 * h + 4 * kq + i] = __expf(P[h][i]);
+      }
+      if (lane == 0) sm.span[w] = spn;
+    }
+    // the next step's rows in flight
+    Frag<T> lgf_n;
+    Frag<float> pkf_n, pqf_n;
+    F4<T> dyc_n;
+    if (st > 0) load_step(c0 - TS, lgf_n, pkf_n, pqf_n, dyc_n, 0);
+    __syncthreads();  // B1: the step's operands visible
+    float spall = 0.f;
+#pragma unroll
+    for (int u = 0; u < NW; ++u) spall = fmaxf(spall, sm.span[u]);
+    const bool mild = spall <= MILD_SPAN;
+    // ---- inter: dV[s][dv] = sum_f Kbar[s][f] dS[f][dv]  (lane (dv = dv0 + r, kq): s = 4 kq + i)
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      float sb[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sb[j] = dS[2 * ks + (j >> 2)][j & 3];
+      const T *kr = sm.kb + r * LD + 32 * ks + 4 * kq;
+      acc = mma(load4x2(kr, kr + 16), frag_from<T>(sb), acc);
+    }
+    for (int g = 0; g < G; ++g) {
+      if (g > 0) {  // this head's Qtil (the previous head's reads ended at its last barrier)
+        Frag<float> pqg;
+        load_head(c0, pqg, dyc, g);
+        float qt[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          qt[j] = pqg.v[j] * __expf(pq[j >> 2][j & 3]);
+          xq[r * LDX + 16 * (j >> 2) + 4 * kq + (j & 3)] = pqg.v[j];
+        }
+        store_il(sm.qt + r * LD, frag_from<T>(qt), w, kq);
+        __syncthreads();  // this head's Qtil visible
+      }
+      // A[t][s] (lane (s = r, kq): t = 4 kq + i), masked to t >= s
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+      if (mild) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const T *qr = sm.qt + r * LD + 32 * ks + 4 * kq, *kr = sm.kt + r * LD + 32 * ks + 4 * kq;
+          a = mma(load4x2(qr, qr + 16), load4x2(kr, kr + 16), a);
+        }
+      } else {
+        // exact: A[t][s] = sum_f phi_q[t][f] phi_k[s][f] e^{p_t[f] - p_s[f]}, each wave over its slice
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 4 * kq + i;
+          float x = 0.f;
+          if (t >= r)
+            for (int f = 0; f < 32; ++f)
+              x += xq[t * LDX + f] * xk[r * LDX + f] * __expf(xp[t * LDX + f] - xp[r * LDX + f]);
+          sm.part[w][t * 17 + r] = x;
+        }
+        __syncthreads();  // the slices' partial scores visible
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = 0.f;
+#pragma unroll
+          for (int u = 0; u < NW; ++u) x += sm.part[u][(4 * kq + i) * 17 + r];
+          a[i] = x;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = (4 * kq + i >= r) ? a[i] : 0.f;
+      // dV[s][dv] += sum_t A[t][s] dy_t[dv]
+      {
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = a[i];
+        acc = mma16(f4_from<T>(x), dyc, acc);
+      }
+      // dS: decay to the step start (once), then + Qtil^T dY of this head
+      if (g == 0) {
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft) {
+          const f32x4 e = *reinterpret_cast<const f32x4 *>(sm.ep + 16 * ft + 4 * kq);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dS[ft][i] *= e[i];
+        }
+      }
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft) dS[ft] = mma16(lds_col4(sm.qt, LD, 4 * kq, 16 * ft), dyc, dS[ft]);
+      __syncthreads();  // B2: the step's (head's) operands read before they are rewritten
+    }
+    // store dV (lane (dv = dv0 + r, kq): s = c0 + 4 kq + i)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s2 = c0 + 4 * kq + i;
+      if (s2 < L) DVG[(size_t)s2 * D + dv0 + r] = p.mix * acc[i];
+    }
+    if (st > 0) {
+      lgf = lgf_n;
+      pkf = pkf_n;
+      pqf = pqf_n;
+      dyc = dyc_n;
+    }
   }
 }
 
@@ -1227,7 +1275,7 @@ static hipError_t launch_bwd_t(const BwdParams &p, hipStream_t st) {
   const int nft = D / 16;
   hipLaunchKernelGGL((bwd_sweep_kernel<T, D, 0>), dim3(p.B * p.Hq * nft), dim3(64), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_sweep_kernel<T, D, 1>), dim3(p.B * p.Hkv * nft), dim3(64), 0, st, p);
+  hipLaunchKernelGGL((bwd_v_kernel<T, D>), dim3((p.B * p.Hkv + 7) / 8 * 16), dim3(64 * (D / 32)), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int ntile = (p.L + TS - 1) / TS, nrun = (ntile + QPW - 1) / QPW;
   hipLaunchKernelGGL((bwd_win_q_kernel<T, D>), dim3(p.B * p.Hq * nrun), dim3(64), 0, st, p);
