@@ -47,7 +47,7 @@ namespace bwd {
 
 constexpr int TS = 16;              // tokens per sweep step / window tile
 constexpr float MILD_SPAN = 60.f;   // -P at most this for the split exponentials
-constexpr int QPW = 16;             // query tiles per wave in the window-q kernel
+constexpr int QPW = 24;             // query tiles per wave in the window-q kernel
 constexpr int FB_CHUNKS = 8;        // 64-row chunks per block of the feature-map backward
 
 template <typename T> struct F4;
@@ -789,6 +789,7 @@ template <typename T, int D> struct WinQLds {
   T dy[TS * LD];   // (1 - mix) dy of the query tile, rows
   T pm[TS * 20];   // meta probabilities [m][t]
   T dm[TS * 20];   // meta ds [m][t]
+  f32x4 cache[6][2][64];  // per lane: logits and dots of the first 6 tiles of a query row
 };
 
 template <typename T, int D>
@@ -863,50 +864,54 @@ __global__ __launch_bounds__(64) void bwd_win_q_kernel(BwdParams p) {
         for (int j = 0; j < KS; ++j) dp = mma(row_nat(V + (size_t)jr * D, j, kq, jr < L), dyf[j], dp);
       }
     };
-    // pass 1: max and sum
-    float mx = -1.0e30f, sum = 0.f;
-    for (int u = -1; u <= uhi; ++u) {
-      if (u >= 0 && u < ulo) continue;
-      f32x4 s;
-      logits(u, s);
-      float m2 = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    // tiles of the row: k = 0 the meta tile, k >= 1 key tile ulo + k - 1; the first NC tiles keep
+    // their logits and dots (in lane-private LDS) for the second pass
+    constexpr int NC = 6;
+    const int ntl = 2 + uhi - ulo;
+    auto tile_of = [&](int k) { return k == 0 ? -1 : ulo + k - 1; };
+    // pass 1 (online): row max, sum of e^{s - max}, and sum of e^{s - max} dp, rescaled as the max grows
+    float mx = -1.0e30f, sum = 0.f, dnum = 0.f;
+    auto online = [&](const f32x4 &sv, const f32x4 &dv) {
+      float m2 = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
       m2 = fmaxf(mx, wave_max_cols(m2));
-      sum *= __expf(mx - m2);
+      const float al = __expf(mx - m2);
+      sum *= al;
+      dnum *= al;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sum += (s[i] > -1.0e29f) ? __expf(s[i] - m2) : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const float e = (sv[i] > -1.0e29f) ? __expf(sv[i] - m2) : 0.f;
+        sum += e;
+        dnum += e * dv[i];
+      }
       mx = m2;
+    };
+    for (int k = 0; k < ntl; ++k) {
+      f32x4 sv, dv;
+      logits(tile_of(k), sv);
+      dots(tile_of(k), dv);
+      online(sv, dv);
+      if (k < NC) {
+        sm.cache[k][0][lane] = sv;
+        sm.cache[k][1][lane] = dv;
+      }
     }
     sum = wave_sum_cols(sum);
     const float inv = 1.f / sum;
-    // pass 2: D_t = sum_j p dp
-    float dsum = 0.f;
-    for (int u = -1; u <= uhi; ++u) {
-      if (u >= 0 && u < ulo) continue;
-      f32x4 s, dp;
-      logits(u, s);
-      dots(u, dp);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dsum += (s[i] > -1.0e29f) ? __expf(s[i] - mx) * inv * dp[i] : 0.f;
-    }
-    dsum = wave_sum_cols(dsum);
+    const float dsum = wave_sum_cols(dnum) * inv;  // D_t = sum_j p dp
     if (tok) {
       float *st = p.wstat + ((size_t)bh * L + t) * 4;
       if (kq == 0) *reinterpret_cast<f32x4 *>(st) = f32x4{mx, inv, dsum, 0.f};
     }
-    // pass 3: ds, dq, meta gradients
+    // pass 2: ds, dq, meta gradients
     f32x4 dq[NDT];  // lane (e = 16 et + r, kq): t = 4 kq + i
 #pragma unroll
     for (int et = 0; et < NDT; ++et) dq[et] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int u = -1; u <= uhi; ++u) {
-      if (u >= 0 && u < ulo) continue;
-      f32x4 s, dp;
-      logits(u, s);
-      dots(u, dp);
+    auto backprop = [&](int u, const f32x4 &sv, const f32x4 &dv) {
       float pr[4], ds[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pr[i] = (s[i] > -1.0e29f) ? __expf(s[i] - mx) * inv : 0.f;
-        ds[i] = pr[i] * (dp[i] - dsum);
+        pr[i] = (sv[i] > -1.0e29f) ? __expf(sv[i] - mx) * inv : 0.f;
+        ds[i] = pr[i] * (dv[i] - dsum);
       }
       // the key tile's rows into LDS for the transposed operand
       const int jr = TS * u + r;
@@ -938,6 +943,17 @@ __global__ __launch_bounds__(64) void bwd_win_q_kernel(BwdParams p) {
         }
       }
       __syncthreads();
+    };
+    for (int k = 0; k < ntl; ++k) {
+      f32x4 sv, dv;
+      if (k < NC) {
+        sv = sm.cache[k][0][lane];
+        dv = sm.cache[k][1][lane];
+      } else {
+        logits(tile_of(k), sv);
+        dots(tile_of(k), dv);
+      }
+      backprop(tile_of(k), sv, dv);
     }
     float *DQW = p.dqw + qo;
 #pragma unroll
