@@ -1144,16 +1144,17 @@ __global__ __launch_bounds__(256) void bwd_fb_kernel(BwdParams p) {
     }
 #pragma unroll
     for (int ks = 0; ks < FC / 32; ++ks) *reinterpret_cast<Frag<T> *>(sZ + (16 * w + r) * LDZ + 32 * ks + 8 * kq) = dzf[ks];
-    // dx[t][i] = sum_c dz[t][c] W[i][c] (lane (i = 16 it + r, kq): t = 16 w + 4 kq + ii)
+    // dx[t][i] = sum_c W[i][c] dz[t][c] (lane (t = 16 w + r, kq): i = 16 it + 4 kq + ii, four
+    // consecutive columns of row t per lane: one 8-byte store, one 16-byte load of the window part)
 #pragma unroll
     for (int it = 0; it < D / 16; ++it) {
       f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < FC / 32; ++ks) a = mma(dzf[ks], load8(sW + (16 * it + r) * LDW + 32 * ks + 8 * kq), a);
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int tt = c0 + 16 * w + 4 * kq + ii;
-        if (tt < L) DX[(size_t)tt * D + 16 * it + r] = from_f<T>(a[ii] + DXW[(size_t)tt * D + 16 * it + r]);
+      for (int ks = 0; ks < FC / 32; ++ks) a = mma(load8(sW + (16 * it + r) * LDW + 32 * ks + 8 * kq), dzf[ks], a);
+      if (tok) {
+        const size_t off = (size_t)t * D + 16 * it + 4 * kq;
+        const f32x4 xw = *reinterpret_cast<const f32x4 *>(DXW + off);
+        store4<T>(DX + off, a[0] + xw[0], a[1] + xw[1], a[2] + xw[2], a[3] + xw[3]);
       }
     }
     __syncthreads();  // x and dz rows of the chunk staged
