@@ -183,8 +183,8 @@ def test_fwd_whole_head_wide_window(gpu_lib, lz_opts, label, kw, nseg):
 @pytest.mark.parametrize("gate", ["one", "const:-0.1", "const:-0.5", "logsigmoid"])
 def test_fwd_whole_head_state_pass_drops_decayed_chunks(gpu_lib, lz_opts, gate):
     """The state pass leaves out the chunks of a segment that reach its end decayed below
-    e^-40 in every feature (with -0.1 per token: all but the last 7 of 13 chunks; -0.5: the
-    last 2), and splits the rest over its pieces; gamma = 1 keeps everything."""
+    e^-24 in every feature (with -0.1 per token: all but the last 4 of 13 chunks; -0.5: all but
+    the last one), and splits the rest over its pieces; gamma = 1 keeps everything."""
     lz_opts("fwd_segments", 2)
     lz_opts("fwd_split_shift", -1)  # the state pass, not the self-started split
     inp = make_fwd_inputs(B=2, Hq=2, Hkv=2, L=1600, d=128, W=64, M=4, dtype="bf16",

@@ -86,7 +86,7 @@ def test_fwd_hedgehog_large_features_beyond_the_decay_cutoff(gpu_lib, lz_opts, n
     """The unnormalised Hedgehog features can reach e^60 (logits up to the documented bound of
     about 80).  A chunk whose keys carry such features and that reaches the next segment decayed
     by about e^-45 still dominates its outputs (e^15 against O(e^3) terms), so the segment walks
-    must not drop it at the softmax map's cutoff of e^-40.  Gate -0.35 per token (22.4 per chunk),
+    must not drop it at the softmax map's cutoff of e^-24.  Gate -0.35 per token (22.4 per chunk),
     16 chunks; the last four keys of chunk `big_chunk` point along one column of W_phi so that
     one logit is 60.  With two segments the second starts at chunk 10 (split shift 2) and walks
     back; with three the state pass walks the middle block.  The global branch (mix = 1) of the
