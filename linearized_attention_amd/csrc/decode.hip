@@ -74,14 +74,21 @@ __global__ __launch_bounds__(256) void decode_phi_kernel(DecParams p) {
 
   const T *Wsrc = reinterpret_cast<const T *>(key ? p.wk : p.wq) + (size_t)h * p.w_stride;
   constexpr int FC = HH ? D / 2 : D;  // columns of W_phi
-  for (int idx = tid; idx < D * (FC / 8); idx += 256) {  // W[i][f] -> wt[f][i] (and -W -> wt[FC + f][i])
-    const int i = idx / (FC / 8), f0 = (idx % (FC / 8)) * 8;
-    const Frag<T> w = load8(Wsrc + (size_t)i * FC + f0);
+  // W[i][f] -> wt[f][i] (and -W -> wt[FC + f][i]).  The lanes of a wave take consecutive rows i
+  // (pairs of rows for 2-byte types, so that each lane writes one 4-byte word per feature): a
+  // wave's writes to a row of wt fall in distinct banks.  Every load below is issued before the
+  // first LDS write.
+  constexpr int RP = sizeof(T) == 2 ? 2 : 1;  // rows of W per item
+  constexpr int NR = D / RP;                  // row items
+  constexpr int NI = NR * (FC / 8);           // (row item, 8-column group) items
+  constexpr int IT = (NI + 255) / 256;
+  Frag<T> wa[IT][RP];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      wt[(f0 + j) * LDW + i] = w.v[j];
-      if constexpr (HH) wt[(FC + f0 + j) * LDW + i] = -w.v[j];
-    }
+  for (int it = 0; it < IT; ++it) {
+    const int idx = min(tid + 256 * it, NI - 1);
+    const int i0 = RP * (idx % NR), f0 = 8 * (idx / NR);
+#pragma unroll
+    for (int u = 0; u < RP; ++u) wa[it][u] = load8(Wsrc + (size_t)(i0 + u) * FC + f0);
   }
 
   // A fragments straight from global: row n = n0 + 16*wv + r
@@ -90,6 +97,26 @@ __global__ __launch_bounds__(256) void decode_phi_kernel(DecParams p) {
   Frag<T> a[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) a[s] = load8(X + 32 * s + 8 * kq);  // rows past N: clamped, not stored
+
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = tid + 256 * it;
+    if (NI % 256 == 0 || idx < NI) {
+      const int i0 = RP * (idx % NR), f0 = 8 * (idx / NR);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if constexpr (RP == 2) {
+          T pair[2] = {wa[it][0].v[j], wa[it][1].v[j]};
+          const uint32_t u = *reinterpret_cast<const uint32_t *>(pair);
+          *reinterpret_cast<uint32_t *>(wt + (f0 + j) * LDW + i0) = u;
+          if constexpr (HH) *reinterpret_cast<uint32_t *>(wt + (FC + f0 + j) * LDW + i0) = u ^ 0x80008000u;
+        } else {
+          wt[(f0 + j) * LDW + i0] = wa[it][0].v[j];
+          if constexpr (HH) wt[(FC + f0 + j) * LDW + i0] = -wa[it][0].v[j];
+        }
+      }
+    }
+  }
   __syncthreads();
 
   f32x4 acc[NC];

@@ -149,3 +149,45 @@ def test_decode_workload3_128_steps_sampled(gpu_lib):
     assert err <= TOL["bf16"] and serr <= TOL["bf16"]
     assert (pg.numpy() == 4096 + 128).all()
     assert torch.equal(rkg[torch.from_numpy(seqs)], torch.from_numpy(np.asarray(rko)).to(rkg.dtype))
+
+
+@pytest.mark.parametrize("fmap", ["softmax", "hedgehog"])
+def test_decode_steps_captured_in_a_graph_match_eager(gpu_lib, fmap):
+    """Consecutive decode steps captured once in a HIP graph (as a serving loop would run them)
+    and replayed three times, the buffers restored by eager copies between replays: every replay
+    gives the eager steps' outputs, state, ring and positions bit for bit."""
+    hh = fmap == "hedgehog"
+    dec = make_decode_inputs(N=8, Hq=4, Hkv=2, d=128, W=64, M=4, steps=6, pos0=60, dtype="bf16", seed=23,
+                             phi_cols=64 if hh else None)
+    fn = api.lizard_attn_decode_hedgehog if hh else api.lizard_attn_decode
+    w = [t.cuda() for t in (dec.w_phi_q, dec.w_phi_k, dec.t_k, dec.t_v)]
+    xs = [tuple(t.cuda() for t in s) for s in dec.steps]
+    init = [t.clone().cuda() for t in (dec.state, dec.ring_k, dec.ring_v, dec.pos)]
+    N, Hq, d = xs[0][0].shape
+    nb = api.lizard_attn_decode_workspace_bytes(N, Hq, xs[0][1].shape[1], d, xs[0][0].dtype)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    bufs = [t.clone() for t in init]
+    outs = [torch.empty_like(x[0]) for x in xs]
+
+    def steps():
+        for (q, k, v, lg), o in zip(xs, outs):
+            fn(*bufs, q, k, v, lg, *w, M=dec.M, mix=dec.mix, scale=dec.scale, out=o, workspace=ws)
+
+    steps()  # eager
+    torch.cuda.synchronize()
+    want = [t.clone() for t in outs + bufs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        steps()
+    for rep in range(3):
+        for b, i in zip(bufs, init):
+            b.copy_(i)
+        for o in outs:
+            o.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = outs + bufs
+        for name, g, e in zip([f"out{s}" for s in range(len(outs))] + ["state", "ring_k", "ring_v", "pos"], got, want):
+            assert torch.equal(g, e), f"replay {rep}: {name} differs from the eager steps"
+    _say(f"[decode graph, {fmap}] {len(xs)} steps captured, 3 replays equal to eager")
