@@ -140,17 +140,14 @@ __global__ __launch_bounds__(256) void decode_phi_kernel(DecParams p) {
       float m = DEC_NEG;
 #pragma unroll
       for (int c = 0; c < NC; ++c) m = fmaxf(m, acc[c][i]);
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+      m = row_max16(m);  // over the 16 lanes of the row (DPP, no LDS round trip)
       float s = 0.f;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         acc[c][i] = __expf(acc[c][i] - m);
         s += acc[c][i];
       }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
-      inv = 1.f / s;
+      inv = 1.f / row_sum16(s);
     }
     const int nr = n0 + 16 * wv + 4 * kq + i;
     if (nr < N) {
@@ -159,6 +156,15 @@ __global__ __launch_bounds__(256) void decode_phi_kernel(DecParams p) {
       for (int c = 0; c < NC; ++c) dst[16 * c + r] = acc[c][i] * inv;
     }
   }
+}
+
+// x summed over the lanes that share lane % O (O = 8, 16 or 32), in the order of an xor
+// butterfly over O, 2 O, ..; every lane gets the same bits.
+template <int O> __device__ __forceinline__ float sum_lanes_mod(float x) {
+  static_assert(O == 8 || O == 16 || O == 32, "lane stride");
+  if constexpr (O == 8) x += __shfl_xor(x, 8);
+  if constexpr (O <= 16) x = pair16_sum(x);
+  return pair32_sum(x);
 }
 
 template <typename T, int D, int GM>  // GM: query heads per pass (1 or DEC_MAXG)
@@ -302,8 +308,8 @@ __global__ __launch_bounds__(256, 2) void decode_step_kernel(DecParams p) {
       }
 #pragma unroll
       for (int u = 0; u < GM; ++u) {
-        acc[u] += __shfl_xor(acc[u], 1);
-        acc[u] += __shfl_xor(acc[u], 2);
+        acc[u] += dpp_f<DPP_XOR1>(acc[u]);
+        acc[u] += dpp_f<DPP_XOR2>(acc[u]);
       }
       if (in && kpart == 0)
         for (int u = 0; u < gp; ++u) slog[u][M + jj] = ok ? acc[u] * p.scale : DEC_NEG;
@@ -318,16 +324,14 @@ __global__ __launch_bounds__(256, 2) void decode_step_kernel(DecParams p) {
     for (int u = wv; u < gp; u += 4) {  // softmax per head (one wave per head)
       float m = DEC_NEG;
       for (int j = lane; j < M + W; j += 64) m = fmaxf(m, slog[u][j]);
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+      m = wave_max_all(m);
       float sum = 0.f;
       for (int j = lane; j < M + W; j += 64) {
         const float ex = __expf(slog[u][j] - m);  // masked entries: exp(-1e30) = 0
         slog[u][j] = ex;
         sum += ex;
       }
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) sum += __shfl_xor(sum, o);
+      sum = wave_sum_cols(row_sum16(sum));
       const float inv = 1.f / sum;
       for (int j = lane; j < M + W; j += 64) slog[u][j] *= inv;
     }
@@ -376,8 +380,7 @@ __global__ __launch_bounds__(256, 2) void decode_step_kernel(DecParams p) {
       for (int u = 0; u < GM; ++u)
 #pragma unroll
         for (int t = 0; t < 8; ++t)
-#pragma unroll
-          for (int o = F8; o < 64; o <<= 1) acc[u][t] += __shfl_xor(acc[u][t], o);
+          acc[u][t] = sum_lanes_mod<F8>(acc[u][t]);
       if (lane < F8) {
 #pragma unroll
         for (int u = 0; u < GM; ++u)
@@ -416,8 +419,7 @@ __global__ __launch_bounds__(256, 2) void decode_step_kernel(DecParams p) {
     for (int u = 0; u < GM; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int o = C4; o < 64; o <<= 1) yp[u][i] += __shfl_xor(yp[u][i], o);
+        yp[u][i] = sum_lanes_mod<C4>(yp[u][i]);
     __syncthreads();  // y_win partials complete
     for (int idx = tid; idx < gp * D; idx += 256) {  // y_win = ring part + meta values
       const int u = idx / D, e = idx % D;
