@@ -1217,13 +1217,24 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p, int D, int
     const size_t e = y % wsz;
     const int H = qs ? p.Hq : p.Hkv;
     const size_t base = qs ? 0 : (size_t)p.B * p.Hq * nsplit;
-    const int hlo = p.w_stride ? mat : 0, hhi = p.w_stride ? mat + 1 : H;
+    const int hlo = p.w_stride ? mat : 0, per = p.w_stride ? 1 : H;  // heads that share the matrix
+    // The partials of this output element in the order (batch, head, split), index idx; group grp
+    // sums those with idx % RG == grp in increasing idx, four loads in flight at a time.
+    const int total = p.B * per * nsplit;
+    auto part = [&](int idx) {
+      const int sp = idx % nsplit, bh = idx / nsplit, b = bh / per, h = hlo + bh % per;
+      return p.dw_part[(base + ((size_t)b * H + h) * nsplit + sp) * wsz + e];
+    };
     float acc = 0.f;
-    int idx = 0;  // running index of the partials of this output element
-    for (int b = 0; b < p.B; ++b)
-      for (int h = hlo; h < hhi; ++h)
-        for (int sp = 0; sp < nsplit; ++sp, ++idx)
-          if (idx % RG == grp) acc += p.dw_part[(base + ((size_t)b * H + h) * nsplit + sp) * wsz + e];
+    int idx = grp;
+    for (; idx + 3 * RG < total; idx += 4 * RG) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = part(idx + u * RG);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc += v[u];
+    }
+    for (; idx < total; idx += RG) acc += part(idx);
     p.dw_tmp[(size_t)grp * nw + x] = acc;
     return;
   }
