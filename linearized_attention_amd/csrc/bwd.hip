@@ -49,6 +49,7 @@ constexpr int TS = 16;              // tokens per sweep step / window tile
 constexpr float MILD_SPAN = 60.f;   // -P at most this for the split exponentials
 constexpr int QPW = 24;             // query tiles per wave in the window-q kernel
 constexpr int FB_CHUNKS = 8;        // 64-row chunks per block of the feature-map backward
+constexpr int NPF = 4;              // ring of step loads in the sweeps
 
 template <typename T> struct F4;
 template <> struct F4<bf16> { bf16x4 v; };
@@ -124,6 +125,33 @@ template <typename T> __device__ __forceinline__ F4<T> col_g(const T *base, int 
   F4<T> f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) f.v[j] = (r0 + j < L) ? base[(size_t)(r0 + j) * D + col] : from_f<T>(0.f);
+  return f;
+}
+// The same column values loaded ahead of their use: rows clamped into [0, L), each value in a
+// register of its own (a 2-byte value zero-extended), so that nothing packs them, and with that
+// waits for every load in flight, until the step that uses them; col_use then gives the operand,
+// zero at rows at or beyond L.
+template <typename T> struct Col4 {
+  using R = typename std::conditional<sizeof(T) == 2, uint32_t, float>::type;
+  R x[4];
+};
+template <typename T> __device__ __forceinline__ Col4<T> col_ld(const T *base, int D, int r0, int col, int L) {
+  Col4<T> c;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const size_t off = (size_t)min(r0 + j, L - 1) * D + col;
+    if constexpr (sizeof(T) == 2) c.x[j] = *reinterpret_cast<const uint16_t *>(base + off);
+    else c.x[j] = base[off];
+  }
+  return c;
+}
+template <typename T> __device__ __forceinline__ F4<T> col_use(const Col4<T> &c, int r0, int L) {
+  F4<T> f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (sizeof(T) == 2) f.v[j] = __builtin_bit_cast(T, (uint16_t)((r0 + j < L) ? c.x[j] : 0u));
+    else f.v[j] = (r0 + j < L) ? c.x[j] : 0.f;
+  }
   return f;
 }
 __device__ __forceinline__ void colf_g(const float *base, int D, int r0, int col, int L, float (&x)[4]) {
@@ -298,33 +326,36 @@ __device__ void sweep_f(const BwdParams &p, LdsF<T, D> &sm, int b, int hq, int f
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) S[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const F4<T> tri = tri_le<T>(r, kq);
-  // a step's loads: dy and v rows c0 + r (interleaved), log gamma and phi_k columns f0 + r; the
-  // next step's are in flight while this one is computed
-  Frag<T> dyr[NKS], vr[NKS];
-  F4<T> lgr;
-  F4<float> pkr;
-  auto load_step = [&](int c0) {
-    const bool ok = c0 + r < L;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      dyr[ks] = row_il(DY + (size_t)(c0 + r) * D, ks, kq, ok);
-      vr[ks] = row_il(V + (size_t)(c0 + r) * D, ks, kq, ok);
-    }
-    lgr = col_g(LG, D, c0 + 4 * kq, f0 + r, L);
-    pkr = col_g(PK, D, c0 + 4 * kq, f0 + r, L);
+  // a step's loads: dy and v rows c0 + r (interleaved), log gamma and phi_k columns f0 + r, rows
+  // clamped into the sequence (zeroed at use where that matters).  One wave per SIMD has nothing
+  // else to hide their latency, so they are issued NPF - 1 steps ahead, at the end of the step
+  // that frees their registers, into a ring of register sets (the loop below is unrolled NPF
+  // times, so each set keeps fixed registers).
+  struct Buf {
+    Frag<T> dy[NKS], v[NKS];
+    Col4<T> lg;
+    Col4<float> pk;
   };
-  load_step(0);
-  for (int c0 = 0; c0 < L; c0 += TS) {
-    Frag<T> dyf[NKS], vf[NKS];
-    const bool rok = c0 + r < L;
+  Buf ring[NPF];
+  auto load_step = [&](Buf &bf, int c0) {
+    const size_t row = (size_t)min(c0 + r, L - 1) * D;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      dyf[ks] = dyr[ks];
-      vf[ks] = vr[ks];
+      bf.dy[ks] = row_il(DY + row, ks, kq, true);
+      bf.v[ks] = row_il(V + row, ks, kq, true);
     }
-    const F4<T> lgc = lgr;
-    const F4<float> pkc = pkr;
-    if (c0 + TS < L) load_step(c0 + TS);
+    bf.lg = col_ld(LG, D, c0 + 4 * kq, f0 + r, L);
+    bf.pk = col_ld(PK, D, c0 + 4 * kq, f0 + r, L);
+  };
+  auto step = [&](Buf &bf, int c0) {
+    const bool rok = c0 + r < L;
+    // (opaque here, so that the packing of the columns stays in this step instead of following
+    // their loads, where it would wait for every load in flight)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(bf.lg.x[j]), "+v"(bf.pk.x[j]));
+    const F4<T> lgc = col_use(bf.lg, c0 + 4 * kq, L);
+    const F4<float> pkc = col_use(bf.pk, c0 + 4 * kq, L);
+    const Frag<T> *dyf = bf.dy, *vf = bf.v;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) store_il(sm.a + r * LD, vf[ks], ks, kq);
     // ---- prefix sums: pK (lane (f = f0 + r, kq): s = 4 kq + i), pQ (lane (t = r, kq): f = f0 + 4 kq + i)
@@ -394,7 +425,18 @@ __device__ void sweep_f(const BwdParams &p, LdsF<T, D> &sm, int b, int hq, int f
       S[dt] = m16_tf<T>(lds_col4(sm.a, LD, 4 * kq, 16 * dt), kb, S[dt]);
     }
     __syncthreads();  // v rows read before the next step overwrites them
+    load_step(bf, c0 + NPF * TS);
+  };
+#pragma unroll
+  for (int u = 0; u < NPF; ++u) load_step(ring[u], u * TS);
+  int c00 = 0;
+  for (; c00 + NPF * TS <= L; c00 += NPF * TS) {
+#pragma unroll
+    for (int u = 0; u < NPF; ++u) step(ring[u], c00 + u * TS);
   }
+#pragma unroll
+  for (int u = 0; u < NPF; ++u)  // the last 1 .. NPF steps (a ragged tail can leave NPF)
+    if (c00 + u * TS < L) step(ring[u], c00 + u * TS);
 }
 
 // Role R: dphi_k for features f0 .. f0 + 15 of key/value head hk and dlg of those features.
