@@ -444,6 +444,7 @@ template <typename T, int D>
 __device__ void sweep_r(const BwdParams &p, LdsR<T, D> &sm, int b, int hk, int ft0) {
   constexpr int NDT = D / 16, NKS = D / 32, LD = LdsR<T, D>::LD, LDF = LdsR<T, D>::LDF;
   const int lane = threadIdx.x & 63, r = lane & 15, kq = lane >> 4;
+  constexpr int NPR = NPF - 1;  // (role R loads more per step than role F)
   const int L = p.L, G = p.G, f0 = 16 * ft0;
   const size_t kvo = ((size_t)b * p.Hkv + hk) * L * D;
   const T *V = reinterpret_cast<const T *>(p.v) + kvo;
@@ -460,36 +461,47 @@ __device__ void sweep_r(const BwdParams &p, LdsR<T, D> &sm, int b, int hk, int f
   for (int j = 0; j < 4; ++j) ufs[j] = (4 * kq + j >= r) ? 1.f : 0.f;
   float rsum = 0.f;  // dlg of feature f0 + r summed over the later steps
   const int nstep = (L + TS - 1) / TS;
-  // loads of a step (v rows, log gamma and phi_k columns) and of a (step, query head) pair (dy
-  // rows, phi_q and dphi_q columns): the next ones are in flight while the current ones are used
-  Frag<T> vr[NKS], dyr[NKS];
-  F4<T> lgr;
-  F4<float> pkr, pqr;
-  float dqr[4];
-  auto load_step = [&](int c0) {
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) vr[ks] = row_il(V + (size_t)(c0 + r) * D, ks, kq, c0 + r < L);
-    lgr = col_g(LG, D, c0 + 4 * kq, f0 + r, L);
-    pkr = col_g(PK, D, c0 + 4 * kq, f0 + r, L);
+  // Loads of a step (v rows, log gamma and phi_k columns) with those of its first query head (dy
+  // rows, phi_q and dphi_q columns), rows clamped into the sequence (zeroed at use where that
+  // matters): a ring of NPR register sets, each refilled at the end of the step that used it, as
+  // in role F.  Further query heads of a group are loaded one head ahead.
+  struct Head {
+    Frag<T> dy[NKS];
+    Col4<float> pq, dq;
   };
-  auto load_head = [&](int c0, int g) {
+  struct Buf {
+    Frag<T> v[NKS];
+    Col4<T> lg;
+    Col4<float> pk;
+    Head h0;
+  };
+  auto load_head = [&](Head &hd, int c0, int g) {
     const size_t qo = ((size_t)b * p.Hq + hk * G + g) * L * D;
     const T *DY = reinterpret_cast<const T *>(p.dy) + qo;
+    const size_t row = (size_t)min(c0 + r, L - 1) * D;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) dyr[ks] = row_il(DY + (size_t)(c0 + r) * D, ks, kq, c0 + r < L);
-    pqr = col_g(p.phq + qo, D, c0 + 4 * kq, f0 + r, L);
-    colf_g(p.dphq + qo, D, c0 + 4 * kq, f0 + r, L, dqr);
+    for (int ks = 0; ks < NKS; ++ks) hd.dy[ks] = row_il(DY + row, ks, kq, true);
+    hd.pq = col_ld(p.phq + qo, D, c0 + 4 * kq, f0 + r, L);
+    hd.dq = col_ld(p.dphq + qo, D, c0 + 4 * kq, f0 + r, L);
   };
-  load_step((nstep - 1) * TS);
-  load_head((nstep - 1) * TS, 0);
-  for (int st = nstep - 1; st >= 0; --st) {
-    const int c0 = st * TS;
-    Frag<T> vf[NKS];
+  auto load_step = [&](Buf &bf, int st) {
+    const int c0 = max(st, 0) * TS;
+    const size_t row = (size_t)min(c0 + r, L - 1) * D;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) vf[ks] = vr[ks];
-    const F4<T> lgc = lgr;
-    const F4<float> pkc = pkr;
-    if (st > 0) load_step(c0 - TS);
+    for (int ks = 0; ks < NKS; ++ks) bf.v[ks] = row_il(V + row, ks, kq, true);
+    bf.lg = col_ld(LG, D, c0 + 4 * kq, f0 + r, L);
+    bf.pk = col_ld(PK, D, c0 + 4 * kq, f0 + r, L);
+    load_head(bf.h0, c0, 0);
+  };
+  auto step = [&](Buf &bf, int st) {
+    const int c0 = st * TS;
+    // (opaque here, so that the columns are packed in this step, not after their loads)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      asm volatile("" : "+v"(bf.lg.x[j]), "+v"(bf.pk.x[j]), "+v"(bf.h0.pq.x[j]), "+v"(bf.h0.dq.x[j]));
+    const F4<T> lgc = col_use(bf.lg, c0 + 4 * kq, L);
+    const F4<float> pkc = col_use(bf.pk, c0 + 4 * kq, L);
+    const Frag<T> *vf = bf.v;
     const f32x4 pK = mma16(tri, lgc, f32x4{0.f, 0.f, 0.f, 0.f});  // lane (f0 + r, kq): s = 4 kq + i
     const float Pf = __shfl(pK[3], 48 + r);
     const bool mild = wave_max_all(-Pf) <= MILD_SPAN;
@@ -516,21 +528,12 @@ __device__ void sweep_r(const BwdParams &p, LdsR<T, D> &sm, int b, int hk, int f
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) dS[dt][i] *= eP;
-    for (int g = 0; g < G; ++g) {
-      Frag<T> dyf[NKS];
+    // one query head of the group: its dy rows, phi_q and dphi_q columns
+    auto head = [&](const Frag<T> (&dyf)[NKS], const F4<float> &pqc, const F4<float> &dqc, int g) {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        dyf[ks] = dyr[ks];
-        store_il(sm.a + r * LD, dyf[ks], ks, kq);
-      }
-      const F4<float> pqc = pqr;
-      float dq4[4];
+      for (int ks = 0; ks < NKS; ++ks) store_il(sm.a + r * LD, dyf[ks], ks, kq);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dq4[j] = dqr[j];
-      if (g + 1 < G) load_head(c0, g + 1);
-      else if (st > 0) load_head(c0 - TS, 0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) gq[j] += f4_at(pqc, j) * dq4[j];
+      for (int j = 0; j < 4; ++j) gq[j] += f4_at(pqc, j) * f4_at(dqc, j);
       // E[t][s] = dy_t . v_s (lane (s = r, kq): t = 4 kq + i), masked to t >= s
       f32x4 e = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -570,6 +573,14 @@ __device__ void sweep_r(const BwdParams &p, LdsR<T, D> &sm, int b, int hk, int f
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) dS[dt] = m16_tf<T>(lds_col4(sm.a, LD, 4 * kq, 16 * dt), qt, dS[dt]);
       __syncthreads();
+    };
+    Head hn;  // further query heads, one ahead
+    if (G > 1) load_head(hn, c0, 1);
+    head(bf.h0.dy, col_use(bf.h0.pq, c0 + 4 * kq, L), col_use(bf.h0.dq, c0 + 4 * kq, L), 0);
+    for (int g = 1; g < G; ++g) {
+      Head hc = hn;
+      if (g + 1 < G) load_head(hn, c0, g + 1);
+      head(hc.dy, col_use(hc.pq, c0 + 4 * kq, L), col_use(hc.dq, c0 + 4 * kq, L), g);
     }
     // ---- dphi_k[s][f] = mix e^{-p_s} (e^{P} X + sum_g intra)   (lane (f0 + r, kq): s = 4 kq + i)
     float dpk[4];
@@ -597,7 +608,20 @@ __device__ void sweep_r(const BwdParams &p, LdsR<T, D> &sm, int b, int hk, int f
     }
     rsum += tot;
     if (!mild) __syncthreads();
+    load_step(bf, st - NPR);
+  };
+  // steps st = nstep - 1 - k for k = 0, 1, ..; ring slot k % NPR
+  Buf ring[NPR];
+#pragma unroll
+  for (int u = 0; u < NPR; ++u) load_step(ring[u], nstep - 1 - u);
+  int k = 0;
+  for (; k + NPR <= nstep; k += NPR) {
+#pragma unroll
+    for (int u = 0; u < NPR; ++u) step(ring[u], nstep - 1 - (k + u));
   }
+#pragma unroll
+  for (int u = 0; u < NPR; ++u)
+    if (k + u < nstep) step(ring[u], nstep - 1 - (k + u));
 }
 
 // One wave per block; ROLE 0: F (blocks: batch, query head, feature tile), 2: R (batch, key/value
