@@ -145,6 +145,15 @@ template <typename T> __device__ __forceinline__ Col4<T> col_ld(const T *base, i
   }
   return c;
 }
+// Keeps the compiler from moving work on a fragment loaded ahead up to its load.
+template <typename T> __device__ __forceinline__ void opaque_frag(Frag<T> &f) {
+  if constexpr (sizeof(T) == 2) {
+    asm volatile("" : "+v"(f.v));
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(f.v[j]));
+  }
+}
 template <typename T> __device__ __forceinline__ F4<T> col_use(const Col4<T> &c, int r0, int L) {
   F4<T> f;
 #pragma unroll
@@ -683,25 +692,46 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_v_kernel(BwdParams p) {
   for (int ft = 0; ft < NFT; ++ft) dS[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
   const F4<T> tri = tri_le<T>(r, kq);
   auto qrow = [&](int g) { return ((size_t)b * p.Hq + hk * G + g) * L * D; };
-  // the slice rows (token c0 + r, features 32 w + slot) and this wave's dy column of a step
-  auto load_step = [&](int c0, Frag<T> &lgf, Frag<float> &pkf, Frag<float> &pqf, F4<T> &dyc, int g) {
-    const bool rok = c0 + r < L;
-    lgf = row_il(LG + (size_t)(c0 + r) * D, w, kq, rok);
-    pkf = row_il(PK + (size_t)(c0 + r) * D, w, kq, rok);
-    pqf = row_il(p.phq + qrow(g) + (size_t)(c0 + r) * D, w, kq, rok);
-    dyc = col_g(reinterpret_cast<const T *>(p.dy) + qrow(g), D, c0 + 4 * kq, dv0 + r, L);
+  // A step's loads: the slice rows (token c0 + r, features 32 w + slot) of log gamma, phi_k and the
+  // first query head's phi_q, and this wave's dy column of that head; rows clamped into the
+  // sequence (zeroed at use where that matters).  A ring of NPF register sets, each refilled at
+  // the end of the step that used it (the loop below is unrolled NPF times).
+  struct Buf {
+    Frag<T> lg;
+    Frag<float> pk, pq;
+    Col4<T> dy;
+  };
+  auto load_step = [&](Buf &bf, int st) {
+    const int c0 = max(st, 0) * TS;
+    const size_t row = (size_t)min(c0 + r, L - 1) * D;
+    bf.lg = row_il(LG + row, w, kq, true);
+    bf.pk = row_il(PK + row, w, kq, true);
+    bf.pq = row_il(p.phq + qrow(0) + row, w, kq, true);
+    bf.dy = col_ld(reinterpret_cast<const T *>(p.dy) + qrow(0), D, c0 + 4 * kq, dv0 + r, L);
   };
   auto load_head = [&](int c0, Frag<float> &pqf, F4<T> &dyc, int g) {
     pqf = row_il(p.phq + qrow(g) + (size_t)(c0 + r) * D, w, kq, c0 + r < L);
     dyc = col_g(reinterpret_cast<const T *>(p.dy) + qrow(g), D, c0 + 4 * kq, dv0 + r, L);
   };
   const int nstep = (L + TS - 1) / TS;
-  Frag<T> lgf;
-  Frag<float> pkf, pqf;
-  F4<T> dyc;
-  load_step((nstep - 1) * TS, lgf, pkf, pqf, dyc, 0);
-  for (int st = nstep - 1; st >= 0; --st) {
+  auto step = [&](Buf &bf, int st) {
     const int c0 = st * TS;
+    const bool rok = c0 + r < L;
+    // (opaque here, so that the packing and zeroing below stay in this step instead of following
+    // the loads, where they would wait for every load in flight)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(bf.dy.x[j]));
+    opaque_frag(bf.lg);
+    opaque_frag(bf.pk);
+    opaque_frag(bf.pq);
+    F4<T> dyc = col_use(bf.dy, c0 + 4 * kq, L);
+    Frag<T> lgf = bf.lg;
+    Frag<float> pkf = bf.pk, pqf = bf.pq;
+    if (!rok) {  // rows beyond the sequence: no decay, no features
+      lgf = frag_zero<T>();
+      pkf = frag_zero<float>();
+      pqf = frag_zero<float>();
+    }
     // ---- the slice's prefix sums (lane (t = r, kq): feature 32 w + 16 h + 4 kq + i) and totals
     store_il(lgs + r * LDL, lgf, 0, kq);
     __builtin_amdgcn_wave_barrier();
@@ -745,11 +775,6 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_v_kernel(BwdParams p) {
       }
       if (lane == 0) sm.span[w] = spn;
     }
-    // the next step's rows in flight
-    Frag<T> lgf_n;
-    Frag<float> pkf_n, pqf_n;
-    F4<T> dyc_n;
-    if (st > 0) load_step(c0 - TS, lgf_n, pkf_n, pqf_n, dyc_n, 0);
     __syncthreads();  // B1: the step's operands visible
     float spall = 0.f;
 #pragma unroll
@@ -834,13 +859,20 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_v_kernel(BwdParams p) {
       const int s2 = c0 + 4 * kq + i;
       if (s2 < L) DVG[(size_t)s2 * D + dv0 + r] = p.mix * acc[i];
     }
-    if (st > 0) {
-      lgf = lgf_n;
-      pkf = pkf_n;
-      pqf = pqf_n;
-      dyc = dyc_n;
-    }
+    load_step(bf, st - NPF);
+  };
+  // steps st = nstep - 1 - k for k = 0, 1, ..; ring slot k % NPF
+  Buf ring[NPF];
+#pragma unroll
+  for (int u = 0; u < NPF; ++u) load_step(ring[u], nstep - 1 - u);
+  int k = 0;
+  for (; k + NPF <= nstep; k += NPF) {
+#pragma unroll
+    for (int u = 0; u < NPF; ++u) step(ring[u], nstep - 1 - (k + u));
   }
+#pragma unroll
+  for (int u = 0; u < NPF; ++u)
+    if (k + u < nstep) step(ring[u], nstep - 1 - (k + u));
 }
 
 // ======================================================================== 4. window, query side
