@@ -51,6 +51,8 @@ constexpr int QPW = 24;             // query tiles per wave in the window-q kern
 constexpr int FB_CHUNKS = 8;        // 64-row chunks per block of the feature-map backward
 constexpr int NPF = 4;              // ring of step loads in the sweeps
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 template <typename T> struct F4;
 template <> struct F4<bf16> { bf16x4 v; };
 template <> struct F4<float> { float v[4]; };
@@ -304,12 +306,6 @@ __global__ __launch_bounds__(256) void bwd_phi_kernel(BwdParams p) {
 // ======================================================================== 2/3. sweeps
 // Wave-private LDS tiles of a step: T rows of 16 tokens (8-byte aligned transposed reads), and
 // fp32 tables of the exact path (16 tokens x the features the wave handles).
-template <typename T, int D> struct LdsF {
-  static constexpr int LD = D + 8, LDF = 20;
-  T a[TS * LD];          // rows of v
-  float pf[TS * LDF];    // p[s][f - f0]
-  float ph1[TS * LDF];   // phi_k[s][f - f0]
-};
 template <typename T, int D> struct LdsR {
   static constexpr int LD = D + 8, LDF = 20;
   T a[TS * LD];          // rows of dy
@@ -318,135 +314,6 @@ template <typename T, int D> struct LdsR {
   float ph2[TS * LDF];   // in-step sums of the exact path
   float dd[TS * 17];     // E[t][s] = dy_t . v_s
 };
-
-// Role F: dphi_q for features f0 .. f0 + 15 of query head hq (see the top of the file).
-template <typename T, int D>
-__device__ void sweep_f(const BwdParams &p, LdsF<T, D> &sm, int b, int hq, int ft0) {
-  constexpr int NDT = D / 16, NKS = D / 32, LD = LdsF<T, D>::LD, LDF = LdsF<T, D>::LDF;
-  const int lane = threadIdx.x & 63, r = lane & 15, kq = lane >> 4;
-  const int L = p.L, hk = hq / p.G, f0 = 16 * ft0;
-  const size_t kvo = ((size_t)b * p.Hkv + hk) * L * D, qo = ((size_t)b * p.Hq + hq) * L * D;
-  const T *V = reinterpret_cast<const T *>(p.v) + kvo;
-  const T *LG = reinterpret_cast<const T *>(p.lg) + kvo;
-  const float *PK = p.phk + kvo;
-  const T *DY = reinterpret_cast<const T *>(p.dy) + qo;
-  float *DPQ = p.dphq + qo;
-  f32x4 S[NDT];  // S^T[dv = 16 dt + 4 kq + i][f = f0 + r]
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) S[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const F4<T> tri = tri_le<T>(r, kq);
-  // a step's loads: dy and v rows c0 + r (interleaved), log gamma and phi_k columns f0 + r, rows
-  // clamped into the sequence (zeroed at use where that matters).  One wave per SIMD has nothing
-  // else to hide their latency, so they are issued NPF - 1 steps ahead, at the end of the step
-  // that frees their registers, into a ring of register sets (the loop below is unrolled NPF
-  // times, so each set keeps fixed registers).
-  struct Buf {
-    Frag<T> dy[NKS], v[NKS];
-    Col4<T> lg;
-    Col4<float> pk;
-  };
-  Buf ring[NPF];
-  auto load_step = [&](Buf &bf, int c0) {
-    const size_t row = (size_t)min(c0 + r, L - 1) * D;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      bf.dy[ks] = row_il(DY + row, ks, kq, true);
-      bf.v[ks] = row_il(V + row, ks, kq, true);
-    }
-    bf.lg = col_ld(LG, D, c0 + 4 * kq, f0 + r, L);
-    bf.pk = col_ld(PK, D, c0 + 4 * kq, f0 + r, L);
-  };
-  auto step = [&](Buf &bf, int c0) {
-    const bool rok = c0 + r < L;
-    // (opaque here, so that the packing of the columns stays in this step instead of following
-    // their loads, where it would wait for every load in flight)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(bf.lg.x[j]), "+v"(bf.pk.x[j]));
-    const F4<T> lgc = col_use(bf.lg, c0 + 4 * kq, L);
-    const F4<float> pkc = col_use(bf.pk, c0 + 4 * kq, L);
-    const Frag<T> *dyf = bf.dy, *vf = bf.v;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) store_il(sm.a + r * LD, vf[ks], ks, kq);
-    // ---- prefix sums: pK (lane (f = f0 + r, kq): s = 4 kq + i), pQ (lane (t = r, kq): f = f0 + 4 kq + i)
-    const f32x4 pK = mma16(tri, lgc, f32x4{0.f, 0.f, 0.f, 0.f});
-    const f32x4 pQ = mma16(lgc, tri, f32x4{0.f, 0.f, 0.f, 0.f});
-    const float Pf = __shfl(pK[3], 48 + r);  // chunk total of feature f0 + r
-    const bool mild = wave_max_all(-Pf) <= MILD_SPAN;
-    // ---- D^T[s][t] = v_s . dy_t (lane (t = r, kq): s = 4 kq + i), masked to s <= t
-    f32x4 dT = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) dT = mma(vf[ks], dyf[ks], dT);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dT[i] = (4 * kq + i <= r) ? dT[i] : 0.f;
-    // ---- inter: Out^T[f][t] = sum_dv S[f][dv] dy_t[dv]
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      float x[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = S[2 * ks + (j >> 2)][j & 3];
-      o = mmx_ft<T>(x, dyf[ks], o);
-    }
-    if (mild) {
-      float kt[4], dm[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        kt[j] = f4_at(pkc, j) * __expf(-pK[j]);
-        dm[j] = dT[j];
-      }
-      o = m16_ff<T>(kt, dm, o);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] *= __expf(pQ[i]);
-    } else {
-      // exact: o = e^{p_t} o_inter + sum_{s <= t} D[t][s] phi_k[s][f] e^{p_t[f] - p_s[f]}
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sm.pf[(4 * kq + i) * LDF + r] = pK[i];
-        sm.ph1[(4 * kq + i) * LDF + r] = f4_at(pkc, i);
-      }
-      __syncthreads();
-      float dts[16];
-#pragma unroll
-      for (int s = 0; s < 16; ++s) dts[s] = __shfl(dT[s & 3], r + 16 * (s >> 2));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int fl = 4 * kq + i;
-        float a = o[i] * __expf(pQ[i]);
-        for (int s = 0; s <= r; ++s) a += dts[s] * sm.ph1[s * LDF + fl] * __expf(pQ[i] - sm.pf[s * LDF + fl]);
-        o[i] = a;
-      }
-      __syncthreads();
-    }
-    if (rok) {
-      *reinterpret_cast<f32x4 *>(DPQ + (size_t)(c0 + r) * D + f0 + 4 * kq) =
-          f32x4{p.mix * o[0], p.mix * o[1], p.mix * o[2], p.mix * o[3]};
-    }
-    // ---- state: S^T = e^{P} S^T + V^T Kbar, Kbar[s][f] = phi_k[s][f] e^{P - p_s[f]}
-    float kb[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) kb[j] = f4_at(pkc, j) * __expf(Pf - pK[j]);
-    const float eP = __expf(Pf);
-    __syncthreads();  // v rows staged
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) S[dt][i] *= eP;
-      S[dt] = m16_tf<T>(lds_col4(sm.a, LD, 4 * kq, 16 * dt), kb, S[dt]);
-    }
-    __syncthreads();  // v rows read before the next step overwrites them
-    load_step(bf, c0 + NPF * TS);
-  };
-#pragma unroll
-  for (int u = 0; u < NPF; ++u) load_step(ring[u], u * TS);
-  int c00 = 0;
-  for (; c00 + NPF * TS <= L; c00 += NPF * TS) {
-#pragma unroll
-    for (int u = 0; u < NPF; ++u) step(ring[u], c00 + u * TS);
-  }
-#pragma unroll
-  for (int u = 0; u < NPF; ++u)  // the last 1 .. NPF steps (a ragged tail can leave NPF)
-    if (c00 + u * TS < L) step(ring[u], c00 + u * TS);
-}
 
 // Role R: dphi_k for features f0 .. f0 + 15 of key/value head hk and dlg of those features.
 template <typename T, int D>
@@ -633,19 +500,193 @@ __device__ void sweep_r(const BwdParams &p, LdsR<T, D> &sm, int b, int hk, int f
     if (k + u < nstep) step(ring[u], nstep - 1 - (k + u));
 }
 
-// One wave per block; ROLE 0: F (blocks: batch, query head, feature tile), 2: R (batch, key/value
-// head, feature tile).  Role V runs in bwd_v_kernel below.
-template <typename T, int D, int ROLE>
-__global__ __launch_bounds__(64) void bwd_sweep_kernel(BwdParams p) {
+// Role R: one wave per block (batch, key/value head, feature tile).
+template <typename T, int D>
+__global__ __launch_bounds__(64) void bwd_sweep_r_kernel(BwdParams p) {
   constexpr int NT = D / 16;
   const int tile = blockIdx.x % NT, bh = blockIdx.x / NT;
-  if constexpr (ROLE == 0) {
-    __shared__ LdsF<T, D> sm;
-    sweep_f<T, D>(p, sm, bh / p.Hq, bh % p.Hq, tile);
-  } else {
-    __shared__ LdsR<T, D> sm;
-    sweep_r<T, D>(p, sm, bh / p.Hkv, bh % p.Hkv, tile);
+  __shared__ LdsR<T, D> sm;
+  sweep_r<T, D>(p, sm, bh / p.Hkv, bh % p.Hkv, tile);
+}
+
+// Role F: dphi_q for the features of query head hq (see the top of the file).  Workgroups of four
+// waves, one 16-feature tile each (D / 64 workgroups per head, 8 launch slots apart: one XCD).
+// Each step's tiles -- dy and v rows (all D columns), log gamma and phi_k rows (the workgroup's 64
+// features) -- are loaded once per workgroup with 16-byte loads, NPF steps ahead into registers,
+// and written into one of two LDS buffers at the step's start; every wave reads its operands
+// there.  One barrier per step: a buffer is rewritten two steps after it was read, and every wave
+// has passed the barrier between.
+template <typename T, int D> struct LdsF2 {
+  static constexpr int LD = D + 16 / (int)sizeof(T);  // T rows of dy and v
+  static constexpr int LDG = 64 + 16 / (int)sizeof(T); // T rows of log gamma (64 features)
+  static constexpr int LDP = 68;                       // fp32 rows of phi_k (64 features)
+  static constexpr int LDF = 20;
+  T dy[2][TS * LD], v[2][TS * LD], lg[2][TS * LDG];
+  float pk[2][TS * LDP];
+  float pf[4][TS * LDF], ph1[4][TS * LDF];  // per wave: exact-path tables
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256, 1) void bwd_f_kernel(BwdParams p) {
+  using SM = LdsF2<T, D>;
+  constexpr int NDT = D / 16, NKS = D / 32, LD = SM::LD, LDG = SM::LDG, LDP = SM::LDP, LDF = SM::LDF;
+  constexpr int NH = D / 64;                      // workgroups per head
+  constexpr int RP = D * (int)sizeof(T) / 16;     // 16-byte pieces per dy / v row
+  constexpr int NPC = TS * RP;                    // pieces per tile (<= 256)
+  __shared__ SM sm;
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, kq = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int x = blockIdx.x;
+  const int bh = NH == 2 ? (x >> 4) * 8 + (x & 7) : x, half = NH == 2 ? (x >> 3) & 1 : 0;
+  if (bh >= p.B * p.Hq) return;  // padding of the launch to whole XCD pairs
+  const int b = bh / p.Hq, hq = bh % p.Hq;
+  const int L = p.L, hk = hq / p.G, fw = 64 * half, f0 = fw + 16 * w;
+  const size_t kvo = ((size_t)b * p.Hkv + hk) * L * D, qo = ((size_t)b * p.Hq + hq) * L * D;
+  const T *V = reinterpret_cast<const T *>(p.v) + kvo;
+  const T *LG = reinterpret_cast<const T *>(p.lg) + kvo;
+  const float *PK = p.phk + kvo;
+  const T *DY = reinterpret_cast<const T *>(p.dy) + qo;
+  float *DPQ = p.dphq + qo;
+  float *pfw = sm.pf[w], *ph1w = sm.ph1[w];
+  f32x4 S[NDT];  // S^T[dv = 16 dt + 4 kq + i][f = f0 + r]
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) S[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const F4<T> tri = tri_le<T>(r, kq);
+  // this thread's pieces of a step: dy and v piece tid (row tid / RP), and four log gamma and
+  // phi_k values (row tid / 16, features fw + 4 (tid % 16) ..)
+  const int prow = tid / RP, pcol = (tid % RP) * (16 / (int)sizeof(T));
+  const int grow = tid / 16, gcol = 4 * (tid % 16);
+  struct Pre {
+    u32x4 dy, v;
+    F4<T> lg;
+    f32x4 pk;
+  };
+  auto load_pre = [&](Pre &pr, int c0) {  // rows clamped into the sequence
+    if (tid < NPC) {
+      const size_t o = (size_t)min(c0 + prow, L - 1) * D + pcol;
+      pr.dy = *reinterpret_cast<const u32x4 *>(DY + o);
+      pr.v = *reinterpret_cast<const u32x4 *>(V + o);
+    }
+    const size_t og = (size_t)min(c0 + grow, L - 1) * D + fw + gcol;
+    if constexpr (sizeof(T) == 2) {
+      pr.lg.v = *reinterpret_cast<const bf16x4 *>(LG + og);
+    } else {
+      const f32x4 t = *reinterpret_cast<const f32x4 *>(LG + og);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pr.lg.v[j] = t[j];
+    }
+    pr.pk = *reinterpret_cast<const f32x4 *>(PK + og);
+  };
+  auto store_pre = [&](const Pre &pr, int buf, int c0) {  // rows at or beyond L: no decay, no phi_k
+    if (tid < NPC) {
+      *reinterpret_cast<u32x4 *>(sm.dy[buf] + prow * LD + pcol) = pr.dy;
+      *reinterpret_cast<u32x4 *>(sm.v[buf] + prow * LD + pcol) = pr.v;
+    }
+    const bool in = c0 + grow < L;
+    T *g = sm.lg[buf] + grow * LDG + gcol;
+    float *k = sm.pk[buf] + grow * LDP + gcol;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      g[j] = in ? pr.lg.v[j] : from_f<T>(0.f);
+      k[j] = in ? pr.pk[j] : 0.f;
+    }
+  };
+  auto step = [&](Pre &pr, int buf, int c0) {
+    store_pre(pr, buf, c0);
+    load_pre(pr, c0 + NPF * TS);  // this ring slot's registers are free now
+    __syncthreads();              // the step's tiles visible
+    const bool rok = c0 + r < L;
+    const T *ty = sm.dy[buf] + r * LD, *tv = sm.v[buf] + r * LD;
+    Frag<T> dyf[NKS], vf[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      dyf[ks] = load4x2(ty + 32 * ks + 4 * kq, ty + 32 * ks + 16 + 4 * kq);
+      vf[ks] = load4x2(tv + 32 * ks + 4 * kq, tv + 32 * ks + 16 + 4 * kq);
+    }
+    const F4<T> lgc = lds_col4(sm.lg[buf], LDG, 4 * kq, 16 * w);  // rows 4 kq + j, feature f0 + r
+    F4<float> pkc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pkc.v[j] = sm.pk[buf][(4 * kq + j) * LDP + 16 * w + r];
+    // ---- prefix sums: pK (lane (f = f0 + r, kq): s = 4 kq + i), pQ (lane (t = r, kq): f = f0 + 4 kq + i)
+    const f32x4 pK = mma16(tri, lgc, f32x4{0.f, 0.f, 0.f, 0.f});
+    const f32x4 pQ = mma16(lgc, tri, f32x4{0.f, 0.f, 0.f, 0.f});
+    const float Pf = __shfl(pK[3], 48 + r);  // chunk total of feature f0 + r
+    const bool mild = wave_max_all(-Pf) <= MILD_SPAN;
+    // ---- D^T[s][t] = v_s . dy_t (lane (t = r, kq): s = 4 kq + i), masked to s <= t
+    f32x4 dT = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) dT = mma(vf[ks], dyf[ks], dT);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dT[i] = (4 * kq + i <= r) ? dT[i] : 0.f;
+    // ---- inter: Out^T[f][t] = sum_dv S[f][dv] dy_t[dv]
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      float xs[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xs[j] = S[2 * ks + (j >> 2)][j & 3];
+      o = mmx_ft<T>(xs, dyf[ks], o);
+    }
+    if (mild) {
+      float kt[4], dm[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kt[j] = f4_at(pkc, j) * __expf(-pK[j]);
+        dm[j] = dT[j];
+      }
+      o = m16_ff<T>(kt, dm, o);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] *= __expf(pQ[i]);
+    } else {
+      // exact: o = e^{p_t} o_inter + sum_{s <= t} D[t][s] phi_k[s][f] e^{p_t[f] - p_s[f]} (the
+      // wave's own tables: a wave barrier orders its writes before its reads)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pfw[(4 * kq + i) * LDF + r] = pK[i];
+        ph1w[(4 * kq + i) * LDF + r] = f4_at(pkc, i);
+      }
+      __builtin_amdgcn_wave_barrier();
+      float dts[16];
+#pragma unroll
+      for (int s2 = 0; s2 < 16; ++s2) dts[s2] = __shfl(dT[s2 & 3], r + 16 * (s2 >> 2));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int fl = 4 * kq + i;
+        float a = o[i] * __expf(pQ[i]);
+        for (int s2 = 0; s2 <= r; ++s2) a += dts[s2] * ph1w[s2 * LDF + fl] * __expf(pQ[i] - pfw[s2 * LDF + fl]);
+        o[i] = a;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    if (rok) {
+      *reinterpret_cast<f32x4 *>(DPQ + (size_t)(c0 + r) * D + f0 + 4 * kq) =
+          f32x4{p.mix * o[0], p.mix * o[1], p.mix * o[2], p.mix * o[3]};
+    }
+    // ---- state: S^T = e^{P} S^T + V^T Kbar, Kbar[s][f] = phi_k[s][f] e^{P - p_s[f]}
+    float kb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kb[j] = f4_at(pkc, j) * __expf(Pf - pK[j]);
+    const float eP = __expf(Pf);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[dt][i] *= eP;
+      S[dt] = m16_tf<T>(lds_col4(sm.v[buf], LD, 4 * kq, 16 * dt), kb, S[dt]);
+    }
+  };
+  // steps c0 = 0, TS, ..: ring slot (c0 / TS) % NPF, LDS buffer (c0 / TS) % 2
+  static_assert(NPF % 2 == 0, "ring slot and LDS buffer parities must agree");
+  Pre ring[NPF];
+#pragma unroll
+  for (int u = 0; u < NPF; ++u) load_pre(ring[u], u * TS);
+  int c00 = 0;
+  for (; c00 + NPF * TS <= L; c00 += NPF * TS) {
+#pragma unroll
+    for (int u = 0; u < NPF; ++u) step(ring[u], u & 1, c00 + u * TS);
   }
+#pragma unroll
+  for (int u = 0; u < NPF; ++u)  // the last 1 .. NPF steps (a ragged tail can leave NPF)
+    if (c00 + u * TS < L) step(ring[u], u & 1, c00 + u * TS);
 }
 
 // Role V: dv_gla[s] = mix dS_s^T phi_k-part for value columns of key/value head hk, summed over its
@@ -1399,14 +1440,15 @@ static hipError_t launch_bwd_t(const BwdParams &p, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nft = D / 16;
-  hipLaunchKernelGGL((bwd_sweep_kernel<T, D, 0>), dim3(p.B * p.Hq * nft), dim3(64), 0, st, p);
+  const int fgrid = D == 128 ? (p.B * p.Hq + 7) / 8 * 16 : p.B * p.Hq;
+  hipLaunchKernelGGL((bwd_f_kernel<T, D>), dim3(fgrid), dim3(256), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_v_kernel<T, D>), dim3((p.B * p.Hkv + 7) / 8 * 16), dim3(64 * (D / 32)), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int ntile = (p.L + TS - 1) / TS, nrun = (ntile + QPW - 1) / QPW;
   hipLaunchKernelGGL((bwd_win_q_kernel<T, D>), dim3(p.B * p.Hq * nrun), dim3(64), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_sweep_kernel<T, D, 2>), dim3(p.B * p.Hkv * nft), dim3(64), 0, st, p);
+  hipLaunchKernelGGL((bwd_sweep_r_kernel<T, D>), dim3(p.B * p.Hkv * nft), dim3(64), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_win_k_kernel<T, D>), dim3(p.B * p.Hkv * ntile), dim3(64), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
