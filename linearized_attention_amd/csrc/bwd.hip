@@ -306,28 +306,47 @@ __global__ __launch_bounds__(256) void bwd_phi_kernel(BwdParams p) {
 // ======================================================================== 2/3. sweeps
 // Wave-private LDS tiles of a step: T rows of 16 tokens (8-byte aligned transposed reads), and
 // fp32 tables of the exact path (16 tokens x the features the wave handles).
-template <typename T, int D> struct LdsR {
-  static constexpr int LD = D + 8, LDF = 20;
-  T a[TS * LD];          // rows of dy
-  float pf[TS * LDF];    // p[t][f - f0]
-  float ph1[TS * LDF];   // phi_q[t][f - f0]
-  float ph2[TS * LDF];   // in-step sums of the exact path
-  float dd[TS * 17];     // E[t][s] = dy_t . v_s
+// Role R: dphi_k for the features of key/value head hk and dlg of those features, backward over
+// the steps with the workgroup's rows of dL/dS in registers (four waves, one 16-feature tile each,
+// D / 64 workgroups per head, 8 launch slots apart).  As in role F, each step's tiles -- v and
+// the first query head's dy rows, log gamma, phi_k and that head's phi_q and dphi_q rows of the
+// workgroup's 64 features -- are loaded once per workgroup NPF steps ahead and shared through two
+// LDS buffers (dynamic shared memory: LdsR2 exceeds the static limit).  Further query heads of a
+// group are loaded into the step's buffer when the previous head is done with it.
+template <typename T, int D> struct LdsR2 {
+  static constexpr int LD = D + 16 / (int)sizeof(T);
+  static constexpr int LDG = 64 + 16 / (int)sizeof(T);
+  static constexpr int LDP = 68;
+  static constexpr int LDF = 20;
+  T v[2][TS * LD], dy[2][TS * LD], lg[2][TS * LDG];
+  float pk[2][TS * LDP], pq[2][TS * LDP], dq[2][TS * LDP];
+  float pf[4][TS * LDF], ph1[4][TS * LDF], ph2[4][TS * LDF], dd[4][TS * 17];  // per wave: exact path
 };
 
-// Role R: dphi_k for features f0 .. f0 + 15 of key/value head hk and dlg of those features.
 template <typename T, int D>
-__device__ void sweep_r(const BwdParams &p, LdsR<T, D> &sm, int b, int hk, int ft0) {
-  constexpr int NDT = D / 16, NKS = D / 32, LD = LdsR<T, D>::LD, LDF = LdsR<T, D>::LDF;
-  const int lane = threadIdx.x & 63, r = lane & 15, kq = lane >> 4;
-  constexpr int NPR = NPF - 1;  // (role R loads more per step than role F)
-  const int L = p.L, G = p.G, f0 = 16 * ft0;
-  const size_t kvo = ((size_t)b * p.Hkv + hk) * L * D;
+__global__ __launch_bounds__(256, 1) void bwd_r_kernel(BwdParams p) {
+  using SM = LdsR2<T, D>;
+  constexpr int NDT = D / 16, NKS = D / 32, LD = SM::LD, LDG = SM::LDG, LDP = SM::LDP, LDF = SM::LDF;
+  constexpr int NH = D / 64;
+  constexpr int RP = D * (int)sizeof(T) / 16;
+  constexpr int NPC = TS * RP;
+  extern __shared__ __attribute__((aligned(16))) char smem_r[];
+  SM &sm = *reinterpret_cast<SM *>(smem_r);
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, kq = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int x = blockIdx.x;
+  const int bh = NH == 2 ? (x >> 4) * 8 + (x & 7) : x, half = NH == 2 ? (x >> 3) & 1 : 0;
+  if (bh >= p.B * p.Hkv) return;  // padding of the launch to whole XCD pairs
+  const int b = bh / p.Hkv, hk = bh % p.Hkv;
+  const int L = p.L, G = p.G, fw = 64 * half, f0 = fw + 16 * w;
+  const size_t kvo = (size_t)bh * L * D;
   const T *V = reinterpret_cast<const T *>(p.v) + kvo;
   const T *LG = reinterpret_cast<const T *>(p.lg) + kvo;
   const float *PK = p.phk + kvo;
   float *DPK = p.dphk + kvo;
   T *DLG = reinterpret_cast<T *>(p.dlg) + kvo;
+  float *pfw = sm.pf[w], *ph1w = sm.ph1[w], *ph2w = sm.ph2[w], *ddw = sm.dd[w];
+  auto qoff = [&](int g) { return ((size_t)b * p.Hq + hk * G + g) * L * D; };
   f32x4 dS[NDT];  // dS^T[dv = 16 dt + 4 kq + i][f = f0 + r]
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) dS[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -337,47 +356,77 @@ __device__ void sweep_r(const BwdParams &p, LdsR<T, D> &sm, int b, int hk, int f
   for (int j = 0; j < 4; ++j) ufs[j] = (4 * kq + j >= r) ? 1.f : 0.f;
   float rsum = 0.f;  // dlg of feature f0 + r summed over the later steps
   const int nstep = (L + TS - 1) / TS;
-  // Loads of a step (v rows, log gamma and phi_k columns) with those of its first query head (dy
-  // rows, phi_q and dphi_q columns), rows clamped into the sequence (zeroed at use where that
-  // matters): a ring of NPR register sets, each refilled at the end of the step that used it, as
-  // in role F.  Further query heads of a group are loaded one head ahead.
-  struct Head {
-    Frag<T> dy[NKS];
-    Col4<float> pq, dq;
+  const int prow = tid / RP, pcol = (tid % RP) * (16 / (int)sizeof(T));
+  const int grow = tid / 16, gcol = 4 * (tid % 16);
+  struct HeadPre {
+    u32x4 dy;
+    f32x4 pq, dq;
   };
-  struct Buf {
-    Frag<T> v[NKS];
-    Col4<T> lg;
-    Col4<float> pk;
-    Head h0;
+  struct Pre {
+    u32x4 v;
+    F4<T> lg;
+    f32x4 pk;
+    HeadPre h;
   };
-  auto load_head = [&](Head &hd, int c0, int g) {
-    const size_t qo = ((size_t)b * p.Hq + hk * G + g) * L * D;
-    const T *DY = reinterpret_cast<const T *>(p.dy) + qo;
-    const size_t row = (size_t)min(c0 + r, L - 1) * D;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) hd.dy[ks] = row_il(DY + row, ks, kq, true);
-    hd.pq = col_ld(p.phq + qo, D, c0 + 4 * kq, f0 + r, L);
-    hd.dq = col_ld(p.dphq + qo, D, c0 + 4 * kq, f0 + r, L);
+  auto load_head = [&](HeadPre &hp, int c0, int g) {  // rows clamped into the sequence
+    const size_t qo = qoff(g);
+    if (tid < NPC)
+      hp.dy = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const T *>(p.dy) + qo +
+                                                 (size_t)min(c0 + prow, L - 1) * D + pcol);
+    const size_t og = qo + (size_t)min(c0 + grow, L - 1) * D + fw + gcol;
+    hp.pq = *reinterpret_cast<const f32x4 *>(p.phq + og);
+    hp.dq = *reinterpret_cast<const f32x4 *>(p.dphq + og);
   };
-  auto load_step = [&](Buf &bf, int st) {
+  auto load_pre = [&](Pre &pr, int st) {
     const int c0 = max(st, 0) * TS;
-    const size_t row = (size_t)min(c0 + r, L - 1) * D;
+    if (tid < NPC) pr.v = *reinterpret_cast<const u32x4 *>(V + (size_t)min(c0 + prow, L - 1) * D + pcol);
+    const size_t og = (size_t)min(c0 + grow, L - 1) * D + fw + gcol;
+    if constexpr (sizeof(T) == 2) {
+      pr.lg.v = *reinterpret_cast<const bf16x4 *>(LG + og);
+    } else {
+      const f32x4 t = *reinterpret_cast<const f32x4 *>(LG + og);
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) bf.v[ks] = row_il(V + row, ks, kq, true);
-    bf.lg = col_ld(LG, D, c0 + 4 * kq, f0 + r, L);
-    bf.pk = col_ld(PK, D, c0 + 4 * kq, f0 + r, L);
-    load_head(bf.h0, c0, 0);
+      for (int j = 0; j < 4; ++j) pr.lg.v[j] = t[j];
+    }
+    pr.pk = *reinterpret_cast<const f32x4 *>(PK + og);
+    load_head(pr.h, c0, 0);
   };
-  auto step = [&](Buf &bf, int st) {
-    const int c0 = st * TS;
-    // (opaque here, so that the columns are packed in this step, not after their loads)
+  // rows at or beyond L: no decay and no features (zeros), so they add nothing anywhere
+  auto store_head = [&](const HeadPre &hp, int buf, int c0) {
+    if (tid < NPC) *reinterpret_cast<u32x4 *>(sm.dy[buf] + prow * LD + pcol) = hp.dy;
+    const bool in = c0 + grow < L;
+    float *q = sm.pq[buf] + grow * LDP + gcol, *d = sm.dq[buf] + grow * LDP + gcol;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      asm volatile("" : "+v"(bf.lg.x[j]), "+v"(bf.pk.x[j]), "+v"(bf.h0.pq.x[j]), "+v"(bf.h0.dq.x[j]));
-    const F4<T> lgc = col_use(bf.lg, c0 + 4 * kq, L);
-    const F4<float> pkc = col_use(bf.pk, c0 + 4 * kq, L);
-    const Frag<T> *vf = bf.v;
+    for (int j = 0; j < 4; ++j) {
+      q[j] = in ? hp.pq[j] : 0.f;
+      d[j] = in ? hp.dq[j] : 0.f;
+    }
+  };
+  auto store_pre = [&](const Pre &pr, int buf, int c0) {
+    if (tid < NPC) *reinterpret_cast<u32x4 *>(sm.v[buf] + prow * LD + pcol) = pr.v;
+    const bool in = c0 + grow < L;
+    T *g = sm.lg[buf] + grow * LDG + gcol;
+    float *k = sm.pk[buf] + grow * LDP + gcol;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      g[j] = in ? pr.lg.v[j] : from_f<T>(0.f);
+      k[j] = in ? pr.pk[j] : 0.f;
+    }
+    store_head(pr.h, buf, c0);
+  };
+  auto step = [&](Pre &pr, int buf, int st) {
+    const int c0 = st * TS;
+    store_pre(pr, buf, c0);
+    load_pre(pr, st - NPF);  // this ring slot's registers are free now
+    __syncthreads();         // the step's tiles visible
+    const T *tv = sm.v[buf] + r * LD;
+    Frag<T> vf[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) vf[ks] = load4x2(tv + 32 * ks + 4 * kq, tv + 32 * ks + 16 + 4 * kq);
+    const F4<T> lgc = lds_col4(sm.lg[buf], LDG, 4 * kq, 16 * w);
+    F4<float> pkc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pkc.v[j] = sm.pk[buf][(4 * kq + j) * LDP + 16 * w + r];
     const f32x4 pK = mma16(tri, lgc, f32x4{0.f, 0.f, 0.f, 0.f});  // lane (f0 + r, kq): s = 4 kq + i
     const float Pf = __shfl(pK[3], 48 + r);
     const bool mild = wave_max_all(-Pf) <= MILD_SPAN;
@@ -385,29 +434,42 @@ __device__ void sweep_r(const BwdParams &p, LdsR<T, D> &sm, int b, int hk, int f
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      float x[8];
+      float xs[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = dS[2 * ks + (j >> 2)][j & 3];
-      o = mmx_tf<T>(vf[ks], x, o);
+      for (int j = 0; j < 8; ++j) xs[j] = dS[2 * ks + (j >> 2)][j & 3];
+      o = mmx_tf<T>(vf[ks], xs, o);
     }
     const float eP = __expf(Pf);
     if (mild) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] *= eP;  // times e^{-p_s} below: e^{P - p_s} in all
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pfw[(4 * kq + i) * LDF + r] = pK[i];
     }
     float gq[4] = {0.f, 0.f, 0.f, 0.f};  // sum_g phi_q dphi_q at (t = 4 kq + i, f0 + r)
-    if (!mild) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sm.pf[(4 * kq + i) * LDF + r] = pK[i];
-    }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) dS[dt][i] *= eP;
-    // one query head of the group: its dy rows, phi_q and dphi_q columns
-    auto head = [&](const Frag<T> (&dyf)[NKS], const F4<float> &pqc, const F4<float> &dqc, int g) {
+    for (int g = 0; g < G; ++g) {
+      if (g > 0) {  // this head's tiles into the step's buffer, once every wave is done with the last
+        HeadPre hp;
+        load_head(hp, c0, g);
+        __syncthreads();
+        store_head(hp, buf, c0);
+        __syncthreads();
+      }
+      const T *ty = sm.dy[buf] + r * LD;
+      Frag<T> dyf[NKS];
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) store_il(sm.a + r * LD, dyf[ks], ks, kq);
+      for (int ks = 0; ks < NKS; ++ks) dyf[ks] = load4x2(ty + 32 * ks + 4 * kq, ty + 32 * ks + 16 + 4 * kq);
+      F4<float> pqc, dqc;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        pqc.v[j] = sm.pq[buf][(4 * kq + j) * LDP + 16 * w + r];
+        dqc.v[j] = sm.dq[buf][(4 * kq + j) * LDP + 16 * w + r];
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) gq[j] += f4_at(pqc, j) * f4_at(dqc, j);
       // E[t][s] = dy_t . v_s (lane (s = r, kq): t = 4 kq + i), masked to t >= s
@@ -428,35 +490,25 @@ __device__ void sweep_r(const BwdParams &p, LdsR<T, D> &sm, int b, int hk, int f
         o = m16_ff<T>(ea, qt, o);
       } else {
         // exact: sum_{t >= s} E[t][s] phi_q[t][f] e^{p_t[f] - p_s[f]}, one exponent per term,
-        // summed over the group's query heads in ph2
+        // summed over the group's query heads in ph2 (the wave's own tables)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sm.ph1[(4 * kq + i) * LDF + r] = f4_at(pqc, i);
+        for (int i = 0; i < 4; ++i) ph1w[(4 * kq + i) * LDF + r] = f4_at(pqc, i);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sm.dd[(4 * kq + i) * 17 + r] = e[i];
-        __syncthreads();
+        for (int i = 0; i < 4; ++i) ddw[(4 * kq + i) * 17 + r] = e[i];
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int s = 4 * kq + i;
-          float x = 0.f;
-          for (int t = s; t < TS; ++t)
-            x += sm.dd[t * 17 + s] * sm.ph1[t * LDF + r] * __expf(sm.pf[t * LDF + r] - sm.pf[s * LDF + r]);
-          sm.ph2[s * LDF + r] = (g == 0 ? 0.f : sm.ph2[s * LDF + r]) + x;
+          const int s2 = 4 * kq + i;
+          float xx = 0.f;
+          for (int t = s2; t < TS; ++t)
+            xx += ddw[t * 17 + s2] * ph1w[t * LDF + r] * __expf(pfw[t * LDF + r] - pfw[s2 * LDF + r]);
+          ph2w[s2 * LDF + r] = (g == 0 ? 0.f : ph2w[s2 * LDF + r]) + xx;
         }
-        __syncthreads();
+        __builtin_amdgcn_wave_barrier();
       }
       // dS^T[dv][f] += sum_t dy_t[dv] Qt[t][f]
-      __syncthreads();  // dy rows staged
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) dS[dt] = m16_tf<T>(lds_col4(sm.a, LD, 4 * kq, 16 * dt), qt, dS[dt]);
-      __syncthreads();
-    };
-    Head hn;  // further query heads, one ahead
-    if (G > 1) load_head(hn, c0, 1);
-    head(bf.h0.dy, col_use(bf.h0.pq, c0 + 4 * kq, L), col_use(bf.h0.dq, c0 + 4 * kq, L), 0);
-    for (int g = 1; g < G; ++g) {
-      Head hc = hn;
-      if (g + 1 < G) load_head(hn, c0, g + 1);
-      head(hc.dy, col_use(hc.pq, c0 + 4 * kq, L), col_use(hc.dq, c0 + 4 * kq, L), g);
+      for (int dt = 0; dt < NDT; ++dt) dS[dt] = m16_tf<T>(lds_col4(sm.dy[buf], LD, 4 * kq, 16 * dt), qt, dS[dt]);
     }
     // ---- dphi_k[s][f] = mix e^{-p_s} (e^{P} X + sum_g intra)   (lane (f0 + r, kq): s = 4 kq + i)
     float dpk[4];
@@ -465,7 +517,7 @@ __device__ void sweep_r(const BwdParams &p, LdsR<T, D> &sm, int b, int hk, int f
       if (mild) {
         dpk[i] = p.mix * o[i] * __expf(-pK[i]);
       } else {  // o: the unscaled inter term
-        dpk[i] = p.mix * (o[i] * __expf(Pf - pK[i]) + sm.ph2[(4 * kq + i) * LDF + r]);
+        dpk[i] = p.mix * (o[i] * __expf(Pf - pK[i]) + ph2w[(4 * kq + i) * LDF + r]);
       }
     }
     // ---- dlg: db[t][f] = sum_g phi_q dphi_q - phi_k dphi_k; reverse cumsum in the step (fp32 MFMA)
@@ -476,37 +528,27 @@ __device__ void sweep_r(const BwdParams &p, LdsR<T, D> &sm, int b, int hk, int f
     const float tot = __shfl(cs[0], r);                              // t = 0: the step's total
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int s = c0 + 4 * kq + i;
-      if (s < L) {
-        DPK[(size_t)s * D + f0 + r] = dpk[i];
-        DLG[(size_t)s * D + f0 + r] = from_f<T>(cs[i] + rsum);
+      const int s2 = c0 + 4 * kq + i;
+      if (s2 < L) {
+        DPK[(size_t)s2 * D + f0 + r] = dpk[i];
+        DLG[(size_t)s2 * D + f0 + r] = from_f<T>(cs[i] + rsum);
       }
     }
     rsum += tot;
-    if (!mild) __syncthreads();
-    load_step(bf, st - NPR);
   };
-  // steps st = nstep - 1 - k for k = 0, 1, ..; ring slot k % NPR
-  Buf ring[NPR];
+  // steps st = nstep - 1 - k for k = 0, 1, ..: ring slot k % NPF, LDS buffer k % 2
+  static_assert(NPF % 2 == 0, "ring slot and LDS buffer parities must agree");
+  Pre ring[NPF];
 #pragma unroll
-  for (int u = 0; u < NPR; ++u) load_step(ring[u], nstep - 1 - u);
+  for (int u = 0; u < NPF; ++u) load_pre(ring[u], nstep - 1 - u);
   int k = 0;
-  for (; k + NPR <= nstep; k += NPR) {
+  for (; k + NPF <= nstep; k += NPF) {
 #pragma unroll
-    for (int u = 0; u < NPR; ++u) step(ring[u], nstep - 1 - (k + u));
+    for (int u = 0; u < NPF; ++u) step(ring[u], u & 1, nstep - 1 - (k + u));
   }
 #pragma unroll
-  for (int u = 0; u < NPR; ++u)
-    if (k + u < nstep) step(ring[u], nstep - 1 - (k + u));
-}
-
-// Role R: one wave per block (batch, key/value head, feature tile).
-template <typename T, int D>
-__global__ __launch_bounds__(64) void bwd_sweep_r_kernel(BwdParams p) {
-  constexpr int NT = D / 16;
-  const int tile = blockIdx.x % NT, bh = blockIdx.x / NT;
-  __shared__ LdsR<T, D> sm;
-  sweep_r<T, D>(p, sm, bh / p.Hkv, bh % p.Hkv, tile);
+  for (int u = 0; u < NPF; ++u)
+    if (k + u < nstep) step(ring[u], u & 1, nstep - 1 - (k + u));
 }
 
 // Role F: dphi_q for the features of query head hq (see the top of the file).  Workgroups of four
@@ -1439,7 +1481,6 @@ static hipError_t launch_bwd_t(const BwdParams &p, hipStream_t st) {
   else hipLaunchKernelGGL((bwd_phi_kernel<T, D, false>), dim3((p.B * p.Hq + p.B * p.Hkv) * ntile64), dim3(256), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nft = D / 16;
   const int fgrid = D == 128 ? (p.B * p.Hq + 7) / 8 * 16 : p.B * p.Hq;
   hipLaunchKernelGGL((bwd_f_kernel<T, D>), dim3(fgrid), dim3(256), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1448,7 +1489,13 @@ static hipError_t launch_bwd_t(const BwdParams &p, hipStream_t st) {
   const int ntile = (p.L + TS - 1) / TS, nrun = (ntile + QPW - 1) / QPW;
   hipLaunchKernelGGL((bwd_win_q_kernel<T, D>), dim3(p.B * p.Hq * nrun), dim3(64), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_sweep_r_kernel<T, D>), dim3(p.B * p.Hkv * nft), dim3(64), 0, st, p);
+  {
+    const void *rk = reinterpret_cast<const void *>(bwd_r_kernel<T, D>);
+    if ((e = hipFuncSetAttribute(rk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(LdsR2<T, D>))) != hipSuccess)
+      return e;
+    const int rgrid = D == 128 ? (p.B * p.Hkv + 7) / 8 * 16 : p.B * p.Hkv;
+    hipLaunchKernelGGL((bwd_r_kernel<T, D>), dim3(rgrid), dim3(256), sizeof(LdsR2<T, D>), st, p);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_win_k_kernel<T, D>), dim3(p.B * p.Hkv * ntile), dim3(64), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
