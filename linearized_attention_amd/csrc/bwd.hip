@@ -48,6 +48,7 @@ namespace bwd {
 constexpr int TS = 16;              // tokens per sweep step / window tile
 constexpr float MILD_SPAN = 60.f;   // -P at most this for the split exponentials
 constexpr int QPW = 24;             // query tiles per wave in the window-q kernel
+constexpr int NB = 5;               // key tiles of a band the window-q kernel loads at once
 constexpr int FB_CHUNKS = 8;        // 64-row chunks per block of the feature-map backward
 constexpr int NPF = 4;              // ring of step loads in the sweeps
 
@@ -1002,31 +1003,47 @@ __global__ __launch_bounds__(64) void bwd_win_q_kernel(BwdParams p) {
   for (int qt = run * QPW; qt < min(ntile, (run + 1) * QPW); ++qt) {
     const int t0 = qt * TS, t = t0 + r;
     const bool tok = t < L;
+    const int jlo = max(0, t0 - W + 1), ulo = jlo / TS, uhi = qt;
+    // Loads first, all in flight together: the query and dy rows, then (when the band has at most
+    // NB key tiles) every key and value tile of the band, rows clamped into the sequence (rows at
+    // or beyond L are masked or weighted by zero).  A band of more tiles loads each as it goes.
+    const bool batched = uhi - ulo + 1 <= NB;
     Frag<T> qf[KS], dyf[KS];
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
       qf[j] = row_nat(Q + (size_t)t * D, j, kq, tok);
-      Frag<T> f = row_nat(DY + (size_t)t * D, j, kq, tok);
+      dyf[j] = row_nat(DY + (size_t)t * D, j, kq, tok);
+    }
+    Frag<T> kb[NB][KS], vb[NB][KS];
+    if (batched) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const size_t jr = (size_t)min(TS * min(ulo + i, uhi) + r, L - 1) * D;
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+          kb[i][j] = load8(K + jr + 32 * j + 8 * kq);
+          vb[i][j] = load8(V + jr + 32 * j + 8 * kq);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
       float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = wmix * to_f(f.v[e]);
+      for (int e = 0; e < 8; ++e) x[e] = wmix * to_f(dyf[j].v[e]);
       dyf[j] = frag_from<T>(x);
       *reinterpret_cast<Frag<T> *>(sm.q + r * LD + 32 * j + 8 * kq) = qf[j];
       *reinterpret_cast<Frag<T> *>(sm.dy + r * LD + 32 * j + 8 * kq) = dyf[j];
     }
-    const int jlo = max(0, t0 - W + 1), ulo = jlo / TS, uhi = qt;
-    // logits of tile u (u = -1: meta), masked
-    auto logits = [&](int u, f32x4 &s) {
+    // logits of tile u (u = -1: meta) from its key fragments, masked
+    auto logits_f = [&](int u, const Frag<T> (&kf)[KS], f32x4 &s) {
       s = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (u < 0) {
 #pragma unroll
-        for (int j = 0; j < KS; ++j) s = mma(tkf[j], qf[j], s);
+      for (int j = 0; j < KS; ++j) s = mma(kf[j], qf[j], s);
+      if (u < 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[i] = (4 * kq + i < M) ? s[i] * sl : -1.0e30f;
       } else {
-        const int jr = TS * u + r;
-#pragma unroll
-        for (int j = 0; j < KS; ++j) s = mma(row_nat(K + (size_t)jr * D, j, kq, jr < L), qf[j], s);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int jj = TS * u + 4 * kq + i;
@@ -1034,20 +1051,20 @@ __global__ __launch_bounds__(64) void bwd_win_q_kernel(BwdParams p) {
         }
       }
     };
-    auto dots = [&](int u, f32x4 &dp) {  // dp[j][t] = v_j . dy_w[t]
+    auto dots_f = [&](const Frag<T> (&vf)[KS], f32x4 &dp) {  // dp[j][t] = v_j . dy_w[t]
       dp = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (u < 0) {
 #pragma unroll
-        for (int j = 0; j < KS; ++j) dp = mma(tvf[j], dyf[j], dp);
-      } else {
-        const int jr = TS * u + r;
+      for (int j = 0; j < KS; ++j) dp = mma(vf[j], dyf[j], dp);
+    };
+    auto load_tile = [&](const T *X, int u, Frag<T> (&f)[KS]) {  // key or value tile u, rows r
+      const int jr = TS * u + r;
 #pragma unroll
-        for (int j = 0; j < KS; ++j) dp = mma(row_nat(V + (size_t)jr * D, j, kq, jr < L), dyf[j], dp);
-      }
+      for (int j = 0; j < KS; ++j) f[j] = row_nat(X + (size_t)jr * D, j, kq, jr < L);
     };
     // tiles of the row: k = 0 the meta tile, k >= 1 key tile ulo + k - 1; the first NC tiles keep
     // their logits and dots (in lane-private LDS) for the second pass
     constexpr int NC = 6;
+    static_assert(NB + 1 <= NC, "a batched band's tiles all keep their logits and dots");
     const int ntl = 2 + uhi - ulo;
     auto tile_of = [&](int k) { return k == 0 ? -1 : ulo + k - 1; };
     // pass 1 (online): row max, sum of e^{s - max}, and sum of e^{s - max} dp, rescaled as the max grows
@@ -1066,14 +1083,27 @@ __global__ __launch_bounds__(64) void bwd_win_q_kernel(BwdParams p) {
       }
       mx = m2;
     };
-    for (int k = 0; k < ntl; ++k) {
+    auto pass1 = [&](int k, const Frag<T> (&kf)[KS], const Frag<T> (&vf)[KS]) {
       f32x4 sv, dv;
-      logits(tile_of(k), sv);
-      dots(tile_of(k), dv);
+      logits_f(tile_of(k), kf, sv);
+      dots_f(vf, dv);
       online(sv, dv);
       if (k < NC) {
         sm.cache[k][0][lane] = sv;
         sm.cache[k][1][lane] = dv;
+      }
+    };
+    pass1(0, tkf, tvf);
+    if (batched) {
+#pragma unroll
+      for (int k = 1; k <= NB; ++k)
+        if (k < ntl) pass1(k, kb[k - 1], vb[k - 1]);
+    } else {
+      for (int k = 1; k < ntl; ++k) {
+        Frag<T> kf[KS], vf[KS];
+        load_tile(K, tile_of(k), kf);
+        load_tile(V, tile_of(k), vf);
+        pass1(k, kf, vf);
       }
     }
     sum = wave_sum_cols(sum);
@@ -1087,7 +1117,7 @@ __global__ __launch_bounds__(64) void bwd_win_q_kernel(BwdParams p) {
     f32x4 dq[NDT];  // lane (e = 16 et + r, kq): t = 4 kq + i
 #pragma unroll
     for (int et = 0; et < NDT; ++et) dq[et] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto backprop = [&](int u, const f32x4 &sv, const f32x4 &dv) {
+    auto backprop = [&](int u, const f32x4 &sv, const f32x4 &dv, const Frag<T> (&kf)[KS]) {
       float pr[4], ds[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -1095,12 +1125,8 @@ __global__ __launch_bounds__(64) void bwd_win_q_kernel(BwdParams p) {
         ds[i] = pr[i] * (dv[i] - dsum);
       }
       // the key tile's rows into LDS for the transposed operand
-      const int jr = TS * u + r;
 #pragma unroll
-      for (int j = 0; j < KS; ++j) {
-        const Frag<T> kf = (u < 0) ? tkf[j] : row_nat(K + (size_t)jr * D, j, kq, jr < L);
-        *reinterpret_cast<Frag<T> *>(sm.k + r * LD + 32 * j + 8 * kq) = kf;
-      }
+      for (int j = 0; j < KS; ++j) *reinterpret_cast<Frag<T> *>(sm.k + r * LD + 32 * j + 8 * kq) = kf[j];
       __syncthreads();
       // dq[t][e] += scale sum_j ds[t][j] K[j][e]: A = ds (lane (t = r, kq): j = 4 kq + i)
       const F4<T> dsa = f4_from<T>(ds);
@@ -1125,16 +1151,27 @@ __global__ __launch_bounds__(64) void bwd_win_q_kernel(BwdParams p) {
       }
       __syncthreads();
     };
-    for (int k = 0; k < ntl; ++k) {
-      f32x4 sv, dv;
-      if (k < NC) {
-        sv = sm.cache[k][0][lane];
-        dv = sm.cache[k][1][lane];
-      } else {
-        logits(tile_of(k), sv);
-        dots(tile_of(k), dv);
+    backprop(-1, sm.cache[0][0][lane], sm.cache[0][1][lane], tkf);
+    if (batched) {
+#pragma unroll
+      for (int k = 1; k <= NB; ++k)
+        if (k < ntl) backprop(tile_of(k), sm.cache[k][0][lane], sm.cache[k][1][lane], kb[k - 1]);
+    } else {
+      for (int k = 1; k < ntl; ++k) {
+        f32x4 sv, dv;
+        Frag<T> kf[KS];
+        load_tile(K, tile_of(k), kf);
+        if (k < NC) {
+          sv = sm.cache[k][0][lane];
+          dv = sm.cache[k][1][lane];
+        } else {
+          Frag<T> vf[KS];
+          load_tile(V, tile_of(k), vf);
+          logits_f(tile_of(k), kf, sv);
+          dots_f(vf, dv);
+        }
+        backprop(tile_of(k), sv, dv, kf);
       }
-      backprop(tile_of(k), sv, dv);
     }
     float *DQW = p.dqw + qo;
 #pragma unroll
