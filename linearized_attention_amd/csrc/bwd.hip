@@ -843,10 +843,6 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_v_kernel(BwdParams p) {
         kb[j] = pkf.v[j] * __expf(P[h][i] - pv);
         kt[j] = pkf.v[j] * __expf(fminf(-pv, MILD_SPAN));
         qt[j] = pqf.v[j] * __expf(pv);
-        const int col = 16 * h + 4 * kq + i;
-        xp[r * LDX + col] = pv;
-        xk[r * LDX + col] = pkf.v[j];
-        xq[r * LDX + col] = pqf.v[j];
       }
       store_il(sm.kb + r * LD, frag_from<T>(kb), w, kq);
       store_il(sm.kt + r * LD, frag_from<T>(kt), w, kq);
@@ -897,6 +893,18 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_v_kernel(BwdParams p) {
         }
       } else {
         // exact: A[t][s] = sum_f phi_q[t][f] phi_k[s][f] e^{p_t[f] - p_s[f]}, each wave over its slice
+        // (its rows of p, phi_k and phi_q in the wave's own tables, written here: mild steps, the
+        // common case, need none of them)
+        if (g == 0) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int col = 16 * (j >> 2) + 4 * kq + (j & 3);
+            xp[r * LDX + col] = pq[j >> 2][j & 3];
+            xk[r * LDX + col] = pkf.v[j];
+            xq[r * LDX + col] = pqf.v[j];
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int t = 4 * kq + i;
