@@ -256,51 +256,90 @@ template <typename T> __device__ __forceinline__ F4<T> tri_le(int r, int kq) {
 using namespace bwd;
 
 // ======================================================================== 1. feature maps
-// One wave per 16 rows of q (blocks < nq) or k: phi = softmax(x W) or exp(xW) (+) exp(-xW), stored
-// in fp32 (the log-gate gradient sums products of phi with its gradient over the whole sequence,
-// and those sums cancel to zero overall: their terms need fp32 accuracy); W^T staged in LDS.
+// One workgroup of four waves per PHI_ROWS rows of q (blocks < nq) or k: phi = softmax(x W) or
+// exp(xW) (+) exp(-xW), stored in fp32 (the log-gate gradient sums products of phi with its
+// gradient over the whole sequence, and those sums cancel to zero overall: their terms need fp32
+// accuracy); W^T staged in LDS once per workgroup, each wave's next 16 rows loaded while the
+// current ones are mapped.
+constexpr int PHI_ROWS = 256;
 template <typename T, int D, bool HH>
 __global__ __launch_bounds__(256) void bwd_phi_kernel(BwdParams p) {
   constexpr int NFT = D / 16, KS = D / 32, LDW = D + 16 / (int)sizeof(T);
   constexpr int FC = HH ? D / 2 : D;
   __shared__ __align__(16) T sW[D * LDW];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, kq = lane >> 4;
-  const int ntile = (p.L + 63) / 64;
-  const int nq = p.B * p.Hq * ntile;
+  const int nblk = (p.L + PHI_ROWS - 1) / PHI_ROWS;
+  const int nq = p.B * p.Hq * nblk;
   const bool qside = (int)blockIdx.x < nq;
   const int bid = qside ? blockIdx.x : blockIdx.x - nq;
   const int H = qside ? p.Hq : p.Hkv;
-  const int bh = bid / ntile, c0 = (bid % ntile) * 64 + 16 * w;
+  const int bh = bid / nblk, r0 = (bid % nblk) * PHI_ROWS, r1 = min(p.L, r0 + PHI_ROWS);
   const int h = bh % H;
   const T *Wsrc = reinterpret_cast<const T *>(qside ? p.wq : p.wk) + (size_t)h * p.w_stride;
-  for (int idx = tid; idx < D * FC; idx += 256) {  // W[i][c] -> sW[c][i] (and -W -> sW[FC + c][i])
-    const int i = idx / FC, c = idx % FC;
-    const T x = Wsrc[(size_t)i * FC + c];
-    sW[c * LDW + i] = x;
-    if constexpr (HH) sW[(FC + c) * LDW + i] = from_f<T>(-to_f(x));
-  }
-  __syncthreads();
   const T *X = reinterpret_cast<const T *>(qside ? p.q : p.k) + (size_t)bh * p.L * D;
   float *PH = (qside ? p.phq : p.phk) + (size_t)bh * p.L * D;
-  const int t = c0 + r;
-  Frag<T> xf[KS];
+  // W[i][c] -> sW[c][i] (and -W -> sW[FC + c][i]): the lanes of a wave take consecutive rows i
+  // (pairs of rows for 2-byte types, one 4-byte word per lane and column), so a wave's writes to a
+  // row of sW fall in distinct banks; every load is issued before the first write
+  constexpr int RPI = sizeof(T) == 2 ? 2 : 1;
+  constexpr int NR = D / RPI, NI = NR * (FC / 8), IT = (NI + 255) / 256;
+  Frag<T> wa[IT][RPI];
 #pragma unroll
-  for (int j = 0; j < KS; ++j) xf[j] = row_nat(X + (size_t)t * D, j, kq, t < p.L);
-  f32x4 z[NFT];
-  feature_logits<T, D, LDW>(sW, xf, r, kq, z);  // z^T[f][t]: lane (t = r, kq) holds f = 16 ft + 4 kq + i
-  float ph[NFT][4];
-  if constexpr (HH) {
+  for (int it = 0; it < IT; ++it) {
+    const int idx = min(tid + 256 * it, NI - 1);
+    const int i0 = RPI * (idx % NR), f0 = 8 * (idx / NR);
 #pragma unroll
-    for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ph[ft][i] = __expf(z[ft][i]);
-  } else {
-    softmax_rows<NFT>(z, ph);
+    for (int u = 0; u < RPI; ++u) wa[it][u] = load8(Wsrc + (size_t)(i0 + u) * FC + f0);
   }
-  if (t < p.L) {
+  Frag<T> xf[KS];
+  {
+    const int t = r0 + 16 * w + r;
 #pragma unroll
-    for (int ft = 0; ft < NFT; ++ft)
-      *reinterpret_cast<f32x4 *>(PH + (size_t)t * D + 16 * ft + 4 * kq) = f32x4{ph[ft][0], ph[ft][1], ph[ft][2], ph[ft][3]};
+    for (int j = 0; j < KS; ++j) xf[j] = row_nat(X + (size_t)t * D, j, kq, t < r1);
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = tid + 256 * it;
+    if (NI % 256 == 0 || idx < NI) {
+      const int i0 = RPI * (idx % NR), f0 = 8 * (idx / NR);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if constexpr (RPI == 2) {
+          T pair[2] = {wa[it][0].v[j], wa[it][1].v[j]};
+          const uint32_t u = *reinterpret_cast<const uint32_t *>(pair);
+          *reinterpret_cast<uint32_t *>(sW + (f0 + j) * LDW + i0) = u;
+          if constexpr (HH) *reinterpret_cast<uint32_t *>(sW + (FC + f0 + j) * LDW + i0) = u ^ 0x80008000u;
+        } else {
+          sW[(f0 + j) * LDW + i0] = wa[it][0].v[j];
+          if constexpr (HH) sW[(FC + f0 + j) * LDW + i0] = -wa[it][0].v[j];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int c0 = r0; c0 < r1; c0 += 64) {
+    const int t = c0 + 16 * w + r;
+    Frag<T> xn[KS];  // the wave's next rows in flight
+#pragma unroll
+    for (int j = 0; j < KS; ++j) xn[j] = row_nat(X + (size_t)(t + 64) * D, j, kq, t + 64 < r1);
+    f32x4 z[NFT];
+    feature_logits<T, D, LDW>(sW, xf, r, kq, z);  // z^T[f][t]: lane (t = r, kq) holds f = 16 ft + 4 kq + i
+    float ph[NFT][4];
+    if constexpr (HH) {
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ph[ft][i] = __expf(z[ft][i]);
+    } else {
+      softmax_rows<NFT>(z, ph);
+    }
+    if (t < r1) {
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft)
+        *reinterpret_cast<f32x4 *>(PH + (size_t)t * D + 16 * ft + 4 * kq) = f32x4{ph[ft][0], ph[ft][1], ph[ft][2], ph[ft][3]};
+    }
+#pragma unroll
+    for (int j = 0; j < KS; ++j) xf[j] = xn[j];
   }
 }
 
@@ -1521,9 +1560,9 @@ size_t bwd_workspace_layout(int B, int Hq, int Hkv, int L, int d, int M, int dty
 
 template <typename T, int D>
 static hipError_t launch_bwd_t(const BwdParams &p, hipStream_t st) {
-  const int ntile64 = (p.L + 63) / 64;
-  if (p.hh) hipLaunchKernelGGL((bwd_phi_kernel<T, D, true>), dim3((p.B * p.Hq + p.B * p.Hkv) * ntile64), dim3(256), 0, st, p);
-  else hipLaunchKernelGGL((bwd_phi_kernel<T, D, false>), dim3((p.B * p.Hq + p.B * p.Hkv) * ntile64), dim3(256), 0, st, p);
+  const int nphi = (p.L + PHI_ROWS - 1) / PHI_ROWS;
+  if (p.hh) hipLaunchKernelGGL((bwd_phi_kernel<T, D, true>), dim3((p.B * p.Hq + p.B * p.Hkv) * nphi), dim3(256), 0, st, p);
+  else hipLaunchKernelGGL((bwd_phi_kernel<T, D, false>), dim3((p.B * p.Hq + p.B * p.Hkv) * nphi), dim3(256), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int fgrid = D == 128 ? (p.B * p.Hq + 7) / 8 * 16 : p.B * p.Hq;
