@@ -1371,6 +1371,12 @@ __global__ __launch_bounds__(256) void bwd_fb_kernel(BwdParams p) {
   for (int c0 = 64 * FB_CHUNKS * split; c0 < min(L, 64 * FB_CHUNKS * (split + 1)); c0 += 64) {
     const int t = c0 + 16 * w + r;
     const bool tok = t < L;
+    // the window part of dx for row t (four consecutive columns per lane and 16-column tile), its
+    // loads issued first so that they are in flight while dz and its products are computed
+    f32x4 xw[D / 16];
+#pragma unroll
+    for (int it = 0; it < D / 16; ++it)
+      xw[it] = *reinterpret_cast<const f32x4 *>(DXW + (size_t)min(t, L - 1) * D + 16 * it + 4 * kq);
     // phi and dphi of row t, natural columns 32 ks + 8 kq .. + 7
     float ph[KS][8], dph[KS][8];
     float dot = 0.f;
@@ -1418,8 +1424,7 @@ __global__ __launch_bounds__(256) void bwd_fb_kernel(BwdParams p) {
       for (int ks = 0; ks < FC / 32; ++ks) a = mma(load8(sW + (16 * it + r) * LDW + 32 * ks + 8 * kq), dzf[ks], a);
       if (tok) {
         const size_t off = (size_t)t * D + 16 * it + 4 * kq;
-        const f32x4 xw = *reinterpret_cast<const f32x4 *>(DXW + off);
-        store4<T>(DX + off, a[0] + xw[0], a[1] + xw[1], a[2] + xw[2], a[3] + xw[3]);
+        store4<T>(DX + off, a[0] + xw[it][0], a[1] + xw[it][1], a[2] + xw[it][2], a[3] + xw[it][3]);
       }
     }
     __syncthreads();  // x and dz rows of the chunk staged
@@ -1439,13 +1444,21 @@ __global__ __launch_bounds__(256) void bwd_fb_kernel(BwdParams p) {
     if (!qside) {  // dv = dv_gla + dv_window for the chunk's rows, 4 elements per thread and step
       const float *DVG = p.dvg + o, *DVW = p.dvw + o;
       T *DV = reinterpret_cast<T *>(p.dvo) + o;
-      for (int idx = 4 * tid; idx < 64 * D; idx += 4 * 256) {
-        const int tt = c0 + idx / D;
-        if (tt < L) {
-          const f32x4 a = *reinterpret_cast<const f32x4 *>(DVG + (size_t)c0 * D + idx);
-          const f32x4 bb = *reinterpret_cast<const f32x4 *>(DVW + (size_t)c0 * D + idx);
-          store4<T>(DV + (size_t)c0 * D + idx, a[0] + bb[0], a[1] + bb[1], a[2] + bb[2], a[3] + bb[3]);
-        }
+      constexpr int NV = 64 * D / (4 * 256);  // 4-element pieces per thread and chunk
+      f32x4 ga[NV], gb[NV];
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {  // every load in flight before the first store (rows clamped)
+        const int idx = 4 * tid + 4 * 256 * u;
+        const size_t off = (size_t)min(c0 + idx / D, L - 1) * D + idx % D;
+        ga[u] = *reinterpret_cast<const f32x4 *>(DVG + off);
+        gb[u] = *reinterpret_cast<const f32x4 *>(DVW + off);
+      }
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int idx = 4 * tid + 4 * 256 * u;
+        if (c0 + idx / D < L)
+          store4<T>(DV + (size_t)c0 * D + idx, ga[u][0] + gb[u][0], ga[u][1] + gb[u][1], ga[u][2] + gb[u][2],
+                    ga[u][3] + gb[u][3]);
       }
     }
     __syncthreads();
