@@ -148,6 +148,17 @@ template <typename T> __device__ __forceinline__ Col4<T> col_ld(const T *base, i
   }
   return c;
 }
+// Four consecutive elements as one LDS (or global) write, and a zero operand.
+template <typename T> __device__ __forceinline__ void store_f4(T *dst, const F4<T> &f) {
+  if constexpr (sizeof(T) == 2) *reinterpret_cast<bf16x4 *>(dst) = f.v;
+  else *reinterpret_cast<f32x4 *>(dst) = f32x4{f.v[0], f.v[1], f.v[2], f.v[3]};
+}
+template <typename T> __device__ __forceinline__ F4<T> f4_zero() {
+  F4<T> f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f.v[j] = from_f<T>(0.f);
+  return f;
+}
 // Keeps the compiler from moving work on a fragment loaded ahead up to its load.
 template <typename T> __device__ __forceinline__ void opaque_frag(Frag<T> &f) {
   if constexpr (sizeof(T) == 2) {
@@ -436,22 +447,16 @@ __global__ __launch_bounds__(256, 1) void bwd_r_kernel(BwdParams p) {
     if (tid < NPC) *reinterpret_cast<u32x4 *>(sm.dy[buf] + prow * LD + pcol) = hp.dy;
     const bool in = c0 + grow < L;
     float *q = sm.pq[buf] + grow * LDP + gcol, *d = sm.dq[buf] + grow * LDP + gcol;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      q[j] = in ? hp.pq[j] : 0.f;
-      d[j] = in ? hp.dq[j] : 0.f;
-    }
+    *reinterpret_cast<f32x4 *>(q) = in ? hp.pq : f32x4{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<f32x4 *>(d) = in ? hp.dq : f32x4{0.f, 0.f, 0.f, 0.f};
   };
   auto store_pre = [&](const Pre &pr, int buf, int c0) {
     if (tid < NPC) *reinterpret_cast<u32x4 *>(sm.v[buf] + prow * LD + pcol) = pr.v;
     const bool in = c0 + grow < L;
     T *g = sm.lg[buf] + grow * LDG + gcol;
     float *k = sm.pk[buf] + grow * LDP + gcol;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      g[j] = in ? pr.lg.v[j] : from_f<T>(0.f);
-      k[j] = in ? pr.pk[j] : 0.f;
-    }
+    store_f4(g, in ? pr.lg : f4_zero<T>());
+    *reinterpret_cast<f32x4 *>(k) = in ? pr.pk : f32x4{0.f, 0.f, 0.f, 0.f};
     store_head(pr.h, buf, c0);
   };
   auto step = [&](Pre &pr, int buf, int st) {
@@ -667,11 +672,8 @@ __global__ __launch_bounds__(256, 1) void bwd_f_kernel(BwdParams p) {
     const bool in = c0 + grow < L;
     T *g = sm.lg[buf] + grow * LDG + gcol;
     float *k = sm.pk[buf] + grow * LDP + gcol;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      g[j] = in ? pr.lg.v[j] : from_f<T>(0.f);
-      k[j] = in ? pr.pk[j] : 0.f;
-    }
+    store_f4(g, in ? pr.lg : f4_zero<T>());
+    *reinterpret_cast<f32x4 *>(k) = in ? pr.pk : f32x4{0.f, 0.f, 0.f, 0.f};
   };
   auto step = [&](Pre &pr, int buf, int c0) {
     store_pre(pr, buf, c0);
