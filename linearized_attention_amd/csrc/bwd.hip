@@ -3,15 +3,16 @@
 //
 // Decomposition (every kernel here; the host sequence is launch_bwd at the end):
 //   1. bwd_phi_kernel       phi_q = fmap(q W_q), phi_k = fmap(k W_k) into the workspace.
-//   2. bwd_sweep_kernel     role F (one wave per batch, query head, 16-feature tile): forward over
-//                           16-token steps with its columns of the state S in registers:
+//   2. bwd_f_kernel         role F (workgroups of four waves, one 16-feature tile each, D / 64
+//                           workgroups per batch and query head): forward over 16-token steps
+//                           with its columns of the state S in registers:
 //                               dphi_q[t] = mix * S_t dy_t
 //                           bwd_v_kernel, role V (workgroups of D / 32 waves, one wave per 16-column
 //                           tile of v, two workgroups per batch and key/value head, the step's
 //                           decayed operands shared in LDS): backward over the steps with its
 //                           columns of dL/dS in registers:
 //                               dv_gla[s] = mix * dS_s^T phi_k[s]
-//   3. bwd_sweep_kernel     role R (one wave per batch, key/value head, 16-feature tile): backward
+//   3. bwd_r_kernel         role R (workgroups as role F, per batch and key/value head): backward
 //                           with its rows of dL/dS:  dphi_k[s] = mix * dS_s v_s, and the log-gate
 //                           gradient dlg_j = sum_{t >= j} (sum_g phi_q phi_q-grad - phi_k phi_k-grad)
 //   4. bwd_win_q_kernel     window softmax statistics, dq of the window, meta-token gradients.
@@ -20,6 +21,14 @@
 //                           dv = both parts, dW partial sums.
 //   7. bwd_reduce_kernel    dW and dT from their partial sums.
 //
+// The sweeps run one wave per SIMD and take 256 short steps per sequence of 4096, so the latency of
+// a step's loads is what bounds them unless it is hidden: each step's inputs are loaded several
+// steps ahead into a ring of register sets (the step loop is unrolled over the ring, so every set
+// keeps fixed registers; a set is refilled once the step that used it no longer needs it), column
+// values are packed into operands only in the step that uses them (packing next to the load would
+// wait for every load in flight), and roles F and R load each step's tiles once per workgroup and
+// share them through LDS.
+
 // Where the recurrence lives.  S_t = diag(gamma_t) S_{t-1} + phi_k(k_t) v_t^T and y_t = phi_q^T S_t
 // (papernotes.org summary, "key designs", Gated Linear Attention item).  Inside a 16-token step
 // with p_t the log-gate prefix from the step start (inclusive) and P its total,
