@@ -1254,24 +1254,43 @@ __global__ __launch_bounds__(64) void bwd_win_q_kernel(BwdParams p) {
 }
 
 // ======================================================================== 5. window, key side
-// One wave per (batch, key/value head, 16-key tile): for every query head of the group and every
-// query tile that sees these keys, p from the stored statistics, ds = p (dp - D_t), then
-// dk_j += scale sum_t ds[t][j] q_t and dv_j += sum_t p[t][j] dyw_t.
+// Workgroups of four waves per (batch, key/value head, run of four 16-key tiles), wave w taking
+// key tile 4 run + w: for every query head of the group and every query tile that sees these keys,
+// p from the stored statistics, ds = p (dp - D_t), then dk_j += scale sum_t ds[t][j] q_t and
+// dv_j += sum_t p[t][j] dyw_t.  The query tiles the run's keys see (eight for W <= 65) are loaded
+// once per workgroup -- query rows, (1 - mix) dy rows and statistics, every load in flight
+// together -- into LDS, where every wave reads its operands; a longer band goes in windows of
+// eight tiles.
 // Logit layout: lane (j = r, kq) holds s[t = 16 u + 4 kq + i][j].
+constexpr int WKQ = 8;  // query tiles per window of the window-k kernel
+template <typename T, int D> struct WinKLds {
+  static constexpr int LD = D + 16 / (int)sizeof(T);
+  T q[WKQ][TS * LD], dy[WKQ][TS * LD];
+  f32x4 st[WKQ][TS];  // (max, 1 / sum, D_t) of the window's query rows
+};
+
 template <typename T, int D>
-__global__ __launch_bounds__(64) void bwd_win_k_kernel(BwdParams p) {
-  constexpr int NDT = D / 16, KS = D / 32, LD = D + 8;
-  __shared__ __align__(16) T sq[TS * LD];
-  __shared__ __align__(16) T sdy[TS * LD];
-  const int lane = threadIdx.x & 63, r = lane & 15, kq = lane >> 4;
+__global__ __launch_bounds__(256) void bwd_win_k_kernel(BwdParams p) {
+  using SM = WinKLds<T, D>;
+  constexpr int NDT = D / 16, KS = D / 32, LD = SM::LD;
+  constexpr int RP = D * (int)sizeof(T) / 16;      // 16-byte pieces per row
+  constexpr int EP = 16 / (int)sizeof(T);          // elements per piece
+  constexpr int NPW = WKQ * TS * RP;               // pieces per window and tensor
+  static_assert(NPW % 256 == 0, "pieces per thread");
+  constexpr int PPT = NPW / 256;
+  extern __shared__ __attribute__((aligned(16))) char smem_k[];
+  SM &sm = *reinterpret_cast<SM *>(smem_k);
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, kq = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int L = p.L, W = p.W, G = p.G;
-  const int ntile = (L + TS - 1) / TS;
-  const int bh = blockIdx.x / ntile, kt = blockIdx.x % ntile;
+  const int ntile = (L + TS - 1) / TS, nrun = (ntile + 3) / 4;
+  const int bh = blockIdx.x / nrun, run = blockIdx.x % nrun;
   const int b = bh / p.Hkv, hk = bh % p.Hkv;
   const size_t kvo = (size_t)bh * L * D;
   const T *K = reinterpret_cast<const T *>(p.k) + kvo;
   const T *V = reinterpret_cast<const T *>(p.v) + kvo;
-  const int j0 = kt * TS, j = j0 + r;
+  const int kt = 4 * run + w, j0 = kt * TS, j = j0 + r;
+  const bool kin = kt < ntile;  // waves past the last key tile take part in the loads and barriers
   Frag<T> kf[KS], vf[KS];
 #pragma unroll
   for (int x = 0; x < KS; ++x) {
@@ -1282,56 +1301,76 @@ __global__ __launch_bounds__(64) void bwd_win_k_kernel(BwdParams p) {
   f32x4 dk[NDT], dv[NDT];  // lane (e = 16 et + r, kq): j = 4 kq + i
 #pragma unroll
   for (int et = 0; et < NDT; ++et) { dk[et] = f32x4{0.f, 0.f, 0.f, 0.f}; dv[et] = f32x4{0.f, 0.f, 0.f, 0.f}; }
-  const int uhi = min(ntile - 1, (j0 + TS - 1 + W - 1) / TS);
+  const int uhi = min(ntile - 1, (j0 + TS - 1 + W - 1) / TS);  // this wave's last query tile
+  const int k0 = 4 * run;                                       // the run's first key tile
+  const int uend = min(ntile - 1, (min(4 * run + 3, ntile - 1) * TS + TS - 1 + W - 1) / TS);
   for (int g = 0; g < G; ++g) {
     const int hq = hk * G + g;
     const size_t qo = ((size_t)b * p.Hq + hq) * L * D;
     const T *Q = reinterpret_cast<const T *>(p.q) + qo;
     const T *DY = reinterpret_cast<const T *>(p.dy) + qo;
     const float *ST = p.wstat + ((size_t)b * p.Hq + hq) * L * 4;
-    for (int u = kt; u <= uhi; ++u) {
-      const int t0 = u * TS, tr = t0 + r;
-      Frag<T> qf[KS], dyf[KS];
+    for (int u0 = k0; u0 <= uend; u0 += WKQ) {
+      // the window's query tiles u0 .. u0 + WKQ - 1 into LDS, rows clamped into the sequence
+      u32x4 qa[PPT], da[PPT];
+      f32x4 sa = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int x = 0; x < KS; ++x) {
-        qf[x] = row_nat(Q + (size_t)tr * D, x, kq, tr < L);
-        const Frag<T> f = row_nat(DY + (size_t)tr * D, x, kq, tr < L);
-        float y[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = wmix * to_f(f.v[e]);
-        dyf[x] = frag_from<T>(y);
-        *reinterpret_cast<Frag<T> *>(sq + r * LD + 32 * x + 8 * kq) = qf[x];
-        *reinterpret_cast<Frag<T> *>(sdy + r * LD + 32 * x + 8 * kq) = dyf[x];
+      for (int i = 0; i < PPT; ++i) {
+        const int pc = tid + 256 * i, row = pc / RP, col = (pc % RP) * EP;
+        const size_t o = (size_t)min(u0 * TS + row, L - 1) * D + col;
+        qa[i] = *reinterpret_cast<const u32x4 *>(Q + o);
+        da[i] = *reinterpret_cast<const u32x4 *>(DY + o);
       }
-      f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+      if (tid < WKQ * TS) sa = *reinterpret_cast<const f32x4 *>(ST + (size_t)min(u0 * TS + tid, L - 1) * 4);
+      __syncthreads();  // the previous window's tiles are no longer read
 #pragma unroll
-      for (int x = 0; x < KS; ++x) {
-        s = mma(qf[x], kf[x], s);   // s[t][j]: lane (j = r, kq) t = 4 kq + i
-        dp = mma(dyf[x], vf[x], dp);
+      for (int i = 0; i < PPT; ++i) {
+        const int pc = tid + 256 * i, row = pc / RP, col = (pc % RP) * EP;
+        T *qd = sm.q[row / TS] + (row % TS) * LD + col, *dd = sm.dy[row / TS] + (row % TS) * LD + col;
+        *reinterpret_cast<u32x4 *>(qd) = qa[i];
+        const T *dsrc = reinterpret_cast<const T *>(&da[i]);
+        T sc[EP];
+#pragma unroll
+        for (int e = 0; e < EP; ++e) sc[e] = from_f<T>(wmix * to_f(dsrc[e]));
+        *reinterpret_cast<u32x4 *>(dd) = *reinterpret_cast<const u32x4 *>(sc);
       }
-      float ds[4], pr[4];
+      if (tid < WKQ * TS) sm.st[tid / TS][tid % TS] = sa;
+      __syncthreads();  // the window's tiles visible
+      if (kin) {
+        for (int u = max(u0, kt); u <= min(u0 + WKQ - 1, uhi); ++u) {
+          const T *tq = sm.q[u - u0], *tdy = sm.dy[u - u0];
+          Frag<T> qf[KS], dyf[KS];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 4 * kq + i;
-        const bool ok = t < L && j < L && j <= t && j > t - W;
-        float mx = 0.f, inv = 0.f, dd = 0.f;
-        if (t < L) {
-          const f32x4 stt = *reinterpret_cast<const f32x4 *>(ST + (size_t)t * 4);
-          mx = stt[0]; inv = stt[1]; dd = stt[2];
+          for (int x = 0; x < KS; ++x) {
+            qf[x] = load8(tq + r * LD + 32 * x + 8 * kq);
+            dyf[x] = load8(tdy + r * LD + 32 * x + 8 * kq);
+          }
+          f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int x = 0; x < KS; ++x) {
+            s = mma(qf[x], kf[x], s);   // s[t][j]: lane (j = r, kq) t = 4 kq + i
+            dp = mma(dyf[x], vf[x], dp);
+          }
+          float ds[4], pr[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = u * TS + 4 * kq + i;
+            const bool ok = t < L && j < L && j <= t && j > t - W;
+            const f32x4 stt = sm.st[u - u0][4 * kq + i];
+            pr[i] = ok ? __expf(s[i] * sl - stt[0]) * stt[1] : 0.f;
+            ds[i] = pr[i] * (dp[i] - (ok ? stt[2] : 0.f));
+          }
+          const F4<T> dsa = f4_from<T>(ds), pa = f4_from<T>(pr);
+#pragma unroll
+          for (int et = 0; et < NDT; ++et) {
+            dk[et] = mma16(dsa, lds_col4(tq, LD, 4 * kq, 16 * et), dk[et]);
+            dv[et] = mma16(pa, lds_col4(tdy, LD, 4 * kq, 16 * et), dv[et]);
+          }
         }
-        pr[i] = ok ? __expf(s[i] * sl - mx) * inv : 0.f;
-        ds[i] = pr[i] * (dp[i] - dd);
       }
-      __syncthreads();
-      const F4<T> dsa = f4_from<T>(ds), pa = f4_from<T>(pr);
-#pragma unroll
-      for (int et = 0; et < NDT; ++et) {
-        dk[et] = mma16(dsa, lds_col4(sq, LD, 4 * kq, 16 * et), dk[et]);
-        dv[et] = mma16(pa, lds_col4(sdy, LD, 4 * kq, 16 * et), dv[et]);
-      }
-      __syncthreads();
     }
   }
+  if (!kin) return;
   float *DKW = p.dkw + kvo, *DVW = p.dvw + kvo;
 #pragma unroll
   for (int et = 0; et < NDT; ++et)
@@ -1605,7 +1644,12 @@ static hipError_t launch_bwd_t(const BwdParams &p, hipStream_t st) {
     hipLaunchKernelGGL((bwd_r_kernel<T, D>), dim3(rgrid), dim3(256), sizeof(LdsR2<T, D>), st, p);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_win_k_kernel<T, D>), dim3(p.B * p.Hkv * ntile), dim3(64), 0, st, p);
+  {
+    const void *kk = reinterpret_cast<const void *>(bwd_win_k_kernel<T, D>);
+    if ((e = hipFuncSetAttribute(kk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(WinKLds<T, D>))) != hipSuccess)
+      return e;
+    hipLaunchKernelGGL((bwd_win_k_kernel<T, D>), dim3(p.B * p.Hkv * ((ntile + 3) / 4)), dim3(256), sizeof(WinKLds<T, D>), st, p);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int nsplit = (p.L + 64 * FB_CHUNKS - 1) / (64 * FB_CHUNKS);
   const dim3 fbgrid((p.B * p.Hq + p.B * p.Hkv) * nsplit);
