@@ -16,9 +16,9 @@
 //                           with its rows of dL/dS:  dphi_k[s] = mix * dS_s v_s, and the log-gate
 //                           gradient dlg_j = sum_{t >= j} (sum_g phi_q phi_q-grad - phi_k phi_k-grad)
 //   4. bwd_win_q_kernel     window softmax statistics, dq of the window, meta-token gradients.
-//   5. bwd_win_k_kernel     dk and dv of the window.
+//   5. bwd_win_k_kernel     dk of the window; dv = role V's part + the window's.
 //   6. bwd_fb_kernel        feature-map backward, dq = dz_q W_q^T (+ window part), dk likewise,
-//                           dv = both parts, dW partial sums.
+//                           dW partial sums.
 //   7. bwd_reduce_kernel    dW and dT from their partial sums.
 //
 // The sweeps run one wave per SIMD and take 256 short steps per sequence of 4096, so the latency of
@@ -1371,7 +1371,16 @@ __global__ __launch_bounds__(256) void bwd_win_k_kernel(BwdParams p) {
     }
   }
   if (!kin) return;
-  float *DKW = p.dkw + kvo, *DVW = p.dvw + kvo;
+  // dk's window part for the feature-map backward; dv = the recurrence's part (role V, already in
+  // the workspace) + the window's, final here
+  float *DKW = p.dkw + kvo;
+  const float *DVG = p.dvg + kvo;
+  T *DV = reinterpret_cast<T *>(p.dvo) + kvo;
+  float g4[NDT][4];
+#pragma unroll
+  for (int et = 0; et < NDT; ++et)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) g4[et][i] = DVG[(size_t)min(j0 + 4 * kq + i, L - 1) * D + 16 * et + r];
 #pragma unroll
   for (int et = 0; et < NDT; ++et)
 #pragma unroll
@@ -1379,7 +1388,7 @@ __global__ __launch_bounds__(256) void bwd_win_k_kernel(BwdParams p) {
       const int jj = j0 + 4 * kq + i;
       if (jj < L) {
         DKW[(size_t)jj * D + 16 * et + r] = sl * dk[et][i];
-        DVW[(size_t)jj * D + 16 * et + r] = dv[et][i];
+        DV[(size_t)jj * D + 16 * et + r] = from_f<T>(g4[et][i] + dv[et][i]);
       }
     }
 }
@@ -1389,7 +1398,7 @@ __global__ __launch_bounds__(256) void bwd_win_k_kernel(BwdParams p) {
 // B*Hq*nsplit blocks) or the key side.  Per chunk: dz = phi (dphi - <phi, dphi>) (softmax) or
 // phi_j dphi_j - phi_{h+j} dphi_{h+j} (Hedgehog), dx = dz W^T + window part; the dW partial sum
 // sum_t x_t^T dz_t accumulates over the run in registers (wave w: rows 16 (NIT w) .. of W) and is
-// written per block.  The key side also writes dv.
+// written per block.
 template <typename T, int D, bool HH>
 __global__ __launch_bounds__(256) void bwd_fb_kernel(BwdParams p) {
   constexpr int KS = D / 32, FC = HH ? D / 2 : D, NCT = FC / 16, NIT = D / 64, LDW = FC + 16 / (int)sizeof(T);
@@ -1491,26 +1500,6 @@ __global__ __launch_bounds__(256) void bwd_fb_kernel(BwdParams p) {
         for (int ct = 0; ct < NCT; ++ct) dw[it][ct] = mma16(xa, za[ct], dw[it][ct]);
       }
     }
-    if (!qside) {  // dv = dv_gla + dv_window for the chunk's rows, 4 elements per thread and step
-      const float *DVG = p.dvg + o, *DVW = p.dvw + o;
-      T *DV = reinterpret_cast<T *>(p.dvo) + o;
-      constexpr int NV = 64 * D / (4 * 256);  // 4-element pieces per thread and chunk
-      f32x4 ga[NV], gb[NV];
-#pragma unroll
-      for (int u = 0; u < NV; ++u) {  // every load in flight before the first store (rows clamped)
-        const int idx = 4 * tid + 4 * 256 * u;
-        const size_t off = (size_t)min(c0 + idx / D, L - 1) * D + idx % D;
-        ga[u] = *reinterpret_cast<const f32x4 *>(DVG + off);
-        gb[u] = *reinterpret_cast<const f32x4 *>(DVW + off);
-      }
-#pragma unroll
-      for (int u = 0; u < NV; ++u) {
-        const int idx = 4 * tid + 4 * 256 * u;
-        if (c0 + idx / D < L)
-          store4<T>(DV + (size_t)c0 * D + idx, ga[u][0] + gb[u][0], ga[u][1] + gb[u][1], ga[u][2] + gb[u][2],
-                    ga[u][3] + gb[u][3]);
-      }
-    }
     __syncthreads();
   }
   float *part = p.dw_part + (size_t)blockIdx.x * D * FC;
@@ -1609,7 +1598,7 @@ size_t bwd_workspace_layout(int B, int Hq, int Hkv, int L, int d, int M, int dty
   w.dvg = take(nk * 4);
   w.dqw = take(nq * 4);
   w.dkw = take(nk * 4);
-  w.dvw = take(nk * 4);
+  w.dvw = take(0);  // (unused: the window-key kernel finishes dv)
   w.wstat = take((size_t)B * Hq * L * 16);
   const int nsplit = (L + 64 * FB_CHUNKS - 1) / (64 * FB_CHUNKS);
   w.dw_part = take((size_t)(B * Hq + B * Hkv) * nsplit * d * d * 4);
