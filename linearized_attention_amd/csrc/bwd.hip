@@ -157,6 +157,18 @@ template <typename T> __device__ __forceinline__ Col4<T> col_ld(const T *base, i
   }
   return c;
 }
+// Four consecutive elements as one load.
+template <typename T> __device__ __forceinline__ F4<T> ld_f4(const T *src) {
+  F4<T> f;
+  if constexpr (sizeof(T) == 2) {
+    f.v = *reinterpret_cast<const bf16x4 *>(src);
+  } else {
+    const f32x4 x = *reinterpret_cast<const f32x4 *>(src);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.v[j] = x[j];
+  }
+  return f;
+}
 // Four consecutive elements as one LDS (or global) write, and a zero operand.
 template <typename T> __device__ __forceinline__ void store_f4(T *dst, const F4<T> &f) {
   if constexpr (sizeof(T) == 2) *reinterpret_cast<bf16x4 *>(dst) = f.v;
@@ -1231,13 +1243,13 @@ __global__ __launch_bounds__(64) void bwd_win_q_kernel(BwdParams p) {
         backprop(tile_of(k), sv, dv, kf);
       }
     }
-    float *DQW = p.dqw + qo;
+    T *DQW = reinterpret_cast<T *>(p.dqw) + qo;  // the window part, in the input type
 #pragma unroll
     for (int et = 0; et < NDT; ++et)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tt = t0 + 4 * kq + i;
-        if (tt < L) DQW[(size_t)tt * D + 16 * et + r] = sl * dq[et][i];
+        if (tt < L) DQW[(size_t)tt * D + 16 * et + r] = from_f<T>(sl * dq[et][i]);
       }
   }
   if (M > 0) {
@@ -1373,7 +1385,7 @@ __global__ __launch_bounds__(256) void bwd_win_k_kernel(BwdParams p) {
   if (!kin) return;
   // dk's window part for the feature-map backward; dv = the recurrence's part (role V, already in
   // the workspace) + the window's, final here
-  float *DKW = p.dkw + kvo;
+  T *DKW = reinterpret_cast<T *>(p.dkw) + kvo;  // the window part, in the input type
   const float *DVG = p.dvg + kvo;
   T *DV = reinterpret_cast<T *>(p.dvo) + kvo;
   float g4[NDT][4];
@@ -1387,7 +1399,7 @@ __global__ __launch_bounds__(256) void bwd_win_k_kernel(BwdParams p) {
     for (int i = 0; i < 4; ++i) {
       const int jj = j0 + 4 * kq + i;
       if (jj < L) {
-        DKW[(size_t)jj * D + 16 * et + r] = sl * dk[et][i];
+        DKW[(size_t)jj * D + 16 * et + r] = from_f<T>(sl * dk[et][i]);
         DV[(size_t)jj * D + 16 * et + r] = from_f<T>(g4[et][i] + dv[et][i]);
       }
     }
@@ -1419,7 +1431,7 @@ __global__ __launch_bounds__(256) void bwd_fb_kernel(BwdParams p) {
   const T *X = reinterpret_cast<const T *>(qside ? p.q : p.k) + o;
   const float *PH = (qside ? p.phq : p.phk) + o;
   const float *DPH = (qside ? p.dphq : p.dphk) + o;
-  const float *DXW = (qside ? p.dqw : p.dkw) + o;
+  const T *DXW = reinterpret_cast<const T *>(qside ? p.dqw : p.dkw) + o;
   T *DX = reinterpret_cast<T *>(qside ? p.dq : p.dk) + o;
   f32x4 dw[NIT][NCT];  // dW[i = 16 (NIT w + it) + 4 kq + ii][c = 16 ct + r]
 #pragma unroll
@@ -1432,10 +1444,9 @@ __global__ __launch_bounds__(256) void bwd_fb_kernel(BwdParams p) {
     const bool tok = t < L;
     // the window part of dx for row t (four consecutive columns per lane and 16-column tile), its
     // loads issued first so that they are in flight while dz and its products are computed
-    f32x4 xw[D / 16];
+    F4<T> xw[D / 16];
 #pragma unroll
-    for (int it = 0; it < D / 16; ++it)
-      xw[it] = *reinterpret_cast<const f32x4 *>(DXW + (size_t)min(t, L - 1) * D + 16 * it + 4 * kq);
+    for (int it = 0; it < D / 16; ++it) xw[it] = ld_f4(DXW + (size_t)min(t, L - 1) * D + 16 * it + 4 * kq);
     // phi and dphi of row t, natural columns 32 ks + 8 kq .. + 7
     float ph[KS][8], dph[KS][8];
     float dot = 0.f;
@@ -1483,7 +1494,8 @@ __global__ __launch_bounds__(256) void bwd_fb_kernel(BwdParams p) {
       for (int ks = 0; ks < FC / 32; ++ks) a = mma(load8(sW + (16 * it + r) * LDW + 32 * ks + 8 * kq), dzf[ks], a);
       if (tok) {
         const size_t off = (size_t)t * D + 16 * it + 4 * kq;
-        store4<T>(DX + off, a[0] + xw[it][0], a[1] + xw[it][1], a[2] + xw[it][2], a[3] + xw[it][3]);
+        store4<T>(DX + off, a[0] + f4_at(xw[it], 0), a[1] + f4_at(xw[it], 1), a[2] + f4_at(xw[it], 2),
+                  a[3] + f4_at(xw[it], 3));
       }
     }
     __syncthreads();  // x and dz rows of the chunk staged
