@@ -573,8 +573,12 @@ __global__ __launch_bounds__(256, 1) void bwd_r_kernel(BwdParams p) {
         __builtin_amdgcn_wave_barrier();
       }
       // dS^T[dv][f] += sum_t dy_t[dv] Qt[t][f]
+      F4<T> dyt[NDT];  // (every fragment read before the first product)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) dS[dt] = m16_tf<T>(lds_col4(sm.dy[buf], LD, 4 * kq, 16 * dt), qt, dS[dt]);
+      for (int dt = 0; dt < NDT; ++dt) dyt[dt] = lds_col4(sm.dy[buf], LD, 4 * kq, 16 * dt);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) dS[dt] = m16_tf<T>(dyt[dt], qt, dS[dt]);
     }
     // ---- dphi_k[s][f] = mix e^{-p_s} (e^{P} X + sum_g intra)   (lane (f0 + r, kq): s = 4 kq + i)
     float dpk[4];
@@ -1003,8 +1007,13 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_v_kernel(BwdParams p) {
           for (int i = 0; i < 4; ++i) dS[ft][i] *= e[i];
         }
       }
+      // (every fragment read before the first product: one read per product waited for each)
+      F4<T> qtf[NFT];
 #pragma unroll
-      for (int ft = 0; ft < NFT; ++ft) dS[ft] = mma16(lds_col4(sm.qt, LD, 4 * kq, 16 * ft), dyc, dS[ft]);
+      for (int ft = 0; ft < NFT; ++ft) qtf[ft] = lds_col4(sm.qt, LD, 4 * kq, 16 * ft);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft) dS[ft] = mma16(qtf[ft], dyc, dS[ft]);
       __syncthreads();  // B2: the step's (head's) operands read before they are rewritten
     }
     // store dV (lane (dv = dv0 + r, kq): s = c0 + 4 kq + i)
