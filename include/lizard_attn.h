@@ -197,7 +197,11 @@ size_t lizard_attn_fwd_ext_workspace_bytes(int B, int Hq, int Hkv, int L,
  *               pass through it between its two kernels, with one counter per
  *               sequence.
  *   Calls on one stream run in order; calls on different streams that share
- *   state, rings, pos or workspace race.
+ *   state, rings, pos or workspace race.  A call launches two kernels and makes
+ *   no other device call (no allocation, no memset, no synchronisation unless
+ *   the debug option asks for one), so a run of steps can be captured in one
+ *   HIP graph and replayed; pos advances on the device, so each replay takes
+ *   the next steps.
  */
 lizard_status lizard_attn_decode(float *state, void *win_k, void *win_v,
                                  int32_t *pos, const void *q, const void *k,
