@@ -442,16 +442,16 @@ __global__ __launch_bounds__(256, 1) void bwd_r_kernel(BwdParams p) {
   };
   auto load_head = [&](HeadPre &hp, int c0, int g) {  // rows clamped into the sequence
     const size_t qo = qoff(g);
-    if (tid < NPC)
-      hp.dy = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const T *>(p.dy) + qo +
-                                                 (size_t)min(c0 + prow, L - 1) * D + pcol);
+    // (unconditional, as in role F: threads past the tile load a duplicate piece, not stored)
+    hp.dy = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const T *>(p.dy) + qo +
+                                               (size_t)min(c0 + prow % TS, L - 1) * D + pcol);
     const size_t og = qo + (size_t)min(c0 + grow, L - 1) * D + fw + gcol;
     hp.pq = *reinterpret_cast<const f32x4 *>(p.phq + og);
     hp.dq = *reinterpret_cast<const f32x4 *>(p.dphq + og);
   };
   auto load_pre = [&](Pre &pr, int st) {
     const int c0 = max(st, 0) * TS;
-    if (tid < NPC) pr.v = *reinterpret_cast<const u32x4 *>(V + (size_t)min(c0 + prow, L - 1) * D + pcol);
+    pr.v = *reinterpret_cast<const u32x4 *>(V + (size_t)min(c0 + prow % TS, L - 1) * D + pcol);
     const size_t og = (size_t)min(c0 + grow, L - 1) * D + fw + gcol;
     if constexpr (sizeof(T) == 2) {
       pr.lg.v = *reinterpret_cast<const bf16x4 *>(LG + og);
@@ -674,11 +674,12 @@ __global__ __launch_bounds__(256, 1) void bwd_f_kernel(BwdParams p) {
     f32x4 pk;
   };
   auto load_pre = [&](Pre &pr, int c0) {  // rows clamped into the sequence
-    if (tid < NPC) {
-      const size_t o = (size_t)min(c0 + prow, L - 1) * D + pcol;
-      pr.dy = *reinterpret_cast<const u32x4 *>(DY + o);
-      pr.v = *reinterpret_cast<const u32x4 *>(V + o);
-    }
+    // (every thread loads, those past the tile a duplicate piece that is not stored: a load
+    // under a condition would leave the compiler unsure it was issued, and it would then wait
+    // for later loads as well before using earlier ones)
+    const size_t o = (size_t)min(c0 + prow % TS, L - 1) * D + pcol;
+    pr.dy = *reinterpret_cast<const u32x4 *>(DY + o);
+    pr.v = *reinterpret_cast<const u32x4 *>(V + o);
     const size_t og = (size_t)min(c0 + grow, L - 1) * D + fw + gcol;
     if constexpr (sizeof(T) == 2) {
       pr.lg.v = *reinterpret_cast<const bf16x4 *>(LG + og);
