@@ -49,6 +49,9 @@
 
 namespace lz {
 
+// Rows past the end of a sequence store their outputs (never read) here: one row, shared by all.
+__device__ __align__(16) unsigned short g_fwd_sink[full::D];
+
 // Exact diagonal-block scores for a sub-chunk whose log decay spans more than
 // SPAN_MAX (e.g. gamma ~ 0): A[t][s] = mix sum_f phi_q[t][f] phi_k[s][f] e^{p_t[f] - p_s[f]}
 // in fp32, p the log-gamma prefix inside the sub-chunk, phi recomputed from q and the
@@ -1570,8 +1573,10 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
             }
           }
         }
-        if (valid) {
-          T *O = Oh + (size_t)pos * D;
+        {  // unconditional stores (rows past the end into a sink): under a condition the compiler
+           // could not count them, and the next chunk's first use of a prefetched load waited for
+           // every store of this one
+          T *O = valid ? Oh + (size_t)pos * D : reinterpret_cast<T *>(g_fwd_sink);
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) store4<T>(O + 16 * dt + 4 * g4, acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
         }
