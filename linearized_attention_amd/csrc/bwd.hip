@@ -52,6 +52,9 @@
 #include "fwd_common.hpp"
 
 namespace lz {
+// Rows past the end of a sequence store their (never read) results here, so that every store is
+// issued unconditionally.
+__device__ __align__(16) float g_bwd_sink[2 * 128];
 namespace bwd {
 
 constexpr int TS = 16;              // tokens per sweep step / window tile
@@ -599,10 +602,9 @@ __global__ __launch_bounds__(256, 1) void bwd_r_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int s2 = c0 + 4 * kq + i;
-      if (s2 < L) {
-        DPK[(size_t)s2 * D + f0 + r] = dpk[i];
-        DLG[(size_t)s2 * D + f0 + r] = from_f<T>(cs[i] + rsum);
-      }
+      const bool in = s2 < L;  // (rows past the end: the sink)
+      (in ? DPK + (size_t)s2 * D : g_bwd_sink)[f0 + r] = dpk[i];
+      (in ? DLG + (size_t)s2 * D : reinterpret_cast<T *>(g_bwd_sink + 128))[f0 + r] = from_f<T>(cs[i] + rsum);
     }
     rsum += tot;
   };
@@ -768,9 +770,10 @@ __global__ __launch_bounds__(256, 1) void bwd_f_kernel(BwdParams p) {
       }
       __builtin_amdgcn_wave_barrier();
     }
-    if (rok) {
-      *reinterpret_cast<f32x4 *>(DPQ + (size_t)(c0 + r) * D + f0 + 4 * kq) =
-          f32x4{p.mix * o[0], p.mix * o[1], p.mix * o[2], p.mix * o[3]};
+    {  // (rows past the end into the sink: stores under a condition make the compiler's waits for
+       // the load ring conservative)
+      float *dst = rok ? DPQ + (size_t)(c0 + r) * D : g_bwd_sink;
+      *reinterpret_cast<f32x4 *>(dst + f0 + 4 * kq) = f32x4{p.mix * o[0], p.mix * o[1], p.mix * o[2], p.mix * o[3]};
     }
     // ---- state: S^T = e^{P} S^T + V^T Kbar, Kbar[s][f] = phi_k[s][f] e^{P - p_s[f]}
     float kb[4];
@@ -1021,7 +1024,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void bwd_v_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int s2 = c0 + 4 * kq + i;
-      if (s2 < L) DVG[(size_t)s2 * D + dv0 + r] = p.mix * acc[i];
+      float *dst = s2 < L ? DVG + (size_t)s2 * D : g_bwd_sink;  // (rows past the end: the sink)
+      dst[dv0 + r] = p.mix * acc[i];
     }
     load_step(bf, st - NPF);
   };
