@@ -130,11 +130,18 @@ bool query_w_differs(const void *wq, const void *wk, int64_t w_stride, int G) {
   return wq != wk || (w_stride != 0 && G > 1);
 }
 
+// The whole-head kernel's workspace: its plan's segment states, then (when the query side's
+// W_phi differs from the key side's) one fragment-ordered W_phi_q^T copy of d x d bf16 per query
+// head, at the next 256-byte boundary.
+size_t full_ws_bytes(const FwdPlan &plan, int Hq, int d, bool qphi) {
+  return qphi ? align256(plan_bytes(plan)) + align256((size_t)Hq * d * d * 2) : plan_bytes(plan);
+}
+
 // Workspace for either plan (the caller does not say whether W_phi is shared).
 size_t seg_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int W, lizard_dtype dtype) {
   const size_t sa = plan_bytes(make_plan(B, Hq, Hkv, L, d, W, false));
   const bool maybe_full = use_full_kernel(d, W, dtype);
-  const size_t sb = maybe_full ? plan_bytes(make_plan(B, Hq, Hkv, L, d, W, true)) : 0;
+  const size_t sb = maybe_full ? full_ws_bytes(make_plan(B, Hq, Hkv, L, d, W, true), Hq, d, true) : 0;
   return sa > sb ? sa : sb;
 }
 
@@ -204,7 +211,8 @@ lizard_status fwd_impl(const void *q, const void *k, const void *v, const void *
   }
   const bool full = use_full_kernel(d, W, dtype);
   const FwdPlan plan = make_plan(B, Hq, Hkv, L, d, W, full);
-  const size_t seg_bytes = plan_bytes(plan);
+  const bool qphi = full && query_w_differs(w_phi_q, w_phi_k, w_phi_head_stride, Hq / Hkv);
+  const size_t seg_bytes = full ? full_ws_bytes(plan, Hq, d, qphi) : plan_bytes(plan);
   const size_t hist_bytes = history ? ext_hist_bytes(B, Hkv, d, W, dtype) : 0;
   const size_t need = (hist_bytes ? align256(seg_bytes) : seg_bytes) + 2 * hist_bytes;
   if (need > 0) {
@@ -227,7 +235,8 @@ lizard_status fwd_impl(const void *q, const void *k, const void *v, const void *
   p.force_4wave = g_opt.fwd_kernel.load(std::memory_order_relaxed) == 2 ? 1 : 0;
   p.sss = plan.sss;
   p.hh = hedgehog ? 1 : 0;
-  p.qphi = full && query_w_differs(w_phi_q, w_phi_k, w_phi_head_stride, Hq / Hkv) ? 1 : 0;
+  p.qphi = qphi ? 1 : 0;
+  p.ws_wq = qphi ? static_cast<char *>(workspace) + align256(plan_bytes(plan)) : nullptr;
   // Two segments on the whole-head path: the second one's workgroups walk the chunks before it
   // themselves (no state pass), and the first segment takes a few chunks more to even out the
   // walk.  Not with a start state or window history (the walk starts from zero at chunk 0).

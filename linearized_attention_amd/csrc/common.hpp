@@ -67,6 +67,19 @@ template <typename T> __device__ __forceinline__ Frag<T> frag_from(const float (
   return f;
 }
 
+// Buffer resource word 3 for the raw (untyped) buffer loads of gfx9-family chips: a 32-bit data
+// format, so that the loads read memory (a zero format makes every access out of range).
+constexpr int BUF_RSRC_WORD3 = 0x00020000;
+
+// 8 bf16 at byte offset voff + soff of a buffer resource (reads past the resource's size return
+// zeros).  soff is wave-uniform, so a wave's operand loads share one address register.
+template <typename T> __device__ __forceinline__ Frag<T> buffer_load8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  static_assert(sizeof(T) == 2, "16-bit elements");
+  Frag<T> f;
+  f.v = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+  return f;
+}
+
 // 8 contiguous elements (16-byte aligned for bf16, 32-byte for fp32).
 template <typename T> __device__ __forceinline__ Frag<T> load8(const T *p) {
   Frag<T> f;

@@ -666,9 +666,10 @@ __device__ __forceinline__ void walk_pipe(const PipeLds &lds, const bf16 *Kh, co
 }
 
 // ZW: windows of 66..129 keys, which reach into the chunk two back (window group Z).
-// QPHI: the query side's W_phi differs from the key side's (separate or per-head matrices): the
-// query feature maps were written into the output rows by fwd_full_phiq_kernel, the query waves
-// copy them into LDS, and W_phi^T in LDS is the key side's (of this key/value head).
+// QPHI: the query side's W_phi differs from the key side's (separate or per-head matrices): W_phi^T
+// in LDS is the key side's (of this key/value head), and the query waves read their operands from
+// the copy fwd_full_wq_frag_kernel wrote in fragment order (with ZW: the query feature maps that
+// fwd_full_phiq_kernel wrote into the output rows).
 template <bool ZW, bool HH, bool QPHI>
 __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
   using namespace full;
@@ -1212,20 +1213,35 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
     store_vpairs(vf, tid);
     load_vpairs(vf, c_begin * CH, tid);
     bool unsafe_seen = false;
-    // QPHI: this wave's phi_q rows of chunk c (in the output rows, which it overwrites only in P4
-    // of chunk c), stored there in the interleaved feature order of the LDS rows.  Loaded one
-    // chunk ahead, after B2 (the wide-window variant, short of registers, loads them at the top
-    // of the chunk).
-    Frag<T> pq[QPHI ? KS : 1];
+    // QPHI: the query logits' W_phi_q^T operands come from the fragment-ordered copy in global
+    // memory (one kilobyte per wave and operand, L2-resident): feature tiles 0..2 are loaded
+    // before B0 and each later tile three tiles ahead, in a ring of four.
+    // QPASS (the wide-window variant, which carries group Z through here and has no registers for
+    // that ring): this wave's phi_q rows of chunk c, which a pass of their own wrote into the
+    // output rows (read here before P4 of chunk c overwrites them), in the interleaved feature
+    // order of the LDS rows, loaded at the top of the chunk.
+    constexpr bool QPASS = QPHI && ZW, QGLOBAL = QPHI && !ZW;
+    const __amdgpu_buffer_rsrc_t wq_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        QGLOBAL ? static_cast<void *>(reinterpret_cast<T *>(p.ws_wq) + (size_t)(p.per_head_q ? hq : 0) * D * D)
+                : static_cast<void *>(smem),
+        (short)0, QGLOBAL ? D * D * (int)sizeof(T) : 0, BUF_RSRC_WORD3);
+    constexpr int NWQ = QGLOBAL ? 4 : 1;
+    Frag<T> wqf[NWQ][KS];
+    auto wq_tile = [&](int ft) {
+      if constexpr (QGLOBAL) {
+#pragma unroll
+        for (int j = 0; j < KS; ++j) wqf[ft % NWQ][j] = buffer_load8<T>(wq_rsrc, 16 * (int)lane, 1024 * (ft * KS + j));
+      }
+    };
+    Frag<T> pq[QPASS ? KS : 1];
     auto load_pq = [&](int c0q) {
-      if constexpr (QPHI) {
+      if constexpr (QPASS) {
         const int t = c0q + 16 * I + r16;
         const T *src = Oh + (size_t)(t < L ? t : 0) * D + 8 * g4;
 #pragma unroll
         for (int js = 0; js < KS; ++js) pq[js] = t < L ? load8(src + 32 * js) : frag_zero<T>();
       }
     };
-    if constexpr (QPHI && !ZW) load_pq(c_begin * CH);
     __syncthreads();  // P
 
     for (int c = c_begin; c < c_end; ++c) {
@@ -1235,7 +1251,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
 
       // lowest key index the window of this row may use
       const int kmin = max(pos - p.W + 1, -hist_avail);
-      if constexpr (QPHI && ZW) load_pq(c0);
+      load_pq(c0);
 
       // ---- P0: window group X (meta tokens and the previous chunk's keys, still in LDS: tiles
       //      I..3, all four with ZW) in base-2 logits, merged with group Z; unnormalised
@@ -1315,18 +1331,33 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
       if constexpr (ZW) {
         if (c + 1 < c_end) window_z(qf_next, c0 + CH, accz, m_z, l_z);
       }
+      if constexpr (QGLOBAL) {
+        wq_tile(0);
+        wq_tile(1);
+        wq_tile(2);
+      }
       __syncthreads();  // B0
       // ---- P1: stage this chunk's values; phi_q of this wave's rows into LDS (the key waves
       //      decay it in place)
       store_vpairs(vf, tid);
-      if constexpr (QPHI) {
+      if constexpr (QPASS) {
 #pragma unroll
         for (int js = 0; js < KS; ++js) *reinterpret_cast<bf16x8 *>(sQ + (16 * I + r16) * LDQ + 32 * js + 8 * g4) = pq[js].v;
       } else {
         f32x4 zq[NFT];
         float qo[NFT][4];
+        if constexpr (QGLOBAL) {
+#pragma unroll
+          for (int ft = 0; ft < NFT; ++ft) {
+            if (ft + 3 < NFT) wq_tile(ft + 3);
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < KS; ++j) a = mma(wqf[ft % NWQ][j], qf[j], a);
+            zq[ft] = a;
+          }
+        }
         // (the wide-window variant carries group Z through here: no registers for prefetching)
-        if constexpr (ZW) feature_logits<T, D, LDWW>(sW, qf, r16, g4, zq);
+        else if constexpr (ZW) feature_logits<T, D, LDWW>(sW, qf, r16, g4, zq);
         else feature_logits_pipe(sW, qf, r16, g4, zq);
         feature_map_rows<HH>(zq, qo);
 #pragma unroll
@@ -1416,7 +1447,6 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
         pairs_in(vf, Vh, c0 + CH, ln + 64 * wv);
         if constexpr (ZW) q_in(qf_next2, c0 + 2 * CH, ln);
         else q_in(qf_next, c0 + CH, ln);
-        if constexpr (QPHI && !ZW) load_pq(c0 + CH);
       }
       // ---- P3: window output normalised and scaled for the merge; for strong-decay chunks the
       //      inter-chunk product (decayed queries and prefix ends are visible since B2, the state
@@ -1692,8 +1722,9 @@ static hipError_t launch_fwd_full_t(const FwdParams &p, hipStream_t stream) {
                        stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (p.qphi && (e = launch_fwd_full_phiq(p, stream)) != hipSuccess) return e;
   const bool zw = p.W > CH + 1;
+  if (p.qphi && (e = zw ? launch_fwd_full_phiq(p, stream) : launch_fwd_full_wq_frag(p, stream)) != hipSuccess)
+    return e;
   return zw ? (p.qphi ? launch_main<true, HH, true>(p, stream) : launch_main<true, HH, false>(p, stream))
             : (p.qphi ? launch_main<false, HH, true>(p, stream) : launch_main<false, HH, false>(p, stream));
 }

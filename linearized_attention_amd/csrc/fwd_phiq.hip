@@ -1,12 +1,51 @@
-// The query feature maps of the whole-head forward, computed on their own when the query side's
-// W_phi differs from the key side's (separate matrices for queries and keys, or one per head):
-// fwd_full_kernel<.., QPHI = true> then keeps the key side's W_phi^T in LDS and reads these maps.
+// The query side of the whole-head forward when its W_phi differs from the key side's (separate
+// matrices for queries and keys, or one per head): fwd_full_kernel<.., QPHI = true> keeps the key
+// side's W_phi^T in LDS (there is no room for a second one) and reads the query side's MFMA
+// operands from a fragment-ordered copy in global memory, where it stays in the L2 cache; the
+// wide-window variant reads the query feature maps, computed by a pass of their own, instead.
 #include "fwd_full.hpp"
 
 namespace lz {
 
-// phi_q = the feature map of q W_phi_q for every query row, bf16, written over the output rows,
-// where fwd_full_kernel<.., QPHI> reads each row before it writes the row's output.  The features
+// One copy of D x D bf16 per workgroup: fragment (ft, j) of lane l is the 16-byte piece
+// W_phi_q^T[16 ft + l % 16][32 j + 8 (l / 16) .. + 7], stored at ((ft * KS + j) * 64 + l) * 16 bytes,
+// so that one wave's operand is one contiguous kilobyte.  The values are those the key side stages
+// in LDS (load_wT_pairs: W^T, and for the Hedgehog map the negated rows of -W below), so the query
+// logits are the same products in the same order as with one shared matrix.
+template <bool HH>
+__global__ __launch_bounds__(256) void fwd_full_wq_frag_kernel(FwdParams p) {
+  using namespace full;
+  using T = bf16;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  T *sW = reinterpret_cast<T *>(smem);
+  const int tid = threadIdx.x, h = blockIdx.x;
+  load_wT_pairs<256, HH>(sW, reinterpret_cast<const T *>(p.wq) + (size_t)h * p.w_stride, tid);
+  __syncthreads();
+  T *dst = reinterpret_cast<T *>(p.ws_wq) + (size_t)h * D * D;
+  constexpr int NF = NFT * KS * 64;  // 16-byte pieces of one copy
+#pragma unroll
+  for (int it = 0; it < NF / 256; ++it) {
+    const int idx = tid + 256 * it, l = idx & 63, fj = idx >> 6, ft = fj / KS, j = fj % KS;
+    *reinterpret_cast<bf16x8 *>(dst + (size_t)idx * 8) =
+        load8(sW + (16 * ft + (l & 15)) * LDWW + 32 * j + 8 * (l >> 4)).v;
+  }
+}
+
+hipError_t launch_fwd_full_wq_frag(const FwdParams &p, hipStream_t stream) {
+  constexpr int kLds = full::D * full::LDWW * 2;
+  const void *kern = p.hh ? reinterpret_cast<const void *>(fwd_full_wq_frag_kernel<true>)
+                          : reinterpret_cast<const void *>(fwd_full_wq_frag_kernel<false>);
+  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+  if (e != hipSuccess) return e;
+  const dim3 grid(p.per_head_q ? p.Hq : 1);
+  if (p.hh) hipLaunchKernelGGL(fwd_full_wq_frag_kernel<true>, grid, dim3(256), kLds, stream, p);
+  else hipLaunchKernelGGL(fwd_full_wq_frag_kernel<false>, grid, dim3(256), kLds, stream, p);
+  return hipGetLastError();
+}
+
+// For the wide-window variant (W > 65), whose registers hold window group Z through the query feature
+// map: phi_q = the feature map of q W_phi_q for every query row, bf16, written over the output rows,
+// where fwd_full_kernel<true, .., QPHI> reads each row before it writes the row's output.  The features
 // of a row are stored in the interleaved order of the kernel's LDS rows (within each group of 32,
 // feature 16 h + 4 g + i at position 8 g + 4 h + i), so that a lane moves one 16-byte piece per
 // K-step both ways.  The same products in the same order, the same map and one bf16 rounding as

@@ -34,7 +34,9 @@ struct FwdParams {
   int sss;   // whole-head kernel: state-pass pieces per segment (divides cps)
   int hh;    // whole-head kernel: Hedgehog feature map (W_phi [d][d/2]) instead of the softmax
   int qphi;  // whole-head kernel: the query side's W_phi differs from the key side's (separate or
-             // per-head matrices); phi_q is computed by a pass of its own into the output rows
+             // per-head matrices); its W_phi^T is read from ws_wq in MFMA fragment order (W > 65:
+             // phi_q from a pass of its own, in the output rows)
+  void *ws_wq;  // qphi: one W_phi_q^T copy of D x D bf16 per query head (per_head_q) or one in all
   int split; // whole-head kernel, two segments: > 0 puts the second segment's start at this chunk
              // plus a shift and has its workgroups walk the chunks before it (no state pass)
   int split_shift;  // the shift: < 0 estimated from the gates in the kernel, else this many chunks
@@ -46,7 +48,9 @@ hipError_t launch_fwd(const FwdParams &p, int dtype_bf16, int d, hipStream_t str
 // whole-head forward kernel (bf16, d = 128, shared W_phi, one query head per key/value
 // head, W <= 65); the state pass of launch_fwd runs first when the sequence is segmented
 hipError_t launch_fwd_full(const FwdParams &p, hipStream_t stream);
-// its query feature maps on their own (p.qphi), written into the output rows
+// before it when p.qphi: the query side's W_phi^T in MFMA fragment order into p.ws_wq
+hipError_t launch_fwd_full_wq_frag(const FwdParams &p, hipStream_t stream);
+// before it when p.qphi and W > 65: the query feature maps, written into the output rows
 hipError_t launch_fwd_full_phiq(const FwdParams &p, hipStream_t stream);
 // before the forward: window history rows from the caller's ring; after it: the ring of
 // the last W tokens and pos += L

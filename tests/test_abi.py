@@ -95,9 +95,13 @@ def test_fwd_workspace_required_when_segmented():
     need = lib.lizard_attn_fwd_workspace_bytes(1, 32, 32, 32768, 128, 128, 1)
     assert need > 0
     assert _fwd(lib, B=1, Hq=32, Hkv=32, L=32768, ws=None) == 3
-    assert _fwd(lib, B=1, Hq=32, Hkv=32, L=32768, ws=4096, wsb=need - 1) == 3
-    # one chunk: nothing to split, no workspace
-    assert lib.lizard_attn_fwd_workspace_bytes(1, 2, 2, 64, 128, 64, 1) == 0
+    # the size covers a separate query-side W_phi (its fragment-ordered copy): one byte less fails
+    assert _fwd(lib, B=1, Hq=32, Hkv=32, L=32768, wk=32, ws=4096, wsb=need - 1) == 3
+    # one chunk: nothing to split; only the query-side W_phi copy (d x d bf16 per query head),
+    # which a shared W_phi does not use
+    assert lib.lizard_attn_fwd_workspace_bytes(1, 2, 2, 64, 128, 64, 1) == 2 * 128 * 128 * 2
+    assert _fwd(lib, L=64, wk=32, ws=None) == 3
+    assert _fwd(lib, L=64, wk=32, ws=4096, wsb=2 * 128 * 128 * 2 - 1) == 3
 
 
 def test_workspace_bytes_matches_plan_formula():
@@ -113,18 +117,22 @@ def test_workspace_bytes_matches_plan_formula():
     nseg, sss = 8, 1
     pieces = B * Hkv * (nseg - 1) * sss
     full = pieces * d * d * 4 + -(-pieces * d * 4 // 256) * 256
+    # then one fragment-ordered W_phi_q^T copy (d x d bf16) per query head, 256-byte aligned
+    full = -(-full // 256) * 256 + Hkv * d * d * 2
     assert got == max(split, full)
 
 
 def test_whole_head_segments_cover_at_most_1024_chunks():
     """The whole-head kernel keeps one LDS flag bit per chunk of its segment (1024 at most): a
     sequence of 2048 chunks over 256 (batch, head) pairs, which would otherwise run as one
-    segment, is split in two and needs the state-pass workspace; 1024 chunks need none."""
+    segment, is split in two and needs the state-pass workspace; 1024 chunks need none (beyond
+    the query-side W_phi copies that every whole-head call's size covers)."""
     lib = api.load()
-    assert lib.lizard_attn_fwd_workspace_bytes(8, 32, 32, 1024 * 64, 128, 64, 1) == 0
+    wq_copies = 32 * 128 * 128 * 2  # one W_phi_q^T copy per query head (separate W_phi only)
+    assert lib.lizard_attn_fwd_workspace_bytes(8, 32, 32, 1024 * 64, 128, 64, 1) == wq_copies
     need = lib.lizard_attn_fwd_workspace_bytes(8, 32, 32, 2048 * 64, 128, 64, 1)
     pieces = 8 * 32 * 1 * 1  # B*Hkv*(nseg - 1)*sss with nseg = 2, sss = 256 // 256
-    assert need == pieces * 128 * 128 * 4 + pieces * 128 * 4
+    assert need == pieces * 128 * 128 * 4 + pieces * 128 * 4 + wq_copies
 
 
 def _dec(lib, fn="lizard_attn_decode", **kw):
@@ -211,7 +219,9 @@ def test_fwd_ext_workspace_bytes():
     ext = lib.lizard_attn_fwd_ext_workspace_bytes(B, Hkv, Hkv, L, d, W, 1)
     hist = B * Hkv * 128 * d * 2            # W - 1 = 99 rows rounded up to 128, bf16
     assert ext >= plain + 2 * hist
-    assert _fwd_ext(lib, B=B, Hq=Hkv, Hkv=Hkv, L=L, W=W, rkin=32, rvin=32, pos=64, ws=4096, wsb=ext - 1) == 3
+    # (a separate query-side W_phi uses the whole size: its copy sits before the history rows)
+    assert _fwd_ext(lib, B=B, Hq=Hkv, Hkv=Hkv, L=L, W=W, wk=32, rkin=32, rvin=32, pos=64, ws=4096,
+                    wsb=ext - 1) == 3
     assert _fwd_ext(lib, L=0) == 0          # empty problem
 
 
@@ -246,17 +256,19 @@ def test_segment_option_changes_the_plan():
     """A 4 x 32 x 4096 forward is planned in two segments on the whole-head path, whose state
     pass (when the second segment does not start itself) needs workspace; one forced segment
     needs none.  Both two and three segments keep 256 state-pass pieces of one 128 x 128 fp32
-    state and 128 log-gate sums each."""
+    state and 128 log-gate sums each.  Every size also covers the query-side W_phi copies
+    (128 x 128 bf16 per query head) that a separate W_phi needs."""
     lib = api.load()
     saved = lib.lizard_get_option(b"fwd_segments")
+    wq_copies = 32 * 128 * 128 * 2
     try:
         lib.lizard_set_option(b"fwd_segments", 0)
         base = lib.lizard_attn_fwd_workspace_bytes(4, 32, 32, 4096, 128, 64, 1)
         lib.lizard_set_option(b"fwd_segments", 1)
-        assert lib.lizard_attn_fwd_workspace_bytes(4, 32, 32, 4096, 128, 64, 1) == 0
+        assert lib.lizard_attn_fwd_workspace_bytes(4, 32, 32, 4096, 128, 64, 1) == wq_copies
         lib.lizard_set_option(b"fwd_segments", 3)
         more = lib.lizard_attn_fwd_workspace_bytes(4, 32, 32, 4096, 128, 64, 1)
-        assert base == more == 256 * (128 * 128 * 4 + 128 * 4)
+        assert base == more == 256 * (128 * 128 * 4 + 128 * 4) + wq_copies
     finally:
         lib.lizard_set_option(b"fwd_segments", saved)
 
