@@ -7,39 +7,38 @@
 
 namespace lz {
 
-// One copy of D x D bf16 per workgroup: fragment (ft, j) of lane l is the 16-byte piece
-// W_phi_q^T[16 ft + l % 16][32 j + 8 (l / 16) .. + 7], stored at ((ft * KS + j) * 64 + l) * 16 bytes,
-// so that one wave's operand is one contiguous kilobyte.  The values are those the key side stages
-// in LDS (load_wT_pairs: W^T, and for the Hedgehog map the negated rows of -W below), so the query
-// logits are the same products in the same order as with one shared matrix.
+// One copy of D x D bf16 per query head (or one in all): fragment (ft, j) of lane l is the 16-byte
+// piece W_phi_q^T[16 ft + l % 16][32 j + 8 (l / 16) .. + 7], stored at ((ft * KS + j) * 64 + l) * 16
+// bytes, so that one wave's operand is one contiguous kilobyte.  The values are those the key side
+// stages in LDS (load_wT_pairs: W^T, and for the Hedgehog map the rows of -W below, the sign flipped
+// on the bits), so the query logits are the same products in the same order as with one shared
+// matrix.  One thread per piece: eight 2-byte loads down a column of W, one 16-byte store (a copy is
+// 2048 pieces, eight workgroups).
 template <bool HH>
 __global__ __launch_bounds__(256) void fwd_full_wq_frag_kernel(FwdParams p) {
   using namespace full;
-  using T = bf16;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  T *sW = reinterpret_cast<T *>(smem);
-  const int tid = threadIdx.x, h = blockIdx.x;
-  load_wT_pairs<256, HH>(sW, reinterpret_cast<const T *>(p.wq) + (size_t)h * p.w_stride, tid);
-  __syncthreads();
-  T *dst = reinterpret_cast<T *>(p.ws_wq) + (size_t)h * D * D;
-  constexpr int NF = NFT * KS * 64;  // 16-byte pieces of one copy
+  constexpr int FC = HH ? D / 2 : D;  // columns of W_phi
+  constexpr int NPC = NFT * KS * 64;  // pieces of one copy
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int h = idx / NPC, pc = idx % NPC;
+  const int l = pc & 63, fj = pc >> 6, ft = fj / KS, j = fj % KS;
+  const int f = 16 * ft + (l & 15), i0 = 32 * j + 8 * (l >> 4);
+  const bool neg = HH && f >= FC;
+  const uint16_t *src = reinterpret_cast<const uint16_t *>(p.wq) + (size_t)h * p.w_stride + (neg ? f - FC : f);
+  uint16_t x[8];
 #pragma unroll
-  for (int it = 0; it < NF / 256; ++it) {
-    const int idx = tid + 256 * it, l = idx & 63, fj = idx >> 6, ft = fj / KS, j = fj % KS;
-    *reinterpret_cast<bf16x8 *>(dst + (size_t)idx * 8) =
-        load8(sW + (16 * ft + (l & 15)) * LDWW + 32 * j + 8 * (l >> 4)).v;
-  }
+  for (int e = 0; e < 8; ++e) x[e] = src[(size_t)(i0 + e) * FC] ^ (neg ? 0x8000u : 0u);
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = (uint32_t)x[2 * e] | ((uint32_t)x[2 * e + 1] << 16);
+  *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(p.ws_wq) + (size_t)idx * 16) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 hipError_t launch_fwd_full_wq_frag(const FwdParams &p, hipStream_t stream) {
-  constexpr int kLds = full::D * full::LDWW * 2;
-  const void *kern = p.hh ? reinterpret_cast<const void *>(fwd_full_wq_frag_kernel<true>)
-                          : reinterpret_cast<const void *>(fwd_full_wq_frag_kernel<false>);
-  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-  if (e != hipSuccess) return e;
-  const dim3 grid(p.per_head_q ? p.Hq : 1);
-  if (p.hh) hipLaunchKernelGGL(fwd_full_wq_frag_kernel<true>, grid, dim3(256), kLds, stream, p);
-  else hipLaunchKernelGGL(fwd_full_wq_frag_kernel<false>, grid, dim3(256), kLds, stream, p);
+  constexpr int kPieces = full::NFT * full::KS * 64;
+  const int copies = p.per_head_q ? p.Hq : 1;
+  if (p.hh) hipLaunchKernelGGL(fwd_full_wq_frag_kernel<true>, dim3(copies * kPieces / 256), dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(fwd_full_wq_frag_kernel<false>, dim3(copies * kPieces / 256), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

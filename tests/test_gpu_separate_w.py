@@ -2,9 +2,10 @@
 
 The pages train the query and key feature maps separately (arXiv page, Experiments: the first
 stage trains phi_q and phi_k); the Hedgehog map is the paper's own (arXiv page, Method).  When the
-query side's matrix differs from the key side's, the query feature maps come from a pass of their
-own and the main kernel keeps the key side's W_phi^T.  Parity with the fp64 oracle per (batch,
-head): relative L2 <= 2e-2 (bf16) for the merged output and each branch; and bitwise equality with
+query side's matrix differs from the key side's, the query waves read their W_phi^T operands
+from a fragment-ordered copy in global memory (windows above 65 keys: the query feature maps
+come from a pass of their own), and the main kernel keeps the key side's W_phi^T in LDS.
+Parity with the fp64 oracle per (batch, head): relative L2 <= 2e-2 (bf16) for the merged output and each branch; and bitwise equality with
 the shared-matrix call when the separate matrices hold equal values.
 """
 import sys
@@ -86,12 +87,14 @@ def test_separate_w_matches_oracle(gpu_lib, lz_opts, fmap, label, kw, nseg):
 
 @pytest.mark.parametrize("fmap", MAPS)
 @pytest.mark.parametrize("nseg", [1, 2, 3])
-def test_separate_matrices_with_equal_values_match_the_shared_call(gpu_lib, lz_opts, fmap, nseg):
+@pytest.mark.parametrize("W", [64, 100])
+def test_separate_matrices_with_equal_values_match_the_shared_call(gpu_lib, lz_opts, fmap, nseg, W):
     """w_phi_k a copy of w_phi_q (another allocation, the same values), and per-head matrices that
-    are all the same: the query feature maps come from their own pass, with the same products,
-    map and rounding as inside the main kernel, so every output bit matches the shared call."""
+    are all the same: the query logits take the same operand values in the same order (from the
+    fragment-ordered copy, or with W = 100 from the feature-map pass), with the same map and
+    rounding as with the shared matrix, so every output bit matches the shared call."""
     lz_opts("fwd_segments", nseg)
-    inp = inputs(f"equal {fmap} {nseg}", fmap, B=1, Hq=4, Hkv=2, L=600, d=128, W=64, M=4,
+    inp = inputs(f"equal {fmap} {nseg}", fmap, B=1, Hq=4, Hkv=2, L=600, d=128, W=W, M=4,
                  gate="uniform:-1.6")
     dev = inp.to("cuda")
     shared = gpu_fwd(dev, inp, inp.mix, fmap).cpu()
