@@ -158,6 +158,124 @@ __global__ __launch_bounds__(256) void decode_phi_kernel(DecParams p) {
   }
 }
 
+// decode_phi for 16-bit inputs: W_phi staged in LDS as it is stored ([D][FC] rows, plain 16-byte
+// copies) and the logits computed transposed, z^T = W_phi^T x^T: the MFMA's A operand (feature m,
+// input dims k) comes from W's rows by transposing LDS reads (ds_read_b64_tr_b16: in a group of 16
+// lanes, lane m reads 4 values of row m / 4 at column 4 (m % 4), and lane i receives column i of
+// the 4 rows), and its B operand is the raw rows x as loaded.  Lane (r, kq) then holds row r's
+// features 16 c + 4 kq + i, i = 0..3: the softmax reduces over the lane's 32 values and the 4
+// lanes of the row, and each lane stores its features 16 bytes at a time.  The Hedgehog map's
+// second half, exp(-xW), is the negation of the same logits (negating W negates every product
+// exactly).
+template <int D, bool HH>
+__global__ __launch_bounds__(256) void decode_phi_b16_kernel(DecParams p) {
+  using T = bf16;
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  constexpr int FC = HH ? D / 2 : D;  // columns of W_phi
+  constexpr int LDR = FC + 16;        // LDS row stride (elements): 32 bytes past a multiple of 256
+  constexpr int NCL = FC / 16;        // 16-feature tiles of logits
+  constexpr int KS = D / 32;          // K = 32 steps
+  constexpr int NP = D * FC / 8;      // 16-byte pieces of W
+  static_assert(NP % 256 == 0, "pieces per thread");
+  constexpr int IT = NP / 256;
+  __shared__ __align__(16) T wl[D * LDR];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int r = lane & 15, kq = lane >> 4;
+  const int Hkv = p.Hkv, Hq = p.Hq, G = p.G, N = p.N;
+  const int hs = blockIdx.y;
+  const bool key = hs < Hkv;
+  const int h = key ? hs : hs - Hkv;
+  const int n0 = blockIdx.x * DEC_ROWS;
+
+  if (hs == 0 && tid < DEC_ROWS && n0 + tid < N) p.ws_count[n0 + tid] = 0;
+
+  const T *Wsrc = reinterpret_cast<const T *>(key ? p.wk : p.wq) + (size_t)h * p.w_stride;
+  Frag<T> wa[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = tid + 256 * it;
+    wa[it] = load8(Wsrc + (size_t)(idx / (FC / 8)) * FC + 8 * (idx % (FC / 8)));
+  }
+  // B operands straight from global: row n = n0 + 16 wv + r (rows past N clamped, not stored)
+  const int n = min(n0 + 16 * wv + r, N - 1);
+  const T *X = reinterpret_cast<const T *>(key ? p.k : p.q) + ((size_t)n * (key ? Hkv : Hq) + h) * D;
+  Frag<T> x[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) x[s] = load8(X + 32 * s + 8 * kq);
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = tid + 256 * it;
+    *reinterpret_cast<bf16x8 *>(wl + (idx / (FC / 8)) * LDR + 8 * (idx % (FC / 8))) = wa[it].v;
+  }
+  __syncthreads();
+
+  // acc[c][i] = z[row r][feature 16 c + 4 kq + i]
+  // (the operands of tile c + 1 are read while tile c is multiplied)
+  typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+  typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+  const T *wsrc = wl + (8 * kq + (r >> 2)) * LDR + 4 * (r & 3);
+  auto wtile = [&](int c, Frag<T> (&a)[KS]) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const T *src = wsrc + 32 * s * LDR + 16 * c;
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(src));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(src + 4 * LDR));
+      const u2 l2 = __builtin_bit_cast(u2, lo), h2 = __builtin_bit_cast(u2, hi);
+      a[s].v = __builtin_bit_cast(bf16x8, u4{l2.x, l2.y, h2.x, h2.y});
+    }
+  };
+  f32x4 acc[NCL];
+  Frag<T> wa2[2][KS];
+  wtile(0, wa2[0]);
+#pragma unroll
+  for (int c = 0; c < NCL; ++c) {
+    if (c + 1 < NCL) wtile(c + 1, wa2[(c + 1) & 1]);
+    acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) acc[c] = mma(wa2[c & 1][s], x[s], acc[c]);
+  }
+
+  constexpr int NC = D / 16;  // feature tiles of phi
+  float ph[NC][4];
+  if constexpr (HH) {
+#pragma unroll
+    for (int c = 0; c < NCL; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ph[c][i] = __expf(acc[c][i]);
+        ph[NCL + c][i] = __expf(-acc[c][i]);
+      }
+  } else {
+    float m = DEC_NEG;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, acc[c][i]);
+    m = wave_max_cols(m);
+    float sum = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ph[c][i] = __expf(acc[c][i] - m);
+        sum += ph[c][i];
+      }
+    const float inv = 1.f / wave_sum_cols(sum);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ph[c][i] *= inv;
+  }
+  const int hk = key ? h : h / G;
+  const int sub = key ? 0 : 1 + h % G;
+  const int nr = n0 + 16 * wv + r;
+  if (nr < N) {
+    float *dst = p.ws_phi + (((size_t)nr * Hkv + hk) * (1 + G) + sub) * D + 4 * kq;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) *reinterpret_cast<f32x4 *>(dst + 16 * c) = f32x4{ph[c][0], ph[c][1], ph[c][2], ph[c][3]};
+  }
+}
+
 // x summed over the lanes that share lane % O (O = 8, 16 or 32), in the order of an xor
 // butterfly over O, 2 O, ..; every lane gets the same bits.
 template <int O> __device__ __forceinline__ float sum_lanes_mod(float x) {
@@ -458,8 +576,13 @@ __global__ __launch_bounds__(256, 2) void decode_step_kernel(DecParams p) {
 template <typename T, int D>
 static hipError_t launch_dec_t(const DecParams &p, hipStream_t stream) {
   const dim3 pgrid((p.N + DEC_ROWS - 1) / DEC_ROWS, p.Hkv + p.Hq);
-  if (p.hh) hipLaunchKernelGGL((decode_phi_kernel<T, D, true>), pgrid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL((decode_phi_kernel<T, D, false>), pgrid, dim3(256), 0, stream, p);
+  if constexpr (sizeof(T) == 2) {
+    if (p.hh) hipLaunchKernelGGL((decode_phi_b16_kernel<D, true>), pgrid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((decode_phi_b16_kernel<D, false>), pgrid, dim3(256), 0, stream, p);
+  } else {
+    if (p.hh) hipLaunchKernelGGL((decode_phi_kernel<T, D, true>), pgrid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((decode_phi_kernel<T, D, false>), pgrid, dim3(256), 0, stream, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.G == 1)
