@@ -16,11 +16,11 @@ constexpr float FAST_SPAN = 60.f; // max |log-decay| across a whole chunk for th
                                   // reference (keys carry e^{+60} at most, queries e^{-60})
 // The state pass and the self-started walk drop the chunks that reach their segment's end decayed
 // below e^{-SKIP_LOG} in every feature.  With features in (0, 1] a dropped token's term is below
-// e^{-24} ~ 4e-11 of the largest term a token can add to the same feature row, and the chunks
-// further back decay geometrically, so what is dropped stays some seven orders of magnitude below
-// bf16 rounding of the output (e^{-40} made the second segment's walk about 60% longer, 3% of the
-// forward on the Llama-3-8B-shaped layer, for no change the output can hold).
-constexpr float SKIP_LOG = 24.f;
+// e^{-16} ~ 1.1e-7 of the largest term a token can add to the same feature row, and the chunks
+// further back decay geometrically, so what is dropped stays about four orders of magnitude below
+// bf16 rounding of the output (e^{-40}, then e^{-24}, made the second segment's walk longer: 5%
+// and 2% of the forward on the Llama-3-8B-shaped layer, for no change the output can hold).
+constexpr float SKIP_LOG = 16.f;
 // The same cutoff for a feature map whose values are not bounded by one: the Hedgehog map's
 // features lie in [e^{-LOGIT_MAX}, e^{LOGIT_MAX}] under its documented logit bound, so a chunk is
 // dropped only once its largest possible term, decayed, is below e^{-SKIP_LOG} times the smallest

@@ -1641,7 +1641,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
 // Piece 0 also carries the block's log-gate sum D, the others D = 0, so that the whole-head
 // kernel's fold S = e^{D_j} S + E_j over the pieces in order gives every segment its start state.
 // Once the suffix is below -SKIP_LOG in every feature, the chunks before reach the block end
-// decayed by less than e^{-SKIP_LOG} (about 4e-11 of their size, far below what the bf16 output
+// decayed by less than e^{-SKIP_LOG} (about 1e-7 of their size, far below what the bf16 output
 // can hold): the walk stops there, and piece 0 sets D = NEG_BIG, dropping the state carried in.
 // With the Hedgehog map (features up to e^{HH_LOGIT_MAX}, not bounded by one) the cutoff is
 // -(SKIP_LOG + 2 HH_LOGIT_MAX), which bounds a dropped term relative to the smallest term any
