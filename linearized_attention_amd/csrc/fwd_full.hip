@@ -1435,6 +1435,29 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
         }
         safe = wave_max_all(span) <= SPAN_MAX;
       }
+      // Products decayed out (sub-chunk references only): once every feature has decayed below
+      // e^{-skip} between a key's sub-chunk end and the start of sub-chunk I - 1, every term of
+      // the block is below that fraction of its undecayed size (p_t - p_s <= C_{I-1} - C_J), the
+      // cutoff of the state pass; likewise the state's product once C_{I-1} is below -skip in
+      // every feature.  far_s: the inter-chunk product; far0, far1: key sub-chunks 0, 1 (J <= I - 2).
+      // C_J decreases with J, so far1 implies far0 and far0 implies far_s.
+      bool far_s = false, far0 = false, far1 = false;
+      if (!mild && I > 0) {
+        float ms = -INFINITY, m0 = -INFINITY, m1 = -INFINITY;
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+#pragma unroll
+        for (int q = 0; q < D / 64; ++q) {
+          const int f = ln + 64 * q;
+          const float cim1 = sTot[(I - 1) * D + f];
+          ms = fmaxf(ms, cim1);
+          m0 = fmaxf(m0, cim1 - sTot[f]);
+          m1 = fmaxf(m1, cim1 - sTot[D + f]);
+        }
+        far_s = wave_max_all(ms) < -skip_log<HH>();
+        far0 = I >= 2 && wave_max_all(m0) < -skip_log<HH>();
+        far1 = I >= 3 && wave_max_all(m1) < -skip_log<HH>();
+      }
       // sub-chunks whose diagonal block needs the exact products (added after the chunk loop)
       const bool unsafe = !safe;
       unsafe_seen |= unsafe;
@@ -1483,7 +1506,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
         // timed better; the wide-window variant has no registers to spare here)
       } else if (I == 0) {
         inter(qcf);
-      } else {
+      } else if (!far_s) {
         // sub-chunk references: the queries carry e^{p_t - C_{I-1}}; the state needs e^{p_t}
         Frag<T> qs[KS];
 #pragma unroll
@@ -1551,6 +1574,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
           // scores of the key sub-chunk pair (2m, 2m + 1), then one product with their v^T
 #pragma unroll 1
           for (int m = 0; 2 * m <= I; ++m) {
+            if (m == 0 && far1) continue;  // key sub-chunks 0 and 1 both decayed out (I = 3)
             f32x4 sc[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -1559,7 +1583,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
               if (J + 1 == I) {
 #pragma unroll
                 for (int js = 0; js < KS; ++js) a = mma(load8(sKt + (16 * J + r16) * LDW + 32 * js + 8 * g4), qcf[js], a);
-              } else if (J < I) {
+              } else if (J < I && !(J == 0 && far0)) {
 #pragma unroll
                 for (int js = 0; js < KS; ++js)
                   a = mma(load8(sKt + (16 * J + r16) * LDW + 32 * js + 8 * g4), qscaled(js, J + 1, I), a);
@@ -1593,7 +1617,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
             for (int dt = 0; dt < NDT; ++dt)
               acc[dt] = mma(load8(sVt + (16 * dt + r16) * LDV + 32 * m + 8 * g4), bf, acc[dt]);
           }
-          if constexpr (ZW) {  // the inter-chunk product (the other variant ran it before B3)
+          if (ZW && !far_s) {  // the inter-chunk product (the other variant ran it before B3)
 #pragma unroll
             for (int js = 0; js < KS; ++js) {
               const Frag<T> bf = I > 0 ? qscaled(js, 0, I) : qcf[js];
