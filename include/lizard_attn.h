@@ -78,7 +78,9 @@ typedef enum { LIZARD_F32 = 0, LIZARD_BF16 = 1 } lizard_dtype;
  *   log_gamma  [B, Hkv, L, d]    log of the gate, one value per key dimension
  *   w_phi_q    query-side feature-map weights [d, d] for head h at
  *              w_phi_q + h * w_phi_head_stride elements (stride 0: one matrix
- *              for every head); w_phi_k likewise, indexed by key/value head
+ *              for every head; otherwise at least d * d elements and a
+ *              multiple of 16 bytes, so that every matrix is 16-byte aligned);
+ *              w_phi_k likewise, indexed by key/value head
  *   t_k, t_v   [Hkv, M, d]       meta-memory keys / values (may be NULL if M = 0)
  *   out        [B, Hq, L, d]     written
  *   Hq must be a multiple of Hkv.  B = 0 or L = 0 is an empty problem: OK,

@@ -183,6 +183,9 @@ lizard_status fwd_impl(const void *q, const void *k, const void *v, const void *
   if (w_phi_head_stride != 0 && w_phi_head_stride < wsize)
     return fail(LIZARD_ERR_INVALID_ARG, "w_phi_head_stride=%lld overlaps matrices of %lld elements",
                 (long long)w_phi_head_stride, (long long)wsize);
+  if (w_phi_head_stride * (dtype == LIZARD_BF16 ? 2 : 4) % 16 != 0)
+    return fail(LIZARD_ERR_INVALID_ARG, "w_phi_head_stride=%lld elements leaves a matrix off 16-byte alignment",
+                (long long)w_phi_head_stride);
   if (hedgehog && !use_full_kernel(d, W, dtype))
     return fail(LIZARD_ERR_UNSUPPORTED, "the Hedgehog map is built for bf16, d = 128, W <= %d", 2 * kChunk + 1);
   if (B == 0 || L == 0) return LIZARD_OK;  // empty problem
@@ -443,6 +446,9 @@ static lizard_status decode_impl(float *state, void *win_k, void *win_v, int32_t
   if (w_phi_head_stride != 0 && w_phi_head_stride < wsize)
     return fail(LIZARD_ERR_INVALID_ARG, "w_phi_head_stride=%lld overlaps matrices of %lld elements",
                 (long long)w_phi_head_stride, (long long)wsize);
+  if (w_phi_head_stride * (dtype == LIZARD_BF16 ? 2 : 4) % 16 != 0)
+    return fail(LIZARD_ERR_INVALID_ARG, "w_phi_head_stride=%lld elements leaves a matrix off 16-byte alignment",
+                (long long)w_phi_head_stride);
   if (N == 0) return LIZARD_OK;
   if (!state || !win_k || !win_v || !pos || !q || !k || !v || !log_gamma || !w_phi_q || !w_phi_k || !out)
     return fail(LIZARD_ERR_INVALID_ARG, "null tensor pointer");

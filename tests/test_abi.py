@@ -54,7 +54,7 @@ def _fwd(lib, fn="lizard_attn_fwd", **kw):
     (dict(q=None), 1), (dict(out=None), 1), (dict(Hq=3, Hkv=2), 1), (dict(Hkv=0), 1),
     (dict(W=0), 1), (dict(M=-1), 1), (dict(L=-5), 1), (dict(dtype=7), 1),
     (dict(q=24), 1),                       # misaligned
-    (dict(stride=-1), 1), (dict(stride=100), 1),
+    (dict(stride=-1), 1), (dict(stride=100), 1), (dict(stride=128 * 128 + 4), 1),  # misaligned matrices
     (dict(d=96), 2), (dict(d=128, dtype=0), 2), (dict(M=17), 2),
     (dict(tk=None), 1),
     (dict(mix=-0.25), 1), (dict(mix=float("nan")), 1), (dict(mix=float("inf")), 1),
@@ -69,6 +69,7 @@ def test_fwd_validation_codes(kw, code):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), 1), (dict(Hq=3, Hkv=2), 1), (dict(stride=100), 1),
     (dict(stride=128 * 64 - 1), 1),                          # overlaps matrices of d x d/2 elements
+    (dict(stride=128 * 64 + 4), 1),                          # matrices off 16-byte alignment
     (dict(d=64), 2), (dict(d=64, dtype=0), 2),            # only bf16, d = 128
     (dict(W=130), 2),                                       # windows of at most 129 keys
 ])
@@ -153,6 +154,7 @@ def _dec(lib, fn="lizard_attn_decode", **kw):
     (dict(d=32), 2), (dict(W=257), 2), (dict(M=20), 2), (dict(q=8), 1), (dict(pos=18), 1),
     (dict(ws=None), 3), (dict(wsb=100), 3), (dict(ws=24), 1),
     (dict(mix=-1.0), 1), (dict(mix=float("nan")), 1), (dict(scale=float("inf")), 1),
+    (dict(stride=128 * 128 + 2), 1),                        # matrices off 16-byte alignment
 ])
 def test_decode_validation_codes(kw, code):
     lib = api.load()
