@@ -61,7 +61,7 @@ constexpr int TS = 16;              // tokens per sweep step / window tile
 constexpr float MILD_SPAN = 60.f;   // -P at most this for the split exponentials
 constexpr int QPW = 32;             // query tiles per wave in the window-q kernel
 constexpr int NB = 5;               // key tiles of a band the window-q kernel loads at once
-constexpr int FB_CHUNKS = 8;        // 64-row chunks per block of the feature-map backward
+constexpr int FB_CHUNKS = 32;       // 64-row chunks per block of the feature-map backward
 constexpr int NPF = 4;              // ring of step loads in the sweeps
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
