@@ -132,3 +132,37 @@ def test_separate_per_head_w_full_size_sampled_heads(gpu_lib, fmap):
             e = float(rel_l2(outs[mix][b:b + 1, h:h + 1].double().numpy(), want).max())
             _say(f"      (b={b}, h={h}) {name}: rel-L2 {e:.3e}")
             assert e <= TOL, f"(b={b},h={h}) {name}: {e:.3e}"
+
+
+@pytest.mark.parametrize("idx,fmap,heads", [
+    (4, "softmax", [(0, 0), (1, 13), (1, 31)]),
+    (4, "hedgehog", [(1, 7)]),
+    (2, "softmax", [(0, 5)]),
+    (2, "hedgehog", [(0, 17)]),
+], ids=["gqa-softmax", "gqa-hedgehog", "32k-softmax", "32k-hedgehog"])
+def test_separate_per_head_w_gqa_and_long_context_sampled_heads(gpu_lib, idx, fmap, heads):
+    """The grouped-query layer (32 query heads on 8 key/value heads, one W_phi copy per query head)
+    and the 32K uniform-gate stress (windows of 128 keys: the feature-map pass) with a W_phi per
+    query head and per key/value head, oracle on sampled heads."""
+    c = WORKLOADS[idx]
+    G = c["Hq"] // c["Hkv"]
+    inp = make_fwd_inputs(B=c["B"], Hq=c["Hq"], Hkv=c["Hkv"], L=c["L"], d=c["d"], W=c["W"], M=c["M"],
+                          dtype="bf16", seed=3100 + idx, gate=c["gate"], per_head_w=True, separate_wk=True,
+                          phi_cols=c["d"] // 2 if fmap == "hedgehog" else None)
+    _say(f"[separate W, {fmap}] workload {idx} q{tuple(inp.q.shape)} k{tuple(inp.k.shape)} "
+         f"w_q{tuple(inp.w_phi_q.shape)} w_k{tuple(inp.w_phi_k.shape)}")
+    dev = inp.to("cuda")
+    outs = {mix: gpu_fwd(dev, inp, mix, fmap).cpu() for mix in (inp.mix, 1.0, 0.0)}
+    del dev
+    for (b, h) in heads:
+        hk = h // G
+        qs = lambda t: t[b:b + 1, h:h + 1]
+        ks = lambda t: t[b:b + 1, hk:hk + 1]
+        y, yg, yw = oracle.lizard_fwd(qs(inp.q), ks(inp.k), ks(inp.v), ks(inp.log_gamma),
+                                      inp.w_phi_q[h:h + 1], inp.w_phi_k[hk:hk + 1], inp.t_k[hk:hk + 1],
+                                      inp.t_v[hk:hk + 1], W=inp.W, M=inp.M, mix=inp.mix, scale=inp.scale,
+                                      return_branches=True, feature_map=fmap)
+        for mix, want, name in ((inp.mix, y, "merged"), (1.0, yg, "gla"), (0.0, yw, "window")):
+            e = float(rel_l2(outs[mix][b:b + 1, h:h + 1].double().numpy(), want).max())
+            _say(f"      (b={b}, h={h}, kv head {hk}) {name}: rel-L2 {e:.3e}")
+            assert e <= TOL, f"(b={b},h={h}) {name}: {e:.3e}"
