@@ -1223,7 +1223,7 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
     constexpr bool QPASS = QPHI && ZW, QGLOBAL = QPHI && !ZW;
     const __amdgpu_buffer_rsrc_t wq_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         QGLOBAL ? static_cast<void *>(reinterpret_cast<T *>(p.ws_wq) + (size_t)(p.per_head_q ? hq : 0) * D * D)
-                : static_cast<void *>(smem),
+                : nullptr,
         (short)0, QGLOBAL ? D * D * (int)sizeof(T) : 0, BUF_RSRC_WORD3);
     constexpr int NWQ = QGLOBAL ? 4 : 1;
     Frag<T> wqf[NWQ][KS];
