@@ -1274,10 +1274,17 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
             f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < KS; ++j) a = mma(load8(sK + (16 * u + r16) * LDW + 32 * j + 8 * g4), qf[j], a);
+            // (wave-uniform, the wide-window variant) every key of the tile in every row's window:
+            // no per-element mask (the narrow variant timed no better without its masks)
+            if (ZW && c0 - CH + 16 * u >= -hist_avail && p.W >= 16 * (I - u) + 80) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int kj = c0 - CH + 16 * u + 4 * g4 + i;
-              lt[1 + u][i] = (kj >= kmin) ? a[i] * sl2 : NEG_BIG;
+              for (int i = 0; i < 4; ++i) lt[1 + u][i] = a[i] * sl2;
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int kj = c0 - CH + 16 * u + 4 * g4 + i;
+                lt[1 + u][i] = (kj >= kmin) ? a[i] * sl2 : NEG_BIG;
+              }
             }
           }
         }
@@ -1378,10 +1385,17 @@ __global__ __launch_bounds__(512, 1) void fwd_full_kernel(FwdParams p) {
             f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < KS; ++j) a = mma(load8(sK + (16 * u + r16) * LDW + 32 * j + 8 * g4), qf[j], a);
+            // (wave-uniform, the wide-window variant) a tile before the diagonal inside every row's
+            // window: no mask
+            if (ZW && u < I && p.W >= 16 * (I - u) + 16) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int kj = c0 + 16 * u + 4 * g4 + i;
-              lt[u][i] = (kj <= pos && kj >= kmin) ? a[i] * sl2 : NEG_BIG;
+              for (int i = 0; i < 4; ++i) lt[u][i] = a[i] * sl2;
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int kj = c0 + 16 * u + 4 * g4 + i;
+                lt[u][i] = (kj <= pos && kj >= kmin) ? a[i] * sl2 : NEG_BIG;
+              }
             }
           }
         }
