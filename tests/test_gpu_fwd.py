@@ -4,6 +4,7 @@ Relative L2 error per (batch, head) over L x d, for the merged output and for
 each branch on its own (mix = 1 isolates the gated-linear-attention branch,
 mix = 0 the window branch): <= 1e-4 for fp32 inputs, <= 2e-2 for bf16.
 """
+import dataclasses
 import sys
 import zlib
 
@@ -97,6 +98,24 @@ def test_fwd_matches_oracle(gpu_lib, label, kw, dtype):
     else:
         inp = make_fwd_inputs(dtype=dtype, seed=zlib.crc32(label.encode()) % 10000, **kw)
     check_case(label, inp, dtype)
+
+
+@pytest.mark.parametrize("W", [64, 100])
+@pytest.mark.parametrize("pattern", ["all fast", "half slow"])
+def test_fwd_decayed_out_products(gpu_lib, W, pattern):
+    """log gamma = -2 per token (32 per 16-token sub-chunk, sub-chunk references): the query waves
+    leave out the products with key sub-chunks two or more back and the inter-chunk product, which
+    have decayed below e^-16 in every feature.  With half the features at -0.01 per token instead,
+    nothing may be left out (the slow features keep every product): a wrong cutoff, taken over
+    the fast features only, would lose half of the global branch.  Both against the oracle per
+    branch, for the narrow and the wide-window variant."""
+    label = f"decayed-out {pattern} W{W}"
+    inp = make_fwd_inputs(B=1, Hq=2, Hkv=2, L=320, d=128, W=W, M=4, dtype="bf16",
+                          seed=zlib.crc32(label.encode()) % 10000)
+    lg = torch.full_like(inp.log_gamma, -2.0)
+    if pattern == "half slow":
+        lg[..., 64:] = -0.01
+    check_case(label, dataclasses.replace(inp, log_gamma=lg), "bf16")
 
 
 def _chunk_kinds(log_gamma, chunk=64, fast_span=60.0):
