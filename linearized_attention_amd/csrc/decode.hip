@@ -14,10 +14,11 @@
 // Two kernels:
 //   decode_phi   every feature map of the step as one small GEMM on the matrix
 //                cores: rows are the new keys (per key/value head) and queries
-//                (per query head) of 64 sequences, times W_phi staged
-//                transposed in LDS, then the softmax over features (or the
-//                Hedgehog map's exponential).  fp32
-//                results go to the workspace.
+//                (per query head) of 64 sequences, times W_phi staged in LDS
+//                (bf16: as stored, the operand read transposed; fp32:
+//                transposed when staged), then the softmax over features (or
+//                the Hedgehog map's exponential).  fp32 results go to the
+//                workspace.
 //   decode_step  one workgroup per (sequence, key/value head), bound by HBM
 //                traffic.  It issues its loads in the order it consumes them
 //                -- the per-token vectors and meta tokens, the ring
