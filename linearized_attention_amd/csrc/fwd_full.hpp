@@ -78,28 +78,14 @@ __device__ __forceinline__ void feature_map_rows(const f32x4 (&z)[NFT], float (&
   } else {
     // softmax over the D features of the row (4 lanes x NFT x 4 values): max and sum as trees
     // rather than one chain through all NFT x 4 values
-    float st[NFT];
-    float zmax;
-    if constexpr (NFT == 8) {
-      // three-input maxima (v_max3): 16 operations over the 32 values, four deep
-      float a[8];
+    float mt[NFT], st[NFT];
 #pragma unroll
-      for (int ft = 0; ft < 8; ++ft) a[ft] = fmaxf(fmaxf(z[ft][0], z[ft][1]), z[ft][2]);
-      const float b0 = fmaxf(fmaxf(a[0], a[1]), a[2]), b1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
-      const float b2 = fmaxf(fmaxf(a[6], a[7]), z[0][3]), b3 = fmaxf(fmaxf(z[1][3], z[2][3]), z[3][3]);
-      const float b4 = fmaxf(fmaxf(z[4][3], z[5][3]), z[6][3]);
-      zmax = fmaxf(fmaxf(fmaxf(b0, b1), b2), fmaxf(fmaxf(b3, b4), z[7][3]));
-    } else {
-      float mt[NFT];
+    for (int ft = 0; ft < NFT; ++ft) mt[ft] = fmaxf(fmaxf(z[ft][0], z[ft][1]), fmaxf(z[ft][2], z[ft][3]));
 #pragma unroll
-      for (int ft = 0; ft < NFT; ++ft) mt[ft] = fmaxf(fmaxf(z[ft][0], z[ft][1]), fmaxf(z[ft][2], z[ft][3]));
+    for (int w = NFT / 2; w >= 1; w /= 2)
 #pragma unroll
-      for (int w = NFT / 2; w >= 1; w /= 2)
-#pragma unroll
-        for (int ft = 0; ft < w; ++ft) mt[ft] = fmaxf(mt[ft], mt[ft + w]);
-      zmax = mt[0];
-    }
-    const float zm2 = -wave_max_cols(zmax) * LOG2E;
+      for (int ft = 0; ft < w; ++ft) mt[ft] = fmaxf(mt[ft], mt[ft + w]);
+    const float zm2 = -wave_max_cols(mt[0]) * LOG2E;
 #pragma unroll
     for (int ft = 0; ft < NFT; ++ft) {
 #pragma unroll
