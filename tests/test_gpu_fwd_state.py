@@ -55,6 +55,11 @@ CASES = [
     ("bf16 d128 W100 split 40 (history shorter than the window)",
      dict(B=1, Hq=2, Hkv=2, L=230, d=128, W=100, M=4, gate="uniform:-1"), 40, "bf16"),
     ("fp32 d64 uniform gate split 70", dict(B=1, Hq=2, Hkv=2, L=250, d=64, W=64, M=4, gate="uniform"), 70, "f32"),
+    # separate query-side W_phi: its fragment-ordered copy sits in the workspace before the history rows
+    ("bf16 d128 separate W split 100", dict(B=2, Hq=2, Hkv=2, L=260, d=128, W=64, M=4, separate_wk=True),
+     100, "bf16"),
+    ("bf16 gqa 4:2 per-head W W100 split 150", dict(B=1, Hq=4, Hkv=2, L=300, d=128, W=100, M=4,
+                                                   per_head_w=True, separate_wk=True), 150, "bf16"),
 ]
 
 
