@@ -1537,6 +1537,171 @@ __global__ __launch_bounds__(256) void bwd_fb_kernel(BwdParams p) {
       for (int ii = 0; ii < 4; ++ii) part[(size_t)(16 * (NIT * w + it) + 4 * kq + ii) * FC + 16 * ct + r] = dw[it][ct][ii];
 }
 
+// The same for bf16 inputs, with phi recomputed from x and W_phi instead of read in fp32 (a quarter
+// less traffic): the logits taken transposed, z^T = W^T x^T, with the A operand read from W's rows
+// in LDS by transposed reads and x as the B operand as loaded, so that lane (r, kq) holds row r's
+// features 16 c + 4 kq + i; dphi is loaded in that order, and dz enters dx = dz W^T with K in the
+// interleaved order (the W rows read in two 8-byte pieces to match).  The feature map repeats
+// bwd_phi_kernel's arithmetic: fp32 logits from the same bf16 products, max subtracted, one
+// normaliser.
+template <int D, bool HH>
+__global__ __launch_bounds__(256) void bwd_fb_b16_kernel(BwdParams p) {
+  using T = bf16;
+  constexpr int KS = D / 32, FC = HH ? D / 2 : D, NCT = FC / 16, NC = D / 16, NIT = D / 64;
+  constexpr int LDW = FC + 8, LDX = D + 8, LDZ = FC + 8;  // 8-byte reads: odd multiples of 16 bytes
+  __shared__ __align__(16) T sW[D * LDW];   // W [i][c] rows
+  __shared__ __align__(16) T sX[64 * LDX];  // x rows of the chunk
+  __shared__ __align__(16) T sZ[64 * LDZ];  // dz rows of the chunk
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, kq = lane >> 4;
+  const int L = p.L;
+  const int nsplit = (L + 64 * FB_CHUNKS - 1) / (64 * FB_CHUNKS);
+  const bool qside = (int)blockIdx.x < p.B * p.Hq * nsplit;
+  const int bid = qside ? blockIdx.x : blockIdx.x - p.B * p.Hq * nsplit;
+  const int bh = bid / nsplit, split = bid % nsplit;
+  const int H = qside ? p.Hq : p.Hkv, h = bh % H;
+  const T *Wsrc = reinterpret_cast<const T *>(qside ? p.wq : p.wk) + (size_t)h * p.w_stride;
+  for (int idx = tid; idx < D * FC / 8; idx += 256)
+    *reinterpret_cast<Frag<T> *>(sW + (idx / (FC / 8)) * LDW + 8 * (idx % (FC / 8))) = load8(Wsrc + 8 * (size_t)idx);
+  const size_t o = (size_t)bh * L * D;
+  const T *X = reinterpret_cast<const T *>(qside ? p.q : p.k) + o;
+  const float *DPH = (qside ? p.dphq : p.dphk) + o;
+  const T *DXW = reinterpret_cast<const T *>(qside ? p.dqw : p.dkw) + o;
+  T *DX = reinterpret_cast<T *>(qside ? p.dq : p.dk) + o;
+  f32x4 dw[NIT][NCT];  // dW[i = 16 (NIT w + it) + 4 kq + ii][c = 16 ct + r]
+#pragma unroll
+  for (int it = 0; it < NIT; ++it)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) dw[it][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+  for (int c0 = 64 * FB_CHUNKS * split; c0 < min(L, 64 * FB_CHUNKS * (split + 1)); c0 += 64) {
+    const int t = c0 + 16 * w + r;
+    const bool tok = t < L;
+    const size_t trow = (size_t)min(t, L - 1) * D;
+    // the window part of dx, x and dphi of row t (clamped into the sequence; zeroed below past it)
+    F4<T> xw[D / 16];
+#pragma unroll
+    for (int it = 0; it < D / 16; ++it) xw[it] = ld_f4(DXW + trow + 16 * it + 4 * kq);
+    Frag<T> xf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) xf[ks] = tok ? load8(X + trow + 32 * ks + 8 * kq) : frag_zero<T>();
+    f32x4 dpv[NC];  // dphi[t][16 c + 4 kq + i]
+#pragma unroll
+    for (int c = 0; c < NC; ++c) dpv[c] = *reinterpret_cast<const f32x4 *>(DPH + trow + 16 * c + 4 * kq);
+    // logits: z[c][i] = (x W)[t][16 c + 4 kq + i]
+    f32x4 z[NCT];
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const F4<T> lo = lds_col4(sW, LDW, 32 * ks + 8 * kq, 16 * c), hi = lds_col4(sW, LDW, 32 * ks + 8 * kq + 4, 16 * c);
+        Frag<T> wa;
+        wa.v = __builtin_shufflevector(lo.v, hi.v, 0, 1, 2, 3, 4, 5, 6, 7);
+        a = mma(wa, xf[ks], a);
+      }
+      z[c] = a;
+    }
+    // dz of row t, features 16 c + 4 kq + i (zero past the sequence)
+    float dz[NCT][4];
+    if constexpr (HH) {
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dz[c][i] = exp2_fast(z[c][i] * LOG2E) * dpv[c][i] - exp2_fast(-z[c][i] * LOG2E) * dpv[NCT + c][i];
+    } else {
+      float m = z[0][0];
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, z[c][i]);
+      const float zm2 = -wave_max_cols(m) * LOG2E;
+      float ph[NCT][4], sum = 0.f;
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ph[c][i] = exp2_fast(__builtin_fmaf(z[c][i], LOG2E, zm2));
+          sum += ph[c][i];
+        }
+      const float inv = 1.f / wave_sum_cols(sum);
+      float dot = 0.f;
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ph[c][i] *= inv;
+          dot += ph[c][i] * dpv[c][i];
+        }
+      dot = wave_sum_cols(dot);
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dz[c][i] = ph[c][i] * (dpv[c][i] - dot);
+    }
+    if (!tok) {
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dz[c][i] = 0.f;
+    }
+    // dz operands in the interleaved K order (slots 0..3: tile 2 ks, 4..7: tile 2 ks + 1), and the
+    // dz rows into LDS in natural order for dW
+    Frag<T> dzf[FC / 32];
+#pragma unroll
+    for (int ks = 0; ks < FC / 32; ++ks) {
+      float y[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        y[i] = dz[2 * ks][i];
+        y[4 + i] = dz[2 * ks + 1][i];
+      }
+      dzf[ks] = frag_from<T>(y);
+    }
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) store4<T>(sZ + (16 * w + r) * LDZ + 16 * c + 4 * kq, dz[c][0], dz[c][1], dz[c][2], dz[c][3]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) *reinterpret_cast<Frag<T> *>(sX + (16 * w + r) * LDX + 32 * ks + 8 * kq) = xf[ks];
+    // dx[t][i] = sum_c W[i][c] dz[t][c] (lane (t = 16 w + r, kq): i = 16 it + 4 kq + ii)
+#pragma unroll
+    for (int it = 0; it < D / 16; ++it) {
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < FC / 32; ++ks) {
+        const T *wr = sW + (16 * it + r) * LDW + 32 * ks + 4 * kq;
+        a = mma(load4x2(wr, wr + 16), dzf[ks], a);
+      }
+      if (tok) {
+        const size_t off = (size_t)t * D + 16 * it + 4 * kq;
+        store4<T>(DX + off, a[0] + f4_at(xw[it], 0), a[1] + f4_at(xw[it], 1), a[2] + f4_at(xw[it], 2),
+                  a[3] + f4_at(xw[it], 3));
+      }
+    }
+    __syncthreads();  // x and dz rows of the chunk staged
+    // dW[i][c] += sum_t x[t][i] dz[t][c]: K = 64 rows in 16-row steps
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+      F4<T> za[NCT];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) za[ct] = lds_col4(sZ, LDZ, 16 * k4 + 4 * kq, 16 * ct);
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const F4<T> xa = lds_col4(sX, LDX, 16 * k4 + 4 * kq, 16 * (NIT * w + it));
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) dw[it][ct] = mma16(xa, za[ct], dw[it][ct]);
+      }
+    }
+    __syncthreads();
+  }
+  float *part = p.dw_part + (size_t)blockIdx.x * D * FC;
+#pragma unroll
+  for (int it = 0; it < NIT; ++it)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) part[(size_t)(16 * (NIT * w + it) + 4 * kq + ii) * FC + 16 * ct + r] = dw[it][ct][ii];
+}
+
 // ======================================================================== 7. reductions
 // dW_q (and dW_k): sum of the per-block partials over the heads that share a matrix, in two stages
 // with a fixed order (deterministic): stage 0 sums the partials of group g (partial index % RG == g)
@@ -1668,8 +1833,13 @@ static hipError_t launch_bwd_t(const BwdParams &p, hipStream_t st) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int nsplit = (p.L + 64 * FB_CHUNKS - 1) / (64 * FB_CHUNKS);
   const dim3 fbgrid((p.B * p.Hq + p.B * p.Hkv) * nsplit);
-  if (p.hh) hipLaunchKernelGGL((bwd_fb_kernel<T, D, true>), fbgrid, dim3(256), 0, st, p);
-  else hipLaunchKernelGGL((bwd_fb_kernel<T, D, false>), fbgrid, dim3(256), 0, st, p);
+  if constexpr (sizeof(T) == 2) {
+    if (p.hh) hipLaunchKernelGGL((bwd_fb_b16_kernel<D, true>), fbgrid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((bwd_fb_b16_kernel<D, false>), fbgrid, dim3(256), 0, st, p);
+  } else {
+    if (p.hh) hipLaunchKernelGGL((bwd_fb_kernel<T, D, true>), fbgrid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((bwd_fb_kernel<T, D, false>), fbgrid, dim3(256), 0, st, p);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int FC = p.hh ? D / 2 : D;
   const size_t nw = (size_t)((p.w_stride ? p.Hq : 1) + (p.w_stride ? p.Hkv : 1)) * D * FC;
