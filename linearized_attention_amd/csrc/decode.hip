@@ -35,7 +35,7 @@
 
 namespace lz {
 
-constexpr int DEC_MAXG = 4;   // query heads per key/value head per pass (grouped heads)
+constexpr int DEC_MAXG = 2;   // query heads per key/value head per pass (grouped heads; four spilled)
 constexpr int DEC_MAXW = 256; // ring length limit
 constexpr int DEC_MAXM = 16;
 constexpr int DEC_RKEYS = 64; // ring keys per logits pass (4 lanes per key)

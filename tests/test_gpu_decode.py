@@ -62,8 +62,10 @@ CASES = [
                                      zero_state=True), "f32"),
     ("fp32 d64 pos0=3 W7 M0", dict(N=3, Hq=2, Hkv=2, d=64, W=7, M=0, steps=9, pos0=3, dtype="f32"), "f32"),
     ("bf16 d64 gqa 8:2 W100", dict(N=9, Hq=8, Hkv=2, d=64, W=100, M=16, steps=4, pos0=250, dtype="bf16"), "bf16"),
-    ("bf16 d128 gqa 6:1 (two head passes)", dict(N=4, Hq=6, Hkv=1, d=128, W=64, M=4, steps=3, pos0=64,
-                                                  dtype="bf16"), "bf16"),
+    ("bf16 d128 gqa 6:1 (three head passes)", dict(N=4, Hq=6, Hkv=1, d=128, W=64, M=4, steps=3, pos0=64,
+                                                    dtype="bf16"), "bf16"),
+    ("bf16 d128 gqa 3:1 (a partial head pass)", dict(N=5, Hq=3, Hkv=1, d=128, W=64, M=4, steps=3, pos0=20,
+                                                     dtype="bf16"), "bf16"),
     ("bf16 d128 W256 M16 (four logits passes)", dict(N=3, Hq=2, Hkv=2, d=128, W=256, M=16, steps=3, pos0=300,
                                                       dtype="bf16"), "bf16"),
 ]
